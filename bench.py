@@ -1,0 +1,180 @@
+#!/usr/bin/env python3
+"""Benchmark of the MHLA forward pass on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload dit_s2_256] [--gpus 1]
+
+One step is one full forward pass (phi, block summaries, mixing, output) over
+the workload's synthetic batch, with inputs resident in HBM before the timed
+region.  Prints ONE JSON line with throughput (tokens/s), model TFLOP/s, the
+HBM roofline of the dominant kernel (per-kernel durations measured with HIP
+events on the launch stream) and the CPU oracle timed on this host's cores.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+import token_level_head_amd as mh
+from token_level_head_amd.workloads import WORKLOADS, make_inputs
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+METRIC = "MHLA fwd tokens/s and TFLOP/s at 1 MI355X; % of HBM/MFMA roofline"
+
+
+def model_flops(w):
+    """Model FLOPs of one forward pass (multiply-add = 2)."""
+    BH, N, d, M, C = w.B * w.H, w.N, w.d, w.M, w.C
+    nnz = M * (M - 1) // 2 if w.causal else M * M
+    per_pair = N * (2 * d * d + d)            # summaries: phi(k) v^T and z
+    per_pair += 2 * nnz * (d * d + d)         # mixing GEMM
+    per_pair += N * (2 * d * d + 3 * d)       # output: numerator, denominator, divide
+    if w.causal:
+        per_pair += N * (2 * d * (C + 1) + (C + 1) / 2)  # within-block prefix (average over positions)
+    return BH * per_pair
+
+
+def kernel_bytes(w):
+    """Algorithmic HBM bytes per launch of each stage (inputs read once, outputs written once)."""
+    BH, N, d, M = w.B * w.H, w.N, w.d, w.M
+    e = 2 if w.dtype == "bf16" else 4
+    L = d * d + d
+    summ = BH * M * L * 4
+    return {
+        "summaries": 2 * BH * N * d * e + summ,
+        "mix": 2 * summ + M * M * 4,
+        "output": BH * N * d * e + summ + BH * N * d * 4 + (2 * BH * N * d * e + M * 4 if w.causal else 0),
+    }
+
+
+def cpu_baseline(w, q, k, v, W, budget_s):
+    import oracle  # test infrastructure: used only for this reported baseline
+
+    orc = oracle.default_oracle()
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    cores = max(1, min(cores, 16))
+    orc.forward(q, k, v, W, causal=w.causal, nthreads=cores)  # warm caches and page-in
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        orc.forward(q, k, v, W, causal=w.causal, nthreads=cores)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= budget_s:
+            break
+    return {
+        "value": w.tokens * reps / dt,
+        "unit": "tokens/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"the whole {w.key} batch ({w.tokens} tokens), repeated {reps}x in {dt:.2f} s on {cores} threads",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="dit_s2_256", choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-budget", type=float, default=1.5, help="seconds of oracle wall time")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path).", file=sys.stderr)
+        return 2
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+
+    w = WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    mh.load_library()
+    q, k, v, W = make_inputs(w)
+    dt_in = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    qd, kd, vd = (torch.from_numpy(a).to(device="cuda", dtype=dt_in) for a in (q, k, v))
+    Wd = torch.from_numpy(W).cuda()
+    out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    fwd = mh.mhla_forward if w.dtype == "bf16" else mh.mhla_forward_f32
+    stream = torch.cuda.current_stream()
+
+    # ---- whole-pass throughput ----
+    for _ in range(args.warmup):
+        fwd(qd, kd, vd, Wd, out, causal=w.causal)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        fwd(qd, kd, vd, Wd, out, causal=w.causal)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    tokens_s = w.tokens / (ms * 1e-3)
+    tflops = model_flops(w) / (ms * 1e-3) / 1e12
+
+    # ---- per-kernel durations: the three stages launched one by one on the same stream ----
+    L = w.d * w.d + w.d
+    S = torch.empty(w.M * w.B * w.H * L, dtype=torch.float32, device="cuda")
+    St = torch.empty_like(S)
+    names = ["summaries", "mix", "output"]
+    stages = [
+        lambda: mh.mhla_block_summaries(kd, vd, S, w.M),
+        lambda: mh.mhla_mix_summaries(S, Wd, St, w.B * w.H, w.d, causal=w.causal, precise=(w.dtype == "f32")),
+        lambda: mh.mhla_output(qd, kd, vd, St, Wd, out, causal=w.causal),
+    ]
+    for _ in range(args.warmup):
+        for f in stages:
+            f()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        for i, f in enumerate(stages):
+            f()
+            ev[s][i + 1].record(stream)
+    torch.cuda.synchronize()
+    kms = {n: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]))
+           for i, n in enumerate(names)}
+    kb = kernel_bytes(w)
+    kernels = {n: {"ms": round(kms[n], 5), "bytes": kb[n],
+                   "GBps": round(kb[n] / (kms[n] * 1e-3) / 1e9, 1),
+                   "hbm_frac": round(kb[n] / (kms[n] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)} for n in names}
+    dom = max(names, key=lambda n: kms[n])
+    achieved = kb[dom] / (kms[dom] * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, q, k, v, W, args.cpu_budget)
+
+    line = {
+        "metric": METRIC,
+        "value": round(tokens_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.key, "description": w.description, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "M": w.M, "causal": w.causal, "global_batch": w.B, "seq_len": w.N, "parallelism": "none (1 GPU)"},
+        "tflops": round(tflops, 3),
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,145 @@
+/*
+ * mhla.h -- C ABI of the MI355X (gfx950) MHLA forward library, libmhla.so.
+ *
+ * MHLA, "MHLA: Restoring Expressivity of Linear Attention via Token-Level
+ * Multi-Head" (§4.1, §4.2, App. C), computes for every (batch, head) pair:
+ *
+ *   phi(x)  = ELU(x) + 1                                  ("Linear Attention 笔记" §2)
+ *   S_b     = sum_{j in block b} phi(k_j) v_j^T   (d x d)  z_b = sum_{j in b} phi(k_j)   (§4.1)
+ *   S~_i    = sum_b W[i,b] S_b,                            z~_i = sum_b W[i,b] z_b       (§4.1, §4.2)
+ *   y_t     = phi(q_t)^T S~_i / (phi(q_t)^T z~_i + 1e-6)   for t in query block i    (§4.1; guard as in
+ *                                                          "Linear Attention 笔记" §4/§5)
+ *
+ * Causal variant (App. C, chunkwise form of §4.2): S~_i mixes only earlier
+ * blocks b < i, and token t of block i adds W[i,i] times the running summary of
+ * its own block up to and including t:
+ *   y_t = phi(q_t)^T (S~_i + W[i,i] P_t) / (phi(q_t)^T (z~_i + W[i,i] p_t) + 1e-6),
+ *   P_t = sum_{j in i, j <= t} phi(k_j) v_j^T,  p_t = sum_{j in i, j <= t} phi(k_j).
+ * Entries of W above the diagonal are never read in the causal variant.
+ *
+ * Common conventions
+ *   - Pointers named q, k, v, W, out, S, St are DEVICE pointers on the current
+ *     HIP device; the caller allocates and owns them.  The library keeps no
+ *     pointer after a call returns, except inside work already enqueued on
+ *     `stream`: keep the buffers alive until that work completes.
+ *   - Layouts are row-major and contiguous: q, k, v, out are [B][H][N][d];
+ *     W is [M][M] float32 with W[i*M + b] the weight of block b's summary for
+ *     query block i.  One W is shared by every batch element and head.
+ *   - Blocks are contiguous: block b holds tokens [b*C, (b+1)*C), C = N / M.
+ *     Spatial (2D/3D) blocks are expressed by storing tokens block-major.
+ *   - Supported sizes: B, H, N, M >= 1, N % M == 0, d in {16, 32, 64}.
+ *     bf16 inputs are IEEE bfloat16 bit patterns (uint16 per element).
+ *   - Pointers must be 16-byte aligned; `out` must not overlap any input.
+ *   - Every call validates its arguments on the host before enqueueing
+ *     anything; a non-zero status means nothing was enqueued, except
+ *     MHLA_ERR_HIP, which reports a failed HIP call or launch (the stream
+ *     may then hold part of the work).  No call synchronises the device,
+ *     throws, or aborts.  mhla_last_error() returns a thread-local message
+ *     describing the last failure on the calling thread.
+ *   - Preconditions not checked on the device: W finite and >= 0 with every
+ *     used row non-zero (§4.2: rows of M_c are nonnegative and normalised).
+ *     NaN inputs give NaN outputs.
+ *   - Identical inputs give bit-identical outputs (no floating-point atomics).
+ */
+#ifndef MHLA_H
+#define MHLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+struct ihipStream_t;
+/* The same type as hipStream_t; NULL means the device's null stream. */
+typedef struct ihipStream_t* mhla_stream_t;
+
+enum {
+    MHLA_OK = 0,
+    MHLA_ERR_INVALID_ARG = -1, /* null or misaligned pointer, bad sizes, N % M != 0, overlap */
+    MHLA_ERR_UNSUPPORTED = -2, /* valid but not implemented here (e.g. d not in {16,32,64}) */
+    MHLA_ERR_NO_MEMORY = -3,   /* workspace allocation failed */
+    MHLA_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
+};
+
+/* Input element type for the stage-level calls. */
+enum { MHLA_DTYPE_BF16 = 0, MHLA_DTYPE_F32 = 1 };
+
+/*
+ * Full forward pass, bfloat16 q/k/v (float32 accumulation, float32 W and out).
+ * Enqueues the three kernels -- block summaries, block mixing, output -- on
+ * `stream`.  The summaries live in a stream-ordered workspace of
+ * mhla_workspace_bytes() bytes taken from a library-owned memory pool on the
+ * current device and returned to it (stream-ordered) before the call returns.
+ * causal != 0 selects the causal variant.
+ */
+int mhla_forward(const void* q, const void* k, const void* v, const float* W, float* out,
+                 int64_t B, int64_t H, int64_t N, int64_t d, int64_t M, int causal,
+                 mhla_stream_t stream);
+
+/* Same as mhla_forward with float32 q/k/v; every step runs in float32. */
+int mhla_forward_f32(const float* q, const float* k, const float* v, const float* W, float* out,
+                     int64_t B, int64_t H, int64_t N, int64_t d, int64_t M, int causal,
+                     mhla_stream_t stream);
+
+/* Bytes of device workspace one forward call uses (the S and S~ summary
+ * arrays, 2 * M * B*H * (d*d + d) floats); -1 for invalid sizes. */
+int64_t mhla_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int64_t M, int causal);
+
+/* Floats in one packed summary vector: d*d + d (S_b followed by z_b). */
+int64_t mhla_summary_floats(int64_t d);
+
+/*
+ * Stage 1 (§4.1, local KV summaries): phi(K) and the per-block reductions.
+ * Writes S[b][p][0 .. d*d+d) for every block b < M and pair p = batch*H + head:
+ * a packed summary vector holding S_b (d*d floats, in the MFMA-native order
+ * decoded by mhla_unpack_summaries) followed by z_b (d floats, plain order).
+ * S must hold M * B*H * (d*d + d) floats.  dtype is MHLA_DTYPE_BF16 or _F32
+ * and describes k and v.
+ */
+int mhla_block_summaries(const void* k, const void* v, int dtype, float* S,
+                         int64_t B, int64_t H, int64_t N, int64_t d, int64_t M,
+                         mhla_stream_t stream);
+
+/*
+ * Stage 2 (§4.1 multi-head mixing, done as one GEMM with the coefficient
+ * matrix as §4.1 describes): St[i][p][:] = sum_b W[i,b] S[b][p][:] over all
+ * b (causal == 0) or over b < i (causal != 0; row 0 becomes zero).  S and St
+ * use the packed layout of mhla_block_summaries; `precise` selects float32
+ * products (used by the float32 path) instead of the bfloat16 hi/lo split
+ * (three bfloat16 products per term, float32 accumulation).
+ */
+int mhla_mix_summaries(const float* S, const float* W, float* St, int64_t BH, int64_t d, int64_t M,
+                       int causal, int precise, mhla_stream_t stream);
+
+/*
+ * Stage 3 (§4.1 output ratio; App. C for causal): y_t from phi(q_t) and the
+ * mixed summaries St of stage 2.  k and v are read only when causal != 0 (the
+ * within-block running summary and W[i,i]); W is read only when causal != 0.
+ * Writes out [B][H][N][d] float32.
+ */
+int mhla_output(const void* q, const void* k, const void* v, int dtype, const float* St,
+                const float* W, float* out, int64_t B, int64_t H, int64_t N, int64_t d, int64_t M,
+                int causal, mhla_stream_t stream);
+
+/*
+ * Host-only helper (no HIP calls): decodes `count` packed summary vectors in
+ * HOST memory into row-major S [count][d][d] (S[r][c] = sum phi(k)[r] v[c])
+ * and z [count][d].  Returns MHLA_OK or MHLA_ERR_INVALID_ARG.
+ */
+int mhla_unpack_summaries(const float* packed, int64_t count, int64_t d, float* S, float* z);
+
+/* Human-readable name of a status code (static storage). */
+const char* mhla_status_string(int status);
+
+/* Thread-local description of the last failing call on this thread ("" if none). */
+const char* mhla_last_error(void);
+
+/* Library version string (static storage). */
+const char* mhla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MHLA_H */

@@ -20,3 +20,14 @@ def orc():
     import oracle
 
     return oracle.default_oracle()
+
+
+@pytest.fixture(scope="session")
+def mhla_lib():
+    """libmhla.so, built first only if it is missing (the build needs no GPU)."""
+    import token_level_head_amd as mh
+    from token_level_head_amd import build
+
+    if not os.path.exists(mh.LIB_PATH):
+        build.build()
+    return mh.load_library()

@@ -1,0 +1,104 @@
+"""The C ABI on the host: exported symbols, argument validation, host helpers.
+
+No GPU is needed: every call here either fails validation before any HIP call
+or is a host-only function.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import token_level_head_amd as mh
+from token_level_head_amd.binding import SIGNATURES
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "mhla.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mhla_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_bound_api():
+    assert header_functions() == sorted(SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol(mhla_lib):
+    for name in header_functions():
+        assert hasattr(mhla_lib, name), name
+
+
+def test_version_and_sizes(mhla_lib):
+    assert mh.mhla_version().startswith("mhla-gfx950")
+    for d in (16, 32, 64):
+        assert mh.mhla_summary_floats(d) == d * d + d
+    assert mh.mhla_workspace_bytes(64, 6, 256, 64, 16) == 2 * 16 * 384 * (64 * 64 + 64) * 4
+    assert mh.mhla_workspace_bytes(1, 1, 250, 64, 16) == -1
+    assert mh.mhla_workspace_bytes(1, 1, 256, 24, 16) == -1
+
+
+FAKE = 1 << 20  # a 16-byte-aligned nonzero address; never dereferenced (validation fails first)
+
+
+@pytest.mark.parametrize("fn", ["mhla_forward", "mhla_forward_f32"])
+def test_forward_validation(mhla_lib, fn):
+    f = getattr(mhla_lib, fn)
+    p = [FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5]
+
+    def call(ptrs=p, B=1, H=1, N=256, d=16, M=4):
+        return f(*ptrs, B, H, N, d, M, 0, None)
+
+    assert call(ptrs=[None] + p[1:]) == mh.MHLA_ERR_INVALID_ARG
+    assert "q is NULL" in mh.mhla_last_error()
+    assert call(ptrs=p[:4] + [None]) == mh.MHLA_ERR_INVALID_ARG
+    assert call(ptrs=[FAKE + 2] + p[1:]) == mh.MHLA_ERR_INVALID_ARG
+    assert "aligned" in mh.mhla_last_error()
+    assert call(N=250) == mh.MHLA_ERR_INVALID_ARG
+    assert "multiple" in mh.mhla_last_error()
+    assert call(B=0) == mh.MHLA_ERR_INVALID_ARG
+    assert call(M=0) == mh.MHLA_ERR_INVALID_ARG
+    assert call(d=24) == mh.MHLA_ERR_UNSUPPORTED
+    assert call(d=128) == mh.MHLA_ERR_UNSUPPORTED
+    assert call(B=1 << 30, H=1 << 30) == mh.MHLA_ERR_INVALID_ARG
+    # out overlapping q
+    assert call(ptrs=[FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE + 64]) == mh.MHLA_ERR_INVALID_ARG
+    assert "overlap" in mh.mhla_last_error()
+
+
+def test_stage_validation(mhla_lib):
+    assert mhla_lib.mhla_block_summaries(FAKE, FAKE * 2, 7, FAKE * 3, 1, 1, 256, 16, 4, None) == mh.MHLA_ERR_INVALID_ARG
+    assert mhla_lib.mhla_block_summaries(None, FAKE * 2, 0, FAKE * 3, 1, 1, 256, 16, 4, None) == mh.MHLA_ERR_INVALID_ARG
+    assert mhla_lib.mhla_mix_summaries(FAKE, FAKE * 2, FAKE, 1, 16, 4, 0, 0, None) == mh.MHLA_ERR_INVALID_ARG
+    assert mhla_lib.mhla_mix_summaries(FAKE, FAKE * 2, FAKE * 3, 1, 48, 4, 0, 0, None) == mh.MHLA_ERR_UNSUPPORTED
+    # the causal output reads k, v and W; the non-causal one does not need them
+    assert mhla_lib.mhla_output(FAKE, None, None, 0, FAKE * 2, None, FAKE * 3, 1, 1, 256, 16, 4, 1, None) == \
+        mh.MHLA_ERR_INVALID_ARG
+
+
+def test_status_strings(mhla_lib):
+    assert mh.mhla_status_string(0) == "MHLA_OK"
+    assert mh.mhla_status_string(mh.MHLA_ERR_HIP) == "MHLA_ERR_HIP"
+    assert mh.mhla_status_string(12345) == "MHLA_ERR_UNKNOWN"
+
+
+@pytest.mark.parametrize("d", [16, 32, 64])
+def test_unpack_is_a_permutation(mhla_lib, d):
+    """The packed summary layout stores every S[r][c] exactly once, then z in order."""
+    L = d * d + d
+    packed = torch.arange(2 * L, dtype=torch.float32).reshape(2, L)
+    S, z = mh.mhla_unpack_summaries(packed, d)
+    for u in range(2):
+        vals = np.sort(S[u].numpy().ravel())
+        assert np.array_equal(vals, np.arange(u * L, u * L + d * d, dtype=np.float32))
+        assert np.array_equal(z[u].numpy(), np.arange(u * L + d * d, (u + 1) * L, dtype=np.float32))
+
+
+def test_unpack_validation(mhla_lib):
+    buf = np.zeros(16, dtype=np.float32)
+    p = buf.ctypes.data_as(ctypes.c_void_p)
+    assert mhla_lib.mhla_unpack_summaries(None, 1, 16, p, p) == mh.MHLA_ERR_INVALID_ARG
+    assert mhla_lib.mhla_unpack_summaries(p, 1, 20, p, p) == mh.MHLA_ERR_UNSUPPORTED

@@ -1,0 +1,166 @@
+"""Thin ctypes binding over libmhla.so (the C ABI in include/mhla.h).
+
+Argument marshalling only: every function here forwards device pointers, sizes
+and the current HIP stream to the C entry point of the same name, and turns a
+non-zero status into :class:`MhlaError`.  All arithmetic runs in the library's
+HIP kernels.  There is no fallback: if the library is not built, or no GPU is
+present, the calls raise.
+"""
+import ctypes
+import os
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmhla.so")
+
+MHLA_OK = 0
+MHLA_ERR_INVALID_ARG = -1
+MHLA_ERR_UNSUPPORTED = -2
+MHLA_ERR_NO_MEMORY = -3
+MHLA_ERR_HIP = -4
+MHLA_DTYPE_BF16 = 0
+MHLA_DTYPE_F32 = 1
+
+# Every symbol include/mhla.h declares, with (restype, argtypes).
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I = ctypes.c_int
+SIGNATURES = {
+    "mhla_forward": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _P]),
+    "mhla_forward_f32": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _P]),
+    "mhla_workspace_bytes": (_I64, [_I64, _I64, _I64, _I64, _I64, _I]),
+    "mhla_summary_floats": (_I64, [_I64]),
+    "mhla_block_summaries": (_I, [_P, _P, _I, _P, _I64, _I64, _I64, _I64, _I64, _P]),
+    "mhla_mix_summaries": (_I, [_P, _P, _P, _I64, _I64, _I64, _I, _I, _P]),
+    "mhla_output": (_I, [_P, _P, _P, _I, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _P]),
+    "mhla_unpack_summaries": (_I, [_P, _I64, _I64, _P, _P]),
+    "mhla_status_string": (ctypes.c_char_p, [_I]),
+    "mhla_last_error": (ctypes.c_char_p, []),
+    "mhla_version": (ctypes.c_char_p, []),
+}
+
+
+class MhlaError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path=LIB_PATH):
+    """Load libmhla.so once; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built: run `python -m token_level_head_amd.build` "
+                               "(or __graft_entry__.build()) first")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _check(status):
+    if status != MHLA_OK:
+        lib = load_library()
+        raise MhlaError(status, f"{lib.mhla_status_string(status).decode()}: {lib.mhla_last_error().decode()}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dims(q, W):
+    B, H, N, d = q.shape
+    return B, H, N, d, W.shape[0]
+
+
+def mhla_forward(q, k, v, W, out, causal=False, stream=None):
+    """bf16 q, k, v [B, H, N, d]; float32 W [M, M] and out [B, H, N, d]."""
+    B, H, N, d, M = _dims(q, W)
+    _check(load_library().mhla_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(W), _ptr(out), B, H, N, d, M,
+                                       int(bool(causal)), _stream(stream)))
+    return out
+
+
+def mhla_forward_f32(q, k, v, W, out, causal=False, stream=None):
+    """float32 q, k, v [B, H, N, d]; float32 W [M, M] and out."""
+    B, H, N, d, M = _dims(q, W)
+    _check(load_library().mhla_forward_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(W), _ptr(out), B, H, N, d, M,
+                                           int(bool(causal)), _stream(stream)))
+    return out
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return MHLA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return MHLA_DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def mhla_workspace_bytes(B, H, N, d, M, causal=False):
+    return int(load_library().mhla_workspace_bytes(B, H, N, d, M, int(bool(causal))))
+
+
+def mhla_summary_floats(d):
+    return int(load_library().mhla_summary_floats(d))
+
+
+def mhla_block_summaries(k, v, S, M, stream=None):
+    """Stage 1 into S (float32, M * B*H * (d*d + d) elements, packed layout)."""
+    B, H, N, d = k.shape
+    _check(load_library().mhla_block_summaries(_ptr(k), _ptr(v), _dtype_code(k), _ptr(S), B, H, N, d, M,
+                                               _stream(stream)))
+    return S
+
+
+def mhla_mix_summaries(S, W, St, BH, d, causal=False, precise=False, stream=None):
+    """Stage 2: St = W-mix of S (both packed, float32)."""
+    M = W.shape[0]
+    _check(load_library().mhla_mix_summaries(_ptr(S), _ptr(W), _ptr(St), BH, d, M, int(bool(causal)),
+                                             int(bool(precise)), _stream(stream)))
+    return St
+
+
+def mhla_output(q, k, v, St, W, out, causal=False, stream=None):
+    """Stage 3 into out (float32 [B, H, N, d])."""
+    B, H, N, d, M = _dims(q, W)
+    _check(load_library().mhla_output(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(St), _ptr(W), _ptr(out),
+                                      B, H, N, d, M, int(bool(causal)), _stream(stream)))
+    return out
+
+
+def mhla_unpack_summaries(packed, d):
+    """Host helper: packed float32 CPU tensor [..., d*d + d] -> (S [..., d, d], z [..., d])."""
+    packed = packed.contiguous()
+    L = d * d + d
+    count = packed.numel() // L
+    lead = packed.shape[:-1]
+    S = torch.empty((count, d, d), dtype=torch.float32)
+    z = torch.empty((count, d), dtype=torch.float32)
+    _check(load_library().mhla_unpack_summaries(_ptr(packed), count, d, _ptr(S), _ptr(z)))
+    return S.reshape(*lead, d, d), z.reshape(*lead, d)
+
+
+def mhla_status_string(status):
+    return load_library().mhla_status_string(status).decode()
+
+
+def mhla_last_error():
+    return load_library().mhla_last_error().decode()
+
+
+def mhla_version():
+    return load_library().mhla_version().decode()

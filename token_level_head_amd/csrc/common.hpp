@@ -1,0 +1,76 @@
+// common.hpp -- device helpers shared by the MHLA kernels (gfx950, wave64).
+//
+// MFMA operand layouts used throughout (lane l of a 64-lane wave, g = l / 16,
+// n = l % 16; verified on gfx950):
+//   v_mfma_f32_16x16x32_bf16 : A[m = n][k = 8g + e], B[k = 8g + e][col = n], e = 0..7
+//   v_mfma_f32_16x16x16_bf16 : A[m = n][k = 4g + e], B[k = 4g + e][col = n], e = 0..3
+//   result (both)            : C[row = 4g + i][col = n], i = 0..3
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mhla {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kEps = 1e-6f;  // denominator guard ("Linear Attention 笔记" §4/§5)
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+__device__ __forceinline__ __bf16 bits_to_bf16(uint16_t b) { return __builtin_bit_cast(__bf16, b); }
+
+__device__ __forceinline__ float bf16v_to_f32(__bf16 b) {
+    return __uint_as_float((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// phi(x) = ELU(x) + 1 ("Linear Attention 笔记" §2).  The fast exp is used where the
+// result is rounded to bfloat16 afterwards; phi_precise keeps float32 accuracy.
+__device__ __forceinline__ float phi_fast(float x) { return x > 0.f ? x + 1.f : __expf(x); }
+__device__ __forceinline__ float phi_precise(float x) { return x > 0.f ? x + 1.f : expf(x); }
+
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi), both round-to-nearest-even:
+// hi*y + lo*y carries about 16 significant bits of x into a bf16 product.
+struct bf16pair {
+    __bf16 hi, lo;
+};
+__device__ __forceinline__ bf16pair split_bf16(float x) {
+    const __bf16 hi = (__bf16)x;
+    return {hi, (__bf16)(x - bf16v_to_f32(hi))};
+}
+
+__device__ __forceinline__ f32x4 mfma32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma16(const bf16x4& a, const bf16x4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Sum over the four 16-lane groups (lanes n, n+16, n+32, n+48).
+__device__ __forceinline__ float sum_over_groups(float x) {
+    x += __shfl_xor(x, 16, 64);
+    x += __shfl_xor(x, 32, 64);
+    return x;
+}
+
+// Packed summary layout (shared by all three kernels).  For d = 16P the d x d part
+// of a summary vector is stored as P*P chunks of 64 lanes x 4 floats: chunk
+// (ia, ib) of lane l = 16g + n holds S[P*(4g + i) + ia][P*n + ib] for i = 0..3 at
+// float offset (ia*P + ib)*256 + l*4 + i.  This is exactly the result layout of
+// the summary MFMAs, and also exactly the B-operand set the output kernel needs
+// in the same lane, so neither kernel moves data across lanes.  z follows at
+// offset d*d in plain order.
+__host__ __device__ __forceinline__ int64_t packed_index(int P, int r, int c) {
+    const int ia = r % P, q = r / P, g = q / 4, i = q % 4;
+    const int n = c / P, ib = c % P;
+    return (int64_t)(ia * P + ib) * 256 + (int64_t)(16 * g + n) * 4 + i;
+}
+
+}  // namespace mhla

@@ -1,0 +1,27 @@
+// kernels.hpp -- internal launchers of the three MHLA stages (not part of the C ABI).
+// Each launcher enqueues its kernel(s) on `stream` and returns hipGetLastError();
+// the caller has already validated every size and pointer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mhla {
+
+constexpr int kDtypeBF16 = 0;
+constexpr int kDtypeF32 = 1;
+
+// Stage 1: S[b][pair][d*d + d] (packed) from K, V [pair][N][d].
+hipError_t launch_summaries(int dtype, const void* k, const void* v, float* S, int64_t BH, int64_t N,
+                            int D, int64_t M, hipStream_t stream);
+
+// Stage 2: St[i][col] = sum_b W[i,b] S[b][col] (causal: b < i), col < BH * (d*d + d).
+hipError_t launch_mix(const float* S, const float* W, float* St, int64_t BH, int D, int64_t M, bool causal,
+                      bool precise, hipStream_t stream);
+
+// Stage 3: out [pair][N][d] from Q and St (causal also K, V and W[i,i]).
+hipError_t launch_output(int dtype, const void* q, const void* k, const void* v, const float* St,
+                         const float* W, float* out, int64_t BH, int64_t N, int D, int64_t M, bool causal,
+                         hipStream_t stream);
+
+}  // namespace mhla

@@ -1,0 +1,264 @@
+// mhla_api.hip -- the C ABI declared in include/mhla.h.
+//
+// Host-side only: argument validation (before anything is enqueued), the
+// stream-ordered workspace for the two summary arrays, and the sequence
+// summaries -> mixing -> output on the caller's stream.  No call synchronises
+// the device.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "common.hpp"
+#include "kernels.hpp"
+#include "mhla.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return MHLA_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(MHLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_ptr(const void* p, const char* name) {
+    if (!p) return fail(MHLA_ERR_INVALID_ARG, "%s is NULL", name);
+    if (!aligned16(p)) return fail(MHLA_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+    return MHLA_OK;
+}
+
+// Sizes shared by every entry point.  Element counts must fit in int64 with
+// margin, and grid sizes in 32 bits.
+int check_sizes(int64_t B, int64_t H, int64_t N, int64_t d, int64_t M) {
+    if (B < 1 || H < 1 || N < 1 || d < 1 || M < 1)
+        return fail(MHLA_ERR_INVALID_ARG, "sizes must be >= 1 (B=%lld H=%lld N=%lld d=%lld M=%lld)",
+                    (long long)B, (long long)H, (long long)N, (long long)d, (long long)M);
+    if (N % M != 0)
+        return fail(MHLA_ERR_INVALID_ARG, "N=%lld is not a multiple of M=%lld", (long long)N, (long long)M);
+    if (d != 16 && d != 32 && d != 64)
+        return fail(MHLA_ERR_UNSUPPORTED, "d=%lld is not one of 16, 32, 64", (long long)d);
+    const int64_t lim = (int64_t)1 << 40;
+    if (B > lim / H || B * H > lim / N || B * H * N > lim / d)
+        return fail(MHLA_ERR_INVALID_ARG, "tensor too large");
+    if (M > 65536 || B * H * M > ((int64_t)1 << 29))
+        return fail(MHLA_ERR_UNSUPPORTED, "too many blocks (M=%lld, B*H*M=%lld)", (long long)M,
+                    (long long)(B * H * M));
+    return MHLA_OK;
+}
+
+bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + bn && b0 < a0 + an;
+}
+
+int64_t summary_floats(int64_t d) { return d * d + d; }
+
+// One memory pool per device for the forward-pass workspace.  Its release
+// threshold keeps freed blocks for reuse, so steady-state calls do not go back
+// to the driver.
+struct Pools {
+    std::mutex mu;
+    std::vector<hipMemPool_t> pools;
+    std::vector<bool> made;
+};
+Pools& pools() {
+    static Pools p;
+    return p;
+}
+
+hipError_t device_pool(hipMemPool_t* out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    Pools& P = pools();
+    std::lock_guard<std::mutex> lock(P.mu);
+    if ((int)P.pools.size() <= dev) {
+        P.pools.resize(dev + 1, nullptr);
+        P.made.resize(dev + 1, false);
+    }
+    if (!P.made[dev]) {
+        hipMemPoolProps props;
+        memset(&props, 0, sizeof props);
+        props.allocType = hipMemAllocationTypePinned;
+        props.handleTypes = hipMemHandleTypeNone;
+        props.location.type = hipMemLocationTypeDevice;
+        props.location.id = dev;
+        hipMemPool_t pool = nullptr;
+        e = hipMemPoolCreate(&pool, &props);
+        if (e != hipSuccess) return e;
+        uint64_t keep = UINT64_MAX;
+        e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+        if (e != hipSuccess) return e;
+        P.pools[dev] = pool;
+        P.made[dev] = true;
+    }
+    *out = P.pools[dev];
+    return hipSuccess;
+}
+
+int forward_impl(int dtype, const void* q, const void* k, const void* v, const float* W, float* out, int64_t B,
+                 int64_t H, int64_t N, int64_t d, int64_t M, int causal, mhla_stream_t stream_) {
+    int st = check_sizes(B, H, N, d, M);
+    if (st) return st;
+    if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
+        (st = check_ptr(W, "W")) || (st = check_ptr(out, "out")))
+        return st;
+    const size_t esz = dtype == mhla::kDtypeF32 ? 4 : 2;
+    const size_t in_bytes = (size_t)(B * H * N * d) * esz;
+    const size_t out_bytes = (size_t)(B * H * N * d) * 4;
+    if (overlaps(out, out_bytes, q, in_bytes) || overlaps(out, out_bytes, k, in_bytes) ||
+        overlaps(out, out_bytes, v, in_bytes) || overlaps(out, out_bytes, W, (size_t)(M * M) * 4))
+        return fail(MHLA_ERR_INVALID_ARG, "out overlaps an input");
+
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+    const int64_t BH = B * H;
+    const size_t arr = (size_t)(M * BH * summary_floats(d)) * sizeof(float);
+    hipMemPool_t pool = nullptr;
+    hipError_t e = device_pool(&pool);
+    if (e != hipSuccess) return hip_fail(e, "workspace pool");
+    void* ws = nullptr;
+    e = hipMallocFromPoolAsync(&ws, 2 * arr, pool, stream);
+    if (e != hipSuccess || !ws) {
+        (void)hipGetLastError();
+        return fail(MHLA_ERR_NO_MEMORY, "workspace of %zu bytes: %s", 2 * arr, hipGetErrorString(e));
+    }
+    float* S = static_cast<float*>(ws);
+    float* St = S + arr / sizeof(float);
+    const char* what = "summary kernel";
+    e = mhla::launch_summaries(dtype, k, v, S, BH, N, (int)d, M, stream);
+    if (e == hipSuccess) {
+        what = "mixing kernel";
+        e = mhla::launch_mix(S, W, St, BH, (int)d, M, causal != 0, dtype == mhla::kDtypeF32, stream);
+    }
+    if (e == hipSuccess) {
+        what = "output kernel";
+        e = mhla::launch_output(dtype, q, k, v, St, W, out, BH, N, (int)d, M, causal != 0, stream);
+    }
+    hipError_t fe = hipFreeAsync(ws, stream);
+    if (e != hipSuccess) return hip_fail(e, what);
+    if (fe != hipSuccess) return hip_fail(fe, "workspace release");
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int mhla_forward(const void* q, const void* k, const void* v, const float* W, float* out, int64_t B, int64_t H,
+                 int64_t N, int64_t d, int64_t M, int causal, mhla_stream_t stream) {
+    return forward_impl(mhla::kDtypeBF16, q, k, v, W, out, B, H, N, d, M, causal, stream);
+}
+
+int mhla_forward_f32(const float* q, const float* k, const float* v, const float* W, float* out, int64_t B,
+                     int64_t H, int64_t N, int64_t d, int64_t M, int causal, mhla_stream_t stream) {
+    return forward_impl(mhla::kDtypeF32, q, k, v, W, out, B, H, N, d, M, causal, stream);
+}
+
+int64_t mhla_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int64_t M, int causal) {
+    (void)causal;
+    if (check_sizes(B, H, N, d, M) != MHLA_OK) return -1;
+    return 2 * M * B * H * summary_floats(d) * (int64_t)sizeof(float);
+}
+
+int64_t mhla_summary_floats(int64_t d) { return d >= 1 ? summary_floats(d) : -1; }
+
+int mhla_block_summaries(const void* k, const void* v, int dtype, float* S, int64_t B, int64_t H, int64_t N,
+                         int64_t d, int64_t M, mhla_stream_t stream) {
+    int st = check_sizes(B, H, N, d, M);
+    if (st) return st;
+    if (dtype != MHLA_DTYPE_BF16 && dtype != MHLA_DTYPE_F32) return fail(MHLA_ERR_INVALID_ARG, "bad dtype %d", dtype);
+    if ((st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) || (st = check_ptr(S, "S"))) return st;
+    const size_t esz = dtype == MHLA_DTYPE_F32 ? 4 : 2;
+    const size_t in_bytes = (size_t)(B * H * N * d) * esz;
+    const size_t s_bytes = (size_t)(M * B * H * summary_floats(d)) * 4;
+    if (overlaps(S, s_bytes, k, in_bytes) || overlaps(S, s_bytes, v, in_bytes))
+        return fail(MHLA_ERR_INVALID_ARG, "S overlaps an input");
+    hipError_t e = mhla::launch_summaries(dtype, k, v, S, B * H, N, (int)d, M, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "summary kernel");
+    return ok();
+}
+
+int mhla_mix_summaries(const float* S, const float* W, float* St, int64_t BH, int64_t d, int64_t M, int causal,
+                       int precise, mhla_stream_t stream) {
+    int st = check_sizes(BH, 1, M, d, M);
+    if (st) return st;
+    if ((st = check_ptr(S, "S")) || (st = check_ptr(W, "W")) || (st = check_ptr(St, "St"))) return st;
+    const size_t s_bytes = (size_t)(M * BH * summary_floats(d)) * 4;
+    if (overlaps(St, s_bytes, S, s_bytes) || overlaps(St, s_bytes, W, (size_t)(M * M) * 4))
+        return fail(MHLA_ERR_INVALID_ARG, "St overlaps an input");
+    hipError_t e = mhla::launch_mix(S, W, St, BH, (int)d, M, causal != 0, precise != 0,
+                                    reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "mixing kernel");
+    return ok();
+}
+
+int mhla_output(const void* q, const void* k, const void* v, int dtype, const float* St, const float* W, float* out,
+                int64_t B, int64_t H, int64_t N, int64_t d, int64_t M, int causal, mhla_stream_t stream) {
+    int st = check_sizes(B, H, N, d, M);
+    if (st) return st;
+    if (dtype != MHLA_DTYPE_BF16 && dtype != MHLA_DTYPE_F32) return fail(MHLA_ERR_INVALID_ARG, "bad dtype %d", dtype);
+    if ((st = check_ptr(q, "q")) || (st = check_ptr(St, "St")) || (st = check_ptr(out, "out"))) return st;
+    if (causal && ((st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) || (st = check_ptr(W, "W")))) return st;
+    const size_t esz = dtype == MHLA_DTYPE_F32 ? 4 : 2;
+    const size_t in_bytes = (size_t)(B * H * N * d) * esz;
+    const size_t out_bytes = (size_t)(B * H * N * d) * 4;
+    const size_t s_bytes = (size_t)(M * B * H * summary_floats(d)) * 4;
+    if (overlaps(out, out_bytes, q, in_bytes) || overlaps(out, out_bytes, St, s_bytes) ||
+        (causal && (overlaps(out, out_bytes, k, in_bytes) || overlaps(out, out_bytes, v, in_bytes) ||
+                    overlaps(out, out_bytes, W, (size_t)(M * M) * 4))))
+        return fail(MHLA_ERR_INVALID_ARG, "out overlaps an input");
+    hipError_t e = mhla::launch_output(dtype, q, k, v, St, W, out, B * H, N, (int)d, M, causal != 0,
+                                       reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "output kernel");
+    return ok();
+}
+
+int mhla_unpack_summaries(const float* packed, int64_t count, int64_t d, float* S, float* z) {
+    if (!packed || !S || !z || count < 0) return fail(MHLA_ERR_INVALID_ARG, "bad unpack arguments");
+    if (d != 16 && d != 32 && d != 64) return fail(MHLA_ERR_UNSUPPORTED, "d=%lld is not one of 16, 32, 64", (long long)d);
+    const int P = (int)(d / 16);
+    const int64_t L = summary_floats(d);
+    for (int64_t u = 0; u < count; ++u) {
+        const float* src = packed + u * L;
+        for (int r = 0; r < d; ++r) {
+            for (int c = 0; c < d; ++c) S[(u * d + r) * d + c] = src[mhla::packed_index(P, r, c)];
+            z[u * d + r] = src[d * d + r];
+        }
+    }
+    return ok();
+}
+
+const char* mhla_status_string(int status) {
+    switch (status) {
+        case MHLA_OK: return "MHLA_OK";
+        case MHLA_ERR_INVALID_ARG: return "MHLA_ERR_INVALID_ARG";
+        case MHLA_ERR_UNSUPPORTED: return "MHLA_ERR_UNSUPPORTED";
+        case MHLA_ERR_NO_MEMORY: return "MHLA_ERR_NO_MEMORY";
+        case MHLA_ERR_HIP: return "MHLA_ERR_HIP";
+        default: return "MHLA_ERR_UNKNOWN";
+    }
+}
+
+const char* mhla_last_error(void) { return g_err; }
+
+const char* mhla_version(void) { return "mhla-gfx950 0.1.0"; }
+
+}  // extern "C"
