@@ -83,8 +83,10 @@ int mhla_forward_f32(const float* q, const float* k, const float* v, const float
                      int64_t B, int64_t H, int64_t N, int64_t d, int64_t M, int causal,
                      mhla_stream_t stream);
 
-/* Bytes of device workspace one forward call uses (the S and S~ summary
- * arrays, 2 * M * B*H * (d*d + d) floats); -1 for invalid sizes. */
+/* Bytes of device workspace one forward call uses: the S and S~ summary
+ * arrays (2 * M * B*H * (d*d + d) floats) plus the bf16 hi/lo split of W for
+ * the mixing kernel when 64 < M <= 1024 (4 * M * M bytes, rounded up to whole
+ * 64 x 32 MFMA tiles; none otherwise); -1 for invalid sizes. */
 int64_t mhla_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int64_t M, int causal);
 
 /* Floats in one packed summary vector: d*d + d (S_b followed by z_b). */
@@ -108,7 +110,8 @@ int mhla_block_summaries(const void* k, const void* v, int dtype, float* S,
  * b (causal == 0) or over b < i (causal != 0; row 0 becomes zero).  S and St
  * use the packed layout of mhla_block_summaries; `precise` selects float32
  * products (used by the float32 path) instead of the bfloat16 hi/lo split
- * (three bfloat16 products per term, float32 accumulation).
+ * (three bfloat16 products per term, float32 accumulation).  The split W
+ * fragments go to stream-ordered scratch from the library's memory pool.
  */
 int mhla_mix_summaries(const float* S, const float* W, float* St, int64_t BH, int64_t d, int64_t M,
                        int causal, int precise, mhla_stream_t stream);

@@ -97,6 +97,10 @@ SWEEP = [  # (B, H, N, d, M, causal, dtype)
     (2, 2, 768, 32, 3, True, "bf16"),   # C = 256, d = 32
     (1, 1, 300, 64, 300, False, "f32"),  # M > 256: several mixing row groups
     (1, 1, 600, 32, 300, True, "bf16"),
+    (1, 1, 2048, 16, 2048, False, "bf16"),  # mixing fragments beyond LDS: global-fragment kernel
+    (1, 1, 2048, 16, 2048, True, "bf16"),
+    (2, 1, 1024, 64, 32, False, "bf16"),  # M = 32 mixing variant
+    (2, 1, 1024, 64, 32, True, "bf16"),
 ]
 
 

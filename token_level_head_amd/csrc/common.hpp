@@ -53,6 +53,34 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x4& a, const bf16x4& b, const 
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// Masked load without a branch: the address falls back to `safe` (any valid,
+// suitably aligned element) when !ok and the bits are then cleared with an
+// integer mask.  A select on the loaded value would let the compiler sink the
+// load into an exec-masked branch with its own wait; this form keeps every load
+// unconditional, so a whole batch is issued before the first wait.
+template <int BYTES>
+struct MaskBits;
+template <>
+struct MaskBits<2> { typedef uint16_t type; };
+template <>
+struct MaskBits<4> { typedef uint32_t type; };
+template <>
+struct MaskBits<8> { typedef uint32_t type __attribute__((ext_vector_type(2))); };
+template <>
+struct MaskBits<16> { typedef uint32_t type __attribute__((ext_vector_type(4))); };
+
+// Keeps the scheduler from moving instructions across this point; placed after a
+// batch of loads so that the whole batch is issued before its consumers run
+// (otherwise the scheduler may serialise the loads to save registers).
+__device__ __forceinline__ void issue_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+template <typename T>
+__device__ __forceinline__ T load_or_zero(const T* p, bool ok, const T* safe) {
+    using U = typename MaskBits<sizeof(T)>::type;
+    const U v = __builtin_bit_cast(U, *(ok ? p : safe));
+    return __builtin_bit_cast(T, (U)(v & (U)(ok ? ~0u : 0u)));
+}
+
 // Sum over the four 16-lane groups (lanes n, n+16, n+32, n+48).
 __device__ __forceinline__ float sum_over_groups(float x) {
     x += __shfl_xor(x, 16, 64);

@@ -16,8 +16,11 @@ hipError_t launch_summaries(int dtype, const void* k, const void* v, float* S, i
                             int D, int64_t M, hipStream_t stream);
 
 // Stage 2: St[i][col] = sum_b W[i,b] S[b][col] (causal: b < i), col < BH * (d*d + d).
+// The bf16 path needs mix_fragment_bytes(M) bytes of device scratch at frag_ws
+// (16-byte aligned) for the split W; 0 bytes means it needs none.
+size_t mix_fragment_bytes(int64_t M);
 hipError_t launch_mix(const float* S, const float* W, float* St, int64_t BH, int D, int64_t M, bool causal,
-                      bool precise, hipStream_t stream);
+                      bool precise, void* frag_ws, hipStream_t stream);
 
 // Stage 3: out [pair][N][d] from Q and St (causal also K, V and W[i,i]).
 hipError_t launch_output(int dtype, const void* q, const void* k, const void* v, const float* St,

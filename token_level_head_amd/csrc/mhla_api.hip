@@ -114,6 +114,24 @@ hipError_t device_pool(hipMemPool_t* out) {
     return hipSuccess;
 }
 
+// Two summary arrays (S, St) followed by the mixing kernel's split-W fragments.
+size_t workspace_bytes(int64_t BH, int64_t d, int64_t M) {
+    return 2 * (size_t)(M * BH * summary_floats(d)) * sizeof(float) + mhla::mix_fragment_bytes(M);
+}
+
+int pool_alloc(void** ptr, size_t bytes, hipStream_t stream) {
+    hipMemPool_t pool = nullptr;
+    hipError_t e = device_pool(&pool);
+    if (e != hipSuccess) return hip_fail(e, "workspace pool");
+    *ptr = nullptr;
+    e = hipMallocFromPoolAsync(ptr, bytes, pool, stream);
+    if (e != hipSuccess || !*ptr) {
+        (void)hipGetLastError();
+        return fail(MHLA_ERR_NO_MEMORY, "workspace of %zu bytes: %s", bytes, hipGetErrorString(e));
+    }
+    return MHLA_OK;
+}
+
 int forward_impl(int dtype, const void* q, const void* k, const void* v, const float* W, float* out, int64_t B,
                  int64_t H, int64_t N, int64_t d, int64_t M, int causal, mhla_stream_t stream_) {
     int st = check_sizes(B, H, N, d, M);
@@ -131,22 +149,18 @@ int forward_impl(int dtype, const void* q, const void* k, const void* v, const f
     hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
     const int64_t BH = B * H;
     const size_t arr = (size_t)(M * BH * summary_floats(d)) * sizeof(float);
-    hipMemPool_t pool = nullptr;
-    hipError_t e = device_pool(&pool);
-    if (e != hipSuccess) return hip_fail(e, "workspace pool");
+    const size_t total = workspace_bytes(BH, d, M);
     void* ws = nullptr;
-    e = hipMallocFromPoolAsync(&ws, 2 * arr, pool, stream);
-    if (e != hipSuccess || !ws) {
-        (void)hipGetLastError();
-        return fail(MHLA_ERR_NO_MEMORY, "workspace of %zu bytes: %s", 2 * arr, hipGetErrorString(e));
-    }
+    int st2 = pool_alloc(&ws, total, stream);
+    if (st2) return st2;
     float* S = static_cast<float*>(ws);
     float* St = S + arr / sizeof(float);
+    void* frags = St + arr / sizeof(float);
     const char* what = "summary kernel";
-    e = mhla::launch_summaries(dtype, k, v, S, BH, N, (int)d, M, stream);
+    hipError_t e = mhla::launch_summaries(dtype, k, v, S, BH, N, (int)d, M, stream);
     if (e == hipSuccess) {
         what = "mixing kernel";
-        e = mhla::launch_mix(S, W, St, BH, (int)d, M, causal != 0, dtype == mhla::kDtypeF32, stream);
+        e = mhla::launch_mix(S, W, St, BH, (int)d, M, causal != 0, dtype == mhla::kDtypeF32, frags, stream);
     }
     if (e == hipSuccess) {
         what = "output kernel";
@@ -175,7 +189,7 @@ int mhla_forward_f32(const float* q, const float* k, const float* v, const float
 int64_t mhla_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int64_t M, int causal) {
     (void)causal;
     if (check_sizes(B, H, N, d, M) != MHLA_OK) return -1;
-    return 2 * M * B * H * summary_floats(d) * (int64_t)sizeof(float);
+    return (int64_t)workspace_bytes(B * H, d, M);
 }
 
 int64_t mhla_summary_floats(int64_t d) { return d >= 1 ? summary_floats(d) : -1; }
@@ -204,9 +218,14 @@ int mhla_mix_summaries(const float* S, const float* W, float* St, int64_t BH, in
     const size_t s_bytes = (size_t)(M * BH * summary_floats(d)) * 4;
     if (overlaps(St, s_bytes, S, s_bytes) || overlaps(St, s_bytes, W, (size_t)(M * M) * 4))
         return fail(MHLA_ERR_INVALID_ARG, "St overlaps an input");
-    hipError_t e = mhla::launch_mix(S, W, St, BH, (int)d, M, causal != 0, precise != 0,
-                                    reinterpret_cast<hipStream_t>(stream));
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    void* frags = nullptr;
+    const size_t fbytes = precise ? 0 : mhla::mix_fragment_bytes(M);
+    if (fbytes && (st = pool_alloc(&frags, fbytes, s))) return st;
+    hipError_t e = mhla::launch_mix(S, W, St, BH, (int)d, M, causal != 0, precise != 0, frags, s);
+    hipError_t fe = frags ? hipFreeAsync(frags, s) : hipSuccess;
     if (e != hipSuccess) return hip_fail(e, "mixing kernel");
+    if (fe != hipSuccess) return hip_fail(fe, "workspace release");
     return ok();
 }
 

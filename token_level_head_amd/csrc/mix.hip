@@ -5,18 +5,326 @@
 //
 // With the summaries stored block-major, S[b][pair][d*d + d], all pairs share
 // one GEMM:  St (M x ncols) = W (M x M) * S (M x ncols),  ncols = BH * (d*d + d).
-// The reduction depth is M (16 to 256) and ncols is large, so each wave owns a
-// 64-column strip and up to 64 output rows.  The S strip is read with 16-byte
-// loads (four columns per lane; MFMA j of the four uses column 4n + j), split
-// into bf16 hi + lo parts, and multiplied on 16x16x32 bf16 MFMA as
+// The reduction depth is M and ncols is large, so each wave owns a strip of
+// 16*J columns (J = 2 or 4 consecutive columns per lane, read with 8- or
+// 16-byte loads; MFMA j uses column J*n + j) and 16*RT output rows.  Both
+// operands are split into bf16 hi + lo parts and multiplied on bf16 MFMA as
 // W_hi S_hi + W_hi S_lo + W_lo S_hi with float32 accumulation (about 16
 // significant bits per operand, well inside the float32 summaries' needs).
-// The float32 path uses plain float32 FMAs instead.
+//
+// W is split into per-lane MFMA fragments (causal mask applied there).  For
+// M <= 64 each workgroup does that itself into LDS; for larger M a small kernel
+// does it once per call and the mixing waves read their fragments as coalesced
+// 16-byte loads that stay in L2, prefetched one k-chunk ahead together with S.
+// In both kernels the next k-chunk of S is loaded while the current one is
+// multiplied.  Workgroups that share a column strip (different row groups) are
+// numbered so that they land on the same XCD and share its L2.  The float32
+// path uses plain float32 FMAs instead.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace mhla {
 
+namespace {
+
+constexpr int64_t kMaxFragM = 1024;  // larger M uses the fragment-free fallback kernel
+
+template <int KSTEP>
+struct MixOps;
+template <>
+struct MixOps<32> {
+    typedef bf16x8 frag;
+    static constexpr int E = 8;
+    static __device__ __forceinline__ f32x4 mma(const frag& a, const frag& b, const f32x4& c) { return mfma32(a, b, c); }
+};
+template <>
+struct MixOps<16> {
+    typedef bf16x4 frag;
+    static constexpr int E = 4;
+    static __device__ __forceinline__ f32x4 mma(const frag& a, const frag& b, const f32x4& c) { return mfma16(a, b, c); }
+};
+
+}  // namespace
+
+size_t mix_fragment_bytes(int64_t M) {
+    if (M <= 64 || M > kMaxFragM) return 0;  // small M splits W in LDS; huge M in every wave
+    const int64_t RG = (M + 63) / 64, KC = (M + 31) / 32;  // RT = 4, 32-deep k-chunks
+    return (size_t)(RG * 4 * KC * 64 * 2) * 16;
+}
+
+// One thread per (row group, row tile, k-chunk, lane) slot: the hi and lo
+// fragments of W that lane feeds to the MFMA A operand.
+template <int KSTEP, int RT, bool CAUSAL>
+__global__ __launch_bounds__(256) void wsplit_kernel(const float* __restrict__ W,
+                                                     typename MixOps<KSTEP>::frag* __restrict__ frags, int M,
+                                                     int RG, int KC) {
+    using frag = typename MixOps<KSTEP>::frag;
+    constexpr int E = MixOps<KSTEP>::E;
+    const int64_t slot = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (slot >= (int64_t)RG * RT * KC * 64) return;
+    const int ln = (int)(slot & 63);
+    const int64_t t = slot >> 6;
+    const int kc = (int)(t % KC);
+    const int rrt = (int)(t / KC);  // rg * RT + rt
+    const int i = 16 * rrt + (ln & 15);
+    const int b0 = kc * KSTEP + E * (ln >> 4);
+    frag h, l;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int b = b0 + e;
+        const bool use = i < M && b < M && (!CAUSAL || b < i);
+        const bf16pair p = split_bf16(load_or_zero(W + (int64_t)i * M + b, use, W));
+        h[e] = p.hi;
+        l[e] = p.lo;
+    }
+    frags[2 * slot] = h;
+    frags[2 * slot + 1] = l;
+}
+
+template <int J>
+__device__ __forceinline__ void load_cols(const float* p, bool ok, const float* safe, float (&v)[J]) {
+    if constexpr (J == 4) {
+        const f32x4 x = load_or_zero(reinterpret_cast<const f32x4*>(p), ok, reinterpret_cast<const f32x4*>(safe));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = x[j];
+    } else {
+        const float2 x = load_or_zero(reinterpret_cast<const float2*>(p), ok, reinterpret_cast<const float2*>(safe));
+        v[0] = x.x;
+        v[1] = x.y;
+    }
+}
+
+template <int KSTEP, int RT, int J, bool CAUSAL>
+__global__ __launch_bounds__(256) void mix_frag_kernel(const float* __restrict__ S,
+                                                       const typename MixOps<KSTEP>::frag* __restrict__ frags,
+                                                       float* __restrict__ St, int64_t ncols, int M, int RG,
+                                                       int64_t ntiles, int KC) {
+    using Ops = MixOps<KSTEP>;
+    using frag = typename Ops::frag;
+    constexpr int E = Ops::E;
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, n = lane & 15;
+    // Workgroup b runs on XCD b % 8; the RG workgroups of one column group share that XCD.
+    const int64_t b = blockIdx.x;
+    const int rg = (int)((b >> 3) % RG);
+    const int64_t ctg = ((b >> 3) / RG) * 8 + (b & 7);
+    const int64_t ct = ctg * 4 + wave;
+    if (ct >= ntiles) return;  // whole wave; no barriers in this kernel
+
+    const int i0 = rg * 16 * RT;
+    const int imax = min(M, i0 + 16 * RT);
+    const int kend = CAUSAL ? imax - 1 : M;  // causal rows use b < i <= imax - 1
+    const int kcn = (kend + KSTEP - 1) / KSTEP;
+    const int64_t col = ct * 16 * J + J * n;
+    const bool colok = col < ncols;
+    const frag* fr = frags + (int64_t)rg * RT * KC * 64 * 2;
+
+    f32x4 acc[RT][J];
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int j = 0; j < J; ++j) acc[r][j] = zero4();
+
+    // One k-chunk of operands: S (E rows x J columns per lane) and this lane's W
+    // fragments for every row tile, loaded together so both are in flight at once.
+    struct Chunk {
+        float sv[E][J];
+        frag wh[RT], wl[RT];
+    };
+    auto load = [&](int kc, Chunk& ch) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int bb = kc * KSTEP + E * g + e;
+            load_cols<J>(S + (int64_t)bb * ncols + col, colok && bb < kend, S, ch.sv[e]);
+        }
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            if (i0 + 16 * r < imax) {  // uniform
+                const frag* f = fr + ((int64_t)(r * KC + kc) * 64 + lane) * 2;
+                ch.wh[r] = f[0];
+                ch.wl[r] = f[1];
+            }
+        }
+    };
+    auto compute = [&](const Chunk& ch) {
+        frag bh[J], bl[J];
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const bf16pair p = split_bf16(ch.sv[e][j]);
+                bh[j][e] = p.hi;
+                bl[j][e] = p.lo;
+            }
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            if (i0 + 16 * r < imax) {  // uniform
+#pragma unroll
+                for (int j = 0; j < J; ++j) {
+                    acc[r][j] = Ops::mma(ch.wh[r], bh[j], acc[r][j]);
+                    acc[r][j] = Ops::mma(ch.wh[r], bl[j], acc[r][j]);
+                    acc[r][j] = Ops::mma(ch.wl[r], bh[j], acc[r][j]);
+                }
+            }
+        }
+    };
+
+    {  // the next k-chunk is in flight while this one is multiplied
+        Chunk ca, cb;
+        if (kcn > 0) load(0, ca);
+        for (int kc = 0; kc < kcn; kc += 2) {
+            if (kc + 1 < kcn) load(kc + 1, cb);
+            issue_fence();
+            compute(ca);
+            if (kc + 1 < kcn) {
+                if (kc + 2 < kcn) load(kc + 2, ca);
+                issue_fence();
+                compute(cb);
+            }
+        }
+    }
+
+    if (!colok) return;
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = i0 + 16 * r + 4 * g + i;
+            if (row < imax) {
+                float* dst = St + (int64_t)row * ncols + col;
+                if constexpr (J == 4)
+                    *reinterpret_cast<f32x4*>(dst) = f32x4{acc[r][0][i], acc[r][1][i], acc[r][2][i], acc[r][3][i]};
+                else
+                    *reinterpret_cast<float2*>(dst) = make_float2(acc[r][0][i], acc[r][1][i]);
+            }
+        }
+    }
+}
+
+
+// Small M (<= 64): the workgroup splits its rows of W into MFMA fragments in LDS
+// itself (at most 16 KiB), which costs less than a separate launch.
+template <int KSTEP, int RT, int J, bool PIPE, bool CAUSAL>
+__global__ __launch_bounds__(256) void mix_lds_kernel(const float* __restrict__ S, const float* __restrict__ W,
+                                                      float* __restrict__ St, int64_t ncols, int M,
+                                                      int64_t ntiles, int kc_cap) {
+    using Ops = MixOps<KSTEP>;
+    using frag = typename Ops::frag;
+    constexpr int E = Ops::E;
+    extern __shared__ __align__(16) unsigned char smem[];
+    frag* wf = reinterpret_cast<frag*>(smem);
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, n = lane & 15;
+    const int imax = min(M, 16 * RT);        // a single row group
+    const int kend = CAUSAL ? imax - 1 : M;  // causal rows use b < i <= imax - 1
+    const int kcn = (kend + KSTEP - 1) / KSTEP;
+
+    for (int slot = threadIdx.x; slot < RT * kcn * 64; slot += blockDim.x) {
+        const int ln = slot & 63, t = slot >> 6;
+        const int kc = t % kcn, rt = t / kcn;
+        const int i = 16 * rt + (ln & 15);
+        const int b0 = kc * KSTEP + E * (ln >> 4);
+        frag h, l;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int b = b0 + e;
+            const bool use = i < M && b < kend && (!CAUSAL || b < i);
+            const bf16pair p = split_bf16(load_or_zero(W + (int64_t)i * M + b, use, W));
+            h[e] = p.hi;
+            l[e] = p.lo;
+        }
+        wf[((rt * kc_cap + kc) * 64 + ln) * 2] = h;
+        wf[((rt * kc_cap + kc) * 64 + ln) * 2 + 1] = l;
+    }
+    __syncthreads();
+
+    const int64_t ct = (int64_t)blockIdx.x * 4 + wave;
+    if (ct >= ntiles) return;  // no barriers below
+    const int64_t col = ct * 16 * J + J * n;
+    const bool colok = col < ncols;
+
+    f32x4 acc[RT][J];
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int j = 0; j < J; ++j) acc[r][j] = zero4();
+
+    auto load = [&](int kc, float (&sv)[E][J]) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int b = kc * KSTEP + E * g + e;
+            load_cols<J>(S + (int64_t)b * ncols + col, colok && b < kend, S, sv[e]);
+        }
+    };
+    auto compute = [&](int kc, const float (&sv)[E][J]) {
+        frag bh[J], bl[J];
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const bf16pair p = split_bf16(sv[e][j]);
+                bh[j][e] = p.hi;
+                bl[j][e] = p.lo;
+            }
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            if (16 * r < imax) {  // uniform
+                const frag ah = wf[((r * kc_cap + kc) * 64 + lane) * 2];
+                const frag al = wf[((r * kc_cap + kc) * 64 + lane) * 2 + 1];
+#pragma unroll
+                for (int j = 0; j < J; ++j) {
+                    acc[r][j] = Ops::mma(ah, bh[j], acc[r][j]);
+                    acc[r][j] = Ops::mma(ah, bl[j], acc[r][j]);
+                    acc[r][j] = Ops::mma(al, bh[j], acc[r][j]);
+                }
+            }
+        }
+    };
+
+    if constexpr (PIPE) {  // next k-chunk in flight while this one is multiplied
+        float sa[E][J], sb[E][J];
+        if (kcn > 0) load(0, sa);
+        for (int kc = 0; kc < kcn; kc += 2) {
+            if (kc + 1 < kcn) load(kc + 1, sb);
+            issue_fence();
+            compute(kc, sa);
+            if (kc + 1 < kcn) {
+                if (kc + 2 < kcn) load(kc + 2, sa);
+                issue_fence();
+                compute(kc + 1, sb);
+            }
+        }
+    } else {
+        for (int kc = 0; kc < kcn; ++kc) {
+            float sa[E][J];
+            load(kc, sa);
+            issue_fence();
+            compute(kc, sa);
+        }
+    }
+
+    if (!colok) return;
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * r + 4 * g + i;
+            if (row < imax) {
+                float* dst = St + (int64_t)row * ncols + col;
+                if constexpr (J == 4)
+                    *reinterpret_cast<f32x4*>(dst) = f32x4{acc[r][0][i], acc[r][1][i], acc[r][2][i], acc[r][3][i]};
+                else
+                    *reinterpret_cast<float2*>(dst) = make_float2(acc[r][0][i], acc[r][1][i]);
+            }
+        }
+    }
+}
+
+// Fallback for M > kMaxFragM: each wave splits its W fragments itself.
 template <bool CAUSAL>
 __global__ __launch_bounds__(256) void mix_split_kernel(const float* __restrict__ S, const float* __restrict__ W,
                                                         float* __restrict__ St, int64_t ncols, int M, int RG,
@@ -31,8 +339,8 @@ __global__ __launch_bounds__(256) void mix_split_kernel(const float* __restrict_
     const int64_t col = ct * 64 + 4 * n;
     const bool colok = col < ncols;
     const int i0 = rg * 64;
-    const int imax = min(M, i0 + 64);        // rows [i0, imax)
-    const int kend = CAUSAL ? imax - 1 : M;  // causal rows use b < i <= imax - 1
+    const int imax = min(M, i0 + 64);
+    const int kend = CAUSAL ? imax - 1 : M;
 
     f32x4 acc[4][4];
 #pragma unroll
@@ -45,7 +353,8 @@ __global__ __launch_bounds__(256) void mix_split_kernel(const float* __restrict_
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int b = kb + 8 * g + e;
-            sv[e] = (b < kend && colok) ? *reinterpret_cast<const f32x4*>(S + (int64_t)b * ncols + col) : zero4();
+            sv[e] = load_or_zero(reinterpret_cast<const f32x4*>(S + (int64_t)b * ncols + col), b < kend && colok,
+                                 reinterpret_cast<const f32x4*>(S));
         }
         bf16x8 bh[4], bl[4];
 #pragma unroll
@@ -66,7 +375,7 @@ __global__ __launch_bounds__(256) void mix_split_kernel(const float* __restrict_
                 for (int e = 0; e < 8; ++e) {
                     const int b = kb + 8 * g + e;
                     const bool use = i < M && b < kend && (!CAUSAL || b < i);
-                    const bf16pair h = split_bf16(use ? W[(int64_t)i * M + b] : 0.f);
+                    const bf16pair h = split_bf16(load_or_zero(W + (int64_t)i * M + b, use, W));
                     ah[e] = h.hi;
                     al[e] = h.lo;
                 }
@@ -111,12 +420,64 @@ __global__ __launch_bounds__(256) void mix_f32_kernel(const float* __restrict__ 
 }
 
 hipError_t launch_mix(const float* S, const float* W, float* St, int64_t BH, int D, int64_t M, bool causal,
-                      bool precise, hipStream_t stream) {
+                      bool precise, void* frag_ws, hipStream_t stream) {
     const int64_t ncols = BH * (int64_t)(D * D + D);
     if (precise) {
         const int64_t threads = ncols / 4;
         mix_f32_kernel<<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream>>>(S, W, St, ncols, (int)M,
                                                                                         causal ? 1 : 0);
+        return hipGetLastError();
+    }
+    using I16 = std::integral_constant<int, 16>;
+    using I32 = std::integral_constant<int, 32>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I4 = std::integral_constant<int, 4>;
+    if (M <= 64) {
+        auto run = [&](auto kstep_c, auto rt_c, auto j_c) {
+            constexpr int KSTEP = decltype(kstep_c)::value, RT = decltype(rt_c)::value, J = decltype(j_c)::value;
+            constexpr bool PIPE = KSTEP == 32;  // the 16-deep variant serves M <= 16: a single k-chunk
+            const int KC = (int)((M + KSTEP - 1) / KSTEP);
+            const size_t lds = (size_t)RT * KC * 64 * 2 * (KSTEP == 32 ? 16 : 8);
+            const int64_t ntiles = (ncols + 16 * J - 1) / (16 * J);
+            const dim3 grid((unsigned)((ntiles + 3) / 4));
+            if (causal)
+                mix_lds_kernel<KSTEP, RT, J, PIPE, true><<<grid, dim3(256), lds, stream>>>(S, W, St, ncols, (int)M,
+                                                                                          ntiles, KC);
+            else
+                mix_lds_kernel<KSTEP, RT, J, PIPE, false><<<grid, dim3(256), lds, stream>>>(S, W, St, ncols, (int)M,
+                                                                                           ntiles, KC);
+        };
+        if (M <= 16)
+            run(I16{}, I1{}, I4{});
+        else if (M <= 32)
+            run(I32{}, I2{}, I4{});
+        else
+            run(I32{}, I4{}, I4{});
+        return hipGetLastError();
+    }
+    if (M <= kMaxFragM) {
+        if (!frag_ws) return hipErrorInvalidValue;
+        constexpr int KSTEP = 32, RT = 4, J = 2;
+        using frag = typename MixOps<KSTEP>::frag;
+        frag* frags = static_cast<frag*>(frag_ws);
+        const int KC = (int)((M + KSTEP - 1) / KSTEP);
+        const int RG = (int)((M + 16 * RT - 1) / (16 * RT));
+        const int64_t slots = (int64_t)RG * RT * KC * 64;
+        const dim3 sgrid((unsigned)((slots + 255) / 256));
+        if (causal)
+            wsplit_kernel<KSTEP, RT, true><<<sgrid, dim3(256), 0, stream>>>(W, frags, (int)M, RG, KC);
+        else
+            wsplit_kernel<KSTEP, RT, false><<<sgrid, dim3(256), 0, stream>>>(W, frags, (int)M, RG, KC);
+        const int64_t ntiles = (ncols + 16 * J - 1) / (16 * J);
+        const int64_t nctg = (ntiles + 3) / 4;
+        const dim3 grid((unsigned)(((nctg + 7) / 8) * 8 * RG));
+        if (causal)
+            mix_frag_kernel<KSTEP, RT, J, true><<<grid, dim3(256), 0, stream>>>(S, frags, St, ncols, (int)M, RG,
+                                                                                ntiles, KC);
+        else
+            mix_frag_kernel<KSTEP, RT, J, false><<<grid, dim3(256), 0, stream>>>(S, frags, St, ncols, (int)M, RG,
+                                                                                 ntiles, KC);
         return hipGetLastError();
     }
     const int64_t ntiles = (ncols + 63) / 64;

@@ -29,15 +29,15 @@ namespace mhla {
 
 // 4P consecutive bf16 values starting at p (P = d/16): 8, 16 or 32 bytes.
 template <int P>
-__device__ __forceinline__ void load_group(const uint16_t* p, bool ok, uint16_t (&out)[4 * P]) {
+__device__ __forceinline__ void load_group(const uint16_t* p, bool ok, const uint16_t* safe, uint16_t (&out)[4 * P]) {
     if constexpr (P == 1) {
-        uint2 x = ok ? *reinterpret_cast<const uint2*>(p) : make_uint2(0u, 0u);
+        const uint2 x = load_or_zero(reinterpret_cast<const uint2*>(p), ok, reinterpret_cast<const uint2*>(safe));
         out[0] = (uint16_t)x.x; out[1] = (uint16_t)(x.x >> 16);
         out[2] = (uint16_t)x.y; out[3] = (uint16_t)(x.y >> 16);
     } else {
 #pragma unroll
         for (int h = 0; h < P / 2; ++h) {
-            uint4 x = ok ? *reinterpret_cast<const uint4*>(p + 8 * h) : make_uint4(0u, 0u, 0u, 0u);
+            const uint4 x = load_or_zero(reinterpret_cast<const uint4*>(p + 8 * h), ok, reinterpret_cast<const uint4*>(safe));
             const uint32_t w[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
@@ -50,16 +50,16 @@ __device__ __forceinline__ void load_group(const uint16_t* p, bool ok, uint16_t 
 
 // P consecutive bf16 values (2P bytes).
 template <int P>
-__device__ __forceinline__ void load_feat3(const uint16_t* p, bool ok, uint16_t (&out)[P]) {
+__device__ __forceinline__ void load_feat3(const uint16_t* p, bool ok, const uint16_t* safe, uint16_t (&out)[P]) {
     if constexpr (P == 4) {
-        uint2 x = ok ? *reinterpret_cast<const uint2*>(p) : make_uint2(0u, 0u);
+        const uint2 x = load_or_zero(reinterpret_cast<const uint2*>(p), ok, reinterpret_cast<const uint2*>(safe));
         out[0] = (uint16_t)x.x; out[1] = (uint16_t)(x.x >> 16);
         out[2] = (uint16_t)x.y; out[3] = (uint16_t)(x.y >> 16);
     } else if constexpr (P == 2) {
-        uint32_t x = ok ? *reinterpret_cast<const uint32_t*>(p) : 0u;
+        const uint32_t x = load_or_zero(reinterpret_cast<const uint32_t*>(p), ok, reinterpret_cast<const uint32_t*>(safe));
         out[0] = (uint16_t)x; out[1] = (uint16_t)(x >> 16);
     } else {
-        out[0] = ok ? *p : (uint16_t)0;
+        out[0] = load_or_zero(p, ok, safe);
     }
 }
 
@@ -144,7 +144,8 @@ __global__ __launch_bounds__(256) void output_bf16_kernel(const uint16_t* __rest
         const int64_t tq = t0 + n;
         const bool qok = tq < bend;
         uint16_t qr[FL];
-        load_group<P>(Qp + tq * D + FL * g, qok, qr);
+        load_group<P>(Qp + tq * D + FL * g, qok, Q, qr);
+        issue_fence();
         bf16x8 aq[KS];
         float qf[FL];
 #pragma unroll
@@ -193,7 +194,7 @@ __global__ __launch_bounds__(256) void output_bf16_kernel(const uint16_t* __rest
             const int64_t tk = t0 + n;
             const bool kok = tk < bend;
             uint16_t kr[FL];
-            load_group<P>(Kp + tk * D + FL * g, kok, kr);
+            load_group<P>(Kp + tk * D + FL * g, kok, K, kr);
             bf16x8 ak[KS];
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
@@ -210,8 +211,8 @@ __global__ __launch_bounds__(256) void output_bf16_kernel(const uint16_t* __rest
                 const int64_t tok = t0 + 4 * g + e;
                 const bool ok = tok < bend;
                 uint16_t k16[P], v16[P];
-                load_feat3<P>(Kp + tok * D + P * n, ok, k16);
-                load_feat3<P>(Vp + tok * D + P * n, ok, v16);
+                load_feat3<P>(Kp + tok * D + P * n, ok, K, k16);
+                load_feat3<P>(Vp + tok * D + P * n, ok, V, v16);
 #pragma unroll
                 for (int f = 0; f < P; ++f) {
                     ak16[f][e] = (__bf16)(ok ? phi_fast(bf16_to_f32(k16[f])) : 0.f);

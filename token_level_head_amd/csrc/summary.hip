@@ -22,16 +22,16 @@
 namespace mhla {
 
 template <int P>
-__device__ __forceinline__ void load_feat(const uint16_t* p, bool ok, uint16_t (&out)[P]) {
+__device__ __forceinline__ void load_feat(const uint16_t* p, bool ok, const uint16_t* safe, uint16_t (&out)[P]) {
     if constexpr (P == 4) {
-        uint2 x = ok ? *reinterpret_cast<const uint2*>(p) : make_uint2(0u, 0u);
+        const uint2 x = load_or_zero(reinterpret_cast<const uint2*>(p), ok, reinterpret_cast<const uint2*>(safe));
         out[0] = (uint16_t)x.x; out[1] = (uint16_t)(x.x >> 16);
         out[2] = (uint16_t)x.y; out[3] = (uint16_t)(x.y >> 16);
     } else if constexpr (P == 2) {
-        uint32_t x = ok ? *reinterpret_cast<const uint32_t*>(p) : 0u;
+        const uint32_t x = load_or_zero(reinterpret_cast<const uint32_t*>(p), ok, reinterpret_cast<const uint32_t*>(safe));
         out[0] = (uint16_t)x; out[1] = (uint16_t)(x >> 16);
     } else {
-        out[0] = ok ? *p : (uint16_t)0;
+        out[0] = load_or_zero(p, ok, safe);
     }
 }
 
@@ -76,9 +76,10 @@ __global__ __launch_bounds__(256) void summaries_bf16_kernel(const uint16_t* __r
             for (int e = 0; e < 8; ++e) {
                 const int64_t tok = t + 8 * g + e;
                 const bool ok = tok < t_end;
-                load_feat<P>(Kp + tok * D, ok, kr[e]);
-                load_feat<P>(Vp + tok * D, ok, vr[e]);
+                load_feat<P>(Kp + tok * D, ok, K, kr[e]);
+                load_feat<P>(Vp + tok * D, ok, V, vr[e]);
             }
+            issue_fence();
             bf16x8 a[P], b[P];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {

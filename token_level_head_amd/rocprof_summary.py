@@ -1,0 +1,105 @@
+"""Summarise rocprofv3 result databases into the short text files kept in profiles/.
+
+    # kernel durations (from a --kernel-trace --stats run)
+    python -m token_level_head_amd.rocprof_summary trace RUN_results.db --cmd "<rocprofv3 command>" \
+        --workload dit_s2_256 > profiles/kernels_dit_s2_256.md
+
+    # HBM traffic (from one --pmc FETCH_SIZE run and one --pmc WRITE_SIZE run)
+    python -m token_level_head_amd.rocprof_summary counters FETCH_results.db WRITE_results.db \
+        --workload dit_s2_256 --cmd-fetch "<command>" --cmd-write "<command>" \
+        --out profiles/counters_dit_s2_256.json
+
+FETCH_SIZE and WRITE_SIZE are scaled by what the same counter reports for the
+plain 1 GiB device copy that ``bench.py --copy-calibration`` runs: bytes =
+counter_KiB * (copy bytes / copy counter KiB).  The counters file records the
+digest of the kernel sources it measured; ``bench.py`` reports the traffic only
+while that digest matches the current sources.
+"""
+import argparse
+import json
+import sqlite3
+import sys
+
+from .build import source_digest
+
+COPY_BYTES = 1 << 30  # bench.py --copy-calibration copies 2^28 float32 values
+
+
+def short_name(name):
+    base = name.split("(")[0].replace("void ", "")
+    return base.replace("mhla::", "")
+
+
+def trace_rows(db):
+    c = sqlite3.connect(db)
+    rows = c.execute("select name, count(*), avg(duration), min(duration), max(duration), sum(duration) "
+                     "from kernels group by name order by sum(duration) desc").fetchall()
+    return [dict(name=r[0], calls=r[1], avg_ns=r[2], min_ns=r[3], max_ns=r[4], total_ns=r[5]) for r in rows]
+
+
+def cmd_trace(args):
+    rows = trace_rows(args.db)
+    total = sum(r["total_ns"] for r in rows) or 1
+    print(f"# rocprofv3 kernel trace: {args.workload}\n")
+    print(f"Command: `{args.cmd}`\n")
+    print(f"Kernel sources digest: `{source_digest()}`\n")
+    print("| kernel | calls | avg us | min us | max us | % of GPU time |")
+    print("|---|---|---|---|---|---|")
+    for r in rows:
+        print(f"| `{short_name(r['name'])}` | {r['calls']} | {r['avg_ns'] / 1e3:.2f} | {r['min_ns'] / 1e3:.2f} | "
+              f"{r['max_ns'] / 1e3:.2f} | {100 * r['total_ns'] / total:.1f} |")
+
+
+def counter_means(db, counter):
+    c = sqlite3.connect(db)
+    rows = c.execute("select kernel_name, count(*), avg(value), max(value) from counters_collection "
+                     "where counter_name = ? group by kernel_name", (counter,)).fetchall()
+    return {r[0]: {"dispatches": r[1], "avg_kib": r[2], "max_kib": r[3]} for r in rows}
+
+
+def cmd_counters(args):
+    fetch = counter_means(args.fetch_db, "FETCH_SIZE")
+    write = counter_means(args.write_db, "WRITE_SIZE")
+    copy_name = next(n for n in fetch if "copyBuffer" in n or "copy" in n.lower())
+    f_scale = COPY_BYTES / (fetch[copy_name]["max_kib"])
+    w_scale = COPY_BYTES / (write[copy_name]["max_kib"])
+    kernels = {}
+    for name in sorted(set(fetch) & set(write)):
+        if not name.startswith("void mhla::") and "mhla::" not in name:
+            continue
+        fb = fetch[name]["avg_kib"] * f_scale
+        wb = write[name]["avg_kib"] * w_scale
+        kernels[short_name(name)] = {"fetch_kib": fetch[name]["avg_kib"], "write_kib": write[name]["avg_kib"],
+                                     "fetch_bytes": fb, "write_bytes": wb, "traffic_bytes": fb + wb,
+                                     "dispatches": fetch[name]["dispatches"]}
+    out = {"workload": args.workload, "source_digest": source_digest(),
+           "copy_reference": {"kernel": copy_name, "bytes": COPY_BYTES, "fetch_kib": fetch[copy_name]["max_kib"],
+                              "write_kib": write[copy_name]["max_kib"], "fetch_scale": f_scale,
+                              "write_scale": w_scale},
+           "commands": {"fetch": args.cmd_fetch, "write": args.cmd_write}, "kernels": kernels}
+    with open(args.out, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="what", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("db")
+    t.add_argument("--cmd", required=True)
+    t.add_argument("--workload", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("fetch_db")
+    c.add_argument("write_db")
+    c.add_argument("--workload", required=True)
+    c.add_argument("--cmd-fetch", required=True)
+    c.add_argument("--cmd-write", required=True)
+    c.add_argument("--out", required=True)
+    args = ap.parse_args(argv)
+    {"trace": cmd_trace, "counters": cmd_counters}[args.what](args)
+
+
+if __name__ == "__main__":
+    sys.exit(main())
