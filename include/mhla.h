@@ -27,7 +27,8 @@
  *     query block i.  One W is shared by every batch element and head.
  *   - Blocks are contiguous: block b holds tokens [b*C, (b+1)*C), C = N / M.
  *     Spatial (2D/3D) blocks are expressed by storing tokens block-major.
- *   - Supported sizes: B, H, N, M >= 1, N % M == 0, d in {16, 32, 64}.
+ *   - Supported sizes: B, H, N, M >= 1, N % M == 0, d in {16, 32, 64},
+ *     N*d <= 2^30, M <= 65536 and B*H*M <= 2^29 (else MHLA_ERR_UNSUPPORTED).
  *     bf16 inputs are IEEE bfloat16 bit patterns (uint16 per element).
  *   - Pointers must be 16-byte aligned; `out` must not overlap any input.
  *   - Every call validates its arguments on the host before enqueueing

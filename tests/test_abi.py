@@ -67,6 +67,7 @@ def test_forward_validation(mhla_lib, fn):
     assert call(d=24) == mh.MHLA_ERR_UNSUPPORTED
     assert call(d=128) == mh.MHLA_ERR_UNSUPPORTED
     assert call(B=1 << 30, H=1 << 30) == mh.MHLA_ERR_INVALID_ARG
+    assert call(N=1 << 25, d=64, M=1) == mh.MHLA_ERR_UNSUPPORTED  # N*d beyond 32-bit pair offsets
     # out overlapping q
     assert call(ptrs=[FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE + 64]) == mh.MHLA_ERR_INVALID_ARG
     assert "overlap" in mh.mhla_last_error()

@@ -27,10 +27,15 @@ __device__ __forceinline__ float bf16v_to_f32(__bf16 b) {
     return __uint_as_float((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
-// phi(x) = ELU(x) + 1 ("Linear Attention 笔记" §2).  The fast exp is used where the
-// result is rounded to bfloat16 afterwards; phi_precise keeps float32 accuracy.
-__device__ __forceinline__ float phi_fast(float x) { return x > 0.f ? x + 1.f : __expf(x); }
-__device__ __forceinline__ float phi_precise(float x) { return x > 0.f ? x + 1.f : expf(x); }
+// phi(x) = ELU(x) + 1 ("Linear Attention 笔记" §2), written as max(x, 0) + exp(min(x, 0)):
+// the same value on both branches (exp(0) = 1) without a compare and select.  The
+// fast exp is used where the result is rounded to bfloat16 afterwards;
+// phi_precise keeps float32 accuracy.
+__device__ __forceinline__ float phi_fast(float x) { return fmaxf(x, 0.f) + __expf(fminf(x, 0.f)); }
+__device__ __forceinline__ float phi_precise(float x) { return fmaxf(x, 0.f) + expf(fminf(x, 0.f)); }
+
+// Hardware reciprocal (about 1 ulp).  Every denominator here is >= 1e-6 and finite.
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
 // x = hi + lo with hi = bf16(x) and lo = bf16(x - hi), both round-to-nearest-even:
 // hi*y + lo*y carries about 16 significant bits of x into a bf16 product.

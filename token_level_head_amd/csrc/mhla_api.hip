@@ -58,6 +58,8 @@ int check_sizes(int64_t B, int64_t H, int64_t N, int64_t d, int64_t M) {
     const int64_t lim = (int64_t)1 << 40;
     if (B > lim / H || B * H > lim / N || B * H * N > lim / d)
         return fail(MHLA_ERR_INVALID_ARG, "tensor too large");
+    if (N * d > ((int64_t)1 << 30))  // kernels index inside one (batch, head) pair with 32-bit offsets
+        return fail(MHLA_ERR_UNSUPPORTED, "N*d=%lld exceeds 2^30", (long long)(N * d));
     if (M > 65536 || B * H * M > ((int64_t)1 << 29))
         return fail(MHLA_ERR_UNSUPPORTED, "too many blocks (M=%lld, B*H*M=%lld)", (long long)M,
                     (long long)(B * H * M));

@@ -6,22 +6,17 @@
 // W[i,i] * (phi(q_t)^T P_t, phi(q_t)^T p_t) with P_t the summary of block i's
 // tokens up to and including t.
 //
-// bf16 path, one wave per 16-token tile sequence of one block:
+// Non-causal, one wave per run of up to four 16-token tiles of one block:
 //   * phi(Q) rows are the MFMA A operand (lane n = token, lane group g = a run of
 //     4P features, read as one or two 16-byte loads);
-//   * S~_i enters as the B operand, split into bf16 hi + lo parts (two MFMAs),
-//     and it is read straight from the packed layout with 16-byte loads: the
+//   * S~_i enters as the B operand, split once per wave into bf16 hi + lo parts
+//     (two MFMAs), read straight from the packed layout with 16-byte loads: the
 //     features a lane's group needs are exactly the ones the summary kernel left
 //     in that lane;
 //   * the denominator phi(q).z~ is a per-lane dot product plus a reduction over
 //     the four lane groups with wavefront shuffles;
-//   * one float32 divide per output, written once with 16-byte stores.
-// Causal: the wave walks its block's tiles in order and keeps the running block
-// summary P (and p) in MFMA accumulators in the packed layout, so the operand
-// S~_i + W[i,i] P is formed lane-locally each tile.  Inside a tile the strictly
-// causal part is the masked 16 x 16 product (phi(Q) phi(K)^T) V (chunkwise form
-// of App. C), with A kept as bf16 hi + lo and its row sums taken from the same
-// rounded values that multiply V.
+//   * one reciprocal per row, written once with 16-byte stores.
+// Causal: see output_causal_kernel below.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -48,21 +43,6 @@ __device__ __forceinline__ void load_group(const uint16_t* p, bool ok, const uin
     }
 }
 
-// P consecutive bf16 values (2P bytes).
-template <int P>
-__device__ __forceinline__ void load_feat3(const uint16_t* p, bool ok, const uint16_t* safe, uint16_t (&out)[P]) {
-    if constexpr (P == 4) {
-        const uint2 x = load_or_zero(reinterpret_cast<const uint2*>(p), ok, reinterpret_cast<const uint2*>(safe));
-        out[0] = (uint16_t)x.x; out[1] = (uint16_t)(x.x >> 16);
-        out[2] = (uint16_t)x.y; out[3] = (uint16_t)(x.y >> 16);
-    } else if constexpr (P == 2) {
-        const uint32_t x = load_or_zero(reinterpret_cast<const uint32_t*>(p), ok, reinterpret_cast<const uint32_t*>(safe));
-        out[0] = (uint16_t)x; out[1] = (uint16_t)(x >> 16);
-    } else {
-        out[0] = load_or_zero(p, ok, safe);
-    }
-}
-
 // B operands from packed chunks: slot e of k-step ks is group-local feature
 // fl = 8*ks + e, held in chunk (fl % P, jb) at row fl / P (zero past 4P).
 template <int P, int KS>
@@ -81,13 +61,36 @@ __device__ __forceinline__ void build_b(const f32x4 (&ch)[P * P], bf16x8 (&bh)[K
             }
 }
 
-template <int D, bool CAUSAL>
+// Lane (g, n) holds acc[jj][i] = numerator of row t0 + 4g + i at column
+// P*n + jb0 + jj (jj < PJ); `den` is the guarded denominator of row t0 + n (any
+// lane group).  PJ consecutive floats are stored per row.
+template <int P, int PJ>
+__device__ __forceinline__ void store_rows(float* Yp, int t0, int bend, int g, int n, int jb0,
+                                           const f32x4 (&acc)[PJ], float den) {
+    constexpr int D = 16 * P;
+    const float rden = fast_rcp(den);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float r = __shfl(rden, 4 * g + i, 64);
+        const int row = t0 + 4 * g + i;
+        if (row < bend) {
+            float* dst = Yp + row * D + P * n + jb0;
+            if constexpr (PJ == 4) {
+                *reinterpret_cast<f32x4*>(dst) = f32x4{acc[0][i] * r, acc[1][i] * r, acc[2][i] * r, acc[3][i] * r};
+            } else if constexpr (PJ == 2) {
+                *reinterpret_cast<float2*>(dst) = make_float2(acc[0][i] * r, acc[1][i] * r);
+            } else {
+                dst[0] = acc[0][i] * r;
+            }
+        }
+    }
+}
+
+// Offsets inside one (batch, head) pair fit in 32 bits (the API limits N*d).
+template <int D>
 __global__ __launch_bounds__(256) void output_bf16_kernel(const uint16_t* __restrict__ Q,
-                                                          const uint16_t* __restrict__ K,
-                                                          const uint16_t* __restrict__ V,
-                                                          const float* __restrict__ St,
-                                                          const float* __restrict__ W, float* __restrict__ Y,
-                                                          int64_t BH, int64_t N, int64_t M, int tpw, int wpu) {
+                                                          const float* __restrict__ St, float* __restrict__ Y,
+                                                          int64_t BH, int N, int64_t M, int tpw, int wpu) {
     constexpr int P = D / 16;
     constexpr int FL = 4 * P;                 // features per lane group
     constexpr int KS = D >= 32 ? D / 32 : 1;  // 16x16x32 k-steps (d = 16 pads to 32)
@@ -99,14 +102,15 @@ __global__ __launch_bounds__(256) void output_bf16_kernel(const uint16_t* __rest
     const int64_t unit = w / wpu;  // unit = pair * M + block
     const int s = (int)(w % wpu);
     if (unit >= BH * M) return;  // whole wave; no barriers in this kernel
-    const int64_t pair = unit / M, blk = unit % M;
-    const int64_t C = N / M;
-    const int ntiles = (int)((C + 15) / 16);
+    const int64_t pair = unit / M;
+    const int blk = (int)(unit % M);
+    const int C = (int)(N / M);
+    const int ntiles = (C + 15) / 16;
     const int tile_beg = s * tpw;
     const int tile_end = min(ntiles, tile_beg + tpw);
-    const int64_t bstart = blk * C, bend = bstart + C;
+    const int bstart = blk * C, bend = bstart + C;
 
-    const float* sv = St + (blk * BH + pair) * (int64_t)L;
+    const float* sv = St + ((int64_t)blk * BH + pair) * L;
     f32x4 sch[P * P];
 #pragma unroll
     for (int c4 = 0; c4 < P * P; ++c4) sch[c4] = *reinterpret_cast<const f32x4*>(sv + c4 * 256 + lane * 4);
@@ -117,37 +121,21 @@ __global__ __launch_bounds__(256) void output_bf16_kernel(const uint16_t* __rest
 #pragma unroll
         for (int u = 0; u < 4; ++u) zt[4 * h + u] = zz[u];
     }
-
     bf16x8 bh[KS][P], bl[KS][P];
-    if constexpr (!CAUSAL) build_b<P, KS>(sch, bh, bl);
-
-    float wii = 0.f;
-    f32x4 pst[P * P];  // running summary of this block's earlier tiles (packed layout)
-    f32x4 pz[P];       // its normaliser: pz[ia][i] = p[P*(4g + i) + ia]
-    if constexpr (CAUSAL) {
-        wii = W[blk * M + blk];
-#pragma unroll
-        for (int c4 = 0; c4 < P * P; ++c4) pst[c4] = zero4();
-#pragma unroll
-        for (int a = 0; a < P; ++a) pz[a] = zero4();
-    }
+    build_b<P, KS>(sch, bh, bl);
 
     const uint16_t* Qp = Q + pair * N * D;
-    const uint16_t* Kp = K + pair * N * D;
-    const uint16_t* Vp = V + pair * N * D;
     float* Yp = Y + pair * N * D;
-
     for (int tile = tile_beg; tile < tile_end; ++tile) {
-        const int64_t t0 = bstart + 16 * (int64_t)tile;
-
+        const int t0 = bstart + 16 * tile;
         // phi(Q) as the A operand: token t0 + n, group-local features of group g.
-        const int64_t tq = t0 + n;
+        const int tq = t0 + n;
         const bool qok = tq < bend;
         uint16_t qr[FL];
         load_group<P>(Qp + tq * D + FL * g, qok, Q, qr);
         issue_fence();
         bf16x8 aq[KS];
-        float qf[FL];
+        float den = 0.f;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
@@ -155,28 +143,9 @@ __global__ __launch_bounds__(256) void output_bf16_kernel(const uint16_t* __rest
                 const int fl = 8 * ks + e;
                 const __bf16 ph = (__bf16)((fl < FL && qok) ? phi_fast(bf16_to_f32(qr[fl < FL ? fl : 0])) : 0.f);
                 aq[ks][e] = ph;
-                if (fl < FL) qf[fl] = bf16v_to_f32(ph);
+                if (fl < FL) den = fmaf(bf16v_to_f32(ph), zt[fl], den);
             }
-
-        float zc[FL];
-        if constexpr (CAUSAL) {
-            f32x4 comb[P * P];
-#pragma unroll
-            for (int c4 = 0; c4 < P * P; ++c4)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) comb[c4][i] = fmaf(wii, pst[c4][i], sch[c4][i]);
-            build_b<P, KS>(comb, bh, bl);
-#pragma unroll
-            for (int fl = 0; fl < FL; ++fl) zc[fl] = fmaf(wii, pz[fl % P][fl / P], zt[fl]);
-        } else {
-#pragma unroll
-            for (int fl = 0; fl < FL; ++fl) zc[fl] = zt[fl];
-        }
-
-        float den = 0.f;
-#pragma unroll
-        for (int fl = 0; fl < FL; ++fl) den = fmaf(qf[fl], zc[fl], den);
-        den = sum_over_groups(den);
+        den = sum_over_groups(den) + kEps;
 
         f32x4 acc[P];
 #pragma unroll
@@ -188,83 +157,186 @@ __global__ __launch_bounds__(256) void output_bf16_kernel(const uint16_t* __rest
                 acc[jb] = mfma32(aq[ks], bl[ks][jb], acc[jb]);
             }
         }
+        store_rows<P, P>(Yp, t0, bend, g, n, 0, acc, den);
+    }
+}
 
-        if constexpr (CAUSAL) {
-            // phi(K) rows (keys t0 + n) as an A operand for A^T = phi(K) phi(Q)^T.
-            const int64_t tk = t0 + n;
-            const bool kok = tk < bend;
-            uint16_t kr[FL];
-            load_group<P>(Kp + tk * D + FL * g, kok, K, kr);
-            bf16x8 ak[KS];
+// Causal: P waves share one block, wave jb computing value columns P*n + jb.
+// The workgroup walks the block's 16-token tiles in order.  For each tile the
+// P waves load Q and K once between them (one 16-byte chunk per lane), apply
+// phi once, and leave the bf16 tiles in LDS (double-buffered, one barrier per
+// tile); every wave then reads the layouts it needs: phi(Q) and phi(K) rows as
+// MFMA operands for the numerator and the 16 x 16 scores, and phi(K) with tokens
+// along k for the state update.
+//
+// The B operand S~_i + W[i,i] P (P = the block's summary over the tiles already
+// done) is one running float32 accumulator set `comb` in the packed layout: it
+// starts as S~_i and each tile adds bf16(W[i,i] phi(k))^T v with MFMA, so it is
+// formed lane-locally with no separate copy of S~_i.  The normaliser works the
+// same way (start z~_i, add with an MFMA against ones).  Inside the tile the
+// masked product (phi(Q) phi(K)^T) V covers the inclusive prefix exactly; its
+// weights are carried as bf16 hi + lo and its row sums come from the same
+// rounded values (chunkwise form of App. C).
+template <int D>
+__global__ __launch_bounds__(256) void output_causal_kernel(const uint16_t* __restrict__ Q,
+                                                            const uint16_t* __restrict__ K,
+                                                            const uint16_t* __restrict__ V,
+                                                            const float* __restrict__ St,
+                                                            const float* __restrict__ W, float* __restrict__ Y,
+                                                            int64_t BH, int N, int64_t M) {
+    constexpr int P = D / 16;
+    constexpr int FL = 4 * P;
+    constexpr int KS = D >= 32 ? D / 32 : 1;
+    constexpr int L = D * D + D;
+    constexpr int BPW = 4 / P;    // blocks per workgroup
+    constexpr int TILE = 16 * D;  // bf16 elements of one 16-token tile
+    __shared__ __align__(16) uint16_t lds[2][BPW][2][TILE];  // [buffer][block slot][phi(Q), phi(K)]
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, n = lane & 15;
+    const int bw = wave / P, jb = wave % P;
+    const int64_t unit = (int64_t)blockIdx.x * BPW + bw;  // pair * M + block
+    const bool active = unit < BH * M;                      // inactive slots still meet the barriers
+    const int64_t pair = active ? unit / M : 0;
+    const int blk = active ? (int)(unit % M) : 0;
+    const int C = (int)(N / M);
+    const int ntiles = (C + 15) / 16;
+    const int bstart = blk * C, bend = bstart + C;
+    const float wii = active ? W[(int64_t)blk * M + blk] : 0.f;
+
+    const float* sv = St + ((int64_t)blk * BH + pair) * L;
+    f32x4 comb[P];  // comb[ia] = chunk (ia, jb) of S~_i + W[i,i] P
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
+    for (int ia = 0; ia < P; ++ia)
+        comb[ia] = load_or_zero(reinterpret_cast<const f32x4*>(sv + (ia * P + jb) * 256 + lane * 4), active,
+                                reinterpret_cast<const f32x4*>(St));
+    f32x4 zacc[P];  // zacc[ia][i] = running normaliser at group-local feature P*i + ia
+#pragma unroll
+    for (int h = 0; h < FL / 4; ++h) {
+        const f32x4 zz = load_or_zero(reinterpret_cast<const f32x4*>(sv + D * D + FL * g + 4 * h), active,
+                                      reinterpret_cast<const f32x4*>(St));
+#pragma unroll
+        for (int u = 0; u < 4; ++u) zacc[(4 * h + u) % P][(4 * h + u) / P] = zz[u];
+    }
+
+    const uint16_t* Qp = Q + pair * N * D;
+    const uint16_t* Kp = K + pair * N * D;
+    const uint16_t* Vp = V + pair * N * D;
+    float* Yp = Y + pair * N * D;
+    const bf16x4 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
+
+    // This lane's share of the tile: one 16-byte chunk of Q or K.
+    constexpr int CPR = D / 8;                    // 8-element chunks per row
+    const int chunk = jb * 64 + lane;             // 0 .. 4D - 1
+    const int which = chunk / (16 * CPR);         // 0: Q, 1: K
+    const int crow = (chunk % (16 * CPR)) / CPR;  // token within the tile
+    const int ccol = 8 * (chunk % CPR);           // first feature
+    const uint16_t* src = which ? Kp : Qp;
+
+    for (int tile = 0; tile < ntiles; ++tile) {
+        const int t0 = bstart + 16 * tile;
+        uint16_t* buf = &lds[tile & 1][bw][0][0];
+        {  // phi of this lane's chunk into LDS
+            const bool ok = active && t0 + crow < bend;
+            const uint4 x = load_or_zero(reinterpret_cast<const uint4*>(src + (t0 + crow) * D + ccol), ok,
+                                         reinterpret_cast<const uint4*>(Q));
+            const uint32_t wv[4] = {x.x, x.y, x.z, x.w};
+            uint32_t o[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const __bf16 lo = (__bf16)(ok ? phi_fast(__uint_as_float(wv[u] << 16)) : 0.f);
+                const __bf16 hi = (__bf16)(ok ? phi_fast(__uint_as_float(wv[u] & 0xffff0000u)) : 0.f);
+                o[u] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+            }
+            *reinterpret_cast<uint4*>(buf + which * TILE + crow * D + ccol) = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+        // This wave's value column for tokens t0 + 4g + e (tokens along k).
+        bf16x4 bv4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int tok = t0 + 4 * g + e;
+            bv4[e] = bits_to_bf16(load_or_zero(Vp + tok * D + P * n + jb, active && tok < bend, V));
+        }
+        __syncthreads();
+
+        const uint16_t* tq = buf;
+        const uint16_t* tk = buf + TILE;
+        bf16x8 aq[KS], ak[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if constexpr (FL >= 8) {
+                aq[ks] = *reinterpret_cast<const bf16x8*>(tq + n * D + FL * g + 8 * ks);
+                ak[ks] = *reinterpret_cast<const bf16x8*>(tk + n * D + FL * g + 8 * ks);
+            } else {  // d = 16: four features per group, zero-padded to the 32-deep MFMA
+                const bf16x4 a4 = *reinterpret_cast<const bf16x4*>(tq + n * D + FL * g);
+                const bf16x4 k4 = *reinterpret_cast<const bf16x4*>(tk + n * D + FL * g);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const int fl = 8 * ks + e;
-                    ak[ks][e] = (__bf16)((fl < FL && kok) ? phi_fast(bf16_to_f32(kr[fl < FL ? fl : 0])) : 0.f);
-                }
-            // The tile's K and V with tokens along k: lane holds tokens t0 + 4g + e
-            // (e < 4) at features / columns P*n .. P*n + P - 1.
-            bf16x4 ak16[P], bv16[P];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int64_t tok = t0 + 4 * g + e;
-                const bool ok = tok < bend;
-                uint16_t k16[P], v16[P];
-                load_feat3<P>(Kp + tok * D + P * n, ok, K, k16);
-                load_feat3<P>(Vp + tok * D + P * n, ok, V, v16);
-#pragma unroll
-                for (int f = 0; f < P; ++f) {
-                    ak16[f][e] = (__bf16)(ok ? phi_fast(bf16_to_f32(k16[f])) : 0.f);
-                    bv16[f][e] = bits_to_bf16(v16[f]);
+                    aq[ks][e] = e < 4 ? a4[e & 3] : (__bf16)0.f;
+                    ak[ks][e] = e < 4 ? k4[e & 3] : (__bf16)0.f;
                 }
             }
-            // Lane (g, n) receives A[query n][key 4g + i], i = 0..3.
-            f32x4 at = zero4();
+        }
+        bf16x4 ak4[P];  // bf16(W[i,i] phi(k)) for tokens t0 + 4g + e, features P*n + ia
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) at = mfma32(ak[ks], aq[ks], at);
-            bf16x4 ahi, alo;
-            float rs = 0.f;
+        for (int e = 0; e < 4; ++e) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float a = (4 * g + i <= n) ? wii * at[i] : 0.f;
-                const bf16pair h = split_bf16(a);
-                ahi[i] = h.hi;
-                alo[i] = h.lo;
-                rs += bf16v_to_f32(h.hi) + bf16v_to_f32(h.lo);
-            }
-            den += sum_over_groups(rs);
-#pragma unroll
-            for (int jb = 0; jb < P; ++jb) {
-                acc[jb] = mfma16(ahi, bv16[jb], acc[jb]);
-                acc[jb] = mfma16(alo, bv16[jb], acc[jb]);
-            }
-            // Fold this tile into the running block summary.
-            const bf16x4 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
-#pragma unroll
-            for (int ia = 0; ia < P; ++ia) {
-#pragma unroll
-                for (int jb = 0; jb < P; ++jb) pst[ia * P + jb] = mfma16(ak16[ia], bv16[jb], pst[ia * P + jb]);
-                pz[ia] = mfma16(ak16[ia], ones, pz[ia]);
-            }
+            for (int ia = 0; ia < P; ++ia)
+                ak4[ia][e] = (__bf16)(wii * bf16_to_f32(tk[(4 * g + e) * D + P * n + ia]));
         }
 
-        den += kEps;
+        // Numerator and denominator against S~_i + W[i,i] P (tiles before this one).
+        f32x4 acc[1];
+        acc[0] = zero4();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            bf16x8 bh, bl;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int fl = 8 * ks + e;
+                const float x = fl < FL ? comb[fl % P][fl / P] : 0.f;
+                const bf16pair hp = split_bf16(x);
+                bh[e] = hp.hi;
+                bl[e] = hp.lo;
+            }
+            acc[0] = mfma32(aq[ks], bh, acc[0]);
+            acc[0] = mfma32(aq[ks], bl, acc[0]);
+        }
+        float den = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int fl = 8 * ks + e;
+                if (fl < FL) den = fmaf(bf16v_to_f32(aq[ks][e]), zacc[fl % P][fl / P], den);
+            }
+        den = sum_over_groups(den);
+
+        // Inside the tile: lane (g, n) gets A[query n][key 4g + i], kept for key <= query.
+        f32x4 at = zero4();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) at = mfma32(ak[ks], aq[ks], at);
+        bf16x4 ahi, alo;
+        float rs = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float dd = __shfl(den, 4 * g + i, 64);
-            const int64_t row = t0 + 4 * g + i;
-            if (row < bend) {
-                float* dst = Yp + row * D + P * n;
-                if constexpr (P == 4) {
-                    *reinterpret_cast<f32x4*>(dst) = f32x4{acc[0][i] / dd, acc[1][i] / dd, acc[2][i] / dd, acc[3][i] / dd};
-                } else if constexpr (P == 2) {
-                    *reinterpret_cast<float2*>(dst) = make_float2(acc[0][i] / dd, acc[1][i] / dd);
-                } else {
-                    dst[0] = acc[0][i] / dd;
-                }
-            }
+            const float a = (4 * g + i <= n) ? wii * at[i] : 0.f;
+            const bf16pair hp = split_bf16(a);
+            ahi[i] = hp.hi;
+            alo[i] = hp.lo;
+            rs += bf16v_to_f32(hp.hi) + bf16v_to_f32(hp.lo);
         }
+        den += sum_over_groups(rs) + kEps;
+        acc[0] = mfma16(ahi, bv4, acc[0]);
+        acc[0] = mfma16(alo, bv4, acc[0]);
+
+        // Fold this tile into the running operand and normaliser.
+#pragma unroll
+        for (int ia = 0; ia < P; ++ia) {
+            comb[ia] = mfma16(ak4[ia], bv4, comb[ia]);
+            zacc[ia] = mfma16(ak4[ia], ones, zacc[ia]);
+        }
+        if (active) store_rows<P, 1>(Yp, t0, bend, g, n, jb, acc, den);
     }
 }
 
@@ -312,33 +384,36 @@ hipError_t launch_output(int dtype, const void* q, const void* k, const void* v,
             (const float*)q, (const float*)k, (const float*)v, St, W, out, BH, N, M, D, causal ? 1 : 0);
         return hipGetLastError();
     }
-    const int64_t C = N / M;
-    const int ntiles = (int)((C + 15) / 16);
-    // Causal: one wave walks all of a block's tiles in order.  Otherwise up to
-    // four tiles per wave, amortising the summary operand over 64 tokens.
-    const int tpw = causal ? ntiles : min(ntiles, 4);
-    const int wpu = (ntiles + tpw - 1) / tpw;
-    const int64_t waves = BH * M * wpu;
-    const dim3 grid((unsigned)((waves + 3) / 4));
     const uint16_t* qq = (const uint16_t*)q;
     const uint16_t* kk = (const uint16_t*)k;
     const uint16_t* vv = (const uint16_t*)v;
-#define MHLA_LAUNCH_OUT(DD, CC) \
-    output_bf16_kernel<DD, CC><<<grid, dim3(256), 0, stream>>>(qq, kk, vv, St, W, out, BH, N, M, tpw, wpu)
-    if (causal) {
+    if (causal) {  // d/16 waves per block, 4 / (d/16) blocks per workgroup
+        const int bpw = 4 / (D / 16);
+        const dim3 grid((unsigned)((BH * M + bpw - 1) / bpw));
+#define MHLA_LAUNCH_OUT(DD) \
+    output_causal_kernel<DD><<<grid, dim3(256), 0, stream>>>(qq, kk, vv, St, W, out, BH, (int)N, M)
         switch (D) {
-            case 16: MHLA_LAUNCH_OUT(16, true); break;
-            case 32: MHLA_LAUNCH_OUT(32, true); break;
-            case 64: MHLA_LAUNCH_OUT(64, true); break;
+            case 16: MHLA_LAUNCH_OUT(16); break;
+            case 32: MHLA_LAUNCH_OUT(32); break;
+            case 64: MHLA_LAUNCH_OUT(64); break;
             default: return hipErrorInvalidValue;
         }
-    } else {
-        switch (D) {
-            case 16: MHLA_LAUNCH_OUT(16, false); break;
-            case 32: MHLA_LAUNCH_OUT(32, false); break;
-            case 64: MHLA_LAUNCH_OUT(64, false); break;
-            default: return hipErrorInvalidValue;
-        }
+#undef MHLA_LAUNCH_OUT
+        return hipGetLastError();
+    }
+    // Up to four tiles per wave, amortising the summary operand over 64 tokens.
+    const int64_t C = N / M;
+    const int ntiles = (int)((C + 15) / 16);
+    const int tpw = min(ntiles, 4);
+    const int wpu = (ntiles + tpw - 1) / tpw;
+    const dim3 grid((unsigned)((BH * M * wpu + 3) / 4));
+#define MHLA_LAUNCH_OUT(DD) \
+    output_bf16_kernel<DD><<<grid, dim3(256), 0, stream>>>(qq, St, out, BH, (int)N, M, tpw, wpu)
+    switch (D) {
+        case 16: MHLA_LAUNCH_OUT(16); break;
+        case 32: MHLA_LAUNCH_OUT(32); break;
+        case 64: MHLA_LAUNCH_OUT(64); break;
+        default: return hipErrorInvalidValue;
     }
 #undef MHLA_LAUNCH_OUT
     return hipGetLastError();
