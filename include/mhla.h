@@ -67,13 +67,21 @@ enum {
 /* Input element type for the stage-level calls. */
 enum { MHLA_DTYPE_BF16 = 0, MHLA_DTYPE_F32 = 1 };
 
+/* The kernels mhla_forward runs (see mhla_forward_path). */
+enum { MHLA_PATH_STAGED = 0, MHLA_PATH_FUSED = 1 };
+
 /*
  * Full forward pass, bfloat16 q/k/v (float32 accumulation, float32 W and out).
- * Enqueues the three kernels -- block summaries, block mixing, output -- on
- * `stream`.  The summaries live in a stream-ordered workspace of
- * mhla_workspace_bytes() bytes taken from a library-owned memory pool on the
- * current device and returned to it (stream-ordered) before the call returns.
- * causal != 0 selects the causal variant.
+ * causal != 0 selects the causal variant.  Two execution paths compute the same
+ * four steps:
+ *   - staged: the three stage kernels below (block summaries, mixing, output)
+ *     through a stream-ordered workspace of mhla_workspace_bytes() bytes taken
+ *     from a library-owned memory pool on the current device and returned to it
+ *     (stream-ordered) before the call returns;
+ *   - fused (non-causal, blocks of at most 16 tokens, M * d <= 1024 and
+ *     B*H*d/16 >= 256): one kernel per (pair, 16 value columns) that keeps the
+ *     block summaries and their mix in LDS; no workspace.
+ * mhla_forward_path() reports which one a call with given sizes uses.
  */
 int mhla_forward(const void* q, const void* k, const void* v, const float* W, float* out,
                  int64_t B, int64_t H, int64_t N, int64_t d, int64_t M, int causal,
@@ -84,7 +92,12 @@ int mhla_forward_f32(const float* q, const float* k, const float* v, const float
                      int64_t B, int64_t H, int64_t N, int64_t d, int64_t M, int causal,
                      mhla_stream_t stream);
 
-/* Bytes of device workspace one forward call uses: the S and S~ summary
+/* Which path mhla_forward (dtype MHLA_DTYPE_BF16) or mhla_forward_f32
+ * (MHLA_DTYPE_F32; always staged) takes for these sizes: MHLA_PATH_STAGED or
+ * MHLA_PATH_FUSED; -1 for invalid sizes or dtype. */
+int mhla_forward_path(int64_t B, int64_t H, int64_t N, int64_t d, int64_t M, int causal, int dtype);
+
+/* Bytes of device workspace one staged forward call uses (the fused path uses none): the S and S~ summary
  * arrays (2 * M * B*H * (d*d + d) floats) plus the bf16 hi/lo split of W for
  * the mixing kernel when 64 < M <= 1024 (4 * M * M bytes, rounded up to whole
  * 64 x 32 MFMA tiles; none otherwise); -1 for invalid sizes. */

@@ -83,6 +83,18 @@ def test_stage_validation(mhla_lib):
         mh.MHLA_ERR_INVALID_ARG
 
 
+def test_forward_path_selection(mhla_lib):
+    # short blocks, small M, enough (pair, 16-column) workgroups: fused; otherwise staged
+    assert mh.mhla_forward_path(64, 6, 256, 64, 16) == mh.MHLA_PATH_FUSED
+    assert mh.mhla_forward_path(64, 6, 256, 64, 16, causal=True) == mh.MHLA_PATH_STAGED
+    assert mh.mhla_forward_path(64, 6, 256, 64, 16, dtype=mh.MHLA_DTYPE_F32) == mh.MHLA_PATH_STAGED
+    assert mh.mhla_forward_path(1, 6, 65536, 64, 256) == mh.MHLA_PATH_STAGED   # M * d too large
+    assert mh.mhla_forward_path(4, 70, 16384, 32, 64) == mh.MHLA_PATH_STAGED   # blocks of 256 tokens
+    assert mh.mhla_forward_path(1, 6, 256, 64, 16) == mh.MHLA_PATH_STAGED      # too few workgroups
+    assert mh.mhla_forward_path(256, 1, 64, 16, 64) == mh.MHLA_PATH_FUSED
+    assert mh.mhla_forward_path(1, 1, 250, 64, 16) == -1
+
+
 def test_status_strings(mhla_lib):
     assert mh.mhla_status_string(0) == "MHLA_OK"
     assert mh.mhla_status_string(mh.MHLA_ERR_HIP) == "MHLA_ERR_HIP"

@@ -113,6 +113,57 @@ def test_shape_sweep(orc, case):
     check(w, q, k, v, W, orc, "sweep")
 
 
+FUSED = [  # (B, H, N, d, M): shapes mhla_forward runs through the fused on-chip kernel
+    (64, 1, 256, 64, 16),   # DiT-S/2 @256 blocks, one head
+    (64, 1, 160, 64, 16),   # 10-token blocks: ragged 16-token k-steps and query tiles
+    (32, 2, 16, 64, 1),     # one block of 16 tokens
+    (128, 1, 96, 32, 32),   # d = 32, 3-token blocks
+    (64, 2, 512, 32, 32),   # 16-token blocks, d = 32
+    (64, 1, 176, 64, 16),   # 11-token blocks
+    (256, 1, 64, 16, 64),   # d = 16, one token per block
+    (96, 4, 256, 64, 16),   # more workgroups than fit at once
+]
+
+
+@pytest.mark.parametrize("case", FUSED, ids=lambda c: "B{}H{}N{}d{}M{}".format(*c))
+def test_fused_path(orc, case):
+    B, H, N, d, M = case
+    assert mh.mhla_forward_path(B, H, N, d, M) == mh.MHLA_PATH_FUSED
+    w = WORKLOADS["dit_s2_256"].shrink(B=B, H=H, N=N, d=d, M=M, seed=4000 + FUSED.index(case))
+    q, k, v, W = make_inputs(w)
+    check(w, q, k, v, W, orc, "fused")
+
+
+def staged_forward(q, k, v, W, causal, dtype):
+    """The three stage entry points chained by hand (the staged path end to end)."""
+    B, H, N, d = q.shape
+    M = W.shape[0]
+    qd, kd, vd = (to_dev(a, dtype) for a in (q, k, v))
+    Wd = torch.from_numpy(W).cuda()
+    L = mh.mhla_summary_floats(d)
+    S = torch.empty(M * B * H * L, dtype=torch.float32, device="cuda")
+    St = torch.empty_like(S)
+    out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    mh.mhla_block_summaries(kd, vd, S, M)
+    mh.mhla_mix_summaries(S, Wd, St, B * H, d, causal=causal, precise=(dtype == "f32"))
+    mh.mhla_output(qd, kd, vd, St, Wd, out, causal=causal)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("key", ["dit_s2_256", "tiny_f32"])
+def test_staged_path_end_to_end(orc, key):
+    """The staged kernels on shapes where mhla_forward would take the fused path."""
+    w = WORKLOADS[key]
+    q, k, v, W = make_inputs(w)
+    say(f"[parity] staged {key}")
+    y = staged_forward(q, k, v, W, w.causal, w.dtype)
+    ref = orc.forward(q, k, v, W, causal=w.causal, nthreads=NTHREADS)
+    e = rel(y, ref)
+    say(f"[parity] staged {key}: max|dY|/max|Y| = {e:.3e}")
+    assert e <= TOL[w.dtype], e
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("d", [16, 32, 64])
 def test_stage_summaries_and_mix(orc, dtype, d):

@@ -11,7 +11,8 @@ import importlib
 _BINDING_NAMES = {
     "LIB_PATH", "MHLA_DTYPE_BF16", "MHLA_DTYPE_F32", "MHLA_ERR_HIP", "MHLA_ERR_INVALID_ARG",
     "MHLA_ERR_NO_MEMORY", "MHLA_ERR_UNSUPPORTED", "MHLA_OK", "MhlaError", "load_library",
-    "mhla_block_summaries", "mhla_forward", "mhla_forward_f32", "mhla_last_error", "mhla_mix_summaries",
+    "mhla_block_summaries", "mhla_forward", "mhla_forward_f32", "mhla_forward_path", "MHLA_PATH_STAGED",
+    "MHLA_PATH_FUSED", "mhla_last_error", "mhla_mix_summaries",
     "mhla_output", "mhla_status_string", "mhla_summary_floats", "mhla_unpack_summaries", "mhla_version",
     "mhla_workspace_bytes",
 }

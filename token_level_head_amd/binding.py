@@ -21,6 +21,8 @@ MHLA_ERR_NO_MEMORY = -3
 MHLA_ERR_HIP = -4
 MHLA_DTYPE_BF16 = 0
 MHLA_DTYPE_F32 = 1
+MHLA_PATH_STAGED = 0
+MHLA_PATH_FUSED = 1
 
 # Every symbol include/mhla.h declares, with (restype, argtypes).
 _P = ctypes.c_void_p
@@ -30,6 +32,7 @@ SIGNATURES = {
     "mhla_forward": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _P]),
     "mhla_forward_f32": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _P]),
     "mhla_workspace_bytes": (_I64, [_I64, _I64, _I64, _I64, _I64, _I]),
+    "mhla_forward_path": (_I, [_I64, _I64, _I64, _I64, _I64, _I, _I]),
     "mhla_summary_floats": (_I64, [_I64]),
     "mhla_block_summaries": (_I, [_P, _P, _I, _P, _I64, _I64, _I64, _I64, _I64, _P]),
     "mhla_mix_summaries": (_I, [_P, _P, _P, _I64, _I64, _I64, _I, _I, _P]),
@@ -112,6 +115,11 @@ def _dtype_code(t):
 
 def mhla_workspace_bytes(B, H, N, d, M, causal=False):
     return int(load_library().mhla_workspace_bytes(B, H, N, d, M, int(bool(causal))))
+
+
+def mhla_forward_path(B, H, N, d, M, causal=False, dtype=MHLA_DTYPE_BF16):
+    """MHLA_PATH_STAGED or MHLA_PATH_FUSED: the kernels mhla_forward runs for these sizes."""
+    return int(load_library().mhla_forward_path(B, H, N, d, M, int(bool(causal)), dtype))
 
 
 def mhla_summary_floats(d):

@@ -74,6 +74,35 @@ struct MaskBits<8> { typedef uint32_t type __attribute__((ext_vector_type(2))); 
 template <>
 struct MaskBits<16> { typedef uint32_t type __attribute__((ext_vector_type(4))); };
 
+// Raw buffer access (gfx9 family): a scalar resource descriptor over `bytes` bytes
+// from `base`, addressed with 32-bit byte offsets in a vector register.  A load
+// whose offset lies at or beyond `bytes` returns zero and touches no memory, so
+// masked loads need neither a branch nor a select, and no 64-bit address
+// arithmetic is spent per lane.  Word 3 = 0x00020000 selects untyped 32-bit
+// data (no swizzle, no per-lane index).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;  // any offset at or past the end reads zero
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint32_t off_if(bool ok, uint32_t byte_off) { return ok ? byte_off : kOutOfRange; }
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint16_t buf_load16(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ uint32_t buf_load32(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ u32x2 buf_load64(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ u32x4 buf_load128(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
 // Keeps the scheduler from moving instructions across this point; placed after a
 // batch of loads so that the whole batch is issued before its consumers run
 // (otherwise the scheduler may serialise the loads to save registers).

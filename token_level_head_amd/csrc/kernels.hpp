@@ -27,4 +27,10 @@ hipError_t launch_output(int dtype, const void* q, const void* k, const void* v,
                          const float* W, float* out, int64_t BH, int64_t N, int D, int64_t M, bool causal,
                          hipStream_t stream);
 
+// Fused path (non-causal bf16, short blocks): the whole pass in one kernel with
+// the summaries in LDS; needs no workspace.
+bool fused_applicable(int D, int64_t BH, int64_t N, int64_t M);
+hipError_t launch_fused(const void* q, const void* k, const void* v, const float* W, float* out, int64_t BH,
+                        int64_t N, int D, int64_t M, hipStream_t stream);
+
 }  // namespace mhla

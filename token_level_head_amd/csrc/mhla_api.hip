@@ -134,6 +134,11 @@ int pool_alloc(void** ptr, size_t bytes, hipStream_t stream) {
     return MHLA_OK;
 }
 
+int forward_path(int64_t B, int64_t H, int64_t N, int64_t d, int64_t M, int causal, int dtype) {
+    return dtype == mhla::kDtypeBF16 && !causal && mhla::fused_applicable((int)d, B * H, N, M) ? MHLA_PATH_FUSED
+                                                                                             : MHLA_PATH_STAGED;
+}
+
 int forward_impl(int dtype, const void* q, const void* k, const void* v, const float* W, float* out, int64_t B,
                  int64_t H, int64_t N, int64_t d, int64_t M, int causal, mhla_stream_t stream_) {
     int st = check_sizes(B, H, N, d, M);
@@ -150,6 +155,11 @@ int forward_impl(int dtype, const void* q, const void* k, const void* v, const f
 
     hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
     const int64_t BH = B * H;
+    if (forward_path(B, H, N, d, M, causal, dtype) == MHLA_PATH_FUSED) {
+        hipError_t e = mhla::launch_fused(q, k, v, W, out, BH, N, (int)d, M, stream);
+        if (e != hipSuccess) return hip_fail(e, "fused kernel");
+        return ok();
+    }
     const size_t arr = (size_t)(M * BH * summary_floats(d)) * sizeof(float);
     const size_t total = workspace_bytes(BH, d, M);
     void* ws = nullptr;
@@ -192,6 +202,12 @@ int64_t mhla_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int64_t
     (void)causal;
     if (check_sizes(B, H, N, d, M) != MHLA_OK) return -1;
     return (int64_t)workspace_bytes(B * H, d, M);
+}
+
+int mhla_forward_path(int64_t B, int64_t H, int64_t N, int64_t d, int64_t M, int causal, int dtype) {
+    if (check_sizes(B, H, N, d, M) != MHLA_OK) return -1;
+    if (dtype != MHLA_DTYPE_BF16 && dtype != MHLA_DTYPE_F32) return fail(MHLA_ERR_INVALID_ARG, "bad dtype %d", dtype);
+    return forward_path(B, H, N, d, M, causal, dtype);
 }
 
 int64_t mhla_summary_floats(int64_t d) { return d >= 1 ? summary_floats(d) : -1; }
