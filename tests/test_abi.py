@@ -84,14 +84,16 @@ def test_stage_validation(mhla_lib):
 
 
 def test_forward_path_selection(mhla_lib):
-    # short blocks, small M, enough (pair, 16-column) workgroups: fused; otherwise staged
+    # non-causal bf16 with blocks of at most 16 tokens and at most 16 blocks: fused; otherwise staged
     assert mh.mhla_forward_path(64, 6, 256, 64, 16) == mh.MHLA_PATH_FUSED
     assert mh.mhla_forward_path(64, 6, 256, 64, 16, causal=True) == mh.MHLA_PATH_STAGED
     assert mh.mhla_forward_path(64, 6, 256, 64, 16, dtype=mh.MHLA_DTYPE_F32) == mh.MHLA_PATH_STAGED
-    assert mh.mhla_forward_path(1, 6, 65536, 64, 256) == mh.MHLA_PATH_STAGED   # M * d too large
+    assert mh.mhla_forward_path(1, 6, 65536, 64, 256) == mh.MHLA_PATH_STAGED   # M > 16
     assert mh.mhla_forward_path(4, 70, 16384, 32, 64) == mh.MHLA_PATH_STAGED   # blocks of 256 tokens
-    assert mh.mhla_forward_path(1, 6, 256, 64, 16) == mh.MHLA_PATH_STAGED      # too few workgroups
-    assert mh.mhla_forward_path(256, 1, 64, 16, 64) == mh.MHLA_PATH_FUSED
+    assert mh.mhla_forward_path(1, 6, 256, 64, 16) == mh.MHLA_PATH_FUSED
+    assert mh.mhla_forward_path(256, 1, 64, 16, 64) == mh.MHLA_PATH_STAGED     # M > 16
+    assert mh.mhla_forward_path(8, 2, 272, 64, 16) == mh.MHLA_PATH_STAGED      # 17-token blocks
+    assert mh.mhla_forward_path(8, 2, 60, 32, 5) == mh.MHLA_PATH_FUSED
     assert mh.mhla_forward_path(1, 1, 250, 64, 16) == -1
 
 

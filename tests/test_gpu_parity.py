@@ -117,11 +117,16 @@ FUSED = [  # (B, H, N, d, M): shapes mhla_forward runs through the fused on-chip
     (64, 1, 256, 64, 16),   # DiT-S/2 @256 blocks, one head
     (64, 1, 160, 64, 16),   # 10-token blocks: ragged 16-token k-steps and query tiles
     (32, 2, 16, 64, 1),     # one block of 16 tokens
-    (128, 1, 96, 32, 32),   # d = 32, 3-token blocks
-    (64, 2, 512, 32, 32),   # 16-token blocks, d = 32
     (64, 1, 176, 64, 16),   # 11-token blocks
-    (256, 1, 64, 16, 64),   # d = 16, one token per block
     (96, 4, 256, 64, 16),   # more workgroups than fit at once
+    (3, 2, 16, 64, 16),     # one token per block
+    (5, 3, 120, 64, 12),    # 12 blocks: waves 4..7 own one block
+    (7, 1, 60, 32, 5),      # 5 blocks (not a multiple of 4), 12-token blocks, d = 32
+    (128, 1, 48, 32, 16),   # d = 32, 3-token blocks
+    (64, 2, 256, 32, 16),   # d = 32, 16-token blocks
+    (256, 1, 16, 16, 16),   # d = 16, one token per block
+    (16, 3, 256, 16, 16),   # d = 16, 16-token blocks
+    (9, 2, 26, 16, 2),      # d = 16, 2 blocks of 13 tokens
 ]
 
 

@@ -7,287 +7,276 @@
 // When blocks are shorter than d (DiT-S/2 at 256x256: 16 tokens, d = 64) the d x d
 // summaries are several times larger than the tokens they summarise, and
 // round-tripping them through HBM dominates the three-stage pass.  Here one
-// workgroup owns one (batch, head) pair and a slice of 16 consecutive value
-// columns (16*slice .. 16*slice + 15) and runs the same four steps with the
-// summaries in LDS:
-//   1. phi(K) and the summaries of every block restricted to the slice's
-//      columns, plus z_b, on 16x16x16 bf16 MFMA (tokens along k; lane holds P
-//      features of 4 tokens, MFMA ia treats row m as feature P*m + ia);
-//   2. the mixing GEMM S~ = W S over the flattened [feature][column] + z
-//      columns, bf16 hi/lo on both operands (three MFMAs), in place in LDS;
-//   3. phi(Q) S~_i / (phi(Q) z~_i + 1e-6) for every query block, S~_i split
-//      into hi/lo as the B operand.
-// The d/16 workgroups of a pair are numbered to run on one XCD, so the second
-// and later reads of the pair's K and Q come from its L2.
+// workgroup of eight waves owns one (batch, head) pair; wave w owns blocks w and
+// w + 8.  Each wave loads its K, V and Q once and computes phi(k) and phi(q) once
+// (bf16, in registers).  The d x d summary space is then walked in P*P sub-tiles
+// of 16 features x 16 value columns (d = 16P; sub-tile (ia, c) holds features
+// P*m + ia and columns P*n + c, the lane layout of the summary MFMA), each in
+// three barrier-separated steps through LDS:
+//   1. every wave computes the sub-tile of S_b for its blocks (one 16x16x16 bf16
+//      MFMA: tokens along k) and, for c == 0, z_b (an MFMA against ones);
+//   2. the 16 entry tiles (+ the z tile) of the sub-tile are mixed,
+//      S~_i = sum_b W[i, b] S_b, on float32 MFMA (16x16x4, blocks along k:
+//      exact products); each result is split into bf16 hi + lo for step 3;
+//   3. every wave adds phi(Q_i) S~_i (sub-tile) into its output accumulators
+//      (2 bf16 MFMAs: hi and lo) and, for c == 0, phi(Q_i) z~_i into the
+//      denominator (an MFMA whose A rows all equal z~_i).
+// The output MFMA puts value columns on rows and tokens on columns, so after the
+// last sub-tile each lane holds 4P consecutive columns of one token; it scales
+// them by 1 / (den + 1e-6) and writes them with 16-byte stores.  K, V, Q and W
+// are read with buffer loads (scalar descriptor, 32-bit offsets; an offset past
+// the end reads zero).
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace mhla {
 
-template <int D>
-struct FusedShape {
-    static constexpr int P = D / 16;
-    static constexpr int NCOL = 16 * D + D;  // flattened S: [feature][16 columns], then z[feature]
-    static constexpr int STR = NCOL + 4;     // LDS row stride in floats (staggers banks across rows)
-    static constexpr int MAXM = 1024 / D;    // rows that fit in ~70 KiB of LDS
-};
+namespace {
 
-int fused_max_blocks(int D) { return 1024 / D; }
+constexpr int kMaxBlocks = 16;  // M: one 16-row MFMA tile of W and S~
+constexpr int kWaves = 8;
+constexpr int kBlocksPerWave = kMaxBlocks / kWaves;
+// LDS layout, in 4-byte words.  Strides are chosen so that every LDS access of
+// the three steps touches 64 distinct banks per wave (or, for 8-byte accesses,
+// 64 distinct banks per half wave).
+constexpr int kRSA = 20;              // S sub-tile: one feature row of 16 columns (+4)
+constexpr int kBSA = 16 * kRSA + 1;   // S sub-tile: one block (= 1 mod 4)
+constexpr int kBSB = 130;             // S~ hi (and lo): one query block, [4 feature quads][16 columns] x 2 words
+constexpr int kBZA = 16;              // z sub-tile: one block
+constexpr int kBZB = 12;              // z~ hi (and lo): one query block, 4 feature quads x 2 words
+constexpr int kLdsWords = kMaxBlocks * kBSA + 2 * kMaxBlocks * kBSB + kMaxBlocks * kBZA + 2 * kMaxBlocks * kBZB;
 
-size_t fused_lds_bytes(int D, int64_t M) { return (size_t)M * (17 * D + 4) * sizeof(float); }
+__device__ __forceinline__ float half_to_f32(uint32_t word, int half) {
+    return __uint_as_float(half ? (word & 0xffff0000u) : (word << 16));
+}
 
-template <int D>
-__global__ __launch_bounds__(256) void fused_small_kernel(const uint16_t* __restrict__ Q,
+}  // namespace
+
+template <int D, bool FULL>
+__global__ __launch_bounds__(512) void fused_small_kernel(const uint16_t* __restrict__ Q,
                                                           const uint16_t* __restrict__ K,
                                                           const uint16_t* __restrict__ V,
                                                           const float* __restrict__ W, float* __restrict__ Y,
-                                                          int64_t BH, int N, int M) {
-    using Sh = FusedShape<D>;
-    constexpr int P = Sh::P, NCOL = Sh::NCOL, STR = Sh::STR, MAXM = Sh::MAXM;
-    constexpr int FL = 4 * P;
-    constexpr int KS = D >= 32 ? D / 32 : 1;
-    constexpr int RT = (MAXM + 15) / 16;  // 16-row tiles of W / S~ (also 16-deep k-chunks over blocks)
-    extern __shared__ __align__(16) float lds[];  // [M][STR]
+                                                          int N, int M) {
+    constexpr int P = D / 16;
+    constexpr int BPW = kBlocksPerWave;
+    __shared__ __align__(16) float lds[kLdsWords];
+    float* A = lds;                                           // [16 blocks][16 features][kRSA]
+    uint2* Bhi = reinterpret_cast<uint2*>(lds + kMaxBlocks * kBSA);  // [16 query blocks][kBSB / 2]
+    uint2* Blo = Bhi + kMaxBlocks * kBSB / 2;
+    float* Az = reinterpret_cast<float*>(Blo + kMaxBlocks * kBSB / 2);  // [16 blocks][kBZA]
+    uint2* Zhi = reinterpret_cast<uint2*>(Az + kMaxBlocks * kBZA);      // [16 query blocks][kBZB / 2]
+    uint2* Zlo = Zhi + kMaxBlocks * kBZB / 2;
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, n = lane & 15;
-    // Workgroup b runs on XCD b % 8; the P slices of one pair share that XCD.
-    const int64_t bid = blockIdx.x;
-    const int slice = (int)((bid >> 3) % P);
-    const int64_t pair = ((bid >> 3) / P) * 8 + (bid & 7);
-    if (pair >= BH) return;  // uniform over the workgroup: no barrier is skipped by part of it
-    const int C = N / M;
-    const int col0 = 16 * slice;
-    const uint16_t* Kp = K + pair * N * D;
-    const uint16_t* Vp = V + pair * N * D;
-    const uint16_t* Qp = Q + pair * N * D;
-    float* Yp = Y + pair * N * D;
-    const bf16x4 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
+    const int64_t pair = blockIdx.x;
+    const int C = FULL ? 16 : N / M;  // tokens per block, <= 16
 
-    // Blocks hold at most 16 tokens (one 16-deep MFMA k-step, one query tile), and
-    // wave w owns blocks w, w + 4, ...; both token phases work on groups of four of
-    // its blocks, with all loads of a group issued before any of them is used.
-    const int nb = (M - wave + 3) / 4;  // blocks of this wave
+    // Blocks M .. 15 take part in the mixing MFMAs with weight zero: clear their rows.
+    for (int x = threadIdx.x; x < (kMaxBlocks - M) * kBSA; x += 512) A[M * kBSA + x] = 0.f;
+    for (int x = threadIdx.x; x < (kMaxBlocks - M) * kBZA; x += 512) Az[M * kBZA + x] = 0.f;
 
-    // Q of the first group of query blocks, loaded now and used after the mixing.
-    uint16_t qpre[4][FL];
-    auto load_q = [&](int j0, uint16_t (&qr)[4][FL]) {
+    // ---- loads: K and V (lane: P features / columns of tokens 4g .. 4g+3), Q (lane:
+    // features 4Pg .. 4Pg + 4P - 1 of token n), W (lane: W[n][4kb + g]) ----
+    const uint32_t pair_bytes = (uint32_t)N * D * 2;
+    const rsrc_t rK = make_rsrc(K + pair * N * D, pair_bytes);
+    const rsrc_t rV = make_rsrc(V + pair * N * D, pair_bytes);
+    const rsrc_t rQ = make_rsrc(Q + pair * N * D, pair_bytes);
+    const rsrc_t rW = make_rsrc(W, (uint32_t)M * M * 4);
+    u32x2 kw[BPW][4], vw[BPW][4];
+    u32x4 qw[BPW][P == 4 ? 2 : 1];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int i = wave + 4 * (j0 + u);
-            const bool ok = j0 + u < nb && n < C;
-            const int tq = i * C + n;
-            if constexpr (P == 1) {
-                const uint2 x = load_or_zero(reinterpret_cast<const uint2*>(Qp + tq * D + FL * g), ok,
-                                             reinterpret_cast<const uint2*>(Q));
-                qr[u][0] = (uint16_t)x.x; qr[u][1] = (uint16_t)(x.x >> 16);
-                qr[u][2] = (uint16_t)x.y; qr[u][3] = (uint16_t)(x.y >> 16);
+    for (int j = 0; j < BPW; ++j) {
+        const int b = wave + kWaves * j;  // b >= M reads past the end: zeros
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t off = ((uint32_t)(b * C + 4 * g + e) * D + P * n) * 2;
+            if constexpr (P == 4) {
+                kw[j][e] = buf_load64(rK, off);
+                vw[j][e] = buf_load64(rV, off);
+            } else if constexpr (P == 2) {
+                kw[j][e] = u32x2{buf_load32(rK, off), 0u};
+                vw[j][e] = u32x2{buf_load32(rV, off), 0u};
             } else {
-#pragma unroll
-                for (int h = 0; h < P / 2; ++h) {
-                    const uint4 x = load_or_zero(reinterpret_cast<const uint4*>(Qp + tq * D + FL * g + 8 * h), ok,
-                                                 reinterpret_cast<const uint4*>(Q));
-                    const uint32_t w4[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-                    for (int v2 = 0; v2 < 4; ++v2) {
-                        qr[u][8 * h + 2 * v2] = (uint16_t)w4[v2];
-                        qr[u][8 * h + 2 * v2 + 1] = (uint16_t)(w4[v2] >> 16);
-                    }
-                }
+                kw[j][e] = u32x2{buf_load16(rK, off), 0u};
+                vw[j][e] = u32x2{buf_load16(rV, off), 0u};
             }
         }
-    };
-    load_q(0, qpre);
-
-    // ---- 1. summaries of every block over this slice's columns ----
-    for (int j0 = 0; j0 < nb; j0 += 4) {
-        uint16_t kr[4][4][P], vr[4][4];  // [block of the group][token e][feature]
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int b = wave + 4 * (j0 + u);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int tl = 4 * g + e;
-                const bool ok = j0 + u < nb && tl < C;
-                const int t = b * C + tl;
-                if constexpr (P == 4) {
-                    const uint2 x = load_or_zero(reinterpret_cast<const uint2*>(Kp + t * D + P * n), ok,
-                                                 reinterpret_cast<const uint2*>(K));
-                    kr[u][e][0] = (uint16_t)x.x; kr[u][e][1] = (uint16_t)(x.x >> 16);
-                    kr[u][e][2] = (uint16_t)x.y; kr[u][e][3] = (uint16_t)(x.y >> 16);
-                } else if constexpr (P == 2) {
-                    const uint32_t x = load_or_zero(reinterpret_cast<const uint32_t*>(Kp + t * D + P * n), ok,
-                                                    reinterpret_cast<const uint32_t*>(K));
-                    kr[u][e][0] = (uint16_t)x; kr[u][e][1] = (uint16_t)(x >> 16);
-                } else {
-                    kr[u][e][0] = load_or_zero(Kp + t * D + n, ok, K);
-                }
-                vr[u][e] = load_or_zero(Vp + t * D + col0 + n, ok, V);
-            }
-        }
-        issue_fence();
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            if (j0 + u < nb) {  // uniform
-                const int b = wave + 4 * (j0 + u);
-                bf16x4 a[P], bv;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const bool ok = 4 * g + e < C;
-#pragma unroll
-                    for (int ia = 0; ia < P; ++ia)
-                        a[ia][e] = (__bf16)(ok ? phi_fast(bf16_to_f32(kr[u][e][ia])) : 0.f);
-                    bv[e] = bits_to_bf16(vr[u][e]);
-                }
-                // lane (g, n) gets S_b[P*(4g + i) + ia][col0 + n] and z_b at the same features.
-                float* row = lds + b * STR;
-#pragma unroll
-                for (int ia = 0; ia < P; ++ia) {
-                    const f32x4 sa = mfma16(a[ia], bv, zero4());
-                    const f32x4 za = mfma16(a[ia], ones, zero4());
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int f = P * (4 * g + i) + ia;
-                        row[f * 16 + n] = sa[i];
-                        if (n == 0) row[16 * D + f] = za[i];
-                    }
-                }
-            }
+        const uint32_t qoff = ((uint32_t)(b * C + n) * D + 4 * P * g) * 2;
+        if constexpr (P == 4) {
+            qw[j][0] = buf_load128(rQ, qoff);
+            qw[j][1] = buf_load128(rQ, qoff + 16);
+        } else if constexpr (P == 2) {
+            qw[j][0] = buf_load128(rQ, qoff);
+        } else {
+            const u32x2 x = buf_load64(rQ, qoff);
+            qw[j][0] = u32x4{x.x, x.y, 0u, 0u};
         }
     }
-    __syncthreads();
+    float wf[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        const int b = 4 * kb + g;
+        wf[kb] = __uint_as_float(buf_load32(rW, off_if(n < M && b < M, (uint32_t)(n * M + b) * 4)));
+    }
+    issue_fence();
 
-    // ---- 2. mixing, in place: S~[i][c] = sum_b W[i, b] S[b][c] ----
-    bf16x4 wh[RT][RT], wl[RT][RT];  // W fragments: row tile rt, k-chunk kc
+    // ---- phi(k) as the summary MFMA's A operand: ak[j][ia][e] = phi(K[4g + e][P n + ia]);
+    // phi(q) as the output MFMA's B operand: bq[j][ia][e] = phi(Q[n][P (4g + e) + ia]) ----
+    bf16x4 ak[BPW][P], bq[BPW][P];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+    for (int j = 0; j < BPW; ++j)
 #pragma unroll
-        for (int kc = 0; kc < RT; ++kc)
+        for (int e = 0; e < 4; ++e) {
+            const bool ok = FULL || 4 * g + e < C;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = 16 * rt + n, bb = 16 * kc + 4 * g + e;
-                const bf16pair p = split_bf16(load_or_zero(W + i * M + bb, i < M && bb < M, W));
-                wh[rt][kc][e] = p.hi;
-                wl[rt][kc][e] = p.lo;
+            for (int ia = 0; ia < P; ++ia) {
+                const uint32_t kword = (P == 4 && ia >= 2) ? kw[j][e].y : kw[j][e].x;
+                const float x = half_to_f32(kword, P == 1 ? 0 : ia & 1);
+                ak[j][ia][e] = (__bf16)(ok ? phi_fast(x) : 0.f);
+                const int fl = P * e + ia;
+                const uint32_t qword = qw[j][fl / 8][(fl % 8) / 2];
+                bq[j][ia][e] = (__bf16)phi_fast(half_to_f32(qword, fl & 1));
             }
-    const int rtn = (M + 15) / 16;
-    for (int ct = wave; ct < NCOL / 16; ct += 4) {
-        const int c = 16 * ct + n;
-        f32x4 acc[RT];
+        }
+
+    const bf16x4 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
+    f32x4 oacc[BPW][P], dacc[BPW];
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) acc[rt] = zero4();
+    for (int j = 0; j < BPW; ++j) {
+        dacc[j] = zero4();
 #pragma unroll
-        for (int kc = 0; kc < RT; ++kc) {
-            if (kc < rtn) {  // uniform
-                bf16x4 bh, bl;
+        for (int c = 0; c < P; ++c) oacc[j][c] = zero4();
+    }
+
+#pragma unroll
+    for (int s = 0; s < P * P; ++s) {
+        const int c = s / P, ia = s % P;
+        // 1. sub-tile (ia, c) of S_b: lane (g, n) gets S_b[P (4g + r) + ia][P n + c]
+#pragma unroll
+        for (int j = 0; j < BPW; ++j) {
+            const int b = wave + kWaves * j;
+            if (b < M) {  // uniform
+                bf16x4 bv;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int bb = 16 * kc + 4 * g + e;
-                    const bf16pair p = split_bf16(bb < M ? lds[bb * STR + c] : 0.f);
-                    bh[e] = p.hi;
-                    bl[e] = p.lo;
+                    const uint32_t vword = (P == 4 && c >= 2) ? vw[j][e].y : vw[j][e].x;
+                    bv[e] = bits_to_bf16((uint16_t)((P > 1 && (c & 1)) ? vword >> 16 : vword));
                 }
+                const f32x4 sa = mfma16(ak[j][ia], bv, zero4());
+                float* dst = A + b * kBSA + 4 * g * kRSA + n;
 #pragma unroll
-                for (int rt = 0; rt < RT; ++rt) {
-                    if (rt < rtn) {
-                        acc[rt] = mfma16(wh[rt][kc], bh, acc[rt]);
-                        acc[rt] = mfma16(wh[rt][kc], bl, acc[rt]);
-                        acc[rt] = mfma16(wl[rt][kc], bh, acc[rt]);
+                for (int r = 0; r < 4; ++r) dst[r * kRSA] = sa[r];
+                if (c == 0) {
+                    const f32x4 za = mfma16(ak[j][ia], ones, zero4());
+                    if (n == 0) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) Az[b * kBZA + 4 * g + r] = za[r];
                     }
                 }
             }
         }
-        // Every row of column c has been read by this wave; only it writes column c.
+        __syncthreads();
+
+        // 2. mixing: tile t < 16 is value column P t + c of the sub-tile, tile 16 is z.
+        //    Lane (g, n) gets S~_{i = n}[feature P (4g + r) + ia][column P t + c].
+        const int ntile = c == 0 ? 17 : 16;
+        for (int t = wave; t < ntile; t += kWaves) {  // uniform
+            const float* src = t < 16 ? A + n * kRSA + t : Az + n;
+            const int bstride = t < 16 ? kBSA : kBZA;
+            f32x4 acc = zero4();
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
+            for (int kb = 0; kb < 4; ++kb)
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(src[(4 * kb + g) * bstride], wf[kb], acc, 0, 0, 0);
+            bf16x4 h, l;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int i = 16 * rt + 4 * g + r;
-                if (rt < rtn && i < M) lds[i * STR + c] = acc[rt][r];
+                const bf16pair p = split_bf16(acc[r]);
+                h[r] = p.hi;
+                l[r] = p.lo;
             }
-    }
-    __syncthreads();
-
-    // ---- 3. output of every query block for this slice ----
-    for (int j0 = 0; j0 < nb; j0 += 4) {
-        uint16_t qr[4][FL];
-        if (j0 == 0) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-#pragma unroll
-                for (int f = 0; f < FL; ++f) qr[u][f] = qpre[u][f];
-        } else {
-            load_q(j0, qr);
-            issue_fence();
+            if (t < 16) {
+                Bhi[n * (kBSB / 2) + g * 16 + t] = __builtin_bit_cast(uint2, h);
+                Blo[n * (kBSB / 2) + g * 16 + t] = __builtin_bit_cast(uint2, l);
+            } else {
+                Zhi[n * (kBZB / 2) + g] = __builtin_bit_cast(uint2, h);
+                Zlo[n * (kBZB / 2) + g] = __builtin_bit_cast(uint2, l);
+            }
         }
+        __syncthreads();
+
+        // 3. output: D[column P (4g + r) + c][token n] += sum_m S~_i[P m + ia][.] phi(q_n)[P m + ia]
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            if (j0 + u < nb) {  // uniform
-                const int i = wave + 4 * (j0 + u);
-                const float* row = lds + i * STR;
-                bf16x8 aq[KS], bh[KS], bl[KS];
-                float den = 0.f;
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int fl = 8 * ks + e;
-                        const bf16pair p = split_bf16(fl < FL ? row[(FL * g + fl) * 16 + n] : 0.f);
-                        bh[ks][e] = p.hi;
-                        bl[ks][e] = p.lo;
-                        const __bf16 ph =
-                            (__bf16)((fl < FL && n < C) ? phi_fast(bf16_to_f32(qr[u][fl < FL ? fl : 0])) : 0.f);
-                        aq[ks][e] = ph;
-                        if (fl < FL) den = fmaf(bf16v_to_f32(ph), row[16 * D + FL * g + fl], den);
-                    }
-                den = sum_over_groups(den) + kEps;
-                f32x4 acc = zero4();
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    acc = mfma32(aq[ks], bh[ks], acc);
-                    acc = mfma32(aq[ks], bl[ks], acc);
+        for (int j = 0; j < BPW; ++j) {
+            const int b = wave + kWaves * j;
+            if (b < M) {  // uniform
+                const bf16x4 sh = __builtin_bit_cast(bf16x4, Bhi[b * (kBSB / 2) + g * 16 + n]);
+                const bf16x4 sl = __builtin_bit_cast(bf16x4, Blo[b * (kBSB / 2) + g * 16 + n]);
+                oacc[j][c] = mfma16(sh, bq[j][ia], oacc[j][c]);
+                oacc[j][c] = mfma16(sl, bq[j][ia], oacc[j][c]);
+                if (c == 0) {
+                    const bf16x4 zh = __builtin_bit_cast(bf16x4, Zhi[b * (kBZB / 2) + g]);
+                    const bf16x4 zl = __builtin_bit_cast(bf16x4, Zlo[b * (kBZB / 2) + g]);
+                    dacc[j] = mfma16(zh, bq[j][ia], dacc[j]);
+                    dacc[j] = mfma16(zl, bq[j][ia], dacc[j]);
                 }
-                const float rden = fast_rcp(den);
+            }
+        }
+        // The next sub-tile's step 1 overwrites only the S and z sub-tiles, whose
+        // last reader (step 2) finished before the barrier above.
+    }
+
+    // ---- y = numerator / (den + 1e-6): lane (g, n) holds columns 4Pg .. 4Pg + 4P - 1 of token n ----
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float rr = __shfl(rden, 4 * g + r, 64);
-                    if (4 * g + r < C) Yp[(i * C + 4 * g + r) * D + col0 + n] = acc[r] * rr;
+    for (int j = 0; j < BPW; ++j) {
+        const int b = wave + kWaves * j;
+        if (b < M && (FULL || n < C)) {
+            const float rden = fast_rcp(dacc[j][0] + kEps);
+            float* dst = Y + (pair * N + b * C + n) * D + 4 * P * g;
+#pragma unroll
+            for (int h = 0; h < P; ++h) {
+                f32x4 o;
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const int col = 4 * h + x;  // = P r + c
+                    o[x] = oacc[j][col % P][col / P] * rden;
                 }
+                *reinterpret_cast<f32x4*>(dst + 4 * h) = o;
             }
         }
     }
 }
 
 bool fused_applicable(int D, int64_t BH, int64_t N, int64_t M) {
-    const int64_t C = N / M;
-    // Blocks of at most 16 tokens (summaries outweigh the tokens; one MFMA k-step
-    // and one query tile per block), all rows in LDS, and enough workgroups
-    // (BH * d/16) to fill the chip.
-    return M <= fused_max_blocks(D) && C <= 16 && BH * (D / 16) >= 256;
+    (void)D;
+    (void)BH;
+    // Blocks of at most 16 tokens (one 16-deep k-step and one query tile per
+    // block) and at most 16 blocks (one 16-row tile of W).
+    return M <= kMaxBlocks && N / M <= 16;
 }
 
 hipError_t launch_fused(const void* q, const void* k, const void* v, const float* W, float* out, int64_t BH,
                         int64_t N, int D, int64_t M, hipStream_t stream) {
-    const int P = D / 16;
-    const size_t lds = fused_lds_bytes(D, M);
-    hipError_t e = hipSuccess;
-    switch (D) {  // allow more than the default 64 KiB of dynamic LDS
-        case 16: e = hipFuncSetAttribute((const void*)fused_small_kernel<16>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); break;
-        case 32: e = hipFuncSetAttribute((const void*)fused_small_kernel<32>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); break;
-        case 64: e = hipFuncSetAttribute((const void*)fused_small_kernel<64>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); break;
-        default: return hipErrorInvalidValue;
-    }
-    if (e != hipSuccess) return e;
-    const dim3 grid((unsigned)(((BH + 7) / 8) * 8 * P));
+    const bool full = N / M == 16;
     const uint16_t* qq = (const uint16_t*)q;
     const uint16_t* kk = (const uint16_t*)k;
     const uint16_t* vv = (const uint16_t*)v;
+    const dim3 grid((unsigned)BH), block(64 * kWaves);
+#define MHLA_FUSED_CASE(DD)                                                                              \
+    case DD:                                                                                             \
+        if (full)                                                                                        \
+            fused_small_kernel<DD, true><<<grid, block, 0, stream>>>(qq, kk, vv, W, out, (int)N, (int)M);  \
+        else                                                                                             \
+            fused_small_kernel<DD, false><<<grid, block, 0, stream>>>(qq, kk, vv, W, out, (int)N, (int)M); \
+        break;
     switch (D) {
-        case 16: fused_small_kernel<16><<<grid, dim3(256), lds, stream>>>(qq, kk, vv, W, out, BH, (int)N, (int)M); break;
-        case 32: fused_small_kernel<32><<<grid, dim3(256), lds, stream>>>(qq, kk, vv, W, out, BH, (int)N, (int)M); break;
-        case 64: fused_small_kernel<64><<<grid, dim3(256), lds, stream>>>(qq, kk, vv, W, out, BH, (int)N, (int)M); break;
+        MHLA_FUSED_CASE(16)
+        MHLA_FUSED_CASE(32)
+        MHLA_FUSED_CASE(64)
         default: return hipErrorInvalidValue;
     }
+#undef MHLA_FUSED_CASE
     return hipGetLastError();
 }
 
