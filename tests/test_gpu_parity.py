@@ -139,6 +139,34 @@ def test_fused_path(orc, case):
     check(w, q, k, v, W, orc, "fused")
 
 
+def test_fused_graph_replay(orc):
+    """The fused forward captured into a HIP graph: every replay, with eager work
+    and synchronisations in between, equals the eager result bit for bit."""
+    w = WORKLOADS["dit_s2_256"].shrink(B=8, seed=4100)
+    q, k, v, W = make_inputs(w)
+    assert mh.mhla_forward_path(w.B, w.H, w.N, w.d, w.M) == mh.MHLA_PATH_FUSED
+    qd, kd, vd = (to_dev(a, "bf16") for a in (q, k, v))
+    Wd = torch.from_numpy(W).cuda()
+    eager = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    mh.mhla_forward(qd, kd, vd, Wd, eager)
+    torch.cuda.synchronize()
+    ref = orc.forward(q, k, v, W, causal=False, nthreads=NTHREADS)
+    assert rel(eager.cpu().numpy(), ref) <= TOL["bf16"]
+    out = torch.empty_like(eager)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        mh.mhla_forward(qd, kd, vd, Wd, out)
+    other = torch.empty_like(eager)
+    for rep in range(4):
+        say(f"[graph] replay {rep}")
+        out.fill_(float("nan"))
+        mh.mhla_forward(kd, qd, vd, Wd, other)  # eager work on the same buffers' neighbours
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), rep
+
+
 def staged_forward(q, k, v, W, causal, dtype):
     """The three stage entry points chained by hand (the staged path end to end)."""
     B, H, N, d = q.shape

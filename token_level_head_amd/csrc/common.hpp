@@ -27,11 +27,16 @@ __device__ __forceinline__ float bf16v_to_f32(__bf16 b) {
     return __uint_as_float((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
-// phi(x) = ELU(x) + 1 ("Linear Attention 笔记" §2), written as max(x, 0) + exp(min(x, 0)):
-// the same value on both branches (exp(0) = 1) without a compare and select.  The
-// fast exp is used where the result is rounded to bfloat16 afterwards;
+// phi(x) = ELU(x) + 1 ("Linear Attention 笔记" §2) = max(x, 0) + exp(min(x, 0)).
+// phi_fast is for results rounded to bfloat16 afterwards: with y = x log2(e),
+// phi = 2^min(y, 0) + max(y, 0) ln(2), i.e. one multiply, a min, a max, the
+// hardware exp2 and one fma, with no compare and select.  (min and max act on y,
+// the result of an arithmetic op, so they need no quieting of a raw input.)
 // phi_precise keeps float32 accuracy.
-__device__ __forceinline__ float phi_fast(float x) { return fmaxf(x, 0.f) + __expf(fminf(x, 0.f)); }
+__device__ __forceinline__ float phi_fast(float x) {
+    const float y = x * 1.44269504088896341f;
+    return fmaf(fmaxf(y, 0.f), 0.693147180559945309f, __builtin_amdgcn_exp2f(fminf(y, 0.f)));
+}
 __device__ __forceinline__ float phi_precise(float x) { return fmaxf(x, 0.f) + expf(fminf(x, 0.f)); }
 
 // Hardware reciprocal (about 1 ulp).  Every denominator here is >= 1e-6 and finite.
@@ -45,6 +50,29 @@ struct bf16pair {
 __device__ __forceinline__ bf16pair split_bf16(float x) {
     const __bf16 hi = (__bf16)x;
     return {hi, (__bf16)(x - bf16v_to_f32(hi))};
+}
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats to packed bf16 (round-to-nearest-even), a in the low half: one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
+// split_bf16 of two values at once, packed: hi = bf16(a) | bf16(b) << 16, lo likewise
+// from a - hi_a and b - hi_b.  Each difference is exact in float32 and is formed
+// by one bf16 dot product (hi . (-1, 0) + a), so the split costs two conversions
+// and two dot products per pair.  The (-1, 0) and (0, -1) operands are kept in
+// registers: folded to the inline constant -1.0, the packed bf16 operand reads as
+// the float32 bit pattern of -1.0, i.e. (0, -1), and the wrong half is subtracted.
+__device__ __forceinline__ void split2_bf16(float a, float b, uint32_t& hi, uint32_t& lo) {
+    hi = pack_bf16(a, b);
+    const bf16x2 h = __builtin_bit_cast(bf16x2, hi);
+    uint32_t m0 = 0x0000bf80u, m1 = 0xbf800000u;  // (-1, 0), (0, -1) as packed bf16
+    asm("" : "+v"(m0), "+v"(m1));
+    lo = pack_bf16(__builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2, m0), a, false),
+                   __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2, m1), b, false));
 }
 
 __device__ __forceinline__ f32x4 mfma32(const bf16x8& a, const bf16x8& b, const f32x4& c) {

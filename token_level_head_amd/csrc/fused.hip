@@ -14,18 +14,21 @@
 // P*m + ia and columns P*n + c, the lane layout of the summary MFMA), each in
 // three barrier-separated steps through LDS:
 //   1. every wave computes the sub-tile of S_b for its blocks (one 16x16x16 bf16
-//      MFMA: tokens along k) and, for c == 0, z_b (an MFMA against ones);
-//   2. the 16 entry tiles (+ the z tile) of the sub-tile are mixed,
-//      S~_i = sum_b W[i, b] S_b, on float32 MFMA (16x16x4, blocks along k:
-//      exact products); each result is split into bf16 hi + lo for step 3;
+//      MFMA, tokens along k) and, for c == 0, z_b (an MFMA against ones), and
+//      stores them as float32;
+//   2. the sub-tile's 16 column tiles (+ the z tile) are mixed,
+//      S~_i = sum_b W[i, b] S_b, with blocks along k: S and W split into bf16
+//      hi + lo, three MFMAs (hi.hi + lo.hi + hi.lo); the result is split into
+//      hi + lo again for step 3;
 //   3. every wave adds phi(Q_i) S~_i (sub-tile) into its output accumulators
-//      (2 bf16 MFMAs: hi and lo) and, for c == 0, phi(Q_i) z~_i into the
-//      denominator (an MFMA whose A rows all equal z~_i).
+//      (MFMAs on hi and lo) and, for c == 0, phi(Q_i) z~_i into the denominator
+//      (an MFMA whose A rows all equal z~_i).
 // The output MFMA puts value columns on rows and tokens on columns, so after the
 // last sub-tile each lane holds 4P consecutive columns of one token; it scales
 // them by 1 / (den + 1e-6) and writes them with 16-byte stores.  K, V, Q and W
 // are read with buffer loads (scalar descriptor, 32-bit offsets; an offset past
-// the end reads zero).
+// the end reads zero).  Blocks M .. 15 run through the same steps on zero K/V
+// (finite summaries) and carry zero mixing weight.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -36,24 +39,27 @@ namespace {
 constexpr int kMaxBlocks = 16;  // M: one 16-row MFMA tile of W and S~
 constexpr int kWaves = 8;
 constexpr int kBlocksPerWave = kMaxBlocks / kWaves;
-// LDS layout, in 4-byte words.  Strides are chosen so that every LDS access of
-// the three steps touches 64 distinct banks per wave (or, for 8-byte accesses,
-// 64 distinct banks per half wave).
-constexpr int kRSA = 20;              // S sub-tile: one feature row of 16 columns (+4)
-constexpr int kBSA = 16 * kRSA + 1;   // S sub-tile: one block (= 1 mod 4)
-constexpr int kBSB = 130;             // S~ hi (and lo): one query block, [4 feature quads][16 columns] x 2 words
-constexpr int kBZA = 16;              // z sub-tile: one block
-constexpr int kBZB = 12;              // z~ hi (and lo): one query block, 4 feature quads x 2 words
+// LDS layout, in 4-byte words.  Strides are chosen so that the accesses of the
+// three steps hit distinct banks.
+constexpr int kRSA = 20;             // S sub-tile: one value column, 16 features (+4)
+constexpr int kBSA = 16 * kRSA + 4;  // S sub-tile: one block (4 blocks apart = 16 banks apart)
+constexpr int kBSB = 130;            // S~ hi (and lo): one query block, [4 feature quads][16 columns] x 2 words
+constexpr int kBZA = 20;             // z sub-tile: one block
+constexpr int kBZB = 12;             // z~ hi (and lo): one query block, 4 feature quads x 2 words
 constexpr int kLdsWords = kMaxBlocks * kBSA + 2 * kMaxBlocks * kBSB + kMaxBlocks * kBZA + 2 * kMaxBlocks * kBZB;
 
 __device__ __forceinline__ float half_to_f32(uint32_t word, int half) {
     return __uint_as_float(half ? (word & 0xffff0000u) : (word << 16));
 }
 
+__device__ __forceinline__ bf16x4 as_bf16x4(uint32_t lo_pair, uint32_t hi_pair) {
+    return __builtin_bit_cast(bf16x4, u32x2{lo_pair, hi_pair});
+}
+
 }  // namespace
 
 template <int D, bool FULL>
-__global__ __launch_bounds__(512) void fused_small_kernel(const uint16_t* __restrict__ Q,
+__global__ __launch_bounds__(64 * kWaves) void fused_small_kernel(const uint16_t* __restrict__ Q,
                                                           const uint16_t* __restrict__ K,
                                                           const uint16_t* __restrict__ V,
                                                           const float* __restrict__ W, float* __restrict__ Y,
@@ -61,24 +67,21 @@ __global__ __launch_bounds__(512) void fused_small_kernel(const uint16_t* __rest
     constexpr int P = D / 16;
     constexpr int BPW = kBlocksPerWave;
     __shared__ __align__(16) float lds[kLdsWords];
-    float* A = lds;                                           // [16 blocks][16 features][kRSA]
+    float* A = lds;                                                  // [16 blocks][16 columns][kRSA]
     uint2* Bhi = reinterpret_cast<uint2*>(lds + kMaxBlocks * kBSA);  // [16 query blocks][kBSB / 2]
     uint2* Blo = Bhi + kMaxBlocks * kBSB / 2;
     float* Az = reinterpret_cast<float*>(Blo + kMaxBlocks * kBSB / 2);  // [16 blocks][kBZA]
     uint2* Zhi = reinterpret_cast<uint2*>(Az + kMaxBlocks * kBZA);      // [16 query blocks][kBZB / 2]
     uint2* Zlo = Zhi + kMaxBlocks * kBZB / 2;
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, n = lane & 15;
     const int64_t pair = blockIdx.x;
     const int C = FULL ? 16 : N / M;  // tokens per block, <= 16
 
-    // Blocks M .. 15 take part in the mixing MFMAs with weight zero: clear their rows.
-    for (int x = threadIdx.x; x < (kMaxBlocks - M) * kBSA; x += 512) A[M * kBSA + x] = 0.f;
-    for (int x = threadIdx.x; x < (kMaxBlocks - M) * kBZA; x += 512) Az[M * kBZA + x] = 0.f;
-
     // ---- loads: K and V (lane: P features / columns of tokens 4g .. 4g+3), Q (lane:
-    // features 4Pg .. 4Pg + 4P - 1 of token n), W (lane: W[n][4kb + g]) ----
+    // features 4Pg .. 4Pg + 4P - 1 of token n), W (lane: W[n][4g + e]) ----
     const uint32_t pair_bytes = (uint32_t)N * D * 2;
     const rsrc_t rK = make_rsrc(K + pair * N * D, pair_bytes);
     const rsrc_t rV = make_rsrc(V + pair * N * D, pair_bytes);
@@ -114,31 +117,38 @@ __global__ __launch_bounds__(512) void fused_small_kernel(const uint16_t* __rest
             qw[j][0] = u32x4{x.x, x.y, 0u, 0u};
         }
     }
-    float wf[4];
+    float wv[4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-        const int b = 4 * kb + g;
-        wf[kb] = __uint_as_float(buf_load32(rW, off_if(n < M && b < M, (uint32_t)(n * M + b) * 4)));
+    for (int e = 0; e < 4; ++e) {
+        const int b = 4 * g + e;
+        wv[e] = __uint_as_float(buf_load32(rW, off_if(n < M && b < M, (uint32_t)(n * M + b) * 4)));
     }
     issue_fence();
 
-    // ---- phi(k) as the summary MFMA's A operand: ak[j][ia][e] = phi(K[4g + e][P n + ia]);
-    // phi(q) as the output MFMA's B operand: bq[j][ia][e] = phi(Q[n][P (4g + e) + ia]) ----
+    // Mixing B operand: W[i = n][b = 4g + e] split into hi + lo.
+    uint32_t w01h, w01l, w23h, w23l;
+    split2_bf16(wv[0], wv[1], w01h, w01l);
+    split2_bf16(wv[2], wv[3], w23h, w23l);
+    const bf16x4 wh = as_bf16x4(w01h, w23h), wl = as_bf16x4(w01l, w23l);
+
+    // phi(k) as the summary MFMA's A operand: ak[j][ia][e] = phi(K[4g + e][P n + ia]);
+    // phi(q) as the output MFMA's B operand: bq[j][ia][e] = phi(Q[n][P (4g + e) + ia]).
     bf16x4 ak[BPW][P], bq[BPW][P];
 #pragma unroll
     for (int j = 0; j < BPW; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const bool ok = FULL || 4 * g + e < C;
+        for (int ia = 0; ia < P; ++ia) {
+            float fk[4], fq[4];
 #pragma unroll
-            for (int ia = 0; ia < P; ++ia) {
+            for (int e = 0; e < 4; ++e) {
                 const uint32_t kword = (P == 4 && ia >= 2) ? kw[j][e].y : kw[j][e].x;
-                const float x = half_to_f32(kword, P == 1 ? 0 : ia & 1);
-                ak[j][ia][e] = (__bf16)(ok ? phi_fast(x) : 0.f);
+                const float pk = phi_fast(half_to_f32(kword, P == 1 ? 0 : ia & 1));
+                fk[e] = (FULL || 4 * g + e < C) ? pk : 0.f;
                 const int fl = P * e + ia;
-                const uint32_t qword = qw[j][fl / 8][(fl % 8) / 2];
-                bq[j][ia][e] = (__bf16)phi_fast(half_to_f32(qword, fl & 1));
+                fq[e] = phi_fast(half_to_f32(qw[j][fl / 8][(fl % 8) / 2], fl & 1));
             }
+            ak[j][ia] = as_bf16x4(pack_bf16(fk[0], fk[1]), pack_bf16(fk[2], fk[3]));
+            bq[j][ia] = as_bf16x4(pack_bf16(fq[0], fq[1]), pack_bf16(fq[2], fq[3]));
         }
 
     const bf16x4 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
@@ -150,77 +160,81 @@ __global__ __launch_bounds__(512) void fused_small_kernel(const uint16_t* __rest
         for (int c = 0; c < P; ++c) oacc[j][c] = zero4();
     }
 
+    // Per-lane LDS bases (words / uint2 units); everything else is an immediate offset.
+    float* const a_wr = A + n * kRSA + 4 * g;              // step 1: S_b[4g .. 4g+3][column n]
+    const float* const a_rd = A + 4 * g * kBSA + n;        // step 2: S_{4g + e}[column t][feature n]
+    float* const z_wr = Az + 4 * g;                        // step 1: z_b[4g .. 4g+3]
+    const float* const z_rd = Az + 4 * g * kBZA + n;       // step 2: z_{4g + e}[feature n]
+    const int b_wr = n * (kBSB / 2) + g * 16;              // step 2: S~_{i = n}[quad g][column t]
+    const int z_wr2 = n * (kBZB / 2) + g;                  // step 2: z~_{i = n}[quad g]
+
 #pragma unroll
     for (int s = 0; s < P * P; ++s) {
         const int c = s / P, ia = s % P;
-        // 1. sub-tile (ia, c) of S_b: lane (g, n) gets S_b[P (4g + r) + ia][P n + c]
+        // 1. sub-tile (ia, c) of S_b: lane (g, n) gets S_b[P (4g + r) + ia][P n + c], r = 0..3
 #pragma unroll
         for (int j = 0; j < BPW; ++j) {
             const int b = wave + kWaves * j;
-            if (b < M) {  // uniform
-                bf16x4 bv;
+            uint32_t v01, v23;
+            {
+                uint32_t h[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const uint32_t vword = (P == 4 && c >= 2) ? vw[j][e].y : vw[j][e].x;
-                    bv[e] = bits_to_bf16((uint16_t)((P > 1 && (c & 1)) ? vword >> 16 : vword));
+                    h[e] = (P > 1 && (c & 1)) ? vword >> 16 : vword & 0xffffu;
                 }
-                const f32x4 sa = mfma16(ak[j][ia], bv, zero4());
-                float* dst = A + b * kBSA + 4 * g * kRSA + n;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) dst[r * kRSA] = sa[r];
-                if (c == 0) {
-                    const f32x4 za = mfma16(ak[j][ia], ones, zero4());
-                    if (n == 0) {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) Az[b * kBZA + 4 * g + r] = za[r];
-                    }
-                }
+                v01 = h[0] | (h[1] << 16);
+                v23 = h[2] | (h[3] << 16);
+            }
+            const f32x4 sa = mfma16(ak[j][ia], as_bf16x4(v01, v23), zero4());
+            *reinterpret_cast<f32x4*>(a_wr + b * kBSA) = sa;
+            if (c == 0) {
+                const f32x4 za = mfma16(ak[j][ia], ones, zero4());
+                if (n == 0) *reinterpret_cast<f32x4*>(z_wr + b * kBZA) = za;
             }
         }
         __syncthreads();
 
-        // 2. mixing: tile t < 16 is value column P t + c of the sub-tile, tile 16 is z.
-        //    Lane (g, n) gets S~_{i = n}[feature P (4g + r) + ia][column P t + c].
-        const int ntile = c == 0 ? 17 : 16;
-        for (int t = wave; t < ntile; t += kWaves) {  // uniform
-            const float* src = t < 16 ? A + n * kRSA + t : Az + n;
-            const int bstride = t < 16 ? kBSA : kBZA;
-            f32x4 acc = zero4();
+        // 2. mixing.  Column tile t < 16 (value column P t + c), and for c == 0 the z
+        //    tile: lane (g, n) gets S~_{i = n}[feature P (4g + r) + ia][.], r = 0..3.
+        auto mix_tile = [&](const float* src, int bstride, uint2* hi_dst, uint2* lo_dst) {
+            float x[4];
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(src[(4 * kb + g) * bstride], wf[kb], acc, 0, 0, 0);
-            bf16x4 h, l;
+            for (int e = 0; e < 4; ++e) x[e] = src[e * bstride];
+            uint32_t h01, l01, h23, l23;
+            split2_bf16(x[0], x[1], h01, l01);
+            split2_bf16(x[2], x[3], h23, l23);
+            const bf16x4 sh = as_bf16x4(h01, h23), sl = as_bf16x4(l01, l23);
+            f32x4 acc = mfma16(sh, wh, zero4());
+            acc = mfma16(sl, wh, acc);
+            acc = mfma16(sh, wl, acc);
+            uint32_t o01h, o01l, o23h, o23l;
+            split2_bf16(acc[0], acc[1], o01h, o01l);
+            split2_bf16(acc[2], acc[3], o23h, o23l);
+            *hi_dst = uint2{o01h, o23h};
+            *lo_dst = uint2{o01l, o23l};
+        };
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const bf16pair p = split_bf16(acc[r]);
-                h[r] = p.hi;
-                l[r] = p.lo;
-            }
-            if (t < 16) {
-                Bhi[n * (kBSB / 2) + g * 16 + t] = __builtin_bit_cast(uint2, h);
-                Blo[n * (kBSB / 2) + g * 16 + t] = __builtin_bit_cast(uint2, l);
-            } else {
-                Zhi[n * (kBZB / 2) + g] = __builtin_bit_cast(uint2, h);
-                Zlo[n * (kBZB / 2) + g] = __builtin_bit_cast(uint2, l);
-            }
+        for (int j = 0; j < 16 / kWaves; ++j) {
+            const int t = wave + kWaves * j;
+            mix_tile(a_rd + t * kRSA, kBSA, Bhi + b_wr + t, Blo + b_wr + t);
         }
+        if (c == 0 && wave == ia) mix_tile(z_rd, kBZA, Zhi + z_wr2, Zlo + z_wr2);
         __syncthreads();
 
         // 3. output: D[column P (4g + r) + c][token n] += sum_m S~_i[P m + ia][.] phi(q_n)[P m + ia]
 #pragma unroll
         for (int j = 0; j < BPW; ++j) {
             const int b = wave + kWaves * j;
-            if (b < M) {  // uniform
-                const bf16x4 sh = __builtin_bit_cast(bf16x4, Bhi[b * (kBSB / 2) + g * 16 + n]);
-                const bf16x4 sl = __builtin_bit_cast(bf16x4, Blo[b * (kBSB / 2) + g * 16 + n]);
-                oacc[j][c] = mfma16(sh, bq[j][ia], oacc[j][c]);
-                oacc[j][c] = mfma16(sl, bq[j][ia], oacc[j][c]);
-                if (c == 0) {
-                    const bf16x4 zh = __builtin_bit_cast(bf16x4, Zhi[b * (kBZB / 2) + g]);
-                    const bf16x4 zl = __builtin_bit_cast(bf16x4, Zlo[b * (kBZB / 2) + g]);
-                    dacc[j] = mfma16(zh, bq[j][ia], dacc[j]);
-                    dacc[j] = mfma16(zl, bq[j][ia], dacc[j]);
-                }
+            const uint2 sh = Bhi[b * (kBSB / 2) + g * 16 + n];
+            const uint2 sl = Blo[b * (kBSB / 2) + g * 16 + n];
+            oacc[j][c] = mfma16(as_bf16x4(sh.x, sh.y), bq[j][ia], oacc[j][c]);
+            oacc[j][c] = mfma16(as_bf16x4(sl.x, sl.y), bq[j][ia], oacc[j][c]);
+            if (c == 0) {
+                const uint2 zh = Zhi[b * (kBZB / 2) + g];
+                const uint2 zl = Zlo[b * (kBZB / 2) + g];
+                dacc[j] = mfma16(as_bf16x4(zh.x, zh.y), bq[j][ia], dacc[j]);
+                dacc[j] = mfma16(as_bf16x4(zl.x, zl.y), bq[j][ia], dacc[j]);
             }
         }
         // The next sub-tile's step 1 overwrites only the S and z sub-tiles, whose
