@@ -95,6 +95,7 @@ SWEEP = [  # (B, H, N, d, M, causal, dtype)
     (1, 2, 1536, 64, 3, False, "bf16"),  # C = 512: split summaries
     (1, 2, 1536, 64, 3, True, "bf16"),
     (2, 2, 768, 32, 3, True, "bf16"),   # C = 256, d = 32
+    (1, 2, 750, 64, 3, True, "bf16"),   # C = 250: 16 causal tiles, ragged last tile
     (1, 1, 300, 64, 300, False, "f32"),  # M > 256: several mixing row groups
     (1, 1, 600, 32, 300, True, "bf16"),
     (1, 1, 2048, 16, 2048, False, "bf16"),  # mixing fragments beyond LDS: global-fragment kernel

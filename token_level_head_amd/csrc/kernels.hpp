@@ -27,6 +27,12 @@ hipError_t launch_output(int dtype, const void* q, const void* k, const void* v,
                          const float* W, float* out, int64_t BH, int64_t N, int D, int64_t M, bool causal,
                          hipStream_t stream);
 
+// Causal bf16 output for blocks of at most 256 tokens: the within-block prefix as one
+// masked C x C product per block (used by launch_output when applicable).
+bool causal_quad_applicable(int64_t C);
+hipError_t launch_causal_quad(const void* q, const void* k, const void* v, const float* St, const float* W,
+                              float* out, int64_t BH, int64_t N, int D, int64_t M, hipStream_t stream);
+
 // Fused path (non-causal bf16, short blocks): the whole pass in one kernel with
 // the summaries in LDS; needs no workspace.
 bool fused_applicable(int D, int64_t BH, int64_t N, int64_t M);

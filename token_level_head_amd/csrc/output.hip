@@ -387,6 +387,8 @@ hipError_t launch_output(int dtype, const void* q, const void* k, const void* v,
     const uint16_t* qq = (const uint16_t*)q;
     const uint16_t* kk = (const uint16_t*)k;
     const uint16_t* vv = (const uint16_t*)v;
+    if (causal && causal_quad_applicable(N / M))
+        return launch_causal_quad(q, k, v, St, W, out, BH, N, D, M, stream);
     if (causal) {  // d/16 waves per block, 4 / (d/16) blocks per workgroup
         const int bpw = 4 / (D / 16);
         const dim3 grid((unsigned)((BH * M + bpw - 1) / bpw));

@@ -5,52 +5,79 @@
 // bf16 path.  S_b = phi(K_b)^T V_b is a d x d product whose reduction runs over
 // tokens, while K and V are stored token-major.  Instead of transposing tiles
 // through LDS, each lane loads P = d/16 consecutive features of 8 tokens (one
-// 8-byte load per token for d = 64; 16 lanes cover a whole 128-byte row) and
+// 8-byte load per token for d = 64; 16 lanes cover a whole 128-byte row; lane
+// group g takes tokens t + 4e + g, so each load instruction reads four
+// consecutive rows) and
 // repacks them in registers: MFMA (ia, ib) of the P x P set treats its row m as
 // feature P*m + ia and its column n as value column P*n + ib.  The accumulators
 // then hold S in the packed layout of common.hpp, which is written with
 // full-wave 1 KiB stores.  phi(k) is rounded to bf16 once; the same rounded
-// values feed both S_b and z_b so numerator and denominator stay consistent.
-// Accumulation is float32 in the MFMA accumulators.
+// values feed both S_b (MFMA) and z_b (bf16 dot products against (1, 1)), so
+// numerator and denominator stay consistent.  Accumulation is float32.
+//
+// K and V are read through one buffer descriptor per (batch, head) pair with
+// 32-bit offsets; a token past the segment gets an out-of-range offset and reads
+// zero.  Only the last 32-token step of a segment needs the phi mask.
 //
 // A block of C tokens may be split over `wpb` waves of one workgroup
-// (wpb in {1, 2, 4}); their partial sums are added in LDS in a fixed order, so
-// results do not depend on scheduling.
+// (wpb in {1, 2, 4}, chosen so that enough waves exist); their partial sums are
+// added in LDS in a fixed order, so results do not depend on scheduling.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace mhla {
 
 template <int P>
-__device__ __forceinline__ void load_feat(const uint16_t* p, bool ok, const uint16_t* safe, uint16_t (&out)[P]) {
-    if constexpr (P == 4) {
-        const uint2 x = load_or_zero(reinterpret_cast<const uint2*>(p), ok, reinterpret_cast<const uint2*>(safe));
-        out[0] = (uint16_t)x.x; out[1] = (uint16_t)(x.x >> 16);
-        out[2] = (uint16_t)x.y; out[3] = (uint16_t)(x.y >> 16);
-    } else if constexpr (P == 2) {
-        const uint32_t x = load_or_zero(reinterpret_cast<const uint32_t*>(p), ok, reinterpret_cast<const uint32_t*>(safe));
-        out[0] = (uint16_t)x; out[1] = (uint16_t)(x >> 16);
-    } else {
-        out[0] = load_or_zero(p, ok, safe);
-    }
+struct TokenWords;  // raw bits of P consecutive bf16 features of one token
+template <>
+struct TokenWords<4> { typedef u32x2 type; };
+template <>
+struct TokenWords<2> { typedef uint32_t type; };
+template <>
+struct TokenWords<1> { typedef uint16_t type; };
+
+template <int P>
+__device__ __forceinline__ typename TokenWords<P>::type load_token(rsrc_t r, uint32_t off) {
+    if constexpr (P == 4) return buf_load64(r, off);
+    else if constexpr (P == 2) return buf_load32(r, off);
+    else return buf_load16(r, off);
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void summaries_bf16_kernel(const uint16_t* __restrict__ K,
-                                                             const uint16_t* __restrict__ V,
-                                                             float* __restrict__ S, int64_t BH, int64_t N,
-                                                             int64_t M, int wpb) {
+// Feature f (< P) of a token's raw bits, as a float.
+template <int P>
+__device__ __forceinline__ float token_feature(const typename TokenWords<P>::type& w, int f) {
+    if constexpr (P == 4) return __uint_as_float((f & 1) ? ((f < 2 ? w.x : w.y) & 0xffff0000u) : ((f < 2 ? w.x : w.y) << 16));
+    else if constexpr (P == 2) return __uint_as_float((f & 1) ? (w & 0xffff0000u) : (w << 16));
+    else return __uint_as_float((uint32_t)w << 16);
+}
+
+// Raw bf16 bits of feature f (< P) of a token.
+template <int P>
+__device__ __forceinline__ uint32_t token_bits(const typename TokenWords<P>::type& w, int f) {
+    if constexpr (P == 4) return (f & 1) ? ((f < 2 ? w.x : w.y) >> 16) : ((f < 2 ? w.x : w.y) & 0xffffu);
+    else if constexpr (P == 2) return (f & 1) ? (w >> 16) : (w & 0xffffu);
+    else return w;
+}
+
+template <int D, bool PIPE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void summaries_bf16_kernel(
+    const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, float* __restrict__ S, int64_t BH, int N, int M,
+    int wpb) {
     constexpr int P = D / 16;
     constexpr int L = D * D + D;
-    extern __shared__ float red[];  // (4 - 4/wpb) partial results of 64 lanes x (4P^2 + P) floats
+    typedef typename TokenWords<P>::type TW;
+    extern __shared__ float red[];  // (4 - 4/wpb) partials of 64 lanes x (4 P^2 + P) floats
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, n = lane & 15;
     const int per_wg = 4 / wpb;
     const int64_t unit = (int64_t)blockIdx.x * per_wg + wave / wpb;  // unit = pair * M + block
     const int seg = wave % wpb;
     const bool active = unit < BH * M;
-    const int64_t C = N / M;
+    const int C = N / M;
 
     f32x4 acc[P][P];
 #pragma unroll
@@ -60,42 +87,97 @@ __global__ __launch_bounds__(256) void summaries_bf16_kernel(const uint16_t* __r
     float zacc[P];
 #pragma unroll
     for (int a = 0; a < P; ++a) zacc[a] = 0.f;
+    uint32_t ones = 0x3f803f80u;  // (1, 1) as packed bf16, kept in a register (see split2_bf16)
+    asm("" : "+v"(ones));
 
     int64_t pair = 0, blk = 0;
     if (active) {
         pair = unit / M;
         blk = unit % M;
-        const int64_t seg_len = ((C + wpb - 1) / wpb + 31) / 32 * 32;
-        const int64_t t_beg = blk * C + seg * seg_len;
-        const int64_t t_end = min(blk * C + C, t_beg + seg_len);
-        const uint16_t* Kp = K + pair * N * D + P * n;
-        const uint16_t* Vp = V + pair * N * D + P * n;
-        for (int64_t t = t_beg; t < t_end; t += 32) {
-            uint16_t kr[8][P], vr[8][P];
+        const int seg_len = ((C + wpb - 1) / wpb + 31) / 32 * 32;
+        const int t_beg = (int)blk * C + seg * seg_len;
+        const int t_end = min((int)blk * C + C, t_beg + seg_len);
+        const uint32_t pair_bytes = (uint32_t)N * D * 2;
+        const rsrc_t rK = make_rsrc(K + pair * N * D, pair_bytes);
+        const rsrc_t rV = make_rsrc(V + pair * N * D, pair_bytes);
+        // One 32-token step: lane (g, n) holds tokens t + 4e + g, e = 0..7 (the MFMA's
+        // k index 8g + e; any token order works, as A and B use the same one).
+        auto load = [&](TW (&kr)[8], TW (&vr)[8], int t) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int64_t tok = t + 8 * g + e;
-                const bool ok = tok < t_end;
-                load_feat<P>(Kp + tok * D, ok, K, kr[e]);
-                load_feat<P>(Vp + tok * D, ok, V, vr[e]);
+                const int tok = t + 4 * e + g;
+                const uint32_t off = off_if(tok < t_end, ((uint32_t)tok * D + P * n) * 2);
+                kr[e] = load_token<P>(rK, off);
+                vr[e] = load_token<P>(rV, off);
             }
-            issue_fence();
-            bf16x8 a[P], b[P];
+        };
+        auto compute = [&](const TW (&kr)[8], const TW (&vr)[8], int t, auto masked_c) {
+            constexpr bool masked = decltype(masked_c)::value;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const bool ok = t + 8 * g + e < t_end;
+            for (int ia = 0; ia < P; ++ia) {
+                uint32_t pk[4];
 #pragma unroll
-                for (int f = 0; f < P; ++f) {
-                    const __bf16 ph = (__bf16)(ok ? phi_fast(bf16_to_f32(kr[e][f])) : 0.f);
-                    a[f][e] = ph;
-                    zacc[f] += bf16v_to_f32(ph);
-                    b[f][e] = bits_to_bf16(vr[e][f]);
+                for (int e2 = 0; e2 < 4; ++e2) {
+                    float f0 = phi_fast(token_feature<P>(kr[2 * e2], ia));
+                    float f1 = phi_fast(token_feature<P>(kr[2 * e2 + 1], ia));
+                    if constexpr (masked) {  // tokens past the segment read zero, but phi(0) = 1
+                        f0 = t + 8 * e2 + g < t_end ? f0 : 0.f;
+                        f1 = t + 8 * e2 + 4 + g < t_end ? f1 : 0.f;
+                    }
+                    pk[e2] = pack_bf16(f0, f1);
+                    zacc[ia] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[e2]),
+                                                               __builtin_bit_cast(bf16x2, ones), zacc[ia], false);
+                }
+                const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
+#pragma unroll
+                for (int ib = 0; ib < P; ++ib) {
+                    uint32_t vb[4];
+#pragma unroll
+                    for (int e2 = 0; e2 < 4; ++e2)
+                        vb[e2] = token_bits<P>(vr[2 * e2], ib) | (token_bits<P>(vr[2 * e2 + 1], ib) << 16);
+                    const bf16x8 b = __builtin_bit_cast(bf16x8, u32x4{vb[0], vb[1], vb[2], vb[3]});
+                    acc[ia][ib] = mfma32(a, b, acc[ia][ib]);
                 }
             }
-#pragma unroll
-            for (int ia = 0; ia < P; ++ia)
-#pragma unroll
-                for (int ib = 0; ib < P; ++ib) acc[ia][ib] = mfma32(a[ia], b[ib], acc[ia][ib]);
+        };
+        auto run = [&](const TW (&kr)[8], const TW (&vr)[8], int t) {
+            if (t + 32 <= t_end)
+                compute(kr, vr, t, std::false_type{});
+            else
+                compute(kr, vr, t, std::true_type{});
+        };
+        int t = t_beg;
+        if constexpr (PIPE) {
+            // Two register sets: the loads of step i + 1 are in flight while step i computes.
+            TW k0[8], v0[8], k1[8], v1[8];
+            load(k0, v0, t);
+            while (true) {
+                const bool more = t + 32 < t_end;
+                if (more) load(k1, v1, t + 32);
+                issue_fence();
+                run(k0, v0, t);
+                if (!more) break;
+                t += 32;
+                const bool more2 = t + 32 < t_end;
+                if (more2) load(k0, v0, t + 32);
+                issue_fence();
+                run(k1, v1, t);
+                if (!more2) break;
+                t += 32;
+            }
+        } else {
+            for (; t + 32 <= t_end; t += 32) {
+                TW kr[8], vr[8];
+                load(kr, vr, t);
+                issue_fence();
+                compute(kr, vr, t, std::false_type{});
+            }
+            if (t < t_end) {
+                TW kr[8], vr[8];
+                load(kr, vr, t);
+                issue_fence();
+                compute(kr, vr, t, std::true_type{});
+            }
         }
     }
     // z: sum the four token groups; lanes (., n) then hold z[P*n + f].
@@ -106,28 +188,28 @@ __global__ __launch_bounds__(256) void summaries_bf16_kernel(const uint16_t* __r
         constexpr int PER_LANE = 4 * P * P + P;
         const int unit_in_wg = wave / wpb;
         if (seg > 0) {
-            float* dst = red + ((size_t)(unit_in_wg * (wpb - 1) + seg - 1) * 64 + lane) * PER_LANE;
+            float* part = red + (size_t)((unit_in_wg * (wpb - 1) + seg - 1) * 64) * PER_LANE;
+            f32x4* dst = reinterpret_cast<f32x4*>(part);
 #pragma unroll
             for (int a = 0; a < P; ++a)
 #pragma unroll
-                for (int b = 0; b < P; ++b)
+                for (int b = 0; b < P; ++b) dst[(a * P + b) * 64 + lane] = acc[a][b];
+            float* zd = part + 4 * P * P * 64;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) dst[(a * P + b) * 4 + i] = acc[a][b][i];
-#pragma unroll
-            for (int f = 0; f < P; ++f) dst[4 * P * P + f] = zacc[f];
+            for (int f = 0; f < P; ++f) zd[f * 64 + lane] = zacc[f];
         }
         __syncthreads();
         if (seg == 0) {
             for (int s = 1; s < wpb; ++s) {
-                const float* src = red + ((size_t)(unit_in_wg * (wpb - 1) + s - 1) * 64 + lane) * PER_LANE;
+                const float* part = red + (size_t)((unit_in_wg * (wpb - 1) + s - 1) * 64) * PER_LANE;
+                const f32x4* src = reinterpret_cast<const f32x4*>(part);
 #pragma unroll
                 for (int a = 0; a < P; ++a)
 #pragma unroll
-                    for (int b = 0; b < P; ++b)
+                    for (int b = 0; b < P; ++b) acc[a][b] += src[(a * P + b) * 64 + lane];
+                const float* zs = part + 4 * P * P * 64;
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) acc[a][b][i] += src[(a * P + b) * 4 + i];
-#pragma unroll
-                for (int f = 0; f < P; ++f) zacc[f] += src[4 * P * P + f];
+                for (int f = 0; f < P; ++f) zacc[f] += zs[f * 64 + lane];
             }
         }
     }
@@ -181,7 +263,10 @@ hipError_t launch_summaries(int dtype, const void* k, const void* v, float* S, i
         return hipGetLastError();
     }
     const int64_t C = N / M;
-    const int wpb = C >= 256 ? 4 : (C >= 128 ? 2 : 1);
+    // Split blocks over 2 or 4 waves only while there are too few waves to keep
+    // the memory system busy, and each wave keeps at least two 32-token steps.
+    int wpb = 1;
+    while (wpb < 4 && units * wpb < 4096 && C >= 64 * (2 * wpb)) wpb *= 2;
     const int per_wg = 4 / wpb;
     const int64_t grid = (units + per_wg - 1) / per_wg;
     const int P = D / 16;
@@ -189,9 +274,9 @@ hipError_t launch_summaries(int dtype, const void* k, const void* v, float* S, i
     const uint16_t* kk = (const uint16_t*)k;
     const uint16_t* vv = (const uint16_t*)v;
     switch (D) {
-        case 16: summaries_bf16_kernel<16><<<dim3((unsigned)grid), dim3(256), lds, stream>>>(kk, vv, S, BH, N, M, wpb); break;
-        case 32: summaries_bf16_kernel<32><<<dim3((unsigned)grid), dim3(256), lds, stream>>>(kk, vv, S, BH, N, M, wpb); break;
-        case 64: summaries_bf16_kernel<64><<<dim3((unsigned)grid), dim3(256), lds, stream>>>(kk, vv, S, BH, N, M, wpb); break;
+        case 16: summaries_bf16_kernel<16, true><<<dim3((unsigned)grid), dim3(256), lds, stream>>>(kk, vv, S, BH, (int)N, (int)M, wpb); break;
+        case 32: summaries_bf16_kernel<32, true><<<dim3((unsigned)grid), dim3(256), lds, stream>>>(kk, vv, S, BH, (int)N, (int)M, wpb); break;
+        case 64: summaries_bf16_kernel<64, false><<<dim3((unsigned)grid), dim3(256), lds, stream>>>(kk, vv, S, BH, (int)N, (int)M, wpb); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
