@@ -40,6 +40,7 @@ def test_version_and_sizes(mhla_lib):
     assert mh.mhla_workspace_bytes(64, 6, 256, 64, 16) == 2 * 16 * 384 * (64 * 64 + 64) * 4
     assert mh.mhla_workspace_bytes(8, 16, 8192, 64, 64, 1) == 2 * 64 * 128 * (64 * 64 + 64) * 4
     assert mh.mhla_workspace_bytes(1, 6, 65536, 64, 256) == 2 * 256 * 6 * (64 * 64 + 64) * 4 + 4 * 256 * 256
+    assert mh.mhla_workspace_bytes(1, 1, 512 * 16, 16, 512) == 2 * 512 * (16 * 16 + 16) * 4 + 4 * 512 * 512
     assert mh.mhla_workspace_bytes(1, 1, 250, 64, 16) == -1
     assert mh.mhla_workspace_bytes(1, 1, 256, 24, 16) == -1
 

@@ -96,6 +96,10 @@ SWEEP = [  # (B, H, N, d, M, causal, dtype)
     (1, 2, 1536, 64, 3, True, "bf16"),
     (2, 2, 768, 32, 3, True, "bf16"),   # C = 256, d = 32
     (1, 2, 750, 64, 3, True, "bf16"),   # C = 250: 16 causal tiles, ragged last tile
+    (1, 2, 1280, 16, 80, False, "bf16"),   # 64 < M <= 128: strip mixing, two row tiles per wave
+    (1, 1, 2560, 32, 160, True, "bf16"),   # M = 160: three row tiles per wave, causal
+    (2, 1, 1536, 64, 192, False, "bf16"),  # M = 192, odd number of 32-deep k-chunks
+    (1, 1, 784, 32, 98, True, "bf16"),     # M = 98: rows of W not 16-byte aligned
     (1, 1, 300, 64, 300, False, "f32"),  # M > 256: several mixing row groups
     (1, 1, 600, 32, 300, True, "bf16"),
     (1, 1, 2048, 16, 2048, False, "bf16"),  # mixing fragments beyond LDS: global-fragment kernel
@@ -140,28 +144,36 @@ def test_fused_path(orc, case):
     check(w, q, k, v, W, orc, "fused")
 
 
-def test_fused_graph_replay(orc):
-    """The fused forward captured into a HIP graph: every replay, with eager work
-    and synchronisations in between, equals the eager result bit for bit."""
-    w = WORKLOADS["dit_s2_256"].shrink(B=8, seed=4100)
+GRAPH_CASES = [  # (workload, shrink): one fused and two staged shapes (pool workspace inside the graph)
+    ("dit_s2_256", dict(B=8)),
+    ("lm_causal_8k", dict(B=1, H=2, N=1024, M=8)),
+    ("dit_s2_4096", dict(H=2, N=4096, M=256)),
+]
+
+
+@pytest.mark.parametrize("case", GRAPH_CASES, ids=lambda c: c[0])
+def test_graph_replay(orc, case):
+    """mhla_forward captured into a HIP graph: every replay, with eager work and
+    synchronisations in between, equals the eager result bit for bit."""
+    key, kw = case
+    w = WORKLOADS[key].shrink(seed=4100 + GRAPH_CASES.index(case), **kw)
     q, k, v, W = make_inputs(w)
-    assert mh.mhla_forward_path(w.B, w.H, w.N, w.d, w.M) == mh.MHLA_PATH_FUSED
     qd, kd, vd = (to_dev(a, "bf16") for a in (q, k, v))
     Wd = torch.from_numpy(W).cuda()
     eager = torch.empty(q.shape, dtype=torch.float32, device="cuda")
-    mh.mhla_forward(qd, kd, vd, Wd, eager)
+    mh.mhla_forward(qd, kd, vd, Wd, eager, causal=w.causal)
     torch.cuda.synchronize()
-    ref = orc.forward(q, k, v, W, causal=False, nthreads=NTHREADS)
+    ref = orc.forward(q, k, v, W, causal=w.causal, nthreads=NTHREADS)
     assert rel(eager.cpu().numpy(), ref) <= TOL["bf16"]
     out = torch.empty_like(eager)
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        mh.mhla_forward(qd, kd, vd, Wd, out)
+        mh.mhla_forward(qd, kd, vd, Wd, out, causal=w.causal)
     other = torch.empty_like(eager)
     for rep in range(4):
-        say(f"[graph] replay {rep}")
+        say(f"[graph] {key} replay {rep}")
         out.fill_(float("nan"))
-        mh.mhla_forward(kd, qd, vd, Wd, other)  # eager work on the same buffers' neighbours
+        mh.mhla_forward(kd, qd, vd, Wd, other, causal=w.causal)  # eager work between replays
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()

@@ -205,6 +205,122 @@ __global__ __launch_bounds__(256) void mix_frag_kernel(const float* __restrict__
 }
 
 
+// 64 < M <= 256: one workgroup per strip of 32 columns and all M rows.  The strip of
+// S (M x 32 floats) is read from HBM once, split into bf16 hi + lo once and kept
+// in LDS transposed to [column][block], so that each MFMA B operand (8
+// consecutive blocks of one column) is one 16-byte LDS read.  Wave w owns rows
+// 16*RT*w .. 16*RT*(w+1) - 1 (RT = ceil(M / 64)) and streams its W fragments
+// (split once per call by wsplit_kernel, resident in L2) one k-chunk ahead.
+template <int RT, bool CAUSAL>
+__global__ __launch_bounds__(256) void mix_strip_kernel(const float* __restrict__ S, const bf16x8* __restrict__ frags,
+                                                        float* __restrict__ St, int64_t ncols, int M, int KC) {
+    constexpr int J = 2;                   // columns per lane: MFMA jj uses column J*n + jj
+    extern __shared__ __align__(16) uint4 strip[];  // hi then lo: [32 columns][RS4 x 16 bytes]
+    const int RS4 = 4 * KC + 1;            // 32*KC bf16 of one column, + 16 bytes against bank conflicts
+    uint4* sh = strip;
+    uint4* sl = strip + 32 * RS4;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4, n = lane & 15;
+    const int64_t col0 = (int64_t)blockIdx.x * 32;
+
+    // 1. strip -> LDS: task (8-block group bg, 4-column group cg), rows 8bg .. 8bg+7.
+    for (int task = threadIdx.x; task < 32 * KC; task += 256) {
+        const int bg = task >> 3, cg = task & 7;
+        const int64_t c = col0 + 4 * cg;
+        f32x4 x[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int b = 8 * bg + r;
+            x[r] = load_or_zero(reinterpret_cast<const f32x4*>(S + (int64_t)b * ncols + c), b < M && c < ncols,
+                                reinterpret_cast<const f32x4*>(S));
+        }
+        issue_fence();
+#pragma unroll
+        for (int xx = 0; xx < 4; ++xx) {
+            uint32_t h[4], l[4];
+#pragma unroll
+            for (int r2 = 0; r2 < 4; ++r2) split2_bf16(x[2 * r2][xx], x[2 * r2 + 1][xx], h[r2], l[r2]);
+            sh[(4 * cg + xx) * RS4 + bg] = uint4{h[0], h[1], h[2], h[3]};
+            sl[(4 * cg + xx) * RS4 + bg] = uint4{l[0], l[1], l[2], l[3]};
+        }
+    }
+    __syncthreads();
+
+    // 2. this wave's rows
+    const int i0 = 16 * RT * wave;
+    if (i0 >= M) return;  // whole wave; no barriers below
+    const int imax = min(M, i0 + 16 * RT);
+    const int kend = CAUSAL ? imax - 1 : M;  // causal rows use b < i <= imax - 1
+    const int kcn = (kend + 31) / 32;
+    const int64_t col = col0 + J * n;
+
+    f32x4 acc[RT][J];
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int j = 0; j < J; ++j) acc[r][j] = zero4();
+
+    struct Frags {
+        bf16x8 wh[RT], wl[RT];
+    };
+    auto load = [&](int kc, Frags& f) {
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            if (i0 + 16 * r < imax) {  // uniform
+                const bf16x8* p = frags + ((int64_t)((i0 / 16 + r) * KC + kc) * 64 + lane) * 2;
+                f.wh[r] = p[0];
+                f.wl[r] = p[1];
+            }
+        }
+    };
+    auto compute = [&](int kc, const Frags& f) {
+        bf16x8 bh[J], bl[J];
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            bh[j] = __builtin_bit_cast(bf16x8, sh[(J * n + j) * RS4 + 4 * kc + g]);
+            bl[j] = __builtin_bit_cast(bf16x8, sl[(J * n + j) * RS4 + 4 * kc + g]);
+        }
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            if (i0 + 16 * r < imax) {  // uniform
+#pragma unroll
+                for (int j = 0; j < J; ++j) {
+                    acc[r][j] = mfma32(f.wh[r], bh[j], acc[r][j]);
+                    acc[r][j] = mfma32(f.wh[r], bl[j], acc[r][j]);
+                    acc[r][j] = mfma32(f.wl[r], bh[j], acc[r][j]);
+                }
+            }
+        }
+    };
+    {
+        Frags fa, fb;
+        if (kcn > 0) load(0, fa);
+        for (int kc = 0; kc < kcn; kc += 2) {
+            if (kc + 1 < kcn) load(kc + 1, fb);
+            issue_fence();
+            compute(kc, fa);
+            if (kc + 1 < kcn) {
+                if (kc + 2 < kcn) load(kc + 2, fa);
+                issue_fence();
+                compute(kc + 1, fb);
+            }
+        }
+    }
+
+    if (col >= ncols) return;
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = i0 + 16 * r + 4 * g + i;
+            if (row < imax)
+                *reinterpret_cast<float2*>(St + (int64_t)row * ncols + col) = make_float2(acc[r][0][i], acc[r][1][i]);
+        }
+    }
+}
+
 // Small M (<= 64): the workgroup splits its rows of W into MFMA fragments in LDS
 // itself (at most 16 KiB), which costs less than a separate launch.
 template <int KSTEP, int RT, int J, bool PIPE, bool CAUSAL>
@@ -469,6 +585,25 @@ hipError_t launch_mix(const float* S, const float* W, float* St, int64_t BH, int
             wsplit_kernel<KSTEP, RT, true><<<sgrid, dim3(256), 0, stream>>>(W, frags, (int)M, RG, KC);
         else
             wsplit_kernel<KSTEP, RT, false><<<sgrid, dim3(256), 0, stream>>>(W, frags, (int)M, RG, KC);
+        if (M <= 256) {
+            const dim3 g2((unsigned)((ncols + 31) / 32));
+            const size_t lds = (size_t)2 * 32 * (4 * KC + 1) * 16;
+            auto run = [&](auto rt_c) {
+                constexpr int RT2 = decltype(rt_c)::value;
+                if (causal)
+                    mix_strip_kernel<RT2, true><<<g2, dim3(256), lds, stream>>>(S, frags, St, ncols, (int)M, KC);
+                else
+                    mix_strip_kernel<RT2, false><<<g2, dim3(256), lds, stream>>>(S, frags, St, ncols, (int)M, KC);
+            };
+            const int rt = (int)((M + 63) / 64);
+            if (rt <= 2)
+                run(std::integral_constant<int, 2>{});
+            else if (rt == 3)
+                run(std::integral_constant<int, 3>{});
+            else
+                run(std::integral_constant<int, 4>{});
+            return hipGetLastError();
+        }
         const int64_t ntiles = (ncols + 16 * J - 1) / (16 * J);
         const int64_t nctg = (ntiles + 3) / 4;
         const dim3 grid((unsigned)(((nctg + 7) / 8) * 8 * RG));
