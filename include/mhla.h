@@ -141,6 +141,35 @@ int mhla_output(const void* q, const void* k, const void* v, int dtype, const fl
                 int causal, mhla_stream_t stream);
 
 /*
+ * Streaming causal decoding (App. C inference: fold the new token into its
+ * block's running summary, re-mix, read out; the running sum is the recurrence of
+ * "Linear Attention 笔记" §4).  One call produces y_t for token t of every
+ * (batch, head) pair with O(d^2) work per pair, equal up to rounding to row t of
+ * mhla_forward(causal = 1) on the tokens 0 .. t of the sequence.
+ *
+ * `state` is a caller-owned device buffer of mhla_decode_state_bytes(B, H, d, M)
+ * bytes (float32, 16-byte aligned): per pair the mixed summary of the current
+ * block's predecessors, the running summary of the current block and the
+ * summaries of the completed blocks.  Calls on one state must come in order
+ * t = 0, 1, 2, ... on one stream; t = 0 starts a new sequence (no clearing
+ * needed beforehand).  Token t belongs to block i = t / C (blocks of C tokens,
+ * i < M, else MHLA_ERR_INVALID_ARG); at the first token of a block the call
+ * first closes the previous block and mixes the completed ones with W[i, b],
+ * b < i.  W[i, i] weights the running summary; entries above the diagonal are
+ * never read.
+ *
+ * q, k, v: [B][H][d] for token t (dtype MHLA_DTYPE_BF16 or _F32); out: [B][H][d]
+ * float32.  All arithmetic is float32 in a fixed order (bit-reproducible).
+ * Sizes as for the forward pass with N = M*C; out must not overlap anything,
+ * and state must not overlap q, k, v or W.
+ */
+int64_t mhla_decode_state_bytes(int64_t B, int64_t H, int64_t d, int64_t M);
+
+int mhla_decode_step(const void* q, const void* k, const void* v, int dtype, const float* W, float* state,
+                     float* out, int64_t B, int64_t H, int64_t d, int64_t M, int64_t C, int64_t t,
+                     mhla_stream_t stream);
+
+/*
  * Host-only helper (no HIP calls): decodes `count` packed summary vectors in
  * HOST memory into row-major S [count][d][d] (S[r][c] = sum phi(k)[r] v[c])
  * and z [count][d].  Returns MHLA_OK or MHLA_ERR_INVALID_ARG.

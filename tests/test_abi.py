@@ -84,6 +84,32 @@ def test_stage_validation(mhla_lib):
         mh.MHLA_ERR_INVALID_ARG
 
 
+def test_decode_validation(mhla_lib):
+    # state: (M + 1) summary vectors per pair
+    assert mh.mhla_decode_state_bytes(8, 16, 64, 64) == 65 * 8 * 16 * (64 * 64 + 64) * 4
+    assert mh.mhla_decode_state_bytes(1, 1, 24, 4) == -1
+    f = mhla_lib.mhla_decode_step
+    p = [FAKE, FAKE * 2, FAKE * 3]
+
+    def call(q=FAKE, k=FAKE * 2, v=FAKE * 3, dtype=0, W=FAKE * 4, state=FAKE * 8, out=FAKE * 16,
+             B=1, H=1, d=16, M=4, C=16, t=0):
+        return f(q, k, v, dtype, W, state, out, B, H, d, M, C, t, None)
+
+    assert call(q=None) == mh.MHLA_ERR_INVALID_ARG
+    assert call(state=None) == mh.MHLA_ERR_INVALID_ARG
+    assert "state is NULL" in mh.mhla_last_error()
+    assert call(out=FAKE + 8) == mh.MHLA_ERR_INVALID_ARG
+    assert call(dtype=5) == mh.MHLA_ERR_INVALID_ARG
+    assert call(d=48) == mh.MHLA_ERR_UNSUPPORTED
+    assert call(C=0) == mh.MHLA_ERR_INVALID_ARG
+    assert call(t=-1) == mh.MHLA_ERR_INVALID_ARG
+    assert call(t=64) == mh.MHLA_ERR_INVALID_ARG  # block 4 of M = 4
+    assert "outside" in mh.mhla_last_error()
+    assert call(out=FAKE * 8 + 256) == mh.MHLA_ERR_INVALID_ARG  # out inside the state
+    assert call(state=FAKE * 4) == mh.MHLA_ERR_INVALID_ARG  # state on top of W
+    assert "overlap" in mh.mhla_last_error()
+
+
 def test_forward_path_selection(mhla_lib):
     # non-causal bf16 with blocks of at most 16 tokens and at most 16 blocks: fused; otherwise staged
     assert mh.mhla_forward_path(64, 6, 256, 64, 16) == mh.MHLA_PATH_FUSED

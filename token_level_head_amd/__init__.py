@@ -14,7 +14,7 @@ _BINDING_NAMES = {
     "mhla_block_summaries", "mhla_forward", "mhla_forward_f32", "mhla_forward_path", "MHLA_PATH_STAGED",
     "MHLA_PATH_FUSED", "mhla_last_error", "mhla_mix_summaries",
     "mhla_output", "mhla_status_string", "mhla_summary_floats", "mhla_unpack_summaries", "mhla_version",
-    "mhla_workspace_bytes",
+    "mhla_workspace_bytes", "mhla_decode_state_bytes", "mhla_decode_step",
 }
 
 

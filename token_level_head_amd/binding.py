@@ -38,6 +38,8 @@ SIGNATURES = {
     "mhla_mix_summaries": (_I, [_P, _P, _P, _I64, _I64, _I64, _I, _I, _P]),
     "mhla_output": (_I, [_P, _P, _P, _I, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _P]),
     "mhla_unpack_summaries": (_I, [_P, _I64, _I64, _P, _P]),
+    "mhla_decode_state_bytes": (_I64, [_I64, _I64, _I64, _I64]),
+    "mhla_decode_step": (_I, [_P, _P, _P, _I, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _P]),
     "mhla_status_string": (ctypes.c_char_p, [_I]),
     "mhla_last_error": (ctypes.c_char_p, []),
     "mhla_version": (ctypes.c_char_p, []),
@@ -147,6 +149,20 @@ def mhla_output(q, k, v, St, W, out, causal=False, stream=None):
     B, H, N, d, M = _dims(q, W)
     _check(load_library().mhla_output(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(St), _ptr(W), _ptr(out),
                                       B, H, N, d, M, int(bool(causal)), _stream(stream)))
+    return out
+
+
+def mhla_decode_state_bytes(B, H, d, M):
+    return int(load_library().mhla_decode_state_bytes(B, H, d, M))
+
+
+def mhla_decode_step(q, k, v, W, state, out, C, t, stream=None):
+    """One causal decoding step: q, k, v [B, H, d] (token t), out [B, H, d] float32,
+    state a device buffer of mhla_decode_state_bytes bytes; blocks of C tokens."""
+    B, H, d = q.shape
+    M = W.shape[0]
+    _check(load_library().mhla_decode_step(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(W), _ptr(state),
+                                           _ptr(out), B, H, d, M, C, t, _stream(stream)))
     return out
 
 

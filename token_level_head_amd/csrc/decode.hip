@@ -1,0 +1,139 @@
+// decode.hip -- streaming causal decoding, one token per call ("MHLA: Restoring
+// Expressivity of Linear Attention via Token-Level Multi-Head", App. C inference:
+// fold token t into its block's running summary, re-mix, read out; the running
+// sum is the recurrence of "Linear Attention 笔记" §4, guard as in §4/§5).
+//
+// State per (batch, head) pair, float32, each vector d*d + d long (S[r][c] row-major
+// with S[r][c] = sum phi(k)[r] v[c], then z[r]):
+//   St    mixed summary of the current block's predecessors, S~_i and z~_i
+//   P     running summary of the current block up to the last token (P, p)
+//   hist  summaries of the completed blocks 0 .. M-2
+// Token t belongs to block i = t / C.  When t % C == 0 the step first closes block
+// i - 1 (P goes to hist[i-1] and is reset) and forms St = sum_{b<i} W[i,b] hist[b];
+// then every token adds phi(k_t) v_t^T to P and writes
+//   y_t = phi(q_t)(St + W[i,i] P) / (phi(q_t)(z~ + W[i,i] p) + 1e-6),
+// which is row t of the causal forward pass.  All arithmetic is float32 (phi with
+// the full-precision exp), in a fixed order: results are bit-reproducible.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace mhla {
+
+namespace {
+
+template <typename T>
+__device__ __forceinline__ float load_in(const T* p, int64_t i);
+template <>
+__device__ __forceinline__ float load_in<uint16_t>(const uint16_t* p, int64_t i) {
+    return bf16_to_f32(p[i]);
+}
+template <>
+__device__ __forceinline__ float load_in<float>(const float* p, int64_t i) {
+    return p[i];
+}
+
+}  // namespace
+
+// Closing block i - 1 and mixing for block i: one thread per (pair, entry).
+__global__ __launch_bounds__(256) void decode_advance_kernel(const float* __restrict__ W, float* __restrict__ state,
+                                                             int64_t BH, int64_t L, int M, int i, int first) {
+    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // pair * L + entry
+    if (e >= BH * L) return;
+    float* St = state;
+    float* P = state + BH * L;
+    float* hist = state + 2 * BH * L;
+    float x = 0.f;
+    if (!first) {
+        x = P[e];
+        hist[(int64_t)(i - 1) * BH * L + e] = x;
+    }
+    P[e] = 0.f;
+    float acc = 0.f;
+    for (int b = 0; b + 1 < i; ++b) acc = fmaf(W[(int64_t)i * M + b], hist[(int64_t)b * BH * L + e], acc);
+    if (i >= 1) acc = fmaf(W[(int64_t)i * M + i - 1], x, acc);
+    St[e] = acc;
+}
+
+// One token: one workgroup of 256 threads per pair.  Thread (c, rg) owns value
+// column c and rows rg*RPT .. rg*RPT + RPT - 1 of the d x d summaries.
+template <int D, typename T>
+__global__ __launch_bounds__(256) void decode_token_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                           const T* __restrict__ v, const float* __restrict__ W,
+                                                           float* __restrict__ state, float* __restrict__ out,
+                                                           int64_t BH, int M, int i) {
+    constexpr int L = D * D + D;
+    constexpr int RG = 256 / D;   // row groups
+    constexpr int RPT = D / RG;   // rows per thread
+    __shared__ float fq[D], fk[D], fv[D], part[RG][D], dpart[D];
+    const int tid = threadIdx.x;
+    const int64_t pair = blockIdx.x;
+    float* St = state + pair * L;
+    float* P = state + BH * L + pair * L;
+    const float wii = W[(int64_t)i * M + i];
+
+    if (tid < D) {
+        fq[tid] = phi_precise(load_in<T>(q, pair * D + tid));
+        fk[tid] = phi_precise(load_in<T>(k, pair * D + tid));
+        fv[tid] = load_in<T>(v, pair * D + tid);
+    }
+    __syncthreads();
+
+    const int c = tid % D, rg = tid / D;
+    float num = 0.f;
+#pragma unroll
+    for (int rr = 0; rr < RPT; ++rr) {
+        const int r = rg * RPT + rr;
+        const float pn = fmaf(fk[r], fv[c], P[r * D + c]);
+        P[r * D + c] = pn;
+        num = fmaf(fq[r], fmaf(wii, pn, St[r * D + c]), num);
+    }
+    part[rg][c] = num;
+    if (tid < D) {  // normaliser: p[r] += phi(k)[r], den term phi(q)[r] (z~[r] + W[i,i] p[r])
+        const float pz = P[D * D + tid] + fk[tid];
+        P[D * D + tid] = pz;
+        dpart[tid] = fq[tid] * fmaf(wii, pz, St[D * D + tid]);
+    }
+    __syncthreads();
+    if (tid < D) {
+        float n = 0.f, den = 0.f;
+        for (int g = 0; g < RG; ++g) n += part[g][tid];
+        for (int r = 0; r < D; ++r) den += dpart[r];
+        out[pair * D + tid] = n / (den + kEps);
+    }
+}
+
+hipError_t launch_decode_step(int dtype, const void* q, const void* k, const void* v, const float* W, float* state,
+                              float* out, int64_t BH, int D, int64_t M, int64_t C, int64_t t, hipStream_t stream) {
+    const int64_t L = (int64_t)D * D + D;
+    const int i = (int)(t / C);
+    if (t % C == 0) {
+        const int64_t total = BH * L;
+        decode_advance_kernel<<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream>>>(W, state, BH, L, (int)M,
+                                                                                            i, t == 0 ? 1 : 0);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const dim3 grid((unsigned)BH), block(256);
+#define MHLA_DECODE(DD, TT)                                                                                \
+    decode_token_kernel<DD, TT><<<grid, block, 0, stream>>>((const TT*)q, (const TT*)k, (const TT*)v, W, state, \
+                                                            out, BH, (int)M, i)
+    if (dtype == kDtypeF32) {
+        switch (D) {
+            case 16: MHLA_DECODE(16, float); break;
+            case 32: MHLA_DECODE(32, float); break;
+            case 64: MHLA_DECODE(64, float); break;
+            default: return hipErrorInvalidValue;
+        }
+    } else {
+        switch (D) {
+            case 16: MHLA_DECODE(16, uint16_t); break;
+            case 32: MHLA_DECODE(32, uint16_t); break;
+            case 64: MHLA_DECODE(64, uint16_t); break;
+            default: return hipErrorInvalidValue;
+        }
+    }
+#undef MHLA_DECODE
+    return hipGetLastError();
+}
+
+}  // namespace mhla

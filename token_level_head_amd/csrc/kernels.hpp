@@ -33,6 +33,10 @@ bool causal_quad_applicable(int64_t C);
 hipError_t launch_causal_quad(const void* q, const void* k, const void* v, const float* St, const float* W,
                               float* out, int64_t BH, int64_t N, int D, int64_t M, hipStream_t stream);
 
+// Streaming causal decoding of token t (state layout in decode.hip).
+hipError_t launch_decode_step(int dtype, const void* q, const void* k, const void* v, const float* W, float* state,
+                              float* out, int64_t BH, int D, int64_t M, int64_t C, int64_t t, hipStream_t stream);
+
 // Fused path (non-causal bf16, short blocks): the whole pass in one kernel with
 // the summaries in LDS; needs no workspace.
 bool fused_applicable(int D, int64_t BH, int64_t N, int64_t M);

@@ -268,6 +268,43 @@ int mhla_output(const void* q, const void* k, const void* v, int dtype, const fl
     return ok();
 }
 
+int64_t mhla_decode_state_bytes(int64_t B, int64_t H, int64_t d, int64_t M) {
+    if (check_sizes(B, H, M, d, M) != MHLA_OK) return -1;
+    return (M + 1) * B * H * summary_floats(d) * 4;
+}
+
+int mhla_decode_step(const void* q, const void* k, const void* v, int dtype, const float* W, float* state,
+                     float* out, int64_t B, int64_t H, int64_t d, int64_t M, int64_t C, int64_t t,
+                     mhla_stream_t stream) {
+    if (C < 1) return fail(MHLA_ERR_INVALID_ARG, "C=%lld must be >= 1", (long long)C);
+    if (M > (((int64_t)1 << 30) / C)) return fail(MHLA_ERR_UNSUPPORTED, "M*C too large");
+    int st = check_sizes(B, H, M * C, d, M);
+    if (st) return st;
+    if (dtype != MHLA_DTYPE_BF16 && dtype != MHLA_DTYPE_F32) return fail(MHLA_ERR_INVALID_ARG, "bad dtype %d", dtype);
+    if (t < 0 || t / C >= M)
+        return fail(MHLA_ERR_INVALID_ARG, "token t=%lld is outside the M*C=%lld tokens", (long long)t,
+                    (long long)(M * C));
+    if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
+        (st = check_ptr(W, "W")) || (st = check_ptr(state, "state")) || (st = check_ptr(out, "out")))
+        return st;
+    const size_t esz = dtype == MHLA_DTYPE_F32 ? 4 : 2;
+    const size_t in_bytes = (size_t)(B * H * d) * esz;
+    const size_t out_bytes = (size_t)(B * H * d) * 4;
+    const size_t st_bytes = (size_t)mhla_decode_state_bytes(B, H, d, M);
+    const size_t w_bytes = (size_t)(M * M) * 4;
+    if (overlaps(out, out_bytes, q, in_bytes) || overlaps(out, out_bytes, k, in_bytes) ||
+        overlaps(out, out_bytes, v, in_bytes) || overlaps(out, out_bytes, W, w_bytes) ||
+        overlaps(out, out_bytes, state, st_bytes))
+        return fail(MHLA_ERR_INVALID_ARG, "out overlaps an input or the state");
+    if (overlaps(state, st_bytes, q, in_bytes) || overlaps(state, st_bytes, k, in_bytes) ||
+        overlaps(state, st_bytes, v, in_bytes) || overlaps(state, st_bytes, W, w_bytes))
+        return fail(MHLA_ERR_INVALID_ARG, "state overlaps an input");
+    hipError_t e = mhla::launch_decode_step(dtype, q, k, v, W, state, out, B * H, (int)d, M, C, t,
+                                            reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "decode kernels");
+    return ok();
+}
+
 int mhla_unpack_summaries(const float* packed, int64_t count, int64_t d, float* S, float* z) {
     if (!packed || !S || !z || count < 0) return fail(MHLA_ERR_INVALID_ARG, "bad unpack arguments");
     if (d != 16 && d != 32 && d != 64) return fail(MHLA_ERR_UNSUPPORTED, "d=%lld is not one of 16, 32, 64", (long long)d);
