@@ -94,6 +94,74 @@ def cpu_baseline(w, q, k, v, W, budget_s):
     }
 
 
+def decode_bench(args, w):
+    """One block of C decode steps starting at the first token of block M/2 (so the
+    timed region includes one block boundary: closing a block and mixing M/2
+    completed summaries), timed as one HIP graph replay and as eager launches; the
+    token kernel alone is timed on the C - 1 steps after the boundary."""
+    B, H, d, M, C = w.B, w.H, w.d, w.M, w.C
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    gen = torch.Generator(device="cpu").manual_seed(w.seed)
+    q, k, v = (torch.randn((C, B, H, d), generator=gen).to("cuda", dt) for _ in range(3))
+    W = torch.from_numpy(make_inputs(w.shrink(B=1, H=1, N=w.M, d=16))[3]).cuda()
+    state = torch.zeros(mh.mhla_decode_state_bytes(B, H, d, M) // 4, device="cuda")
+    out = torch.empty((B, H, d), dtype=torch.float32, device="cuda")
+    t0 = (M // 2) * C
+    stream = torch.cuda.current_stream()
+
+    def steps(first, count):
+        for j in range(first, first + count):
+            mh.mhla_decode_step(q[j], k[j], v[j], W, state, out, C, t0 + j)
+
+    def elapsed_ms(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    def best_ms(first, count):
+        steps(first, count)  # warm-up
+        eager = elapsed_ms(lambda: steps(first, count)) / count
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            steps(first, count)
+        graph.replay()
+        return min(eager, elapsed_ms(graph.replay) / count), eager
+
+    ms, eager_ms = best_ms(0, C)
+    tok_ms, _ = best_ms(1, C - 1) if C > 1 else (ms, ms)
+    L = d * d + d
+    e = 2 if w.dtype == "bf16" else 4
+    tok_bytes = B * H * (3 * L * 4 + 3 * d * e + d * 4)  # read S~ and P, write P; q, k, v in, y out
+    achieved = tok_bytes / (tok_ms * 1e-3) / 1e9
+    line = {
+        "metric": "MHLA causal decode tokens/s at 1 MI355X (one token per sequence per step)",
+        "value": round(B / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": C,
+        "warmup": C,
+        "ms_per_step": round(ms, 5),
+        "eager_ms_per_step": round(eager_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.key + "_decode", "B": B, "H": H, "d": d, "M": M, "C": C, "first_token": t0,
+                   "global_batch": B, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "kernel": "decode_token_kernel", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -102,6 +170,9 @@ def main():
     ap.add_argument("--workload", default="dit_s2_256", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-budget", type=float, default=1.5, help="seconds of oracle wall time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode", action="store_true",
+                    help="time the streaming causal decode step (one token per call) on the workload's "
+                         "B, H, d, M, C instead of the forward pass; prints its own JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy (3x), the reference that scales "
                          "the FETCH_SIZE / WRITE_SIZE counters in counter-collection runs")
@@ -118,6 +189,8 @@ def main():
     w = WORKLOADS[args.workload]
     torch.cuda.set_device(0)
     mh.load_library()
+    if args.decode:
+        return decode_bench(args, w)
     q, k, v, W = make_inputs(w)
     dt_in = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     qd, kd, vd = (torch.from_numpy(a).to(device="cuda", dtype=dt_in) for a in (q, k, v))

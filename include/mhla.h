@@ -148,8 +148,9 @@ int mhla_output(const void* q, const void* k, const void* v, int dtype, const fl
  * mhla_forward(causal = 1) on the tokens 0 .. t of the sequence.
  *
  * `state` is a caller-owned device buffer of mhla_decode_state_bytes(B, H, d, M)
- * bytes (float32, 16-byte aligned): per pair the mixed summary of the current
- * block's predecessors, the running summary of the current block and the
+ * = ((M + 1) * (d*d + d) + d) * B*H * 4 bytes (float32, 16-byte aligned): per
+ * pair the mixed summary of the current block's predecessors, the running
+ * summary of the current block (with a second copy of its normaliser) and the
  * summaries of the completed blocks.  Calls on one state must come in order
  * t = 0, 1, 2, ... on one stream; t = 0 starts a new sequence (no clearing
  * needed beforehand).  Token t belongs to block i = t / C (blocks of C tokens,

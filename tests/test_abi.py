@@ -85,8 +85,8 @@ def test_stage_validation(mhla_lib):
 
 
 def test_decode_validation(mhla_lib):
-    # state: (M + 1) summary vectors per pair
-    assert mh.mhla_decode_state_bytes(8, 16, 64, 64) == 65 * 8 * 16 * (64 * 64 + 64) * 4
+    # state: (M + 1) summary vectors and one more normaliser per pair
+    assert mh.mhla_decode_state_bytes(8, 16, 64, 64) == (65 * (64 * 64 + 64) + 64) * 8 * 16 * 4
     assert mh.mhla_decode_state_bytes(1, 1, 24, 4) == -1
     f = mhla_lib.mhla_decode_step
     p = [FAKE, FAKE * 2, FAKE * 3]

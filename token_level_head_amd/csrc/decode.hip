@@ -3,10 +3,14 @@
 // fold token t into its block's running summary, re-mix, read out; the running
 // sum is the recurrence of "Linear Attention 笔记" §4, guard as in §4/§5).
 //
-// State per (batch, head) pair, float32, each vector d*d + d long (S[r][c] row-major
-// with S[r][c] = sum phi(k)[r] v[c], then z[r]):
+// State per (batch, head) pair, float32, each vector d*d + d long (S[r][c] with
+// S[r][c] = sum phi(k)[r] v[c], stored by 16-column groups as described at the
+// token kernel, then z[r]):
 //   St    mixed summary of the current block's predecessors, S~_i and z~_i
 //   P     running summary of the current block up to the last token (P, p)
+//   p2    a second copy of p: token t reads p from P when t is even and from p2
+//         when t is odd and writes the other one, so the d/16 workgroups of a
+//         pair never read a p that another of them has already updated
 //   hist  summaries of the completed blocks 0 .. M-2
 // Token t belongs to block i = t / C.  When t % C == 0 the step first closes block
 // i - 1 (P goes to hist[i-1] and is reset) and forms St = sum_{b<i} W[i,b] hist[b];
@@ -36,69 +40,87 @@ __device__ __forceinline__ float load_in<float>(const float* p, int64_t i) {
 
 // Closing block i - 1 and mixing for block i: one thread per (pair, entry).
 __global__ __launch_bounds__(256) void decode_advance_kernel(const float* __restrict__ W, float* __restrict__ state,
-                                                             int64_t BH, int64_t L, int M, int i, int first) {
+                                                             int64_t BH, int D, int M, int i, int first, int odd) {
+    const int64_t L = (int64_t)D * D + D;
     const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // pair * L + entry
     if (e >= BH * L) return;
     float* St = state;
     float* P = state + BH * L;
-    float* hist = state + 2 * BH * L;
+    float* p2 = state + 2 * BH * L;
+    float* hist = p2 + BH * D;
+    const int64_t pair = e / L, ent = e % L;
+    // p of an odd token index lives in p2 (see the state description above)
+    float* src = (odd && ent >= (int64_t)D * D) ? p2 + pair * D + (ent - (int64_t)D * D) : P + e;
     float x = 0.f;
     if (!first) {
-        x = P[e];
+        x = *src;
         hist[(int64_t)(i - 1) * BH * L + e] = x;
     }
-    P[e] = 0.f;
+    *src = 0.f;
     float acc = 0.f;
     for (int b = 0; b + 1 < i; ++b) acc = fmaf(W[(int64_t)i * M + b], hist[(int64_t)b * BH * L + e], acc);
     if (i >= 1) acc = fmaf(W[(int64_t)i * M + i - 1], x, acc);
     St[e] = acc;
 }
 
-// One token: one workgroup of 256 threads per pair.  Thread (c, rg) owns value
-// column c and rows rg*RPT .. rg*RPT + RPT - 1 of the d x d summaries.
+// One token.  The d x d part of each state vector is stored by groups of 16 value
+// columns, [c / 16][r][c % 16], so that the workgroup owning one column group of
+// one pair reads and writes one contiguous span; z follows in plain order.  The
+// d/16 workgroups of a pair are numbered to run on one XCD (they all read the
+// pair's q, k, z~ and p).  Thread (c, rg) owns column c of the group and rows
+// rg*RPT .. rg*RPT + RPT - 1.
 template <int D, typename T>
 __global__ __launch_bounds__(256) void decode_token_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                            const T* __restrict__ v, const float* __restrict__ W,
                                                            float* __restrict__ state, float* __restrict__ out,
-                                                           int64_t BH, int M, int i) {
+                                                           int64_t BH, int M, int i, int odd) {
     constexpr int L = D * D + D;
-    constexpr int RG = 256 / D;   // row groups
-    constexpr int RPT = D / RG;   // rows per thread
-    __shared__ float fq[D], fk[D], fv[D], part[RG][D], dpart[D];
+    constexpr int CG = D / 16;  // column groups (workgroups) per pair
+    constexpr int RPT = D / 16; // rows per thread: 16 row groups of 16 threads
+    __shared__ float fq[D], fk[D], fv[16], part[16][16], dpart[D];
     const int tid = threadIdx.x;
-    const int64_t pair = blockIdx.x;
+    const int64_t bid = blockIdx.x;
+    const int cg = (int)((bid >> 3) % CG);
+    const int64_t pair = ((bid >> 3) / CG) * 8 + (bid & 7);
+    if (pair >= BH) return;  // uniform over the workgroup
     float* St = state + pair * L;
     float* P = state + BH * L + pair * L;
+    float* p2 = state + 2 * BH * L + pair * D;
+    const float* pin = odd ? p2 : P + D * D;  // p after the previous token
+    float* pout = odd ? P + D * D : p2;       // p after this one
     const float wii = W[(int64_t)i * M + i];
 
     if (tid < D) {
         fq[tid] = phi_precise(load_in<T>(q, pair * D + tid));
         fk[tid] = phi_precise(load_in<T>(k, pair * D + tid));
-        fv[tid] = load_in<T>(v, pair * D + tid);
+    } else if (tid < D + 16) {
+        fv[tid - D] = load_in<T>(v, pair * D + 16 * cg + tid - D);
     }
     __syncthreads();
 
-    const int c = tid % D, rg = tid / D;
+    const int c = tid & 15, rg = tid >> 4;
+    const int base = cg * 16 * D;  // this column group's span
     float num = 0.f;
 #pragma unroll
     for (int rr = 0; rr < RPT; ++rr) {
         const int r = rg * RPT + rr;
-        const float pn = fmaf(fk[r], fv[c], P[r * D + c]);
-        P[r * D + c] = pn;
-        num = fmaf(fq[r], fmaf(wii, pn, St[r * D + c]), num);
+        const int e = base + r * 16 + c;
+        const float pn = fmaf(fk[r], fv[c], P[e]);
+        P[e] = pn;
+        num = fmaf(fq[r], fmaf(wii, pn, St[e]), num);
     }
     part[rg][c] = num;
-    if (tid < D) {  // normaliser: p[r] += phi(k)[r], den term phi(q)[r] (z~[r] + W[i,i] p[r])
-        const float pz = P[D * D + tid] + fk[tid];
-        P[D * D + tid] = pz;
+    if (tid < D) {  // normaliser: p[r] + phi(k)[r]; the den term phi(q)[r] (z~[r] + W[i,i] p[r])
+        const float pz = pin[tid] + fk[tid];
+        if (cg == 0) pout[tid] = pz;
         dpart[tid] = fq[tid] * fmaf(wii, pz, St[D * D + tid]);
     }
     __syncthreads();
-    if (tid < D) {
+    if (tid < 16) {
         float n = 0.f, den = 0.f;
-        for (int g = 0; g < RG; ++g) n += part[g][tid];
+        for (int g = 0; g < 16; ++g) n += part[g][tid];
         for (int r = 0; r < D; ++r) den += dpart[r];
-        out[pair * D + tid] = n / (den + kEps);
+        out[pair * D + 16 * cg + tid] = n / (den + kEps);
     }
 }
 
@@ -108,15 +130,15 @@ hipError_t launch_decode_step(int dtype, const void* q, const void* k, const voi
     const int i = (int)(t / C);
     if (t % C == 0) {
         const int64_t total = BH * L;
-        decode_advance_kernel<<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream>>>(W, state, BH, L, (int)M,
-                                                                                            i, t == 0 ? 1 : 0);
+        decode_advance_kernel<<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream>>>(
+            W, state, BH, D, (int)M, i, t == 0 ? 1 : 0, (int)(t & 1));
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const dim3 grid((unsigned)BH), block(256);
+    const dim3 grid((unsigned)(((BH + 7) / 8) * 8 * (D / 16))), block(256);
 #define MHLA_DECODE(DD, TT)                                                                                \
     decode_token_kernel<DD, TT><<<grid, block, 0, stream>>>((const TT*)q, (const TT*)k, (const TT*)v, W, state, \
-                                                            out, BH, (int)M, i)
+                                                            out, BH, (int)M, i, (int)(t & 1))
     if (dtype == kDtypeF32) {
         switch (D) {
             case 16: MHLA_DECODE(16, float); break;

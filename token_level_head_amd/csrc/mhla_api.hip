@@ -270,7 +270,7 @@ int mhla_output(const void* q, const void* k, const void* v, int dtype, const fl
 
 int64_t mhla_decode_state_bytes(int64_t B, int64_t H, int64_t d, int64_t M) {
     if (check_sizes(B, H, M, d, M) != MHLA_OK) return -1;
-    return (M + 1) * B * H * summary_floats(d) * 4;
+    return ((M + 1) * summary_floats(d) + d) * B * H * 4;
 }
 
 int mhla_decode_step(const void* q, const void* k, const void* v, int dtype, const float* W, float* state,
