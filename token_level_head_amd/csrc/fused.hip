@@ -8,11 +8,12 @@
 // summaries are several times larger than the tokens they summarise, and
 // round-tripping them through HBM dominates the three-stage pass.  Here one
 // workgroup of eight waves owns one (batch, head) pair; wave w owns blocks w and
-// w + 8.  Each wave loads its K, V and Q once and computes phi(k) and phi(q) once
-// (bf16, in registers).  The d x d summary space is then walked in P*P sub-tiles
-// of 16 features x 16 value columns (d = 16P; sub-tile (ia, c) holds features
-// P*m + ia and columns P*n + c, the lane layout of the summary MFMA), each in
-// three barrier-separated steps through LDS:
+// w + 8.  Each wave loads its K, V, W (first) and Q (last) once and computes phi(k)
+// and phi(q) once (bf16, in registers); V goes once through LDS so that each lane
+// holds one value column of its tokens.  The d x d summary space is then walked in
+// P*P sub-tiles (d = 16P; sub-tile (ia, c) holds features P*m + ia and value
+// columns 16c .. 16c + 15), in column-chunk-major order, each in three
+// barrier-separated steps through LDS:
 //   1. every wave computes the sub-tile of S_b for its blocks (one 16x16x16 bf16
 //      MFMA, tokens along k) and, for c == 0, z_b (an MFMA against ones), and
 //      stores them as float32;
@@ -23,12 +24,13 @@
 //   3. every wave adds phi(Q_i) S~_i (sub-tile) into its output accumulators
 //      (MFMAs on hi and lo) and, for c == 0, phi(Q_i) z~_i into the denominator
 //      (an MFMA whose A rows all equal z~_i).
-// The output MFMA puts value columns on rows and tokens on columns, so after the
-// last sub-tile each lane holds 4P consecutive columns of one token; it scales
-// them by 1 / (den + 1e-6) and writes them with 16-byte stores.  K, V, Q and W
-// are read with buffer loads (scalar descriptor, 32-bit offsets; an offset past
-// the end reads zero).  Blocks M .. 15 run through the same steps on zero K/V
-// (finite summaries) and carry zero mixing weight.
+// The output MFMA puts value columns on rows and tokens on columns, so once a
+// column chunk is complete each lane holds 4 consecutive columns of one token: it
+// scales them by 1 / (den + 1e-6) and writes them with one 16-byte store while the
+// next chunks are computed.  K, V, Q and W are read with buffer loads (scalar
+// descriptor, 32-bit offsets; an offset past the end reads zero).  Blocks M .. 15
+// run through the same steps on zero K/V (finite summaries) and carry zero mixing
+// weight.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -39,6 +41,7 @@ namespace {
 constexpr int kMaxBlocks = 16;  // M: one 16-row MFMA tile of W and S~
 constexpr int kWaves = 8;
 constexpr int kBlocksPerWave = kMaxBlocks / kWaves;
+
 // LDS layout, in 4-byte words.  Strides are chosen so that the accesses of the
 // three steps hit distinct banks.
 constexpr int kRSA = 20;             // S sub-tile: one value column, 16 features (+4)
@@ -106,6 +109,18 @@ __global__ __launch_bounds__(64 * kWaves) void fused_small_kernel(const uint16_t
                 vw[j][e] = u32x2{buf_load16(rV, off), 0u};
             }
         }
+    }
+    float wv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int b = 4 * g + e;
+        wv[e] = __uint_as_float(buf_load32(rW, off_if(n < M && b < M, (uint32_t)(n * M + b) * 4)));
+    }
+    // Q last: it is first needed after the first mixing step, so the summaries start
+    // as soon as K and V have arrived.
+#pragma unroll
+    for (int j = 0; j < BPW; ++j) {
+        const int b = wave + kWaves * j;
         const uint32_t qoff = ((uint32_t)(b * C + n) * D + 4 * P * g) * 2;
         if constexpr (P == 4) {
             qw[j][0] = buf_load128(rQ, qoff);
@@ -117,12 +132,6 @@ __global__ __launch_bounds__(64 * kWaves) void fused_small_kernel(const uint16_t
             qw[j][0] = u32x4{x.x, x.y, 0u, 0u};
         }
     }
-    float wv[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int b = 4 * g + e;
-        wv[e] = __uint_as_float(buf_load32(rW, off_if(n < M && b < M, (uint32_t)(n * M + b) * 4)));
-    }
     issue_fence();
 
     // Mixing B operand: W[i = n][b = 4g + e] split into hi + lo.
@@ -131,28 +140,73 @@ __global__ __launch_bounds__(64 * kWaves) void fused_small_kernel(const uint16_t
     split2_bf16(wv[2], wv[3], w23h, w23l);
     const bf16x4 wh = as_bf16x4(w01h, w23h), wl = as_bf16x4(w01l, w23l);
 
-    // phi(k) as the summary MFMA's A operand: ak[j][ia][e] = phi(K[4g + e][P n + ia]);
-    // phi(q) as the output MFMA's B operand: bq[j][ia][e] = phi(Q[n][P (4g + e) + ia]).
+    // phi(k) as the summary MFMA's A operand: ak[j][ia][e] = phi(K[4g + e][P n + ia]).
     bf16x4 ak[BPW][P], bq[BPW][P];
 #pragma unroll
     for (int j = 0; j < BPW; ++j)
 #pragma unroll
         for (int ia = 0; ia < P; ++ia) {
-            float fk[4], fq[4];
+            float fk[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const uint32_t kword = (P == 4 && ia >= 2) ? kw[j][e].y : kw[j][e].x;
                 const float pk = phi_fast(half_to_f32(kword, P == 1 ? 0 : ia & 1));
                 fk[e] = (FULL || 4 * g + e < C) ? pk : 0.f;
-                const int fl = P * e + ia;
-                fq[e] = phi_fast(half_to_f32(qw[j][fl / 8][(fl % 8) / 2], fl & 1));
             }
             ak[j][ia] = as_bf16x4(pack_bf16(fk[0], fk[1]), pack_bf16(fk[2], fk[3]));
-            bq[j][ia] = as_bf16x4(pack_bf16(fq[0], fq[1]), pack_bf16(fq[2], fq[3]));
         }
+    // V as the summary MFMA's B operand for column chunk c (value columns 16c .. 16c+15):
+    // vb[j][c][e] = V[4g + e][16c + n].  The coalesced loads gave lane n columns
+    // Pn .. Pn + P - 1, so the tile goes once through LDS (in the space the S and S~
+    // sub-tiles use later) in token-major order and is read back by column.
+    bf16x4 vb[BPW][P];
+    {
+        uint16_t* vt = reinterpret_cast<uint16_t*>(lds) + (size_t)wave * BPW * 16 * D;  // [j][token][column]
+#pragma unroll
+        for (int j = 0; j < BPW; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                uint16_t* dst = vt + (j * 16 + 4 * g + e) * D + P * n;
+                if constexpr (P == 4)
+                    *reinterpret_cast<uint2*>(dst) = uint2{vw[j][e].x, vw[j][e].y};
+                else if constexpr (P == 2)
+                    *reinterpret_cast<uint32_t*>(dst) = vw[j][e].x;
+                else
+                    *dst = (uint16_t)vw[j][e].x;
+            }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < BPW; ++j)
+#pragma unroll
+            for (int c = 0; c < P; ++c) {
+                uint32_t h[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) h[e] = vt[(j * 16 + 4 * g + e) * D + 16 * c + n];
+                vb[j][c] = as_bf16x4(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+            }
+        __syncthreads();  // the space is reused by the first sub-tile's step 1
+    }
+
+    // phi(q) as the output MFMA's B operand, bq[j][ia][e] = phi(Q[n][P (4g + e) + ia]);
+    // formed just before the first output step.
+    auto make_bq = [&]() {
+#pragma unroll
+        for (int j = 0; j < BPW; ++j)
+#pragma unroll
+            for (int ia = 0; ia < P; ++ia) {
+                float fq[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int fl = P * e + ia;
+                    fq[e] = phi_fast(half_to_f32(qw[j][fl / 8][(fl % 8) / 2], fl & 1));
+                }
+                bq[j][ia] = as_bf16x4(pack_bf16(fq[0], fq[1]), pack_bf16(fq[2], fq[3]));
+            }
+    };
 
     const bf16x4 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
     f32x4 oacc[BPW][P], dacc[BPW];
+    float rden[BPW];
 #pragma unroll
     for (int j = 0; j < BPW; ++j) {
         dacc[j] = zero4();
@@ -171,22 +225,11 @@ __global__ __launch_bounds__(64 * kWaves) void fused_small_kernel(const uint16_t
 #pragma unroll
     for (int s = 0; s < P * P; ++s) {
         const int c = s / P, ia = s % P;
-        // 1. sub-tile (ia, c) of S_b: lane (g, n) gets S_b[P (4g + r) + ia][P n + c], r = 0..3
+        // 1. sub-tile (ia, c) of S_b: lane (g, n) gets S_b[P (4g + r) + ia][16 c + n], r = 0..3
 #pragma unroll
         for (int j = 0; j < BPW; ++j) {
             const int b = wave + kWaves * j;
-            uint32_t v01, v23;
-            {
-                uint32_t h[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t vword = (P == 4 && c >= 2) ? vw[j][e].y : vw[j][e].x;
-                    h[e] = (P > 1 && (c & 1)) ? vword >> 16 : vword & 0xffffu;
-                }
-                v01 = h[0] | (h[1] << 16);
-                v23 = h[2] | (h[3] << 16);
-            }
-            const f32x4 sa = mfma16(ak[j][ia], as_bf16x4(v01, v23), zero4());
+            const f32x4 sa = mfma16(ak[j][ia], vb[j][c], zero4());
             *reinterpret_cast<f32x4*>(a_wr + b * kBSA) = sa;
             if (c == 0) {
                 const f32x4 za = mfma16(ak[j][ia], ones, zero4());
@@ -195,7 +238,7 @@ __global__ __launch_bounds__(64 * kWaves) void fused_small_kernel(const uint16_t
         }
         __syncthreads();
 
-        // 2. mixing.  Column tile t < 16 (value column P t + c), and for c == 0 the z
+        // 2. mixing.  Column tile t < 16 (value column 16 c + t), and for c == 0 the z
         //    tile: lane (g, n) gets S~_{i = n}[feature P (4g + r) + ia][.], r = 0..3.
         auto mix_tile = [&](const float* src, int bstride, uint2* hi_dst, uint2* lo_dst) {
             float x[4];
@@ -222,7 +265,8 @@ __global__ __launch_bounds__(64 * kWaves) void fused_small_kernel(const uint16_t
         if (c == 0 && wave == ia) mix_tile(z_rd, kBZA, Zhi + z_wr2, Zlo + z_wr2);
         __syncthreads();
 
-        // 3. output: D[column P (4g + r) + c][token n] += sum_m S~_i[P m + ia][.] phi(q_n)[P m + ia]
+        // 3. output: D[column 16 c + 4g + r][token n] += sum_m S~_i[P m + ia][.] phi(q_n)[P m + ia]
+        if (s == 0) make_bq();
 #pragma unroll
         for (int j = 0; j < BPW; ++j) {
             const int b = wave + kWaves * j;
@@ -239,24 +283,22 @@ __global__ __launch_bounds__(64 * kWaves) void fused_small_kernel(const uint16_t
         }
         // The next sub-tile's step 1 overwrites only the S and z sub-tiles, whose
         // last reader (step 2) finished before the barrier above.
-    }
 
-    // ---- y = numerator / (den + 1e-6): lane (g, n) holds columns 4Pg .. 4Pg + 4P - 1 of token n ----
+        // Column chunk c is complete after its last feature group (the denominator
+        // after chunk 0): write it now, so the stores overlap the remaining chunks.
+        if (ia == P - 1) {
+            if (c == 0) {
 #pragma unroll
-    for (int j = 0; j < BPW; ++j) {
-        const int b = wave + kWaves * j;
-        if (b < M && (FULL || n < C)) {
-            const float rden = fast_rcp(dacc[j][0] + kEps);
-            float* dst = Y + (pair * N + b * C + n) * D + 4 * P * g;
+                for (int j = 0; j < BPW; ++j) rden[j] = fast_rcp(dacc[j][0] + kEps);
+            }
 #pragma unroll
-            for (int h = 0; h < P; ++h) {
-                f32x4 o;
-#pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    const int col = 4 * h + x;  // = P r + c
-                    o[x] = oacc[j][col % P][col / P] * rden;
+            for (int j = 0; j < BPW; ++j) {
+                const int b = wave + kWaves * j;
+                if (b < M && (FULL || n < C)) {
+                    float* dst = Y + (pair * N + b * C + n) * D + 16 * c + 4 * g;
+                    const f32x4 o = oacc[j][c];
+                    *reinterpret_cast<f32x4*>(dst) = f32x4{o[0] * rden[j], o[1] * rden[j], o[2] * rden[j], o[3] * rden[j]};
                 }
-                *reinterpret_cast<f32x4*>(dst + 4 * h) = o;
             }
         }
     }
