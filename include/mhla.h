@@ -141,6 +141,29 @@ int mhla_output(const void* q, const void* k, const void* v, int dtype, const fl
                 int causal, mhla_stream_t stream);
 
 /*
+ * Backward pass: gradients of L = sum(dy * Y), Y = the forward pass of these
+ * inputs (same sizes and causal flag), with respect to q, k, v and W (the
+ * coefficient matrix M_c is learned end to end, §4.2).  The chain rule runs
+ * through the four steps of §4.1 (App. C running summary when causal): it
+ * recomputes S_b and S~_i, then forms dq and the gradients of S~, maps them
+ * back through W^T to the summaries' gradients, and from those dk and dv; dW
+ * sums <dS~_i, S_b> over every batch element and head.  Causal: entries of W
+ * above the diagonal get zero gradient.
+ *
+ * q, k, v: [B][H][N][d] (dtype MHLA_DTYPE_BF16 or _F32); W [M][M] float32;
+ * dy, dq, dk, dv: [B][H][N][d] float32; dW: [M][M] float32.  Outputs are
+ * overwritten (not accumulated).  All arithmetic is float32 on the exact input
+ * values, in a fixed order (bit-reproducible).  Workspace of
+ * mhla_backward_workspace_bytes() bytes comes from the library's stream-ordered
+ * pool, as for mhla_forward.  Outputs must not overlap each other or an input.
+ */
+int64_t mhla_backward_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int64_t M, int causal);
+
+int mhla_backward(const void* q, const void* k, const void* v, int dtype, const float* W, const float* dy,
+                  float* dq, float* dk, float* dv, float* dW, int64_t B, int64_t H, int64_t N, int64_t d,
+                  int64_t M, int causal, mhla_stream_t stream);
+
+/*
  * Streaming causal decoding (App. C inference: fold the new token into its
  * block's running summary, re-mix, read out; the running sum is the recurrence of
  * "Linear Attention 笔记" §4).  One call produces y_t for token t of every

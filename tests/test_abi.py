@@ -110,6 +110,28 @@ def test_decode_validation(mhla_lib):
     assert "overlap" in mh.mhla_last_error()
 
 
+def test_backward_validation(mhla_lib):
+    assert mh.mhla_backward_workspace_bytes(1, 1, 250, 64, 16) == -1
+    assert mh.mhla_backward_workspace_bytes(2, 3, 256, 64, 16) > 4 * 16 * 6 * (64 * 64 + 64) * 4
+    f = mhla_lib.mhla_backward
+    base = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, dtype=0, W=FAKE * 4, dy=FAKE * 5, dq=FAKE * 6, dk=FAKE * 7,
+                dv=FAKE * 8, dW=FAKE * 9, B=1, H=1, N=256, d=16, M=4, causal=0)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return f(a["q"], a["k"], a["v"], a["dtype"], a["W"], a["dy"], a["dq"], a["dk"], a["dv"], a["dW"],
+                 a["B"], a["H"], a["N"], a["d"], a["M"], a["causal"], None)
+
+    assert call(dy=None) == mh.MHLA_ERR_INVALID_ARG
+    assert "dy is NULL" in mh.mhla_last_error()
+    assert call(dtype=3) == mh.MHLA_ERR_INVALID_ARG
+    assert call(d=48) == mh.MHLA_ERR_UNSUPPORTED
+    assert call(N=250) == mh.MHLA_ERR_INVALID_ARG
+    assert call(dq=FAKE * 5 + 64) == mh.MHLA_ERR_INVALID_ARG  # dq inside dy
+    assert call(dk=FAKE * 6 + 16) == mh.MHLA_ERR_INVALID_ARG  # dk inside dq
+    assert "overlap" in mh.mhla_last_error()
+
+
 def test_forward_path_selection(mhla_lib):
     # non-causal bf16 with blocks of at most 16 tokens and at most 16 blocks: fused; otherwise staged
     assert mh.mhla_forward_path(64, 6, 256, 64, 16) == mh.MHLA_PATH_FUSED

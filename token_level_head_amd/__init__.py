@@ -15,6 +15,7 @@ _BINDING_NAMES = {
     "MHLA_PATH_FUSED", "mhla_last_error", "mhla_mix_summaries",
     "mhla_output", "mhla_status_string", "mhla_summary_floats", "mhla_unpack_summaries", "mhla_version",
     "mhla_workspace_bytes", "mhla_decode_state_bytes", "mhla_decode_step",
+    "mhla_backward_workspace_bytes", "mhla_backward",
 }
 
 

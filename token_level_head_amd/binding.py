@@ -39,6 +39,8 @@ SIGNATURES = {
     "mhla_output": (_I, [_P, _P, _P, _I, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _P]),
     "mhla_unpack_summaries": (_I, [_P, _I64, _I64, _P, _P]),
     "mhla_decode_state_bytes": (_I64, [_I64, _I64, _I64, _I64]),
+    "mhla_backward_workspace_bytes": (_I64, [_I64, _I64, _I64, _I64, _I64, _I]),
+    "mhla_backward": (_I, [_P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _P]),
     "mhla_decode_step": (_I, [_P, _P, _P, _I, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _P]),
     "mhla_status_string": (ctypes.c_char_p, [_I]),
     "mhla_last_error": (ctypes.c_char_p, []),
@@ -150,6 +152,20 @@ def mhla_output(q, k, v, St, W, out, causal=False, stream=None):
     _check(load_library().mhla_output(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(St), _ptr(W), _ptr(out),
                                       B, H, N, d, M, int(bool(causal)), _stream(stream)))
     return out
+
+
+def mhla_backward_workspace_bytes(B, H, N, d, M, causal=False):
+    return int(load_library().mhla_backward_workspace_bytes(B, H, N, d, M, int(bool(causal))))
+
+
+def mhla_backward(q, k, v, W, dy, dq, dk, dv, dW, causal=False, stream=None):
+    """Gradients of sum(dy * forward(q, k, v, W)): q, k, v [B, H, N, d] bf16 or float32,
+    dy and the outputs dq, dk, dv float32 [B, H, N, d], dW float32 [M, M]."""
+    B, H, N, d, M = _dims(q, W)
+    _check(load_library().mhla_backward(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(W), _ptr(dy), _ptr(dq),
+                                        _ptr(dk), _ptr(dv), _ptr(dW), B, H, N, d, M, int(bool(causal)),
+                                        _stream(stream)))
+    return dq, dk, dv, dW
 
 
 def mhla_decode_state_bytes(B, H, d, M):

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmhla.so")
-SOURCES = ["summary.hip", "mix.hip", "output.hip", "causal.hip", "decode.hip", "fused.hip", "mhla_api.hip"]
+SOURCES = ["summary.hip", "mix.hip", "output.hip", "causal.hip", "decode.hip", "backward.hip", "fused.hip", "mhla_api.hip"]
 OBJDIR = os.path.join(ROOT, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

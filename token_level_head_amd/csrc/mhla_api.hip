@@ -268,6 +268,52 @@ int mhla_output(const void* q, const void* k, const void* v, int dtype, const fl
     return ok();
 }
 
+int64_t mhla_backward_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int64_t M, int causal) {
+    if (check_sizes(B, H, N, d, M) != MHLA_OK) return -1;
+    const size_t f = mhla::backward_workspace_floats(B * H, N, (int)d, M, causal != 0) * sizeof(float);
+    return (int64_t)((f + 15) / 16 * 16 + mhla::mix_fragment_bytes(M));
+}
+
+int mhla_backward(const void* q, const void* k, const void* v, int dtype, const float* W, const float* dy,
+                  float* dq, float* dk, float* dv, float* dW, int64_t B, int64_t H, int64_t N, int64_t d,
+                  int64_t M, int causal, mhla_stream_t stream_) {
+    int st = check_sizes(B, H, N, d, M);
+    if (st) return st;
+    if (dtype != MHLA_DTYPE_BF16 && dtype != MHLA_DTYPE_F32) return fail(MHLA_ERR_INVALID_ARG, "bad dtype %d", dtype);
+    if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
+        (st = check_ptr(W, "W")) || (st = check_ptr(dy, "dy")) || (st = check_ptr(dq, "dq")) ||
+        (st = check_ptr(dk, "dk")) || (st = check_ptr(dv, "dv")) || (st = check_ptr(dW, "dW")))
+        return st;
+    const size_t esz = dtype == MHLA_DTYPE_F32 ? 4 : 2;
+    const size_t in_bytes = (size_t)(B * H * N * d) * esz;
+    const size_t g_bytes = (size_t)(B * H * N * d) * 4;
+    const size_t w_bytes = (size_t)(M * M) * 4;
+    const void* ins[5] = {q, k, v, W, dy};
+    const size_t in_sz[5] = {in_bytes, in_bytes, in_bytes, w_bytes, g_bytes};
+    const void* outs[4] = {dq, dk, dv, dW};
+    const size_t out_sz[4] = {g_bytes, g_bytes, g_bytes, w_bytes};
+    for (int o = 0; o < 4; ++o) {
+        for (int i = 0; i < 5; ++i)
+            if (overlaps(outs[o], out_sz[o], ins[i], in_sz[i]))
+                return fail(MHLA_ERR_INVALID_ARG, "a gradient output overlaps an input");
+        for (int o2 = 0; o2 < o; ++o2)
+            if (overlaps(outs[o], out_sz[o], outs[o2], out_sz[o2]))
+                return fail(MHLA_ERR_INVALID_ARG, "gradient outputs overlap each other");
+    }
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+    const size_t fbytes = (mhla::backward_workspace_floats(B * H, N, (int)d, M, causal != 0) * sizeof(float) + 15) /
+                          16 * 16;
+    const size_t total = fbytes + mhla::mix_fragment_bytes(M);
+    void* ws = nullptr;
+    if ((st = pool_alloc(&ws, total, stream))) return st;
+    hipError_t e = mhla::launch_backward(dtype, q, k, v, W, dy, dq, dk, dv, dW, B * H, N, (int)d, M, causal != 0,
+                                         static_cast<float*>(ws), static_cast<char*>(ws) + fbytes, stream);
+    hipError_t fe = hipFreeAsync(ws, stream);
+    if (e != hipSuccess) return hip_fail(e, "backward kernels");
+    if (fe != hipSuccess) return hip_fail(fe, "workspace release");
+    return ok();
+}
+
 int64_t mhla_decode_state_bytes(int64_t B, int64_t H, int64_t d, int64_t M) {
     if (check_sizes(B, H, M, d, M) != MHLA_OK) return -1;
     return ((M + 1) * summary_floats(d) + d) * B * H * 4;
