@@ -8,29 +8,30 @@
 // summaries are several times larger than the tokens they summarise, and
 // round-tripping them through HBM dominates the three-stage pass.  Here one
 // workgroup of eight waves owns one (batch, head) pair; wave w owns blocks w and
-// w + 8.  Each wave loads its K, V, W (first) and Q (last) once and computes phi(k)
-// and phi(q) once (bf16, in registers); V goes once through LDS so that each lane
-// holds one value column of its tokens.  The d x d summary space is then walked in
-// P*P sub-tiles (d = 16P; sub-tile (ia, c) holds features P*m + ia and value
-// columns 16c .. 16c + 15), in column-chunk-major order, each in three
-// barrier-separated steps through LDS:
-//   1. every wave computes the sub-tile of S_b for its blocks (one 16x16x16 bf16
-//      MFMA, tokens along k) and, for c == 0, z_b (an MFMA against ones), and
+// w + 8.  Each wave loads its K, V and W, stages V once through LDS (so that each
+// lane holds one value column of its tokens), and only then issues its Q loads, so
+// that the K and V requests of all workgroups reach memory first; phi(k) and phi(q)
+// are computed once (bf16, in registers).  The d x d summary space is walked in P*P
+// sub-tiles (d = 16P; sub-tile (ia, c) holds features P*m + ia and value columns
+// 16c .. 16c + 15), in column-chunk-major order, two sub-tiles of one column chunk
+// at a time, each batch in three barrier-separated steps through LDS:
+//   1. every wave computes both sub-tiles of S_b for its blocks (one 16x16x16 bf16
+//      MFMA each, tokens along k) and, for c == 0, z_b (an MFMA against ones), and
 //      stores them as float32;
-//   2. the sub-tile's 16 column tiles (+ the z tile) are mixed,
+//   2. each sub-tile's 16 column tiles (+ the z tile) are mixed,
 //      S~_i = sum_b W[i, b] S_b, with blocks along k: S and W split into bf16
 //      hi + lo, three MFMAs (hi.hi + lo.hi + hi.lo); the result is split into
 //      hi + lo again for step 3;
-//   3. every wave adds phi(Q_i) S~_i (sub-tile) into its output accumulators
-//      (MFMAs on hi and lo) and, for c == 0, phi(Q_i) z~_i into the denominator
-//      (an MFMA whose A rows all equal z~_i).
+//   3. every wave adds phi(Q_i) S~_i (both sub-tiles) into the accumulators of the
+//      current column chunk (MFMAs on hi and lo) and, for c == 0, phi(Q_i) z~_i into
+//      the denominator (an MFMA whose A rows all equal z~_i).
 // The output MFMA puts value columns on rows and tokens on columns, so once a
 // column chunk is complete each lane holds 4 consecutive columns of one token: it
 // scales them by 1 / (den + 1e-6) and writes them with one 16-byte store while the
 // next chunks are computed.  K, V, Q and W are read with buffer loads (scalar
 // descriptor, 32-bit offsets; an offset past the end reads zero).  Blocks M .. 15
 // run through the same steps on zero K/V (finite summaries) and carry zero mixing
-// weight.
+// weight.  LDS holds two batch slots (80 KiB), so two workgroups share a CU.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -49,7 +50,12 @@ constexpr int kBSA = 16 * kRSA + 4;  // S sub-tile: one block (4 blocks apart = 
 constexpr int kBSB = 130;            // S~ hi (and lo): one query block, [4 feature quads][16 columns] x 2 words
 constexpr int kBZA = 20;             // z sub-tile: one block
 constexpr int kBZB = 12;             // z~ hi (and lo): one query block, 4 feature quads x 2 words
-constexpr int kLdsWords = kMaxBlocks * kBSA + 2 * kMaxBlocks * kBSB + kMaxBlocks * kBZA + 2 * kMaxBlocks * kBZB;
+// One batch slot: an S sub-tile, the S~ sub-tile (hi, lo), a z sub-tile, z~ (hi, lo).
+constexpr int kSlotS = kMaxBlocks * kBSA;
+constexpr int kSlotSt = 2 * kMaxBlocks * kBSB;
+constexpr int kSlotZ = kMaxBlocks * kBZA;
+constexpr int kSlotZt = 2 * kMaxBlocks * kBZB;
+constexpr int kSlotWords = kSlotS + kSlotSt + kSlotZ + kSlotZt;
 
 __device__ __forceinline__ float half_to_f32(uint32_t word, int half) {
     return __uint_as_float(half ? (word & 0xffff0000u) : (word << 16));
@@ -58,6 +64,7 @@ __device__ __forceinline__ float half_to_f32(uint32_t word, int half) {
 __device__ __forceinline__ bf16x4 as_bf16x4(uint32_t lo_pair, uint32_t hi_pair) {
     return __builtin_bit_cast(bf16x4, u32x2{lo_pair, hi_pair});
 }
+
 
 }  // namespace
 
@@ -69,13 +76,13 @@ __global__ __launch_bounds__(64 * kWaves) void fused_small_kernel(const uint16_t
                                                           int N, int M) {
     constexpr int P = D / 16;
     constexpr int BPW = kBlocksPerWave;
-    __shared__ __align__(16) float lds[kLdsWords];
-    float* A = lds;                                                  // [16 blocks][16 columns][kRSA]
-    uint2* Bhi = reinterpret_cast<uint2*>(lds + kMaxBlocks * kBSA);  // [16 query blocks][kBSB / 2]
-    uint2* Blo = Bhi + kMaxBlocks * kBSB / 2;
-    float* Az = reinterpret_cast<float*>(Blo + kMaxBlocks * kBSB / 2);  // [16 blocks][kBZA]
-    uint2* Zhi = reinterpret_cast<uint2*>(Az + kMaxBlocks * kBZA);      // [16 query blocks][kBZB / 2]
-    uint2* Zlo = Zhi + kMaxBlocks * kBZB / 2;
+    constexpr int SB = P > 1 ? 2 : 1;  // sub-tiles per batch (same column chunk)
+    constexpr int NB = P * P / SB;     // batches
+    __shared__ __align__(16) float lds[SB * kSlotWords];
+    float* const A = lds;                                                   // [SB][16 blocks][16 columns][kRSA]
+    uint2* const Bhi = reinterpret_cast<uint2*>(lds + SB * kSlotS);        // [SB][hi, lo][16 query blocks][kBSB / 2]
+    float* const Az = lds + SB * (kSlotS + kSlotSt);                       // [SB][16 blocks][kBZA]
+    uint2* const Zhi = reinterpret_cast<uint2*>(Az + SB * kSlotZ);         // [SB][hi, lo][16 query blocks][kBZB / 2]
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -83,8 +90,9 @@ __global__ __launch_bounds__(64 * kWaves) void fused_small_kernel(const uint16_t
     const int64_t pair = blockIdx.x;
     const int C = FULL ? 16 : N / M;  // tokens per block, <= 16
 
-    // ---- loads: K and V (lane: P features / columns of tokens 4g .. 4g+3), Q (lane:
-    // features 4Pg .. 4Pg + 4P - 1 of token n), W (lane: W[n][4g + e]) ----
+    // ---- loads: K and V (lane: P features / columns of tokens 4g .. 4g+3), W (lane:
+    // W[n][4g + e]); Q (lane: features 4Pg .. 4Pg + 4P - 1 of token n) after V has gone
+    // through LDS, so that the K and V requests of all workgroups come first ----
     const uint32_t pair_bytes = (uint32_t)N * D * 2;
     const rsrc_t rK = make_rsrc(K + pair * N * D, pair_bytes);
     const rsrc_t rV = make_rsrc(V + pair * N * D, pair_bytes);
@@ -116,22 +124,22 @@ __global__ __launch_bounds__(64 * kWaves) void fused_small_kernel(const uint16_t
         const int b = 4 * g + e;
         wv[e] = __uint_as_float(buf_load32(rW, off_if(n < M && b < M, (uint32_t)(n * M + b) * 4)));
     }
-    // Q last: it is first needed after the first mixing step, so the summaries start
-    // as soon as K and V have arrived.
+    auto load_q = [&]() {
 #pragma unroll
-    for (int j = 0; j < BPW; ++j) {
-        const int b = wave + kWaves * j;
-        const uint32_t qoff = ((uint32_t)(b * C + n) * D + 4 * P * g) * 2;
-        if constexpr (P == 4) {
-            qw[j][0] = buf_load128(rQ, qoff);
-            qw[j][1] = buf_load128(rQ, qoff + 16);
-        } else if constexpr (P == 2) {
-            qw[j][0] = buf_load128(rQ, qoff);
-        } else {
-            const u32x2 x = buf_load64(rQ, qoff);
-            qw[j][0] = u32x4{x.x, x.y, 0u, 0u};
+        for (int j = 0; j < BPW; ++j) {
+            const int b = wave + kWaves * j;
+            const uint32_t qoff = ((uint32_t)(b * C + n) * D + 4 * P * g) * 2;
+            if constexpr (P == 4) {
+                qw[j][0] = buf_load128(rQ, qoff);
+                qw[j][1] = buf_load128(rQ, qoff + 16);
+            } else if constexpr (P == 2) {
+                qw[j][0] = buf_load128(rQ, qoff);
+            } else {
+                const u32x2 x = buf_load64(rQ, qoff);
+                qw[j][0] = u32x4{x.x, x.y, 0u, 0u};
+            }
         }
-    }
+    };
     issue_fence();
 
     // Mixing B operand: W[i = n][b = 4g + e] split into hi + lo.
@@ -157,11 +165,12 @@ __global__ __launch_bounds__(64 * kWaves) void fused_small_kernel(const uint16_t
         }
     // V as the summary MFMA's B operand for column chunk c (value columns 16c .. 16c+15):
     // vb[j][c][e] = V[4g + e][16c + n].  The coalesced loads gave lane n columns
-    // Pn .. Pn + P - 1, so the tile goes once through LDS (in the space the S and S~
-    // sub-tiles use later) in token-major order and is read back by column.
+    // Pn .. Pn + P - 1, so the tile goes once through LDS (each wave its own region,
+    // inside the S~ buffers, which are first written after the first batch's barrier)
+    // in token-major order and is read back by column.
     bf16x4 vb[BPW][P];
     {
-        uint16_t* vt = reinterpret_cast<uint16_t*>(lds) + (size_t)wave * BPW * 16 * D;  // [j][token][column]
+        uint16_t* vt = reinterpret_cast<uint16_t*>(Bhi) + (size_t)wave * BPW * 16 * D;  // [j][token][column]
 #pragma unroll
         for (int j = 0; j < BPW; ++j)
 #pragma unroll
@@ -175,6 +184,7 @@ __global__ __launch_bounds__(64 * kWaves) void fused_small_kernel(const uint16_t
                     *dst = (uint16_t)vw[j][e].x;
             }
         __syncthreads();
+        load_q();
 #pragma unroll
         for (int j = 0; j < BPW; ++j)
 #pragma unroll
@@ -184,7 +194,6 @@ __global__ __launch_bounds__(64 * kWaves) void fused_small_kernel(const uint16_t
                 for (int e = 0; e < 4; ++e) h[e] = vt[(j * 16 + 4 * g + e) * D + 16 * c + n];
                 vb[j][c] = as_bf16x4(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
             }
-        __syncthreads();  // the space is reused by the first sub-tile's step 1
     }
 
     // phi(q) as the output MFMA's B operand, bq[j][ia][e] = phi(Q[n][P (4g + e) + ia]);
@@ -205,99 +214,111 @@ __global__ __launch_bounds__(64 * kWaves) void fused_small_kernel(const uint16_t
     };
 
     const bf16x4 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
-    f32x4 oacc[BPW][P], dacc[BPW];
+    f32x4 oacc[BPW], dacc[BPW];  // output accumulators of the current column chunk; denominator
     float rden[BPW];
-#pragma unroll
-    for (int j = 0; j < BPW; ++j) {
-        dacc[j] = zero4();
-#pragma unroll
-        for (int c = 0; c < P; ++c) oacc[j][c] = zero4();
-    }
 
-    // Per-lane LDS bases (words / uint2 units); everything else is an immediate offset.
-    float* const a_wr = A + n * kRSA + 4 * g;              // step 1: S_b[4g .. 4g+3][column n]
-    const float* const a_rd = A + 4 * g * kBSA + n;        // step 2: S_{4g + e}[column t][feature n]
-    float* const z_wr = Az + 4 * g;                        // step 1: z_b[4g .. 4g+3]
-    const float* const z_rd = Az + 4 * g * kBZA + n;       // step 2: z_{4g + e}[feature n]
-    const int b_wr = n * (kBSB / 2) + g * 16;              // step 2: S~_{i = n}[quad g][column t]
-    const int z_wr2 = n * (kBZB / 2) + g;                  // step 2: z~_{i = n}[quad g]
+    // Mixing of one 16-column tile: four blocks' values, split hi + lo, against the
+    // split W; the result split again for the output step.
+    auto mix_tile = [&](const float* src, int bstride, uint2* hi_dst, uint2* lo_dst) {
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = src[e * bstride];
+        uint32_t h01, l01, h23, l23;
+        split2_bf16(x[0], x[1], h01, l01);
+        split2_bf16(x[2], x[3], h23, l23);
+        const bf16x4 sh = as_bf16x4(h01, h23), sl = as_bf16x4(l01, l23);
+        f32x4 acc = mfma16(sh, wh, zero4());
+        acc = mfma16(sl, wh, acc);
+        acc = mfma16(sh, wl, acc);
+        uint32_t o01h, o01l, o23h, o23l;
+        split2_bf16(acc[0], acc[1], o01h, o01l);
+        split2_bf16(acc[2], acc[3], o23h, o23l);
+        *hi_dst = uint2{o01h, o23h};
+        *lo_dst = uint2{o01l, o23l};
+    };
 
 #pragma unroll
-    for (int s = 0; s < P * P; ++s) {
-        const int c = s / P, ia = s % P;
+    for (int bt = 0; bt < NB; ++bt) {
         // 1. sub-tile (ia, c) of S_b: lane (g, n) gets S_b[P (4g + r) + ia][16 c + n], r = 0..3
 #pragma unroll
-        for (int j = 0; j < BPW; ++j) {
-            const int b = wave + kWaves * j;
-            const f32x4 sa = mfma16(ak[j][ia], vb[j][c], zero4());
-            *reinterpret_cast<f32x4*>(a_wr + b * kBSA) = sa;
-            if (c == 0) {
-                const f32x4 za = mfma16(ak[j][ia], ones, zero4());
-                if (n == 0) *reinterpret_cast<f32x4*>(z_wr + b * kBZA) = za;
+        for (int u = 0; u < SB; ++u) {
+            const int s = bt * SB + u, c = s / P, ia = s % P;
+            float* const a_wr = A + u * kSlotS + n * kRSA + 4 * g;
+            float* const z_wr = Az + u * kSlotZ + 4 * g;
+#pragma unroll
+            for (int j = 0; j < BPW; ++j) {
+                const int b = wave + kWaves * j;
+                *reinterpret_cast<f32x4*>(a_wr + b * kBSA) = mfma16(ak[j][ia], vb[j][c], zero4());
+                if (c == 0) {
+                    const f32x4 za = mfma16(ak[j][ia], ones, zero4());
+                    if (n == 0) *reinterpret_cast<f32x4*>(z_wr + b * kBZA) = za;
+                }
             }
         }
         __syncthreads();
 
         // 2. mixing.  Column tile t < 16 (value column 16 c + t), and for c == 0 the z
         //    tile: lane (g, n) gets S~_{i = n}[feature P (4g + r) + ia][.], r = 0..3.
-        auto mix_tile = [&](const float* src, int bstride, uint2* hi_dst, uint2* lo_dst) {
-            float x[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = src[e * bstride];
-            uint32_t h01, l01, h23, l23;
-            split2_bf16(x[0], x[1], h01, l01);
-            split2_bf16(x[2], x[3], h23, l23);
-            const bf16x4 sh = as_bf16x4(h01, h23), sl = as_bf16x4(l01, l23);
-            f32x4 acc = mfma16(sh, wh, zero4());
-            acc = mfma16(sl, wh, acc);
-            acc = mfma16(sh, wl, acc);
-            uint32_t o01h, o01l, o23h, o23l;
-            split2_bf16(acc[0], acc[1], o01h, o01l);
-            split2_bf16(acc[2], acc[3], o23h, o23l);
-            *hi_dst = uint2{o01h, o23h};
-            *lo_dst = uint2{o01l, o23l};
-        };
+        for (int u = 0; u < SB; ++u) {
+            const int s = bt * SB + u, c = s / P, ia = s % P;
+            const float* const a_rd = A + u * kSlotS + 4 * g * kBSA + n;
+            uint2* const bhi = Bhi + u * (kSlotSt / 2) + n * (kBSB / 2) + g * 16;
+            uint2* const blo = bhi + kMaxBlocks * kBSB / 2;
 #pragma unroll
-        for (int j = 0; j < 16 / kWaves; ++j) {
-            const int t = wave + kWaves * j;
-            mix_tile(a_rd + t * kRSA, kBSA, Bhi + b_wr + t, Blo + b_wr + t);
+            for (int j = 0; j < 16 / kWaves; ++j) {
+                const int t = wave + kWaves * j;
+                mix_tile(a_rd + t * kRSA, kBSA, bhi + t, blo + t);
+            }
+            if (c == 0 && wave == (ia + 4 * u) % kWaves) {
+                uint2* const zhi = Zhi + u * (kSlotZt / 2) + n * (kBZB / 2) + g;
+                mix_tile(Az + u * kSlotZ + 4 * g * kBZA + n, kBZA, zhi, zhi + kMaxBlocks * kBZB / 2);
+            }
         }
-        if (c == 0 && wave == ia) mix_tile(z_rd, kBZA, Zhi + z_wr2, Zlo + z_wr2);
         __syncthreads();
 
         // 3. output: D[column 16 c + 4g + r][token n] += sum_m S~_i[P m + ia][.] phi(q_n)[P m + ia]
-        if (s == 0) make_bq();
+        if (bt == 0) make_bq();
 #pragma unroll
-        for (int j = 0; j < BPW; ++j) {
-            const int b = wave + kWaves * j;
-            const uint2 sh = Bhi[b * (kBSB / 2) + g * 16 + n];
-            const uint2 sl = Blo[b * (kBSB / 2) + g * 16 + n];
-            oacc[j][c] = mfma16(as_bf16x4(sh.x, sh.y), bq[j][ia], oacc[j][c]);
-            oacc[j][c] = mfma16(as_bf16x4(sl.x, sl.y), bq[j][ia], oacc[j][c]);
-            if (c == 0) {
-                const uint2 zh = Zhi[b * (kBZB / 2) + g];
-                const uint2 zl = Zlo[b * (kBZB / 2) + g];
-                dacc[j] = mfma16(as_bf16x4(zh.x, zh.y), bq[j][ia], dacc[j]);
-                dacc[j] = mfma16(as_bf16x4(zl.x, zl.y), bq[j][ia], dacc[j]);
-            }
-        }
-        // The next sub-tile's step 1 overwrites only the S and z sub-tiles, whose
-        // last reader (step 2) finished before the barrier above.
-
-        // Column chunk c is complete after its last feature group (the denominator
-        // after chunk 0): write it now, so the stores overlap the remaining chunks.
-        if (ia == P - 1) {
-            if (c == 0) {
-#pragma unroll
-                for (int j = 0; j < BPW; ++j) rden[j] = fast_rcp(dacc[j][0] + kEps);
-            }
+        for (int u = 0; u < SB; ++u) {
+            const int s = bt * SB + u, c = s / P, ia = s % P;
+            const uint2* const bhi = Bhi + u * (kSlotSt / 2);
+            const uint2* const blo = bhi + kMaxBlocks * kBSB / 2;
+            const uint2* const zhi = Zhi + u * (kSlotZt / 2);
+            const uint2* const zlo = zhi + kMaxBlocks * kBZB / 2;
 #pragma unroll
             for (int j = 0; j < BPW; ++j) {
                 const int b = wave + kWaves * j;
-                if (b < M && (FULL || n < C)) {
-                    float* dst = Y + (pair * N + b * C + n) * D + 16 * c + 4 * g;
-                    const f32x4 o = oacc[j][c];
-                    *reinterpret_cast<f32x4*>(dst) = f32x4{o[0] * rden[j], o[1] * rden[j], o[2] * rden[j], o[3] * rden[j]};
+                const uint2 sh = bhi[b * (kBSB / 2) + g * 16 + n];
+                const uint2 sl = blo[b * (kBSB / 2) + g * 16 + n];
+                oacc[j] = mfma16(as_bf16x4(sh.x, sh.y), bq[j][ia], ia == 0 ? zero4() : oacc[j]);
+                oacc[j] = mfma16(as_bf16x4(sl.x, sl.y), bq[j][ia], oacc[j]);
+                if (c == 0) {
+                    const uint2 zh = zhi[b * (kBZB / 2) + g];
+                    const uint2 zl = zlo[b * (kBZB / 2) + g];
+                    dacc[j] = mfma16(as_bf16x4(zh.x, zh.y), bq[j][ia], ia == 0 ? zero4() : dacc[j]);
+                    dacc[j] = mfma16(as_bf16x4(zl.x, zl.y), bq[j][ia], dacc[j]);
+                }
+            }
+            // The next batch's step 1 overwrites only the S and z sub-tiles, whose last
+            // reader (step 2) finished before the barrier above.
+
+            // Column chunk c is complete after its last feature group (the denominator
+            // after chunk 0): write it now, so the stores overlap the remaining chunks.
+            if (ia == P - 1) {
+                if (c == 0) {
+#pragma unroll
+                    for (int j = 0; j < BPW; ++j) rden[j] = fast_rcp(dacc[j][0] + kEps);
+                }
+#pragma unroll
+                for (int j = 0; j < BPW; ++j) {
+                    const int b = wave + kWaves * j;
+                    if (b < M && (FULL || n < C)) {
+                        float* dst = Y + (pair * N + b * C + n) * D + 16 * c + 4 * g;
+                        const f32x4 o = oacc[j];
+                        *reinterpret_cast<f32x4*>(dst) =
+                            f32x4{o[0] * rden[j], o[1] * rden[j], o[2] * rden[j], o[3] * rden[j]};
+                    }
                 }
             }
         }
