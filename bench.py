@@ -55,18 +55,19 @@ def kernel_bytes(w):
 
 def measured_traffic(workload, stage):
     """HBM bytes per launch of `stage` from the committed counter summary, or None when
-    there is none for this workload or the kernel sources changed since it was taken."""
-    from token_level_head_amd.build import source_digest
+    there is none for this workload or the kernel's source changed since it was taken."""
+    from token_level_head_amd.build import kernel_source_digest
 
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", f"counters_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         prof = json.load(f)
-    if prof.get("source_digest") != source_digest():
-        return None
+    prefix = {"fused": "fused_small_kernel", "summaries": "summaries_", "mix": "mix_", "output": "output_"}[stage]
     for name, k in prof["kernels"].items():
-        if name.startswith(stage):
+        if name.startswith(prefix):
+            if k.get("source_digest") != kernel_source_digest(name):
+                return None
             return round(k["traffic_bytes"])
     return None
 

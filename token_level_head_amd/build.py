@@ -23,16 +23,43 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, 
          "-Wall", "-Wno-unused-result"]
 
 
-def source_digest():
-    """SHA-256 over the kernel and ABI sources: identifies which code a profile measured."""
+# The source file that defines each kernel family (by kernel-name prefix); a
+# kernel's measurements stay valid while this file and the shared headers do.
+KERNEL_SOURCES = [
+    ("fused_small_kernel", "fused.hip"),
+    ("summaries_", "summary.hip"),
+    ("mix_", "mix.hip"),
+    ("wsplit_", "mix.hip"),
+    ("output_causal_quad", "causal.hip"),
+    ("output_", "output.hip"),
+    ("decode_", "decode.hip"),
+    ("bwd_", "backward.hip"),
+]
+SHARED_SOURCES = ["common.hpp", "kernels.hpp", "mhla_api.hip", "../../include/mhla.h"]
+
+
+def source_digest(files=None):
+    """SHA-256 (first 16 hex digits) over kernel and ABI sources: identifies which
+    code a profile measured.  Without `files`, every source of the library."""
     import hashlib
 
+    if files is None:
+        files = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".hpp"))) + ["../../include/mhla.h"]
     h = hashlib.sha256()
-    files = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".hpp")))
-    for f in files + ["../../include/mhla.h"]:
+    for f in files:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
+
+
+def kernel_source_digest(kernel_name):
+    """Digest of the file defining `kernel_name` plus the shared headers, or of all
+    sources when the name matches no known family."""
+    base = kernel_name.replace("mhla::", "").replace("void ", "").strip()
+    for prefix, src in KERNEL_SOURCES:
+        if base.startswith(prefix):
+            return source_digest([src] + SHARED_SOURCES)
+    return source_digest()
 
 
 def _run(cmd):

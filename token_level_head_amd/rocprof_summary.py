@@ -12,15 +12,15 @@
 FETCH_SIZE and WRITE_SIZE are scaled by what the same counter reports for the
 plain 1 GiB device copy that ``bench.py --copy-calibration`` runs: bytes =
 counter_KiB * (copy bytes / copy counter KiB).  The counters file records the
-digest of the kernel sources it measured; ``bench.py`` reports the traffic only
-while that digest matches the current sources.
+digest of the source file of each kernel it measured (with the shared headers);
+``bench.py`` reports a kernel's traffic only while that digest matches.
 """
 import argparse
 import json
 import sqlite3
 import sys
 
-from .build import source_digest
+from .build import kernel_source_digest, source_digest
 
 COPY_BYTES = 1 << 30  # bench.py --copy-calibration copies 2^28 float32 values
 
@@ -43,11 +43,13 @@ def cmd_trace(args):
     print(f"# rocprofv3 kernel trace: {args.workload}\n")
     print(f"Command: `{args.cmd}`\n")
     print(f"Kernel sources digest: `{source_digest()}`\n")
-    print("| kernel | calls | avg us | min us | max us | % of GPU time |")
-    print("|---|---|---|---|---|---|")
+    print("| kernel | calls | avg us | min us | max us | % of GPU time | source digest |")
+    print("|---|---|---|---|---|---|---|")
     for r in rows:
-        print(f"| `{short_name(r['name'])}` | {r['calls']} | {r['avg_ns'] / 1e3:.2f} | {r['min_ns'] / 1e3:.2f} | "
-              f"{r['max_ns'] / 1e3:.2f} | {100 * r['total_ns'] / total:.1f} |")
+        name = short_name(r['name'])
+        dig = kernel_source_digest(name) if "mhla::" in r['name'] else ""
+        print(f"| `{name}` | {r['calls']} | {r['avg_ns'] / 1e3:.2f} | {r['min_ns'] / 1e3:.2f} | "
+              f"{r['max_ns'] / 1e3:.2f} | {100 * r['total_ns'] / total:.1f} | {dig} |")
 
 
 def counter_means(db, counter):
@@ -71,7 +73,8 @@ def cmd_counters(args):
         wb = write[name]["avg_kib"] * w_scale
         kernels[short_name(name)] = {"fetch_kib": fetch[name]["avg_kib"], "write_kib": write[name]["avg_kib"],
                                      "fetch_bytes": fb, "write_bytes": wb, "traffic_bytes": fb + wb,
-                                     "dispatches": fetch[name]["dispatches"]}
+                                     "dispatches": fetch[name]["dispatches"],
+                                     "source_digest": kernel_source_digest(short_name(name))}
     out = {"workload": args.workload, "source_digest": source_digest(),
            "copy_reference": {"kernel": copy_name, "bytes": COPY_BYTES, "fetch_kib": fetch[copy_name]["max_kib"],
                               "write_kib": write[copy_name]["max_kib"], "fetch_scale": f_scale,
