@@ -2,6 +2,7 @@
 """Benchmark of the MHLA forward pass on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload dit_s2_256] [--gpus 1]
+    python bench.py --sweep          # N x M throughput grid (the paper's scaling study)
 
 One step is one full forward pass (phi, block summaries, mixing, output) over
 the workload's synthetic batch, with inputs resident in HBM before the timed
@@ -163,6 +164,58 @@ def decode_bench(args, w):
     return 0
 
 
+def sweep_bench(args):
+    """Throughput over a grid of sequence lengths N and block counts M at the DiT-S/2 head
+    shape (H = 6, d = 64, bf16, non-causal), each point on a batch of about 2^18 tokens,
+    relative to M = 1 (global linear attention): the design of the N x M scaling study of
+    the MHLA paper (App. F.4, Table 14), whose cost model puts the mixing term M^2 d^2 next
+    to N d^2.  Inputs: Q, K, V ~ N(0, 1) drawn on the device from a fixed seed; W rows are
+    softmaxes of N(0, 1) logits."""
+    H, d = 6, 64
+    stream = torch.cuda.current_stream()
+    gen = torch.Generator(device="cuda").manual_seed(4242)
+    points = []
+    for N in (256, 1024, 4096, 16384, 65536):
+        B = max(1, (1 << 18) // N)
+        q, k, v = (torch.randn((B, H, N, d), generator=gen, device="cuda").to(torch.bfloat16) for _ in range(3))
+        out = torch.empty((B, H, N, d), dtype=torch.float32, device="cuda")
+        base = None
+        for M in (1, 4, 16, 64, 256):
+            if M > N or N % M:
+                continue
+            W = torch.softmax(torch.randn((M, M), generator=gen, device="cuda", dtype=torch.float64), dim=1).float()
+            for _ in range(args.warmup):
+                mh.mhla_forward(q, k, v, W, out)
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for _ in range(args.steps):
+                    mh.mhla_forward(q, k, v, W, out)
+            graph.replay()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            graph.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / args.steps
+            tok_s = B * N / (ms * 1e-3)
+            base = tok_s if M == 1 else base
+            path = mh.mhla_forward_path(B, H, N, d, M, False, mh.MHLA_DTYPE_BF16)
+            points.append({"N": N, "M": M, "B": B, "M2_lt_N": M * M < N, "ms": round(ms, 5),
+                           "tokens_per_s": round(tok_s, 1), "rel_to_M1": round(tok_s / base, 4),
+                           "path": "fused" if path == mh.MHLA_PATH_FUSED else "staged"})
+            print(f"N={N} M={M} B={B}: {ms * 1e3:.1f} us, {tok_s:.3e} tokens/s, x{tok_s / base:.3f} of M=1",
+                  file=sys.stderr, flush=True)
+            del graph
+        del q, k, v, out
+    line = {"metric": "MHLA fwd tokens/s over an N x M grid at 1 MI355X (DiT-S/2 heads: H=6, d=64, bf16)",
+            "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+            "data": "synthetic", "config": {"workload": "nm_sweep", "H": H, "d": d, "tokens_per_point": 1 << 18},
+            "points": points}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -174,6 +227,9 @@ def main():
     ap.add_argument("--decode", action="store_true",
                     help="time the streaming causal decode step (one token per call) on the workload's "
                          "B, H, d, M, C instead of the forward pass; prints its own JSON line")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time mhla_forward over the N x M grid of the paper's scaling study instead of one "
+                         "workload; prints its own JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy (3x), the reference that scales "
                          "the FETCH_SIZE / WRITE_SIZE counters in counter-collection runs")
@@ -192,6 +248,8 @@ def main():
     mh.load_library()
     if args.decode:
         return decode_bench(args, w)
+    if args.sweep:
+        return sweep_bench(args)
     q, k, v, W = make_inputs(w)
     dt_in = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     qd, kd, vd = (torch.from_numpy(a).to(device="cuda", dtype=dt_in) for a in (q, k, v))

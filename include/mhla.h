@@ -97,10 +97,13 @@ int mhla_forward_f32(const float* q, const float* k, const float* v, const float
  * MHLA_PATH_FUSED; -1 for invalid sizes or dtype. */
 int mhla_forward_path(int64_t B, int64_t H, int64_t N, int64_t d, int64_t M, int causal, int dtype);
 
-/* Bytes of device workspace one staged forward call uses (the fused path uses none): the S and S~ summary
- * arrays (2 * M * B*H * (d*d + d) floats) plus the bf16 hi/lo split of W for
- * the mixing kernel when 64 < M <= 1024 (4 * M * M bytes, rounded up to whole
- * 64 x 32 MFMA tiles; none otherwise); -1 for invalid sizes. */
+/* Bytes of device workspace one staged bf16 forward call uses (the fused path uses none): the S and
+ * S~ summary arrays (2 * M * B*H * (d*d + d) floats), the bf16 hi/lo split of W
+ * for the mixing kernel when 64 < M <= 1024 (4 * M * M bytes, rounded up to
+ * whole 64 x 32 MFMA tiles, then to 256 bytes; none otherwise), and, when
+ * blocks are long and B*H*M small (global linear attention over a long
+ * sequence), the partial summaries of the token segments each block is cut
+ * into (nseg * M * B*H * (d*d + d) floats); -1 for invalid sizes. */
 int64_t mhla_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int64_t M, int causal);
 
 /* Floats in one packed summary vector: d*d + d (S_b followed by z_b). */

@@ -99,6 +99,9 @@ SWEEP = [  # (B, H, N, d, M, causal, dtype)
     (1, 2, 1536, 32, 3, True, "bf16"),  # C = 512 causal at d = 32: running-state output kernel
     (1, 1, 1024, 16, 2, True, "bf16"),  # C = 512 causal at d = 16
     (1, 1, 600, 32, 2, True, "bf16"),   # C = 300 causal at d = 32, ragged last tile
+    (1, 3, 5000, 32, 2, False, "bf16"),  # long blocks on few pairs: 10 token segments, ragged last one
+    (2, 1, 16384, 16, 1, False, "bf16"),  # global linear attention, 64 token segments per block
+    (1, 2, 8192, 64, 4, True, "bf16"),   # causal, 8 token segments per block
     (1, 2, 1280, 16, 80, False, "bf16"),   # 64 < M <= 128: strip mixing, two row tiles per wave
     (1, 1, 2560, 32, 160, True, "bf16"),   # M = 160: three row tiles per wave, causal
     (2, 1, 1536, 64, 192, False, "bf16"),  # M = 192, odd number of 32-deep k-chunks

@@ -11,9 +11,13 @@ namespace mhla {
 constexpr int kDtypeBF16 = 0;
 constexpr int kDtypeF32 = 1;
 
-// Stage 1: S[b][pair][d*d + d] (packed) from K, V [pair][N][d].
+// Stage 1: S[b][pair][d*d + d] (packed) from K, V [pair][N][d].  Long blocks on few
+// (batch, head) pairs are cut into token segments whose partial summaries go to
+// `partial` (summary_partial_bytes() bytes, 16-byte aligned; may be null when that
+// is 0) and are then added into S.
+size_t summary_partial_bytes(int dtype, int64_t BH, int64_t N, int D, int64_t M);
 hipError_t launch_summaries(int dtype, const void* k, const void* v, float* S, int64_t BH, int64_t N,
-                            int D, int64_t M, hipStream_t stream);
+                            int D, int64_t M, float* partial, hipStream_t stream);
 
 // Stage 2: St[i][col] = sum_b W[i,b] S[b][col] (causal: b < i), col < BH * (d*d + d).
 // The bf16 path needs mix_fragment_bytes(M) bytes of device scratch at frag_ws

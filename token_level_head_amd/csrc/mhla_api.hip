@@ -116,9 +116,13 @@ hipError_t device_pool(hipMemPool_t* out) {
     return hipSuccess;
 }
 
-// Two summary arrays (S, St) followed by the mixing kernel's split-W fragments.
-size_t workspace_bytes(int64_t BH, int64_t d, int64_t M) {
-    return 2 * (size_t)(M * BH * summary_floats(d)) * sizeof(float) + mhla::mix_fragment_bytes(M);
+// Two summary arrays (S, St), the mixing kernel's split-W fragments, then the
+// summary kernel's partial sums when it cuts long blocks into token segments.
+size_t frag_bytes_aligned(int64_t M) { return (mhla::mix_fragment_bytes(M) + 255) / 256 * 256; }
+
+size_t workspace_bytes(int dtype, int64_t BH, int64_t N, int64_t d, int64_t M) {
+    return 2 * (size_t)(M * BH * summary_floats(d)) * sizeof(float) + frag_bytes_aligned(M) +
+           mhla::summary_partial_bytes(dtype, BH, N, (int)d, M);
 }
 
 int pool_alloc(void** ptr, size_t bytes, hipStream_t stream) {
@@ -161,15 +165,18 @@ int forward_impl(int dtype, const void* q, const void* k, const void* v, const f
         return ok();
     }
     const size_t arr = (size_t)(M * BH * summary_floats(d)) * sizeof(float);
-    const size_t total = workspace_bytes(BH, d, M);
+    const size_t total = workspace_bytes(dtype, BH, N, d, M);
     void* ws = nullptr;
     int st2 = pool_alloc(&ws, total, stream);
     if (st2) return st2;
     float* S = static_cast<float*>(ws);
     float* St = S + arr / sizeof(float);
     void* frags = St + arr / sizeof(float);
+    float* partial = mhla::summary_partial_bytes(dtype, BH, N, (int)d, M)
+                         ? reinterpret_cast<float*>(static_cast<char*>(frags) + frag_bytes_aligned(M))
+                         : nullptr;
     const char* what = "summary kernel";
-    hipError_t e = mhla::launch_summaries(dtype, k, v, S, BH, N, (int)d, M, stream);
+    hipError_t e = mhla::launch_summaries(dtype, k, v, S, BH, N, (int)d, M, partial, stream);
     if (e == hipSuccess) {
         what = "mixing kernel";
         e = mhla::launch_mix(S, W, St, BH, (int)d, M, causal != 0, dtype == mhla::kDtypeF32, frags, stream);
@@ -201,7 +208,7 @@ int mhla_forward_f32(const float* q, const float* k, const float* v, const float
 int64_t mhla_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int64_t M, int causal) {
     (void)causal;
     if (check_sizes(B, H, N, d, M) != MHLA_OK) return -1;
-    return (int64_t)workspace_bytes(B * H, d, M);
+    return (int64_t)workspace_bytes(mhla::kDtypeBF16, B * H, N, d, M);
 }
 
 int mhla_forward_path(int64_t B, int64_t H, int64_t N, int64_t d, int64_t M, int causal, int dtype) {
@@ -223,8 +230,14 @@ int mhla_block_summaries(const void* k, const void* v, int dtype, float* S, int6
     const size_t s_bytes = (size_t)(M * B * H * summary_floats(d)) * 4;
     if (overlaps(S, s_bytes, k, in_bytes) || overlaps(S, s_bytes, v, in_bytes))
         return fail(MHLA_ERR_INVALID_ARG, "S overlaps an input");
-    hipError_t e = mhla::launch_summaries(dtype, k, v, S, B * H, N, (int)d, M, reinterpret_cast<hipStream_t>(stream));
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    void* partial = nullptr;
+    const size_t pbytes = mhla::summary_partial_bytes(dtype, B * H, N, (int)d, M);
+    if (pbytes && (st = pool_alloc(&partial, pbytes, s))) return st;
+    hipError_t e = mhla::launch_summaries(dtype, k, v, S, B * H, N, (int)d, M, static_cast<float*>(partial), s);
+    hipError_t fe = partial ? hipFreeAsync(partial, s) : hipSuccess;
     if (e != hipSuccess) return hip_fail(e, "summary kernel");
+    if (fe != hipSuccess) return hip_fail(fe, "workspace release");
     return ok();
 }
 

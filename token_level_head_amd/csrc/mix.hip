@@ -17,9 +17,10 @@
 // does it once per call and the mixing waves read their fragments as coalesced
 // 16-byte loads that stay in L2, prefetched one k-chunk ahead together with S.
 // In both kernels the next k-chunk of S is loaded while the current one is
-// multiplied.  Workgroups that share a column strip (different row groups) are
+// multiplied.  A single block (M = 1) is a plain float32 scale.  Workgroups that share a column strip (different row groups) are
 // numbered so that they land on the same XCD and share its L2.  The float32
 // path uses plain float32 FMAs instead.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.hpp"
@@ -440,6 +441,18 @@ __global__ __launch_bounds__(256) void mix_lds_kernel(const float* __restrict__ 
     }
 }
 
+// M = 1: the mixing is a single scale, St = W[0][0] S (causal: no earlier block, St = 0),
+// done as a streaming float32 multiply (exact products, HBM-bound).
+template <bool CAUSAL>
+__global__ __launch_bounds__(256) void mix_scale_kernel(const f32x4* __restrict__ S, const float* __restrict__ W,
+                                                        f32x4* __restrict__ St, int64_t n4) {
+    const float w = CAUSAL ? 0.f : W[0];
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+        const f32x4 x = S[i];
+        St[i] = CAUSAL ? zero4() : f32x4{w * x[0], w * x[1], w * x[2], w * x[3]};
+    }
+}
+
 // Fallback for M > kMaxFragM: each wave splits its W fragments itself.
 template <bool CAUSAL>
 __global__ __launch_bounds__(256) void mix_split_kernel(const float* __restrict__ S, const float* __restrict__ W,
@@ -542,6 +555,17 @@ hipError_t launch_mix(const float* S, const float* W, float* St, int64_t BH, int
         const int64_t threads = ncols / 4;
         mix_f32_kernel<<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream>>>(S, W, St, ncols, (int)M,
                                                                                         causal ? 1 : 0);
+        return hipGetLastError();
+    }
+    if (M == 1) {
+        const int64_t n4 = ncols / 4;  // d*d + d is a multiple of 4
+        const dim3 grid((unsigned)std::min<int64_t>((n4 + 255) / 256, 256 * 8));
+        if (causal)
+            mix_scale_kernel<true><<<grid, dim3(256), 0, stream>>>(reinterpret_cast<const f32x4*>(S), W,
+                                                                   reinterpret_cast<f32x4*>(St), n4);
+        else
+            mix_scale_kernel<false><<<grid, dim3(256), 0, stream>>>(reinterpret_cast<const f32x4*>(S), W,
+                                                                    reinterpret_cast<f32x4*>(St), n4);
         return hipGetLastError();
     }
     using I16 = std::integral_constant<int, 16>;

@@ -21,7 +21,13 @@
 //
 // A block of C tokens may be split over `wpb` waves of one workgroup
 // (wpb in {1, 2, 4}, chosen so that enough waves exist); their partial sums are
-// added in LDS in a fixed order, so results do not depend on scheduling.
+// added in LDS in a fixed order, so results do not depend on scheduling.  When
+// even that leaves too few workgroups (long blocks, few (batch, head) pairs:
+// global linear attention over a long sequence), each block is also cut into
+// `nseg` token segments handled by different workgroups, which write partial
+// summaries in the summary layout; summary_reduce_kernel then adds the partials
+// in segment order.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.hpp"
@@ -64,7 +70,7 @@ __device__ __forceinline__ uint32_t token_bits(const typename TokenWords<P>::typ
 template <int D, bool PIPE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void summaries_bf16_kernel(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, float* __restrict__ S, int64_t BH, int N, int M,
-    int wpb) {
+    int wpb, int nseg, int segC) {
     constexpr int P = D / 16;
     constexpr int L = D * D + D;
     typedef typename TokenWords<P>::type TW;
@@ -74,7 +80,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, n = lane & 15;
     const int per_wg = 4 / wpb;
-    const int64_t unit = (int64_t)blockIdx.x * per_wg + wave / wpb;  // unit = pair * M + block
+    // nseg > 1 only with wpb == 4 (one unit per workgroup): workgroup -> (unit, token segment).
+    const int64_t unit = nseg > 1 ? (int64_t)blockIdx.x / nseg
+                                  : (int64_t)blockIdx.x * per_wg + wave / wpb;  // unit = pair * M + block
+    const int wseg = nseg > 1 ? (int)(blockIdx.x % nseg) : 0;
     const int seg = wave % wpb;
     const bool active = unit < BH * M;
     const int C = N / M;
@@ -94,9 +103,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
     if (active) {
         pair = unit / M;
         blk = unit % M;
-        const int seg_len = ((C + wpb - 1) / wpb + 31) / 32 * 32;
-        const int t_beg = (int)blk * C + seg * seg_len;
-        const int t_end = min((int)blk * C + C, t_beg + seg_len);
+        const int base = (int)blk * C + wseg * segC;            // this workgroup's token range
+        const int len = nseg > 1 ? min(segC, C - wseg * segC) : C;
+        const int seg_len = ((len + wpb - 1) / wpb + 31) / 32 * 32;
+        const int t_beg = base + seg * seg_len;
+        const int t_end = min(base + len, t_beg + seg_len);
         const uint32_t pair_bytes = (uint32_t)N * D * 2;
         const rsrc_t rK = make_rsrc(K + pair * N * D, pair_bytes);
         const rsrc_t rV = make_rsrc(V + pair * N * D, pair_bytes);
@@ -215,7 +226,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
     }
     if (!active || seg != 0) return;
 
-    float* out = S + (blk * BH + pair) * (int64_t)L;
+    // With token segments, S points at the partial array [nseg][M][BH][L].
+    float* out = S + ((int64_t)wseg * M * BH + blk * BH + pair) * (int64_t)L;
 #pragma unroll
     for (int a = 0; a < P; ++a)
 #pragma unroll
@@ -254,30 +266,79 @@ __global__ __launch_bounds__(256) void summaries_f32_kernel(const float* __restr
     }
 }
 
+// S[i] = sum over s of part[s][i] (i < n4 float4 groups), in segment order.
+__global__ __launch_bounds__(256) void summary_reduce_kernel(const f32x4* __restrict__ part, f32x4* __restrict__ S,
+                                                             int64_t n4, int nseg) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n4) return;
+    f32x4 acc = part[i];
+    for (int s = 1; s < nseg; ++s) acc += part[(int64_t)s * n4 + i];
+    S[i] = acc;
+}
+
+namespace {
+
+struct SummarySplit {
+    int wpb, nseg, segC;
+};
+
+// Waves per block (1, 2, 4) and, for long blocks on few (batch, head) pairs, token
+// segments over several workgroups, so that about 1024 workgroups exist.  Every
+// wave keeps at least two 32-token steps; segments are multiples of 128 tokens.
+SummarySplit summary_split(int64_t BH, int64_t N, int64_t M) {
+    const int64_t units = BH * M, C = N / M;
+    SummarySplit sp{1, 1, (int)C};
+    while (sp.wpb < 4 && units * sp.wpb < 4096 && C >= 64 * (2 * sp.wpb)) sp.wpb *= 2;
+    if (sp.wpb == 4 && units < 1024 && C >= 512) {
+        const int64_t want = (1024 + units - 1) / units;
+        const int64_t segC = ((C + want - 1) / want + 127) / 128 * 128;
+        const int64_t seg = (C + segC - 1) / segC;
+        if (seg > 1) {
+            sp.nseg = (int)seg;
+            sp.segC = (int)std::max<int64_t>(segC, 256);
+            sp.nseg = (int)((C + sp.segC - 1) / sp.segC);
+        }
+    }
+    return sp;
+}
+
+}  // namespace
+
+size_t summary_partial_bytes(int dtype, int64_t BH, int64_t N, int D, int64_t M) {
+    if (dtype == kDtypeF32) return 0;
+    const SummarySplit sp = summary_split(BH, N, M);
+    return sp.nseg > 1 ? (size_t)sp.nseg * (size_t)(M * BH) * (size_t)(D * D + D) * sizeof(float) : 0;
+}
+
 hipError_t launch_summaries(int dtype, const void* k, const void* v, float* S, int64_t BH, int64_t N,
-                            int D, int64_t M, hipStream_t stream) {
+                            int D, int64_t M, float* partial, hipStream_t stream) {
     const int64_t units = BH * M;
     if (dtype == kDtypeF32) {
         summaries_f32_kernel<<<dim3((unsigned)units), dim3(256), 0, stream>>>(
             (const float*)k, (const float*)v, S, BH, N, M, D);
         return hipGetLastError();
     }
-    const int64_t C = N / M;
-    // Split blocks over 2 or 4 waves only while there are too few waves to keep
-    // the memory system busy, and each wave keeps at least two 32-token steps.
-    int wpb = 1;
-    while (wpb < 4 && units * wpb < 4096 && C >= 64 * (2 * wpb)) wpb *= 2;
-    const int per_wg = 4 / wpb;
-    const int64_t grid = (units + per_wg - 1) / per_wg;
+    const SummarySplit sp = summary_split(BH, N, M);
+    if (sp.nseg > 1 && !partial) return hipErrorInvalidValue;
+    const int per_wg = 4 / sp.wpb;
+    const int64_t grid = sp.nseg > 1 ? units * sp.nseg : (units + per_wg - 1) / per_wg;
     const int P = D / 16;
-    const size_t lds = wpb > 1 ? (size_t)(4 - per_wg) * 64 * (4 * P * P + P) * sizeof(float) : 0;
+    const size_t lds = sp.wpb > 1 ? (size_t)(4 - per_wg) * 64 * (4 * P * P + P) * sizeof(float) : 0;
     const uint16_t* kk = (const uint16_t*)k;
     const uint16_t* vv = (const uint16_t*)v;
+    float* dst = sp.nseg > 1 ? partial : S;
     switch (D) {
-        case 16: summaries_bf16_kernel<16, true><<<dim3((unsigned)grid), dim3(256), lds, stream>>>(kk, vv, S, BH, (int)N, (int)M, wpb); break;
-        case 32: summaries_bf16_kernel<32, true><<<dim3((unsigned)grid), dim3(256), lds, stream>>>(kk, vv, S, BH, (int)N, (int)M, wpb); break;
-        case 64: summaries_bf16_kernel<64, false><<<dim3((unsigned)grid), dim3(256), lds, stream>>>(kk, vv, S, BH, (int)N, (int)M, wpb); break;
+        case 16: summaries_bf16_kernel<16, true><<<dim3((unsigned)grid), dim3(256), lds, stream>>>(kk, vv, dst, BH, (int)N, (int)M, sp.wpb, sp.nseg, sp.segC); break;
+        case 32: summaries_bf16_kernel<32, true><<<dim3((unsigned)grid), dim3(256), lds, stream>>>(kk, vv, dst, BH, (int)N, (int)M, sp.wpb, sp.nseg, sp.segC); break;
+        case 64: summaries_bf16_kernel<64, false><<<dim3((unsigned)grid), dim3(256), lds, stream>>>(kk, vv, dst, BH, (int)N, (int)M, sp.wpb, sp.nseg, sp.segC); break;
         default: return hipErrorInvalidValue;
+    }
+    if (sp.nseg > 1) {
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int64_t n4 = units * (D * D + D) / 4;
+        summary_reduce_kernel<<<dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream>>>(
+            reinterpret_cast<const f32x4*>(partial), reinterpret_cast<f32x4*>(S), n4, sp.nseg);
     }
     return hipGetLastError();
 }
