@@ -7,8 +7,9 @@
 One step is one full forward pass (phi, block summaries, mixing, output) over
 the workload's synthetic batch, with inputs resident in HBM before the timed
 region.  Prints ONE JSON line with throughput (tokens/s), model TFLOP/s, the
-HBM roofline of the dominant kernel (durations measured with HIP events on the
-launch stream around HIP-graph replays of the timed calls) and the CPU oracle
+HBM roofline of the dominant kernel (its duration measured with HIP events on
+the launch stream: the whole step on the fused path, the stage inside a chain of
+summaries -> mixing -> output calls on the staged path) and the CPU oracle
 timed on this host's cores.
 """
 import argparse
@@ -274,16 +275,6 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1)
 
-    def graph_ms_per_call(fn, calls):
-        """Average duration of `fn` when `calls` calls are captured into one HIP graph and
-        replayed, so the timed region holds the kernels back to back with no host gaps."""
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for _ in range(calls):
-                fn()
-        graph.replay()
-        return elapsed_ms(graph.replay) / calls
-
     run_steps(args.warmup)
     eager_ms = elapsed_ms(lambda: run_steps(args.steps)) / args.steps
     # The timed steps run as one HIP graph replay (the launch-bound short workloads would
@@ -305,12 +296,13 @@ def main():
     tokens_s = w.tokens / (ms * 1e-3)
     tflops = model_flops(w) / (ms * 1e-3) / 1e12
 
-    # ---- per-stage durations: each stage called `steps` times, once inside one HIP
-    # graph replay and once as eager launches (the stages are idempotent), between
-    # two events on the launch stream; the smaller average is the stage's time
-    # without host gaps, comparable with rocprofv3 --kernel-trace.  When mhla_forward takes the fused
-    # path these stage timings are reported for reference only (`staged_kernels`);
-    # the step itself is the fused kernel. ----
+    # ---- per-stage durations inside the chain: `steps` iterations of summaries -> mixing
+    # -> output on the launch stream, with HIP events between the stages.  Each stage
+    # consumes the previous one's output, as inside mhla_forward, so the caches hold what
+    # they would in a forward pass (timing a stage alone, repeated, would let the 256 MiB
+    # Infinity Cache keep its inputs).  When mhla_forward takes the fused path these
+    # stage timings are reported for reference only (`staged_kernels`); the step itself
+    # is the fused kernel. ----
     stream = torch.cuda.current_stream()
     L = w.d * w.d + w.d
     S = torch.empty(w.M * w.B * w.H * L, dtype=torch.float32, device="cuda")
@@ -321,12 +313,29 @@ def main():
         lambda: mh.mhla_mix_summaries(S, Wd, St, w.B * w.H, w.d, causal=w.causal, precise=(w.dtype == "f32")),
         lambda: mh.mhla_output(qd, kd, vd, St, Wd, out, causal=w.causal),
     ]
-    kms = {}
-    for name, f in zip(names, stages):
-        for _ in range(args.warmup):
+    for _ in range(args.warmup):
+        for f in stages:
             f()
-        torch.cuda.synchronize()
-        kms[name] = min(graph_ms_per_call(f, args.steps), elapsed_ms(lambda: [f() for _ in range(args.steps)]) / args.steps)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # A pre-roll of device fills keeps the GPU busy while the host enqueues the timed
+    # stages, so no host launch gap falls between two events.  `pre_done` still pending
+    # once everything is enqueued shows that the GPU never waited for the host.
+    filler = torch.empty(1 << 26, dtype=torch.float32, device="cuda")
+    for _ in range(64):
+        filler.fill_(0.0)
+    pre_done = torch.cuda.Event()
+    pre_done.record(stream)
+    for it in range(args.steps):
+        evs[it][0].record(stream)
+        for j, f in enumerate(stages):
+            f()
+            evs[it][j + 1].record(stream)
+    gapless = not pre_done.query()
+    torch.cuda.synchronize()
+    del filler
+    kms = {name: sum(evs[it][j].elapsed_time(evs[it][j + 1]) for it in range(args.steps)) / args.steps
+           for j, name in enumerate(names)}
     kb = kernel_bytes(w)
 
     def entry(name, t_ms):
@@ -381,6 +390,7 @@ def main():
         "path": "fused" if path == mh.MHLA_PATH_FUSED else "staged",
         "kernels": kernels,
         "staged_kernels": staged,
+        "stage_timing": "in chain, " + ("no host gaps" if gapless else "host gaps possible"),
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -99,7 +99,7 @@ int mhla_forward_path(int64_t B, int64_t H, int64_t N, int64_t d, int64_t M, int
 
 /* Bytes of device workspace one staged bf16 forward call uses (the fused path uses none): the S and
  * S~ summary arrays (2 * M * B*H * (d*d + d) floats), the bf16 hi/lo split of W
- * for the mixing kernel when 64 < M <= 1024 (4 * M * M bytes, rounded up to
+ * for the mixing kernel when 256 < M <= 1024 (4 * M * M bytes, rounded up to
  * whole 64 x 32 MFMA tiles, then to 256 bytes; none otherwise), and, when
  * blocks are long and B*H*M small (global linear attention over a long
  * sequence), the partial summaries of the token segments each block is cut

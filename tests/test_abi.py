@@ -39,7 +39,7 @@ def test_version_and_sizes(mhla_lib):
     # two summary arrays, plus the split-W fragments (4 * M * M bytes) when 64 < M <= 1024
     assert mh.mhla_workspace_bytes(64, 6, 256, 64, 16) == 2 * 16 * 384 * (64 * 64 + 64) * 4
     assert mh.mhla_workspace_bytes(8, 16, 8192, 64, 64, 1) == 2 * 64 * 128 * (64 * 64 + 64) * 4
-    assert mh.mhla_workspace_bytes(1, 6, 65536, 64, 256) == 2 * 256 * 6 * (64 * 64 + 64) * 4 + 4 * 256 * 256
+    assert mh.mhla_workspace_bytes(1, 6, 65536, 64, 256) == 2 * 256 * 6 * (64 * 64 + 64) * 4
     assert mh.mhla_workspace_bytes(1, 1, 512 * 16, 16, 512) == 2 * 512 * (16 * 16 + 16) * 4 + 4 * 512 * 512
     # global linear attention over 65536 tokens on 24 pairs: each block is cut into 43 segments
     # of 1536 tokens whose partial summaries are part of the workspace

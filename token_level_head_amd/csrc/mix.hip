@@ -13,9 +13,11 @@
 // significant bits per operand, well inside the float32 summaries' needs).
 //
 // W is split into per-lane MFMA fragments (causal mask applied there).  For
-// M <= 64 each workgroup does that itself into LDS; for larger M a small kernel
-// does it once per call and the mixing waves read their fragments as coalesced
-// 16-byte loads that stay in L2, prefetched one k-chunk ahead together with S.
+// M <= 64 each workgroup does that itself into LDS; for 64 < M <= 256 each wave
+// splits its rows of W in registers as it streams them from L2 (the strip of S
+// is what lives in LDS); for larger M a small kernel does it once per call and
+// the mixing waves read their fragments as coalesced 16-byte loads that stay in
+// L2, prefetched one k-chunk ahead together with S.
 // In both kernels the next k-chunk of S is loaded while the current one is
 // multiplied.  A single block (M = 1) is a plain float32 scale.  Workgroups that share a column strip (different row groups) are
 // numbered so that they land on the same XCD and share its L2.  The float32
@@ -31,6 +33,10 @@ namespace mhla {
 namespace {
 
 constexpr int64_t kMaxFragM = 1024;  // larger M uses the fragment-free fallback kernel
+constexpr int kWideMaxNT = 8;        // 64 < M <= 256 kernel: column tiles of 16 per workgroup
+constexpr int kWideMaxKC = 8;        // ... k-chunks of 32 (M <= 256)
+constexpr int kWideTasks = 2;        // ... strip-load tasks per thread: 16 * KC * NT / 512
+constexpr int kWideRT = 2;           // ... row tiles of 16 per wave (8 waves: 256 rows)
 
 template <int KSTEP>
 struct MixOps;
@@ -50,7 +56,7 @@ struct MixOps<16> {
 }  // namespace
 
 size_t mix_fragment_bytes(int64_t M) {
-    if (M <= 64 || M > kMaxFragM) return 0;  // small M splits W in LDS; huge M in every wave
+    if (M <= 256 || M > kMaxFragM) return 0;  // M <= 256 splits W in LDS or registers; huge M in every wave
     const int64_t RG = (M + 63) / 64, KC = (M + 31) / 32;  // RT = 4, 32-deep k-chunks
     return (size_t)(RG * 4 * KC * 64 * 2) * 16;
 }
@@ -206,118 +212,154 @@ __global__ __launch_bounds__(256) void mix_frag_kernel(const float* __restrict__
 }
 
 
-// 64 < M <= 256: one workgroup per strip of 32 columns and all M rows.  The strip of
-// S (M x 32 floats) is read from HBM once, split into bf16 hi + lo once and kept
-// in LDS transposed to [column][block], so that each MFMA B operand (8
-// consecutive blocks of one column) is one 16-byte LDS read.  Wave w owns rows
-// 16*RT*w .. 16*RT*(w+1) - 1 (RT = ceil(M / 64)) and streams its W fragments
-// (split once per call by wsplit_kernel, resident in L2) one k-chunk ahead.
-template <int RT, bool CAUSAL>
-__global__ __launch_bounds__(256) void mix_strip_kernel(const float* __restrict__ S, const bf16x8* __restrict__ frags,
-                                                        float* __restrict__ St, int64_t ncols, int M, int KC) {
-    constexpr int J = 2;                   // columns per lane: MFMA jj uses column J*n + jj
-    extern __shared__ __align__(16) uint4 strip[];  // hi then lo: [32 columns][RS4 x 16 bytes]
-    const int RS4 = 4 * KC + 1;            // 32*KC bf16 of one column, + 16 bytes against bank conflicts
-    uint4* sh = strip;
-    uint4* sl = strip + 32 * RS4;
+// 64 < M <= 256: one workgroup per strip of 16*NT columns (NT <= 8) and all M rows.
+// The strip of S (M x 16*NT floats) is read from HBM once, split into bf16 hi + lo
+// once and kept in LDS transposed to [column][block] (about 135 KiB: one
+// workgroup of eight waves per CU), so that each MFMA B operand (8 consecutive
+// blocks of one column) is one 16-byte LDS read.  Wave w owns rows 32w .. 32w + 31 and reads its
+// rows of W as float32 straight from L2 (W is at most 256 KiB), two k-chunks ahead,
+// splitting them into hi + lo A operands in registers; every A operand then serves
+// the NT column tiles of the strip.
+template <int NT, bool CAUSAL>
+__global__ __launch_bounds__(512) void mix_wide_kernel(const float* __restrict__ S, const float* __restrict__ W,
+                                                       float* __restrict__ St, int64_t ncols, int M, int KC) {
+    __shared__ __align__(16) uint4 strip[2 * 16 * kWideMaxNT * (4 * kWideMaxKC + 1)];  // hi then lo
+    const int RS4 = 4 * KC + 1;  // 32*KC bf16 of one column, + 16 bytes against bank conflicts
+    uint4* const sh = strip;
+    uint4* const sl = strip + 16 * NT * RS4;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, n = lane & 15;
-    const int64_t col0 = (int64_t)blockIdx.x * 32;
+    const int64_t col0 = (int64_t)blockIdx.x * 16 * NT;
 
-    // 1. strip -> LDS: task (8-block group bg, 4-column group cg), rows 8bg .. 8bg+7.
-    for (int task = threadIdx.x; task < 32 * KC; task += 256) {
-        const int bg = task >> 3, cg = task & 7;
+    // 1. strip -> LDS: task (8-block group bg, 4-column group cg), blocks 8bg .. 8bg+7;
+    //    a thread's (at most kWideTasks) tasks issue all their loads before any is used.
+    const int ntask = 4 * KC * 4 * NT;
+    f32x4 x[kWideTasks][8];
+#pragma unroll
+    for (int q = 0; q < kWideTasks; ++q) {
+        const int task = threadIdx.x + 512 * q;
+        const int bg = task / (4 * NT), cg = task % (4 * NT);
         const int64_t c = col0 + 4 * cg;
-        f32x4 x[8];
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
             const int b = 8 * bg + r;
-            x[r] = load_or_zero(reinterpret_cast<const f32x4*>(S + (int64_t)b * ncols + c), b < M && c < ncols,
-                                reinterpret_cast<const f32x4*>(S));
+            x[q][r] = load_or_zero(reinterpret_cast<const f32x4*>(S + (int64_t)b * ncols + c),
+                                   task < ntask && b < M && c < ncols, reinterpret_cast<const f32x4*>(S));
         }
-        issue_fence();
+    }
+    issue_fence();
 #pragma unroll
-        for (int xx = 0; xx < 4; ++xx) {
-            uint32_t h[4], l[4];
+    for (int q = 0; q < kWideTasks; ++q) {
+        const int task = threadIdx.x + 512 * q;
+        if (task < ntask) {
+            const int bg = task / (4 * NT), cg = task % (4 * NT);
 #pragma unroll
-            for (int r2 = 0; r2 < 4; ++r2) split2_bf16(x[2 * r2][xx], x[2 * r2 + 1][xx], h[r2], l[r2]);
-            sh[(4 * cg + xx) * RS4 + bg] = uint4{h[0], h[1], h[2], h[3]};
-            sl[(4 * cg + xx) * RS4 + bg] = uint4{l[0], l[1], l[2], l[3]};
+            for (int xx = 0; xx < 4; ++xx) {
+                uint32_t h[4], l[4];
+#pragma unroll
+                for (int r2 = 0; r2 < 4; ++r2) split2_bf16(x[q][2 * r2][xx], x[q][2 * r2 + 1][xx], h[r2], l[r2]);
+                sh[(4 * cg + xx) * RS4 + bg] = uint4{h[0], h[1], h[2], h[3]};
+                sl[(4 * cg + xx) * RS4 + bg] = uint4{l[0], l[1], l[2], l[3]};
+            }
         }
     }
     __syncthreads();
 
-    // 2. this wave's rows
-    const int i0 = 16 * RT * wave;
-    if (i0 >= M) return;  // whole wave; no barriers below
-    const int imax = min(M, i0 + 16 * RT);
-    const int kend = CAUSAL ? imax - 1 : M;  // causal rows use b < i <= imax - 1
+    // 2. this wave's rows (no barriers below)
+    const int i0 = 16 * kWideRT * wave;
+    if (i0 >= M) return;
+    const int rows = min(16 * kWideRT, M - i0);
+    const int nrt = (rows + 15) / 16;
+    const int kend = CAUSAL ? min(M, i0 + rows - 1) : M;  // causal rows use b < i <= i0 + rows - 1
     const int kcn = (kend + 31) / 32;
-    const int64_t col = col0 + J * n;
+    const bool vec = (M & 3) == 0;  // rows of W 16-byte aligned
 
-    f32x4 acc[RT][J];
+    f32x4 acc[kWideRT][NT];
 #pragma unroll
-    for (int r = 0; r < RT; ++r)
+    for (int r = 0; r < kWideRT; ++r)
 #pragma unroll
-        for (int j = 0; j < J; ++j) acc[r][j] = zero4();
+        for (int t = 0; t < NT; ++t) acc[r][t] = zero4();
 
-    struct Frags {
-        bf16x8 wh[RT], wl[RT];
-    };
-    auto load = [&](int kc, Frags& f) {
+    // A operands of k-chunk kc: lane (g, n) row tile r holds W[i0 + 16r + n][32kc + 8g + e], e < 8.
+    auto load_w = [&](int kc, f32x4 (&w)[kWideRT][2]) {
 #pragma unroll
-        for (int r = 0; r < RT; ++r) {
-            if (i0 + 16 * r < imax) {  // uniform
-                const bf16x8* p = frags + ((int64_t)((i0 / 16 + r) * KC + kc) * 64 + lane) * 2;
-                f.wh[r] = p[0];
-                f.wl[r] = p[1];
+        for (int r = 0; r < kWideRT; ++r) {
+            const int i = i0 + 16 * r + n;
+            const int b0 = 32 * kc + 8 * g;
+            if (vec) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    w[r][h] = load_or_zero(reinterpret_cast<const f32x4*>(W + (int64_t)i * M + b0 + 4 * h),
+                                           i < M && b0 + 4 * h < M, reinterpret_cast<const f32x4*>(W));
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    w[r][e / 4][e % 4] = load_or_zero(W + (int64_t)i * M + b0 + e, i < M && b0 + e < M, W);
             }
         }
     };
-    auto compute = [&](int kc, const Frags& f) {
-        bf16x8 bh[J], bl[J];
+    auto compute = [&](int kc, const f32x4 (&w)[kWideRT][2]) {
+        // Entries past M were loaded as zero; causal rows also drop b >= i.
+        bf16x8 ah[kWideRT], al[kWideRT];
 #pragma unroll
-        for (int j = 0; j < J; ++j) {
-            bh[j] = __builtin_bit_cast(bf16x8, sh[(J * n + j) * RS4 + 4 * kc + g]);
-            bl[j] = __builtin_bit_cast(bf16x8, sl[(J * n + j) * RS4 + 4 * kc + g]);
+        for (int r = 0; r < kWideRT; ++r) {
+            const int i = i0 + 16 * r + n;
+            uint32_t h[4], l[4];
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                float x0 = w[r][e2 / 2][(2 * e2) % 4], x1 = w[r][e2 / 2][(2 * e2 + 1) % 4];
+                if constexpr (CAUSAL) {
+                    const int b = 32 * kc + 8 * g + 2 * e2;
+                    x0 = b < i ? x0 : 0.f;
+                    x1 = b + 1 < i ? x1 : 0.f;
+                }
+                split2_bf16(x0, x1, h[e2], l[e2]);
+            }
+            ah[r] = __builtin_bit_cast(bf16x8, u32x4{h[0], h[1], h[2], h[3]});
+            al[r] = __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], l[2], l[3]});
         }
 #pragma unroll
-        for (int r = 0; r < RT; ++r) {
-            if (i0 + 16 * r < imax) {  // uniform
+        for (int t = 0; t < NT; ++t) {
+            const bf16x8 bh = __builtin_bit_cast(bf16x8, sh[(16 * t + n) * RS4 + 4 * kc + g]);
+            const bf16x8 bl = __builtin_bit_cast(bf16x8, sl[(16 * t + n) * RS4 + 4 * kc + g]);
 #pragma unroll
-                for (int j = 0; j < J; ++j) {
-                    acc[r][j] = mfma32(f.wh[r], bh[j], acc[r][j]);
-                    acc[r][j] = mfma32(f.wh[r], bl[j], acc[r][j]);
-                    acc[r][j] = mfma32(f.wl[r], bh[j], acc[r][j]);
+            for (int r = 0; r < kWideRT; ++r) {
+                if (r < nrt) {  // uniform
+                    acc[r][t] = mfma32(ah[r], bh, acc[r][t]);
+                    acc[r][t] = mfma32(ah[r], bl, acc[r][t]);
+                    acc[r][t] = mfma32(al[r], bh, acc[r][t]);
                 }
             }
         }
     };
     {
-        Frags fa, fb;
-        if (kcn > 0) load(0, fa);
-        for (int kc = 0; kc < kcn; kc += 2) {
-            if (kc + 1 < kcn) load(kc + 1, fb);
-            issue_fence();
-            compute(kc, fa);
-            if (kc + 1 < kcn) {
-                if (kc + 2 < kcn) load(kc + 2, fa);
+        // W two k-chunks ahead (ring of three; the chunk loop is unrolled, at most kWideMaxKC)
+        f32x4 wr[3][kWideRT][2];
+        if (kcn > 0) load_w(0, wr[0]);
+        if (kcn > 1) load_w(1, wr[1]);
+#pragma unroll
+        for (int kc = 0; kc < kWideMaxKC; ++kc) {
+            if (kc < kcn) {  // uniform
+                if (kc + 2 < kcn) load_w(kc + 2, wr[(kc + 2) % 3]);
                 issue_fence();
-                compute(kc + 1, fb);
+                compute(kc, wr[kc % 3]);
             }
         }
     }
 
-    if (col >= ncols) return;
 #pragma unroll
-    for (int r = 0; r < RT; ++r) {
+    for (int t = 0; t < NT; ++t) {
+        const int64_t col = col0 + 16 * t + n;
+        if (col >= ncols) continue;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = i0 + 16 * r + 4 * g + i;
-            if (row < imax)
-                *reinterpret_cast<float2*>(St + (int64_t)row * ncols + col) = make_float2(acc[r][0][i], acc[r][1][i]);
+        for (int r = 0; r < kWideRT; ++r) {
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int row = 16 * r + 4 * g + ii;
+                if (row < rows) St[(int64_t)(i0 + row) * ncols + col] = acc[r][t][ii];
+            }
         }
     }
 }
@@ -596,6 +638,31 @@ hipError_t launch_mix(const float* S, const float* W, float* St, int64_t BH, int
             run(I32{}, I4{}, I4{});
         return hipGetLastError();
     }
+    if (M <= 256) {  // 64 < M <= 256: wide strips, W split per wave
+        const int KC = (int)((M + 31) / 32);
+        const int64_t tiles16 = (ncols + 15) / 16;
+        // strips of NT column tiles: one strip per CU when that takes at most kWideMaxNT tiles
+        const int nt = (int)std::min<int64_t>(kWideMaxNT, std::max<int64_t>(1, (tiles16 + 255) / 256));
+        const dim3 grid((unsigned)((tiles16 + nt - 1) / nt));
+        auto run = [&](auto nt_c) {
+            constexpr int NT = decltype(nt_c)::value;
+            if (causal)
+                mix_wide_kernel<NT, true><<<grid, dim3(512), 0, stream>>>(S, W, St, ncols, (int)M, KC);
+            else
+                mix_wide_kernel<NT, false><<<grid, dim3(512), 0, stream>>>(S, W, St, ncols, (int)M, KC);
+        };
+        switch (nt) {
+            case 1: run(std::integral_constant<int, 1>{}); break;
+            case 2: run(std::integral_constant<int, 2>{}); break;
+            case 3: run(std::integral_constant<int, 3>{}); break;
+            case 4: run(std::integral_constant<int, 4>{}); break;
+            case 5: run(std::integral_constant<int, 5>{}); break;
+            case 6: run(std::integral_constant<int, 6>{}); break;
+            case 7: run(std::integral_constant<int, 7>{}); break;
+            default: run(std::integral_constant<int, 8>{}); break;
+        }
+        return hipGetLastError();
+    }
     if (M <= kMaxFragM) {
         if (!frag_ws) return hipErrorInvalidValue;
         constexpr int KSTEP = 32, RT = 4, J = 2;
@@ -609,25 +676,6 @@ hipError_t launch_mix(const float* S, const float* W, float* St, int64_t BH, int
             wsplit_kernel<KSTEP, RT, true><<<sgrid, dim3(256), 0, stream>>>(W, frags, (int)M, RG, KC);
         else
             wsplit_kernel<KSTEP, RT, false><<<sgrid, dim3(256), 0, stream>>>(W, frags, (int)M, RG, KC);
-        if (M <= 256) {
-            const dim3 g2((unsigned)((ncols + 31) / 32));
-            const size_t lds = (size_t)2 * 32 * (4 * KC + 1) * 16;
-            auto run = [&](auto rt_c) {
-                constexpr int RT2 = decltype(rt_c)::value;
-                if (causal)
-                    mix_strip_kernel<RT2, true><<<g2, dim3(256), lds, stream>>>(S, frags, St, ncols, (int)M, KC);
-                else
-                    mix_strip_kernel<RT2, false><<<g2, dim3(256), lds, stream>>>(S, frags, St, ncols, (int)M, KC);
-            };
-            const int rt = (int)((M + 63) / 64);
-            if (rt <= 2)
-                run(std::integral_constant<int, 2>{});
-            else if (rt == 3)
-                run(std::integral_constant<int, 3>{});
-            else
-                run(std::integral_constant<int, 4>{});
-            return hipGetLastError();
-        }
         const int64_t ntiles = (ncols + 16 * J - 1) / (16 * J);
         const int64_t nctg = (ntiles + 3) / 4;
         const dim3 grid((unsigned)(((nctg + 7) / 8) * 8 * RG));
