@@ -45,17 +45,17 @@ constexpr int kQuadMaxOwn = kQuadMaxTiles / 4;
 __device__ __forceinline__ int own_tile(int wave, int s) { return 8 * (s >> 1) + ((s & 1) ? 7 - wave : wave); }
 
 // 4P consecutive bf16 of one token row, as 2P words.
-template <int P>
+template <int P, bool NT>
 __device__ __forceinline__ void load_row(rsrc_t r, uint32_t off, uint32_t (&w)[2 * P]) {
     if constexpr (P == 4) {
-        const u32x4 a = buf_load128(r, off), b = buf_load128(r, off + 16);
+        const u32x4 a = buf_load128<NT>(r, off), b = buf_load128<NT>(r, off + 16);
         w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
         w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
     } else if constexpr (P == 2) {
-        const u32x4 a = buf_load128(r, off);
+        const u32x4 a = buf_load128<NT>(r, off);
         w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
     } else {
-        const u32x2 a = buf_load64(r, off);
+        const u32x2 a = buf_load64<NT>(r, off);
         w[0] = a.x; w[1] = a.y;
     }
 }
@@ -111,7 +111,7 @@ size_t causal_quad_lds_bytes(int D, int64_t C) {
 
 bool causal_quad_applicable(int64_t C) { return C <= 16 * kQuadMaxTiles; }
 
-template <int D>
+template <int D, bool NT>
 __global__ __launch_bounds__(256) void output_causal_quad_kernel(const uint16_t* __restrict__ Q,
                                                                  const uint16_t* __restrict__ K,
                                                                  const uint16_t* __restrict__ V,
@@ -159,14 +159,14 @@ __global__ __launch_bounds__(256) void output_causal_quad_kernel(const uint16_t*
         sl[pi * 64 + lane] = __builtin_bit_cast(uint4, lo);
     }
     uint32_t qraw[2 * P];  // Q row of the first own tile, loaded before the barrier
-    load_row<P>(rQ, off_if(16 * own_tile(wave, 0) + n < C, row_off(own_tile(wave, 0), n)), qraw);
+    load_row<P, NT>(rQ, off_if(16 * own_tile(wave, 0) + n < C, row_off(own_tile(wave, 0), n)), qraw);
 #pragma unroll
     for (int s = 0; s < kQuadMaxOwn; ++s) {
         const int t = own_tile(wave, s);
         if (t < T) {  // uniform
             uint32_t kraw[2 * P];
             const bool ok = 16 * t + n < C;
-            load_row<P>(rK, off_if(ok, row_off(t, n)), kraw);
+            load_row<P, NT>(rK, off_if(ok, row_off(t, n)), kraw);
             bf16x8 ak[KS];
             phi_operand<P, KS>(kraw, ok, ak);
 #pragma unroll
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(256) void output_causal_quad_kernel(const uint16_t*
         phi_operand<P, KS>(qraw, true, aq);
         if (s + 1 < kQuadMaxOwn) {  // next own tile's Q row, in flight while this tile computes
             const int tn = own_tile(wave, s + 1);
-            load_row<P>(rQ, off_if(tn < T && 16 * tn + n < C, row_off(tn, n)), qraw);
+            load_row<P, NT>(rQ, off_if(tn < T && 16 * tn + n < C, row_off(tn, n)), qraw);
         }
 
         f32x4 acc[P], dacc = zero4();
@@ -254,13 +254,13 @@ __global__ __launch_bounds__(256) void output_causal_quad_kernel(const uint16_t*
                 const bool ok = (e < 4 || two) && row < C;
                 const uint32_t off = off_if(ok, ((uint32_t)(bstart + row) * D + P * n) * 2);
                 if constexpr (P == 4) {
-                    const u32x2 x = buf_load64(rV, off);
+                    const u32x2 x = buf_load64<NT>(rV, off);
                     vr[e][0] = x.x;
                     vr[e][1] = x.y;
                 } else if constexpr (P == 2) {
-                    vr[e][0] = buf_load32(rV, off);
+                    vr[e][0] = buf_load32<NT>(rV, off);
                 } else {
-                    vr[e][0] = buf_load16(rV, off);
+                    vr[e][0] = buf_load16<NT>(rV, off);
                 }
             }
 #pragma unroll
@@ -292,11 +292,11 @@ __global__ __launch_bounds__(256) void output_causal_quad_kernel(const uint16_t*
                 const float rd = fast_rcp(dacc[r] + kEps);
                 float* dst = Yp + (int64_t)(bstart + row) * D + P * n;
                 if constexpr (P == 4) {
-                    *reinterpret_cast<f32x4*>(dst) = f32x4{acc[0][r] * rd, acc[1][r] * rd, acc[2][r] * rd, acc[3][r] * rd};
+                    store_out(dst, f32x4{acc[0][r] * rd, acc[1][r] * rd, acc[2][r] * rd, acc[3][r] * rd});
                 } else if constexpr (P == 2) {
-                    *reinterpret_cast<float2*>(dst) = make_float2(acc[0][r] * rd, acc[1][r] * rd);
+                    store_out(dst, f32x2{acc[0][r] * rd, acc[1][r] * rd});
                 } else {
-                    dst[0] = acc[0][r] * rd;
+                    store_out(dst, acc[0][r] * rd);
                 }
             }
         }
@@ -310,12 +310,21 @@ hipError_t launch_causal_quad(const void* q, const void* k, const void* v, const
     const uint16_t* vv = (const uint16_t*)v;
     const size_t lds = causal_quad_lds_bytes(D, N / M);
     const dim3 grid((unsigned)(BH * M)), block(256);
+    const bool nt = stream_token_inputs(BH, N, D, 2);
+#define MHLA_QUAD_CASE(DD)                                                                                     \
+    case DD:                                                                                                   \
+        if (nt)                                                                                                \
+            output_causal_quad_kernel<DD, true><<<grid, block, lds, stream>>>(qq, kk, vv, St, W, out, BH, (int)N, (int)M);  \
+        else                                                                                                   \
+            output_causal_quad_kernel<DD, false><<<grid, block, lds, stream>>>(qq, kk, vv, St, W, out, BH, (int)N, (int)M); \
+        break;
     switch (D) {
-        case 16: output_causal_quad_kernel<16><<<grid, block, lds, stream>>>(qq, kk, vv, St, W, out, BH, (int)N, (int)M); break;
-        case 32: output_causal_quad_kernel<32><<<grid, block, lds, stream>>>(qq, kk, vv, St, W, out, BH, (int)N, (int)M); break;
-        case 64: output_causal_quad_kernel<64><<<grid, block, lds, stream>>>(qq, kk, vv, St, W, out, BH, (int)N, (int)M); break;
+        MHLA_QUAD_CASE(16)
+        MHLA_QUAD_CASE(32)
+        MHLA_QUAD_CASE(64)
         default: return hipErrorInvalidValue;
     }
+#undef MHLA_QUAD_CASE
     return hipGetLastError();
 }
 

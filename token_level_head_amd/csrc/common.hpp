@@ -84,6 +84,17 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x4& a, const bf16x4& b, const 
                                                      __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
 }
 
+// Stores of the attention output Y, which nothing later in the pass reads: marked
+// non-temporal, so that the output stream does not evict the block summaries that
+// the next stage reads back from the caches.
+__device__ __forceinline__ void store_out(float* p, f32x4 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+}
+__device__ __forceinline__ void store_out(float* p, f32x2 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x2*>(p));
+}
+__device__ __forceinline__ void store_out(float* p, float v) { __builtin_nontemporal_store(v, p); }
+
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 // Masked load without a branch: the address falls back to `safe` (any valid,
@@ -118,17 +129,23 @@ __device__ __forceinline__ uint32_t off_if(bool ok, uint32_t byte_off) { return 
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// NT selects the non-temporal policy (for token inputs streamed once; see
+// stream_token_inputs in kernels.hpp).
+template <bool NT = false>
 __device__ __forceinline__ uint16_t buf_load16(rsrc_t r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+    return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, NT ? 2 : 0);
 }
+template <bool NT = false>
 __device__ __forceinline__ uint32_t buf_load32(rsrc_t r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, NT ? 2 : 0);
 }
+template <bool NT = false>
 __device__ __forceinline__ u32x2 buf_load64(rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, NT ? 2 : 0));
 }
+template <bool NT = false>
 __device__ __forceinline__ u32x4 buf_load128(rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, NT ? 2 : 0));
 }
 
 // Keeps the scheduler from moving instructions across this point; placed after a
@@ -140,6 +157,14 @@ template <typename T>
 __device__ __forceinline__ T load_or_zero(const T* p, bool ok, const T* safe) {
     using U = typename MaskBits<sizeof(T)>::type;
     const U v = __builtin_bit_cast(U, *(ok ? p : safe));
+    return __builtin_bit_cast(T, (U)(v & (U)(ok ? ~0u : 0u)));
+}
+// The same for token inputs (Q, K, V); NT as for the buffer loads.
+template <bool NT, typename T>
+__device__ __forceinline__ T load_token_or_zero(const T* p, bool ok, const T* safe) {
+    using U = typename MaskBits<sizeof(T)>::type;
+    const U* q = reinterpret_cast<const U*>(ok ? p : safe);
+    const U v = NT ? __builtin_nontemporal_load(q) : *q;
     return __builtin_bit_cast(T, (U)(v & (U)(ok ? ~0u : 0u)));
 }
 

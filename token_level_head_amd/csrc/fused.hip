@@ -316,8 +316,7 @@ __global__ __launch_bounds__(64 * kWaves) void fused_small_kernel(const uint16_t
                     if (b < M && (FULL || n < C)) {
                         float* dst = Y + (pair * N + b * C + n) * D + 16 * c + 4 * g;
                         const f32x4 o = oacc[j];
-                        *reinterpret_cast<f32x4*>(dst) =
-                            f32x4{o[0] * rden[j], o[1] * rden[j], o[2] * rden[j], o[3] * rden[j]};
+                        store_out(dst, f32x4{o[0] * rden[j], o[1] * rden[j], o[2] * rden[j], o[3] * rden[j]});
                     }
                 }
             }

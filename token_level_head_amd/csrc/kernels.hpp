@@ -11,6 +11,15 @@ namespace mhla {
 constexpr int kDtypeBF16 = 0;
 constexpr int kDtypeF32 = 1;
 
+// Token inputs (Q, K, V together) larger than the 256 MiB Infinity Cache are read
+// with the non-temporal policy, so that streaming them does not evict the block
+// summaries that the next stage reads back.  Smaller inputs are read normally: they
+// may be cache-resident (just written by whatever produced them) and stay so.
+constexpr int64_t kInfinityCacheBytes = int64_t(256) << 20;
+inline bool stream_token_inputs(int64_t BH, int64_t N, int D, int esize) {
+    return 3 * BH * N * D * esize > kInfinityCacheBytes;
+}
+
 // Stage 1: S[b][pair][d*d + d] (packed) from K, V [pair][N][d].  Long blocks on few
 // (batch, head) pairs are cut into token segments whose partial summaries go to
 // `partial` (summary_partial_bytes() bytes, 16-byte aligned; may be null when that

@@ -23,16 +23,16 @@
 namespace mhla {
 
 // 4P consecutive bf16 values starting at p (P = d/16): 8, 16 or 32 bytes.
-template <int P>
+template <int P, bool NT>
 __device__ __forceinline__ void load_group(const uint16_t* p, bool ok, const uint16_t* safe, uint16_t (&out)[4 * P]) {
     if constexpr (P == 1) {
-        const uint2 x = load_or_zero(reinterpret_cast<const uint2*>(p), ok, reinterpret_cast<const uint2*>(safe));
+        const uint2 x = load_token_or_zero<NT>(reinterpret_cast<const uint2*>(p), ok, reinterpret_cast<const uint2*>(safe));
         out[0] = (uint16_t)x.x; out[1] = (uint16_t)(x.x >> 16);
         out[2] = (uint16_t)x.y; out[3] = (uint16_t)(x.y >> 16);
     } else {
 #pragma unroll
         for (int h = 0; h < P / 2; ++h) {
-            const uint4 x = load_or_zero(reinterpret_cast<const uint4*>(p + 8 * h), ok, reinterpret_cast<const uint4*>(safe));
+            const uint4 x = load_token_or_zero<NT>(reinterpret_cast<const uint4*>(p + 8 * h), ok, reinterpret_cast<const uint4*>(safe));
             const uint32_t w[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
@@ -76,18 +76,18 @@ __device__ __forceinline__ void store_rows(float* Yp, int t0, int bend, int g, i
         if (row < bend) {
             float* dst = Yp + row * D + P * n + jb0;
             if constexpr (PJ == 4) {
-                *reinterpret_cast<f32x4*>(dst) = f32x4{acc[0][i] * r, acc[1][i] * r, acc[2][i] * r, acc[3][i] * r};
+                store_out(dst, f32x4{acc[0][i] * r, acc[1][i] * r, acc[2][i] * r, acc[3][i] * r});
             } else if constexpr (PJ == 2) {
-                *reinterpret_cast<float2*>(dst) = make_float2(acc[0][i] * r, acc[1][i] * r);
+                store_out(dst, f32x2{acc[0][i] * r, acc[1][i] * r});
             } else {
-                dst[0] = acc[0][i] * r;
+                store_out(dst, acc[0][i] * r);
             }
         }
     }
 }
 
 // Offsets inside one (batch, head) pair fit in 32 bits (the API limits N*d).
-template <int D>
+template <int D, bool NT>
 __global__ __launch_bounds__(256) void output_bf16_kernel(const uint16_t* __restrict__ Q,
                                                           const float* __restrict__ St, float* __restrict__ Y,
                                                           int64_t BH, int N, int64_t M, int tpw, int wpu) {
@@ -132,7 +132,7 @@ __global__ __launch_bounds__(256) void output_bf16_kernel(const uint16_t* __rest
         const int tq = t0 + n;
         const bool qok = tq < bend;
         uint16_t qr[FL];
-        load_group<P>(Qp + tq * D + FL * g, qok, Q, qr);
+        load_group<P, NT>(Qp + tq * D + FL * g, qok, Q, qr);
         issue_fence();
         bf16x8 aq[KS];
         float den = 0.f;
@@ -177,7 +177,7 @@ __global__ __launch_bounds__(256) void output_bf16_kernel(const uint16_t* __rest
 // masked product (phi(Q) phi(K)^T) V covers the inclusive prefix exactly; its
 // weights are carried as bf16 hi + lo and its row sums come from the same
 // rounded values (chunkwise form of App. C).
-template <int D>
+template <int D, bool NT>
 __global__ __launch_bounds__(256) void output_causal_kernel(const uint16_t* __restrict__ Q,
                                                             const uint16_t* __restrict__ K,
                                                             const uint16_t* __restrict__ V,
@@ -238,7 +238,7 @@ __global__ __launch_bounds__(256) void output_causal_kernel(const uint16_t* __re
         uint16_t* buf = &lds[tile & 1][bw][0][0];
         {  // phi of this lane's chunk into LDS
             const bool ok = active && t0 + crow < bend;
-            const uint4 x = load_or_zero(reinterpret_cast<const uint4*>(src + (t0 + crow) * D + ccol), ok,
+            const uint4 x = load_token_or_zero<NT>(reinterpret_cast<const uint4*>(src + (t0 + crow) * D + ccol), ok,
                                          reinterpret_cast<const uint4*>(Q));
             const uint32_t wv[4] = {x.x, x.y, x.z, x.w};
             uint32_t o[4];
@@ -255,7 +255,7 @@ __global__ __launch_bounds__(256) void output_causal_kernel(const uint16_t* __re
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int tok = t0 + 4 * g + e;
-            bv4[e] = bits_to_bf16(load_or_zero(Vp + tok * D + P * n + jb, active && tok < bend, V));
+            bv4[e] = bits_to_bf16(load_token_or_zero<NT>(Vp + tok * D + P * n + jb, active && tok < bend, V));
         }
         __syncthreads();
 
@@ -387,13 +387,17 @@ hipError_t launch_output(int dtype, const void* q, const void* k, const void* v,
     const uint16_t* qq = (const uint16_t*)q;
     const uint16_t* kk = (const uint16_t*)k;
     const uint16_t* vv = (const uint16_t*)v;
+    const bool nt = stream_token_inputs(BH, N, D, 2);
     if (causal && causal_quad_applicable(N / M))
         return launch_causal_quad(q, k, v, St, W, out, BH, N, D, M, stream);
     if (causal) {  // d/16 waves per block, 4 / (d/16) blocks per workgroup
         const int bpw = 4 / (D / 16);
         const dim3 grid((unsigned)((BH * M + bpw - 1) / bpw));
-#define MHLA_LAUNCH_OUT(DD) \
-    output_causal_kernel<DD><<<grid, dim3(256), 0, stream>>>(qq, kk, vv, St, W, out, BH, (int)N, M)
+#define MHLA_LAUNCH_OUT(DD)                                                                                   \
+    if (nt)                                                                                                   \
+        output_causal_kernel<DD, true><<<grid, dim3(256), 0, stream>>>(qq, kk, vv, St, W, out, BH, (int)N, M);  \
+    else                                                                                                      \
+        output_causal_kernel<DD, false><<<grid, dim3(256), 0, stream>>>(qq, kk, vv, St, W, out, BH, (int)N, M)
         switch (D) {
             case 16: MHLA_LAUNCH_OUT(16); break;
             case 32: MHLA_LAUNCH_OUT(32); break;
@@ -409,8 +413,11 @@ hipError_t launch_output(int dtype, const void* q, const void* k, const void* v,
     const int tpw = min(ntiles, 4);
     const int wpu = (ntiles + tpw - 1) / tpw;
     const dim3 grid((unsigned)((BH * M * wpu + 3) / 4));
-#define MHLA_LAUNCH_OUT(DD) \
-    output_bf16_kernel<DD><<<grid, dim3(256), 0, stream>>>(qq, St, out, BH, (int)N, M, tpw, wpu)
+#define MHLA_LAUNCH_OUT(DD)                                                                        \
+    if (nt)                                                                                        \
+        output_bf16_kernel<DD, true><<<grid, dim3(256), 0, stream>>>(qq, St, out, BH, (int)N, M, tpw, wpu); \
+    else                                                                                           \
+        output_bf16_kernel<DD, false><<<grid, dim3(256), 0, stream>>>(qq, St, out, BH, (int)N, M, tpw, wpu)
     switch (D) {
         case 16: MHLA_LAUNCH_OUT(16); break;
         case 32: MHLA_LAUNCH_OUT(32); break;

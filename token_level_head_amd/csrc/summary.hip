@@ -44,11 +44,11 @@ struct TokenWords<2> { typedef uint32_t type; };
 template <>
 struct TokenWords<1> { typedef uint16_t type; };
 
-template <int P>
+template <int P, bool NT>
 __device__ __forceinline__ typename TokenWords<P>::type load_token(rsrc_t r, uint32_t off) {
-    if constexpr (P == 4) return buf_load64(r, off);
-    else if constexpr (P == 2) return buf_load32(r, off);
-    else return buf_load16(r, off);
+    if constexpr (P == 4) return buf_load64<NT>(r, off);
+    else if constexpr (P == 2) return buf_load32<NT>(r, off);
+    else return buf_load16<NT>(r, off);
 }
 
 // Feature f (< P) of a token's raw bits, as a float.
@@ -67,7 +67,7 @@ __device__ __forceinline__ uint32_t token_bits(const typename TokenWords<P>::typ
     else return w;
 }
 
-template <int D, bool PIPE>
+template <int D, bool PIPE, bool NT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void summaries_bf16_kernel(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, float* __restrict__ S, int64_t BH, int N, int M,
     int wpb, int nseg, int segC) {
@@ -118,8 +118,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
             for (int e = 0; e < 8; ++e) {
                 const int tok = t + 4 * e + g;
                 const uint32_t off = off_if(tok < t_end, ((uint32_t)tok * D + P * n) * 2);
-                kr[e] = load_token<P>(rK, off);
-                vr[e] = load_token<P>(rV, off);
+                kr[e] = load_token<P, NT>(rK, off);
+                vr[e] = load_token<P, NT>(rV, off);
             }
         };
         auto compute = [&](const TW (&kr)[8], const TW (&vr)[8], int t, auto masked_c) {
@@ -159,22 +159,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
         };
         int t = t_beg;
         if constexpr (PIPE) {
-            // Two register sets: the loads of step i + 1 are in flight while step i computes.
+            // Two register sets: the loads of step s + 1 are issued before step s computes,
+            // unconditionally (a step past the segment reads zero), so that every path
+            // keeps the same loads in flight and each wait covers the current step only.
+            const int nsteps = (t_end - t_beg + 31) / 32;
             TW k0[8], v0[8], k1[8], v1[8];
             load(k0, v0, t);
-            while (true) {
-                const bool more = t + 32 < t_end;
-                if (more) load(k1, v1, t + 32);
+            for (int s = 0; s < nsteps; s += 2, t += 64) {
+                load(k1, v1, t + 32);
                 issue_fence();
                 run(k0, v0, t);
-                if (!more) break;
-                t += 32;
-                const bool more2 = t + 32 < t_end;
-                if (more2) load(k0, v0, t + 32);
+                if (s + 1 >= nsteps) break;
+                load(k0, v0, t + 64);
                 issue_fence();
-                run(k1, v1, t);
-                if (!more2) break;
-                t += 32;
+                run(k1, v1, t + 32);
             }
         } else {
             for (; t + 32 <= t_end; t += 32) {
@@ -327,12 +325,23 @@ hipError_t launch_summaries(int dtype, const void* k, const void* v, float* S, i
     const uint16_t* kk = (const uint16_t*)k;
     const uint16_t* vv = (const uint16_t*)v;
     float* dst = sp.nseg > 1 ? partial : S;
+    const bool nt = stream_token_inputs(BH, N, D, 2);
+#define MHLA_SUMMARIES_CASE(DD, PIPE)                                                                           \
+    case DD:                                                                                                  \
+        if (nt)                                                                                               \
+            summaries_bf16_kernel<DD, PIPE, true><<<dim3((unsigned)grid), dim3(256), lds, stream>>>(          \
+                kk, vv, dst, BH, (int)N, (int)M, sp.wpb, sp.nseg, sp.segC);                                   \
+        else                                                                                                  \
+            summaries_bf16_kernel<DD, PIPE, false><<<dim3((unsigned)grid), dim3(256), lds, stream>>>(         \
+                kk, vv, dst, BH, (int)N, (int)M, sp.wpb, sp.nseg, sp.segC);                                   \
+        break;
     switch (D) {
-        case 16: summaries_bf16_kernel<16, true><<<dim3((unsigned)grid), dim3(256), lds, stream>>>(kk, vv, dst, BH, (int)N, (int)M, sp.wpb, sp.nseg, sp.segC); break;
-        case 32: summaries_bf16_kernel<32, true><<<dim3((unsigned)grid), dim3(256), lds, stream>>>(kk, vv, dst, BH, (int)N, (int)M, sp.wpb, sp.nseg, sp.segC); break;
-        case 64: summaries_bf16_kernel<64, false><<<dim3((unsigned)grid), dim3(256), lds, stream>>>(kk, vv, dst, BH, (int)N, (int)M, sp.wpb, sp.nseg, sp.segC); break;
+        MHLA_SUMMARIES_CASE(16, true)
+        MHLA_SUMMARIES_CASE(32, true)
+        MHLA_SUMMARIES_CASE(64, false)
         default: return hipErrorInvalidValue;
     }
+#undef MHLA_SUMMARIES_CASE
     if (sp.nseg > 1) {
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
