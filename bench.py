@@ -356,6 +356,18 @@ def main():
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(w.key, dom)}
 
+    # Device-copy bandwidth on this GPU (2^28 floats = 1 GiB read and 1 GiB written, far
+    # larger than the caches): the practical ceiling of streaming kernels, reported next to
+    # the 8 TB/s datasheet figure that `frac` uses.
+    csrc = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+    cdst = torch.empty_like(csrc)
+    cdst.copy_(csrc)
+    copy_ms = elapsed_ms(lambda: [cdst.copy_(csrc) for _ in range(5)]) / 5
+    del csrc, cdst
+    copy_gbs = 2 * (1 << 30) / (copy_ms * 1e-3) / 1e9
+    roofline["copy_GBps"] = round(copy_gbs, 1)
+    roofline["copy_frac"] = round(achieved / copy_gbs, 4)
+
     if args.copy_calibration:
         src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)

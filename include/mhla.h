@@ -92,6 +92,30 @@ int mhla_forward_f32(const float* q, const float* k, const float* v, const float
                      int64_t B, int64_t H, int64_t N, int64_t d, int64_t M, int causal,
                      mhla_stream_t stream);
 
+/* Options of mhla_forward_ex (bit flags, combined with |). */
+enum {
+    MHLA_OPT_CAUSAL = 1,        /* the causal variant (as causal != 0 above) */
+    MHLA_OPT_NO_NORMALIZER = 2, /* y_t = phi(q_t)^T S~_i (plus, causal, W[i,i] phi(q_t)^T P_t), with
+                                   no division by phi(q_t)^T z~_i + 1e-6: the form §4.1 allows for
+                                   long sequences (its remark on the output), for training stability */
+    MHLA_OPT_OUT_BF16 = 4       /* out holds bfloat16 bit patterns, each value rounded to nearest
+                                   even, instead of float32; the arithmetic is unchanged */
+};
+
+/*
+ * The forward pass with options.  dtype (MHLA_DTYPE_BF16 or _F32) describes q, k
+ * and v; out is [B][H][N][d] float32, or bfloat16 with MHLA_OPT_OUT_BF16.
+ * mhla_forward(..., causal, ...) and mhla_forward_ex(..., MHLA_DTYPE_BF16, ...,
+ * causal ? MHLA_OPT_CAUSAL : 0, ...) give bit-identical results (likewise
+ * mhla_forward_f32 with MHLA_DTYPE_F32).  Unknown option bits give
+ * MHLA_ERR_INVALID_ARG.  Paths, workspace and all other conventions as for
+ * mhla_forward; mhla_forward_path() applies unchanged (the options do not change
+ * the path).
+ */
+int mhla_forward_ex(const void* q, const void* k, const void* v, int dtype, const float* W, void* out,
+                    int64_t B, int64_t H, int64_t N, int64_t d, int64_t M, unsigned options,
+                    mhla_stream_t stream);
+
 /* Which path mhla_forward (dtype MHLA_DTYPE_BF16) or mhla_forward_f32
  * (MHLA_DTYPE_F32; always staged) takes for these sizes: MHLA_PATH_STAGED or
  * MHLA_PATH_FUSED; -1 for invalid sizes or dtype. */

@@ -57,6 +57,8 @@ class Oracle:
         self.lib.mhla_oracle_mix.argtypes = [_f64p, _f64p, _f32p, _L, _L, _L, ctypes.c_int, _f64p, _f64p]
         self.lib.mhla_oracle_forward.argtypes = [_f32p, _f32p, _f32p, _f32p, _f64p, _L, _L, _L, _L, _L,
                                                  ctypes.c_int, ctypes.c_int]
+        self.lib.mhla_oracle_forward_ex.argtypes = [_f32p, _f32p, _f32p, _f32p, _f64p, _L, _L, _L, _L, _L,
+                                                    ctypes.c_int, ctypes.c_int]
 
     def phi(self, x):
         return self.lib.mhla_oracle_phi(float(x))
@@ -65,14 +67,17 @@ class Oracle:
     def _f32(a):
         return np.ascontiguousarray(a, dtype=np.float32)
 
-    def forward(self, q, k, v, W, causal=False, nthreads=1):
-        """q, k, v: [B, H, N, d] float32; W: [M, M] float32 -> float64 [B, H, N, d]."""
+    def forward(self, q, k, v, W, causal=False, nthreads=1, normalize=True):
+        """q, k, v: [B, H, N, d] float32; W: [M, M] float32 -> float64 [B, H, N, d].
+
+        normalize=False drops the normaliser (MHLA §4.1, remark on the output)."""
         q, k, v, W = (self._f32(a) for a in (q, k, v, W))
         B, H, N, d = q.shape
         M = W.shape[0]
         out = np.empty((B, H, N, d), dtype=np.float64)
-        rc = self.lib.mhla_oracle_forward(_ptr(q, _f32p), _ptr(k, _f32p), _ptr(v, _f32p), _ptr(W, _f32p),
-                                          _ptr(out, _f64p), B, H, N, d, M, int(bool(causal)), int(nthreads))
+        opts = (1 if causal else 0) | (0 if normalize else 2)
+        rc = self.lib.mhla_oracle_forward_ex(_ptr(q, _f32p), _ptr(k, _f32p), _ptr(v, _f32p), _ptr(W, _f32p),
+                                             _ptr(out, _f64p), B, H, N, d, M, opts, int(nthreads))
         if rc != 0:
             raise ValueError("mhla_oracle_forward rejected its arguments")
         return out

@@ -49,12 +49,14 @@ def weight_matrix(q, k, W, blk, causal, rows=None):
     return mix * sim
 
 
-def forward(q, k, v, W, causal=False, blk=None, rows=None):
+def forward(q, k, v, W, causal=False, blk=None, rows=None, normalize=True):
     """Y for q, k, v [B, H, N, d] (any float dtype) and W [M, M].
 
     ``blk`` gives each token's block (default: contiguous equal blocks); ``rows``
     restricts the output to those token indices (same for every (batch, head)).
-    Returns binary64 [B, H, len(rows), d].
+    ``normalize=False`` returns A V itself, without the row normalisation (the form
+    §4.1 of the MHLA page allows for long sequences).  Returns binary64
+    [B, H, len(rows), d].
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -67,5 +69,5 @@ def forward(q, k, v, W, causal=False, blk=None, rows=None):
     for b in range(B):
         for h in range(H):
             A = weight_matrix(q[b, h], k[b, h], W, blk, causal, rows)
-            out[b, h] = (A @ v[b, h]) / (A.sum(axis=1, keepdims=True) + EPS)
+            out[b, h] = (A @ v[b, h]) / (A.sum(axis=1, keepdims=True) + EPS) if normalize else A @ v[b, h]
     return out

@@ -87,7 +87,7 @@ int mhla_oracle_mix(const double* S, const double* z, const float* W, long BH, l
 
 /* One (batch, head) pair; q, k, v, out point at its [N][d] slices. */
 static int forward_pair(const float* q, const float* k, const float* v, const float* W,
-                        double* out, long N, long d, long M, int causal) {
+                        double* out, long N, long d, long M, int causal, int normalise) {
     const long C = N / M;
     double* S = (double*)malloc(sizeof(double) * M * d * d);
     double* z = (double*)malloc(sizeof(double) * M * d);
@@ -127,7 +127,9 @@ static int forward_pair(const float* q, const float* k, const float* v, const fl
                 double num = 0.0;
                 for (long r = 0; r < d; ++r)
                     num += fq[r] * (causal ? Si[r * d + c] + wii * P[r * d + c] : Si[r * d + c]);
-                out[t * d + c] = num / den;
+                /* Without the normaliser (the [MHLA] §4.1 remark on long sequences) the
+                   output is the mixed numerator itself. */
+                out[t * d + c] = normalise ? num / den : num;
             }
         }
     }
@@ -137,10 +139,13 @@ done:
     return rc;
 }
 
-int mhla_oracle_forward(const float* q, const float* k, const float* v, const float* W,
-                        double* out, long B, long H, long N, long d, long M, int causal,
-                        int nthreads) {
+int mhla_oracle_forward_ex(const float* q, const float* k, const float* v, const float* W,
+                           double* out, long B, long H, long N, long d, long M, int options,
+                           int nthreads) {
     if (B < 1 || H < 1 || !sizes_ok(B * H, N, d, M) || !q || !k || !v || !W || !out) return -1;
+    if (options & ~(MHLA_ORACLE_CAUSAL | MHLA_ORACLE_NO_NORMALISER)) return -1;
+    const int causal = (options & MHLA_ORACLE_CAUSAL) != 0;
+    const int normalise = (options & MHLA_ORACLE_NO_NORMALISER) == 0;
     const long BH = B * H;
     int failures = 0;
     (void)nthreads;
@@ -150,7 +155,14 @@ int mhla_oracle_forward(const float* q, const float* k, const float* v, const fl
 #endif
     for (long p = 0; p < BH; ++p) {
         const long off = p * N * d;
-        failures += forward_pair(q + off, k + off, v + off, W, out + off, N, d, M, causal) != 0;
+        failures += forward_pair(q + off, k + off, v + off, W, out + off, N, d, M, causal, normalise) != 0;
     }
     return failures ? -1 : 0;
+}
+
+int mhla_oracle_forward(const float* q, const float* k, const float* v, const float* W,
+                        double* out, long B, long H, long N, long d, long M, int causal,
+                        int nthreads) {
+    return mhla_oracle_forward_ex(q, k, v, W, out, B, H, N, d, M, causal ? MHLA_ORACLE_CAUSAL : 0,
+                                  nthreads);
 }

@@ -58,6 +58,17 @@ int mhla_oracle_forward(const float* q, const float* k, const float* v, const fl
                         double* out, long B, long H, long N, long d, long M, int causal,
                         int nthreads);
 
+/* Options of mhla_oracle_forward_ex (bit flags). */
+#define MHLA_ORACLE_CAUSAL 1        /* the causal variant ([MHLA] App. C) */
+#define MHLA_ORACLE_NO_NORMALISER 2 /* y_t = phi(q_t)^T S~_i (plus the causal prefix term), no
+                                       division: [MHLA] §4.1, remark on the output for long sequences */
+
+/* The forward pass with options; mhla_oracle_forward(.., causal, ..) is
+ * mhla_oracle_forward_ex(.., causal ? MHLA_ORACLE_CAUSAL : 0, ..). */
+int mhla_oracle_forward_ex(const float* q, const float* k, const float* v, const float* W,
+                           double* out, long B, long H, long N, long d, long M, int options,
+                           int nthreads);
+
 #ifdef __cplusplus
 }
 #endif

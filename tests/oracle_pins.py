@@ -339,6 +339,40 @@ def pin_rank_bounds(orc):
     assert np.linalg.matrix_rank(A) == 64
 
 
+# ---- the form without the normaliser (MHLA §4.1, remark on the output) ----
+
+def pin_no_normaliser_bruteforce(orc):
+    """Without the normaliser: linear-time oracle == A V of the explicit definition."""
+    for i, (B, H, N, d, M, causal) in enumerate(BRUTE_CASES):
+        q, k, v, W = _inputs(B, H, N, d, M, causal, seed=300 + i)
+        y = orc.forward(q, k, v, W, causal=causal, normalize=False)
+        ref = bruteforce.forward(q, k, v, W, causal=causal, normalize=False)
+        assert rel_err(y, ref) < 1e-12, (B, H, N, d, M, causal, rel_err(y, ref))
+
+
+def pin_no_normaliser_ratio(orc):
+    """The normalised output is the bare numerator divided by the bare numerator for V = 1, plus 1e-6."""
+    for causal in (False, True):
+        q, k, v, W = _inputs(2, 1, 96, 8, 6, causal, seed=310)
+        y = orc.forward(q, k, v, W, causal=causal)
+        num = orc.forward(q, k, v, W, causal=causal, normalize=False)
+        den = orc.forward(q, k, np.ones_like(v), W, causal=causal, normalize=False)[..., :1]
+        assert rel_err(y, num / (den + EPS)) < 1e-13, causal
+
+
+def pin_no_normaliser_one_token_per_block(orc):
+    """M = N, W = I, no normaliser: y_t = a_t v_t with a_t = phi(q_t).phi(k_t)."""
+    N, d = 24, 5
+    q, k, v, _ = _inputs(1, 1, N, d, N, False, seed=311)
+    eye = np.eye(N, dtype=np.float32)
+    for causal in (False, True):
+        y = orc.forward(q, k, v, eye, causal=causal, normalize=False)[0, 0]
+        for t in range(N):
+            a = sum(_phi_scalar(float(q[0, 0, t, r])) * _phi_scalar(float(k[0, 0, t, r])) for r in range(d))
+            expect = a * v[0, 0, t].astype(np.float64)
+            assert np.max(np.abs(y[t] - expect)) <= 1e-14 * np.max(np.abs(expect)), (causal, t)
+
+
 def _recover(phiq, num):
     """Solve phi(Q) X = num for X (phi(Q) square and invertible)."""
     return np.linalg.solve(phiq, num)

@@ -1,0 +1,121 @@
+"""GPU parity of mhla_forward_ex: the form without the normaliser and the bfloat16 output.
+
+The form without the normaliser (MHLA §4.1, the remark on the output for long
+sequences) is compared with the oracle's own option on the same seeded inputs,
+to the bars of the plain pass (1e-5 for float32 inputs, 3e-3 for bfloat16).  The
+bfloat16 output must equal the float32 output of the same call rounded to
+nearest even, bit for bit, and so lies within the plain bar plus the bfloat16
+unit roundoff (half an ulp: at most 2^-8 of |y|, so of max|Y|) of the oracle.
+Every case also checks that mhla_forward_ex without options gives
+mhla_forward's bits.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import token_level_head_amd as mh
+from token_level_head_amd.workloads import WORKLOADS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 3e-3}
+NTHREADS = min(16, os.cpu_count() or 1)
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "these tests need the MI355X"
+    mh.load_library()
+    yield
+
+
+def rel(y, ref):
+    return float(np.max(np.abs(y.astype(np.float64) - ref)) / np.max(np.abs(ref)))
+
+
+def round_bf16_bits(x):
+    """float32 -> bfloat16 bit patterns, round to nearest even (finite inputs)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+CASES = [  # (B, H, N, d, M, causal, dtype): one per kernel the options pass through
+    (4, 2, 256, 64, 16, False, "bf16"),   # fused path
+    (1, 2, 120, 32, 10, False, "bf16"),   # fused path, blocks of 12 tokens
+    (2, 1, 1024, 32, 16, False, "bf16"),  # staged, non-causal output kernel
+    (1, 2, 500, 64, 4, True, "bf16"),     # causal, one masked product per block
+    (1, 2, 1536, 32, 3, True, "bf16"),    # causal, running-state output kernel (C = 512)
+    (2, 3, 128, 64, 8, True, "f32"),      # float32 path
+    (2, 1, 160, 16, 10, False, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}H{}N{}d{}M{}{}{}".format(*c[:5], "c" if c[5] else "", c[6]))
+def test_options(orc, case):
+    B, H, N, d, M, causal, dtype = case
+    w = WORKLOADS["tiny_f32"].shrink(B=B, H=H, N=N, d=d, M=M, causal=causal, dtype=dtype, seed=900 + N + M)
+    q, k, v, W = make_inputs(w)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    qd, kd, vd = (torch.from_numpy(a).to("cuda", tdt) for a in (q, k, v))
+    Wd = torch.from_numpy(W).cuda()
+    say(f"[variants] B={B} H={H} N={N} d={d} M={M} causal={causal} dtype={dtype}")
+
+    plain = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    (mh.mhla_forward if dtype == "bf16" else mh.mhla_forward_f32)(qd, kd, vd, Wd, plain, causal=causal)
+    ex = torch.full(q.shape, float("nan"), dtype=torch.float32, device="cuda")
+    mh.mhla_forward_ex(qd, kd, vd, Wd, ex, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(plain, ex), "mhla_forward_ex without options differs from mhla_forward"
+
+    for normalize in (True, False):
+        y32 = torch.full(q.shape, float("nan"), dtype=torch.float32, device="cuda")
+        y16 = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+        mh.mhla_forward_ex(qd, kd, vd, Wd, y32, causal=causal, normalize=normalize)
+        mh.mhla_forward_ex(qd, kd, vd, Wd, y16, causal=causal, normalize=normalize)
+        torch.cuda.synchronize()
+        a32 = y32.cpu().numpy()
+        b16 = y16.view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.all(np.isfinite(a32))
+        assert np.array_equal(b16, round_bf16_bits(a32)), "bf16 output is not the rounded float32 output"
+        ref = orc.forward(q, k, v, W, causal=causal, nthreads=NTHREADS, normalize=normalize)
+        e32 = rel(a32, ref)
+        e16 = rel((b16.astype(np.uint32) << 16).view(np.float32), ref)
+        say(f"[variants]   normalize={normalize}: f32 out {e32:.3e}, bf16 out {e16:.3e}")
+        assert e32 <= TOL[dtype], (normalize, e32)
+        assert e16 <= TOL[dtype] + 2.0 ** -8, (normalize, e16)
+
+
+def test_options_full_size_dit(orc):
+    """The 256 x 256 DiT-S/2 workload without the normaliser, bfloat16 output."""
+    w = WORKLOADS["dit_s2_256"]
+    q, k, v, W = make_inputs(w)
+    qd, kd, vd = (torch.from_numpy(a).to("cuda", torch.bfloat16) for a in (q, k, v))
+    Wd = torch.from_numpy(W).cuda()
+    y16 = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
+    mh.mhla_forward_ex(qd, kd, vd, Wd, y16, normalize=False)
+    torch.cuda.synchronize()
+    y = y16.float().cpu().numpy()
+    ref = orc.forward(q, k, v, W, nthreads=NTHREADS, normalize=False)
+    e = rel(y, ref)
+    say(f"[variants] dit_s2_256 without normaliser, bf16 out: {e:.3e}")
+    assert e <= TOL["bf16"] + 2.0 ** -8
+
+
+def test_unknown_option_rejected():
+    q = torch.zeros((1, 1, 16, 16), dtype=torch.bfloat16, device="cuda")
+    W = torch.ones((1, 1), dtype=torch.float32, device="cuda")
+    out = torch.zeros((1, 1, 16, 16), dtype=torch.float32, device="cuda")
+    lib = mh.load_library()
+    import ctypes
+    st = lib.mhla_forward_ex(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(q.data_ptr()),
+                             ctypes.c_void_p(q.data_ptr()), 0, ctypes.c_void_p(W.data_ptr()),
+                             ctypes.c_void_p(out.data_ptr()), 1, 1, 16, 16, 1, 1 << 10, None)
+    assert st == mh.MHLA_ERR_INVALID_ARG

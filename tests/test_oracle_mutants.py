@@ -38,6 +38,10 @@ MUTANTS = {
     "eps_per_block": ("den += MHLA_ORACLE_EPS;", "den += MHLA_ORACLE_EPS * M;"),
     "query_phi_skipped": ("fq[r] = mhla_oracle_phi((double)q[t * d + r]);", "fq[r] = (double)q[t * d + r] + 1.0;"),
     "causal_key_phi_skipped": ("fk[r] = mhla_oracle_phi((double)k[t * d + r]);", "fk[r] = (double)k[t * d + r];"),
+    "no_normaliser_ignored": ("out[t * d + c] = normalise ? num / den : num;", "out[t * d + c] = num / den;"),
+    "no_normaliser_always": ("out[t * d + c] = normalise ? num / den : num;", "out[t * d + c] = num;"),
+    "no_normaliser_option_ignored": ("const int normalise = (options & MHLA_ORACLE_NO_NORMALISER) == 0;",
+                                     "const int normalise = 1;"),
 }
 
 

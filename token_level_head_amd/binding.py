@@ -23,6 +23,9 @@ MHLA_DTYPE_BF16 = 0
 MHLA_DTYPE_F32 = 1
 MHLA_PATH_STAGED = 0
 MHLA_PATH_FUSED = 1
+MHLA_OPT_CAUSAL = 1
+MHLA_OPT_NO_NORMALIZER = 2
+MHLA_OPT_OUT_BF16 = 4
 
 # Every symbol include/mhla.h declares, with (restype, argtypes).
 _P = ctypes.c_void_p
@@ -31,6 +34,7 @@ _I = ctypes.c_int
 SIGNATURES = {
     "mhla_forward": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _P]),
     "mhla_forward_f32": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _P]),
+    "mhla_forward_ex": (_I, [_P, _P, _P, _I, _P, _P, _I64, _I64, _I64, _I64, _I64, ctypes.c_uint, _P]),
     "mhla_workspace_bytes": (_I64, [_I64, _I64, _I64, _I64, _I64, _I]),
     "mhla_forward_path": (_I, [_I64, _I64, _I64, _I64, _I64, _I, _I]),
     "mhla_summary_floats": (_I64, [_I64]),
@@ -106,6 +110,20 @@ def mhla_forward_f32(q, k, v, W, out, causal=False, stream=None):
     B, H, N, d, M = _dims(q, W)
     _check(load_library().mhla_forward_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(W), _ptr(out), B, H, N, d, M,
                                            int(bool(causal)), _stream(stream)))
+    return out
+
+
+def mhla_forward_ex(q, k, v, W, out, causal=False, normalize=True, stream=None):
+    """q, k, v [B, H, N, d] bf16 or float32; W [M, M] float32; out [B, H, N, d] float32 or
+    bfloat16 (which selects the bf16 output).  normalize=False drops the normaliser."""
+    B, H, N, d, M = _dims(q, W)
+    opts = (MHLA_OPT_CAUSAL if causal else 0) | (0 if normalize else MHLA_OPT_NO_NORMALIZER)
+    if out.dtype == torch.bfloat16:
+        opts |= MHLA_OPT_OUT_BF16
+    elif out.dtype != torch.float32:
+        raise TypeError(f"unsupported output dtype {out.dtype}")
+    _check(load_library().mhla_forward_ex(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(W), _ptr(out),
+                                          B, H, N, d, M, opts, _stream(stream)))
     return out
 
 

@@ -116,7 +116,7 @@ __global__ __launch_bounds__(256) void output_causal_quad_kernel(const uint16_t*
                                                                  const uint16_t* __restrict__ K,
                                                                  const uint16_t* __restrict__ V,
                                                                  const float* __restrict__ St,
-                                                                 const float* __restrict__ W, float* __restrict__ Y,
+                                                                 const float* __restrict__ W, OutSpec o,
                                                                  int64_t BH, int N, int M) {
     constexpr int P = D / 16;
     constexpr int KS = D >= 32 ? D / 32 : 1;
@@ -142,7 +142,7 @@ __global__ __launch_bounds__(256) void output_causal_quad_kernel(const uint16_t*
     const rsrc_t rQ = make_rsrc(Q + pair * N * D, pair_bytes);
     const rsrc_t rK = make_rsrc(K + pair * N * D, pair_bytes);
     const rsrc_t rV = make_rsrc(V + pair * N * D, pair_bytes);
-    float* Yp = Y + pair * N * D;
+    const int64_t ybase = pair * N * D;
     // Lane (g, n) of a row load reads features 4Pg .. 4Pg + 4P - 1 of token row n.
     auto row_off = [&](int tile, int r) { return ((uint32_t)(bstart + 16 * tile + r) * D + 4 * P * g) * 2; };
 
@@ -289,14 +289,14 @@ __global__ __launch_bounds__(256) void output_causal_quad_kernel(const uint16_t*
         for (int r = 0; r < 4; ++r) {
             const int row = 16 * t + 4 * g + r;
             if (row < C) {
-                const float rd = fast_rcp(dacc[r] + kEps);
-                float* dst = Yp + (int64_t)(bstart + row) * D + P * n;
+                const float rd = out_scale(o, dacc[r] + kEps);
+                const int64_t e = ybase + (int64_t)(bstart + row) * D + P * n;
                 if constexpr (P == 4) {
-                    store_out(dst, f32x4{acc[0][r] * rd, acc[1][r] * rd, acc[2][r] * rd, acc[3][r] * rd});
+                    store_out(o, e, f32x4{acc[0][r] * rd, acc[1][r] * rd, acc[2][r] * rd, acc[3][r] * rd});
                 } else if constexpr (P == 2) {
-                    store_out(dst, f32x2{acc[0][r] * rd, acc[1][r] * rd});
+                    store_out(o, e, f32x2{acc[0][r] * rd, acc[1][r] * rd});
                 } else {
-                    store_out(dst, acc[0][r] * rd);
+                    store_out(o, e, acc[0][r] * rd);
                 }
             }
         }
@@ -304,7 +304,7 @@ __global__ __launch_bounds__(256) void output_causal_quad_kernel(const uint16_t*
 }
 
 hipError_t launch_causal_quad(const void* q, const void* k, const void* v, const float* St, const float* W,
-                              float* out, int64_t BH, int64_t N, int D, int64_t M, hipStream_t stream) {
+                              const OutSpec& out, int64_t BH, int64_t N, int D, int64_t M, hipStream_t stream) {
     const uint16_t* qq = (const uint16_t*)q;
     const uint16_t* kk = (const uint16_t*)k;
     const uint16_t* vv = (const uint16_t*)v;

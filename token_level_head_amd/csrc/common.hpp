@@ -10,6 +10,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kernels.hpp"  // OutSpec
+
 namespace mhla {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -53,6 +55,8 @@ __device__ __forceinline__ bf16pair split_bf16(float x) {
 }
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // Two floats to packed bf16 (round-to-nearest-even), a in the low half: one v_cvt_pk_bf16_f32.
@@ -84,16 +88,35 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x4& a, const bf16x4& b, const 
                                                      __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
 }
 
-// Stores of the attention output Y, which nothing later in the pass reads: marked
+// Factor applied to a row's numerator: 1 / (phi(q)^T z~ + eps), or 1 without the
+// normaliser.  `guarded_den` already includes eps.
+__device__ __forceinline__ float out_scale(const OutSpec& o, float guarded_den) {
+    return o.norm ? fast_rcp(guarded_den) : 1.f;
+}
+
+// Stores of Y (element offset e), which nothing later in the pass reads: marked
 // non-temporal, so that the output stream does not evict the block summaries that
 // the next stage reads back from the caches.
-__device__ __forceinline__ void store_out(float* p, f32x4 v) {
-    __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+__device__ __forceinline__ void store_out(const OutSpec& o, int64_t e, f32x4 v) {
+    if (o.bf16) {
+        const u32x2 w = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(static_cast<uint16_t*>(o.y) + e));
+    } else {
+        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(static_cast<float*>(o.y) + e));
+    }
 }
-__device__ __forceinline__ void store_out(float* p, f32x2 v) {
-    __builtin_nontemporal_store(v, reinterpret_cast<f32x2*>(p));
+__device__ __forceinline__ void store_out(const OutSpec& o, int64_t e, f32x2 v) {
+    if (o.bf16)
+        __builtin_nontemporal_store(pack_bf16(v[0], v[1]), reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(o.y) + e));
+    else
+        __builtin_nontemporal_store(v, reinterpret_cast<f32x2*>(static_cast<float*>(o.y) + e));
 }
-__device__ __forceinline__ void store_out(float* p, float v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void store_out(const OutSpec& o, int64_t e, float v) {
+    if (o.bf16)
+        __builtin_nontemporal_store(__builtin_bit_cast(uint16_t, (__bf16)v), static_cast<uint16_t*>(o.y) + e);
+    else
+        __builtin_nontemporal_store(v, static_cast<float*>(o.y) + e);
+}
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
@@ -127,8 +150,6 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 }
 __device__ __forceinline__ uint32_t off_if(bool ok, uint32_t byte_off) { return ok ? byte_off : kOutOfRange; }
 
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // NT selects the non-temporal policy (for token inputs streamed once; see
 // stream_token_inputs in kernels.hpp).
 template <bool NT = false>

@@ -72,7 +72,7 @@ template <int D, bool FULL>
 __global__ __launch_bounds__(64 * kWaves) void fused_small_kernel(const uint16_t* __restrict__ Q,
                                                           const uint16_t* __restrict__ K,
                                                           const uint16_t* __restrict__ V,
-                                                          const float* __restrict__ W, float* __restrict__ Y,
+                                                          const float* __restrict__ W, OutSpec o,
                                                           int N, int M) {
     constexpr int P = D / 16;
     constexpr int BPW = kBlocksPerWave;
@@ -308,15 +308,15 @@ __global__ __launch_bounds__(64 * kWaves) void fused_small_kernel(const uint16_t
             if (ia == P - 1) {
                 if (c == 0) {
 #pragma unroll
-                    for (int j = 0; j < BPW; ++j) rden[j] = fast_rcp(dacc[j][0] + kEps);
+                    for (int j = 0; j < BPW; ++j) rden[j] = out_scale(o, dacc[j][0] + kEps);
                 }
 #pragma unroll
                 for (int j = 0; j < BPW; ++j) {
                     const int b = wave + kWaves * j;
                     if (b < M && (FULL || n < C)) {
-                        float* dst = Y + (pair * N + b * C + n) * D + 16 * c + 4 * g;
-                        const f32x4 o = oacc[j];
-                        store_out(dst, f32x4{o[0] * rden[j], o[1] * rden[j], o[2] * rden[j], o[3] * rden[j]});
+                        const int64_t e = (pair * N + b * C + n) * D + 16 * c + 4 * g;
+                        const f32x4 a = oacc[j];
+                        store_out(o, e, f32x4{a[0] * rden[j], a[1] * rden[j], a[2] * rden[j], a[3] * rden[j]});
                     }
                 }
             }
@@ -332,8 +332,8 @@ bool fused_applicable(int D, int64_t BH, int64_t N, int64_t M) {
     return M <= kMaxBlocks && N / M <= 16;
 }
 
-hipError_t launch_fused(const void* q, const void* k, const void* v, const float* W, float* out, int64_t BH,
-                        int64_t N, int D, int64_t M, hipStream_t stream) {
+hipError_t launch_fused(const void* q, const void* k, const void* v, const float* W, const OutSpec& out,
+                        int64_t BH, int64_t N, int D, int64_t M, hipStream_t stream) {
     const bool full = N / M == 16;
     const uint16_t* qq = (const uint16_t*)q;
     const uint16_t* kk = (const uint16_t*)k;

@@ -11,6 +11,13 @@ namespace mhla {
 constexpr int kDtypeBF16 = 0;
 constexpr int kDtypeF32 = 1;
 
+// Where and how a kernel writes the attention output Y ([pair][N][d], row-major).
+struct OutSpec {
+    void* y;   // float32 values, or bfloat16 bit patterns when bf16 != 0
+    int bf16;  // 1: each value rounded to bfloat16, nearest even
+    int norm;  // 0: the numerator phi(q)^T S~ alone, without the normaliser
+};
+
 // Token inputs (Q, K, V together) larger than the 256 MiB Infinity Cache are read
 // with the non-temporal policy, so that streaming them does not evict the block
 // summaries that the next stage reads back.  Smaller inputs are read normally: they
@@ -35,16 +42,16 @@ size_t mix_fragment_bytes(int64_t M);
 hipError_t launch_mix(const float* S, const float* W, float* St, int64_t BH, int D, int64_t M, bool causal,
                       bool precise, void* frag_ws, hipStream_t stream);
 
-// Stage 3: out [pair][N][d] from Q and St (causal also K, V and W[i,i]).
+// Stage 3: Y [pair][N][d] from Q and St (causal also K, V and W[i,i]), written as `out` says.
 hipError_t launch_output(int dtype, const void* q, const void* k, const void* v, const float* St,
-                         const float* W, float* out, int64_t BH, int64_t N, int D, int64_t M, bool causal,
+                         const float* W, const OutSpec& out, int64_t BH, int64_t N, int D, int64_t M, bool causal,
                          hipStream_t stream);
 
 // Causal bf16 output for blocks of at most 256 tokens: the within-block prefix as one
 // masked C x C product per block (used by launch_output when applicable).
 bool causal_quad_applicable(int64_t C);
 hipError_t launch_causal_quad(const void* q, const void* k, const void* v, const float* St, const float* W,
-                              float* out, int64_t BH, int64_t N, int D, int64_t M, hipStream_t stream);
+                              const OutSpec& out, int64_t BH, int64_t N, int D, int64_t M, hipStream_t stream);
 
 // Streaming causal decoding of token t (state layout in decode.hip).
 hipError_t launch_decode_step(int dtype, const void* q, const void* k, const void* v, const float* W, float* state,
@@ -60,7 +67,7 @@ hipError_t launch_backward(int dtype, const void* q, const void* k, const void* 
 // Fused path (non-causal bf16, short blocks): the whole pass in one kernel with
 // the summaries in LDS; needs no workspace.
 bool fused_applicable(int D, int64_t BH, int64_t N, int64_t M);
-hipError_t launch_fused(const void* q, const void* k, const void* v, const float* W, float* out, int64_t BH,
-                        int64_t N, int D, int64_t M, hipStream_t stream);
+hipError_t launch_fused(const void* q, const void* k, const void* v, const float* W, const OutSpec& out,
+                        int64_t BH, int64_t N, int D, int64_t M, hipStream_t stream);
 
 }  // namespace mhla

@@ -143,16 +143,21 @@ int forward_path(int64_t B, int64_t H, int64_t N, int64_t d, int64_t M, int caus
                                                                                              : MHLA_PATH_STAGED;
 }
 
-int forward_impl(int dtype, const void* q, const void* k, const void* v, const float* W, float* out, int64_t B,
-                 int64_t H, int64_t N, int64_t d, int64_t M, int causal, mhla_stream_t stream_) {
+constexpr unsigned kKnownOptions = MHLA_OPT_CAUSAL | MHLA_OPT_NO_NORMALIZER | MHLA_OPT_OUT_BF16;
+
+int forward_impl(int dtype, const void* q, const void* k, const void* v, const float* W, void* out, int64_t B,
+                 int64_t H, int64_t N, int64_t d, int64_t M, unsigned options, mhla_stream_t stream_) {
     int st = check_sizes(B, H, N, d, M);
     if (st) return st;
+    if (options & ~kKnownOptions) return fail(MHLA_ERR_INVALID_ARG, "unknown option bits 0x%x", options & ~kKnownOptions);
     if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
         (st = check_ptr(W, "W")) || (st = check_ptr(out, "out")))
         return st;
+    const int causal = (options & MHLA_OPT_CAUSAL) != 0;
+    const mhla::OutSpec os{out, (options & MHLA_OPT_OUT_BF16) != 0, (options & MHLA_OPT_NO_NORMALIZER) == 0};
     const size_t esz = dtype == mhla::kDtypeF32 ? 4 : 2;
     const size_t in_bytes = (size_t)(B * H * N * d) * esz;
-    const size_t out_bytes = (size_t)(B * H * N * d) * 4;
+    const size_t out_bytes = (size_t)(B * H * N * d) * (os.bf16 ? 2 : 4);
     if (overlaps(out, out_bytes, q, in_bytes) || overlaps(out, out_bytes, k, in_bytes) ||
         overlaps(out, out_bytes, v, in_bytes) || overlaps(out, out_bytes, W, (size_t)(M * M) * 4))
         return fail(MHLA_ERR_INVALID_ARG, "out overlaps an input");
@@ -160,7 +165,7 @@ int forward_impl(int dtype, const void* q, const void* k, const void* v, const f
     hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
     const int64_t BH = B * H;
     if (forward_path(B, H, N, d, M, causal, dtype) == MHLA_PATH_FUSED) {
-        hipError_t e = mhla::launch_fused(q, k, v, W, out, BH, N, (int)d, M, stream);
+        hipError_t e = mhla::launch_fused(q, k, v, W, os, BH, N, (int)d, M, stream);
         if (e != hipSuccess) return hip_fail(e, "fused kernel");
         return ok();
     }
@@ -183,7 +188,7 @@ int forward_impl(int dtype, const void* q, const void* k, const void* v, const f
     }
     if (e == hipSuccess) {
         what = "output kernel";
-        e = mhla::launch_output(dtype, q, k, v, St, W, out, BH, N, (int)d, M, causal != 0, stream);
+        e = mhla::launch_output(dtype, q, k, v, St, W, os, BH, N, (int)d, M, causal != 0, stream);
     }
     hipError_t fe = hipFreeAsync(ws, stream);
     if (e != hipSuccess) return hip_fail(e, what);
@@ -197,12 +202,18 @@ extern "C" {
 
 int mhla_forward(const void* q, const void* k, const void* v, const float* W, float* out, int64_t B, int64_t H,
                  int64_t N, int64_t d, int64_t M, int causal, mhla_stream_t stream) {
-    return forward_impl(mhla::kDtypeBF16, q, k, v, W, out, B, H, N, d, M, causal, stream);
+    return forward_impl(mhla::kDtypeBF16, q, k, v, W, out, B, H, N, d, M, causal ? MHLA_OPT_CAUSAL : 0u, stream);
 }
 
 int mhla_forward_f32(const float* q, const float* k, const float* v, const float* W, float* out, int64_t B,
                      int64_t H, int64_t N, int64_t d, int64_t M, int causal, mhla_stream_t stream) {
-    return forward_impl(mhla::kDtypeF32, q, k, v, W, out, B, H, N, d, M, causal, stream);
+    return forward_impl(mhla::kDtypeF32, q, k, v, W, out, B, H, N, d, M, causal ? MHLA_OPT_CAUSAL : 0u, stream);
+}
+
+int mhla_forward_ex(const void* q, const void* k, const void* v, int dtype, const float* W, void* out, int64_t B,
+                    int64_t H, int64_t N, int64_t d, int64_t M, unsigned options, mhla_stream_t stream) {
+    if (dtype != MHLA_DTYPE_BF16 && dtype != MHLA_DTYPE_F32) return fail(MHLA_ERR_INVALID_ARG, "bad dtype %d", dtype);
+    return forward_impl(dtype, q, k, v, W, out, B, H, N, d, M, options, stream);
 }
 
 int64_t mhla_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int64_t M, int causal) {
@@ -275,7 +286,8 @@ int mhla_output(const void* q, const void* k, const void* v, int dtype, const fl
         (causal && (overlaps(out, out_bytes, k, in_bytes) || overlaps(out, out_bytes, v, in_bytes) ||
                     overlaps(out, out_bytes, W, (size_t)(M * M) * 4))))
         return fail(MHLA_ERR_INVALID_ARG, "out overlaps an input");
-    hipError_t e = mhla::launch_output(dtype, q, k, v, St, W, out, B * H, N, (int)d, M, causal != 0,
+    const mhla::OutSpec os{out, 0, 1};
+    hipError_t e = mhla::launch_output(dtype, q, k, v, St, W, os, B * H, N, (int)d, M, causal != 0,
                                        reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "output kernel");
     return ok();

@@ -63,24 +63,25 @@ __device__ __forceinline__ void build_b(const f32x4 (&ch)[P * P], bf16x8 (&bh)[K
 
 // Lane (g, n) holds acc[jj][i] = numerator of row t0 + 4g + i at column
 // P*n + jb0 + jj (jj < PJ); `den` is the guarded denominator of row t0 + n (any
-// lane group).  PJ consecutive floats are stored per row.
+// lane group).  PJ consecutive values are stored per row, from element offset
+// ybase (the pair's first element of Y).
 template <int P, int PJ>
-__device__ __forceinline__ void store_rows(float* Yp, int t0, int bend, int g, int n, int jb0,
-                                           const f32x4 (&acc)[PJ], float den) {
+__device__ __forceinline__ void store_rows(const OutSpec& o, int64_t ybase, int t0, int bend, int g, int n,
+                                           int jb0, const f32x4 (&acc)[PJ], float den) {
     constexpr int D = 16 * P;
-    const float rden = fast_rcp(den);
+    const float rden = out_scale(o, den);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const float r = __shfl(rden, 4 * g + i, 64);
         const int row = t0 + 4 * g + i;
         if (row < bend) {
-            float* dst = Yp + row * D + P * n + jb0;
+            const int64_t e = ybase + row * D + P * n + jb0;
             if constexpr (PJ == 4) {
-                store_out(dst, f32x4{acc[0][i] * r, acc[1][i] * r, acc[2][i] * r, acc[3][i] * r});
+                store_out(o, e, f32x4{acc[0][i] * r, acc[1][i] * r, acc[2][i] * r, acc[3][i] * r});
             } else if constexpr (PJ == 2) {
-                store_out(dst, f32x2{acc[0][i] * r, acc[1][i] * r});
+                store_out(o, e, f32x2{acc[0][i] * r, acc[1][i] * r});
             } else {
-                store_out(dst, acc[0][i] * r);
+                store_out(o, e, acc[0][i] * r);
             }
         }
     }
@@ -89,7 +90,7 @@ __device__ __forceinline__ void store_rows(float* Yp, int t0, int bend, int g, i
 // Offsets inside one (batch, head) pair fit in 32 bits (the API limits N*d).
 template <int D, bool NT>
 __global__ __launch_bounds__(256) void output_bf16_kernel(const uint16_t* __restrict__ Q,
-                                                          const float* __restrict__ St, float* __restrict__ Y,
+                                                          const float* __restrict__ St, OutSpec o,
                                                           int64_t BH, int N, int64_t M, int tpw, int wpu) {
     constexpr int P = D / 16;
     constexpr int FL = 4 * P;                 // features per lane group
@@ -125,7 +126,7 @@ __global__ __launch_bounds__(256) void output_bf16_kernel(const uint16_t* __rest
     build_b<P, KS>(sch, bh, bl);
 
     const uint16_t* Qp = Q + pair * N * D;
-    float* Yp = Y + pair * N * D;
+    const int64_t ybase = pair * N * D;
     for (int tile = tile_beg; tile < tile_end; ++tile) {
         const int t0 = bstart + 16 * tile;
         // phi(Q) as the A operand: token t0 + n, group-local features of group g.
@@ -157,7 +158,7 @@ __global__ __launch_bounds__(256) void output_bf16_kernel(const uint16_t* __rest
                 acc[jb] = mfma32(aq[ks], bl[ks][jb], acc[jb]);
             }
         }
-        store_rows<P, P>(Yp, t0, bend, g, n, 0, acc, den);
+        store_rows<P, P>(o, ybase, t0, bend, g, n, 0, acc, den);
     }
 }
 
@@ -182,7 +183,7 @@ __global__ __launch_bounds__(256) void output_causal_kernel(const uint16_t* __re
                                                             const uint16_t* __restrict__ K,
                                                             const uint16_t* __restrict__ V,
                                                             const float* __restrict__ St,
-                                                            const float* __restrict__ W, float* __restrict__ Y,
+                                                            const float* __restrict__ W, OutSpec o,
                                                             int64_t BH, int N, int64_t M) {
     constexpr int P = D / 16;
     constexpr int FL = 4 * P;
@@ -222,7 +223,7 @@ __global__ __launch_bounds__(256) void output_causal_kernel(const uint16_t* __re
     const uint16_t* Qp = Q + pair * N * D;
     const uint16_t* Kp = K + pair * N * D;
     const uint16_t* Vp = V + pair * N * D;
-    float* Yp = Y + pair * N * D;
+    const int64_t ybase = pair * N * D;
     const bf16x4 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
 
     // This lane's share of the tile: one 16-byte chunk of Q or K.
@@ -336,14 +337,14 @@ __global__ __launch_bounds__(256) void output_causal_kernel(const uint16_t* __re
             comb[ia] = mfma16(ak4[ia], bv4, comb[ia]);
             zacc[ia] = mfma16(ak4[ia], ones, zacc[ia]);
         }
-        if (active) store_rows<P, 1>(Yp, t0, bend, g, n, jb, acc, den);
+        if (active) store_rows<P, 1>(o, ybase, t0, bend, g, n, jb, acc, den);
     }
 }
 
 // float32 path: one thread per output element, float32 arithmetic throughout.
 __global__ __launch_bounds__(256) void output_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                                                          const float* __restrict__ V, const float* __restrict__ St,
-                                                         const float* __restrict__ W, float* __restrict__ Y,
+                                                         const float* __restrict__ W, OutSpec o,
                                                          int64_t BH, int64_t N, int64_t M, int D, int causal) {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= BH * N * D) return;
@@ -372,11 +373,11 @@ __global__ __launch_bounds__(256) void output_f32_kernel(const float* __restrict
         num = fmaf(wii, ni, num);
         den = fmaf(wii, di, den);
     }
-    Y[idx] = num / (den + kEps);
+    store_out(o, idx, o.norm ? num / (den + kEps) : num);
 }
 
 hipError_t launch_output(int dtype, const void* q, const void* k, const void* v, const float* St,
-                         const float* W, float* out, int64_t BH, int64_t N, int D, int64_t M, bool causal,
+                         const float* W, const OutSpec& out, int64_t BH, int64_t N, int D, int64_t M, bool causal,
                          hipStream_t stream) {
     if (dtype == kDtypeF32) {
         const int64_t total = BH * N * D;
