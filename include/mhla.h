@@ -98,8 +98,11 @@ enum {
     MHLA_OPT_NO_NORMALIZER = 2, /* y_t = phi(q_t)^T S~_i (plus, causal, W[i,i] phi(q_t)^T P_t), with
                                    no division by phi(q_t)^T z~_i + 1e-6: the form §4.1 allows for
                                    long sequences (its remark on the output), for training stability */
-    MHLA_OPT_OUT_BF16 = 4       /* out holds bfloat16 bit patterns, each value rounded to nearest
+    MHLA_OPT_OUT_BF16 = 4,      /* out holds bfloat16 bit patterns, each value rounded to nearest
                                    even, instead of float32; the arithmetic is unchanged */
+    MHLA_OPT_W_PER_HEAD = 8     /* W is [H][M][M]: head h (of every batch element) mixes with its
+                                   own matrix W + h*M*M (§4.1/§4.2 applied per head; the pages
+                                   describe one M_c shared by all heads) */
 };
 
 /*
@@ -110,7 +113,10 @@ enum {
  * mhla_forward_f32 with MHLA_DTYPE_F32).  Unknown option bits give
  * MHLA_ERR_INVALID_ARG.  Paths, workspace and all other conventions as for
  * mhla_forward; mhla_forward_path() applies unchanged (the options do not change
- * the path).
+ * the path).  With MHLA_OPT_W_PER_HEAD the staged path's workspace holds one
+ * split copy of W per head when 256 < M <= 1024: H times the split-W bytes that
+ * mhla_workspace_bytes() counts once.  The summary arrays are then ordered head-major
+ * inside the workspace, so that each head's mix is one contiguous GEMM.
  */
 int mhla_forward_ex(const void* q, const void* k, const void* v, int dtype, const float* W, void* out,
                     int64_t B, int64_t H, int64_t N, int64_t d, int64_t M, unsigned options,

@@ -68,14 +68,17 @@ class Oracle:
         return np.ascontiguousarray(a, dtype=np.float32)
 
     def forward(self, q, k, v, W, causal=False, nthreads=1, normalize=True):
-        """q, k, v: [B, H, N, d] float32; W: [M, M] float32 -> float64 [B, H, N, d].
+        """q, k, v: [B, H, N, d] float32; W: [M, M] float32 (or [H, M, M]: one matrix per
+        head) -> float64 [B, H, N, d].
 
         normalize=False drops the normaliser (MHLA §4.1, remark on the output)."""
         q, k, v, W = (self._f32(a) for a in (q, k, v, W))
         B, H, N, d = q.shape
-        M = W.shape[0]
+        M = W.shape[-1]
+        if W.ndim == 3 and W.shape != (H, M, M):
+            raise ValueError("a per-head W must be [H, M, M]")
         out = np.empty((B, H, N, d), dtype=np.float64)
-        opts = (1 if causal else 0) | (0 if normalize else 2)
+        opts = (1 if causal else 0) | (0 if normalize else 2) | (4 if W.ndim == 3 else 0)
         rc = self.lib.mhla_oracle_forward_ex(_ptr(q, _f32p), _ptr(k, _f32p), _ptr(v, _f32p), _ptr(W, _f32p),
                                              _ptr(out, _f64p), B, H, N, d, M, opts, int(nthreads))
         if rc != 0:

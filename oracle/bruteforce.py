@@ -50,7 +50,8 @@ def weight_matrix(q, k, W, blk, causal, rows=None):
 
 
 def forward(q, k, v, W, causal=False, blk=None, rows=None, normalize=True):
-    """Y for q, k, v [B, H, N, d] (any float dtype) and W [M, M].
+    """Y for q, k, v [B, H, N, d] (any float dtype) and W [M, M] (or [H, M, M]: head h
+    mixes with W[h]).
 
     ``blk`` gives each token's block (default: contiguous equal blocks); ``rows``
     restricts the output to those token indices (same for every (batch, head)).
@@ -62,12 +63,13 @@ def forward(q, k, v, W, causal=False, blk=None, rows=None, normalize=True):
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     B, H, N, d = q.shape
-    M = np.asarray(W).shape[0]
+    W = np.asarray(W)
+    M = W.shape[-1]
     blk = contiguous_blocks(N, M) if blk is None else np.asarray(blk)
     nrows = N if rows is None else len(rows)
     out = np.empty((B, H, nrows, d), dtype=np.float64)
     for b in range(B):
         for h in range(H):
-            A = weight_matrix(q[b, h], k[b, h], W, blk, causal, rows)
+            A = weight_matrix(q[b, h], k[b, h], W[h] if W.ndim == 3 else W, blk, causal, rows)
             out[b, h] = (A @ v[b, h]) / (A.sum(axis=1, keepdims=True) + EPS) if normalize else A @ v[b, h]
     return out

@@ -143,9 +143,10 @@ int mhla_oracle_forward_ex(const float* q, const float* k, const float* v, const
                            double* out, long B, long H, long N, long d, long M, int options,
                            int nthreads) {
     if (B < 1 || H < 1 || !sizes_ok(B * H, N, d, M) || !q || !k || !v || !W || !out) return -1;
-    if (options & ~(MHLA_ORACLE_CAUSAL | MHLA_ORACLE_NO_NORMALISER)) return -1;
+    if (options & ~(MHLA_ORACLE_CAUSAL | MHLA_ORACLE_NO_NORMALISER | MHLA_ORACLE_W_PER_HEAD)) return -1;
     const int causal = (options & MHLA_ORACLE_CAUSAL) != 0;
     const int normalise = (options & MHLA_ORACLE_NO_NORMALISER) == 0;
+    const int per_head = (options & MHLA_ORACLE_W_PER_HEAD) != 0;
     const long BH = B * H;
     int failures = 0;
     (void)nthreads;
@@ -155,7 +156,9 @@ int mhla_oracle_forward_ex(const float* q, const float* k, const float* v, const
 #endif
     for (long p = 0; p < BH; ++p) {
         const long off = p * N * d;
-        failures += forward_pair(q + off, k + off, v + off, W, out + off, N, d, M, causal, normalise) != 0;
+        /* pair p is (batch p / H, head p % H); with one matrix per head it uses W[p % H] */
+        const float* Wp = per_head ? W + (p % H) * M * M : W;
+        failures += forward_pair(q + off, k + off, v + off, Wp, out + off, N, d, M, causal, normalise) != 0;
     }
     return failures ? -1 : 0;
 }

@@ -62,6 +62,8 @@ int mhla_oracle_forward(const float* q, const float* k, const float* v, const fl
 #define MHLA_ORACLE_CAUSAL 1        /* the causal variant ([MHLA] App. C) */
 #define MHLA_ORACLE_NO_NORMALISER 2 /* y_t = phi(q_t)^T S~_i (plus the causal prefix term), no
                                        division: [MHLA] §4.1, remark on the output for long sequences */
+#define MHLA_ORACLE_W_PER_HEAD 4    /* W is [H][M][M]: head h applies §4.1 with its own matrix
+                                       W + h*M*M (the pages describe one matrix for all heads) */
 
 /* The forward pass with options; mhla_oracle_forward(.., causal, ..) is
  * mhla_oracle_forward_ex(.., causal ? MHLA_ORACLE_CAUSAL : 0, ..). */

@@ -32,7 +32,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 from oracle import bruteforce  # noqa: E402
-from token_level_head_amd.workloads import WORKLOADS, make_inputs, mixing_weights  # noqa: E402
+from token_level_head_amd.workloads import WORKLOADS, make_inputs, mixing_weights, per_head_weights  # noqa: E402
 
 EPS = 1e-6
 GOLDEN = os.path.join(ROOT, "tests", "golden", "hand_example.txt")
@@ -371,6 +371,30 @@ def pin_no_normaliser_one_token_per_block(orc):
             a = sum(_phi_scalar(float(q[0, 0, t, r])) * _phi_scalar(float(k[0, 0, t, r])) for r in range(d))
             expect = a * v[0, 0, t].astype(np.float64)
             assert np.max(np.abs(y[t] - expect)) <= 1e-14 * np.max(np.abs(expect)), (causal, t)
+
+
+# ---- one mixing matrix per head ----
+
+def pin_per_head_bruteforce(orc):
+    """W [H, M, M]: every head against the explicit definition with its own matrix."""
+    for i, (B, H, N, d, M, causal) in enumerate([(2, 3, 64, 8, 4, False), (3, 2, 60, 5, 6, True),
+                                                   (2, 2, 48, 4, 48, False)]):
+        w = WORKLOADS["tiny_f32"].shrink(B=B, H=H, N=N, d=d, M=M, causal=causal, seed=320 + i)
+        q, k, v, _ = make_inputs(w)
+        Wh = per_head_weights(w)
+        for normalize in (True, False):
+            y = orc.forward(q, k, v, Wh, causal=causal, normalize=normalize)
+            ref = bruteforce.forward(q, k, v, Wh, causal=causal, normalize=normalize)
+            assert rel_err(y, ref) < 1e-12, (B, H, N, d, M, causal, normalize)
+
+
+def pin_per_head_equal_matrices(orc):
+    """W [H, M, M] with every head's matrix equal to W0 is the shared-W0 pass."""
+    for causal in (False, True):
+        q, k, v, W0 = _inputs(2, 3, 80, 6, 5, causal, seed=330)
+        y = orc.forward(q, k, v, W0, causal=causal)
+        yh = orc.forward(q, k, v, np.stack([W0] * 3), causal=causal)
+        assert np.array_equal(y, yh), causal
 
 
 def _recover(phiq, num):

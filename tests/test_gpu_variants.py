@@ -119,3 +119,42 @@ def test_unknown_option_rejected():
                              ctypes.c_void_p(q.data_ptr()), 0, ctypes.c_void_p(W.data_ptr()),
                              ctypes.c_void_p(out.data_ptr()), 1, 1, 16, 16, 1, 1 << 10, None)
     assert st == mh.MHLA_ERR_INVALID_ARG
+
+
+PER_HEAD = [  # (B, H, N, d, M, causal, dtype): one per mixing kernel and output kernel
+    (2, 3, 256, 64, 16, False, "bf16"),   # fused path
+    (2, 3, 2048, 32, 1, False, "bf16"),   # M = 1 (token segments in the summaries)
+    (2, 2, 1024, 16, 32, True, "bf16"),   # M <= 64 mixing, causal masked products
+    (1, 3, 1024, 32, 64, False, "bf16"),
+    (1, 2, 2560, 16, 160, True, "bf16"),  # 64 < M <= 256 mixing
+    (1, 2, 600, 32, 300, False, "bf16"),  # split-W fragments, one copy per head
+    (1, 2, 2048, 16, 2048, False, "bf16"),  # M > 1024 mixing
+    (1, 2, 1536, 32, 3, True, "bf16"),    # running-state causal output kernel
+    (2, 3, 128, 64, 8, True, "f32"),      # float32 path
+]
+
+
+@pytest.mark.parametrize("case", PER_HEAD, ids=lambda c: "B{}H{}N{}d{}M{}{}{}".format(*c[:5], "c" if c[5] else "", c[6]))
+def test_per_head_mixing(orc, case):
+    """W [H, M, M]: against the oracle with per-head matrices; equal matrices give the shared pass's bits."""
+    from token_level_head_amd.workloads import per_head_weights
+    B, H, N, d, M, causal, dtype = case
+    w = WORKLOADS["tiny_f32"].shrink(B=B, H=H, N=N, d=d, M=M, causal=causal, dtype=dtype, seed=950 + N + M)
+    q, k, v, W = make_inputs(w)
+    Wh = per_head_weights(w)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    qd, kd, vd = (torch.from_numpy(a).to("cuda", tdt) for a in (q, k, v))
+    say(f"[per-head] B={B} H={H} N={N} d={d} M={M} causal={causal} dtype={dtype}")
+    y = torch.full(q.shape, float("nan"), dtype=torch.float32, device="cuda")
+    mh.mhla_forward_ex(qd, kd, vd, torch.from_numpy(Wh).cuda(), y, causal=causal)
+    shared = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    same = torch.full(q.shape, float("nan"), dtype=torch.float32, device="cuda")
+    Wd = torch.from_numpy(W).cuda()
+    mh.mhla_forward_ex(qd, kd, vd, Wd, shared, causal=causal)
+    mh.mhla_forward_ex(qd, kd, vd, Wd.unsqueeze(0).repeat(H, 1, 1).contiguous(), same, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(same, shared), "per-head mixing with equal matrices differs from the shared pass"
+    ref = orc.forward(q, k, v, Wh, causal=causal, nthreads=NTHREADS)
+    e = rel(y.cpu().numpy(), ref)
+    say(f"[per-head]   max|dY|/max|Y| = {e:.3e}")
+    assert e <= TOL[dtype], e

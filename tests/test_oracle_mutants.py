@@ -42,6 +42,9 @@ MUTANTS = {
     "no_normaliser_always": ("out[t * d + c] = normalise ? num / den : num;", "out[t * d + c] = num;"),
     "no_normaliser_option_ignored": ("const int normalise = (options & MHLA_ORACLE_NO_NORMALISER) == 0;",
                                      "const int normalise = 1;"),
+    "per_head_by_batch": ("const float* Wp = per_head ? W + (p % H) * M * M : W;",
+                          "const float* Wp = per_head ? W + (p / H) * M * M : W;"),
+    "per_head_ignored": ("const float* Wp = per_head ? W + (p % H) * M * M : W;", "const float* Wp = W;"),
 }
 
 

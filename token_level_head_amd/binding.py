@@ -26,6 +26,7 @@ MHLA_PATH_FUSED = 1
 MHLA_OPT_CAUSAL = 1
 MHLA_OPT_NO_NORMALIZER = 2
 MHLA_OPT_OUT_BF16 = 4
+MHLA_OPT_W_PER_HEAD = 8
 
 # Every symbol include/mhla.h declares, with (restype, argtypes).
 _P = ctypes.c_void_p
@@ -94,7 +95,7 @@ def _stream(stream):
 
 def _dims(q, W):
     B, H, N, d = q.shape
-    return B, H, N, d, W.shape[0]
+    return B, H, N, d, W.shape[-1]
 
 
 def mhla_forward(q, k, v, W, out, causal=False, stream=None):
@@ -114,10 +115,15 @@ def mhla_forward_f32(q, k, v, W, out, causal=False, stream=None):
 
 
 def mhla_forward_ex(q, k, v, W, out, causal=False, normalize=True, stream=None):
-    """q, k, v [B, H, N, d] bf16 or float32; W [M, M] float32; out [B, H, N, d] float32 or
-    bfloat16 (which selects the bf16 output).  normalize=False drops the normaliser."""
+    """q, k, v [B, H, N, d] bf16 or float32; W [M, M] float32, or [H, M, M] for one matrix
+    per head; out [B, H, N, d] float32 or bfloat16 (which selects the bf16 output).
+    normalize=False drops the normaliser."""
     B, H, N, d, M = _dims(q, W)
     opts = (MHLA_OPT_CAUSAL if causal else 0) | (0 if normalize else MHLA_OPT_NO_NORMALIZER)
+    if W.dim() == 3:
+        if tuple(W.shape) != (H, M, M):
+            raise ValueError("a per-head W must be [H, M, M]")
+        opts |= MHLA_OPT_W_PER_HEAD
     if out.dtype == torch.bfloat16:
         opts |= MHLA_OPT_OUT_BF16
     elif out.dtype != torch.float32:

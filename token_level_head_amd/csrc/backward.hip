@@ -441,7 +441,7 @@ hipError_t launch_backward(int dtype, const void* q, const void* k, const void* 
         const T* vv = (const T*)v;                                                                               \
         bwd_summary_kernel<DD, T><<<units, block, 0, stream>>>(kk, vv, S, BH, (int)N, (int)M);                  \
         if ((e = hipGetLastError()) != hipSuccess) return e;                                                     \
-        if ((e = launch_mix(S, W, St, BH, DD, M, causal, false, frag_ws, stream)) != hipSuccess) return e;       \
+        if ((e = launch_mix(S, W, St, BH, DD, M, causal, false, 0, frag_ws, stream)) != hipSuccess) return e;       \
         if (causal)                                                                                              \
             bwd_query_kernel<DD, T, true><<<units, block, 0, stream>>>(qq, kk, vv, dy, W, St, dSt, G, dq, dk, dv, \
                                                                        dWdiag, BH, (int)N, (int)M);              \
@@ -451,7 +451,7 @@ hipError_t launch_backward(int dtype, const void* q, const void* k, const void* 
         if ((e = hipGetLastError()) != hipSuccess) return e;                                                     \
         bwd_wt_kernel<<<dim3((unsigned)((M * M + 255) / 256)), block, 0, stream>>>(W, Wt, (int)M, causal);      \
         if ((e = hipGetLastError()) != hipSuccess) return e;                                                     \
-        if ((e = launch_mix(dSt, Wt, dS, BH, DD, M, false, false, frag_ws, stream)) != hipSuccess) return e;     \
+        if ((e = launch_mix(dSt, Wt, dS, BH, DD, M, false, false, 0, frag_ws, stream)) != hipSuccess) return e;     \
         if (causal)                                                                                              \
             bwd_key_kernel<DD, T, true><<<units, block, 0, stream>>>(kk, vv, dS, dk, dv, BH, (int)N, (int)M);   \
         else                                                                                                     \

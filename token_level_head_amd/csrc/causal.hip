@@ -117,7 +117,7 @@ __global__ __launch_bounds__(256) void output_causal_quad_kernel(const uint16_t*
                                                                  const uint16_t* __restrict__ V,
                                                                  const float* __restrict__ St,
                                                                  const float* __restrict__ W, OutSpec o,
-                                                                 int64_t BH, int N, int M) {
+                                                                 int64_t BH, int N, int M, int heads) {
     constexpr int P = D / 16;
     constexpr int KS = D >= 32 ? D / 32 : 1;
     constexpr int L = D * D + D;
@@ -135,8 +135,8 @@ __global__ __launch_bounds__(256) void output_causal_quad_kernel(const uint16_t*
     const int C = N / M;
     const int T = (C + 15) / 16;
     const int bstart = blk * C;
-    const float wii = W[(int64_t)blk * M + blk];
-    const float* sv = St + ((int64_t)blk * BH + pair) * L;
+    const float wii = pair_w(W, pair, heads, M)[(int64_t)blk * M + blk];
+    const float* sv = St + ((int64_t)blk * BH + summary_row(pair, heads, BH)) * L;
 
     const uint32_t pair_bytes = (uint32_t)N * D * 2;
     const rsrc_t rQ = make_rsrc(Q + pair * N * D, pair_bytes);
@@ -304,7 +304,8 @@ __global__ __launch_bounds__(256) void output_causal_quad_kernel(const uint16_t*
 }
 
 hipError_t launch_causal_quad(const void* q, const void* k, const void* v, const float* St, const float* W,
-                              const OutSpec& out, int64_t BH, int64_t N, int D, int64_t M, hipStream_t stream) {
+                              const OutSpec& out, int64_t BH, int64_t N, int D, int64_t M, int heads,
+                              hipStream_t stream) {
     const uint16_t* qq = (const uint16_t*)q;
     const uint16_t* kk = (const uint16_t*)k;
     const uint16_t* vv = (const uint16_t*)v;
@@ -314,9 +315,9 @@ hipError_t launch_causal_quad(const void* q, const void* k, const void* v, const
 #define MHLA_QUAD_CASE(DD)                                                                                     \
     case DD:                                                                                                   \
         if (nt)                                                                                                \
-            output_causal_quad_kernel<DD, true><<<grid, block, lds, stream>>>(qq, kk, vv, St, W, out, BH, (int)N, (int)M);  \
+            output_causal_quad_kernel<DD, true><<<grid, block, lds, stream>>>(qq, kk, vv, St, W, out, BH, (int)N, (int)M, heads);  \
         else                                                                                                   \
-            output_causal_quad_kernel<DD, false><<<grid, block, lds, stream>>>(qq, kk, vv, St, W, out, BH, (int)N, (int)M); \
+            output_causal_quad_kernel<DD, false><<<grid, block, lds, stream>>>(qq, kk, vv, St, W, out, BH, (int)N, (int)M, heads); \
         break;
     switch (D) {
         MHLA_QUAD_CASE(16)

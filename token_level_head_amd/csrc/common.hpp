@@ -118,6 +118,18 @@ __device__ __forceinline__ void store_out(const OutSpec& o, int64_t e, float v) 
         __builtin_nontemporal_store(v, static_cast<float*>(o.y) + e);
 }
 
+// Per-head mixing (heads > 0: one M x M matrix per head).  The summary arrays are
+// then head-major, row head * B + batch for pair = batch * H + head, so that one
+// head's summaries form a contiguous column block of the mixing GEMM; heads == 0
+// means one shared matrix and batch-major rows (row = pair).
+__device__ __forceinline__ int64_t summary_row(int64_t pair, int heads, int64_t BH) {
+    return heads > 0 ? (pair % heads) * (BH / heads) + pair / heads : pair;
+}
+// The mixing matrix a (batch, head) pair uses.
+__device__ __forceinline__ const float* pair_w(const float* W, int64_t pair, int heads, int64_t M) {
+    return heads > 0 ? W + (pair % heads) * M * M : W;
+}
+
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 // Masked load without a branch: the address falls back to `safe` (any valid,

@@ -73,7 +73,7 @@ __global__ __launch_bounds__(64 * kWaves) void fused_small_kernel(const uint16_t
                                                           const uint16_t* __restrict__ K,
                                                           const uint16_t* __restrict__ V,
                                                           const float* __restrict__ W, OutSpec o,
-                                                          int N, int M) {
+                                                          int N, int M, int heads) {
     constexpr int P = D / 16;
     constexpr int BPW = kBlocksPerWave;
     constexpr int SB = P > 1 ? 2 : 1;  // sub-tiles per batch (same column chunk)
@@ -97,7 +97,7 @@ __global__ __launch_bounds__(64 * kWaves) void fused_small_kernel(const uint16_t
     const rsrc_t rK = make_rsrc(K + pair * N * D, pair_bytes);
     const rsrc_t rV = make_rsrc(V + pair * N * D, pair_bytes);
     const rsrc_t rQ = make_rsrc(Q + pair * N * D, pair_bytes);
-    const rsrc_t rW = make_rsrc(W, (uint32_t)M * M * 4);
+    const rsrc_t rW = make_rsrc(pair_w(W, pair, heads, M), (uint32_t)M * M * 4);
     u32x2 kw[BPW][4], vw[BPW][4];
     u32x4 qw[BPW][P == 4 ? 2 : 1];
 #pragma unroll
@@ -333,7 +333,7 @@ bool fused_applicable(int D, int64_t BH, int64_t N, int64_t M) {
 }
 
 hipError_t launch_fused(const void* q, const void* k, const void* v, const float* W, const OutSpec& out,
-                        int64_t BH, int64_t N, int D, int64_t M, hipStream_t stream) {
+                        int64_t BH, int64_t N, int D, int64_t M, int heads, hipStream_t stream) {
     const bool full = N / M == 16;
     const uint16_t* qq = (const uint16_t*)q;
     const uint16_t* kk = (const uint16_t*)k;
@@ -342,9 +342,9 @@ hipError_t launch_fused(const void* q, const void* k, const void* v, const float
 #define MHLA_FUSED_CASE(DD)                                                                              \
     case DD:                                                                                             \
         if (full)                                                                                        \
-            fused_small_kernel<DD, true><<<grid, block, 0, stream>>>(qq, kk, vv, W, out, (int)N, (int)M);  \
+            fused_small_kernel<DD, true><<<grid, block, 0, stream>>>(qq, kk, vv, W, out, (int)N, (int)M, heads);  \
         else                                                                                             \
-            fused_small_kernel<DD, false><<<grid, block, 0, stream>>>(qq, kk, vv, W, out, (int)N, (int)M); \
+            fused_small_kernel<DD, false><<<grid, block, 0, stream>>>(qq, kk, vv, W, out, (int)N, (int)M, heads); \
         break;
     switch (D) {
         MHLA_FUSED_CASE(16)

@@ -27,31 +27,36 @@ inline bool stream_token_inputs(int64_t BH, int64_t N, int D, int esize) {
     return 3 * BH * N * D * esize > kInfinityCacheBytes;
 }
 
-// Stage 1: S[b][pair][d*d + d] (packed) from K, V [pair][N][d].  Long blocks on few
+// `heads` (every launcher): 0 for one mixing matrix shared by all (batch, head)
+// pairs; H for one M x M matrix per head (W is [H][M][M]), with head-major rows in
+// the summary arrays (summary_row in common.hpp).
+//
+// Stage 1: S[b][row][d*d + d] (packed) from K, V [pair][N][d].  Long blocks on few
 // (batch, head) pairs are cut into token segments whose partial summaries go to
 // `partial` (summary_partial_bytes() bytes, 16-byte aligned; may be null when that
 // is 0) and are then added into S.
 size_t summary_partial_bytes(int dtype, int64_t BH, int64_t N, int D, int64_t M);
 hipError_t launch_summaries(int dtype, const void* k, const void* v, float* S, int64_t BH, int64_t N,
-                            int D, int64_t M, float* partial, hipStream_t stream);
+                            int D, int64_t M, int heads, float* partial, hipStream_t stream);
 
 // Stage 2: St[i][col] = sum_b W[i,b] S[b][col] (causal: b < i), col < BH * (d*d + d).
 // The bf16 path needs mix_fragment_bytes(M) bytes of device scratch at frag_ws
 // (16-byte aligned) for the split W; 0 bytes means it needs none.
 size_t mix_fragment_bytes(int64_t M);
 hipError_t launch_mix(const float* S, const float* W, float* St, int64_t BH, int D, int64_t M, bool causal,
-                      bool precise, void* frag_ws, hipStream_t stream);
+                      bool precise, int heads, void* frag_ws, hipStream_t stream);
 
 // Stage 3: Y [pair][N][d] from Q and St (causal also K, V and W[i,i]), written as `out` says.
 hipError_t launch_output(int dtype, const void* q, const void* k, const void* v, const float* St,
                          const float* W, const OutSpec& out, int64_t BH, int64_t N, int D, int64_t M, bool causal,
-                         hipStream_t stream);
+                         int heads, hipStream_t stream);
 
 // Causal bf16 output for blocks of at most 256 tokens: the within-block prefix as one
 // masked C x C product per block (used by launch_output when applicable).
 bool causal_quad_applicable(int64_t C);
 hipError_t launch_causal_quad(const void* q, const void* k, const void* v, const float* St, const float* W,
-                              const OutSpec& out, int64_t BH, int64_t N, int D, int64_t M, hipStream_t stream);
+                              const OutSpec& out, int64_t BH, int64_t N, int D, int64_t M, int heads,
+                              hipStream_t stream);
 
 // Streaming causal decoding of token t (state layout in decode.hip).
 hipError_t launch_decode_step(int dtype, const void* q, const void* k, const void* v, const float* W, float* state,
@@ -68,6 +73,6 @@ hipError_t launch_backward(int dtype, const void* q, const void* k, const void* 
 // the summaries in LDS; needs no workspace.
 bool fused_applicable(int D, int64_t BH, int64_t N, int64_t M);
 hipError_t launch_fused(const void* q, const void* k, const void* v, const float* W, const OutSpec& out,
-                        int64_t BH, int64_t N, int D, int64_t M, hipStream_t stream);
+                        int64_t BH, int64_t N, int D, int64_t M, int heads, hipStream_t stream);
 
 }  // namespace mhla

@@ -118,10 +118,13 @@ hipError_t device_pool(hipMemPool_t* out) {
 
 // Two summary arrays (S, St), the mixing kernel's split-W fragments, then the
 // summary kernel's partial sums when it cuts long blocks into token segments.
-size_t frag_bytes_aligned(int64_t M) { return (mhla::mix_fragment_bytes(M) + 255) / 256 * 256; }
+// nw: number of M x M mixing matrices (H with one per head, else 1).
+size_t frag_bytes_aligned(int64_t M, int64_t nw = 1) {
+    return (nw * mhla::mix_fragment_bytes(M) + 255) / 256 * 256;
+}
 
-size_t workspace_bytes(int dtype, int64_t BH, int64_t N, int64_t d, int64_t M) {
-    return 2 * (size_t)(M * BH * summary_floats(d)) * sizeof(float) + frag_bytes_aligned(M) +
+size_t workspace_bytes(int dtype, int64_t BH, int64_t N, int64_t d, int64_t M, int64_t nw = 1) {
+    return 2 * (size_t)(M * BH * summary_floats(d)) * sizeof(float) + frag_bytes_aligned(M, nw) +
            mhla::summary_partial_bytes(dtype, BH, N, (int)d, M);
 }
 
@@ -143,7 +146,7 @@ int forward_path(int64_t B, int64_t H, int64_t N, int64_t d, int64_t M, int caus
                                                                                              : MHLA_PATH_STAGED;
 }
 
-constexpr unsigned kKnownOptions = MHLA_OPT_CAUSAL | MHLA_OPT_NO_NORMALIZER | MHLA_OPT_OUT_BF16;
+constexpr unsigned kKnownOptions = MHLA_OPT_CAUSAL | MHLA_OPT_NO_NORMALIZER | MHLA_OPT_OUT_BF16 | MHLA_OPT_W_PER_HEAD;
 
 int forward_impl(int dtype, const void* q, const void* k, const void* v, const float* W, void* out, int64_t B,
                  int64_t H, int64_t N, int64_t d, int64_t M, unsigned options, mhla_stream_t stream_) {
@@ -155,22 +158,24 @@ int forward_impl(int dtype, const void* q, const void* k, const void* v, const f
         return st;
     const int causal = (options & MHLA_OPT_CAUSAL) != 0;
     const mhla::OutSpec os{out, (options & MHLA_OPT_OUT_BF16) != 0, (options & MHLA_OPT_NO_NORMALIZER) == 0};
+    const int heads = (options & MHLA_OPT_W_PER_HEAD) ? (int)H : 0;  // H fits: B*H*M <= 2^29
+    const int64_t nw = heads ? H : 1;
     const size_t esz = dtype == mhla::kDtypeF32 ? 4 : 2;
     const size_t in_bytes = (size_t)(B * H * N * d) * esz;
     const size_t out_bytes = (size_t)(B * H * N * d) * (os.bf16 ? 2 : 4);
     if (overlaps(out, out_bytes, q, in_bytes) || overlaps(out, out_bytes, k, in_bytes) ||
-        overlaps(out, out_bytes, v, in_bytes) || overlaps(out, out_bytes, W, (size_t)(M * M) * 4))
+        overlaps(out, out_bytes, v, in_bytes) || overlaps(out, out_bytes, W, (size_t)(nw * M * M) * 4))
         return fail(MHLA_ERR_INVALID_ARG, "out overlaps an input");
 
     hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
     const int64_t BH = B * H;
     if (forward_path(B, H, N, d, M, causal, dtype) == MHLA_PATH_FUSED) {
-        hipError_t e = mhla::launch_fused(q, k, v, W, os, BH, N, (int)d, M, stream);
+        hipError_t e = mhla::launch_fused(q, k, v, W, os, BH, N, (int)d, M, heads, stream);
         if (e != hipSuccess) return hip_fail(e, "fused kernel");
         return ok();
     }
     const size_t arr = (size_t)(M * BH * summary_floats(d)) * sizeof(float);
-    const size_t total = workspace_bytes(dtype, BH, N, d, M);
+    const size_t total = workspace_bytes(dtype, BH, N, d, M, nw);
     void* ws = nullptr;
     int st2 = pool_alloc(&ws, total, stream);
     if (st2) return st2;
@@ -178,17 +183,17 @@ int forward_impl(int dtype, const void* q, const void* k, const void* v, const f
     float* St = S + arr / sizeof(float);
     void* frags = St + arr / sizeof(float);
     float* partial = mhla::summary_partial_bytes(dtype, BH, N, (int)d, M)
-                         ? reinterpret_cast<float*>(static_cast<char*>(frags) + frag_bytes_aligned(M))
+                         ? reinterpret_cast<float*>(static_cast<char*>(frags) + frag_bytes_aligned(M, nw))
                          : nullptr;
     const char* what = "summary kernel";
-    hipError_t e = mhla::launch_summaries(dtype, k, v, S, BH, N, (int)d, M, partial, stream);
+    hipError_t e = mhla::launch_summaries(dtype, k, v, S, BH, N, (int)d, M, heads, partial, stream);
     if (e == hipSuccess) {
         what = "mixing kernel";
-        e = mhla::launch_mix(S, W, St, BH, (int)d, M, causal != 0, dtype == mhla::kDtypeF32, frags, stream);
+        e = mhla::launch_mix(S, W, St, BH, (int)d, M, causal != 0, dtype == mhla::kDtypeF32, heads, frags, stream);
     }
     if (e == hipSuccess) {
         what = "output kernel";
-        e = mhla::launch_output(dtype, q, k, v, St, W, os, BH, N, (int)d, M, causal != 0, stream);
+        e = mhla::launch_output(dtype, q, k, v, St, W, os, BH, N, (int)d, M, causal != 0, heads, stream);
     }
     hipError_t fe = hipFreeAsync(ws, stream);
     if (e != hipSuccess) return hip_fail(e, what);
@@ -245,7 +250,7 @@ int mhla_block_summaries(const void* k, const void* v, int dtype, float* S, int6
     void* partial = nullptr;
     const size_t pbytes = mhla::summary_partial_bytes(dtype, B * H, N, (int)d, M);
     if (pbytes && (st = pool_alloc(&partial, pbytes, s))) return st;
-    hipError_t e = mhla::launch_summaries(dtype, k, v, S, B * H, N, (int)d, M, static_cast<float*>(partial), s);
+    hipError_t e = mhla::launch_summaries(dtype, k, v, S, B * H, N, (int)d, M, 0, static_cast<float*>(partial), s);
     hipError_t fe = partial ? hipFreeAsync(partial, s) : hipSuccess;
     if (e != hipSuccess) return hip_fail(e, "summary kernel");
     if (fe != hipSuccess) return hip_fail(fe, "workspace release");
@@ -264,7 +269,7 @@ int mhla_mix_summaries(const float* S, const float* W, float* St, int64_t BH, in
     void* frags = nullptr;
     const size_t fbytes = precise ? 0 : mhla::mix_fragment_bytes(M);
     if (fbytes && (st = pool_alloc(&frags, fbytes, s))) return st;
-    hipError_t e = mhla::launch_mix(S, W, St, BH, (int)d, M, causal != 0, precise != 0, frags, s);
+    hipError_t e = mhla::launch_mix(S, W, St, BH, (int)d, M, causal != 0, precise != 0, 0, frags, s);
     hipError_t fe = frags ? hipFreeAsync(frags, s) : hipSuccess;
     if (e != hipSuccess) return hip_fail(e, "mixing kernel");
     if (fe != hipSuccess) return hip_fail(fe, "workspace release");
@@ -287,7 +292,7 @@ int mhla_output(const void* q, const void* k, const void* v, int dtype, const fl
                     overlaps(out, out_bytes, W, (size_t)(M * M) * 4))))
         return fail(MHLA_ERR_INVALID_ARG, "out overlaps an input");
     const mhla::OutSpec os{out, 0, 1};
-    hipError_t e = mhla::launch_output(dtype, q, k, v, St, W, os, B * H, N, (int)d, M, causal != 0,
+    hipError_t e = mhla::launch_output(dtype, q, k, v, St, W, os, B * H, N, (int)d, M, causal != 0, 0,
                                        reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "output kernel");
     return ok();

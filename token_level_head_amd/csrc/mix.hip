@@ -69,6 +69,8 @@ __global__ __launch_bounds__(256) void wsplit_kernel(const float* __restrict__ W
                                                      int RG, int KC) {
     using frag = typename MixOps<KSTEP>::frag;
     constexpr int E = MixOps<KSTEP>::E;
+    W += (int64_t)blockIdx.y * M * M;  // grid row y: one head's W and fragments
+    frags += (int64_t)blockIdx.y * 2 * RG * RT * KC * 64;
     const int64_t slot = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (slot >= (int64_t)RG * RT * KC * 64) return;
     const int ln = (int)(slot & 63);
@@ -106,8 +108,12 @@ __device__ __forceinline__ void load_cols(const float* p, bool ok, const float* 
 template <int KSTEP, int RT, int J, bool CAUSAL>
 __global__ __launch_bounds__(256) void mix_frag_kernel(const float* __restrict__ S,
                                                        const typename MixOps<KSTEP>::frag* __restrict__ frags,
-                                                       float* __restrict__ St, int64_t ncols, int M, int RG,
+                                                       float* __restrict__ St, int64_t ncols, int64_t ld, int M, int RG,
                                                        int64_t ntiles, int KC) {
+    // Grid row y: one head's contiguous column block (head-major summaries) and its W.
+    S += (int64_t)blockIdx.y * ncols;
+    St += (int64_t)blockIdx.y * ncols;
+    frags += (int64_t)blockIdx.y * 2 * RG * RT * KC * 64;  // hi and lo per slot
     using Ops = MixOps<KSTEP>;
     using frag = typename Ops::frag;
     constexpr int E = Ops::E;
@@ -145,7 +151,7 @@ __global__ __launch_bounds__(256) void mix_frag_kernel(const float* __restrict__
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             const int bb = kc * KSTEP + E * g + e;
-            load_cols<J>(S + (int64_t)bb * ncols + col, colok && bb < kend, S, ch.sv[e]);
+            load_cols<J>(S + (int64_t)bb * ld + col, colok && bb < kend, S, ch.sv[e]);
         }
 #pragma unroll
         for (int r = 0; r < RT; ++r) {
@@ -201,7 +207,7 @@ __global__ __launch_bounds__(256) void mix_frag_kernel(const float* __restrict__
         for (int i = 0; i < 4; ++i) {
             const int row = i0 + 16 * r + 4 * g + i;
             if (row < imax) {
-                float* dst = St + (int64_t)row * ncols + col;
+                float* dst = St + (int64_t)row * ld + col;
                 if constexpr (J == 4)
                     *reinterpret_cast<f32x4*>(dst) = f32x4{acc[r][0][i], acc[r][1][i], acc[r][2][i], acc[r][3][i]};
                 else
@@ -222,7 +228,11 @@ __global__ __launch_bounds__(256) void mix_frag_kernel(const float* __restrict__
 // the NT column tiles of the strip.
 template <int NT, bool CAUSAL>
 __global__ __launch_bounds__(512) void mix_wide_kernel(const float* __restrict__ S, const float* __restrict__ W,
-                                                       float* __restrict__ St, int64_t ncols, int M, int KC) {
+                                                       float* __restrict__ St, int64_t ncols, int64_t ld, int M, int KC) {
+    // Grid row y: one head's contiguous column block (head-major summaries) and its W.
+    S += (int64_t)blockIdx.y * ncols;
+    St += (int64_t)blockIdx.y * ncols;
+    W += (int64_t)blockIdx.y * M * M;
     __shared__ __align__(16) uint4 strip[2 * 16 * kWideMaxNT * (4 * kWideMaxKC + 1)];  // hi then lo
     const int RS4 = 4 * KC + 1;  // 32*KC bf16 of one column, + 16 bytes against bank conflicts
     uint4* const sh = strip;
@@ -245,7 +255,7 @@ __global__ __launch_bounds__(512) void mix_wide_kernel(const float* __restrict__
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
             const int b = 8 * bg + r;
-            x[q][r] = load_or_zero(reinterpret_cast<const f32x4*>(S + (int64_t)b * ncols + c),
+            x[q][r] = load_or_zero(reinterpret_cast<const f32x4*>(S + (int64_t)b * ld + c),
                                    task < ntask && b < M && c < ncols, reinterpret_cast<const f32x4*>(S));
         }
     }
@@ -358,7 +368,7 @@ __global__ __launch_bounds__(512) void mix_wide_kernel(const float* __restrict__
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
                 const int row = 16 * r + 4 * g + ii;
-                if (row < rows) St[(int64_t)(i0 + row) * ncols + col] = acc[r][t][ii];
+                if (row < rows) St[(int64_t)(i0 + row) * ld + col] = acc[r][t][ii];
             }
         }
     }
@@ -368,8 +378,12 @@ __global__ __launch_bounds__(512) void mix_wide_kernel(const float* __restrict__
 // itself (at most 16 KiB), which costs less than a separate launch.
 template <int KSTEP, int RT, int J, bool PIPE, bool CAUSAL>
 __global__ __launch_bounds__(256) void mix_lds_kernel(const float* __restrict__ S, const float* __restrict__ W,
-                                                      float* __restrict__ St, int64_t ncols, int M,
+                                                      float* __restrict__ St, int64_t ncols, int64_t ld, int M,
                                                       int64_t ntiles, int kc_cap) {
+    // Grid row y: one head's contiguous column block (head-major summaries) and its W.
+    S += (int64_t)blockIdx.y * ncols;
+    St += (int64_t)blockIdx.y * ncols;
+    W += (int64_t)blockIdx.y * M * M;
     using Ops = MixOps<KSTEP>;
     using frag = typename Ops::frag;
     constexpr int E = Ops::E;
@@ -416,7 +430,7 @@ __global__ __launch_bounds__(256) void mix_lds_kernel(const float* __restrict__ 
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             const int b = kc * KSTEP + E * g + e;
-            load_cols<J>(S + (int64_t)b * ncols + col, colok && b < kend, S, sv[e]);
+            load_cols<J>(S + (int64_t)b * ld + col, colok && b < kend, S, sv[e]);
         }
     };
     auto compute = [&](int kc, const float (&sv)[E][J]) {
@@ -473,7 +487,7 @@ __global__ __launch_bounds__(256) void mix_lds_kernel(const float* __restrict__ 
         for (int i = 0; i < 4; ++i) {
             const int row = 16 * r + 4 * g + i;
             if (row < imax) {
-                float* dst = St + (int64_t)row * ncols + col;
+                float* dst = St + (int64_t)row * ld + col;
                 if constexpr (J == 4)
                     *reinterpret_cast<f32x4*>(dst) = f32x4{acc[r][0][i], acc[r][1][i], acc[r][2][i], acc[r][3][i]};
                 else
@@ -488,7 +502,9 @@ __global__ __launch_bounds__(256) void mix_lds_kernel(const float* __restrict__ 
 template <bool CAUSAL>
 __global__ __launch_bounds__(256) void mix_scale_kernel(const f32x4* __restrict__ S, const float* __restrict__ W,
                                                         f32x4* __restrict__ St, int64_t n4) {
-    const float w = CAUSAL ? 0.f : W[0];
+    S += (int64_t)blockIdx.y * n4;  // grid row y: one head's column block and its 1 x 1 W
+    St += (int64_t)blockIdx.y * n4;
+    const float w = CAUSAL ? 0.f : W[blockIdx.y];
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
         const f32x4 x = S[i];
         St[i] = CAUSAL ? zero4() : f32x4{w * x[0], w * x[1], w * x[2], w * x[3]};
@@ -498,8 +514,12 @@ __global__ __launch_bounds__(256) void mix_scale_kernel(const f32x4* __restrict_
 // Fallback for M > kMaxFragM: each wave splits its W fragments itself.
 template <bool CAUSAL>
 __global__ __launch_bounds__(256) void mix_split_kernel(const float* __restrict__ S, const float* __restrict__ W,
-                                                        float* __restrict__ St, int64_t ncols, int M, int RG,
+                                                        float* __restrict__ St, int64_t ncols, int64_t ld, int M, int RG,
                                                         int64_t ntiles) {
+    // Grid row y: one head's contiguous column block (head-major summaries) and its W.
+    S += (int64_t)blockIdx.y * ncols;
+    St += (int64_t)blockIdx.y * ncols;
+    W += (int64_t)blockIdx.y * M * M;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, n = lane & 15;
     const int64_t w = (int64_t)blockIdx.x * 4 + wave;
@@ -524,7 +544,7 @@ __global__ __launch_bounds__(256) void mix_split_kernel(const float* __restrict_
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int b = kb + 8 * g + e;
-            sv[e] = load_or_zero(reinterpret_cast<const f32x4*>(S + (int64_t)b * ncols + col), b < kend && colok,
+            sv[e] = load_or_zero(reinterpret_cast<const f32x4*>(S + (int64_t)b * ld + col), b < kend && colok,
                                  reinterpret_cast<const f32x4*>(S));
         }
         bf16x8 bh[4], bl[4];
@@ -566,7 +586,7 @@ __global__ __launch_bounds__(256) void mix_split_kernel(const float* __restrict_
         for (int i = 0; i < 4; ++i) {
             const int row = i0 + 16 * r + 4 * g + i;
             if (row < imax)
-                *reinterpret_cast<f32x4*>(St + (int64_t)row * ncols + col) =
+                *reinterpret_cast<f32x4*>(St + (int64_t)row * ld + col) =
                     f32x4{acc[r][0][i], acc[r][1][i], acc[r][2][i], acc[r][3][i]};
         }
     }
@@ -574,7 +594,11 @@ __global__ __launch_bounds__(256) void mix_split_kernel(const float* __restrict_
 
 // float32 path: one thread per four columns, float32 FMAs in a fixed order.
 __global__ __launch_bounds__(256) void mix_f32_kernel(const float* __restrict__ S, const float* __restrict__ W,
-                                                      float* __restrict__ St, int64_t ncols, int M, int causal) {
+                                                      float* __restrict__ St, int64_t ncols, int64_t ld, int M, int causal) {
+    // Grid row y: one head's contiguous column block (head-major summaries) and its W.
+    S += (int64_t)blockIdx.y * ncols;
+    St += (int64_t)blockIdx.y * ncols;
+    W += (int64_t)blockIdx.y * M * M;
     const int64_t col = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
     if (col >= ncols) return;
     for (int i = 0; i < M; ++i) {
@@ -582,26 +606,30 @@ __global__ __launch_bounds__(256) void mix_f32_kernel(const float* __restrict__ 
         const int bend = causal ? i : M;
         for (int b = 0; b < bend; ++b) {
             const float wv = W[(int64_t)i * M + b];
-            const f32x4 s = *reinterpret_cast<const f32x4*>(S + (int64_t)b * ncols + col);
+            const f32x4 s = *reinterpret_cast<const f32x4*>(S + (int64_t)b * ld + col);
 #pragma unroll
             for (int c = 0; c < 4; ++c) acc[c] = fmaf(wv, s[c], acc[c]);
         }
-        *reinterpret_cast<f32x4*>(St + (int64_t)i * ncols + col) = acc;
+        *reinterpret_cast<f32x4*>(St + (int64_t)i * ld + col) = acc;
     }
 }
 
 hipError_t launch_mix(const float* S, const float* W, float* St, int64_t BH, int D, int64_t M, bool causal,
-                      bool precise, void* frag_ws, hipStream_t stream) {
-    const int64_t ncols = BH * (int64_t)(D * D + D);
+                      bool precise, int heads, void* frag_ws, hipStream_t stream) {
+    // heads > 0: W holds one M x M matrix per head and the summaries are head-major,
+    // so that head h owns columns [h*ncols, (h+1)*ncols); grid row y runs head y.
+    const int64_t ld = BH * (int64_t)(D * D + D);
+    const unsigned gy = heads > 0 ? (unsigned)heads : 1u;
+    const int64_t ncols = ld / gy;
     if (precise) {
         const int64_t threads = ncols / 4;
-        mix_f32_kernel<<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream>>>(S, W, St, ncols, (int)M,
-                                                                                        causal ? 1 : 0);
+        mix_f32_kernel<<<dim3((unsigned)((threads + 255) / 256), gy), dim3(256), 0, stream>>>(S, W, St, ncols, ld,
+                                                                                            (int)M, causal ? 1 : 0);
         return hipGetLastError();
     }
     if (M == 1) {
         const int64_t n4 = ncols / 4;  // d*d + d is a multiple of 4
-        const dim3 grid((unsigned)std::min<int64_t>((n4 + 255) / 256, 256 * 8));
+        const dim3 grid((unsigned)std::min<int64_t>((n4 + 255) / 256, 256 * 8), gy);
         if (causal)
             mix_scale_kernel<true><<<grid, dim3(256), 0, stream>>>(reinterpret_cast<const f32x4*>(S), W,
                                                                    reinterpret_cast<f32x4*>(St), n4);
@@ -622,13 +650,13 @@ hipError_t launch_mix(const float* S, const float* W, float* St, int64_t BH, int
             const int KC = (int)((M + KSTEP - 1) / KSTEP);
             const size_t lds = (size_t)RT * KC * 64 * 2 * (KSTEP == 32 ? 16 : 8);
             const int64_t ntiles = (ncols + 16 * J - 1) / (16 * J);
-            const dim3 grid((unsigned)((ntiles + 3) / 4));
+            const dim3 grid((unsigned)((ntiles + 3) / 4), gy);
             if (causal)
-                mix_lds_kernel<KSTEP, RT, J, PIPE, true><<<grid, dim3(256), lds, stream>>>(S, W, St, ncols, (int)M,
-                                                                                          ntiles, KC);
+                mix_lds_kernel<KSTEP, RT, J, PIPE, true><<<grid, dim3(256), lds, stream>>>(S, W, St, ncols, ld,
+                                                                                          (int)M, ntiles, KC);
             else
-                mix_lds_kernel<KSTEP, RT, J, PIPE, false><<<grid, dim3(256), lds, stream>>>(S, W, St, ncols, (int)M,
-                                                                                           ntiles, KC);
+                mix_lds_kernel<KSTEP, RT, J, PIPE, false><<<grid, dim3(256), lds, stream>>>(S, W, St, ncols, ld,
+                                                                                           (int)M, ntiles, KC);
         };
         if (M <= 16)
             run(I16{}, I1{}, I4{});
@@ -643,13 +671,13 @@ hipError_t launch_mix(const float* S, const float* W, float* St, int64_t BH, int
         const int64_t tiles16 = (ncols + 15) / 16;
         // strips of NT column tiles: one strip per CU when that takes at most kWideMaxNT tiles
         const int nt = (int)std::min<int64_t>(kWideMaxNT, std::max<int64_t>(1, (tiles16 + 255) / 256));
-        const dim3 grid((unsigned)((tiles16 + nt - 1) / nt));
+        const dim3 grid((unsigned)((tiles16 + nt - 1) / nt), gy);
         auto run = [&](auto nt_c) {
             constexpr int NT = decltype(nt_c)::value;
             if (causal)
-                mix_wide_kernel<NT, true><<<grid, dim3(512), 0, stream>>>(S, W, St, ncols, (int)M, KC);
+                mix_wide_kernel<NT, true><<<grid, dim3(512), 0, stream>>>(S, W, St, ncols, ld, (int)M, KC);
             else
-                mix_wide_kernel<NT, false><<<grid, dim3(512), 0, stream>>>(S, W, St, ncols, (int)M, KC);
+                mix_wide_kernel<NT, false><<<grid, dim3(512), 0, stream>>>(S, W, St, ncols, ld, (int)M, KC);
         };
         switch (nt) {
             case 1: run(std::integral_constant<int, 1>{}); break;
@@ -671,30 +699,30 @@ hipError_t launch_mix(const float* S, const float* W, float* St, int64_t BH, int
         const int KC = (int)((M + KSTEP - 1) / KSTEP);
         const int RG = (int)((M + 16 * RT - 1) / (16 * RT));
         const int64_t slots = (int64_t)RG * RT * KC * 64;
-        const dim3 sgrid((unsigned)((slots + 255) / 256));
+        const dim3 sgrid((unsigned)((slots + 255) / 256), gy);
         if (causal)
             wsplit_kernel<KSTEP, RT, true><<<sgrid, dim3(256), 0, stream>>>(W, frags, (int)M, RG, KC);
         else
             wsplit_kernel<KSTEP, RT, false><<<sgrid, dim3(256), 0, stream>>>(W, frags, (int)M, RG, KC);
         const int64_t ntiles = (ncols + 16 * J - 1) / (16 * J);
         const int64_t nctg = (ntiles + 3) / 4;
-        const dim3 grid((unsigned)(((nctg + 7) / 8) * 8 * RG));
+        const dim3 grid((unsigned)(((nctg + 7) / 8) * 8 * RG), gy);
         if (causal)
-            mix_frag_kernel<KSTEP, RT, J, true><<<grid, dim3(256), 0, stream>>>(S, frags, St, ncols, (int)M, RG,
+            mix_frag_kernel<KSTEP, RT, J, true><<<grid, dim3(256), 0, stream>>>(S, frags, St, ncols, ld, (int)M, RG,
                                                                                 ntiles, KC);
         else
-            mix_frag_kernel<KSTEP, RT, J, false><<<grid, dim3(256), 0, stream>>>(S, frags, St, ncols, (int)M, RG,
+            mix_frag_kernel<KSTEP, RT, J, false><<<grid, dim3(256), 0, stream>>>(S, frags, St, ncols, ld, (int)M, RG,
                                                                                  ntiles, KC);
         return hipGetLastError();
     }
     const int64_t ntiles = (ncols + 63) / 64;
     const int RG = (int)((M + 63) / 64);
     const int64_t waves = ntiles * RG;
-    const dim3 grid((unsigned)((waves + 3) / 4));
+    const dim3 grid((unsigned)((waves + 3) / 4), gy);
     if (causal)
-        mix_split_kernel<true><<<grid, dim3(256), 0, stream>>>(S, W, St, ncols, (int)M, RG, ntiles);
+        mix_split_kernel<true><<<grid, dim3(256), 0, stream>>>(S, W, St, ncols, ld, (int)M, RG, ntiles);
     else
-        mix_split_kernel<false><<<grid, dim3(256), 0, stream>>>(S, W, St, ncols, (int)M, RG, ntiles);
+        mix_split_kernel<false><<<grid, dim3(256), 0, stream>>>(S, W, St, ncols, ld, (int)M, RG, ntiles);
     return hipGetLastError();
 }
 

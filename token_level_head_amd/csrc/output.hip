@@ -91,7 +91,7 @@ __device__ __forceinline__ void store_rows(const OutSpec& o, int64_t ybase, int 
 template <int D, bool NT>
 __global__ __launch_bounds__(256) void output_bf16_kernel(const uint16_t* __restrict__ Q,
                                                           const float* __restrict__ St, OutSpec o,
-                                                          int64_t BH, int N, int64_t M, int tpw, int wpu) {
+                                                          int64_t BH, int N, int64_t M, int tpw, int wpu, int heads) {
     constexpr int P = D / 16;
     constexpr int FL = 4 * P;                 // features per lane group
     constexpr int KS = D >= 32 ? D / 32 : 1;  // 16x16x32 k-steps (d = 16 pads to 32)
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(256) void output_bf16_kernel(const uint16_t* __rest
     const int tile_end = min(ntiles, tile_beg + tpw);
     const int bstart = blk * C, bend = bstart + C;
 
-    const float* sv = St + ((int64_t)blk * BH + pair) * L;
+    const float* sv = St + ((int64_t)blk * BH + summary_row(pair, heads, BH)) * L;
     f32x4 sch[P * P];
 #pragma unroll
     for (int c4 = 0; c4 < P * P; ++c4) sch[c4] = *reinterpret_cast<const f32x4*>(sv + c4 * 256 + lane * 4);
@@ -184,7 +184,7 @@ __global__ __launch_bounds__(256) void output_causal_kernel(const uint16_t* __re
                                                             const uint16_t* __restrict__ V,
                                                             const float* __restrict__ St,
                                                             const float* __restrict__ W, OutSpec o,
-                                                            int64_t BH, int N, int64_t M) {
+                                                            int64_t BH, int N, int64_t M, int heads) {
     constexpr int P = D / 16;
     constexpr int FL = 4 * P;
     constexpr int KS = D >= 32 ? D / 32 : 1;
@@ -203,9 +203,9 @@ __global__ __launch_bounds__(256) void output_causal_kernel(const uint16_t* __re
     const int C = (int)(N / M);
     const int ntiles = (C + 15) / 16;
     const int bstart = blk * C, bend = bstart + C;
-    const float wii = active ? W[(int64_t)blk * M + blk] : 0.f;
+    const float wii = active ? pair_w(W, pair, heads, M)[(int64_t)blk * M + blk] : 0.f;
 
-    const float* sv = St + ((int64_t)blk * BH + pair) * L;
+    const float* sv = St + ((int64_t)blk * BH + summary_row(pair, heads, BH)) * L;
     f32x4 comb[P];  // comb[ia] = chunk (ia, jb) of S~_i + W[i,i] P
 #pragma unroll
     for (int ia = 0; ia < P; ++ia)
@@ -345,14 +345,15 @@ __global__ __launch_bounds__(256) void output_causal_kernel(const uint16_t* __re
 __global__ __launch_bounds__(256) void output_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                                                          const float* __restrict__ V, const float* __restrict__ St,
                                                          const float* __restrict__ W, OutSpec o,
-                                                         int64_t BH, int64_t N, int64_t M, int D, int causal) {
+                                                         int64_t BH, int64_t N, int64_t M, int D, int causal,
+                                                         int heads) {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= BH * N * D) return;
     const int c = (int)(idx % D);
     const int64_t t = (idx / D) % N, pair = idx / ((int64_t)N * D);
     const int64_t C = N / M, blk = t / C;
     const int P = D / 16;
-    const float* sv = St + (blk * BH + pair) * (int64_t)(D * D + D);
+    const float* sv = St + (blk * BH + summary_row(pair, heads, BH)) * (int64_t)(D * D + D);
     const float* q = Q + (pair * N + t) * D;
     float num = 0.f, den = 0.f;
     for (int r = 0; r < D; ++r) {
@@ -361,7 +362,7 @@ __global__ __launch_bounds__(256) void output_f32_kernel(const float* __restrict
         den = fmaf(fq, sv[D * D + r], den);
     }
     if (causal) {
-        const float wii = W[blk * M + blk];
+        const float wii = pair_w(W, pair, heads, M)[blk * M + blk];
         float ni = 0.f, di = 0.f;
         for (int64_t j = blk * C; j <= t; ++j) {
             const float* kj = K + (pair * N + j) * D;
@@ -378,11 +379,11 @@ __global__ __launch_bounds__(256) void output_f32_kernel(const float* __restrict
 
 hipError_t launch_output(int dtype, const void* q, const void* k, const void* v, const float* St,
                          const float* W, const OutSpec& out, int64_t BH, int64_t N, int D, int64_t M, bool causal,
-                         hipStream_t stream) {
+                         int heads, hipStream_t stream) {
     if (dtype == kDtypeF32) {
         const int64_t total = BH * N * D;
         output_f32_kernel<<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream>>>(
-            (const float*)q, (const float*)k, (const float*)v, St, W, out, BH, N, M, D, causal ? 1 : 0);
+            (const float*)q, (const float*)k, (const float*)v, St, W, out, BH, N, M, D, causal ? 1 : 0, heads);
         return hipGetLastError();
     }
     const uint16_t* qq = (const uint16_t*)q;
@@ -390,15 +391,15 @@ hipError_t launch_output(int dtype, const void* q, const void* k, const void* v,
     const uint16_t* vv = (const uint16_t*)v;
     const bool nt = stream_token_inputs(BH, N, D, 2);
     if (causal && causal_quad_applicable(N / M))
-        return launch_causal_quad(q, k, v, St, W, out, BH, N, D, M, stream);
+        return launch_causal_quad(q, k, v, St, W, out, BH, N, D, M, heads, stream);
     if (causal) {  // d/16 waves per block, 4 / (d/16) blocks per workgroup
         const int bpw = 4 / (D / 16);
         const dim3 grid((unsigned)((BH * M + bpw - 1) / bpw));
 #define MHLA_LAUNCH_OUT(DD)                                                                                   \
     if (nt)                                                                                                   \
-        output_causal_kernel<DD, true><<<grid, dim3(256), 0, stream>>>(qq, kk, vv, St, W, out, BH, (int)N, M);  \
+        output_causal_kernel<DD, true><<<grid, dim3(256), 0, stream>>>(qq, kk, vv, St, W, out, BH, (int)N, M, heads);  \
     else                                                                                                      \
-        output_causal_kernel<DD, false><<<grid, dim3(256), 0, stream>>>(qq, kk, vv, St, W, out, BH, (int)N, M)
+        output_causal_kernel<DD, false><<<grid, dim3(256), 0, stream>>>(qq, kk, vv, St, W, out, BH, (int)N, M, heads)
         switch (D) {
             case 16: MHLA_LAUNCH_OUT(16); break;
             case 32: MHLA_LAUNCH_OUT(32); break;
@@ -416,9 +417,9 @@ hipError_t launch_output(int dtype, const void* q, const void* k, const void* v,
     const dim3 grid((unsigned)((BH * M * wpu + 3) / 4));
 #define MHLA_LAUNCH_OUT(DD)                                                                        \
     if (nt)                                                                                        \
-        output_bf16_kernel<DD, true><<<grid, dim3(256), 0, stream>>>(qq, St, out, BH, (int)N, M, tpw, wpu); \
+        output_bf16_kernel<DD, true><<<grid, dim3(256), 0, stream>>>(qq, St, out, BH, (int)N, M, tpw, wpu, heads); \
     else                                                                                           \
-        output_bf16_kernel<DD, false><<<grid, dim3(256), 0, stream>>>(qq, St, out, BH, (int)N, M, tpw, wpu)
+        output_bf16_kernel<DD, false><<<grid, dim3(256), 0, stream>>>(qq, St, out, BH, (int)N, M, tpw, wpu, heads)
     switch (D) {
         case 16: MHLA_LAUNCH_OUT(16); break;
         case 32: MHLA_LAUNCH_OUT(32); break;

@@ -70,7 +70,7 @@ __device__ __forceinline__ uint32_t token_bits(const typename TokenWords<P>::typ
 template <int D, bool PIPE, bool NT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void summaries_bf16_kernel(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, float* __restrict__ S, int64_t BH, int N, int M,
-    int wpb, int nseg, int segC) {
+    int wpb, int nseg, int segC, int heads) {
     constexpr int P = D / 16;
     constexpr int L = D * D + D;
     typedef typename TokenWords<P>::type TW;
@@ -225,7 +225,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
     if (!active || seg != 0) return;
 
     // With token segments, S points at the partial array [nseg][M][BH][L].
-    float* out = S + ((int64_t)wseg * M * BH + blk * BH + pair) * (int64_t)L;
+    float* out = S + ((int64_t)wseg * M * BH + blk * BH + summary_row(pair, heads, BH)) * (int64_t)L;
 #pragma unroll
     for (int a = 0; a < P; ++a)
 #pragma unroll
@@ -241,14 +241,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
 __global__ __launch_bounds__(256) void summaries_f32_kernel(const float* __restrict__ K,
                                                             const float* __restrict__ V,
                                                             float* __restrict__ S, int64_t BH, int64_t N,
-                                                            int64_t M, int D) {
+                                                            int64_t M, int D, int heads) {
     const int64_t unit = blockIdx.x;  // pair * M + block
     const int64_t pair = unit / M, blk = unit % M;
     const int64_t C = N / M;
     const int P = D / 16, L = D * D + D;
     const float* Kp = K + (pair * N + blk * C) * D;
     const float* Vp = V + (pair * N + blk * C) * D;
-    float* out = S + (blk * BH + pair) * (int64_t)L;
+    float* out = S + (blk * BH + summary_row(pair, heads, BH)) * (int64_t)L;
     for (int e = threadIdx.x; e < L; e += blockDim.x) {
         float acc = 0.f;
         if (e < D * D) {
@@ -309,11 +309,11 @@ size_t summary_partial_bytes(int dtype, int64_t BH, int64_t N, int D, int64_t M)
 }
 
 hipError_t launch_summaries(int dtype, const void* k, const void* v, float* S, int64_t BH, int64_t N,
-                            int D, int64_t M, float* partial, hipStream_t stream) {
+                            int D, int64_t M, int heads, float* partial, hipStream_t stream) {
     const int64_t units = BH * M;
     if (dtype == kDtypeF32) {
         summaries_f32_kernel<<<dim3((unsigned)units), dim3(256), 0, stream>>>(
-            (const float*)k, (const float*)v, S, BH, N, M, D);
+            (const float*)k, (const float*)v, S, BH, N, M, D, heads);
         return hipGetLastError();
     }
     const SummarySplit sp = summary_split(BH, N, M);
@@ -330,10 +330,10 @@ hipError_t launch_summaries(int dtype, const void* k, const void* v, float* S, i
     case DD:                                                                                                  \
         if (nt)                                                                                               \
             summaries_bf16_kernel<DD, PIPE, true><<<dim3((unsigned)grid), dim3(256), lds, stream>>>(          \
-                kk, vv, dst, BH, (int)N, (int)M, sp.wpb, sp.nseg, sp.segC);                                   \
+                kk, vv, dst, BH, (int)N, (int)M, sp.wpb, sp.nseg, sp.segC, heads);                                   \
         else                                                                                                  \
             summaries_bf16_kernel<DD, PIPE, false><<<dim3((unsigned)grid), dim3(256), lds, stream>>>(         \
-                kk, vv, dst, BH, (int)N, (int)M, sp.wpb, sp.nseg, sp.segC);                                   \
+                kk, vv, dst, BH, (int)N, (int)M, sp.wpb, sp.nseg, sp.segC, heads);                                   \
         break;
     switch (D) {
         MHLA_SUMMARIES_CASE(16, true)

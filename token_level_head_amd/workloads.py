@@ -90,6 +90,13 @@ def mixing_weights(logits, causal):
     return (e / e.sum(axis=1, keepdims=True)).astype(np.float32)
 
 
+def per_head_weights(w: Workload, seed=None):
+    """[H, M, M] float32: one mixing matrix per head, drawn like W from a stream of
+    its own (seed + 7919), for the per-head option."""
+    rng = np.random.default_rng((w.seed if seed is None else seed) + 7919)
+    return np.stack([mixing_weights(rng.standard_normal((w.M, w.M)) * w.wscale, w.causal) for _ in range(w.H)])
+
+
 def make_inputs(w: Workload, seed=None):
     """q, k, v [B, H, N, d] float32 (bf16-exact for bf16 workloads) and W [M, M] float32."""
     if w.N % w.M:
