@@ -322,7 +322,7 @@ def main():
     # stages, so no host launch gap falls between two events.  `pre_done` still pending
     # once everything is enqueued shows that the GPU never waited for the host.
     filler = torch.empty(1 << 26, dtype=torch.float32, device="cuda")
-    for _ in range(64):
+    for _ in range(8 * args.steps):  # ~50 us of GPU work per fill, several per timed launch
         filler.fill_(0.0)
     pre_done = torch.cuda.Event()
     pre_done.record(stream)
