@@ -122,6 +122,32 @@ int mhla_forward_ex(const void* q, const void* k, const void* v, int dtype, cons
                     int64_t B, int64_t H, int64_t N, int64_t d, int64_t M, unsigned options,
                     mhla_stream_t stream);
 
+/*
+ * The forward pass over blocks given as token lists (§4.1: blocks are defined along
+ * spatial or spatio-temporal axes, "N_b tokens" each, of any sizes; App. E pads a
+ * 224 grid to 256 only so that equal blocks divide it).  Block b holds the tokens
+ * order[offsets[b]] .. order[offsets[b+1] - 1] -- positions 0 .. N-1 of the sequence,
+ * the same for every (batch, head) pair -- so 2D/3D tiles of a raster-ordered grid,
+ * ragged edge tiles included, need no reordering of q, k, v or out.
+ *
+ * order: device int32 [N], a permutation of 0 .. N-1; offsets: device int32 [M + 1],
+ * non-decreasing, offsets[0] = 0, offsets[M] = N (blocks may differ in size; an empty
+ * block has S_b = 0).  Both 4-byte aligned and not written by the call.  max_block:
+ * an upper bound of offsets[b+1] - offsets[b] (1 <= max_block <= N) used to plan the
+ * launches.  These preconditions are not checked on the device: the kernels clamp
+ * offsets to [0, N] and skip entries outside [0, N), so other contents give wrong
+ * results but no out-of-bounds access, and rows of out missing from `order` are not
+ * written.  N need not be a multiple of M.
+ *
+ * Non-causal only (MHLA_OPT_CAUSAL gives MHLA_ERR_UNSUPPORTED); the other options of
+ * mhla_forward_ex apply.  Always the staged path; with offsets[b] = b*N/M and the
+ * identity order it gives mhla_forward_ex's staged results.  Workspace: as
+ * mhla_workspace_bytes() with blocks of max_block tokens.
+ */
+int mhla_forward_blocks(const void* q, const void* k, const void* v, int dtype, const float* W, void* out,
+                        int64_t B, int64_t H, int64_t N, int64_t d, int64_t M, const int32_t* order,
+                        const int32_t* offsets, int64_t max_block, unsigned options, mhla_stream_t stream);
+
 /* Which path mhla_forward (dtype MHLA_DTYPE_BF16) or mhla_forward_f32
  * (MHLA_DTYPE_F32; always staged) takes for these sizes: MHLA_PATH_STAGED or
  * MHLA_PATH_FUSED; -1 for invalid sizes or dtype. */

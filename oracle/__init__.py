@@ -59,6 +59,8 @@ class Oracle:
                                                  ctypes.c_int, ctypes.c_int]
         self.lib.mhla_oracle_forward_ex.argtypes = [_f32p, _f32p, _f32p, _f32p, _f64p, _L, _L, _L, _L, _L,
                                                     ctypes.c_int, ctypes.c_int]
+        self.lib.mhla_oracle_forward_blocks.argtypes = [_f32p, _f32p, _f32p, _f32p, _f64p, _L, _L, _L, _L, _L,
+                                                        ctypes.POINTER(ctypes.c_int), ctypes.c_int, ctypes.c_int]
 
     def phi(self, x):
         return self.lib.mhla_oracle_phi(float(x))
@@ -67,11 +69,12 @@ class Oracle:
     def _f32(a):
         return np.ascontiguousarray(a, dtype=np.float32)
 
-    def forward(self, q, k, v, W, causal=False, nthreads=1, normalize=True):
+    def forward(self, q, k, v, W, causal=False, nthreads=1, normalize=True, blk=None):
         """q, k, v: [B, H, N, d] float32; W: [M, M] float32 (or [H, M, M]: one matrix per
         head) -> float64 [B, H, N, d].
 
-        normalize=False drops the normaliser (MHLA §4.1, remark on the output)."""
+        normalize=False drops the normaliser (MHLA §4.1, remark on the output); blk [N]
+        assigns token t to block blk[t] (blocks of any sizes; non-causal only)."""
         q, k, v, W = (self._f32(a) for a in (q, k, v, W))
         B, H, N, d = q.shape
         M = W.shape[-1]
@@ -79,6 +82,16 @@ class Oracle:
             raise ValueError("a per-head W must be [H, M, M]")
         out = np.empty((B, H, N, d), dtype=np.float64)
         opts = (1 if causal else 0) | (0 if normalize else 2) | (4 if W.ndim == 3 else 0)
+        if blk is not None:
+            blk = np.ascontiguousarray(blk, dtype=np.intc)
+            if causal or blk.shape != (N,):
+                raise ValueError("blk must be [N] and the pass non-causal")
+            rc = self.lib.mhla_oracle_forward_blocks(
+                _ptr(q, _f32p), _ptr(k, _f32p), _ptr(v, _f32p), _ptr(W, _f32p), _ptr(out, _f64p), B, H, N, d, M,
+                blk.ctypes.data_as(ctypes.POINTER(ctypes.c_int)), opts, int(nthreads))
+            if rc != 0:
+                raise ValueError("mhla_oracle_forward_blocks rejected its arguments")
+            return out
         rc = self.lib.mhla_oracle_forward_ex(_ptr(q, _f32p), _ptr(k, _f32p), _ptr(v, _f32p), _ptr(W, _f32p),
                                              _ptr(out, _f64p), B, H, N, d, M, opts, int(nthreads))
         if rc != 0:

@@ -139,6 +139,70 @@ done:
     return rc;
 }
 
+/* One (batch, head) pair with an explicit block assignment: token t belongs to block
+ * blk[t] ([MHLA] §4.1: blocks of N_b tokens along spatial or spatio-temporal axes, of
+ * any sizes).  Non-causal. */
+static int forward_pair_blocks(const float* q, const float* k, const float* v, const float* W,
+                               double* out, long N, long d, long M, const int* blk, int normalise) {
+    double* S = (double*)calloc((size_t)(M * d * d), sizeof(double));
+    double* z = (double*)calloc((size_t)(M * d), sizeof(double));
+    double* St = (double*)malloc(sizeof(double) * M * d * d);
+    double* zt = (double*)malloc(sizeof(double) * M * d);
+    double* fq = (double*)malloc(sizeof(double) * d);
+    double* fk = (double*)malloc(sizeof(double) * d);
+    int rc = -1;
+    if (!S || !z || !St || !zt || !fq || !fk) goto done;
+    for (long j = 0; j < N; ++j) { /* step 2: every token into its own block's summary */
+        const long b = blk[j];
+        if (b < 0 || b >= M) goto done;
+        for (long r = 0; r < d; ++r) fk[r] = mhla_oracle_phi((double)k[j * d + r]);
+        for (long r = 0; r < d; ++r) {
+            for (long c = 0; c < d; ++c) S[(b * d + r) * d + c] += fk[r] * (double)v[j * d + c];
+            z[b * d + r] += fk[r];
+        }
+    }
+    if (mhla_oracle_mix(S, z, W, 1, d, M, 0, St, zt) != 0) goto done;
+    for (long t = 0; t < N; ++t) { /* step 4 with the mixed summary of t's block */
+        const long i = blk[t];
+        const float* qt = q + t * d;
+        for (long r = 0; r < d; ++r) fq[r] = mhla_oracle_phi((double)qt[r]);
+        double dot = 0.0;
+        for (long r = 0; r < d; ++r) dot += fq[r] * zt[i * d + r];
+        const double guarded = dot + MHLA_ORACLE_EPS;
+        for (long c = 0; c < d; ++c) {
+            double acc = 0.0;
+            for (long r = 0; r < d; ++r) acc += fq[r] * St[(i * d + r) * d + c];
+            out[t * d + c] = normalise ? acc / guarded : acc;
+        }
+    }
+    rc = 0;
+done:
+    free(S); free(z); free(St); free(zt); free(fq); free(fk);
+    return rc;
+}
+
+int mhla_oracle_forward_blocks(const float* q, const float* k, const float* v, const float* W,
+                               double* out, long B, long H, long N, long d, long M, const int* blk,
+                               int options, int nthreads) {
+    if (B < 1 || H < 1 || N < 1 || d < 1 || M < 1 || !q || !k || !v || !W || !out || !blk) return -1;
+    if (options & ~(MHLA_ORACLE_NO_NORMALISER | MHLA_ORACLE_W_PER_HEAD)) return -1; /* non-causal */
+    const int normalise = !(options & MHLA_ORACLE_NO_NORMALISER);
+    const int per_head = (options & MHLA_ORACLE_W_PER_HEAD) != 0;
+    const long BH = B * H;
+    int failures = 0;
+    (void)nthreads;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads > 0 ? nthreads : 1) \
+    reduction(+ : failures)
+#endif
+    for (long p = 0; p < BH; ++p) {
+        const long off = p * N * d;
+        const float* Wq = per_head ? W + (p % H) * M * M : W;
+        failures += forward_pair_blocks(q + off, k + off, v + off, Wq, out + off, N, d, M, blk, normalise) != 0;
+    }
+    return failures ? -1 : 0;
+}
+
 int mhla_oracle_forward_ex(const float* q, const float* k, const float* v, const float* W,
                            double* out, long B, long H, long N, long d, long M, int options,
                            int nthreads) {

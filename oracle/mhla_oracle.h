@@ -65,6 +65,13 @@ int mhla_oracle_forward(const float* q, const float* k, const float* v, const fl
 #define MHLA_ORACLE_W_PER_HEAD 4    /* W is [H][M][M]: head h applies §4.1 with its own matrix
                                        W + h*M*M (the pages describe one matrix for all heads) */
 
+/* The non-causal forward pass with an explicit block assignment: token t of every
+ * (batch, head) pair belongs to block blk[t] (0 <= blk[t] < M; blocks of any sizes and
+ * shapes, [MHLA] §4.1).  options: MHLA_ORACLE_NO_NORMALISER, MHLA_ORACLE_W_PER_HEAD. */
+int mhla_oracle_forward_blocks(const float* q, const float* k, const float* v, const float* W,
+                               double* out, long B, long H, long N, long d, long M, const int* blk,
+                               int options, int nthreads);
+
 /* The forward pass with options; mhla_oracle_forward(.., causal, ..) is
  * mhla_oracle_forward_ex(.., causal ? MHLA_ORACLE_CAUSAL : 0, ..). */
 int mhla_oracle_forward_ex(const float* q, const float* k, const float* v, const float* W,

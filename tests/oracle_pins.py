@@ -32,7 +32,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 from oracle import bruteforce  # noqa: E402
-from token_level_head_amd.workloads import WORKLOADS, make_inputs, mixing_weights, per_head_weights  # noqa: E402
+from token_level_head_amd.workloads import (WORKLOADS, grid_blocks, make_inputs, mixing_weights,  # noqa: E402
+                                            per_head_weights, random_blocks)
 
 EPS = 1e-6
 GOLDEN = os.path.join(ROOT, "tests", "golden", "hand_example.txt")
@@ -395,6 +396,42 @@ def pin_per_head_equal_matrices(orc):
         y = orc.forward(q, k, v, W0, causal=causal)
         yh = orc.forward(q, k, v, np.stack([W0] * 3), causal=causal)
         assert np.array_equal(y, yh), causal
+
+
+# ---- blocks given as token lists (any sizes and shapes, MHLA §4.1) ----
+
+def pin_token_list_bruteforce(orc):
+    """Unequal, scattered blocks (one of them empty) against the explicit definition."""
+    for i, (B, H, N, d, M) in enumerate([(2, 2, 90, 6, 7), (1, 3, 64, 8, 16)]):
+        q, k, v, _ = _inputs(B, H, N, d, 1, False, seed=340 + i)  # N need not divide into M blocks
+        W = mixing_weights(np.random.default_rng(340 + i).standard_normal((M, M)), False)
+        order, offsets, blk = random_blocks(N, M, seed=340 + i)
+        blk = np.where(blk == 3, 4, blk)  # leave block 3 empty
+        Wh = per_head_weights(WORKLOADS["tiny_f32"].shrink(H=H, M=M, seed=341 + i))
+        for W_ in (W, Wh):
+            for normalize in (True, False):
+                y = orc.forward(q, k, v, W_, normalize=normalize, blk=blk)
+                ref = bruteforce.forward(q, k, v, W_, blk=blk, normalize=normalize)
+                assert rel_err(y, ref) < 1e-12, (B, H, N, d, M, W_.ndim, normalize)
+
+
+def pin_token_list_2d_tiles(orc):
+    """A 6 x 10 raster grid in 4 x 4 tiles (ragged edge tiles) against the explicit definition."""
+    order, offsets, blk = grid_blocks((6, 10), (4, 4))
+    M = len(offsets) - 1
+    q, k, v, W = _inputs(1, 2, 60, 8, M, False, seed=350)
+    y = orc.forward(q, k, v, W, blk=blk)
+    assert rel_err(y, bruteforce.forward(q, k, v, W, blk=blk)) < 1e-12
+    assert sorted(np.diff(offsets)) == [4, 8, 8, 8, 16, 16]  # 2 x 3 tiles, ragged bottom and right
+
+
+def pin_token_list_contiguous_is_plain(orc):
+    """Equal contiguous blocks given as a token list reproduce the plain pass bit for bit."""
+    q, k, v, W = _inputs(2, 2, 120, 6, 10, False, seed=351)
+    blk = np.arange(120) // 12
+    for normalize in (True, False):
+        assert np.array_equal(orc.forward(q, k, v, W, normalize=normalize, blk=blk),
+                              orc.forward(q, k, v, W, normalize=normalize))
 
 
 def _recover(phiq, num):

@@ -158,3 +158,70 @@ def test_per_head_mixing(orc, case):
     e = rel(y.cpu().numpy(), ref)
     say(f"[per-head]   max|dY|/max|Y| = {e:.3e}")
     assert e <= TOL[dtype], e
+
+
+TOKEN_LISTS = [  # (B, H, grid, tile, d, dtype, per_head): raster grids cut into tiles, ragged edges
+    (2, 2, (16, 16), (4, 4), 64, "bf16", False),    # equal 4 x 4 tiles (C = 16)
+    (1, 3, (14, 14), (4, 4), 64, "bf16", False),    # 224 / 16 without padding: 2-wide edge tiles
+    (1, 2, (40, 48), (16, 16), 32, "bf16", True),   # 16 x 16 tiles, ragged bottom row, per-head W
+    (2, 1, (8, 12, 12), (2, 8, 8), 16, "bf16", False),  # 3D (time, h, w) tiles
+    (1, 2, (20, 30), (16, 16), 32, "f32", False),   # float32 path
+]
+
+
+@pytest.mark.parametrize("case", TOKEN_LISTS, ids=lambda c: "B{}H{}g{}t{}d{}{}{}".format(
+    c[0], c[1], "x".join(map(str, c[2])), "x".join(map(str, c[3])), c[4], c[5], "ph" if c[6] else ""))
+def test_token_list_blocks(orc, case):
+    """Raster-ordered grids cut into tiles, given as token lists, against the oracle's block assignment."""
+    from token_level_head_amd.workloads import grid_blocks, per_head_weights, mixing_weights
+    B, H, grid, tile, d, dtype, per_head = case
+    order, offsets, blk = grid_blocks(grid, tile)
+    N, M = len(order), len(offsets) - 1
+    w = WORKLOADS["tiny_f32"].shrink(B=B, H=H, N=N, d=d, M=1, dtype=dtype, seed=970 + N)
+    q, k, v, _ = make_inputs(w)
+    W = (per_head_weights(w.shrink(M=M)) if per_head
+         else mixing_weights(np.random.default_rng(971 + N).standard_normal((M, M)), False))
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    qd, kd, vd = (torch.from_numpy(a).to("cuda", tdt) for a in (q, k, v))
+    Wd = torch.from_numpy(W).cuda()
+    od, fd = torch.from_numpy(order).cuda(), torch.from_numpy(offsets).cuda()
+    say(f"[token lists] B={B} H={H} grid={grid} tile={tile} N={N} M={M} d={d} dtype={dtype} per_head={per_head}")
+    for normalize in (True, False):
+        y = torch.full(q.shape, float("nan"), dtype=torch.float32, device="cuda")
+        mh.mhla_forward_blocks(qd, kd, vd, Wd, y, od, fd, int(np.diff(offsets).max()), normalize=normalize)
+        torch.cuda.synchronize()
+        ref = orc.forward(q, k, v, W, nthreads=NTHREADS, normalize=normalize, blk=blk)
+        e = rel(y.cpu().numpy(), ref)
+        say(f"[token lists]   normalize={normalize}: {e:.3e}")
+        assert e <= TOL[dtype], (normalize, e)
+
+
+def test_token_list_identity_is_staged_path():
+    """Equal contiguous blocks as a token list give the staged path's bits."""
+    w = WORKLOADS["tiny_f32"].shrink(B=2, H=2, N=1024, d=32, M=16, dtype="bf16", seed=980)
+    q, k, v, W = make_inputs(w)
+    qd, kd, vd = (torch.from_numpy(a).to("cuda", torch.bfloat16) for a in (q, k, v))
+    Wd = torch.from_numpy(W).cuda()
+    order = torch.arange(1024, dtype=torch.int32, device="cuda")
+    offsets = torch.arange(0, 1025, 64, dtype=torch.int32, device="cuda")
+    a = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    assert mh.mhla_forward_path(2, 2, 1024, 32, 16) == mh.MHLA_PATH_STAGED
+    mh.mhla_forward(qd, kd, vd, Wd, a)
+    mh.mhla_forward_blocks(qd, kd, vd, Wd, b, order, offsets, 64)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_token_list_rejects_causal():
+    q = torch.zeros((1, 1, 16, 16), dtype=torch.bfloat16, device="cuda")
+    W = torch.ones((1, 1), dtype=torch.float32, device="cuda")
+    out = torch.zeros((1, 1, 16, 16), dtype=torch.float32, device="cuda")
+    order = torch.arange(16, dtype=torch.int32, device="cuda")
+    offsets = torch.tensor([0, 16], dtype=torch.int32, device="cuda")
+    import ctypes
+    st = mh.load_library().mhla_forward_blocks(*(ctypes.c_void_p(t.data_ptr()) for t in (q, q, q)), 0,
+                                               ctypes.c_void_p(W.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                                               1, 1, 16, 16, 1, ctypes.c_void_p(order.data_ptr()),
+                                               ctypes.c_void_p(offsets.data_ptr()), 16, mh.MHLA_OPT_CAUSAL, None)
+    assert st == mh.MHLA_ERR_UNSUPPORTED

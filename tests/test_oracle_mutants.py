@@ -45,6 +45,14 @@ MUTANTS = {
     "per_head_by_batch": ("const float* Wp = per_head ? W + (p % H) * M * M : W;",
                           "const float* Wp = per_head ? W + (p / H) * M * M : W;"),
     "per_head_ignored": ("const float* Wp = per_head ? W + (p % H) * M * M : W;", "const float* Wp = W;"),
+    "token_list_output_block_shifted": ("const long i = blk[t];", "const long i = blk[(t + 1) % N];"),
+    "token_list_summary_contiguous": ("const long b = blk[j];", "const long b = j * M / N;"),
+    "token_list_eps_dropped": ("const double guarded = dot + MHLA_ORACLE_EPS;", "const double guarded = dot;"),
+    "token_list_normaliser_ignored": ("out[t * d + c] = normalise ? acc / guarded : acc;",
+                                      "out[t * d + c] = acc / guarded;"),
+    "token_list_option_ignored": ("const int normalise = !(options & MHLA_ORACLE_NO_NORMALISER);",
+                                  "const int normalise = 1;"),
+    "token_list_per_head_ignored": ("const float* Wq = per_head ? W + (p % H) * M * M : W;", "const float* Wq = W;"),
 }
 
 

@@ -16,7 +16,7 @@ _BINDING_NAMES = {
     "mhla_output", "mhla_status_string", "mhla_summary_floats", "mhla_unpack_summaries", "mhla_version",
     "mhla_workspace_bytes", "mhla_decode_state_bytes", "mhla_decode_step",
     "mhla_backward_workspace_bytes", "mhla_backward", "mhla_forward_ex", "MHLA_OPT_CAUSAL",
-    "MHLA_OPT_NO_NORMALIZER", "MHLA_OPT_OUT_BF16", "MHLA_OPT_W_PER_HEAD",
+    "MHLA_OPT_NO_NORMALIZER", "MHLA_OPT_OUT_BF16", "MHLA_OPT_W_PER_HEAD", "mhla_forward_blocks",
 }
 
 

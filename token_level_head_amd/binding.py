@@ -36,6 +36,8 @@ SIGNATURES = {
     "mhla_forward": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _P]),
     "mhla_forward_f32": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _P]),
     "mhla_forward_ex": (_I, [_P, _P, _P, _I, _P, _P, _I64, _I64, _I64, _I64, _I64, ctypes.c_uint, _P]),
+    "mhla_forward_blocks": (_I, [_P, _P, _P, _I, _P, _P, _I64, _I64, _I64, _I64, _I64, _P, _P, _I64, ctypes.c_uint,
+                                 _P]),
     "mhla_workspace_bytes": (_I64, [_I64, _I64, _I64, _I64, _I64, _I]),
     "mhla_forward_path": (_I, [_I64, _I64, _I64, _I64, _I64, _I, _I]),
     "mhla_summary_floats": (_I64, [_I64]),
@@ -130,6 +132,26 @@ def mhla_forward_ex(q, k, v, W, out, causal=False, normalize=True, stream=None):
         raise TypeError(f"unsupported output dtype {out.dtype}")
     _check(load_library().mhla_forward_ex(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(W), _ptr(out),
                                           B, H, N, d, M, opts, _stream(stream)))
+    return out
+
+
+def mhla_forward_blocks(q, k, v, W, out, order, offsets, max_block, normalize=True, stream=None):
+    """Blocks as token lists: order [N] and offsets [M + 1] int32 device tensors (block b =
+    order[offsets[b]:offsets[b+1]]), max_block >= the longest block.  W [M, M] or [H, M, M];
+    out float32 or bfloat16, as for mhla_forward_ex.  Non-causal."""
+    B, H, N, d, M = _dims(q, W)
+    if order.dtype != torch.int32 or offsets.dtype != torch.int32:
+        raise TypeError("order and offsets must be int32")
+    if tuple(order.shape) != (N,) or tuple(offsets.shape) != (M + 1,):
+        raise ValueError("order must be [N] and offsets [M + 1]")
+    opts = 0 if normalize else MHLA_OPT_NO_NORMALIZER
+    if W.dim() == 3:
+        opts |= MHLA_OPT_W_PER_HEAD
+    if out.dtype == torch.bfloat16:
+        opts |= MHLA_OPT_OUT_BF16
+    _check(load_library().mhla_forward_blocks(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(W), _ptr(out),
+                                              B, H, N, d, M, _ptr(order), _ptr(offsets), int(max_block), opts,
+                                              _stream(stream)))
     return out
 
 

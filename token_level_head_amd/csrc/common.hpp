@@ -130,6 +130,26 @@ __device__ __forceinline__ const float* pair_w(const float* W, int64_t pair, int
     return heads > 0 ? W + (pair % heads) * M * M : W;
 }
 
+// Token range [beg, end) of block b in the block layout's token list.
+__device__ __forceinline__ void block_range(const BlockLayout& lay, int64_t b, int N, int64_t M, int& beg,
+                                            int& end) {
+    if (lay.offsets) {
+        beg = min(max(lay.offsets[b], 0), N);
+        end = min(max(lay.offsets[b + 1], beg), N);
+    } else {
+        const int C = (int)(N / M);
+        beg = (int)b * C;
+        end = beg + C;
+    }
+}
+// Sequence position of list entry i of a block layout (i < N), or -1 for an entry
+// outside [0, N).  Identity without a token list.
+__device__ __forceinline__ int token_row(const BlockLayout& lay, int i, int N) {
+    if (!lay.order) return i;
+    const int r = lay.order[i];
+    return (unsigned)r < (unsigned)N ? r : -1;
+}
+
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 // Masked load without a branch: the address falls back to `safe` (any valid,

@@ -11,6 +11,16 @@ namespace mhla {
 constexpr int kDtypeBF16 = 0;
 constexpr int kDtypeF32 = 1;
 
+// Which tokens form each block.  Null pointers: M equal contiguous blocks of N / M
+// tokens.  Otherwise block b is the token list order[offsets[b]] .. order[offsets[b+1]-1]
+// (positions in the sequence, the same for every (batch, head) pair): blocks of any
+// sizes and shapes (2D/3D tiles of a raster-ordered grid).  Kernels clamp offsets to
+// [0, N] and skip list entries outside [0, N), so any array contents are memory-safe.
+struct BlockLayout {
+    const int32_t* order;    // [N] device
+    const int32_t* offsets;  // [M + 1] device
+};
+
 // Where and how a kernel writes the attention output Y ([pair][N][d], row-major).
 struct OutSpec {
     void* y;   // float32 values, or bfloat16 bit patterns when bf16 != 0
@@ -35,9 +45,11 @@ inline bool stream_token_inputs(int64_t BH, int64_t N, int D, int esize) {
 // (batch, head) pairs are cut into token segments whose partial summaries go to
 // `partial` (summary_partial_bytes() bytes, 16-byte aligned; may be null when that
 // is 0) and are then added into S.
-size_t summary_partial_bytes(int dtype, int64_t BH, int64_t N, int D, int64_t M);
+// `cmax` bounds the block length (N / M without a token list) and plans the split.
+size_t summary_partial_bytes(int dtype, int64_t BH, int64_t cmax, int D, int64_t M);
 hipError_t launch_summaries(int dtype, const void* k, const void* v, float* S, int64_t BH, int64_t N,
-                            int D, int64_t M, int heads, float* partial, hipStream_t stream);
+                            int D, int64_t M, int heads, const BlockLayout& lay, int64_t cmax, float* partial,
+                            hipStream_t stream);
 
 // Stage 2: St[i][col] = sum_b W[i,b] S[b][col] (causal: b < i), col < BH * (d*d + d).
 // The bf16 path needs mix_fragment_bytes(M) bytes of device scratch at frag_ws
@@ -49,7 +61,7 @@ hipError_t launch_mix(const float* S, const float* W, float* St, int64_t BH, int
 // Stage 3: Y [pair][N][d] from Q and St (causal also K, V and W[i,i]), written as `out` says.
 hipError_t launch_output(int dtype, const void* q, const void* k, const void* v, const float* St,
                          const float* W, const OutSpec& out, int64_t BH, int64_t N, int D, int64_t M, bool causal,
-                         int heads, hipStream_t stream);
+                         int heads, const BlockLayout& lay, int64_t cmax, hipStream_t stream);
 
 // Causal bf16 output for blocks of at most 256 tokens: the within-block prefix as one
 // masked C x C product per block (used by launch_output when applicable).

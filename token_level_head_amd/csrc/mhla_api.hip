@@ -47,11 +47,11 @@ int check_ptr(const void* p, const char* name) {
 
 // Sizes shared by every entry point.  Element counts must fit in int64 with
 // margin, and grid sizes in 32 bits.
-int check_sizes(int64_t B, int64_t H, int64_t N, int64_t d, int64_t M) {
+int check_sizes(int64_t B, int64_t H, int64_t N, int64_t d, int64_t M, bool equal_blocks = true) {
     if (B < 1 || H < 1 || N < 1 || d < 1 || M < 1)
         return fail(MHLA_ERR_INVALID_ARG, "sizes must be >= 1 (B=%lld H=%lld N=%lld d=%lld M=%lld)",
                     (long long)B, (long long)H, (long long)N, (long long)d, (long long)M);
-    if (N % M != 0)
+    if (equal_blocks && N % M != 0)
         return fail(MHLA_ERR_INVALID_ARG, "N=%lld is not a multiple of M=%lld", (long long)N, (long long)M);
     if (d != 16 && d != 32 && d != 64)
         return fail(MHLA_ERR_UNSUPPORTED, "d=%lld is not one of 16, 32, 64", (long long)d);
@@ -123,9 +123,10 @@ size_t frag_bytes_aligned(int64_t M, int64_t nw = 1) {
     return (nw * mhla::mix_fragment_bytes(M) + 255) / 256 * 256;
 }
 
-size_t workspace_bytes(int dtype, int64_t BH, int64_t N, int64_t d, int64_t M, int64_t nw = 1) {
+// cmax: the longest block (N / M for equal blocks).
+size_t workspace_bytes(int dtype, int64_t BH, int64_t cmax, int64_t d, int64_t M, int64_t nw = 1) {
     return 2 * (size_t)(M * BH * summary_floats(d)) * sizeof(float) + frag_bytes_aligned(M, nw) +
-           mhla::summary_partial_bytes(dtype, BH, N, (int)d, M);
+           mhla::summary_partial_bytes(dtype, BH, cmax, (int)d, M);
 }
 
 int pool_alloc(void** ptr, size_t bytes, hipStream_t stream) {
@@ -148,15 +149,30 @@ int forward_path(int64_t B, int64_t H, int64_t N, int64_t d, int64_t M, int caus
 
 constexpr unsigned kKnownOptions = MHLA_OPT_CAUSAL | MHLA_OPT_NO_NORMALIZER | MHLA_OPT_OUT_BF16 | MHLA_OPT_W_PER_HEAD;
 
+// order/offsets: a token list per block (both null: M equal contiguous blocks);
+// max_block bounds the block lengths for launch planning.
 int forward_impl(int dtype, const void* q, const void* k, const void* v, const float* W, void* out, int64_t B,
-                 int64_t H, int64_t N, int64_t d, int64_t M, unsigned options, mhla_stream_t stream_) {
-    int st = check_sizes(B, H, N, d, M);
+                 int64_t H, int64_t N, int64_t d, int64_t M, unsigned options, const int32_t* order,
+                 const int32_t* offsets, int64_t max_block, mhla_stream_t stream_) {
+    const bool listed = order || offsets;
+    int st = check_sizes(B, H, N, d, M, !listed);
     if (st) return st;
     if (options & ~kKnownOptions) return fail(MHLA_ERR_INVALID_ARG, "unknown option bits 0x%x", options & ~kKnownOptions);
     if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
         (st = check_ptr(W, "W")) || (st = check_ptr(out, "out")))
         return st;
     const int causal = (options & MHLA_OPT_CAUSAL) != 0;
+    if (listed) {
+        if (!order || !offsets) return fail(MHLA_ERR_INVALID_ARG, "order and offsets must both be given");
+        if (((uintptr_t)order & 3u) || ((uintptr_t)offsets & 3u))
+            return fail(MHLA_ERR_INVALID_ARG, "order and offsets must be 4-byte aligned");
+        if (max_block < 1 || max_block > N)
+            return fail(MHLA_ERR_INVALID_ARG, "max_block=%lld is outside [1, N]", (long long)max_block);
+        if (causal) return fail(MHLA_ERR_UNSUPPORTED, "token-list blocks are non-causal only");
+    } else {
+        max_block = N / M;
+    }
+    const mhla::BlockLayout lay{order, offsets};
     const mhla::OutSpec os{out, (options & MHLA_OPT_OUT_BF16) != 0, (options & MHLA_OPT_NO_NORMALIZER) == 0};
     const int heads = (options & MHLA_OPT_W_PER_HEAD) ? (int)H : 0;  // H fits: B*H*M <= 2^29
     const int64_t nw = heads ? H : 1;
@@ -169,31 +185,32 @@ int forward_impl(int dtype, const void* q, const void* k, const void* v, const f
 
     hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
     const int64_t BH = B * H;
-    if (forward_path(B, H, N, d, M, causal, dtype) == MHLA_PATH_FUSED) {
+    if (!listed && forward_path(B, H, N, d, M, causal, dtype) == MHLA_PATH_FUSED) {
         hipError_t e = mhla::launch_fused(q, k, v, W, os, BH, N, (int)d, M, heads, stream);
         if (e != hipSuccess) return hip_fail(e, "fused kernel");
         return ok();
     }
     const size_t arr = (size_t)(M * BH * summary_floats(d)) * sizeof(float);
-    const size_t total = workspace_bytes(dtype, BH, N, d, M, nw);
+    const size_t total = workspace_bytes(dtype, BH, max_block, d, M, nw);
     void* ws = nullptr;
     int st2 = pool_alloc(&ws, total, stream);
     if (st2) return st2;
     float* S = static_cast<float*>(ws);
     float* St = S + arr / sizeof(float);
     void* frags = St + arr / sizeof(float);
-    float* partial = mhla::summary_partial_bytes(dtype, BH, N, (int)d, M)
+    float* partial = mhla::summary_partial_bytes(dtype, BH, max_block, (int)d, M)
                          ? reinterpret_cast<float*>(static_cast<char*>(frags) + frag_bytes_aligned(M, nw))
                          : nullptr;
     const char* what = "summary kernel";
-    hipError_t e = mhla::launch_summaries(dtype, k, v, S, BH, N, (int)d, M, heads, partial, stream);
+    hipError_t e = mhla::launch_summaries(dtype, k, v, S, BH, N, (int)d, M, heads, lay, max_block, partial, stream);
     if (e == hipSuccess) {
         what = "mixing kernel";
         e = mhla::launch_mix(S, W, St, BH, (int)d, M, causal != 0, dtype == mhla::kDtypeF32, heads, frags, stream);
     }
     if (e == hipSuccess) {
         what = "output kernel";
-        e = mhla::launch_output(dtype, q, k, v, St, W, os, BH, N, (int)d, M, causal != 0, heads, stream);
+        e = mhla::launch_output(dtype, q, k, v, St, W, os, BH, N, (int)d, M, causal != 0, heads, lay, max_block,
+                                stream);
     }
     hipError_t fe = hipFreeAsync(ws, stream);
     if (e != hipSuccess) return hip_fail(e, what);
@@ -207,24 +224,34 @@ extern "C" {
 
 int mhla_forward(const void* q, const void* k, const void* v, const float* W, float* out, int64_t B, int64_t H,
                  int64_t N, int64_t d, int64_t M, int causal, mhla_stream_t stream) {
-    return forward_impl(mhla::kDtypeBF16, q, k, v, W, out, B, H, N, d, M, causal ? MHLA_OPT_CAUSAL : 0u, stream);
+    return forward_impl(mhla::kDtypeBF16, q, k, v, W, out, B, H, N, d, M, causal ? MHLA_OPT_CAUSAL : 0u, nullptr,
+                        nullptr, 0, stream);
 }
 
 int mhla_forward_f32(const float* q, const float* k, const float* v, const float* W, float* out, int64_t B,
                      int64_t H, int64_t N, int64_t d, int64_t M, int causal, mhla_stream_t stream) {
-    return forward_impl(mhla::kDtypeF32, q, k, v, W, out, B, H, N, d, M, causal ? MHLA_OPT_CAUSAL : 0u, stream);
+    return forward_impl(mhla::kDtypeF32, q, k, v, W, out, B, H, N, d, M, causal ? MHLA_OPT_CAUSAL : 0u, nullptr,
+                        nullptr, 0, stream);
 }
 
 int mhla_forward_ex(const void* q, const void* k, const void* v, int dtype, const float* W, void* out, int64_t B,
                     int64_t H, int64_t N, int64_t d, int64_t M, unsigned options, mhla_stream_t stream) {
     if (dtype != MHLA_DTYPE_BF16 && dtype != MHLA_DTYPE_F32) return fail(MHLA_ERR_INVALID_ARG, "bad dtype %d", dtype);
-    return forward_impl(dtype, q, k, v, W, out, B, H, N, d, M, options, stream);
+    return forward_impl(dtype, q, k, v, W, out, B, H, N, d, M, options, nullptr, nullptr, 0, stream);
+}
+
+int mhla_forward_blocks(const void* q, const void* k, const void* v, int dtype, const float* W, void* out,
+                        int64_t B, int64_t H, int64_t N, int64_t d, int64_t M, const int32_t* order,
+                        const int32_t* offsets, int64_t max_block, unsigned options, mhla_stream_t stream) {
+    if (dtype != MHLA_DTYPE_BF16 && dtype != MHLA_DTYPE_F32) return fail(MHLA_ERR_INVALID_ARG, "bad dtype %d", dtype);
+    if (!order || !offsets) return fail(MHLA_ERR_INVALID_ARG, "order and offsets are required");
+    return forward_impl(dtype, q, k, v, W, out, B, H, N, d, M, options, order, offsets, max_block, stream);
 }
 
 int64_t mhla_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int64_t M, int causal) {
     (void)causal;
     if (check_sizes(B, H, N, d, M) != MHLA_OK) return -1;
-    return (int64_t)workspace_bytes(mhla::kDtypeBF16, B * H, N, d, M);
+    return (int64_t)workspace_bytes(mhla::kDtypeBF16, B * H, N / M, d, M);
 }
 
 int mhla_forward_path(int64_t B, int64_t H, int64_t N, int64_t d, int64_t M, int causal, int dtype) {
@@ -248,9 +275,11 @@ int mhla_block_summaries(const void* k, const void* v, int dtype, float* S, int6
         return fail(MHLA_ERR_INVALID_ARG, "S overlaps an input");
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     void* partial = nullptr;
-    const size_t pbytes = mhla::summary_partial_bytes(dtype, B * H, N, (int)d, M);
+    const size_t pbytes = mhla::summary_partial_bytes(dtype, B * H, N / M, (int)d, M);
     if (pbytes && (st = pool_alloc(&partial, pbytes, s))) return st;
-    hipError_t e = mhla::launch_summaries(dtype, k, v, S, B * H, N, (int)d, M, 0, static_cast<float*>(partial), s);
+    const mhla::BlockLayout equal{nullptr, nullptr};
+    hipError_t e = mhla::launch_summaries(dtype, k, v, S, B * H, N, (int)d, M, 0, equal, N / M,
+                                          static_cast<float*>(partial), s);
     hipError_t fe = partial ? hipFreeAsync(partial, s) : hipSuccess;
     if (e != hipSuccess) return hip_fail(e, "summary kernel");
     if (fe != hipSuccess) return hip_fail(fe, "workspace release");
@@ -292,7 +321,8 @@ int mhla_output(const void* q, const void* k, const void* v, int dtype, const fl
                     overlaps(out, out_bytes, W, (size_t)(M * M) * 4))))
         return fail(MHLA_ERR_INVALID_ARG, "out overlaps an input");
     const mhla::OutSpec os{out, 0, 1};
-    hipError_t e = mhla::launch_output(dtype, q, k, v, St, W, os, B * H, N, (int)d, M, causal != 0, 0,
+    const mhla::BlockLayout equal{nullptr, nullptr};
+    hipError_t e = mhla::launch_output(dtype, q, k, v, St, W, os, B * H, N, (int)d, M, causal != 0, 0, equal, N / M,
                                        reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "output kernel");
     return ok();

@@ -67,14 +67,16 @@ __device__ __forceinline__ void build_b(const f32x4 (&ch)[P * P], bf16x8 (&bh)[K
 // ybase (the pair's first element of Y).
 template <int P, int PJ>
 __device__ __forceinline__ void store_rows(const OutSpec& o, int64_t ybase, int t0, int bend, int g, int n,
-                                           int jb0, const f32x4 (&acc)[PJ], float den) {
+                                           int jb0, const f32x4 (&acc)[PJ], float den,
+                                           const BlockLayout& lay = BlockLayout{nullptr, nullptr}, int N = 0) {
     constexpr int D = 16 * P;
     const float rden = out_scale(o, den);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const float r = __shfl(rden, 4 * g + i, 64);
-        const int row = t0 + 4 * g + i;
-        if (row < bend) {
+        const int entry = t0 + 4 * g + i;  // list entry; the row of Y it fills:
+        const int row = entry < bend ? token_row(lay, entry, N) : -1;
+        if (row >= 0) {
             const int64_t e = ybase + row * D + P * n + jb0;
             if constexpr (PJ == 4) {
                 store_out(o, e, f32x4{acc[0][i] * r, acc[1][i] * r, acc[2][i] * r, acc[3][i] * r});
@@ -91,7 +93,8 @@ __device__ __forceinline__ void store_rows(const OutSpec& o, int64_t ybase, int 
 template <int D, bool NT>
 __global__ __launch_bounds__(256) void output_bf16_kernel(const uint16_t* __restrict__ Q,
                                                           const float* __restrict__ St, OutSpec o,
-                                                          int64_t BH, int N, int64_t M, int tpw, int wpu, int heads) {
+                                                          int64_t BH, int N, int64_t M, int tpw, int wpu, int heads,
+                                                          BlockLayout lay) {
     constexpr int P = D / 16;
     constexpr int FL = 4 * P;                 // features per lane group
     constexpr int KS = D >= 32 ? D / 32 : 1;  // 16x16x32 k-steps (d = 16 pads to 32)
@@ -105,11 +108,11 @@ __global__ __launch_bounds__(256) void output_bf16_kernel(const uint16_t* __rest
     if (unit >= BH * M) return;  // whole wave; no barriers in this kernel
     const int64_t pair = unit / M;
     const int blk = (int)(unit % M);
-    const int C = (int)(N / M);
-    const int ntiles = (C + 15) / 16;
+    int bstart, bend;  // the block's range in the token list
+    block_range(lay, blk, N, M, bstart, bend);
+    const int ntiles = (bend - bstart + 15) / 16;
     const int tile_beg = s * tpw;
     const int tile_end = min(ntiles, tile_beg + tpw);
-    const int bstart = blk * C, bend = bstart + C;
 
     const float* sv = St + ((int64_t)blk * BH + summary_row(pair, heads, BH)) * L;
     f32x4 sch[P * P];
@@ -130,10 +133,11 @@ __global__ __launch_bounds__(256) void output_bf16_kernel(const uint16_t* __rest
     for (int tile = tile_beg; tile < tile_end; ++tile) {
         const int t0 = bstart + 16 * tile;
         // phi(Q) as the A operand: token t0 + n, group-local features of group g.
-        const int tq = t0 + n;
-        const bool qok = tq < bend;
+        const int tq = t0 + n;  // list entry
+        const int qrow = tq < bend ? token_row(lay, tq, N) : -1;
+        const bool qok = qrow >= 0;
         uint16_t qr[FL];
-        load_group<P, NT>(Qp + tq * D + FL * g, qok, Q, qr);
+        load_group<P, NT>(Qp + (qok ? qrow : 0) * D + FL * g, qok, Q, qr);
         issue_fence();
         bf16x8 aq[KS];
         float den = 0.f;
@@ -158,7 +162,7 @@ __global__ __launch_bounds__(256) void output_bf16_kernel(const uint16_t* __rest
                 acc[jb] = mfma32(aq[ks], bl[ks][jb], acc[jb]);
             }
         }
-        store_rows<P, P>(o, ybase, t0, bend, g, n, 0, acc, den);
+        store_rows<P, P>(o, ybase, t0, bend, g, n, 0, acc, den, lay, N);
     }
 }
 
@@ -346,12 +350,27 @@ __global__ __launch_bounds__(256) void output_f32_kernel(const float* __restrict
                                                          const float* __restrict__ V, const float* __restrict__ St,
                                                          const float* __restrict__ W, OutSpec o,
                                                          int64_t BH, int64_t N, int64_t M, int D, int causal,
-                                                         int heads) {
+                                                         int heads, BlockLayout lay) {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= BH * N * D) return;
     const int c = (int)(idx % D);
-    const int64_t t = (idx / D) % N, pair = idx / ((int64_t)N * D);
-    const int64_t C = N / M, blk = t / C;
+    const int64_t pair = idx / ((int64_t)N * D);
+    int64_t t = (idx / D) % N, blk;  // without a token list: token t of block t / C
+    if (lay.offsets) {
+        // list entry p = t: its block by binary search over the offsets, its row in the sequence
+        const int p = (int)t;
+        int lo = 0, hi = (int)M;  // the last b with offsets[b] <= p
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) / 2;
+            if (lay.offsets[mid] <= p) lo = mid; else hi = mid;
+        }
+        blk = lo;
+        t = token_row(lay, p, (int)N);
+        if (t < 0) return;
+    } else {
+        blk = t / (N / M);
+    }
+    const int64_t C = N / M;
     const int P = D / 16;
     const float* sv = St + (blk * BH + summary_row(pair, heads, BH)) * (int64_t)(D * D + D);
     const float* q = Q + (pair * N + t) * D;
@@ -374,16 +393,16 @@ __global__ __launch_bounds__(256) void output_f32_kernel(const float* __restrict
         num = fmaf(wii, ni, num);
         den = fmaf(wii, di, den);
     }
-    store_out(o, idx, o.norm ? num / (den + kEps) : num);
+    store_out(o, (pair * N + t) * D + c, o.norm ? num / (den + kEps) : num);
 }
 
 hipError_t launch_output(int dtype, const void* q, const void* k, const void* v, const float* St,
                          const float* W, const OutSpec& out, int64_t BH, int64_t N, int D, int64_t M, bool causal,
-                         int heads, hipStream_t stream) {
+                         int heads, const BlockLayout& lay, int64_t cmax, hipStream_t stream) {
     if (dtype == kDtypeF32) {
         const int64_t total = BH * N * D;
         output_f32_kernel<<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream>>>(
-            (const float*)q, (const float*)k, (const float*)v, St, W, out, BH, N, M, D, causal ? 1 : 0, heads);
+            (const float*)q, (const float*)k, (const float*)v, St, W, out, BH, N, M, D, causal ? 1 : 0, heads, lay);
         return hipGetLastError();
     }
     const uint16_t* qq = (const uint16_t*)q;
@@ -410,16 +429,16 @@ hipError_t launch_output(int dtype, const void* q, const void* k, const void* v,
         return hipGetLastError();
     }
     // Up to four tiles per wave, amortising the summary operand over 64 tokens.
-    const int64_t C = N / M;
+    const int64_t C = cmax;
     const int ntiles = (int)((C + 15) / 16);
     const int tpw = min(ntiles, 4);
     const int wpu = (ntiles + tpw - 1) / tpw;
     const dim3 grid((unsigned)((BH * M * wpu + 3) / 4));
 #define MHLA_LAUNCH_OUT(DD)                                                                        \
     if (nt)                                                                                        \
-        output_bf16_kernel<DD, true><<<grid, dim3(256), 0, stream>>>(qq, St, out, BH, (int)N, M, tpw, wpu, heads); \
+        output_bf16_kernel<DD, true><<<grid, dim3(256), 0, stream>>>(qq, St, out, BH, (int)N, M, tpw, wpu, heads, lay); \
     else                                                                                           \
-        output_bf16_kernel<DD, false><<<grid, dim3(256), 0, stream>>>(qq, St, out, BH, (int)N, M, tpw, wpu, heads)
+        output_bf16_kernel<DD, false><<<grid, dim3(256), 0, stream>>>(qq, St, out, BH, (int)N, M, tpw, wpu, heads, lay)
     switch (D) {
         case 16: MHLA_LAUNCH_OUT(16); break;
         case 32: MHLA_LAUNCH_OUT(32); break;

@@ -70,7 +70,7 @@ __device__ __forceinline__ uint32_t token_bits(const typename TokenWords<P>::typ
 template <int D, bool PIPE, bool NT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void summaries_bf16_kernel(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, float* __restrict__ S, int64_t BH, int N, int M,
-    int wpb, int nseg, int segC, int heads) {
+    int wpb, int nseg, int segC, int heads, BlockLayout lay) {
     constexpr int P = D / 16;
     constexpr int L = D * D + D;
     typedef typename TokenWords<P>::type TW;
@@ -86,7 +86,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
     const int wseg = nseg > 1 ? (int)(blockIdx.x % nseg) : 0;
     const int seg = wave % wpb;
     const bool active = unit < BH * M;
-    const int C = N / M;
 
     f32x4 acc[P][P];
 #pragma unroll
@@ -103,8 +102,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
     if (active) {
         pair = unit / M;
         blk = unit % M;
-        const int base = (int)blk * C + wseg * segC;            // this workgroup's token range
-        const int len = nseg > 1 ? min(segC, C - wseg * segC) : C;
+        int bstart, bend;  // the block's range in the token list
+        block_range(lay, blk, N, M, bstart, bend);
+        const int base = bstart + wseg * segC;  // this workgroup's token range
+        const int len = max(0, nseg > 1 ? min(segC, bend - bstart - wseg * segC) : bend - bstart);
         const int seg_len = ((len + wpb - 1) / wpb + 31) / 32 * 32;
         const int t_beg = base + seg * seg_len;
         const int t_end = min(base + len, t_beg + seg_len);
@@ -116,8 +117,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
         auto load = [&](TW (&kr)[8], TW (&vr)[8], int t) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int tok = t + 4 * e + g;
-                const uint32_t off = off_if(tok < t_end, ((uint32_t)tok * D + P * n) * 2);
+                const int tok = t + 4 * e + g;  // list entry; its row in the sequence:
+                const int row = token_row(lay, tok < t_end ? tok : 0, N);
+                const uint32_t off = off_if(tok < t_end && row >= 0, ((uint32_t)row * D + P * n) * 2);
                 kr[e] = load_token<P, NT>(rK, off);
                 vr[e] = load_token<P, NT>(rV, off);
             }
@@ -241,13 +243,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
 __global__ __launch_bounds__(256) void summaries_f32_kernel(const float* __restrict__ K,
                                                             const float* __restrict__ V,
                                                             float* __restrict__ S, int64_t BH, int64_t N,
-                                                            int64_t M, int D, int heads) {
+                                                            int64_t M, int D, int heads, BlockLayout lay) {
     const int64_t unit = blockIdx.x;  // pair * M + block
     const int64_t pair = unit / M, blk = unit % M;
-    const int64_t C = N / M;
+    int bstart, bend;
+    block_range(lay, blk, (int)N, M, bstart, bend);
     const int P = D / 16, L = D * D + D;
-    const float* Kp = K + (pair * N + blk * C) * D;
-    const float* Vp = V + (pair * N + blk * C) * D;
+    const float* Kp = K + pair * N * D;
+    const float* Vp = V + pair * N * D;
     float* out = S + (blk * BH + summary_row(pair, heads, BH)) * (int64_t)L;
     for (int e = threadIdx.x; e < L; e += blockDim.x) {
         float acc = 0.f;
@@ -255,10 +258,16 @@ __global__ __launch_bounds__(256) void summaries_f32_kernel(const float* __restr
             const int chunk = e / 256, rem = e % 256, ln = rem / 4, i = rem % 4;
             const int ia = chunk / P, ib = chunk % P;
             const int r = P * (4 * (ln / 16) + i) + ia, c = P * (ln % 16) + ib;
-            for (int64_t j = 0; j < C; ++j) acc = fmaf(phi_precise(Kp[j * D + r]), Vp[j * D + c], acc);
+            for (int j = bstart; j < bend; ++j) {
+                const int64_t row = token_row(lay, j, (int)N);
+                if (row >= 0) acc = fmaf(phi_precise(Kp[row * D + r]), Vp[row * D + c], acc);
+            }
         } else {
             const int r = e - D * D;
-            for (int64_t j = 0; j < C; ++j) acc += phi_precise(Kp[j * D + r]);
+            for (int j = bstart; j < bend; ++j) {
+                const int64_t row = token_row(lay, j, (int)N);
+                if (row >= 0) acc += phi_precise(Kp[row * D + r]);
+            }
         }
         out[e] = acc;
     }
@@ -283,8 +292,8 @@ struct SummarySplit {
 // Waves per block (1, 2, 4) and, for long blocks on few (batch, head) pairs, token
 // segments over several workgroups, so that about 1024 workgroups exist.  Every
 // wave keeps at least two 32-token steps; segments are multiples of 128 tokens.
-SummarySplit summary_split(int64_t BH, int64_t N, int64_t M) {
-    const int64_t units = BH * M, C = N / M;
+SummarySplit summary_split(int64_t BH, int64_t C, int64_t M) {
+    const int64_t units = BH * M;
     SummarySplit sp{1, 1, (int)C};
     while (sp.wpb < 4 && units * sp.wpb < 4096 && C >= 64 * (2 * sp.wpb)) sp.wpb *= 2;
     if (sp.wpb == 4 && units < 1024 && C >= 512) {
@@ -302,21 +311,22 @@ SummarySplit summary_split(int64_t BH, int64_t N, int64_t M) {
 
 }  // namespace
 
-size_t summary_partial_bytes(int dtype, int64_t BH, int64_t N, int D, int64_t M) {
+size_t summary_partial_bytes(int dtype, int64_t BH, int64_t C, int D, int64_t M) {
     if (dtype == kDtypeF32) return 0;
-    const SummarySplit sp = summary_split(BH, N, M);
+    const SummarySplit sp = summary_split(BH, C, M);
     return sp.nseg > 1 ? (size_t)sp.nseg * (size_t)(M * BH) * (size_t)(D * D + D) * sizeof(float) : 0;
 }
 
 hipError_t launch_summaries(int dtype, const void* k, const void* v, float* S, int64_t BH, int64_t N,
-                            int D, int64_t M, int heads, float* partial, hipStream_t stream) {
+                            int D, int64_t M, int heads, const BlockLayout& lay, int64_t cmax, float* partial,
+                            hipStream_t stream) {
     const int64_t units = BH * M;
     if (dtype == kDtypeF32) {
         summaries_f32_kernel<<<dim3((unsigned)units), dim3(256), 0, stream>>>(
-            (const float*)k, (const float*)v, S, BH, N, M, D, heads);
+            (const float*)k, (const float*)v, S, BH, N, M, D, heads, lay);
         return hipGetLastError();
     }
-    const SummarySplit sp = summary_split(BH, N, M);
+    const SummarySplit sp = summary_split(BH, cmax, M);
     if (sp.nseg > 1 && !partial) return hipErrorInvalidValue;
     const int per_wg = 4 / sp.wpb;
     const int64_t grid = sp.nseg > 1 ? units * sp.nseg : (units + per_wg - 1) / per_wg;
@@ -330,10 +340,10 @@ hipError_t launch_summaries(int dtype, const void* k, const void* v, float* S, i
     case DD:                                                                                                  \
         if (nt)                                                                                               \
             summaries_bf16_kernel<DD, PIPE, true><<<dim3((unsigned)grid), dim3(256), lds, stream>>>(          \
-                kk, vv, dst, BH, (int)N, (int)M, sp.wpb, sp.nseg, sp.segC, heads);                                   \
+                kk, vv, dst, BH, (int)N, (int)M, sp.wpb, sp.nseg, sp.segC, heads, lay);                                   \
         else                                                                                                  \
             summaries_bf16_kernel<DD, PIPE, false><<<dim3((unsigned)grid), dim3(256), lds, stream>>>(         \
-                kk, vv, dst, BH, (int)N, (int)M, sp.wpb, sp.nseg, sp.segC, heads);                                   \
+                kk, vv, dst, BH, (int)N, (int)M, sp.wpb, sp.nseg, sp.segC, heads, lay);                                   \
         break;
     switch (D) {
         MHLA_SUMMARIES_CASE(16, true)

@@ -97,6 +97,32 @@ def per_head_weights(w: Workload, seed=None):
     return np.stack([mixing_weights(rng.standard_normal((w.M, w.M)) * w.wscale, w.causal) for _ in range(w.H)])
 
 
+def grid_blocks(dims, tile):
+    """Blocks as token lists for a raster-ordered grid of `dims` (e.g. (h, w) or (t, h, w))
+    cut into tiles of `tile` (edge tiles are smaller when a side does not divide).
+    Returns order [N] int32 (tokens block by block, raster order inside a tile),
+    offsets [M + 1] int32 and blk [N] (each token's block)."""
+    dims, tile = tuple(dims), tuple(tile)
+    N = int(np.prod(dims))
+    coords = np.stack(np.unravel_index(np.arange(N), dims), axis=1)
+    ntile = [(a + b - 1) // b for a, b in zip(dims, tile)]
+    blk = np.ravel_multi_index(tuple((coords // np.array(tile)).T), ntile)
+    order = np.argsort(blk, kind="stable").astype(np.int32)
+    M = int(np.prod(ntile))
+    offsets = np.concatenate([[0], np.cumsum(np.bincount(blk, minlength=M))]).astype(np.int32)
+    return order, offsets, blk.astype(np.int32)
+
+
+def random_blocks(N, M, seed):
+    """An unequal partition of N tokens into M blocks (some possibly empty), each block's
+    tokens scattered over the sequence: order, offsets, blk as grid_blocks returns."""
+    rng = np.random.default_rng(seed)
+    blk = rng.integers(0, M, N)
+    order = np.argsort(blk, kind="stable").astype(np.int32)
+    offsets = np.concatenate([[0], np.cumsum(np.bincount(blk, minlength=M))]).astype(np.int32)
+    return order, offsets, blk.astype(np.int32)
+
+
 def make_inputs(w: Workload, seed=None):
     """q, k, v [B, H, N, d] float32 (bf16-exact for bf16 workloads) and W [M, M] float32."""
     if w.N % w.M:
