@@ -78,9 +78,9 @@ enum { MHLA_PATH_STAGED = 0, MHLA_PATH_FUSED = 1 };
  *     through a stream-ordered workspace of mhla_workspace_bytes() bytes taken
  *     from a library-owned memory pool on the current device and returned to it
  *     (stream-ordered) before the call returns;
- *   - fused (non-causal, M <= 16 blocks of at most 16 tokens): one workgroup
- *     per (batch, head) pair that keeps the block summaries and their mix in
- *     LDS; no workspace.
+ *   - fused (non-causal; M <= 16 blocks of at most 16 tokens, or N <= 256 in
+ *     blocks of 32, 48 or 64 tokens): one workgroup per (batch, head) pair that
+ *     keeps the block summaries and their mix in LDS; no workspace.
  * mhla_forward_path() reports which one a call with given sizes uses.
  */
 int mhla_forward(const void* q, const void* k, const void* v, const float* W, float* out,

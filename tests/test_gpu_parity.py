@@ -138,6 +138,10 @@ FUSED = [  # (B, H, N, d, M): shapes mhla_forward runs through the fused on-chip
     (256, 1, 16, 16, 16),   # d = 16, one token per block
     (16, 3, 256, 16, 16),   # d = 16, 16-token blocks
     (9, 2, 26, 16, 2),      # d = 16, 2 blocks of 13 tokens
+    (16, 3, 256, 64, 4),    # blocks of 64 tokens: 4 tiles each
+    (8, 2, 192, 32, 4),     # blocks of 48 tokens: 12 tiles, 3 per block
+    (16, 1, 128, 16, 2),    # 8 tiles, 4 per block
+    (4, 2, 256, 64, 8),     # blocks of 32 tokens
 ]
 
 

@@ -50,6 +50,7 @@ def round_bf16_bits(x):
 CASES = [  # (B, H, N, d, M, causal, dtype): one per kernel the options pass through
     (4, 2, 256, 64, 16, False, "bf16"),   # fused path
     (1, 2, 120, 32, 10, False, "bf16"),   # fused path, blocks of 12 tokens
+    (2, 2, 256, 64, 4, False, "bf16"),    # fused path over tiles: blocks of 64 tokens
     (2, 1, 1024, 32, 16, False, "bf16"),  # staged, non-causal output kernel
     (1, 2, 500, 64, 4, True, "bf16"),     # causal, one masked product per block
     (1, 2, 1536, 32, 3, True, "bf16"),    # causal, running-state output kernel (C = 512)
@@ -123,6 +124,7 @@ def test_unknown_option_rejected():
 
 PER_HEAD = [  # (B, H, N, d, M, causal, dtype): one per mixing kernel and output kernel
     (2, 3, 256, 64, 16, False, "bf16"),   # fused path
+    (4, 3, 256, 32, 4, False, "bf16"),    # fused path over 16-token tiles (blocks of 64 tokens)
     (2, 3, 2048, 32, 1, False, "bf16"),   # M = 1 (token segments in the summaries)
     (2, 2, 1024, 16, 32, True, "bf16"),   # M <= 64 mixing, causal masked products
     (1, 3, 1024, 32, 64, False, "bf16"),

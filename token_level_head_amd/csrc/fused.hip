@@ -32,6 +32,12 @@
 // descriptor, 32-bit offsets; an offset past the end reads zero).  Blocks M .. 15
 // run through the same steps on zero K/V (finite summaries) and carry zero mixing
 // weight.  LDS holds two batch slots (80 KiB), so two workgroups share a CU.
+//
+// Sequences of at most 256 tokens whose blocks are 2 to 4 whole 16-token tiles
+// (C = 32, 48, 64) run through the same kernel with the tiles as its blocks
+// (M = N / 16 here, T = C / 16 tiles per block) and tile weights W[i / T][b / T]:
+// a block's summary is the sum of its tiles' summaries, so the mix of tile i is
+// exactly S~ of its block.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -73,7 +79,7 @@ __global__ __launch_bounds__(64 * kWaves) void fused_small_kernel(const uint16_t
                                                           const uint16_t* __restrict__ K,
                                                           const uint16_t* __restrict__ V,
                                                           const float* __restrict__ W, OutSpec o,
-                                                          int N, int M, int heads) {
+                                                          int N, int M, int heads, int T) {
     constexpr int P = D / 16;
     constexpr int BPW = kBlocksPerWave;
     constexpr int SB = P > 1 ? 2 : 1;  // sub-tiles per batch (same column chunk)
@@ -97,7 +103,8 @@ __global__ __launch_bounds__(64 * kWaves) void fused_small_kernel(const uint16_t
     const rsrc_t rK = make_rsrc(K + pair * N * D, pair_bytes);
     const rsrc_t rV = make_rsrc(V + pair * N * D, pair_bytes);
     const rsrc_t rQ = make_rsrc(Q + pair * N * D, pair_bytes);
-    const rsrc_t rW = make_rsrc(pair_w(W, pair, heads, M), (uint32_t)M * M * 4);
+    const int MW = M / T;  // blocks of W (M counts 16-token tiles when T > 1)
+    const rsrc_t rW = make_rsrc(pair_w(W, pair, heads, MW), (uint32_t)MW * MW * 4);
     u32x2 kw[BPW][4], vw[BPW][4];
     u32x4 qw[BPW][P == 4 ? 2 : 1];
 #pragma unroll
@@ -122,7 +129,7 @@ __global__ __launch_bounds__(64 * kWaves) void fused_small_kernel(const uint16_t
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int b = 4 * g + e;
-        wv[e] = __uint_as_float(buf_load32(rW, off_if(n < M && b < M, (uint32_t)(n * M + b) * 4)));
+        wv[e] = __uint_as_float(buf_load32(rW, off_if(n < M && b < M, (uint32_t)((n / T) * MW + b / T) * 4)));
     }
     auto load_q = [&]() {
 #pragma unroll
@@ -328,13 +335,22 @@ bool fused_applicable(int D, int64_t BH, int64_t N, int64_t M) {
     (void)D;
     (void)BH;
     // Blocks of at most 16 tokens (one 16-deep k-step and one query tile per
-    // block) and at most 16 blocks (one 16-row tile of W).
-    return M <= kMaxBlocks && N / M <= 16;
+    // block) and at most 16 blocks (one 16-row tile of W); or at most 256 tokens in
+    // blocks of 2 to 4 whole 16-token tiles, run as tiles: a block's summary is the
+    // sum of its tiles' summaries, so mixing the tiles with W[block(i), block(b)]
+    // gives every tile of block i exactly S~_i.  Longer blocks stay on the staged
+    // path, whose summaries are then small next to the tokens (one block of 256
+    // tokens: 12% faster staged than fused, measured).
+    const int64_t C = N / M;
+    return (M <= kMaxBlocks && C <= 16) || (N <= 16 * kMaxBlocks && C % 16 == 0 && C <= 64);
 }
 
 hipError_t launch_fused(const void* q, const void* k, const void* v, const float* W, const OutSpec& out,
                         int64_t BH, int64_t N, int D, int64_t M, int heads, hipStream_t stream) {
-    const bool full = N / M == 16;
+    const int64_t C = N / M;
+    const int T = C > 16 ? (int)(C / 16) : 1;  // 16-token tiles per block
+    const bool full = C >= 16;
+    M = M * T;
     const uint16_t* qq = (const uint16_t*)q;
     const uint16_t* kk = (const uint16_t*)k;
     const uint16_t* vv = (const uint16_t*)v;
@@ -342,9 +358,9 @@ hipError_t launch_fused(const void* q, const void* k, const void* v, const float
 #define MHLA_FUSED_CASE(DD)                                                                              \
     case DD:                                                                                             \
         if (full)                                                                                        \
-            fused_small_kernel<DD, true><<<grid, block, 0, stream>>>(qq, kk, vv, W, out, (int)N, (int)M, heads);  \
+            fused_small_kernel<DD, true><<<grid, block, 0, stream>>>(qq, kk, vv, W, out, (int)N, (int)M, heads, T);  \
         else                                                                                             \
-            fused_small_kernel<DD, false><<<grid, block, 0, stream>>>(qq, kk, vv, W, out, (int)N, (int)M, heads); \
+            fused_small_kernel<DD, false><<<grid, block, 0, stream>>>(qq, kk, vv, W, out, (int)N, (int)M, heads, T); \
         break;
     switch (D) {
         MHLA_FUSED_CASE(16)
