@@ -150,6 +150,16 @@ __device__ __forceinline__ int token_row(const BlockLayout& lay, int i, int N) {
     return (unsigned)r < (unsigned)N ? r : -1;
 }
 
+// Workgroup barrier ordering LDS accesses only.  __syncthreads() is a fence over all
+// memory, which on gfx9 waits for every outstanding global load and store of the wave
+// (vmcnt(0)) before the barrier; with fences scoped to LDS ("local"), only the wave's
+// LDS operations are awaited, and prefetched loads and output stores stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 // Masked load without a branch: the address falls back to `safe` (any valid,

@@ -376,6 +376,156 @@ __global__ __launch_bounds__(512) void mix_wide_kernel(const float* __restrict__
 
 // Small M (<= 64): the workgroup splits its rows of W into MFMA fragments in LDS
 // itself (at most 16 KiB), which costs less than a separate launch.
+// 64 < M <= 256, persistent: one workgroup of eight waves per CU walks the 16-column
+// tiles blockIdx.x, blockIdx.x + gridDim.x, ...  Wave w owns rows 32w .. 32w + 31 and
+// keeps its rows of W resident in registers as bf16 hi + lo MFMA operands (128
+// VGPRs), split once.  Each tile of S (M x 16 floats) is loaded into registers two
+// tiles ahead of its use, split into hi + lo and written to LDS transposed to
+// [column][block] (double-buffered, one barrier per tile), so that loads, MFMAs and
+// stores of different tiles overlap.  The MFMA takes the S tile as its A operand and
+// W as its B operand, so each lane ends with 4 consecutive columns of one output row
+// and writes them with one 16-byte store.
+constexpr int kStreamRS = 256 + 8;  // bf16 per LDS column (M <= 256 blocks, padded)
+constexpr int kStreamKC = 8;        // 32-deep k-chunks for M <= 256
+
+template <bool CAUSAL, bool FULL>  // FULL: M == 256, non-causal (every wave: 32 rows, 8 k-chunks)
+__global__ __launch_bounds__(512) void mix_stream_kernel(const float* __restrict__ S, const float* __restrict__ W,
+                                                         float* __restrict__ St, int64_t ncols, int64_t ld, int M,
+                                                         int64_t ntiles) {
+    // Grid row y: one head's contiguous column block (head-major summaries) and its W.
+    S += (int64_t)blockIdx.y * ncols;
+    St += (int64_t)blockIdx.y * ncols;
+    W += (int64_t)blockIdx.y * M * M;
+    __shared__ __align__(16) uint32_t tile[2][2][16 * kStreamRS / 2];  // [buffer][hi, lo][column][block pair]
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4, n = lane & 15;
+    // Wave w owns rows 32((w + blockIdx.x) mod 8) ..: neighbouring workgroups read
+    // different rows of W at any moment instead of all the same L2 lines.
+    const int i0 = 32 * ((wave + (int)blockIdx.x) & 7);
+    const int rows = FULL ? 32 : max(0, min(32, M - i0));
+    const int nrt = FULL ? 2 : (rows + 15) / 16;
+    const int kend = CAUSAL ? min(M, i0 + rows - 1) : M;  // causal rows use b < i <= i0 + rows - 1
+    const int kcn = FULL ? kStreamKC : max(0, (kend + 31) / 32);
+
+    bf16x8 wh[2][kStreamKC], wl[2][kStreamKC];  // this wave's rows of W (B operands), filled below
+
+    // Tile loads: thread -> blocks 2bp, 2bp + 1 (bp < 128) and columns 4cg .. 4cg + 3.
+    const int bp = threadIdx.x >> 2, cg = threadIdx.x & 3;
+    const int64_t my_tiles = ntiles > blockIdx.x ? (ntiles - 1 - blockIdx.x) / gridDim.x + 1 : 0;
+    // S through a buffer descriptor (the caller guarantees M * ld * 4 < 2^32): 32-bit
+    // offsets, an offset past the end reads zero, and the loads stay where they are
+    // written, two tiles ahead of their use.
+    const rsrc_t rS = make_rsrc(S, (uint32_t)((int64_t)M * ld * 4));
+    const uint32_t soff0 = (uint32_t)(((int64_t)(2 * bp) * ld + 4 * cg) * 4);
+    auto load_tile = [&](int64_t j, f32x4 (&x)[2]) {
+        const uint32_t col = (uint32_t)((blockIdx.x + j * gridDim.x) * 16);
+        const bool ok = j < my_tiles;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const bool okh = ok && 2 * bp + h < M;
+            x[h] = __builtin_bit_cast(f32x4, buf_load128(rS, off_if(okh, soff0 + (uint32_t)(h * ld + col) * 4)));
+        }
+    };
+    auto store_lds = [&](int buf, const f32x4 (&x)[2]) {
+#pragma unroll
+        for (int xx = 0; xx < 4; ++xx) {
+            uint32_t hi, lo;
+            split2_bf16(x[0][xx], x[1][xx], hi, lo);
+            tile[buf][0][((4 * cg + xx) * kStreamRS) / 2 + bp] = hi;
+            tile[buf][1][((4 * cg + xx) * kStreamRS) / 2 + bp] = lo;
+        }
+    };
+    // One tile: products from LDS buffer buf, 16-byte stores, then tile j + 1 (registers
+    // xn) into the other buffer, whose last readers passed the previous barrier, and the
+    // loads of tile j + 3 into the registers xf just freed.
+    auto step = [&](int64_t j, int buf, const f32x4 (&xn)[2], f32x4 (&xf)[2]) {
+        f32x4 acc[2] = {zero4(), zero4()};
+        const uint32_t* th = &tile[buf][0][(n * kStreamRS) / 2];
+        const uint32_t* tl = &tile[buf][1][(n * kStreamRS) / 2];
+#pragma unroll
+        for (int kc = 0; kc < kStreamKC; ++kc) {
+            if (kc < kcn) {  // uniform
+                const bf16x8 ah = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(th + 16 * kc + 4 * g));
+                const bf16x8 al = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(tl + 16 * kc + 4 * g));
+#pragma unroll
+                for (int r = 0; r < 2; ++r) {
+                    if (r < nrt) {  // uniform
+                        acc[r] = mfma32(ah, wh[r][kc], acc[r]);
+                        acc[r] = mfma32(al, wh[r][kc], acc[r]);
+                        acc[r] = mfma32(ah, wl[r][kc], acc[r]);
+                    }
+                }
+            }
+        }
+        const int64_t col0 = (blockIdx.x + j * gridDim.x) * 16;
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {  // lane (g, n): row i0 + 16r + n, columns 4g .. 4g + 3
+            const int row = 16 * r + n;
+            if (row < rows) *reinterpret_cast<f32x4*>(St + (int64_t)(i0 + row) * ld + col0 + 4 * g) = acc[r];
+        }
+        store_lds(buf ^ 1, xn);
+        load_tile(j + 3, xf);
+        lds_barrier();
+    };
+
+    f32x4 p0[2], p1[2], p2[2];  // ring of three tiles in flight
+    load_tile(0, p0);  // (the first tile loads while W is read from L2)
+    // W rows of this wave, split once: B operand of k-chunk kc, row tile r:
+    // lane (g, n) holds W[i0 + 16r + n][32kc + 8g + e], e < 8 (zero past M; causal b < i).
+    // W (at most 256 KiB) is read through a buffer descriptor: 32-bit offsets, and an
+    // offset past the end reads zero.
+    const rsrc_t rW = make_rsrc(W, (uint32_t)M * M * 4);
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {  // one row tile at a time: all its loads, then the splits
+        const int i = i0 + 16 * r + n;
+        f32x4 x[kStreamKC][2];
+#pragma unroll
+        for (int kc = 0; kc < kStreamKC; ++kc)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int b = 32 * kc + 8 * g + 4 * h;
+                if constexpr (FULL) {  // M = 256: rows 16-byte aligned, 16-byte loads
+                    x[kc][h] = __builtin_bit_cast(f32x4, buf_load128(rW, (uint32_t)(i * M + b) * 4));
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        x[kc][h][e] = __uint_as_float(buf_load32(rW, off_if(i < M && b + e < M, (uint32_t)(i * M + b + e) * 4)));
+                }
+            }
+        issue_fence();
+#pragma unroll
+        for (int kc = 0; kc < kStreamKC; ++kc) {
+            uint32_t hw[4], lw[4];
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                const int b = 32 * kc + 8 * g + 2 * e2;
+                float x0 = x[kc][e2 / 2][(2 * e2) % 4], x1 = x[kc][e2 / 2][(2 * e2 + 1) % 4];
+                if constexpr (CAUSAL) {
+                    x0 = b < i ? x0 : 0.f;
+                    x1 = b + 1 < i ? x1 : 0.f;
+                }
+                split2_bf16(x0, x1, hw[e2], lw[e2]);
+            }
+            wh[r][kc] = __builtin_bit_cast(bf16x8, u32x4{hw[0], hw[1], hw[2], hw[3]});
+            wl[r][kc] = __builtin_bit_cast(bf16x8, u32x4{lw[0], lw[1], lw[2], lw[3]});
+        }
+    }
+
+    load_tile(1, p1);
+    load_tile(2, p2);
+    store_lds(0, p0);
+    lds_barrier();
+    for (int64_t j = 0; j < my_tiles; j += 3) {  // unrolled by the ring length (uniform exits);
+        step(j, (int)(j & 1), p1, p0);           // tile j sits in LDS buffer j & 1
+        if (j + 1 >= my_tiles) break;
+        step(j + 1, (int)((j + 1) & 1), p2, p1);
+        if (j + 2 >= my_tiles) break;
+        step(j + 2, (int)((j + 2) & 1), p0, p2);
+    }
+}
+
 template <int KSTEP, int RT, int J, bool PIPE, bool CAUSAL>
 __global__ __launch_bounds__(256) void mix_lds_kernel(const float* __restrict__ S, const float* __restrict__ W,
                                                       float* __restrict__ St, int64_t ncols, int64_t ld, int M,
@@ -666,7 +816,25 @@ hipError_t launch_mix(const float* S, const float* W, float* St, int64_t BH, int
             run(I32{}, I4{}, I4{});
         return hipGetLastError();
     }
-    if (M <= 256) {  // 64 < M <= 256: wide strips, W split per wave
+    if (M <= 256 && M * ld * 4 < (int64_t(1) << 32) - 64) {  // 64 < M <= 256: persistent tile walk
+        const int64_t ntiles = ncols / 16;  // d*d + d is a multiple of 16
+        static int cus = 0;
+        if (!cus) {
+            int dev = 0;
+            if (hipGetDevice(&dev) != hipSuccess ||
+                hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+                cus = 256;
+        }
+        const dim3 grid((unsigned)std::max<int64_t>(1, std::min<int64_t>(ntiles, cus)), gy);
+        if (causal)
+            mix_stream_kernel<true, false><<<grid, dim3(512), 0, stream>>>(S, W, St, ncols, ld, (int)M, ntiles);
+        else if (M == 256)
+            mix_stream_kernel<false, true><<<grid, dim3(512), 0, stream>>>(S, W, St, ncols, ld, (int)M, ntiles);
+        else
+            mix_stream_kernel<false, false><<<grid, dim3(512), 0, stream>>>(S, W, St, ncols, ld, (int)M, ntiles);
+        return hipGetLastError();
+    }
+    if (M <= 256) {  // 64 < M <= 256 with S of 4 GiB or more: wide strips, W split per wave
         const int KC = (int)((M + 31) / 32);
         const int64_t tiles16 = (ncols + 15) / 16;
         // strips of NT column tiles: one strip per CU when that takes at most kWideMaxNT tiles
