@@ -142,6 +142,8 @@ FUSED = [  # (B, H, N, d, M): shapes mhla_forward runs through the fused on-chip
     (8, 2, 192, 32, 4),     # blocks of 48 tokens: 12 tiles, 3 per block
     (16, 1, 128, 16, 2),    # 8 tiles, 4 per block
     (4, 2, 256, 64, 8),     # blocks of 32 tokens
+    (100, 3, 256, 32, 16),  # 300 pairs: some split into column halves over two workgroups
+    (70, 5, 160, 64, 16),   # 350 pairs, 10-token blocks, column halves
 ]
 
 

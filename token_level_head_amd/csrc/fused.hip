@@ -32,6 +32,10 @@
 // descriptor, 32-bit offsets; an offset past the end reads zero).  Blocks M .. 15
 // run through the same steps on zero K/V (finite summaries) and carry zero mixing
 // weight.  LDS holds two batch slots (80 KiB), so two workgroups share a CU.
+// With between one and two pairs per CU (DiT-S/2: 384 pairs on 256 CUs) the CUs
+// holding two whole pairs would set the time, so 2 * CUs - B*H pairs are split into
+// column halves run by two workgroups (each recomputes phi and z for its half), and
+// every CU gets one whole pair and one half (measured: 24.3 -> 22.2 us).
 //
 // Sequences of at most 256 tokens whose blocks are 2 to 4 whole 16-token tiles
 // (C = 32, 48, 64) run through the same kernel with the tiles as its blocks
@@ -74,17 +78,21 @@ __device__ __forceinline__ bf16x4 as_bf16x4(uint32_t lo_pair, uint32_t hi_pair) 
 
 }  // namespace
 
-template <int D, bool FULL>
-__global__ __launch_bounds__(64 * kWaves) void fused_small_kernel(const uint16_t* __restrict__ Q,
-                                                          const uint16_t* __restrict__ K,
-                                                          const uint16_t* __restrict__ V,
-                                                          const float* __restrict__ W, OutSpec o,
-                                                          int N, int M, int heads, int T) {
+// One (batch, head) pair, value columns of column chunks [C0, C1) (HC = 0: all P
+// chunks; 1 and 2: the first and second half, for pairs split over two workgroups).
+// `lds` holds SB batch slots.
+template <int D, bool FULL, int HC>
+__device__ __forceinline__ void fused_pair(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                                           const uint16_t* __restrict__ V, const float* __restrict__ W,
+                                           const OutSpec& o, int N, int M, int heads, int T, float* lds,
+                                           int64_t pair) {
     constexpr int P = D / 16;
     constexpr int BPW = kBlocksPerWave;
     constexpr int SB = P > 1 ? 2 : 1;  // sub-tiles per batch (same column chunk)
     constexpr int NB = P * P / SB;     // batches
-    __shared__ __align__(16) float lds[SB * kSlotWords];
+    static_assert(HC == 0 || P >= 2, "column halves need at least two column chunks");
+    constexpr int BT0 = HC == 2 ? NB / 2 : 0, BT1 = HC == 1 ? NB / 2 : NB;  // this workgroup's batches
+    constexpr int C0 = BT0 * SB / P;                                         // its first column chunk
     float* const A = lds;                                                   // [SB][16 blocks][16 columns][kRSA]
     uint2* const Bhi = reinterpret_cast<uint2*>(lds + SB * kSlotS);        // [SB][hi, lo][16 query blocks][kBSB / 2]
     float* const Az = lds + SB * (kSlotS + kSlotSt);                       // [SB][16 blocks][kBZA]
@@ -93,7 +101,6 @@ __global__ __launch_bounds__(64 * kWaves) void fused_small_kernel(const uint16_t
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, n = lane & 15;
-    const int64_t pair = blockIdx.x;
     const int C = FULL ? 16 : N / M;  // tokens per block, <= 16
 
     // ---- loads: K and V (lane: P features / columns of tokens 4g .. 4g+3), W (lane:
@@ -245,7 +252,7 @@ __global__ __launch_bounds__(64 * kWaves) void fused_small_kernel(const uint16_t
     };
 
 #pragma unroll
-    for (int bt = 0; bt < NB; ++bt) {
+    for (int bt = BT0; bt < BT1; ++bt) {
         // 1. sub-tile (ia, c) of S_b: lane (g, n) gets S_b[P (4g + r) + ia][16 c + n], r = 0..3
 #pragma unroll
         for (int u = 0; u < SB; ++u) {
@@ -256,7 +263,7 @@ __global__ __launch_bounds__(64 * kWaves) void fused_small_kernel(const uint16_t
             for (int j = 0; j < BPW; ++j) {
                 const int b = wave + kWaves * j;
                 *reinterpret_cast<f32x4*>(a_wr + b * kBSA) = mfma16(ak[j][ia], vb[j][c], zero4());
-                if (c == 0) {
+                if (c == C0) {
                     const f32x4 za = mfma16(ak[j][ia], ones, zero4());
                     if (n == 0) *reinterpret_cast<f32x4*>(z_wr + b * kBZA) = za;
                 }
@@ -277,7 +284,7 @@ __global__ __launch_bounds__(64 * kWaves) void fused_small_kernel(const uint16_t
                 const int t = wave + kWaves * j;
                 mix_tile(a_rd + t * kRSA, kBSA, bhi + t, blo + t);
             }
-            if (c == 0 && wave == (ia + 4 * u) % kWaves) {
+            if (c == C0 && wave == (ia + 4 * u) % kWaves) {
                 uint2* const zhi = Zhi + u * (kSlotZt / 2) + n * (kBZB / 2) + g;
                 mix_tile(Az + u * kSlotZ + 4 * g * kBZA + n, kBZA, zhi, zhi + kMaxBlocks * kBZB / 2);
             }
@@ -285,7 +292,7 @@ __global__ __launch_bounds__(64 * kWaves) void fused_small_kernel(const uint16_t
         __syncthreads();
 
         // 3. output: D[column 16 c + 4g + r][token n] += sum_m S~_i[P m + ia][.] phi(q_n)[P m + ia]
-        if (bt == 0) make_bq();
+        if (bt == BT0) make_bq();
 #pragma unroll
         for (int u = 0; u < SB; ++u) {
             const int s = bt * SB + u, c = s / P, ia = s % P;
@@ -300,7 +307,7 @@ __global__ __launch_bounds__(64 * kWaves) void fused_small_kernel(const uint16_t
                 const uint2 sl = blo[b * (kBSB / 2) + g * 16 + n];
                 oacc[j] = mfma16(as_bf16x4(sh.x, sh.y), bq[j][ia], ia == 0 ? zero4() : oacc[j]);
                 oacc[j] = mfma16(as_bf16x4(sl.x, sl.y), bq[j][ia], oacc[j]);
-                if (c == 0) {
+                if (c == C0) {
                     const uint2 zh = zhi[b * (kBZB / 2) + g];
                     const uint2 zl = zlo[b * (kBZB / 2) + g];
                     dacc[j] = mfma16(as_bf16x4(zh.x, zh.y), bq[j][ia], ia == 0 ? zero4() : dacc[j]);
@@ -313,7 +320,7 @@ __global__ __launch_bounds__(64 * kWaves) void fused_small_kernel(const uint16_t
             // Column chunk c is complete after its last feature group (the denominator
             // after chunk 0): write it now, so the stores overlap the remaining chunks.
             if (ia == P - 1) {
-                if (c == 0) {
+                if (c == C0) {
 #pragma unroll
                     for (int j = 0; j < BPW; ++j) rden[j] = out_scale(o, dacc[j][0] + kEps);
                 }
@@ -328,6 +335,32 @@ __global__ __launch_bounds__(64 * kWaves) void fused_small_kernel(const uint16_t
                 }
             }
         }
+    }
+}
+
+// Workgroups [0, nfull) each run the whole pair of their index; the rest run the
+// remaining pairs in column halves, two workgroups per pair (dispatched after all
+// the whole pairs, so that a CU holding two workgroups gets a whole pair and a half).
+template <int D, bool FULL>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4))) void fused_small_kernel(
+                                                          const uint16_t* __restrict__ Q,
+                                                          const uint16_t* __restrict__ K,
+                                                          const uint16_t* __restrict__ V,
+                                                          const float* __restrict__ W, OutSpec o,
+                                                          int N, int M, int heads, int T, int nfull) {
+    constexpr int P = D / 16;
+    constexpr int SB = P > 1 ? 2 : 1;
+    __shared__ __align__(16) float lds[SB * kSlotWords];
+    const int w = blockIdx.x;
+    if (w < nfull) {
+        fused_pair<D, FULL, 0>(Q, K, V, W, o, N, M, heads, T, lds, w);
+    } else if constexpr (P >= 2) {
+        const int u = w - nfull;
+        const int64_t pair = nfull + u / 2;
+        if (u & 1)
+            fused_pair<D, FULL, 2>(Q, K, V, W, o, N, M, heads, T, lds, pair);
+        else
+            fused_pair<D, FULL, 1>(Q, K, V, W, o, N, M, heads, T, lds, pair);
     }
 }
 
@@ -354,13 +387,25 @@ hipError_t launch_fused(const void* q, const void* k, const void* v, const float
     const uint16_t* qq = (const uint16_t*)q;
     const uint16_t* kk = (const uint16_t*)k;
     const uint16_t* vv = (const uint16_t*)v;
-    const dim3 grid((unsigned)BH), block(64 * kWaves);
+    // Between one and two pairs per CU, the CUs holding two whole pairs would set the
+    // time: split 2 * CUs - BH pairs into column halves, so that every CU gets a whole
+    // pair and a half (d >= 32; d = 16 has a single column chunk).
+    static int cus = 0;
+    if (!cus) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+            cus = 256;
+    }
+    const int64_t nhalf = (D >= 32 && BH > cus && BH < 2 * (int64_t)cus) ? 2 * cus - BH : 0;
+    const int nfull = (int)(BH - nhalf);
+    const dim3 grid((unsigned)(nfull + 2 * nhalf)), block(64 * kWaves);
 #define MHLA_FUSED_CASE(DD)                                                                              \
     case DD:                                                                                             \
         if (full)                                                                                        \
-            fused_small_kernel<DD, true><<<grid, block, 0, stream>>>(qq, kk, vv, W, out, (int)N, (int)M, heads, T);  \
+            fused_small_kernel<DD, true><<<grid, block, 0, stream>>>(qq, kk, vv, W, out, (int)N, (int)M, heads, T, nfull);  \
         else                                                                                             \
-            fused_small_kernel<DD, false><<<grid, block, 0, stream>>>(qq, kk, vv, W, out, (int)N, (int)M, heads, T); \
+            fused_small_kernel<DD, false><<<grid, block, 0, stream>>>(qq, kk, vv, W, out, (int)N, (int)M, heads, T, nfull); \
         break;
     switch (D) {
         MHLA_FUSED_CASE(16)
