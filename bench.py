@@ -25,6 +25,7 @@ import token_level_head_amd as mh
 from token_level_head_amd.workloads import WORKLOADS, make_inputs
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 METRIC = "MHLA fwd tokens/s and TFLOP/s at 1 MI355X; % of HBM/MFMA roofline"
 
 
@@ -38,6 +39,15 @@ def model_flops(w):
     if w.causal:
         per_pair += N * (2 * d * (C + 1) + (C + 1) / 2)  # within-block prefix (average over positions)
     return BH * per_pair
+
+
+def mix_flops(w):
+    """(model, executed) FLOPs of the mixing GEMM: 2 * nnz(W) * (d*d + d) per pair, and the
+    bf16 MFMA work that carries it out (three hi/lo products per term)."""
+    BH, d, M = w.B * w.H, w.d, w.M
+    nnz = M * (M - 1) // 2 if w.causal else M * M
+    model = 2 * nnz * (d * d + d) * BH
+    return model, (3 * model if w.dtype == "bf16" else model)
 
 
 def kernel_bytes(w):
@@ -343,6 +353,14 @@ def main():
                 "hbm_frac": round(kb[name] / (t_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
     staged = {n: entry(n, kms[n]) for n in names}
+    # The mixing GEMM also against the MFMA roofline: model FLOPs, and the bf16 MFMA work
+    # executed (hi/lo products) as a fraction of the dense bf16 peak.
+    mf_model, mf_exec = mix_flops(w)
+    t_mix = kms["mix"] * 1e-3
+    staged["mix"]["model_TFLOPs"] = round(mf_model / t_mix / 1e12, 2)
+    if w.dtype == "bf16":
+        staged["mix"]["mfma_TFLOPs"] = round(mf_exec / t_mix / 1e12, 2)
+        staged["mix"]["mfma_frac"] = round(mf_exec / t_mix / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
     if path == mh.MHLA_PATH_FUSED:
         # the step is the fused kernel alone: its duration is the step's
         kms["fused"] = ms

@@ -4,6 +4,10 @@
     python -m token_level_head_amd.rocprof_summary trace RUN_results.db --cmd "<rocprofv3 command>" \
         --workload dit_s2_256 > profiles/kernels_dit_s2_256.md
 
+    # any counters of one --pmc run (e.g. the MFMA and SQ counters of the mixing kernel)
+    python -m token_level_head_amd.rocprof_summary pmc RUN_results.db --workload dit_s2_4096 \
+        --cmd "<command>" --kernel mix_ --out profiles/mfma_dit_s2_4096.json
+
     # HBM traffic (from one --pmc FETCH_SIZE run and one --pmc WRITE_SIZE run)
     python -m token_level_head_amd.rocprof_summary counters FETCH_results.db WRITE_results.db \
         --workload dit_s2_256 --cmd-fetch "<command>" --cmd-write "<command>" \
@@ -86,6 +90,28 @@ def cmd_counters(args):
     print(json.dumps(out, indent=1))
 
 
+def cmd_pmc(args):
+    c = sqlite3.connect(args.db)
+    rows = c.execute("select kernel_name, counter_name, avg(value), count(*) from counters_collection "
+                     "group by kernel_name, counter_name").fetchall()
+    kernels = {}
+    for name, counter, avg, n in rows:
+        if "mhla::" not in name or args.kernel not in name:
+            continue
+        k = kernels.setdefault(short_name(name), {"dispatches": n, "source_digest": kernel_source_digest(short_name(name))})
+        k[counter] = avg
+    for k in kernels.values():
+        # SQ_VALU_MFMA_BUSY_CYCLES sums MFMA-busy cycles over all SIMDs; with the SQ busy
+        # cycles (summed over the shader engines) it gives the MFMA-busy share of the SIMDs.
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in k and "SQ_BUSY_CYCLES" in k and args.simds_per_se:
+            k["mfma_busy_frac"] = k["SQ_VALU_MFMA_BUSY_CYCLES"] / (k["SQ_BUSY_CYCLES"] * args.simds_per_se)
+    out = {"workload": args.workload, "source_digest": source_digest(), "command": args.cmd, "kernels": kernels}
+    with open(args.out, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -100,8 +126,15 @@ def main(argv=None):
     c.add_argument("--cmd-fetch", required=True)
     c.add_argument("--cmd-write", required=True)
     c.add_argument("--out", required=True)
+    m = sub.add_parser("pmc")
+    m.add_argument("db")
+    m.add_argument("--workload", required=True)
+    m.add_argument("--cmd", required=True)
+    m.add_argument("--kernel", default="", help="substring of the kernel names to keep")
+    m.add_argument("--simds-per-se", type=int, default=32, help="SIMDs per shader engine (MI355X: 8 CUs x 4)")
+    m.add_argument("--out", required=True)
     args = ap.parse_args(argv)
-    {"trace": cmd_trace, "counters": cmd_counters}[args.what](args)
+    {"trace": cmd_trace, "counters": cmd_counters, "pmc": cmd_pmc}[args.what](args)
 
 
 if __name__ == "__main__":
