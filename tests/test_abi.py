@@ -36,7 +36,7 @@ def test_version_and_sizes(mhla_lib):
     assert mh.mhla_version().startswith("mhla-gfx950")
     for d in (16, 32, 64):
         assert mh.mhla_summary_floats(d) == d * d + d
-    # two summary arrays, plus the split-W fragments (4 * M * M bytes) when 64 < M <= 1024
+    # two summary arrays, plus the split-W fragments (4 * M * M bytes) when 256 < M <= 1024
     assert mh.mhla_workspace_bytes(64, 6, 256, 64, 16) == 2 * 16 * 384 * (64 * 64 + 64) * 4
     assert mh.mhla_workspace_bytes(8, 16, 8192, 64, 64, 1) == 2 * 64 * 128 * (64 * 64 + 64) * 4
     assert mh.mhla_workspace_bytes(1, 6, 65536, 64, 256) == 2 * 256 * 6 * (64 * 64 + 64) * 4
@@ -50,6 +50,41 @@ def test_version_and_sizes(mhla_lib):
 
 
 FAKE = 1 << 20  # a 16-byte-aligned nonzero address; never dereferenced (validation fails first)
+
+
+def test_forward_ex_validation(mhla_lib):
+    p = [FAKE, FAKE * 2, FAKE * 3]
+
+    def call(dtype=0, opts=0, W=FAKE * 4, out=FAKE * 5, B=1, H=1, N=256, d=16, M=4):
+        return mhla_lib.mhla_forward_ex(*p, dtype, W, out, B, H, N, d, M, opts, None)
+
+    assert call(opts=1 << 7) == mh.MHLA_ERR_INVALID_ARG
+    assert "option" in mh.mhla_last_error()
+    assert call(dtype=5) == mh.MHLA_ERR_INVALID_ARG
+    assert call(N=250) == mh.MHLA_ERR_INVALID_ARG
+    # a float32 output of B*H*N*d*4 bytes reaches W placed half-way along it
+    assert call(W=FAKE * 5 + 256 * 16 * 2, out=FAKE * 5) == mh.MHLA_ERR_INVALID_ARG
+    assert "overlap" in mh.mhla_last_error()
+    # per-head W spans H * M * M floats: an output right after the first head's matrix overlaps
+    assert call(W=FAKE * 5, out=FAKE * 5 + 4 * 4 * 4, H=2, opts=mh.MHLA_OPT_W_PER_HEAD) == mh.MHLA_ERR_INVALID_ARG
+
+
+def test_forward_blocks_validation(mhla_lib):
+    p = [FAKE, FAKE * 2, FAKE * 3]
+    order, offsets = FAKE * 6, FAKE * 7
+
+    def call(order=order, offsets=offsets, max_block=64, opts=0, N=250, M=4):
+        return mhla_lib.mhla_forward_blocks(*p, 0, FAKE * 4, FAKE * 5, 1, 1, N, 16, M, order, offsets,
+                                            max_block, opts, None)
+
+    assert call(order=None) == mh.MHLA_ERR_INVALID_ARG
+    assert call(offsets=None) == mh.MHLA_ERR_INVALID_ARG
+    assert call(order=FAKE * 6 + 2) == mh.MHLA_ERR_INVALID_ARG
+    assert "aligned" in mh.mhla_last_error()
+    assert call(max_block=0) == mh.MHLA_ERR_INVALID_ARG
+    assert call(max_block=251) == mh.MHLA_ERR_INVALID_ARG
+    assert call(opts=mh.MHLA_OPT_CAUSAL) == mh.MHLA_ERR_UNSUPPORTED
+    assert call(opts=1 << 9) == mh.MHLA_ERR_INVALID_ARG
 
 
 @pytest.mark.parametrize("fn", ["mhla_forward", "mhla_forward_f32"])
