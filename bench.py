@@ -3,6 +3,8 @@
 
     python bench.py [--steps K] [--warmup W] [--workload dit_s2_256] [--gpus 1]
     python bench.py --sweep          # N x M throughput grid (the paper's scaling study)
+    python bench.py --decode         # streaming causal decode step (lm_causal_8k shape)
+    python bench.py --backward       # backward pass (dq, dk, dv, dW) on the workload
 
 One step is one full forward pass (phi, block summaries, mixing, output) over
 the workload's synthetic batch, with inputs resident in HBM before the timed
@@ -175,6 +177,62 @@ def decode_bench(args, w):
     return 0
 
 
+def backward_bench(args, w):
+    """The backward pass (dq, dk, dv, dW of sum(dy * Y)) on the workload's batch: K calls
+    timed between HIP events (faster of one HIP-graph replay and eager launches).  Bytes
+    per call counted as q, k, v, dy read once and dq, dk, dv written once (float32
+    arithmetic; the kernels recompute the summaries and read the inputs more than once)."""
+    q, k, v, W = make_inputs(w)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    qd, kd, vd = (torch.from_numpy(a).to("cuda", dt) for a in (q, k, v))
+    Wd = torch.from_numpy(W).cuda()
+    gen = torch.Generator(device="cuda").manual_seed(w.seed + 1)
+    dy = torch.randn(q.shape, generator=gen, device="cuda", dtype=torch.float32)
+    dq, dk, dv = (torch.empty(q.shape, dtype=torch.float32, device="cuda") for _ in range(3))
+    dW = torch.empty_like(Wd)
+    stream = torch.cuda.current_stream()
+
+    def run(n):
+        for _ in range(n):
+            mh.mhla_backward(qd, kd, vd, Wd, dy, dq, dk, dv, dW, causal=w.causal)
+
+    def elapsed_ms(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    run(args.warmup)
+    eager = elapsed_ms(lambda: run(args.steps)) / args.steps
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(args.steps)
+    graph.replay()
+    gms = elapsed_ms(graph.replay) / args.steps
+    ms = min(eager, gms)
+    e = 2 if w.dtype == "bf16" else 4
+    nbytes = w.B * w.H * w.N * w.d * (3 * e + 4 + 3 * 4)
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    line = {
+        "metric": "MHLA backward (dq, dk, dv, dW) tokens/s at 1 MI355X",
+        "value": round(w.tokens / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "graph_ms_per_step": round(gms, 5), "eager_ms_per_step": round(eager, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.key + "_backward", "B": w.B, "H": w.H, "N": w.N, "d": w.d, "M": w.M,
+                   "causal": w.causal, "global_batch": w.B, "seq_len": w.N, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "kernel": "backward (all kernels)", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def sweep_bench(args):
     """Throughput over a grid of sequence lengths N and block counts M at the DiT-S/2 head
     shape (H = 6, d = 64, bf16, non-causal), each point on a batch of about 2^18 tokens,
@@ -238,6 +296,8 @@ def main():
     ap.add_argument("--decode", action="store_true",
                     help="time the streaming causal decode step (one token per call) on the workload's "
                          "B, H, d, M, C instead of the forward pass; prints its own JSON line")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass (dq, dk, dv, dW) on the workload instead of the forward")
     ap.add_argument("--sweep", action="store_true",
                     help="time mhla_forward over the N x M grid of the paper's scaling study instead of one "
                          "workload; prints its own JSON line")
@@ -259,6 +319,8 @@ def main():
     mh.load_library()
     if args.decode:
         return decode_bench(args, w)
+    if args.backward:
+        return backward_bench(args, w)
     if args.sweep:
         return sweep_bench(args)
     q, k, v, W = make_inputs(w)
