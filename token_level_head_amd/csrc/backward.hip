@@ -1,26 +1,53 @@
 // backward.hip -- gradients of the MHLA forward pass ("MHLA: Restoring Expressivity
 // of Linear Attention via Token-Level Multi-Head", §4.1 steps, App. C causal form;
-// the coefficient matrix M_c is learned end to end, §4.2).  For L = sum(dY * Y):
+// the coefficient matrix M_c is learned end to end, §4.2).  For L = sum(dY * Y),
+// token t in block i, A_t = S~_i (+ W_ii P_t causal), a_t = z~_i (+ W_ii p_t causal),
+// P_t, p_t = the summary of block i's tokens up to and including t:
 //
-//   num_t = phi(q_t) A_t, den_t = phi(q_t).a_t + 1e-6, A_t = S~_i (+ W_ii P_t causal),
-//   a_t = z~_i (+ W_ii p_t causal); dnum_t = dy_t / den_t, dden_t = -(dy_t . num_t) / den_t^2
-//   d phi(q_t) = A_t dnum_t + dden_t a_t
+//   U_t = A_t dy_t,  den_t = phi(q_t).a_t + 1e-6,  dy_t.num_t = phi(q_t).U_t
+//   dden_t = -(phi(q_t).U_t) / den_t^2,  dnum_t = dy_t / den_t
+//   d phi(q_t) = U_t / den_t + dden_t a_t
 //   dS~_i = sum_{t in i} phi(q_t) dnum_t^T,  dz~_i = sum_{t in i} dden_t phi(q_t)
 //   dS_b = sum_i W[i,b] dS~_i (causal: i > b),  dW[i,b] = sum_pairs <dS~_i | dz~_i, S_b | z_b>
-//   d phi(k_j) = dS_b v_j + dz_b,  dv_j = dS_b^T phi(k_j)          (j in block b)
-//   causal, keys j of block i: with R_j = sum_{t in i, t >= j} phi(q_t) dnum_t^T and
-//   r_j = sum_{t >= j} dden_t phi(q_t):  d phi(k_j) += W_ii (R_j v_j + r_j),
-//   dv_j += W_ii R_j^T phi(k_j),  dW[i,i] += sum_j phi(k_j)^T R_j v_j + phi(k_j) . r_j
+//   d phi(k_j) = dS_b v_j + dz_b,  dv_j = dS_b^T phi(k_j)                 (j in block b)
+//   causal, keys j of block b, R_j = sum_{t in b, t >= j} phi(q_t) dnum_t^T, r_j likewise
+//   with dden_t:  d phi(k_j) += W_bb (R_j v_j + r_j),  dv_j += W_bb R_j^T phi(k_j),
+//   dW[b,b] += sum_t phi(q_t).(P_t dnum_t) + dden_t phi(q_t).p_t
 //   dq = d phi(q) * phi'(q), dk = d phi(k) * phi'(k), phi'(x) = 1 (x > 0) or exp(x).
 //
-// Every step is float32 arithmetic on the exact input values (phi with the
-// full-precision exp).  Summaries here use the plain layout, [r][c] row-major then
-// z: the backward recomputes S_b (bwd_summary_kernel) and S~_i (the mixing GEMM),
-// then runs one workgroup per (pair, block) over 16-token tiles staged in LDS:
-// bwd_query_kernel (dq, dS~, dz~; causal: a second, reverse pass over the block
-// for the within-block terms of dk, dv, dW_ii), the mixing GEMM with the
-// transposed W (dS), bwd_key_kernel (dk, dv), and a two-step deterministic
-// reduction for dW.
+// The numerator phi(q_t)^T A_t itself is never formed: its only use, dy_t.num_t, equals
+// phi(q_t).U_t.  Every d x d operand is therefore contracted over its value index c,
+// which is why the summaries here are stored transposed: X^T[c][r] (rows = value
+// column c, columns = feature r) in the packed layout of common.hpp, so that a
+// lane's packed chunks are exactly the B operand of U = dy X^T-style products.
+//
+// Precision: every product runs on bf16 MFMA with both operands split into hi + lo
+// bf16 parts (three products; two when an operand is an exact bf16 input), with
+// float32 accumulation in a fixed order -- about 16 significant bits per operand and
+// bit-reproducible results.  phi uses the full-precision exp.
+//
+// Tiles are 16 tokens.  Two register layouts of a tile are used (lane l, g = l / 16,
+// n = l % 16, d = 16P, FL = 4P):
+//   row layout (RL):  lane holds token n, features FL*g .. FL*g + FL - 1; it is the A
+//                     (or B) operand of the 16x16x32 MFMA with tokens along m (or n);
+//   dot layout (DL):  lane holds tokens 4g + i (i < 4), features P*n .. P*n + P - 1;
+//                     it is the result layout of those MFMAs (with the packed B
+//                     operand) and the A/B operand of the 16x16x16 MFMA with tokens
+//                     along k (the summary-type products).
+// Each tile is read through its own buffer descriptor whose range ends at the block's
+// last token: rows past it read as zero and stores to them are dropped.
+//
+// Kernels: bwd_sum_kernel recomputes S_b^T, z_b; the mixing GEMM (mix.hip) forms S~;
+// bwd_query_kernel / bwd_query_causal_kernel produce dq and dS~^T, dz~ (causal: also
+// per-token den, dden and the diagonal part of dW); the mixing GEMM with W^T forms dS;
+// bwd_key_kernel / bwd_key_causal_kernel produce dk, dv; bwd_dw_kernel and
+// bwd_dw_reduce_kernel form dW as a split-K MFMA GEMM with a fixed-order reduction.
+// Non-causal kernels spread a block's tiles over up to four waves of one workgroup
+// (partial sums added in LDS in a fixed order); causal kernels walk a block's tiles
+// in order (queries) or in reverse (keys) in one wave, carrying the running summary.
+#include <algorithm>
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -28,288 +55,760 @@ namespace mhla {
 
 namespace {
 
-constexpr int kTile = 16;  // tokens per LDS tile
+template <int D>
+struct Dim {
+    static constexpr int P = D / 16;
+    static constexpr int FL = 4 * P;                 // features per lane group (row layout)
+    static constexpr int KS = D >= 32 ? D / 32 : 1;  // 16x16x32 k-steps over features (d = 16 pads to 32)
+    static constexpr int L = D * D + D;              // floats per summary vector
+};
 
+// CNT consecutive elements (bf16 or float) at byte offset `off`, as floats.
+template <typename T, int CNT>
+__device__ __forceinline__ void load_run(rsrc_t r, uint32_t off, float (&x)[CNT]) {
+    constexpr int BYTES = CNT * (int)sizeof(T);
+    constexpr int WORDS = BYTES >= 4 ? BYTES / 4 : 1;
+    uint32_t w[WORDS];
+    if constexpr (BYTES >= 16) {
+#pragma unroll
+        for (int h = 0; h < BYTES / 16; ++h) {
+            const u32x4 v = buf_load128(r, off + 16 * h);
+            w[4 * h] = v.x;
+            w[4 * h + 1] = v.y;
+            w[4 * h + 2] = v.z;
+            w[4 * h + 3] = v.w;
+        }
+    } else if constexpr (BYTES == 8) {
+        const u32x2 v = buf_load64(r, off);
+        w[0] = v.x;
+        w[1] = v.y;
+    } else if constexpr (BYTES == 4) {
+        w[0] = buf_load32(r, off);
+    } else {
+        w[0] = buf_load16(r, off);
+    }
+#pragma unroll
+    for (int c = 0; c < CNT; ++c) {
+        if constexpr (std::is_same<T, float>::value)
+            x[c] = __uint_as_float(w[c]);
+        else
+            x[c] = __uint_as_float((c & 1) ? (w[c >> 1] & 0xffff0000u) : (w[c >> 1] << 16));
+    }
+}
+
+template <int CNT>
+__device__ __forceinline__ void store_run(rsrc_t r, uint32_t off, const float (&x)[CNT]) {
+    if constexpr (CNT == 4) {
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u32x4{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])}, r,
+            (int)off, 0, 0);
+    } else if constexpr (CNT == 2) {
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(x[0]), __float_as_uint(x[1])}, r, (int)off, 0, 0);
+    } else {
+        static_assert(CNT == 1, "runs of 1, 2 or 4 floats");
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x[0]), r, (int)off, 0, 0);
+    }
+}
+
+// Descriptor over `rows` rows of width D starting at row `row0` of X.
 template <typename T>
-__device__ __forceinline__ float in_val(const T* p, int64_t i);
-template <>
-__device__ __forceinline__ float in_val<uint16_t>(const uint16_t* p, int64_t i) {
-    return bf16_to_f32(p[i]);
-}
-template <>
-__device__ __forceinline__ float in_val<float>(const float* p, int64_t i) {
-    return p[i];
+__device__ __forceinline__ rsrc_t tile_rsrc(const T* X, int64_t row0, int rows, int width) {
+    return make_rsrc(X + row0 * width, (uint32_t)(rows * width * (int)sizeof(T)));
 }
 
-__device__ __forceinline__ float dphi(float x) { return x > 0.f ? 1.f : expf(x); }
+template <typename T, int D>
+__device__ __forceinline__ void load_rl(rsrc_t r, int g, int n, float (&x)[D / 4]) {
+    load_run<T, D / 4>(r, (uint32_t)((n * D + (D / 4) * g) * (int)sizeof(T)), x);
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void load_dl(rsrc_t r, int g, int n, float (&x)[4][D / 16]) {
+    constexpr int P = D / 16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) load_run<T, P>(r, (uint32_t)(((4 * g + i) * D + P * n) * (int)sizeof(T)), x[i]);
+}
+
+template <int D>
+__device__ __forceinline__ void store_dl(rsrc_t r, int g, int n, int i, const float (&x)[D / 16]) {
+    constexpr int P = D / 16;
+    store_run<P>(r, (uint32_t)(((4 * g + i) * D + P * n) * 4), x);
+}
+
+// phi(x) = ELU(x) + 1 and its derivative.
+__device__ __forceinline__ float phi_grad(float x, float& dphi) {
+    const float e = expf(fminf(x, 0.f));
+    dphi = x > 0.f ? 1.f : e;
+    return fmaxf(x, 0.f) + e;
+}
+
+// Row-layout values as 16x16x32 operands (slot 8ks + e = group-local feature).
+template <int FL, int KS>
+__device__ __forceinline__ void split_rl(const float (&x)[FL], bf16x8 (&hi)[KS], bf16x8 (&lo)[KS]) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int f = 8 * ks + e;
+            const bf16pair h = split_bf16(f < FL ? x[f < FL ? f : 0] : 0.f);
+            hi[ks][e] = h.hi;
+            lo[ks][e] = h.lo;
+        }
+}
+
+// Dot-layout values as 16x16x16 operands, one per feature block.
+template <int P>
+__device__ __forceinline__ void split_dl(const float (&x)[4][P], bf16x4 (&hi)[P], bf16x4 (&lo)[P]) {
+#pragma unroll
+    for (int b = 0; b < P; ++b)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const bf16pair h = split_bf16(x[e][b]);
+            hi[b][e] = h.hi;
+            lo[b][e] = h.lo;
+        }
+}
+
+__device__ __forceinline__ void split4(const f32x4& x, bf16x4& hi, bf16x4& lo) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const bf16pair h = split_bf16(x[e]);
+        hi[e] = h.hi;
+        lo[e] = h.lo;
+    }
+}
+
+// B operands from packed chunks of X: slot (ks, e) of column block jb is
+// X[FL*g + 8ks + e][P*n + jb], held in chunk (f % P, jb) at position f / P.
+template <int P, int KS>
+__device__ __forceinline__ void packed_b(const f32x4 (&ch)[P * P], bf16x8 (&bh)[KS][P], bf16x8 (&bl)[KS][P]) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int jb = 0; jb < P; ++jb)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int f = 8 * ks + e;
+                const bf16pair h = split_bf16(f < 4 * P ? ch[(f % P) * P + jb][f / P] : 0.f);
+                bh[ks][jb][e] = h.hi;
+                bl[ks][jb][e] = h.lo;
+            }
+}
+
+// acc[jb] += A (row layout, tokens along m) x X (packed B operands), column block jb
+// = columns P*n + jb.  ALO: the A operand has a lo part (else it is exact in bf16).
+template <int P, int KS, bool ALO>
+__device__ __forceinline__ void gemm_rl(const bf16x8 (&ah)[KS], const bf16x8 (&al)[KS], const bf16x8 (&bh)[KS][P],
+                                        const bf16x8 (&bl)[KS][P], f32x4 (&acc)[P]) {
+#pragma unroll
+    for (int jb = 0; jb < P; ++jb)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            acc[jb] = mfma32(ah[ks], bh[ks][jb], acc[jb]);
+            acc[jb] = mfma32(ah[ks], bl[ks][jb], acc[jb]);
+            if constexpr (ALO) acc[jb] = mfma32(al[ks], bh[ks][jb], acc[jb]);
+        }
+}
+
+// acc (packed chunks of X) += sum over the tile's tokens of a_t b_t^T, X[r][c] with
+// r from the A side and c from the B side (both in dot layout).
+template <int P, bool ALO>
+__device__ __forceinline__ void acc_outer(const bf16x4 (&ah)[P], const bf16x4 (&al)[P], const bf16x4 (&bh)[P],
+                                          const bf16x4 (&bl)[P], f32x4 (&acc)[P * P]) {
+#pragma unroll
+    for (int ia = 0; ia < P; ++ia)
+#pragma unroll
+        for (int ib = 0; ib < P; ++ib) {
+            f32x4 c = acc[ia * P + ib];
+            c = mfma16(ah[ia], bh[ib], c);
+            c = mfma16(ah[ia], bl[ib], c);
+            if constexpr (ALO) c = mfma16(al[ia], bh[ib], c);
+            acc[ia * P + ib] = c;
+        }
+}
+
+// Sum over the 16 lanes of a lane group.
+__device__ __forceinline__ float sum16(float x) {
+    x += __shfl_xor(x, 1, 64);
+    x += __shfl_xor(x, 2, 64);
+    x += __shfl_xor(x, 4, 64);
+    x += __shfl_xor(x, 8, 64);
+    return x;
+}
+
+template <int P>
+__device__ __forceinline__ void load_packed(const float* X, int lane, f32x4 (&ch)[P * P]) {
+#pragma unroll
+    for (int c = 0; c < P * P; ++c) ch[c] = *reinterpret_cast<const f32x4*>(X + c * 256 + lane * 4);
+}
+
+// Packed chunks of Y = X^T from the packed X: chunk (ia, ib) position i of lane (g, n)
+// is Y[P(4g + i) + ia][Pn + ib] = X[Pn + ib][P(4g + i) + ia].
+template <int P>
+__device__ __forceinline__ void load_packed_t(const float* X, int g, int n, f32x4 (&ch)[P * P]) {
+#pragma unroll
+    for (int ia = 0; ia < P; ++ia)
+#pragma unroll
+        for (int ib = 0; ib < P; ++ib)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ch[ia * P + ib][i] = X[packed_index(P, P * n + ib, P * (4 * g + i) + ia)];
+}
+
+template <int P>
+__device__ __forceinline__ void store_packed(float* X, int lane, int g, int n, const f32x4 (&ch)[P * P],
+                                             const float (&z)[P]) {
+    constexpr int D = 16 * P;
+#pragma unroll
+    for (int c = 0; c < P * P; ++c) *reinterpret_cast<f32x4*>(X + c * 256 + lane * 4) = ch[c];
+    if (g == 0)
+#pragma unroll
+        for (int b = 0; b < P; ++b) X[D * D + P * n + b] = z[b];
+}
+
+// Adds the partial summaries of the `wpu` waves of a workgroup into wave 0, pairwise
+// through LDS in a fixed order.  z must already be summed over the lane groups.
+template <int P>
+__device__ void reduce_waves(f32x4 (&acc)[P * P], float (&z)[P], float* lds, int wave, int wpu, int lane, int g,
+                             int n) {
+    constexpr int D = 16 * P, L = D * D + D;
+    for (int s = wpu >> 1; s >= 1; s >>= 1) {
+        if (wave >= s && wave < 2 * s) {
+            float* dst = lds + (wave - s) * L;
+#pragma unroll
+            for (int c = 0; c < P * P; ++c) *reinterpret_cast<f32x4*>(dst + c * 256 + lane * 4) = acc[c];
+            if (g == 0)
+#pragma unroll
+                for (int b = 0; b < P; ++b) dst[D * D + P * n + b] = z[b];
+        }
+        __syncthreads();
+        if (wave < s) {
+            const float* src = lds + wave * L;
+#pragma unroll
+            for (int c = 0; c < P * P; ++c) acc[c] += *reinterpret_cast<const f32x4*>(src + c * 256 + lane * 4);
+#pragma unroll
+            for (int b = 0; b < P; ++b) z[b] += src[D * D + P * n + b];
+        }
+        __syncthreads();
+    }
+}
 
 }  // namespace
 
-// S_b, z_b in float32, plain layout: one workgroup per (pair, block).
+// S_b^T, z_b (packed, transposed) for one (pair, block) per workgroup of wpu waves.
 template <int D, typename T>
-__global__ __launch_bounds__(256) void bwd_summary_kernel(const T* __restrict__ K, const T* __restrict__ V,
-                                                          float* __restrict__ S, int64_t BH, int N, int M) {
-    constexpr int L = D * D + D;
-    constexpr int EPT = (L + 255) / 256;  // entries per thread
-    __shared__ float fk[kTile][D], vv[kTile][D];
-    const int tid = threadIdx.x;
-    const int64_t unit = blockIdx.x;  // pair * M + block
-    const int64_t pair = unit / M;
-    const int blk = (int)(unit % M);
-    const int C = N / M;
-    const T* Kp = K + (pair * N + (int64_t)blk * C) * D;
-    const T* Vp = V + (pair * N + (int64_t)blk * C) * D;
-    float acc[EPT];
+__global__ __launch_bounds__(256) void bwd_sum_kernel(const T* __restrict__ K, const T* __restrict__ V,
+                                                      float* __restrict__ S, int64_t BH, int N, int M, int wpu) {
+    using Dm = Dim<D>;
+    constexpr int P = Dm::P, L = Dm::L;
+    constexpr bool VLO = !std::is_same<T, uint16_t>::value;  // bf16 inputs are exact bf16 operands
+    extern __shared__ float red[];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, n = lane & 15;
+    const int64_t unit = blockIdx.x, pair = unit / M;
+    const int blk = (int)(unit % M), C = N / M;
+    const int64_t row0 = pair * N + (int64_t)blk * C;
+    const int ntiles = (C + 15) / 16;
+    f32x4 acc[P * P];
+    float z[P];
 #pragma unroll
-    for (int u = 0; u < EPT; ++u) acc[u] = 0.f;
-    for (int t0 = 0; t0 < C; t0 += kTile) {
-        for (int x = tid; x < kTile * D; x += 256) {
-            const int t = x / D, r = x % D;
-            const bool ok = t0 + t < C;
-            fk[t][r] = ok ? phi_precise(in_val<T>(Kp, (int64_t)(t0 + t) * D + r)) : 0.f;
-            vv[t][r] = ok ? in_val<T>(Vp, (int64_t)(t0 + t) * D + r) : 0.f;
-        }
-        __syncthreads();
+    for (int c = 0; c < P * P; ++c) acc[c] = zero4();
 #pragma unroll
-        for (int u = 0; u < EPT; ++u) {
-            const int e = tid + 256 * u;
-            if (e < D * D) {
-                const int r = e / D, c = e % D;
-                for (int t = 0; t < kTile; ++t) acc[u] = fmaf(fk[t][r], vv[t][c], acc[u]);
-            } else if (e < L) {
-                for (int t = 0; t < kTile; ++t) acc[u] += fk[t][e - D * D];
+    for (int b = 0; b < P; ++b) z[b] = 0.f;
+    for (int tile = wave; tile < ntiles; tile += wpu) {
+        const int t0 = 16 * tile, rows = min(16, C - t0);
+        const rsrc_t rk = tile_rsrc(K, row0 + t0, rows, D), rv = tile_rsrc(V, row0 + t0, rows, D);
+        float kx[4][P], vx[4][P];
+        load_dl<T, D>(rk, g, n, kx);
+        load_dl<T, D>(rv, g, n, vx);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int b = 0; b < P; ++b) {
+                kx[i][b] = 4 * g + i < rows ? phi_precise(kx[i][b]) : 0.f;
+                z[b] += kx[i][b];
             }
-        }
-        __syncthreads();
+        bf16x4 kh[P], kl[P], vh[P], vl[P];
+        split_dl<P>(kx, kh, kl);
+        split_dl<P>(vx, vh, vl);
+        acc_outer<P, VLO>(vh, vl, kh, kl, acc);
     }
-    float* out = S + ((int64_t)blk * BH + pair) * L;
 #pragma unroll
-    for (int u = 0; u < EPT; ++u) {
-        const int e = tid + 256 * u;
-        if (e < L) out[e] = acc[u];
+    for (int b = 0; b < P; ++b) z[b] = sum_over_groups(z[b]);
+    if (wpu > 1) reduce_waves<P>(acc, z, red, wave, wpu, lane, g, n);
+    if (wave == 0) store_packed<P>(S + ((int64_t)blk * BH + pair) * L, lane, g, n, acc, z);
+}
+
+// dq and dS~_i^T, dz~_i for one (pair, block i) per workgroup of wpu waves (non-causal).
+template <int D, typename T>
+__global__ __launch_bounds__(256) void bwd_query_kernel(const T* __restrict__ Q, const float* __restrict__ dY,
+                                                        const float* __restrict__ St, float* __restrict__ dQ,
+                                                        float* __restrict__ dSt, int64_t BH, int N, int M, int wpu) {
+    using Dm = Dim<D>;
+    constexpr int P = Dm::P, FL = Dm::FL, KS = Dm::KS, L = Dm::L;
+    extern __shared__ float red[];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, n = lane & 15;
+    const int64_t unit = blockIdx.x, pair = unit / M;
+    const int blk = (int)(unit % M), C = N / M;
+    const int64_t row0 = pair * N + (int64_t)blk * C;
+    const int ntiles = (C + 15) / 16;
+
+    const float* sv = St + ((int64_t)blk * BH + pair) * L;
+    bf16x8 bh[KS][P], bl[KS][P];  // B[k = c][col = r] = S~[r][c]
+    float zt[P];
+    {
+        f32x4 ch[P * P];
+        load_packed<P>(sv, lane, ch);
+        packed_b<P, KS>(ch, bh, bl);
+#pragma unroll
+        for (int b = 0; b < P; ++b) zt[b] = sv[D * D + P * n + b];
+    }
+    f32x4 acc[P * P];
+    float zacc[P];
+#pragma unroll
+    for (int c = 0; c < P * P; ++c) acc[c] = zero4();
+#pragma unroll
+    for (int b = 0; b < P; ++b) zacc[b] = 0.f;
+
+    for (int tile = wave; tile < ntiles; tile += wpu) {
+        const int t0 = 16 * tile, rows = min(16, C - t0);
+        const rsrc_t rq = tile_rsrc(Q, row0 + t0, rows, D), ry = tile_rsrc(dY, row0 + t0, rows, D);
+        const rsrc_t rdq = tile_rsrc(dQ, row0 + t0, rows, D);
+        float yr[FL], yd[4][P], qd[4][P];
+        load_rl<float, D>(ry, g, n, yr);
+        load_dl<float, D>(ry, g, n, yd);
+        load_dl<T, D>(rq, g, n, qd);
+        bf16x8 yh[KS], yl[KS];
+        split_rl<FL, KS>(yr, yh, yl);
+        f32x4 u[P];  // U[4g + i][Pn + jb] = (S~_i dy_t)[r]
+#pragma unroll
+        for (int jb = 0; jb < P; ++jb) u[jb] = zero4();
+        gemm_rl<P, KS, true>(yh, yl, bh, bl, u);
+
+        float fq[4][P], dp[4][P], dn[4][P], dden[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float den = 0.f, dyn = 0.f;
+#pragma unroll
+            for (int b = 0; b < P; ++b) {
+                fq[i][b] = phi_grad(qd[i][b], dp[i][b]);
+                den = fmaf(fq[i][b], zt[b], den);
+                dyn = fmaf(fq[i][b], u[b][i], dyn);
+            }
+            den = sum16(den) + kEps;
+            dyn = sum16(dyn);
+            const float rden = 1.f / den;
+            dden[i] = -dyn * rden * rden;
+            float out[P];
+#pragma unroll
+            for (int b = 0; b < P; ++b) {
+                out[b] = fmaf(u[b][i], rden, dden[i] * zt[b]) * dp[i][b];
+                dn[i][b] = yd[i][b] * rden;
+            }
+            store_dl<D>(rdq, g, n, i, out);
+        }
+        bf16x4 nh[P], nl[P], qh[P], ql[P];
+        split_dl<P>(dn, nh, nl);
+        split_dl<P>(fq, qh, ql);
+        acc_outer<P, true>(nh, nl, qh, ql, acc);  // dS~^T[c][r] += dnum[c] phi(q)[r]
+#pragma unroll
+        for (int b = 0; b < P; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) zacc[b] = fmaf(dden[i], fq[i][b], zacc[b]);
+    }
+#pragma unroll
+    for (int b = 0; b < P; ++b) zacc[b] = sum_over_groups(zacc[b]);
+    if (wpu > 1) reduce_waves<P>(acc, zacc, red, wave, wpu, lane, g, n);
+    if (wave == 0) store_packed<P>(dSt + ((int64_t)blk * BH + pair) * L, lane, g, n, acc, zacc);
+}
+
+// dk, dv for one (pair, key block b) from dS_b^T, dz_b (non-causal); waves of the
+// workgroup take the block's tiles in turn.
+template <int D, typename T>
+__global__ __launch_bounds__(256) void bwd_key_kernel(const T* __restrict__ K, const T* __restrict__ V,
+                                                      const float* __restrict__ dS, float* __restrict__ dK,
+                                                      float* __restrict__ dV, int64_t BH, int N, int M, int wpu) {
+    using Dm = Dim<D>;
+    constexpr int P = Dm::P, FL = Dm::FL, KS = Dm::KS, L = Dm::L;
+    constexpr bool VLO = !std::is_same<T, uint16_t>::value;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, n = lane & 15;
+    const int64_t unit = blockIdx.x, pair = unit / M;
+    const int blk = (int)(unit % M), C = N / M;
+    const int64_t row0 = pair * N + (int64_t)blk * C;
+    const int ntiles = (C + 15) / 16;
+    if (wave >= ntiles) return;  // no barriers in this kernel
+
+    const float* sv = dS + ((int64_t)blk * BH + pair) * L;
+    bf16x8 b1h[KS][P], b1l[KS][P];  // B[k = c][col = r] = dS[r][c]   (d phi(k) = dS v + dz)
+    bf16x8 b2h[KS][P], b2l[KS][P];  // B[k = r][col = c] = dS[r][c]   (dv = dS^T phi(k))
+    float dz[P];
+    {
+        f32x4 ch[P * P];
+        load_packed<P>(sv, lane, ch);
+        packed_b<P, KS>(ch, b1h, b1l);
+        load_packed_t<P>(sv, g, n, ch);
+        packed_b<P, KS>(ch, b2h, b2l);
+#pragma unroll
+        for (int b = 0; b < P; ++b) dz[b] = sv[D * D + P * n + b];
+    }
+    for (int tile = wave; tile < ntiles; tile += wpu) {
+        const int t0 = 16 * tile, rows = min(16, C - t0);
+        const rsrc_t rk = tile_rsrc(K, row0 + t0, rows, D), rv = tile_rsrc(V, row0 + t0, rows, D);
+        const rsrc_t rdk = tile_rsrc(dK, row0 + t0, rows, D), rdv = tile_rsrc(dV, row0 + t0, rows, D);
+        float vr[FL], kr[FL], kd[4][P];
+        load_rl<T, D>(rv, g, n, vr);
+        load_rl<T, D>(rk, g, n, kr);
+        load_dl<T, D>(rk, g, n, kd);
+#pragma unroll
+        for (int f = 0; f < FL; ++f) kr[f] = phi_precise(kr[f]);
+        bf16x8 vh[KS], vl[KS], kh[KS], kl[KS];
+        split_rl<FL, KS>(vr, vh, vl);
+        split_rl<FL, KS>(kr, kh, kl);
+        f32x4 a1[P], a2[P];
+#pragma unroll
+        for (int b = 0; b < P; ++b) a1[b] = a2[b] = zero4();
+        gemm_rl<P, KS, VLO>(vh, vl, b1h, b1l, a1);
+        gemm_rl<P, KS, true>(kh, kl, b2h, b2l, a2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float ok[P], ov[P];
+#pragma unroll
+            for (int b = 0; b < P; ++b) {
+                float dp;
+                phi_grad(kd[i][b], dp);
+                ok[b] = (a1[b][i] + dz[b]) * dp;
+                ov[b] = a2[b][i];
+            }
+            store_dl<D>(rdk, g, n, i, ok);
+            store_dl<D>(rdv, g, n, i, ov);
+        }
     }
 }
 
-// dq, dS~_i, dz~_i for one (pair, query block i); causal also the within-block
-// terms of dk, dv (written to dk, dv as d phi(k) and dv partials) and dW_ii.
-template <int D, typename T, bool CAUSAL>
-__global__ __launch_bounds__(256) void bwd_query_kernel(const T* __restrict__ Q, const T* __restrict__ K,
-                                                        const T* __restrict__ V, const float* __restrict__ dY,
-                                                        const float* __restrict__ W, const float* __restrict__ St,
-                                                        float* __restrict__ dSt, float* __restrict__ G,
-                                                        float* __restrict__ dQ, float* __restrict__ dK,
-                                                        float* __restrict__ dV, float* __restrict__ dWdiag,
-                                                        int64_t BH, int N, int M) {
-    constexpr int L = D * D + D;
-    constexpr int EPT = (L + 255) / 256;
-    constexpr int OPT = kTile * D / 256;  // (token, column) outputs per thread
-    __shared__ float A[L];  // S~_i (+ W_ii P of the earlier tiles) and z~_i (+ W_ii p); reverse pass: R, r
-    __shared__ float fq[kTile][D], fk[kTile][D], vv[kTile][D], dyv[kTile][D], nm[kTile][D];
-    __shared__ float sc[kTile][kTile], gg[kTile][kTile], den[kTile], dd[kTile], red[kTile];
-    const int tid = threadIdx.x;
-    const int64_t unit = blockIdx.x;
-    const int64_t pair = unit / M;
-    const int blk = (int)(unit % M);
-    const int C = N / M;
-    const int64_t base = pair * N + (int64_t)blk * C;  // first token row of the block
-    const float wii = CAUSAL ? W[(int64_t)blk * M + blk] : 0.f;
-    const float* Sv = St + ((int64_t)blk * BH + pair) * L;
-    for (int e = tid; e < L; e += 256) A[e] = Sv[e];
-    float acc[EPT];  // dS~_i, dz~_i entries tid + 256u
-#pragma unroll
-    for (int u = 0; u < EPT; ++u) acc[u] = 0.f;
-    __syncthreads();
+// Causal, one wave per (pair, query block i), tiles in order.  Besides dq and
+// dS~_i^T, dz~_i it keeps (den_t, dden_t) per token for the key pass and writes the
+// block's part of dW[i,i].  The running summary of the block's earlier tiles is held
+// transposed (P^T, packed) next to the constant S~_i^T; inside a tile the masked
+// scores (v_j . dy_t, j <= t) carry the rest of P_t dy_t.
+template <int D, typename T>
+__global__ __launch_bounds__(64) void bwd_query_causal_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const float* __restrict__ dY,
+    const float* __restrict__ W, const float* __restrict__ St, float* __restrict__ dQ, float* __restrict__ dSt,
+    float* __restrict__ G, float* __restrict__ dWdiag, int64_t BH, int N, int M) {
+    using Dm = Dim<D>;
+    constexpr int P = Dm::P, FL = Dm::FL, KS = Dm::KS, L = Dm::L;
+    constexpr bool VLO = !std::is_same<T, uint16_t>::value;
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4, n = lane & 15;
+    const int64_t unit = blockIdx.x, pair = unit / M;
+    const int blk = (int)(unit % M), C = N / M;
+    const int64_t row0 = pair * N + (int64_t)blk * C;
+    const int ntiles = (C + 15) / 16;
+    const float wii = W[(int64_t)blk * M + blk];
 
-    for (int t0 = 0; t0 < C; t0 += kTile) {
-        for (int x = tid; x < kTile * D; x += 256) {
-            const int t = x / D, r = x % D;
-            const bool ok = t0 + t < C;
-            const int64_t row = (base + t0 + t) * D + r;
-            fq[t][r] = ok ? phi_precise(in_val<T>(Q, row)) : 0.f;
-            dyv[t][r] = ok ? dY[row] : 0.f;
-            if constexpr (CAUSAL) {
-                fk[t][r] = ok ? phi_precise(in_val<T>(K, row)) : 0.f;
-                vv[t][r] = ok ? in_val<T>(V, row) : 0.f;
-            }
-        }
-        __syncthreads();
-        if constexpr (CAUSAL) {  // in-tile scores phi(q_t).phi(k_j)
-            const int t = tid / kTile, j = tid % kTile;
-            float s = 0.f;
-            for (int r = 0; r < D; ++r) s = fmaf(fq[t][r], fk[j][r], s);
-            sc[t][j] = s;
-            __syncthreads();
-        }
-        // numerator and denominator (A holds S~_i + W_ii P of the earlier tiles)
+    const float* sv = St + ((int64_t)blk * BH + pair) * L;
+    bf16x8 bh[KS][P], bl[KS][P];  // S~_i as B[k = c][col = r]
+    float zt[P];
+    {
+        f32x4 ch[P * P];
+        load_packed<P>(sv, lane, ch);
+        packed_b<P, KS>(ch, bh, bl);
 #pragma unroll
-        for (int o = 0; o < OPT; ++o) {
-            const int x = tid + 256 * o, t = x / D, c = x % D;
-            float s = 0.f;
-            for (int r = 0; r < D; ++r) s = fmaf(fq[t][r], A[r * D + c], s);
-            if constexpr (CAUSAL)
-                for (int j = 0; j <= t; ++j) s = fmaf(wii * sc[t][j], vv[j][c], s);
-            nm[t][c] = s;
-        }
-        if (tid < kTile) {
-            const int t = tid;
-            float s = 0.f;
-            for (int r = 0; r < D; ++r) s = fmaf(fq[t][r], A[D * D + r], s);
-            if constexpr (CAUSAL)
-                for (int j = 0; j <= t; ++j) s = fmaf(wii, sc[t][j], s);
-            den[t] = s + kEps;
-        }
-        __syncthreads();
-        if (tid < kTile) {
-            const int t = tid;
-            float s = 0.f;
-            for (int c = 0; c < D; ++c) s = fmaf(dyv[t][c], nm[t][c], s);
-            dd[t] = t0 + t < C ? -s / (den[t] * den[t]) : 0.f;
-        }
-        __syncthreads();
-        for (int x = tid; x < kTile * D; x += 256) {  // nm becomes dnum
-            const int t = x / D, c = x % D;
-            nm[t][c] = t0 + t < C ? dyv[t][c] / den[t] : 0.f;
-        }
-        __syncthreads();
-        if constexpr (CAUSAL) {  // g[t][j] = v_j . dnum_t + dden_t
-            const int t = tid / kTile, j = tid % kTile;
-            float s = dd[t];
-            for (int c = 0; c < D; ++c) s = fmaf(vv[j][c], nm[t][c], s);
-            gg[t][j] = s;
-            __syncthreads();
-        }
-        // d phi(q_t) = A dnum_t + dden_t a (+ W_ii sum_{j <= t in tile} g[t][j] phi(k_j)) -> dq
-#pragma unroll
-        for (int o = 0; o < OPT; ++o) {
-            const int x = tid + 256 * o, t = x / D, r = x % D;
-            float s = dd[t] * A[D * D + r];
-            for (int c = 0; c < D; ++c) s = fmaf(A[r * D + c], nm[t][c], s);
-            if constexpr (CAUSAL)
-                for (int j = 0; j <= t; ++j) s = fmaf(wii * gg[t][j], fk[j][r], s);
-            if (t0 + t < C) {
-                const int64_t row = (base + t0 + t) * D + r;
-                dQ[row] = s * dphi(in_val<T>(Q, row));
-            }
-        }
-        // dS~_i += phi(q_t) dnum_t^T, dz~_i += dden_t phi(q_t)
-#pragma unroll
-        for (int u = 0; u < EPT; ++u) {
-            const int e = tid + 256 * u;
-            if (e < D * D) {
-                const int r = e / D, c = e % D;
-                for (int t = 0; t < kTile; ++t) acc[u] = fmaf(fq[t][r], nm[t][c], acc[u]);
-            } else if (e < L) {
-                for (int t = 0; t < kTile; ++t) acc[u] = fmaf(dd[t], fq[t][e - D * D], acc[u]);
-            }
-        }
-        if constexpr (CAUSAL) {
-            // keep dnum, dden for the reverse pass
-            for (int x = tid; x < kTile * (D + 1); x += 256) {
-                const int t = x / (D + 1), c = x % (D + 1);
-                if (t0 + t < C) G[(base + t0 + t) * (D + 1) + c] = c < D ? nm[t][c] : dd[t];
-            }
-            __syncthreads();
-            // fold this tile's summary, times W_ii, into A
-            for (int e = tid; e < L; e += 256) {
-                float s = 0.f;
-                if (e < D * D) {
-                    const int r = e / D, c = e % D;
-                    for (int j = 0; j < kTile; ++j) s = fmaf(fk[j][r], vv[j][c], s);
-                } else {
-                    for (int j = 0; j < kTile; ++j) s += fk[j][e - D * D];
-                }
-                A[e] = fmaf(wii, s, A[e]);
-            }
-        }
-        __syncthreads();
+        for (int b = 0; b < P; ++b) zt[b] = sv[D * D + P * n + b];
     }
-    float* out = dSt + ((int64_t)blk * BH + pair) * L;
+    f32x4 pt[P * P], acc[P * P];  // running P^T of the earlier tiles; dS~_i^T
+    float pz[P], zacc[P], dwl = 0.f;
 #pragma unroll
-    for (int u = 0; u < EPT; ++u) {
-        const int e = tid + 256 * u;
-        if (e < L) out[e] = acc[u];
-    }
-    if constexpr (!CAUSAL) return;
+    for (int c = 0; c < P * P; ++c) pt[c] = acc[c] = zero4();
+#pragma unroll
+    for (int b = 0; b < P; ++b) pz[b] = zacc[b] = 0.f;
 
-    // ---- reverse pass over the block: R_j, r_j for keys j (later queries first) ----
-    for (int e = tid; e < L; e += 256) A[e] = 0.f;  // A now holds R (after the current tile), r
-    float dw = 0.f;
-    __syncthreads();
-    const int ntiles = (C + kTile - 1) / kTile;
-    for (int ti = ntiles - 1; ti >= 0; --ti) {
-        const int t0 = ti * kTile;
-        for (int x = tid; x < kTile * D; x += 256) {
-            const int t = x / D, r = x % D;
-            const bool ok = t0 + t < C;
-            const int64_t row = (base + t0 + t) * D + r;
-            fq[t][r] = ok ? phi_precise(in_val<T>(Q, row)) : 0.f;
-            fk[t][r] = ok ? phi_precise(in_val<T>(K, row)) : 0.f;
-            vv[t][r] = ok ? in_val<T>(V, row) : 0.f;
-            nm[t][r] = ok ? G[(base + t0 + t) * (D + 1) + r] : 0.f;
-        }
-        if (tid < kTile) dd[tid] = t0 + tid < C ? G[(base + t0 + tid) * (D + 1) + D] : 0.f;
-        __syncthreads();
-        {  // sc[t][j] = phi(q_t).phi(k_j), gg[t][j] = v_j . dnum_t + dden_t
-            const int t = tid / kTile, j = tid % kTile;
-            float s = 0.f, u = dd[t];
-            for (int r = 0; r < D; ++r) {
-                s = fmaf(fq[t][r], fk[j][r], s);
-                u = fmaf(vv[j][r], nm[t][r], u);
-            }
-            sc[t][j] = s;
-            gg[t][j] = u;
-        }
-        __syncthreads();
-        // d phi(k_j) += W_ii (R v_j + r + sum_{t >= j in tile} g[t][j] phi(q_t)); dv_j += W_ii (R^T phi(k_j) + ...)
-        float dwp = 0.f;
+    for (int tile = 0; tile < ntiles; ++tile) {
+        const int t0 = 16 * tile, rows = min(16, C - t0);
+        const int64_t r0 = row0 + t0;
+        const rsrc_t rq = tile_rsrc(Q, r0, rows, D), rk = tile_rsrc(K, r0, rows, D), rv = tile_rsrc(V, r0, rows, D);
+        const rsrc_t ry = tile_rsrc(dY, r0, rows, D), rdq = tile_rsrc(dQ, r0, rows, D);
+        const rsrc_t rg = tile_rsrc(G, r0, rows, 2);
+        float yr[FL], vr[FL], yd[4][P], vd[4][P], kd[4][P], qd[4][P];
+        load_rl<float, D>(ry, g, n, yr);
+        load_rl<T, D>(rv, g, n, vr);
+        load_dl<float, D>(ry, g, n, yd);
+        load_dl<T, D>(rv, g, n, vd);
+        load_dl<T, D>(rk, g, n, kd);
+        load_dl<T, D>(rq, g, n, qd);
+
+        bf16x8 yh[KS], yl[KS];
+        split_rl<FL, KS>(yr, yh, yl);
+        f32x4 ui[P], us[P];  // S~_i dy_t and P_{<tile} dy_t, dot layout
 #pragma unroll
-        for (int o = 0; o < OPT; ++o) {
-            const int x = tid + 256 * o, j = x / D, r = x % D;
-            float s = A[D * D + r], sv = 0.f;
-            for (int c = 0; c < D; ++c) {
-                s = fmaf(A[r * D + c], vv[j][c], s);
-                sv = fmaf(A[c * D + r], fk[j][c], sv);
+        for (int b = 0; b < P; ++b) ui[b] = us[b] = zero4();
+        gemm_rl<P, KS, true>(yh, yl, bh, bl, ui);
+        {
+            bf16x8 sh[KS][P], sl[KS][P];
+            packed_b<P, KS>(pt, sh, sl);
+            gemm_rl<P, KS, true>(yh, yl, sh, sl, us);
+        }
+        // scores v_j . dy_t: lane (g, n) holds j = 4g + e, t = n, kept for j <= t
+        f32x4 gy = zero4();
+        {
+            bf16x8 vh[KS], vl[KS];
+            split_rl<FL, KS>(vr, vh, vl);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                gy = mfma32(vh[ks], yh[ks], gy);
+                gy = mfma32(vh[ks], yl[ks], gy);
+                if constexpr (VLO) gy = mfma32(vl[ks], yh[ks], gy);
             }
-            // phi(k_j)^T R v_j + phi(k_j) . r, summed over r by the reduction below
-            dwp = fmaf(fk[j][r], s, dwp);
-            for (int t = j; t < kTile; ++t) {
-                s = fmaf(gg[t][j], fq[t][r], s);
-                sv = fmaf(sc[t][j], nm[t][r], sv);
-            }
-            if (t0 + j < C) {
-                const int64_t row = (base + t0 + j) * D + r;
-                dK[row] = wii * s;
-                dV[row] = wii * sv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) gy[e] = 4 * g + e <= n ? gy[e] : 0.f;
+        }
+        float fk[4][P];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int b = 0; b < P; ++b) fk[i][b] = 4 * g + i < rows ? phi_precise(kd[i][b]) : 0.f;
+        bf16x4 kh[P], kl[P];
+        split_dl<P>(fk, kh, kl);
+        {
+            bf16x4 gh, gl;
+            split4(gy, gh, gl);
+#pragma unroll
+            for (int b = 0; b < P; ++b) {  // us += sum_{j <= t in tile} (v_j . dy_t) phi(k_j)
+                us[b] = mfma16(gh, kh[b], us[b]);
+                us[b] = mfma16(gh, kl[b], us[b]);
+                us[b] = mfma16(gl, kh[b], us[b]);
             }
         }
-        if (tid < kTile * kTile) {  // in-tile part of dW_ii: sum_{t >= j} sc[t][j] g[t][j]
-            const int t = tid / kTile, j = tid % kTile;
-            if (t >= j) dwp = fmaf(sc[t][j], gg[t][j], dwp);
-        }
-        dw += dwp;
-        __syncthreads();
-        // R += sum_t phi(q_t) dnum_t^T, r += sum_t dden_t phi(q_t)
-        for (int e = tid; e < L; e += 256) {
-            float s = 0.f;
-            if (e < D * D) {
-                const int r = e / D, c = e % D;
-                for (int t = 0; t < kTile; ++t) s = fmaf(fq[t][r], nm[t][c], s);
-            } else {
-                for (int t = 0; t < kTile; ++t) s = fmaf(dd[t], fq[t][e - D * D], s);
+        // p_t = the block's phi(k) sum up to and including t (dot layout)
+        float pin[4][P];
+#pragma unroll
+        for (int b = 0; b < P; ++b) {
+            float run = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                run += fk[i][b];
+                pin[i][b] = run;
             }
-            A[e] += s;
+            float excl = 0.f;
+#pragma unroll
+            for (int h = 0; h < 3; ++h) {
+                const float t = __shfl(run, 16 * h + n, 64);
+                excl += h < g ? t : 0.f;
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pin[i][b] += pz[b] + excl;
+            pz[b] += sum_over_groups(run);
         }
-        __syncthreads();
+
+        float fq[4][P], dp[4][P], dn[4][P], dden[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float den = 0.f, idn = 0.f, dyn = 0.f, idy = 0.f;
+            float a[P];
+#pragma unroll
+            for (int b = 0; b < P; ++b) {
+                fq[i][b] = phi_grad(qd[i][b], dp[i][b]);
+                a[b] = fmaf(wii, pin[i][b], zt[b]);
+                const float uu = fmaf(wii, us[b][i], ui[b][i]);
+                den = fmaf(fq[i][b], a[b], den);
+                idn = fmaf(fq[i][b], pin[i][b], idn);
+                dyn = fmaf(fq[i][b], uu, dyn);
+                idy = fmaf(fq[i][b], us[b][i], idy);
+            }
+            den = sum16(den) + kEps;
+            idn = sum16(idn);
+            dyn = sum16(dyn);
+            idy = sum16(idy);
+            const float rden = 1.f / den;
+            dden[i] = -dyn * rden * rden;
+            float out[P];
+#pragma unroll
+            for (int b = 0; b < P; ++b) {
+                const float uu = fmaf(wii, us[b][i], ui[b][i]);
+                out[b] = fmaf(uu, rden, dden[i] * a[b]) * dp[i][b];
+                dn[i][b] = yd[i][b] * rden;
+            }
+            store_dl<D>(rdq, g, n, i, out);
+            if (n == 0) {
+                dwl += fmaf(idy, rden, dden[i] * idn);
+                const float gd[2] = {den, dden[i]};
+                store_run<2>(rg, (uint32_t)((4 * g + i) * 8), gd);
+            }
+        }
+        bf16x4 qh[P], ql[P];
+        split_dl<P>(fq, qh, ql);
+        {
+            bf16x4 nh[P], nl[P];
+            split_dl<P>(dn, nh, nl);
+            acc_outer<P, true>(nh, nl, qh, ql, acc);
+        }
+#pragma unroll
+        for (int b = 0; b < P; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) zacc[b] = fmaf(dden[i], fq[i][b], zacc[b]);
+        {  // P^T += v^T phi(k) over this tile
+            bf16x4 vh[P], vl[P];
+            split_dl<P>(vd, vh, vl);
+            acc_outer<P, VLO>(vh, vl, kh, kl, pt);
+        }
     }
-    // dW_ii of this (pair, block): fixed-order sum of the threads' partials
-    dw = sum_over_groups(dw);
-    dw += __shfl_xor(dw, 1, 64);
-    dw += __shfl_xor(dw, 2, 64);
-    dw += __shfl_xor(dw, 4, 64);
-    dw += __shfl_xor(dw, 8, 64);
-    if ((tid & 63) == 0) red[tid >> 6] = dw;
-    __syncthreads();
-    if (tid == 0) dWdiag[pair * M + blk] = red[0] + red[1] + red[2] + red[3];
+#pragma unroll
+    for (int b = 0; b < P; ++b) zacc[b] = sum_over_groups(zacc[b]);
+    store_packed<P>(dSt + ((int64_t)blk * BH + pair) * L, lane, g, n, acc, zacc);
+    dwl = sum_over_groups(sum16(dwl));
+    if (lane == 0) dWdiag[pair * M + blk] = dwl;
+}
+
+// Causal, one wave per (pair, key block b), tiles in reverse order.  The running
+// (dS_b + W_bb R_{>tile}) is held in both orientations: rows c for d phi(k) (contracted
+// over c with v) and rows r for dv (contracted over r with phi(k)).  Inside a tile the
+// masked scores phi(q_t).phi(k_j) and dnum_t . v_j + dden_t (t >= j) carry the rest.
+template <int D, typename T>
+__global__ __launch_bounds__(64) void bwd_key_causal_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const float* __restrict__ dY,
+    const float* __restrict__ W, const float* __restrict__ G, const float* __restrict__ dS, float* __restrict__ dK,
+    float* __restrict__ dV, int64_t BH, int N, int M) {
+    using Dm = Dim<D>;
+    constexpr int P = Dm::P, FL = Dm::FL, KS = Dm::KS, L = Dm::L;
+    constexpr bool VLO = !std::is_same<T, uint16_t>::value;
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4, n = lane & 15;
+    const int64_t unit = blockIdx.x, pair = unit / M;
+    const int blk = (int)(unit % M), C = N / M;
+    const int64_t row0 = pair * N + (int64_t)blk * C;
+    const int ntiles = (C + 15) / 16;
+    const float wbb = W[(int64_t)blk * M + blk];
+
+    const float* sv = dS + ((int64_t)blk * BH + pair) * L;
+    f32x4 s1[P * P], s2[P * P];  // rows c (= dS^T + W R^T), rows r (= dS + W R)
+    float s1z[P];
+    load_packed<P>(sv, lane, s1);
+    load_packed_t<P>(sv, g, n, s2);
+#pragma unroll
+    for (int b = 0; b < P; ++b) s1z[b] = sv[D * D + P * n + b];
+
+    for (int tile = ntiles - 1; tile >= 0; --tile) {
+        const int t0 = 16 * tile, rows = min(16, C - t0);
+        const int64_t r0 = row0 + t0;
+        const rsrc_t rq = tile_rsrc(Q, r0, rows, D), rk = tile_rsrc(K, r0, rows, D), rv = tile_rsrc(V, r0, rows, D);
+        const rsrc_t ry = tile_rsrc(dY, r0, rows, D), rg = tile_rsrc(G, r0, rows, 2);
+        const rsrc_t rdk = tile_rsrc(dK, r0, rows, D), rdv = tile_rsrc(dV, r0, rows, D);
+        float vr[FL], kr[FL], qr[FL], yr[FL], kd[4][P], qd[4][P], yd[4][P];
+        load_rl<T, D>(rv, g, n, vr);
+        load_rl<T, D>(rk, g, n, kr);
+        load_rl<T, D>(rq, g, n, qr);
+        load_rl<float, D>(ry, g, n, yr);
+        load_dl<T, D>(rk, g, n, kd);
+        load_dl<T, D>(rq, g, n, qd);
+        load_dl<float, D>(ry, g, n, yd);
+        float gn[2], gd[4][2];
+        load_run<float, 2>(rg, (uint32_t)(n * 8), gn);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) load_run<float, 2>(rg, (uint32_t)((4 * g + i) * 8), gd[i]);
+
+        // dnum in both layouts (rows past the block: zero)
+        const float rn = n < rows ? 1.f / gn[0] : 0.f;
+#pragma unroll
+        for (int f = 0; f < FL; ++f) yr[f] *= rn;
+        float fqd[4][P], dden[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float ri = 4 * g + i < rows ? 1.f / gd[i][0] : 0.f;
+            dden[i] = gd[i][1];
+#pragma unroll
+            for (int b = 0; b < P; ++b) {
+                yd[i][b] *= ri;
+                fqd[i][b] = phi_precise(qd[i][b]);
+            }
+        }
+#pragma unroll
+        for (int f = 0; f < FL; ++f) {
+            kr[f] = phi_precise(kr[f]);
+            qr[f] = phi_precise(qr[f]);
+        }
+        bf16x8 vh[KS], vl[KS], kh[KS], kl[KS];
+        split_rl<FL, KS>(vr, vh, vl);
+        split_rl<FL, KS>(kr, kh, kl);
+        f32x4 a1[P], a2[P];
+#pragma unroll
+        for (int b = 0; b < P; ++b) a1[b] = a2[b] = zero4();
+        {
+            bf16x8 sh[KS][P], sl[KS][P];
+            packed_b<P, KS>(s1, sh, sl);
+            gemm_rl<P, KS, VLO>(vh, vl, sh, sl, a1);
+            packed_b<P, KS>(s2, sh, sl);
+            gemm_rl<P, KS, true>(kh, kl, sh, sl, a2);
+        }
+        // scores: lane (g, n) holds t = 4g + e, j = n, kept for t >= j, times W_bb
+        f32x4 sc = zero4(), gg = zero4();
+        {
+            bf16x8 qh[KS], ql[KS], nh[KS], nl[KS];
+            split_rl<FL, KS>(qr, qh, ql);
+            split_rl<FL, KS>(yr, nh, nl);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                sc = mfma32(qh[ks], kh[ks], sc);
+                sc = mfma32(qh[ks], kl[ks], sc);
+                sc = mfma32(ql[ks], kh[ks], sc);
+                gg = mfma32(nh[ks], vh[ks], gg);
+                gg = mfma32(nl[ks], vh[ks], gg);
+                if constexpr (VLO) gg = mfma32(nh[ks], vl[ks], gg);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bool keep = 4 * g + e >= n;
+                sc[e] = keep ? wbb * sc[e] : 0.f;
+                gg[e] = keep ? wbb * (gg[e] + dden[e]) : 0.f;
+            }
+        }
+        bf16x4 qdh[P], qdl[P], ndh[P], ndl[P];
+        split_dl<P>(fqd, qdh, qdl);
+        split_dl<P>(yd, ndh, ndl);
+        {
+            bf16x4 sch, scl, ggh, ggl;
+            split4(sc, sch, scl);
+            split4(gg, ggh, ggl);
+#pragma unroll
+            for (int b = 0; b < P; ++b) {
+                a1[b] = mfma16(ggh, qdh[b], a1[b]);
+                a1[b] = mfma16(ggh, qdl[b], a1[b]);
+                a1[b] = mfma16(ggl, qdh[b], a1[b]);
+                a2[b] = mfma16(sch, ndh[b], a2[b]);
+                a2[b] = mfma16(sch, ndl[b], a2[b]);
+                a2[b] = mfma16(scl, ndh[b], a2[b]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float ok[P], ov[P];
+#pragma unroll
+            for (int b = 0; b < P; ++b) {
+                float dp;
+                phi_grad(kd[i][b], dp);
+                ok[b] = (a1[b][i] + s1z[b]) * dp;
+                ov[b] = a2[b][i];
+            }
+            store_dl<D>(rdk, g, n, i, ok);
+            store_dl<D>(rdv, g, n, i, ov);
+        }
+        // fold this tile into the running sums, times W_bb
+        float wdn[4][P];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int b = 0; b < P; ++b) wdn[i][b] = wbb * yd[i][b];
+        bf16x4 wh[P], wl[P];
+        split_dl<P>(wdn, wh, wl);
+        acc_outer<P, true>(wh, wl, qdh, qdl, s1);  // rows c: dnum[c] phi(q)[r]
+        acc_outer<P, true>(qdh, qdl, wh, wl, s2);  // rows r: phi(q)[r] dnum[c]
+#pragma unroll
+        for (int b = 0; b < P; ++b) {
+            float s = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s = fmaf(dden[i], fqd[i][b], s);
+            s1z[b] = fmaf(wbb, sum_over_groups(s), s1z[b]);
+        }
+    }
 }
 
 // Wt[b][i] = W[i][b] for the summaries that block b feeds (causal: i > b), else 0.
@@ -321,149 +820,206 @@ __global__ __launch_bounds__(256) void bwd_wt_kernel(const float* __restrict__ W
     Wt[x] = (!causal || i > b) ? W[(int64_t)i * M + b] : 0.f;
 }
 
-// dk, dv for one (pair, key block b) from dS_b, dz_b (causal: added to the
-// within-block partials the query kernel left in dK, dV).
-template <int D, typename T, bool CAUSAL>
-__global__ __launch_bounds__(256) void bwd_key_kernel(const T* __restrict__ K, const T* __restrict__ V,
-                                                      const float* __restrict__ dS, float* __restrict__ dK,
-                                                      float* __restrict__ dV, int64_t BH, int N, int M) {
-    constexpr int L = D * D + D;
-    constexpr int OPT = kTile * D / 256;
-    __shared__ float G[L], fk[kTile][D], vv[kTile][D];
-    const int tid = threadIdx.x;
-    const int64_t unit = blockIdx.x;
-    const int64_t pair = unit / M;
-    const int blk = (int)(unit % M);
-    const int C = N / M;
-    const int64_t base = pair * N + (int64_t)blk * C;
-    const float* g = dS + ((int64_t)blk * BH + pair) * L;
-    for (int e = tid; e < L; e += 256) G[e] = g[e];
-    __syncthreads();
-    for (int t0 = 0; t0 < C; t0 += kTile) {
-        for (int x = tid; x < kTile * D; x += 256) {
-            const int t = x / D, r = x % D;
-            const bool ok = t0 + t < C;
-            const int64_t row = (base + t0 + t) * D + r;
-            fk[t][r] = ok ? phi_precise(in_val<T>(K, row)) : 0.f;
-            vv[t][r] = ok ? in_val<T>(V, row) : 0.f;
-        }
-        __syncthreads();
+// dW partials: part[ch][i][b] = sum over columns of chunk ch of dSt[i][col] S[b][col],
+// one 64 x 64 output block per workgroup (wave w: rows 16w .. 16w + 15), on MFMA
+// with hi + lo operands.  ncols and chunk are multiples of 8.
+__global__ __launch_bounds__(256) void bwd_dw_kernel(const float* __restrict__ dSt, const float* __restrict__ S,
+                                                     float* __restrict__ part, int64_t ncols, int M, int64_t chunk,
+                                                     int nb) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, n = lane & 15;
+    const int ob = (int)(blockIdx.x % (nb * nb));
+    const int64_t ch = blockIdx.x / (nb * nb);
+    const int i0 = 64 * (ob / nb) + 16 * wave, b0 = 64 * (ob % nb);
+    const int64_t k0 = ch * chunk, k1 = min(ncols, k0 + chunk);
+    const int ai = i0 + n;
+    f32x4 acc[4];
 #pragma unroll
-        for (int o = 0; o < OPT; ++o) {
-            const int x = tid + 256 * o, j = x / D, r = x % D;
-            float s = G[D * D + r], sv = 0.f;
-            for (int c = 0; c < D; ++c) {
-                s = fmaf(G[r * D + c], vv[j][c], s);
-                sv = fmaf(G[c * D + r], fk[j][c], sv);
-            }
-            if (t0 + j < C) {
-                const int64_t row = (base + t0 + j) * D + r;
-                if constexpr (CAUSAL) {
-                    s += dK[row];
-                    sv += dV[row];
+    for (int jb = 0; jb < 4; ++jb) acc[jb] = zero4();
+    if (i0 < M) {
+        for (int64_t k = k0 + 8 * g; k < k1 + 8 * g; k += 32) {
+            const bool kok = k < k1;
+            float a[8];
+            {
+                const bool ok = kok && ai < M;
+                const f32x4* p = reinterpret_cast<const f32x4*>(dSt + (ok ? (int64_t)ai * ncols + k : 0));
+                const f32x4 x0 = ok ? p[0] : zero4(), x1 = ok ? p[1] : zero4();
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    a[e] = x0[e];
+                    a[4 + e] = x1[e];
                 }
-                dK[row] = s * dphi(in_val<T>(K, row));
-                dV[row] = sv;
+            }
+            bf16x8 ah, al;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const bf16pair h = split_bf16(a[e]);
+                ah[e] = h.hi;
+                al[e] = h.lo;
+            }
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb) {
+                const int bi = b0 + 16 * jb + n;
+                const bool ok = kok && bi < M;
+                const f32x4* p = reinterpret_cast<const f32x4*>(S + (ok ? (int64_t)bi * ncols + k : 0));
+                const f32x4 x0 = ok ? p[0] : zero4(), x1 = ok ? p[1] : zero4();
+                bf16x8 bh, bl;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const bf16pair h = split_bf16(e < 4 ? x0[e] : x1[e - 4]);
+                    bh[e] = h.hi;
+                    bl[e] = h.lo;
+                }
+                acc[jb] = mfma32(ah, bh, acc[jb]);
+                acc[jb] = mfma32(ah, bl, acc[jb]);
+                acc[jb] = mfma32(al, bh, acc[jb]);
             }
         }
-        __syncthreads();
     }
-}
-
-// dW partials: workgroup (tile of 16 x 16 (i, b), column chunk) sums dSt[i][col] S[b][col].
-__global__ __launch_bounds__(256) void bwd_dw_partial_kernel(const float* __restrict__ dSt,
-                                                             const float* __restrict__ S, float* __restrict__ part,
-                                                             int64_t ncols, int M, int64_t chunk, int ntiles) {
-    __shared__ float a[16][65], b[16][65];
-    const int tid = threadIdx.x;
-    const int tile = (int)(blockIdx.x % ntiles);
-    const int64_t ch = blockIdx.x / ntiles;
-    const int tpr = (M + 15) / 16;
-    const int i0 = 16 * (tile / tpr), b0 = 16 * (tile % tpr);
-    const int il = tid / 16, bl = tid % 16;
-    const int64_t c0 = ch * chunk, c1 = min(ncols, c0 + chunk);
-    float s = 0.f;
-    for (int64_t c = c0; c < c1; c += 64) {
-        for (int x = tid; x < 16 * 64; x += 256) {
-            const int rr = x / 64, cc = x % 64;
-            const int64_t col = c + cc;
-            a[rr][cc] = (i0 + rr < M && col < c1) ? dSt[(int64_t)(i0 + rr) * ncols + col] : 0.f;
-            b[rr][cc] = (b0 + rr < M && col < c1) ? S[(int64_t)(b0 + rr) * ncols + col] : 0.f;
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = i0 + 4 * g + i, col = b0 + 16 * jb + n;
+            if (row < M && col < M) part[(ch * M + row) * (int64_t)M + col] = acc[jb][i];
         }
-        __syncthreads();
-        for (int cc = 0; cc < 64; ++cc) s = fmaf(a[il][cc], b[bl][cc], s);
-        __syncthreads();
-    }
-    if (i0 + il < M && b0 + bl < M) part[(ch * M + i0 + il) * (int64_t)M + b0 + bl] = s;
 }
 
 // dW[i][b] = sum over chunks (fixed order); causal: b < i only, plus the diagonal
-// from the within-block partials of every pair.
+// from the per-pair partials.  `lanes` (1 or 64) consecutive lanes share an output:
+// lane l adds chunks (and pairs) l, l + lanes, ...; the lanes then combine in a
+// fixed butterfly order.
 __global__ __launch_bounds__(256) void bwd_dw_reduce_kernel(const float* __restrict__ part,
                                                             const float* __restrict__ dWdiag, float* __restrict__ dW,
-                                                            int M, int64_t nchunks, int64_t BH, int causal) {
-    const int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (x >= (int64_t)M * M) return;
-    const int i = (int)(x / M), b = (int)(x % M);
+                                                            int M, int64_t nchunks, int64_t BH, int causal, int lanes) {
+    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t x = tid / lanes;
+    const int l = (int)(tid % lanes);
+    const bool live = x < (int64_t)M * M;
+    const int i = live ? (int)(x / M) : 0, b = live ? (int)(x % M) : 0;
     float s = 0.f;
-    if (!causal || b < i)
-        for (int64_t ch = 0; ch < nchunks; ++ch) s += part[ch * M * M + x];
-    if (causal && b == i)
-        for (int64_t p = 0; p < BH; ++p) s += dWdiag[p * M + i];
-    dW[x] = s;
+    if (live && (!causal || b < i))
+        for (int64_t ch = l; ch < nchunks; ch += lanes) s += part[ch * M * M + x];
+    if (live && causal && b == i)
+        for (int64_t p = l; p < BH; p += lanes) s += dWdiag[p * M + i];
+    if (lanes == 64) {
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m, 64);
+    }
+    if (live && l == 0) dW[x] = s;
 }
 
-size_t backward_dw_chunk(int64_t ncols) { return ncols >= (1 << 16) ? 4096 : 1024; }
+namespace {
+
+struct DwPlan {
+    int nb;           // 64 x 64 output blocks per dimension
+    int64_t chunk;    // columns per partial
+    int64_t nchunks;
+    int lanes;        // lanes per output in the reduction
+};
+
+DwPlan dw_plan(int64_t ncols, int64_t M) {
+    DwPlan p;
+    p.nb = (int)((M + 63) / 64);
+    const int64_t nblk = (int64_t)p.nb * p.nb;
+    const int64_t want = std::max<int64_t>(1, 2048 / nblk);
+    const int64_t most = std::max<int64_t>(1, ncols / 512);  // at least 512 columns per chunk
+    int64_t nch = std::min(want, most);
+    p.chunk = ((ncols + nch - 1) / nch + 31) / 32 * 32;
+    p.nchunks = (ncols + p.chunk - 1) / p.chunk;
+    p.lanes = p.nchunks >= 32 ? 64 : 1;
+    return p;
+}
+
+// Waves per (pair, block) for the non-causal kernels: enough waves in flight for the
+// memory system, never more than the block has tiles.
+int waves_per_unit(int64_t units, int64_t ntiles) {
+    int w = 1;
+    while (w < 4 && 2 * w <= ntiles && units * w < 8192) w *= 2;
+    return w;
+}
+
+constexpr int64_t align64(int64_t x) { return (x + 63) / 64 * 64; }
+
+struct BwdLayout {
+    int64_t S, St, dSt, dS, Wt, G, dWdiag, part, total;  // float offsets
+};
+
+BwdLayout bwd_layout(int64_t BH, int64_t N, int D, int64_t M, bool causal) {
+    const int64_t L = (int64_t)D * D + D;
+    const int64_t arr = align64(M * BH * L);
+    const DwPlan p = dw_plan(BH * L, M);
+    BwdLayout o;
+    o.S = 0;
+    o.St = o.S + arr;
+    o.dSt = o.St + arr;
+    o.dS = o.dSt + arr;
+    o.Wt = o.dS + arr;
+    o.G = o.Wt + align64(M * M);
+    o.dWdiag = o.G + (causal ? align64(2 * BH * N) : 0);
+    o.part = o.dWdiag + align64(BH * M);
+    o.total = o.part + align64(p.nchunks * M * M);
+    return o;
+}
+
+template <int D, typename T>
+hipError_t run_backward(const T* q, const T* k, const T* v, const float* W, const float* dy, float* dq, float* dk,
+                        float* dv, float* dW, int64_t BH, int64_t N, int64_t M, bool causal, float* ws,
+                        void* frag_ws, hipStream_t stream) {
+    constexpr int L = D * D + D;
+    const BwdLayout o = bwd_layout(BH, N, D, M, causal);
+    float *S = ws + o.S, *St = ws + o.St, *dSt = ws + o.dSt, *dS = ws + o.dS, *Wt = ws + o.Wt;
+    float *G = ws + o.G, *dWdiag = ws + o.dWdiag, *part = ws + o.part;
+    const int64_t units = BH * M, C = N / M, ntiles = (C + 15) / 16;
+    const int wpu = waves_per_unit(units, ntiles);
+    const size_t red = (size_t)(wpu / 2) * L * sizeof(float);
+    const dim3 grid((unsigned)units), block(64 * wpu), one(64);
+    hipError_t e;
+    bwd_sum_kernel<D, T><<<grid, block, red, stream>>>(k, v, S, BH, (int)N, (int)M, wpu);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch_mix(S, W, St, BH, D, M, causal, false, 0, frag_ws, stream)) != hipSuccess) return e;
+    if (causal)
+        bwd_query_causal_kernel<D, T><<<grid, one, 0, stream>>>(q, k, v, dy, W, St, dq, dSt, G, dWdiag, BH, (int)N,
+                                                                (int)M);
+    else
+        bwd_query_kernel<D, T><<<grid, block, red, stream>>>(q, dy, St, dq, dSt, BH, (int)N, (int)M, wpu);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    bwd_wt_kernel<<<dim3((unsigned)((M * M + 255) / 256)), dim3(256), 0, stream>>>(W, Wt, (int)M, causal);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch_mix(dSt, Wt, dS, BH, D, M, false, false, 0, frag_ws, stream)) != hipSuccess) return e;
+    if (causal)
+        bwd_key_causal_kernel<D, T><<<grid, one, 0, stream>>>(q, k, v, dy, W, G, dS, dk, dv, BH, (int)N, (int)M);
+    else
+        bwd_key_kernel<D, T><<<grid, block, 0, stream>>>(k, v, dS, dk, dv, BH, (int)N, (int)M, wpu);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const DwPlan p = dw_plan(BH * L, M);
+    bwd_dw_kernel<<<dim3((unsigned)(p.nchunks * p.nb * p.nb)), dim3(256), 0, stream>>>(dSt, S, part, BH * L, (int)M,
+                                                                                      p.chunk, p.nb);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t threads = M * M * p.lanes;
+    bwd_dw_reduce_kernel<<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream>>>(
+        part, dWdiag, dW, (int)M, p.nchunks, BH, causal ? 1 : 0, p.lanes);
+    return hipGetLastError();
+}
+
+}  // namespace
 
 hipError_t launch_backward(int dtype, const void* q, const void* k, const void* v, const float* W, const float* dy,
                            float* dq, float* dk, float* dv, float* dW, int64_t BH, int64_t N, int D, int64_t M,
                            bool causal, float* ws, void* frag_ws, hipStream_t stream) {
-    const int64_t L = (int64_t)D * D + D;
-    const int64_t arr = M * BH * L;
-    float* S = ws;
-    float* St = S + arr;
-    float* dSt = St + arr;
-    float* dS = dSt + arr;
-    float* Wt = dS + arr;
-    float* G = Wt + M * M;                        // causal: dnum, dden per token
-    float* dWdiag = G + (causal ? BH * N * (D + 1) : 0);
-    float* part = dWdiag + BH * M;
-    const int64_t ncols = BH * L;
-    const int64_t chunk = (int64_t)backward_dw_chunk(ncols);
-    const int64_t nchunks = (ncols + chunk - 1) / chunk;
-    const int ntiles = (int)(((M + 15) / 16) * ((M + 15) / 16));
-    const dim3 units((unsigned)(BH * M)), block(256);
-    hipError_t e;
-#define MHLA_BWD_D(T, DD)                                                                                        \
-    do {                                                                                                         \
-        const T* qq = (const T*)q;                                                                               \
-        const T* kk = (const T*)k;                                                                               \
-        const T* vv = (const T*)v;                                                                               \
-        bwd_summary_kernel<DD, T><<<units, block, 0, stream>>>(kk, vv, S, BH, (int)N, (int)M);                  \
-        if ((e = hipGetLastError()) != hipSuccess) return e;                                                     \
-        if ((e = launch_mix(S, W, St, BH, DD, M, causal, false, 0, frag_ws, stream)) != hipSuccess) return e;       \
-        if (causal)                                                                                              \
-            bwd_query_kernel<DD, T, true><<<units, block, 0, stream>>>(qq, kk, vv, dy, W, St, dSt, G, dq, dk, dv, \
-                                                                       dWdiag, BH, (int)N, (int)M);              \
-        else                                                                                                     \
-            bwd_query_kernel<DD, T, false><<<units, block, 0, stream>>>(qq, kk, vv, dy, W, St, dSt, G, dq, dk,    \
-                                                                        dv, dWdiag, BH, (int)N, (int)M);         \
-        if ((e = hipGetLastError()) != hipSuccess) return e;                                                     \
-        bwd_wt_kernel<<<dim3((unsigned)((M * M + 255) / 256)), block, 0, stream>>>(W, Wt, (int)M, causal);      \
-        if ((e = hipGetLastError()) != hipSuccess) return e;                                                     \
-        if ((e = launch_mix(dSt, Wt, dS, BH, DD, M, false, false, 0, frag_ws, stream)) != hipSuccess) return e;     \
-        if (causal)                                                                                              \
-            bwd_key_kernel<DD, T, true><<<units, block, 0, stream>>>(kk, vv, dS, dk, dv, BH, (int)N, (int)M);   \
-        else                                                                                                     \
-            bwd_key_kernel<DD, T, false><<<units, block, 0, stream>>>(kk, vv, dS, dk, dv, BH, (int)N, (int)M);  \
-        if ((e = hipGetLastError()) != hipSuccess) return e;                                                     \
-    } while (0)
-#define MHLA_BWD(T)                         \
-    switch (D) {                            \
-        case 16: MHLA_BWD_D(T, 16); break;  \
-        case 32: MHLA_BWD_D(T, 32); break;  \
-        case 64: MHLA_BWD_D(T, 64); break;  \
-        default: return hipErrorInvalidValue; \
+#define MHLA_BWD(T)                                                                                             \
+    switch (D) {                                                                                                \
+        case 16:                                                                                                \
+            return run_backward<16, T>((const T*)q, (const T*)k, (const T*)v, W, dy, dq, dk, dv, dW, BH, N, M,  \
+                                       causal, ws, frag_ws, stream);                                            \
+        case 32:                                                                                                \
+            return run_backward<32, T>((const T*)q, (const T*)k, (const T*)v, W, dy, dq, dk, dv, dW, BH, N, M,  \
+                                       causal, ws, frag_ws, stream);                                            \
+        case 64:                                                                                                \
+            return run_backward<64, T>((const T*)q, (const T*)k, (const T*)v, W, dy, dq, dk, dv, dW, BH, N, M,  \
+                                       causal, ws, frag_ws, stream);                                            \
+        default:                                                                                                \
+            return hipErrorInvalidValue;                                                                        \
     }
     if (dtype == kDtypeF32) {
         MHLA_BWD(float);
@@ -471,21 +1027,10 @@ hipError_t launch_backward(int dtype, const void* q, const void* k, const void* 
         MHLA_BWD(uint16_t);
     }
 #undef MHLA_BWD
-#undef MHLA_BWD_D
-    bwd_dw_partial_kernel<<<dim3((unsigned)(nchunks * ntiles)), block, 0, stream>>>(dSt, S, part, ncols, (int)M, chunk,
-                                                                                    ntiles);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    bwd_dw_reduce_kernel<<<dim3((unsigned)((M * M + 255) / 256)), block, 0, stream>>>(part, dWdiag, dW, (int)M, nchunks,
-                                                                                      BH, causal ? 1 : 0);
-    return hipGetLastError();
 }
 
 size_t backward_workspace_floats(int64_t BH, int64_t N, int D, int64_t M, bool causal) {
-    const int64_t L = (int64_t)D * D + D;
-    const int64_t ncols = BH * L;
-    const int64_t chunk = (int64_t)backward_dw_chunk(ncols);
-    const int64_t nchunks = (ncols + chunk - 1) / chunk;
-    return (size_t)(4 * M * BH * L + M * M + (causal ? BH * N * (D + 1) : 0) + BH * M + nchunks * M * M);
+    return (size_t)bwd_layout(BH, N, D, M, causal).total;
 }
 
 }  // namespace mhla
