@@ -41,7 +41,8 @@
 // bwd_query_kernel / bwd_query_causal_kernel produce dq and dS~^T, dz~ (causal: also
 // per-token den, dden and the diagonal part of dW); the mixing GEMM with W^T forms dS;
 // bwd_key_kernel / bwd_key_causal_kernel produce dk, dv; bwd_dw_kernel and
-// bwd_dw_reduce_kernel form dW as a split-K MFMA GEMM with a fixed-order reduction.
+// bwd_dw_reduce1_kernel / bwd_dw_reduce_kernel form dW as a split-K MFMA GEMM with a
+// two-level fixed-order reduction.
 // Non-causal kernels spread a block's tiles over up to four waves of one workgroup
 // (partial sums added in LDS in a fixed order); causal kernels walk a block's tiles
 // in order (queries) or in reverse (keys) in one wave, carrying the running summary.
@@ -209,6 +210,29 @@ __device__ __forceinline__ void gemm_rl(const bf16x8 (&ah)[KS], const bf16x8 (&a
         }
 }
 
+// gemm_rl with the B operands built from packed float32 chunks of X one (k-step,
+// column block) at a time, so that no full split copy of X is live.
+template <int P, int KS, bool ALO>
+__device__ __forceinline__ void gemm_packed(const bf16x8 (&ah)[KS], const bf16x8 (&al)[KS], const f32x4 (&ch)[P * P],
+                                            f32x4 (&acc)[P]) {
+#pragma unroll
+    for (int jb = 0; jb < P; ++jb)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            bf16x8 bh, bl;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int f = 8 * ks + e;
+                const bf16pair h = split_bf16(f < 4 * P ? ch[(f % P) * P + jb][f / P] : 0.f);
+                bh[e] = h.hi;
+                bl[e] = h.lo;
+            }
+            acc[jb] = mfma32(ah[ks], bh, acc[jb]);
+            acc[jb] = mfma32(ah[ks], bl, acc[jb]);
+            if constexpr (ALO) acc[jb] = mfma32(al[ks], bh, acc[jb]);
+        }
+}
+
 // acc (packed chunks of X) += sum over the tile's tokens of a_t b_t^T, X[r][c] with
 // r from the A side and c from the B side (both in dot layout).
 template <int P, bool ALO>
@@ -339,7 +363,7 @@ __global__ __launch_bounds__(256) void bwd_sum_kernel(const T* __restrict__ K, c
 
 // dq and dS~_i^T, dz~_i for one (pair, block i) per workgroup of wpu waves (non-causal).
 template <int D, typename T>
-__global__ __launch_bounds__(256) void bwd_query_kernel(const T* __restrict__ Q, const float* __restrict__ dY,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_query_kernel(const T* __restrict__ Q, const float* __restrict__ dY,
                                                         const float* __restrict__ St, float* __restrict__ dQ,
                                                         float* __restrict__ dSt, int64_t BH, int N, int M, int wpu) {
     using Dm = Dim<D>;
@@ -424,7 +448,7 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(const T* __restrict__ Q,
 // dk, dv for one (pair, key block b) from dS_b^T, dz_b (non-causal); waves of the
 // workgroup take the block's tiles in turn.
 template <int D, typename T>
-__global__ __launch_bounds__(256) void bwd_key_kernel(const T* __restrict__ K, const T* __restrict__ V,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_key_kernel(const T* __restrict__ K, const T* __restrict__ V,
                                                       const float* __restrict__ dS, float* __restrict__ dK,
                                                       float* __restrict__ dV, int64_t BH, int N, int M, int wpu) {
     using Dm = Dim<D>;
@@ -732,13 +756,8 @@ __global__ __launch_bounds__(64) void bwd_key_causal_kernel(
         f32x4 a1[P], a2[P];
 #pragma unroll
         for (int b = 0; b < P; ++b) a1[b] = a2[b] = zero4();
-        {
-            bf16x8 sh[KS][P], sl[KS][P];
-            packed_b<P, KS>(s1, sh, sl);
-            gemm_rl<P, KS, VLO>(vh, vl, sh, sl, a1);
-            packed_b<P, KS>(s2, sh, sl);
-            gemm_rl<P, KS, true>(kh, kl, sh, sl, a2);
-        }
+        gemm_packed<P, KS, VLO>(vh, vl, s1, a1);
+        gemm_packed<P, KS, true>(kh, kl, s2, a2);
         // scores: lane (g, n) holds t = 4g + e, j = n, kept for t >= j, times W_bb
         f32x4 sc = zero4(), gg = zero4();
         {
@@ -822,60 +841,78 @@ __global__ __launch_bounds__(256) void bwd_wt_kernel(const float* __restrict__ W
 
 // dW partials: part[ch][i][b] = sum over columns of chunk ch of dSt[i][col] S[b][col],
 // one 64 x 64 output block per workgroup (wave w: rows 16w .. 16w + 15), on MFMA
-// with hi + lo operands.  ncols and chunk are multiples of 8.
+// with hi + lo operands.  ncols and chunk are multiples of 8.  Each step's loads are
+// issued one step ahead (unconditional loads: a column or row out of range reads a
+// valid address and is masked to zero).
+struct DwRun {  // 8 consecutive floats of one row, loaded ahead; masked when used
+    f32x4 x[2];
+    bool ok;
+};
+
+__device__ __forceinline__ void dw_load(const float* X, int64_t ncols, int row, int M, int64_t k, int64_t k1,
+                                        DwRun& r) {
+    r.ok = row < M && k < k1;
+    const f32x4* p = reinterpret_cast<const f32x4*>(X + (r.ok ? (int64_t)row * ncols + k : 0));
+    r.x[0] = p[0];
+    r.x[1] = p[1];
+}
+
+__device__ __forceinline__ void dw_split(const DwRun& r, bf16x8& hi, bf16x8& lo) {
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float a = r.ok ? r.x[e >> 1][2 * (e & 1)] : 0.f, b = r.ok ? r.x[e >> 1][2 * (e & 1) + 1] : 0.f;
+        split2_bf16(a, b, h[e], l[e]);
+    }
+    hi = __builtin_bit_cast(bf16x8, u32x4{h[0], h[1], h[2], h[3]});
+    lo = __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], l[2], l[3]});
+}
+
 __global__ __launch_bounds__(256) void bwd_dw_kernel(const float* __restrict__ dSt, const float* __restrict__ S,
                                                      float* __restrict__ part, int64_t ncols, int M, int64_t chunk,
-                                                     int nb) {
+                                                     int nb, int rt) {
+    // rt row tiles of 16 per workgroup (min(4, ceil(M / 16))); the 4 / rt wave slots
+    // left over take consecutive column chunks of their own.
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, n = lane & 15;
     const int ob = (int)(blockIdx.x % (nb * nb));
-    const int64_t ch = blockIdx.x / (nb * nb);
-    const int i0 = 64 * (ob / nb) + 16 * wave, b0 = 64 * (ob % nb);
+    const int64_t ch = (blockIdx.x / (nb * nb)) * (4 / rt) + wave / rt;
+    const int i0 = 64 * (ob / nb) + 16 * (wave % rt), b0 = 64 * (ob % nb);
+    const int jt = min(4, (M - b0 + 15) / 16);  // column tiles of this block
     const int64_t k0 = ch * chunk, k1 = min(ncols, k0 + chunk);
-    const int ai = i0 + n;
     f32x4 acc[4];
 #pragma unroll
     for (int jb = 0; jb < 4; ++jb) acc[jb] = zero4();
-    if (i0 < M) {
-        for (int64_t k = k0 + 8 * g; k < k1 + 8 * g; k += 32) {
-            const bool kok = k < k1;
-            float a[8];
-            {
-                const bool ok = kok && ai < M;
-                const f32x4* p = reinterpret_cast<const f32x4*>(dSt + (ok ? (int64_t)ai * ncols + k : 0));
-                const f32x4 x0 = ok ? p[0] : zero4(), x1 = ok ? p[1] : zero4();
+    if (i0 < M && k0 < ncols) {
+        const int nsteps = (int)((k1 - k0 + 31) / 32);
+        DwRun xa, xb[4];
+        int64_t k = k0 + 8 * g;
+        dw_load(dSt, ncols, i0 + n, M, k, k1, xa);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    a[e] = x0[e];
-                    a[4 + e] = x1[e];
+        for (int jb = 0; jb < 4; ++jb)
+            if (jb < jt) dw_load(S, ncols, b0 + 16 * jb + n, M, k, k1, xb[jb]);
+        for (int st = 0; st < nsteps; ++st) {
+            bf16x8 ah, al, bh[4], bl[4];
+            dw_split(xa, ah, al);
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb)
+                if (jb < jt) dw_split(xb[jb], bh[jb], bl[jb]);
+            k += 32;
+            dw_load(dSt, ncols, i0 + n, M, k, k1, xa);
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb)
+                if (jb < jt) dw_load(S, ncols, b0 + 16 * jb + n, M, k, k1, xb[jb]);
+            issue_fence();
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb)
+                if (jb < jt) {
+                    acc[jb] = mfma32(ah, bh[jb], acc[jb]);
+                    acc[jb] = mfma32(ah, bl[jb], acc[jb]);
+                    acc[jb] = mfma32(al, bh[jb], acc[jb]);
                 }
-            }
-            bf16x8 ah, al;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const bf16pair h = split_bf16(a[e]);
-                ah[e] = h.hi;
-                al[e] = h.lo;
-            }
-#pragma unroll
-            for (int jb = 0; jb < 4; ++jb) {
-                const int bi = b0 + 16 * jb + n;
-                const bool ok = kok && bi < M;
-                const f32x4* p = reinterpret_cast<const f32x4*>(S + (ok ? (int64_t)bi * ncols + k : 0));
-                const f32x4 x0 = ok ? p[0] : zero4(), x1 = ok ? p[1] : zero4();
-                bf16x8 bh, bl;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const bf16pair h = split_bf16(e < 4 ? x0[e] : x1[e - 4]);
-                    bh[e] = h.hi;
-                    bl[e] = h.lo;
-                }
-                acc[jb] = mfma32(ah, bh, acc[jb]);
-                acc[jb] = mfma32(ah, bl, acc[jb]);
-                acc[jb] = mfma32(al, bh, acc[jb]);
-            }
         }
     }
+    if (k0 >= ncols) return;
 #pragma unroll
     for (int jb = 0; jb < 4; ++jb)
 #pragma unroll
@@ -885,49 +922,72 @@ __global__ __launch_bounds__(256) void bwd_dw_kernel(const float* __restrict__ d
         }
 }
 
-// dW[i][b] = sum over chunks (fixed order); causal: b < i only, plus the diagonal
-// from the per-pair partials.  `lanes` (1 or 64) consecutive lanes share an output:
-// lane l adds chunks (and pairs) l, l + lanes, ...; the lanes then combine in a
-// fixed butterfly order.
-__global__ __launch_bounds__(256) void bwd_dw_reduce_kernel(const float* __restrict__ part,
+// First reduction level: part2[s][x] = sum of part[ch][x] over chunks ch of group s
+// (cps chunks per group), in chunk order; consecutive threads take consecutive x.
+__global__ __launch_bounds__(256) void bwd_dw_reduce1_kernel(const float* __restrict__ part,
+                                                             float* __restrict__ part2, int64_t MM, int64_t nchunks,
+                                                             int64_t cps, int64_t ngroups) {
+    const int64_t x = (int64_t)(blockIdx.x % ngroups) * 256 + threadIdx.x;
+    const int64_t s = blockIdx.x / ngroups;
+    if (x >= MM) return;
+    const int64_t c0 = s * cps, c1 = min(nchunks, c0 + cps);
+    float acc = 0.f;
+#pragma unroll 8
+    for (int64_t c = c0; c < c1; ++c) acc += part[c * MM + x];
+    part2[s * MM + x] = acc;
+}
+
+// dW[i][b] = sum of the first-level sums in group order; causal: b < i only, plus the
+// diagonal from the per-pair partials (in pair order).
+__global__ __launch_bounds__(256) void bwd_dw_reduce_kernel(const float* __restrict__ part2,
                                                             const float* __restrict__ dWdiag, float* __restrict__ dW,
-                                                            int M, int64_t nchunks, int64_t BH, int causal, int lanes) {
-    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t x = tid / lanes;
-    const int l = (int)(tid % lanes);
-    const bool live = x < (int64_t)M * M;
-    const int i = live ? (int)(x / M) : 0, b = live ? (int)(x % M) : 0;
+                                                            int M, int64_t nsplit, int64_t BH, int causal) {
+    const int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (x >= (int64_t)M * M) return;
+    const int i = (int)(x / M), b = (int)(x % M);
     float s = 0.f;
-    if (live && (!causal || b < i))
-        for (int64_t ch = l; ch < nchunks; ch += lanes) s += part[ch * M * M + x];
-    if (live && causal && b == i)
-        for (int64_t p = l; p < BH; p += lanes) s += dWdiag[p * M + i];
-    if (lanes == 64) {
-#pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m, 64);
+    if (!causal || b < i) {
+#pragma unroll 8
+        for (int64_t p = 0; p < nsplit; ++p) s += part2[p * M * M + x];
     }
-    if (live && l == 0) dW[x] = s;
+    if (causal && b == i) {
+#pragma unroll 8
+        for (int64_t p = 0; p < BH; ++p) s += dWdiag[p * M + i];
+    }
+    dW[x] = s;
 }
 
 namespace {
 
 struct DwPlan {
     int nb;           // 64 x 64 output blocks per dimension
+    int rt;           // row tiles of 16 per workgroup; 4 / rt chunks per workgroup
     int64_t chunk;    // columns per partial
     int64_t nchunks;
-    int lanes;        // lanes per output in the reduction
+    int64_t cps;      // chunks per first-level reduction group
+    int64_t nsplit;   // first-level groups
 };
 
 DwPlan dw_plan(int64_t ncols, int64_t M) {
     DwPlan p;
     p.nb = (int)((M + 63) / 64);
+    p.rt = (int)std::min<int64_t>(4, (M + 15) / 16);
+    if (p.rt == 3) p.rt = 4;
+    const int64_t subs = 4 / p.rt;
     const int64_t nblk = (int64_t)p.nb * p.nb;
-    const int64_t want = std::max<int64_t>(1, 2048 / nblk);
-    const int64_t most = std::max<int64_t>(1, ncols / 512);  // at least 512 columns per chunk
-    int64_t nch = std::min(want, most);
+    const int64_t want = std::max<int64_t>(1, 2048 / nblk) * subs;  // partials (one per wave slot)
+    const int64_t most = std::max<int64_t>(1, ncols / 512);         // at least 512 columns per partial
+    const int64_t nch = std::min(want, most);
     p.chunk = ((ncols + nch - 1) / nch + 31) / 32 * 32;
     p.nchunks = (ncols + p.chunk - 1) / p.chunk;
-    p.lanes = p.nchunks >= 32 ? 64 : 1;
+    // first level: up to 2048 workgroups, and about sqrt(nchunks) groups so that
+    // neither level sums a long run per thread
+    const int64_t groups = (M * M + 255) / 256;
+    int64_t root = 1;
+    while (root * root < p.nchunks) ++root;
+    const int64_t split = std::max<int64_t>(1, std::min<int64_t>(root, 2048 / groups));
+    p.cps = (p.nchunks + split - 1) / split;
+    p.nsplit = (p.nchunks + p.cps - 1) / p.cps;
     return p;
 }
 
@@ -942,7 +1002,7 @@ int waves_per_unit(int64_t units, int64_t ntiles) {
 constexpr int64_t align64(int64_t x) { return (x + 63) / 64 * 64; }
 
 struct BwdLayout {
-    int64_t S, St, dSt, dS, Wt, G, dWdiag, part, total;  // float offsets
+    int64_t S, St, dSt, dS, Wt, G, dWdiag, part, part2, total;  // float offsets
 };
 
 BwdLayout bwd_layout(int64_t BH, int64_t N, int D, int64_t M, bool causal) {
@@ -958,7 +1018,8 @@ BwdLayout bwd_layout(int64_t BH, int64_t N, int D, int64_t M, bool causal) {
     o.G = o.Wt + align64(M * M);
     o.dWdiag = o.G + (causal ? align64(2 * BH * N) : 0);
     o.part = o.dWdiag + align64(BH * M);
-    o.total = o.part + align64(p.nchunks * M * M);
+    o.part2 = o.part + align64(p.nchunks * M * M);
+    o.total = o.part2 + align64(p.nsplit * M * M);
     return o;
 }
 
@@ -969,7 +1030,7 @@ hipError_t run_backward(const T* q, const T* k, const T* v, const float* W, cons
     constexpr int L = D * D + D;
     const BwdLayout o = bwd_layout(BH, N, D, M, causal);
     float *S = ws + o.S, *St = ws + o.St, *dSt = ws + o.dSt, *dS = ws + o.dS, *Wt = ws + o.Wt;
-    float *G = ws + o.G, *dWdiag = ws + o.dWdiag, *part = ws + o.part;
+    float *G = ws + o.G, *dWdiag = ws + o.dWdiag, *part = ws + o.part, *part2 = ws + o.part2;
     const int64_t units = BH * M, C = N / M, ntiles = (C + 15) / 16;
     const int wpu = waves_per_unit(units, ntiles);
     const size_t red = (size_t)(wpu / 2) * L * sizeof(float);
@@ -993,12 +1054,17 @@ hipError_t run_backward(const T* q, const T* k, const T* v, const float* W, cons
         bwd_key_kernel<D, T><<<grid, block, 0, stream>>>(k, v, dS, dk, dv, BH, (int)N, (int)M, wpu);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const DwPlan p = dw_plan(BH * L, M);
-    bwd_dw_kernel<<<dim3((unsigned)(p.nchunks * p.nb * p.nb)), dim3(256), 0, stream>>>(dSt, S, part, BH * L, (int)M,
-                                                                                      p.chunk, p.nb);
+    const int64_t subs = 4 / p.rt;
+    bwd_dw_kernel<<<dim3((unsigned)((p.nchunks + subs - 1) / subs * p.nb * p.nb)), dim3(256), 0, stream>>>(
+        dSt, S, part, BH * L, (int)M, p.chunk, p.nb, p.rt);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const int64_t threads = M * M * p.lanes;
-    bwd_dw_reduce_kernel<<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream>>>(
-        part, dWdiag, dW, (int)M, p.nchunks, BH, causal ? 1 : 0, p.lanes);
+    const int64_t groups = (M * M + 255) / 256;
+    bwd_dw_reduce1_kernel<<<dim3((unsigned)(groups * p.nsplit)), dim3(256), 0, stream>>>(part, part2, M * M,
+                                                                                        p.nchunks, p.cps, groups);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    bwd_dw_reduce_kernel<<<dim3((unsigned)((M * M + 255) / 256)), dim3(256), 0, stream>>>(part2, dWdiag, dW, (int)M,
+                                                                                         p.nsplit, BH,
+                                                                                         causal ? 1 : 0);
     return hipGetLastError();
 }
 
