@@ -24,7 +24,7 @@
 // Precision: every product runs on bf16 MFMA with both operands split into hi + lo
 // bf16 parts (three products; two when an operand is an exact bf16 input), with
 // float32 accumulation in a fixed order -- about 16 significant bits per operand and
-// bit-reproducible results.  phi uses the full-precision exp.
+// bit-reproducible results.  phi and the reciprocals use the hardware exp2 and rcp.
 //
 // Tiles are 16 tokens.  Two register layouts of a tile are used (lane l, g = l / 16,
 // n = l % 16, d = 16P, FL = 4P):
@@ -135,64 +135,80 @@ __device__ __forceinline__ void store_dl(rsrc_t r, int g, int n, int i, const fl
     store_run<P>(r, (uint32_t)(((4 * g + i) * D + P * n) * 4), x);
 }
 
-// phi(x) = ELU(x) + 1 and its derivative.
+// phi(x) = ELU(x) + 1 = max(x, 0) + exp(min(x, 0)) and its derivative, with the
+// hardware exp2 (relative error about |x| 2^-24 + 1 ulp, far inside what the split
+// products keep).
+__device__ __forceinline__ float bexp(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
+__device__ __forceinline__ float phi_b(float x) { return fmaxf(x, 0.f) + bexp(fminf(x, 0.f)); }
 __device__ __forceinline__ float phi_grad(float x, float& dphi) {
-    const float e = expf(fminf(x, 0.f));
+    const float e = bexp(fminf(x, 0.f));
     dphi = x > 0.f ? 1.f : e;
     return fmaxf(x, 0.f) + e;
 }
 
-// Row-layout values as 16x16x32 operands (slot 8ks + e = group-local feature).
+// Row-layout values as 16x16x32 operands (slot 8ks + e = group-local feature); the
+// hi + lo split is done two values at a time (split2_bf16).
 template <int FL, int KS>
 __device__ __forceinline__ void split_rl(const float (&x)[FL], bf16x8 (&hi)[KS], bf16x8 (&lo)[KS]) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+    for (int ks = 0; ks < KS; ++ks) {
+        uint32_t h[4], l[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int f = 8 * ks + e;
-            const bf16pair h = split_bf16(f < FL ? x[f < FL ? f : 0] : 0.f);
-            hi[ks][e] = h.hi;
-            lo[ks][e] = h.lo;
+        for (int e = 0; e < 4; ++e) {
+            const int f = 8 * ks + 2 * e;
+            if (f < FL) {
+                split2_bf16(x[f], x[f + 1], h[e], l[e]);
+            } else {
+                h[e] = l[e] = 0u;
+            }
         }
+        hi[ks] = __builtin_bit_cast(bf16x8, u32x4{h[0], h[1], h[2], h[3]});
+        lo[ks] = __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], l[2], l[3]});
+    }
+}
+
+__device__ __forceinline__ void split4(float a, float b, float c, float d, bf16x4& hi, bf16x4& lo) {
+    uint32_t h0, l0, h1, l1;
+    split2_bf16(a, b, h0, l0);
+    split2_bf16(c, d, h1, l1);
+    hi = __builtin_bit_cast(bf16x4, u32x2{h0, h1});
+    lo = __builtin_bit_cast(bf16x4, u32x2{l0, l1});
 }
 
 // Dot-layout values as 16x16x16 operands, one per feature block.
 template <int P>
 __device__ __forceinline__ void split_dl(const float (&x)[4][P], bf16x4 (&hi)[P], bf16x4 (&lo)[P]) {
 #pragma unroll
-    for (int b = 0; b < P; ++b)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const bf16pair h = split_bf16(x[e][b]);
-            hi[b][e] = h.hi;
-            lo[b][e] = h.lo;
-        }
+    for (int b = 0; b < P; ++b) split4(x[0][b], x[1][b], x[2][b], x[3][b], hi[b], lo[b]);
 }
 
-__device__ __forceinline__ void split4(const f32x4& x, bf16x4& hi, bf16x4& lo) {
+__device__ __forceinline__ void split4(const f32x4& x, bf16x4& hi, bf16x4& lo) { split4(x[0], x[1], x[2], x[3], hi, lo); }
+
+// The 8 B-operand slots of k-step ks, column block jb, from packed chunks of X: slot
+// (ks, e) is X[FL*g + 8ks + e][P*n + jb], held in chunk (f % P, jb) at position f / P.
+template <int P>
+__device__ __forceinline__ void packed_slots(const f32x4 (&ch)[P * P], int ks, int jb, bf16x8& bh, bf16x8& bl) {
+    uint32_t h[4], l[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        const bf16pair h = split_bf16(x[e]);
-        hi[e] = h.hi;
-        lo[e] = h.lo;
+        const int f = 8 * ks + 2 * e;
+        if (f < 4 * P) {
+            split2_bf16(ch[(f % P) * P + jb][f / P], ch[((f + 1) % P) * P + jb][(f + 1) / P], h[e], l[e]);
+        } else {
+            h[e] = l[e] = 0u;
+        }
     }
+    bh = __builtin_bit_cast(bf16x8, u32x4{h[0], h[1], h[2], h[3]});
+    bl = __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], l[2], l[3]});
 }
 
-// B operands from packed chunks of X: slot (ks, e) of column block jb is
-// X[FL*g + 8ks + e][P*n + jb], held in chunk (f % P, jb) at position f / P.
+// B operands from packed chunks of X (all k-steps and column blocks).
 template <int P, int KS>
 __device__ __forceinline__ void packed_b(const f32x4 (&ch)[P * P], bf16x8 (&bh)[KS][P], bf16x8 (&bl)[KS][P]) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int jb = 0; jb < P; ++jb)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int f = 8 * ks + e;
-                const bf16pair h = split_bf16(f < 4 * P ? ch[(f % P) * P + jb][f / P] : 0.f);
-                bh[ks][jb][e] = h.hi;
-                bl[ks][jb][e] = h.lo;
-            }
+        for (int jb = 0; jb < P; ++jb) packed_slots<P>(ch, ks, jb, bh[ks][jb], bl[ks][jb]);
 }
 
 // acc[jb] += A (row layout, tokens along m) x X (packed B operands), column block jb
@@ -220,13 +236,7 @@ __device__ __forceinline__ void gemm_packed(const bf16x8 (&ah)[KS], const bf16x8
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             bf16x8 bh, bl;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int f = 8 * ks + e;
-                const bf16pair h = split_bf16(f < 4 * P ? ch[(f % P) * P + jb][f / P] : 0.f);
-                bh[e] = h.hi;
-                bl[e] = h.lo;
-            }
+            packed_slots<P>(ch, ks, jb, bh, bl);
             acc[jb] = mfma32(ah[ks], bh, acc[jb]);
             acc[jb] = mfma32(ah[ks], bl, acc[jb]);
             if constexpr (ALO) acc[jb] = mfma32(al[ks], bh, acc[jb]);
@@ -347,7 +357,7 @@ __global__ __launch_bounds__(256) void bwd_sum_kernel(const T* __restrict__ K, c
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int b = 0; b < P; ++b) {
-                kx[i][b] = 4 * g + i < rows ? phi_precise(kx[i][b]) : 0.f;
+                kx[i][b] = 4 * g + i < rows ? phi_b(kx[i][b]) : 0.f;
                 z[b] += kx[i][b];
             }
         bf16x4 kh[P], kl[P], vh[P], vl[P];
@@ -420,7 +430,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
             }
             den = sum16(den) + kEps;
             dyn = sum16(dyn);
-            const float rden = 1.f / den;
+            const float rden = fast_rcp(den);
             dden[i] = -dyn * rden * rden;
             float out[P];
 #pragma unroll
@@ -484,7 +494,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
         load_rl<T, D>(rk, g, n, kr);
         load_dl<T, D>(rk, g, n, kd);
 #pragma unroll
-        for (int f = 0; f < FL; ++f) kr[f] = phi_precise(kr[f]);
+        for (int f = 0; f < FL; ++f) kr[f] = phi_b(kr[f]);
         bf16x8 vh[KS], vl[KS], kh[KS], kl[KS];
         split_rl<FL, KS>(vr, vh, vl);
         split_rl<FL, KS>(kr, kh, kl);
@@ -509,19 +519,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
     }
 }
 
-// Causal, one wave per (pair, query block i), tiles in order.  Besides dq and
-// dS~_i^T, dz~_i it keeps (den_t, dden_t) per token for the key pass and writes the
-// block's part of dW[i,i].  The running summary of the block's earlier tiles is held
-// transposed (P^T, packed) next to the constant S~_i^T; inside a tile the masked
-// scores (v_j . dy_t, j <= t) carry the rest of P_t dy_t.
-template <int D, typename T>
-__global__ __launch_bounds__(64) void bwd_query_causal_kernel(
-    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const float* __restrict__ dY,
-    const float* __restrict__ W, const float* __restrict__ St, float* __restrict__ dQ, float* __restrict__ dSt,
-    float* __restrict__ G, float* __restrict__ dWdiag, int64_t BH, int N, int M) {
+// Causal, CP waves per (pair, query block i) (CP = 2 for d >= 32, else 1), tiles in
+// order.  Wave w owns the feature blocks b = w*P/CP .. (w+1)*P/CP - 1 (features P*n + b
+// of lane n): those columns of U_t = A_t dy_t and dq, those columns of the running
+// P^T of the earlier tiles, of dS~_i^T and of dz~_i.  The per-row sums over all
+// features (den_t, phi(q_t).U_t and the within-block parts that dW[i,i] needs) are
+// formed from the waves' partial sums, exchanged through LDS (one barrier per tile,
+// double-buffered, added in wave order).  The constant S~_i^T is split once into
+// per-lane B operands kept in LDS.  Inside a tile the masked scores (v_j . dy_t,
+// j <= t) carry the rest of P_t dy_t.  Wave 0 also stores (den_t, dden_t) per token
+// for the key pass and the block's part of dW[i,i].
+template <int D>
+struct QcShared {
+    static constexpr int P = D / 16, KS = D >= 32 ? D / 32 : 1, CP = P >= 2 ? 2 : 1, PH = P / CP;
+    u32x4 sb[2 * KS * PH][CP][64];  // S~_i B operands of each wave's column blocks
+    float xch[2][CP][4][16];        // [tile parity][wave][quantity][row]
+};
+
+// The body of wave w (a template parameter, so that the owned blocks index registers
+// statically).
+template <int D, typename T, int w>
+__device__ __forceinline__ void query_causal_wave(const T* __restrict__ Q, const T* __restrict__ K,
+                                                  const T* __restrict__ V, const float* __restrict__ dY,
+                                                  const float* __restrict__ W, const float* __restrict__ St,
+                                                  float* __restrict__ dQ, float* __restrict__ dSt,
+                                                  float* __restrict__ G, float* __restrict__ dWdiag, int64_t BH,
+                                                  int N, int M, QcShared<D>& sh) {
     using Dm = Dim<D>;
     constexpr int P = Dm::P, FL = Dm::FL, KS = Dm::KS, L = Dm::L;
+    constexpr int CP = QcShared<D>::CP, PH = QcShared<D>::PH;
     constexpr bool VLO = !std::is_same<T, uint16_t>::value;
+    auto& sb = sh.sb;
+    auto& xch = sh.xch;
     const int lane = threadIdx.x & 63;
     const int g = lane >> 4, n = lane & 15;
     const int64_t unit = blockIdx.x, pair = unit / M;
@@ -529,49 +558,81 @@ __global__ __launch_bounds__(64) void bwd_query_causal_kernel(
     const int64_t row0 = pair * N + (int64_t)blk * C;
     const int ntiles = (C + 15) / 16;
     const float wii = W[(int64_t)blk * M + blk];
+    constexpr int b0 = w * PH;  // first owned feature block
 
     const float* sv = St + ((int64_t)blk * BH + pair) * L;
-    bf16x8 bh[KS][P], bl[KS][P];  // S~_i as B[k = c][col = r]
-    float zt[P];
+    float zt[PH];
     {
         f32x4 ch[P * P];
         load_packed<P>(sv, lane, ch);
-        packed_b<P, KS>(ch, bh, bl);
 #pragma unroll
-        for (int b = 0; b < P; ++b) zt[b] = sv[D * D + P * n + b];
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int j = 0; j < PH; ++j) {
+                bf16x8 h, l;
+                packed_slots<P>(ch, ks, b0 + j, h, l);
+                sb[2 * (ks * PH + j)][w][lane] = __builtin_bit_cast(u32x4, h);
+                sb[2 * (ks * PH + j) + 1][w][lane] = __builtin_bit_cast(u32x4, l);
+            }
+#pragma unroll
+        for (int j = 0; j < PH; ++j) zt[j] = sv[D * D + P * n + b0 + j];
     }
-    f32x4 pt[P * P], acc[P * P];  // running P^T of the earlier tiles; dS~_i^T
-    float pz[P], zacc[P], dwl = 0.f;
+    f32x4 pt[P * PH], acc[P * PH];  // chunks (ia, b0 + j) at [ia * PH + j]
+    float pz[PH], zacc[PH], dwl = 0.f;
 #pragma unroll
-    for (int c = 0; c < P * P; ++c) pt[c] = acc[c] = zero4();
+    for (int c = 0; c < P * PH; ++c) pt[c] = acc[c] = zero4();
 #pragma unroll
-    for (int b = 0; b < P; ++b) pz[b] = zacc[b] = 0.f;
+    for (int j = 0; j < PH; ++j) pz[j] = zacc[j] = 0.f;
+    __syncthreads();
 
     for (int tile = 0; tile < ntiles; ++tile) {
         const int t0 = 16 * tile, rows = min(16, C - t0);
         const int64_t r0 = row0 + t0;
         const rsrc_t rq = tile_rsrc(Q, r0, rows, D), rk = tile_rsrc(K, r0, rows, D), rv = tile_rsrc(V, r0, rows, D);
-        const rsrc_t ry = tile_rsrc(dY, r0, rows, D), rdq = tile_rsrc(dQ, r0, rows, D);
-        const rsrc_t rg = tile_rsrc(G, r0, rows, 2);
-        float yr[FL], vr[FL], yd[4][P], vd[4][P], kd[4][P], qd[4][P];
+        const rsrc_t ry = tile_rsrc(dY, r0, rows, D);
+        float yr[FL], vr[FL], kd[4][P], qd[4][P];
         load_rl<float, D>(ry, g, n, yr);
         load_rl<T, D>(rv, g, n, vr);
-        load_dl<float, D>(ry, g, n, yd);
-        load_dl<T, D>(rv, g, n, vd);
         load_dl<T, D>(rk, g, n, kd);
         load_dl<T, D>(rq, g, n, qd);
 
         bf16x8 yh[KS], yl[KS];
         split_rl<FL, KS>(yr, yh, yl);
-        f32x4 ui[P], us[P];  // S~_i dy_t and P_{<tile} dy_t, dot layout
+        f32x4 ui[PH], us[PH];  // S~_i dy_t and P_t dy_t (owned columns), dot layout
 #pragma unroll
-        for (int b = 0; b < P; ++b) ui[b] = us[b] = zero4();
-        gemm_rl<P, KS, true>(yh, yl, bh, bl, ui);
-        {
-            bf16x8 sh[KS][P], sl[KS][P];
-            packed_b<P, KS>(pt, sh, sl);
-            gemm_rl<P, KS, true>(yh, yl, sh, sl, us);
-        }
+        for (int j = 0; j < PH; ++j) ui[j] = us[j] = zero4();
+#pragma unroll
+        for (int j = 0; j < PH; ++j)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 bh = __builtin_bit_cast(bf16x8, sb[2 * (ks * PH + j)][w][lane]);
+                const bf16x8 bl = __builtin_bit_cast(bf16x8, sb[2 * (ks * PH + j) + 1][w][lane]);
+                ui[j] = mfma32(yh[ks], bh, ui[j]);
+                ui[j] = mfma32(yh[ks], bl, ui[j]);
+                ui[j] = mfma32(yl[ks], bh, ui[j]);
+            }
+        // P_{<tile} dy_t: B slot (ks, e) of column block b0 + j is P^T[FL g + 8ks + e][P n + b0 + j],
+        // held in chunk ((8ks + e) % P, b0 + j) at position (8ks + e) / P
+#pragma unroll
+        for (int j = 0; j < PH; ++j)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                uint32_t h[4], l[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int f = 8 * ks + 2 * e;
+                    if (f < FL) {
+                        split2_bf16(pt[(f % P) * PH + j][f / P], pt[((f + 1) % P) * PH + j][(f + 1) / P], h[e], l[e]);
+                    } else {
+                        h[e] = l[e] = 0u;
+                    }
+                }
+                const bf16x8 bh = __builtin_bit_cast(bf16x8, u32x4{h[0], h[1], h[2], h[3]});
+                const bf16x8 bl = __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], l[2], l[3]});
+                us[j] = mfma32(yh[ks], bh, us[j]);
+                us[j] = mfma32(yh[ks], bl, us[j]);
+                us[j] = mfma32(yl[ks], bh, us[j]);
+            }
         // scores v_j . dy_t: lane (g, n) holds j = 4g + e, t = n, kept for j <= t
         f32x4 gy = zero4();
         {
@@ -590,28 +651,28 @@ __global__ __launch_bounds__(64) void bwd_query_causal_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int b = 0; b < P; ++b) fk[i][b] = 4 * g + i < rows ? phi_precise(kd[i][b]) : 0.f;
+            for (int b = 0; b < P; ++b) fk[i][b] = 4 * g + i < rows ? phi_b(kd[i][b]) : 0.f;
         bf16x4 kh[P], kl[P];
         split_dl<P>(fk, kh, kl);
         {
             bf16x4 gh, gl;
             split4(gy, gh, gl);
 #pragma unroll
-            for (int b = 0; b < P; ++b) {  // us += sum_{j <= t in tile} (v_j . dy_t) phi(k_j)
-                us[b] = mfma16(gh, kh[b], us[b]);
-                us[b] = mfma16(gh, kl[b], us[b]);
-                us[b] = mfma16(gl, kh[b], us[b]);
+            for (int j = 0; j < PH; ++j) {  // us += sum_{j' <= t in tile} (v_j' . dy_t) phi(k_j')
+                us[j] = mfma16(gh, kh[b0 + j], us[j]);
+                us[j] = mfma16(gh, kl[b0 + j], us[j]);
+                us[j] = mfma16(gl, kh[b0 + j], us[j]);
             }
         }
-        // p_t = the block's phi(k) sum up to and including t (dot layout)
-        float pin[4][P];
+        // p_t = the block's phi(k) sum up to and including t (owned features)
+        float pin[4][PH];
 #pragma unroll
-        for (int b = 0; b < P; ++b) {
+        for (int j = 0; j < PH; ++j) {
             float run = 0.f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                run += fk[i][b];
-                pin[i][b] = run;
+                run += fk[i][b0 + j];
+                pin[i][j] = run;
             }
             float excl = 0.f;
 #pragma unroll
@@ -620,82 +681,153 @@ __global__ __launch_bounds__(64) void bwd_query_causal_kernel(
                 excl += h < g ? t : 0.f;
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) pin[i][b] += pz[b] + excl;
-            pz[b] += sum_over_groups(run);
+            for (int i = 0; i < 4; ++i) pin[i][j] += pz[j] + excl;
+            pz[j] += sum_over_groups(run);
         }
 
-        float fq[4][P], dp[4][P], dn[4][P], dden[4];
+        // per-row partial sums over the owned features, exchanged between the waves
+        float fq[4][PH], dp[4][PH], part[4][4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             float den = 0.f, idn = 0.f, dyn = 0.f, idy = 0.f;
-            float a[P];
 #pragma unroll
-            for (int b = 0; b < P; ++b) {
-                fq[i][b] = phi_grad(qd[i][b], dp[i][b]);
-                a[b] = fmaf(wii, pin[i][b], zt[b]);
-                const float uu = fmaf(wii, us[b][i], ui[b][i]);
-                den = fmaf(fq[i][b], a[b], den);
-                idn = fmaf(fq[i][b], pin[i][b], idn);
-                dyn = fmaf(fq[i][b], uu, dyn);
-                idy = fmaf(fq[i][b], us[b][i], idy);
+            for (int j = 0; j < PH; ++j) {
+                fq[i][j] = phi_grad(qd[i][b0 + j], dp[i][j]);
+                const float a = fmaf(wii, pin[i][j], zt[j]);
+                const float uu = fmaf(wii, us[j][i], ui[j][i]);
+                den = fmaf(fq[i][j], a, den);
+                idn = fmaf(fq[i][j], pin[i][j], idn);
+                dyn = fmaf(fq[i][j], uu, dyn);
+                idy = fmaf(fq[i][j], us[j][i], idy);
             }
-            den = sum16(den) + kEps;
-            idn = sum16(idn);
-            dyn = sum16(dyn);
-            idy = sum16(idy);
-            const float rden = 1.f / den;
-            dden[i] = -dyn * rden * rden;
-            float out[P];
+            part[0][i] = sum16(den);
+            part[1][i] = sum16(idn);
+            part[2][i] = sum16(dyn);
+            part[3][i] = sum16(idy);
+        }
+        float tot[4][4];
+        if constexpr (CP == 2) {
+            float(*x)[4][16] = xch[tile & 1];
+            if (n == 0)
 #pragma unroll
-            for (int b = 0; b < P; ++b) {
-                const float uu = fmaf(wii, us[b][i], ui[b][i]);
-                out[b] = fmaf(uu, rden, dden[i] * a[b]) * dp[i][b];
-                dn[i][b] = yd[i][b] * rden;
+                for (int qn = 0; qn < 4; ++qn)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) x[w][qn][4 * g + i] = part[qn][i];
+            __syncthreads();
+#pragma unroll
+            for (int qn = 0; qn < 4; ++qn)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) tot[qn][i] = x[0][qn][4 * g + i] + x[1][qn][4 * g + i];
+        } else {
+#pragma unroll
+            for (int qn = 0; qn < 4; ++qn)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) tot[qn][i] = part[qn][i];
+        }
+        const rsrc_t rdq = tile_rsrc(dQ, r0, rows, D), rg = tile_rsrc(G, r0, rows, 2);
+        float yd[4][P], dn[4][P], dden[4];
+        load_dl<float, D>(ry, g, n, yd);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float den = tot[0][i] + kEps;
+            const float rden = fast_rcp(den);
+            dden[i] = -tot[2][i] * rden * rden;
+            float out[PH];
+#pragma unroll
+            for (int j = 0; j < PH; ++j) {
+                const float a = fmaf(wii, pin[i][j], zt[j]);
+                const float uu = fmaf(wii, us[j][i], ui[j][i]);
+                out[j] = fmaf(uu, rden, dden[i] * a) * dp[i][j];
             }
-            store_dl<D>(rdq, g, n, i, out);
-            if (n == 0) {
-                dwl += fmaf(idy, rden, dden[i] * idn);
+#pragma unroll
+            for (int b = 0; b < P; ++b) dn[i][b] = yd[i][b] * rden;
+            store_run<PH>(rdq, (uint32_t)(((4 * g + i) * D + P * n + b0) * 4), out);
+            if (w == 0 && n == 0) {
+                dwl += fmaf(tot[3][i], rden, dden[i] * tot[1][i]);
                 const float gd[2] = {den, dden[i]};
                 store_run<2>(rg, (uint32_t)((4 * g + i) * 8), gd);
             }
         }
-        bf16x4 qh[P], ql[P];
-        split_dl<P>(fq, qh, ql);
-        {
+        {  // dS~^T chunks (ia, b0 + j) += dnum[c] phi(q)[r]
             bf16x4 nh[P], nl[P];
             split_dl<P>(dn, nh, nl);
-            acc_outer<P, true>(nh, nl, qh, ql, acc);
+#pragma unroll
+            for (int j = 0; j < PH; ++j) {
+                bf16x4 qh, ql;
+                split4(fq[0][j], fq[1][j], fq[2][j], fq[3][j], qh, ql);
+#pragma unroll
+                for (int ia = 0; ia < P; ++ia) {
+                    f32x4 c = acc[ia * PH + j];
+                    c = mfma16(nh[ia], qh, c);
+                    c = mfma16(nh[ia], ql, c);
+                    c = mfma16(nl[ia], qh, c);
+                    acc[ia * PH + j] = c;
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) zacc[j] = fmaf(dden[i], fq[i][j], zacc[j]);
+            }
         }
-#pragma unroll
-        for (int b = 0; b < P; ++b)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) zacc[b] = fmaf(dden[i], fq[i][b], zacc[b]);
-        {  // P^T += v^T phi(k) over this tile
+        {  // P^T chunks (ia, b0 + j) += v[c] phi(k)[r] over this tile
+            float vd[4][P];
+            load_dl<T, D>(rv, g, n, vd);
             bf16x4 vh[P], vl[P];
             split_dl<P>(vd, vh, vl);
-            acc_outer<P, VLO>(vh, vl, kh, kl, pt);
+#pragma unroll
+            for (int j = 0; j < PH; ++j)
+#pragma unroll
+                for (int ia = 0; ia < P; ++ia) {
+                    f32x4 c = pt[ia * PH + j];
+                    c = mfma16(vh[ia], kh[b0 + j], c);
+                    c = mfma16(vh[ia], kl[b0 + j], c);
+                    if constexpr (VLO) c = mfma16(vl[ia], kh[b0 + j], c);
+                    pt[ia * PH + j] = c;
+                }
         }
     }
+    float* out = dSt + ((int64_t)blk * BH + pair) * L;
 #pragma unroll
-    for (int b = 0; b < P; ++b) zacc[b] = sum_over_groups(zacc[b]);
-    store_packed<P>(dSt + ((int64_t)blk * BH + pair) * L, lane, g, n, acc, zacc);
-    dwl = sum_over_groups(sum16(dwl));
-    if (lane == 0) dWdiag[pair * M + blk] = dwl;
+    for (int ia = 0; ia < P; ++ia)
+#pragma unroll
+        for (int j = 0; j < PH; ++j)
+            *reinterpret_cast<f32x4*>(out + (ia * P + b0 + j) * 256 + lane * 4) = acc[ia * PH + j];
+#pragma unroll
+    for (int j = 0; j < PH; ++j) {
+        const float z = sum_over_groups(zacc[j]);
+        if (g == 0) out[D * D + P * n + b0 + j] = z;
+    }
+    if constexpr (w == 0) {
+        dwl = sum_over_groups(sum16(dwl));
+        if (lane == 0) dWdiag[pair * M + blk] = dwl;
+    }
 }
 
-// Causal, one wave per (pair, key block b), tiles in reverse order.  The running
-// (dS_b + W_bb R_{>tile}) is held in both orientations: rows c for d phi(k) (contracted
-// over c with v) and rows r for dv (contracted over r with phi(k)).  Inside a tile the
-// masked scores phi(q_t).phi(k_j) and dnum_t . v_j + dden_t (t >= j) carry the rest.
 template <int D, typename T>
-__global__ __launch_bounds__(64) void bwd_key_causal_kernel(
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void bwd_query_causal_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const float* __restrict__ dY,
+    const float* __restrict__ W, const float* __restrict__ St, float* __restrict__ dQ, float* __restrict__ dSt,
+    float* __restrict__ G, float* __restrict__ dWdiag, int64_t BH, int N, int M) {
+    __shared__ QcShared<D> sh;
+    if (threadIdx.x < 64)
+        query_causal_wave<D, T, 0>(Q, K, V, dY, W, St, dQ, dSt, G, dWdiag, BH, N, M, sh);
+    else if constexpr (QcShared<D>::CP == 2)
+        query_causal_wave<D, T, 1>(Q, K, V, dY, W, St, dQ, dSt, G, dWdiag, BH, N, M, sh);
+}
+
+// Causal, two waves per (pair, key block b), tiles in reverse order.  The running
+// dS_b + W_bb R_{>tile} is needed in two orientations: rows c for d phi(k) (contracted
+// over c with v) and rows r for dv (contracted over r with phi(k)).  Wave 0 keeps the
+// first and produces dk, wave 1 keeps the second and produces dv, each folding the
+// tile's W_bb phi(q) dnum^T into its own copy; inside a tile the masked scores
+// dnum_t . v_j + dden_t (wave 0) and phi(q_t).phi(k_j) (wave 1), t >= j, carry the rest.
+template <int D, typename T>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void bwd_key_causal_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const float* __restrict__ dY,
     const float* __restrict__ W, const float* __restrict__ G, const float* __restrict__ dS, float* __restrict__ dK,
     float* __restrict__ dV, int64_t BH, int N, int M) {
     using Dm = Dim<D>;
     constexpr int P = Dm::P, FL = Dm::FL, KS = Dm::KS, L = Dm::L;
     constexpr bool VLO = !std::is_same<T, uint16_t>::value;
-    const int lane = threadIdx.x & 63;
+    const int lane = threadIdx.x & 63, role = threadIdx.x >> 6;
     const int g = lane >> 4, n = lane & 15;
     const int64_t unit = blockIdx.x, pair = unit / M;
     const int blk = (int)(unit % M), C = N / M;
@@ -704,113 +836,137 @@ __global__ __launch_bounds__(64) void bwd_key_causal_kernel(
     const float wbb = W[(int64_t)blk * M + blk];
 
     const float* sv = dS + ((int64_t)blk * BH + pair) * L;
-    f32x4 s1[P * P], s2[P * P];  // rows c (= dS^T + W R^T), rows r (= dS + W R)
-    float s1z[P];
-    load_packed<P>(sv, lane, s1);
-    load_packed_t<P>(sv, g, n, s2);
+    f32x4 st[P * P];  // role 0: rows c (dS^T + W R^T); role 1: rows r (dS + W R)
+    float s1z[P];     // role 0: dz_b + W r
+    if (role == 0) {
+        load_packed<P>(sv, lane, st);
 #pragma unroll
-    for (int b = 0; b < P; ++b) s1z[b] = sv[D * D + P * n + b];
+        for (int b = 0; b < P; ++b) s1z[b] = sv[D * D + P * n + b];
+    } else {
+        load_packed_t<P>(sv, g, n, st);
+    }
 
     for (int tile = ntiles - 1; tile >= 0; --tile) {
         const int t0 = 16 * tile, rows = min(16, C - t0);
         const int64_t r0 = row0 + t0;
-        const rsrc_t rq = tile_rsrc(Q, r0, rows, D), rk = tile_rsrc(K, r0, rows, D), rv = tile_rsrc(V, r0, rows, D);
+        const rsrc_t rq = tile_rsrc(Q, r0, rows, D), rk = tile_rsrc(K, r0, rows, D);
         const rsrc_t ry = tile_rsrc(dY, r0, rows, D), rg = tile_rsrc(G, r0, rows, 2);
-        const rsrc_t rdk = tile_rsrc(dK, r0, rows, D), rdv = tile_rsrc(dV, r0, rows, D);
-        float vr[FL], kr[FL], qr[FL], yr[FL], kd[4][P], qd[4][P], yd[4][P];
-        load_rl<T, D>(rv, g, n, vr);
-        load_rl<T, D>(rk, g, n, kr);
-        load_rl<T, D>(rq, g, n, qr);
-        load_rl<float, D>(ry, g, n, yr);
-        load_dl<T, D>(rk, g, n, kd);
+        float qd[4][P], yd[4][P], gd[4][2];
         load_dl<T, D>(rq, g, n, qd);
         load_dl<float, D>(ry, g, n, yd);
-        float gn[2], gd[4][2];
-        load_run<float, 2>(rg, (uint32_t)(n * 8), gn);
 #pragma unroll
         for (int i = 0; i < 4; ++i) load_run<float, 2>(rg, (uint32_t)((4 * g + i) * 8), gd[i]);
-
-        // dnum in both layouts (rows past the block: zero)
-        const float rn = n < rows ? 1.f / gn[0] : 0.f;
+        float dden[4];
 #pragma unroll
-        for (int f = 0; f < FL; ++f) yr[f] *= rn;
-        float fqd[4][P], dden[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float ri = 4 * g + i < rows ? 1.f / gd[i][0] : 0.f;
+        for (int i = 0; i < 4; ++i) {  // dnum (dot layout; rows past the block: zero)
+            const float ri = 4 * g + i < rows ? fast_rcp(gd[i][0]) : 0.f;
             dden[i] = gd[i][1];
 #pragma unroll
             for (int b = 0; b < P; ++b) {
                 yd[i][b] *= ri;
-                fqd[i][b] = phi_precise(qd[i][b]);
+                qd[i][b] = phi_b(qd[i][b]);
             }
         }
+        bf16x4 qdh[P], qdl[P];
+        split_dl<P>(qd, qdh, qdl);
+        f32x4 a[P];
 #pragma unroll
-        for (int f = 0; f < FL; ++f) {
-            kr[f] = phi_precise(kr[f]);
-            qr[f] = phi_precise(qr[f]);
-        }
-        bf16x8 vh[KS], vl[KS], kh[KS], kl[KS];
-        split_rl<FL, KS>(vr, vh, vl);
-        split_rl<FL, KS>(kr, kh, kl);
-        f32x4 a1[P], a2[P];
+        for (int b = 0; b < P; ++b) a[b] = zero4();
+        if (role == 0) {
+            // d phi(k_j) = (dS + W R_{>tile}) v_j + dz + W r + W sum_{t >= j} (dnum_t . v_j + dden_t) phi(q_t)
+            const rsrc_t rv = tile_rsrc(V, r0, rows, D), rdk = tile_rsrc(dK, r0, rows, D);
+            float vr[FL], yr[FL], kd[4][P], gn[2];
+            load_rl<T, D>(rv, g, n, vr);
+            load_rl<float, D>(ry, g, n, yr);
+            load_dl<T, D>(rk, g, n, kd);
+            load_run<float, 2>(rg, (uint32_t)(n * 8), gn);
+            const float rn = n < rows ? fast_rcp(gn[0]) : 0.f;
 #pragma unroll
-        for (int b = 0; b < P; ++b) a1[b] = a2[b] = zero4();
-        gemm_packed<P, KS, VLO>(vh, vl, s1, a1);
-        gemm_packed<P, KS, true>(kh, kl, s2, a2);
-        // scores: lane (g, n) holds t = 4g + e, j = n, kept for t >= j, times W_bb
-        f32x4 sc = zero4(), gg = zero4();
-        {
-            bf16x8 qh[KS], ql[KS], nh[KS], nl[KS];
-            split_rl<FL, KS>(qr, qh, ql);
-            split_rl<FL, KS>(yr, nh, nl);
+            for (int f = 0; f < FL; ++f) yr[f] *= rn;
+            bf16x8 vh[KS], vl[KS];
+            split_rl<FL, KS>(vr, vh, vl);
+            gemm_packed<P, KS, VLO>(vh, vl, st, a);
+            f32x4 gg = zero4();  // lane (g, n): t = 4g + e, j = n
+            {
+                bf16x8 nh[KS], nl[KS];
+                split_rl<FL, KS>(yr, nh, nl);
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                sc = mfma32(qh[ks], kh[ks], sc);
-                sc = mfma32(qh[ks], kl[ks], sc);
-                sc = mfma32(ql[ks], kh[ks], sc);
-                gg = mfma32(nh[ks], vh[ks], gg);
-                gg = mfma32(nl[ks], vh[ks], gg);
-                if constexpr (VLO) gg = mfma32(nh[ks], vl[ks], gg);
+                for (int ks = 0; ks < KS; ++ks) {
+                    gg = mfma32(nh[ks], vh[ks], gg);
+                    gg = mfma32(nl[ks], vh[ks], gg);
+                    if constexpr (VLO) gg = mfma32(nh[ks], vl[ks], gg);
+                }
             }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const bool keep = 4 * g + e >= n;
-                sc[e] = keep ? wbb * sc[e] : 0.f;
-                gg[e] = keep ? wbb * (gg[e] + dden[e]) : 0.f;
+            for (int e = 0; e < 4; ++e) gg[e] = 4 * g + e >= n ? wbb * (gg[e] + dden[e]) : 0.f;
+            {
+                bf16x4 gh, gl;
+                split4(gg, gh, gl);
+#pragma unroll
+                for (int b = 0; b < P; ++b) {
+                    a[b] = mfma16(gh, qdh[b], a[b]);
+                    a[b] = mfma16(gh, qdl[b], a[b]);
+                    a[b] = mfma16(gl, qdh[b], a[b]);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float o[P];
+#pragma unroll
+                for (int b = 0; b < P; ++b) {
+                    float dp;
+                    phi_grad(kd[i][b], dp);
+                    o[b] = (a[b][i] + s1z[b]) * dp;
+                }
+                store_dl<D>(rdk, g, n, i, o);
+            }
+        } else {
+            // dv_j = (dS + W R_{>tile})^T phi(k_j) + W sum_{t >= j} (phi(q_t) . phi(k_j)) dnum_t
+            const rsrc_t rdv = tile_rsrc(dV, r0, rows, D);
+            float kr[FL], qr[FL];
+            load_rl<T, D>(rk, g, n, kr);
+            load_rl<T, D>(rq, g, n, qr);
+#pragma unroll
+            for (int f = 0; f < FL; ++f) {
+                kr[f] = phi_b(kr[f]);
+                qr[f] = phi_b(qr[f]);
+            }
+            bf16x8 kh[KS], kl[KS];
+            split_rl<FL, KS>(kr, kh, kl);
+            gemm_packed<P, KS, true>(kh, kl, st, a);
+            f32x4 sc = zero4();  // lane (g, n): t = 4g + e, j = n
+            {
+                bf16x8 qh[KS], ql[KS];
+                split_rl<FL, KS>(qr, qh, ql);
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    sc = mfma32(qh[ks], kh[ks], sc);
+                    sc = mfma32(qh[ks], kl[ks], sc);
+                    sc = mfma32(ql[ks], kh[ks], sc);
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sc[e] = 4 * g + e >= n ? wbb * sc[e] : 0.f;
+            {
+                bf16x4 ndh[P], ndl[P], sh, sl;
+                split_dl<P>(yd, ndh, ndl);
+                split4(sc, sh, sl);
+#pragma unroll
+                for (int b = 0; b < P; ++b) {
+                    a[b] = mfma16(sh, ndh[b], a[b]);
+                    a[b] = mfma16(sh, ndl[b], a[b]);
+                    a[b] = mfma16(sl, ndh[b], a[b]);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float o[P];
+#pragma unroll
+                for (int b = 0; b < P; ++b) o[b] = a[b][i];
+                store_dl<D>(rdv, g, n, i, o);
             }
         }
-        bf16x4 qdh[P], qdl[P], ndh[P], ndl[P];
-        split_dl<P>(fqd, qdh, qdl);
-        split_dl<P>(yd, ndh, ndl);
-        {
-            bf16x4 sch, scl, ggh, ggl;
-            split4(sc, sch, scl);
-            split4(gg, ggh, ggl);
-#pragma unroll
-            for (int b = 0; b < P; ++b) {
-                a1[b] = mfma16(ggh, qdh[b], a1[b]);
-                a1[b] = mfma16(ggh, qdl[b], a1[b]);
-                a1[b] = mfma16(ggl, qdh[b], a1[b]);
-                a2[b] = mfma16(sch, ndh[b], a2[b]);
-                a2[b] = mfma16(sch, ndl[b], a2[b]);
-                a2[b] = mfma16(scl, ndh[b], a2[b]);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float ok[P], ov[P];
-#pragma unroll
-            for (int b = 0; b < P; ++b) {
-                float dp;
-                phi_grad(kd[i][b], dp);
-                ok[b] = (a1[b][i] + s1z[b]) * dp;
-                ov[b] = a2[b][i];
-            }
-            store_dl<D>(rdk, g, n, i, ok);
-            store_dl<D>(rdv, g, n, i, ov);
-        }
-        // fold this tile into the running sums, times W_bb
+        // fold this tile into the running sum, times W_bb
         float wdn[4][P];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -818,14 +974,17 @@ __global__ __launch_bounds__(64) void bwd_key_causal_kernel(
             for (int b = 0; b < P; ++b) wdn[i][b] = wbb * yd[i][b];
         bf16x4 wh[P], wl[P];
         split_dl<P>(wdn, wh, wl);
-        acc_outer<P, true>(wh, wl, qdh, qdl, s1);  // rows c: dnum[c] phi(q)[r]
-        acc_outer<P, true>(qdh, qdl, wh, wl, s2);  // rows r: phi(q)[r] dnum[c]
+        if (role == 0) {
+            acc_outer<P, true>(wh, wl, qdh, qdl, st);  // rows c: dnum[c] phi(q)[r]
 #pragma unroll
-        for (int b = 0; b < P; ++b) {
-            float s = 0.f;
+            for (int b = 0; b < P; ++b) {
+                float z = 0.f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) s = fmaf(dden[i], fqd[i][b], s);
-            s1z[b] = fmaf(wbb, sum_over_groups(s), s1z[b]);
+                for (int i = 0; i < 4; ++i) z = fmaf(dden[i], qd[i][b], z);
+                s1z[b] = fmaf(wbb, sum_over_groups(z), s1z[b]);
+            }
+        } else {
+            acc_outer<P, true>(qdh, qdl, wh, wl, st);  // rows r: phi(q)[r] dnum[c]
         }
     }
 }
@@ -1040,8 +1199,8 @@ hipError_t run_backward(const T* q, const T* k, const T* v, const float* W, cons
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = launch_mix(S, W, St, BH, D, M, causal, false, 0, frag_ws, stream)) != hipSuccess) return e;
     if (causal)
-        bwd_query_causal_kernel<D, T><<<grid, one, 0, stream>>>(q, k, v, dy, W, St, dq, dSt, G, dWdiag, BH, (int)N,
-                                                                (int)M);
+        bwd_query_causal_kernel<D, T><<<grid, dim3(D >= 32 ? 128 : 64), 0, stream>>>(q, k, v, dy, W, St, dq, dSt, G,
+                                                                                     dWdiag, BH, (int)N, (int)M);
     else
         bwd_query_kernel<D, T><<<grid, block, red, stream>>>(q, dy, St, dq, dSt, BH, (int)N, (int)M, wpu);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1049,7 +1208,8 @@ hipError_t run_backward(const T* q, const T* k, const T* v, const float* W, cons
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = launch_mix(dSt, Wt, dS, BH, D, M, false, false, 0, frag_ws, stream)) != hipSuccess) return e;
     if (causal)
-        bwd_key_causal_kernel<D, T><<<grid, one, 0, stream>>>(q, k, v, dy, W, G, dS, dk, dv, BH, (int)N, (int)M);
+        bwd_key_causal_kernel<D, T><<<grid, dim3(128), 0, stream>>>(q, k, v, dy, W, G, dS, dk, dv, BH, (int)N,
+                                                                      (int)M);
     else
         bwd_key_kernel<D, T><<<grid, block, 0, stream>>>(k, v, dS, dk, dv, BH, (int)N, (int)M, wpu);
     if ((e = hipGetLastError()) != hipSuccess) return e;
