@@ -211,8 +211,10 @@ int mhla_output(const void* q, const void* k, const void* v, int dtype, const fl
  *
  * q, k, v: [B][H][N][d] (dtype MHLA_DTYPE_BF16 or _F32); W [M][M] float32;
  * dy, dq, dk, dv: [B][H][N][d] float32; dW: [M][M] float32.  Outputs are
- * overwritten (not accumulated).  All arithmetic is float32 on the exact input
- * values, in a fixed order (bit-reproducible).  Workspace of
+ * overwritten (not accumulated).  Every product runs on bf16 matrix cores with
+ * both operands split into bf16 hi + lo parts (about 16 significant bits each;
+ * exact bf16 inputs enter unsplit), accumulated in float32 in a fixed order
+ * (bit-reproducible); phi uses the hardware exp2.  Workspace of
  * mhla_backward_workspace_bytes() bytes comes from the library's stream-ordered
  * pool, as for mhla_forward.  Outputs must not overlap each other or an input.
  */

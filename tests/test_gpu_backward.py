@@ -1,9 +1,8 @@
 """GPU parity of the backward pass against the float64 backward oracle.
 
-mhla_backward computes dq, dk, dv, dW in float32 on the exact input values
-(the recomputed summaries are mixed with bf16 hi/lo products, about 16
-significant bits per operand), so the bar is max|dX - dX_ref| / max|dX_ref| <=
-1e-4 for every gradient; the oracle (oracle/backward.py) is pinned by finite
+mhla_backward forms every product on bf16 MFMA with both operands split into
+hi + lo parts (about 16 significant bits per operand) and float32 accumulation,
+so the bar is max|dX - dX_ref| / max|dX_ref| <= 1e-4 for every gradient; the oracle (oracle/backward.py) is pinned by finite
 differences of the explicit O(N^2) definition.
 """
 import sys
