@@ -14,7 +14,8 @@
 // One workgroup of four waves owns one block.  Before a single barrier the waves
 // split S~_i into bf16 hi + lo MFMA operands in LDS and each wave applies phi to
 // the keys of its own tiles (tile t belongs to wave t mod 8 < 4 ? t mod 4 : 7 - t
-// mod 8, which balances the triangular work) and leaves them in LDS.  Then each
+// mod 8, which balances the triangular work) and leaves them in LDS, together with
+// the tiles' V rows already packed as score x V operands.  Then each
 // wave, for each of its query tiles t:
 //   * numerator phi(Q_t) S~_i (16x16x32 MFMAs, hi and lo) and denominator
 //     phi(Q_t) z~_i (an MFMA whose B columns all equal z~_i);
@@ -106,7 +107,7 @@ __device__ __forceinline__ void split8(const float (&x)[8], bf16x8& hi, bf16x8& 
 size_t causal_quad_lds_bytes(int D, int64_t C) {
     const int P = D / 16, KS = D >= 32 ? D / 32 : 1;
     const int64_t T = (C + 15) / 16;
-    return (size_t)(2 * KS * P + T * KS) * 64 * 16;
+    return (size_t)(2 * KS * P + T * KS) * 64 * 16 + (size_t)T * P * 64 * 8;
 }
 
 bool causal_quad_applicable(int64_t C) { return C <= 16 * kQuadMaxTiles; }
@@ -134,6 +135,7 @@ __global__ __launch_bounds__(256) void output_causal_quad_kernel(const uint16_t*
     const int blk = (int)(unit % M);
     const int C = N / M;
     const int T = (C + 15) / 16;
+    u32x2* vbuf = reinterpret_cast<u32x2*>(kb + T * KS * 64);  // [T][P][64]: V operand halves per key tile
     const int bstart = blk * C;
     const float wii = pair_w(W, pair, heads, M)[(int64_t)blk * M + blk];
     const float* sv = St + ((int64_t)blk * BH + summary_row(pair, heads, BH)) * L;
@@ -171,6 +173,33 @@ __global__ __launch_bounds__(256) void output_causal_quad_kernel(const uint16_t*
             phi_operand<P, KS>(kraw, ok, ak);
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) kb[(t * KS + ks) * 64 + lane] = __builtin_bit_cast(uint4, ak[ks]);
+            // V of keys 4g + e (e < 4) of tile t, value columns P n + jb, packed per column
+            // block as the four bf16 of one half of the score x V B operand.
+            uint32_t vr[4][P == 4 ? 2 : 1];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = 16 * t + 4 * g + e;
+                const uint32_t off = off_if(row < C, ((uint32_t)(bstart + row) * D + P * n) * 2);
+                if constexpr (P == 4) {
+                    const u32x2 x = buf_load64<NT>(rV, off);
+                    vr[e][0] = x.x;
+                    vr[e][1] = x.y;
+                } else if constexpr (P == 2) {
+                    vr[e][0] = buf_load32<NT>(rV, off);
+                } else {
+                    vr[e][0] = buf_load16<NT>(rV, off);
+                }
+            }
+#pragma unroll
+            for (int jb = 0; jb < P; ++jb) {
+                uint32_t hv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t word = vr[e][jb / 2];
+                    hv[e] = (P > 1 && (jb & 1)) ? word >> 16 : word & 0xffffu;
+                }
+                vbuf[(t * P + jb) * 64 + lane] = u32x2{hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16)};
+            }
         }
     }
     // z~ operand (every B column equal to z~), hi and lo.
@@ -246,37 +275,11 @@ __global__ __launch_bounds__(256) void output_causal_quad_kernel(const uint16_t*
             }
             bf16x8 ahi, alo;
             split8(a, ahi, alo);
-            // V rows of the 8 keys of this lane, P columns each (P n .. P n + P - 1).
-            uint32_t vr[8][P == 4 ? 2 : 1];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int row = 16 * (u + e / 4) + 4 * g + (e % 4);
-                const bool ok = (e < 4 || two) && row < C;
-                const uint32_t off = off_if(ok, ((uint32_t)(bstart + row) * D + P * n) * 2);
-                if constexpr (P == 4) {
-                    const u32x2 x = buf_load64<NT>(rV, off);
-                    vr[e][0] = x.x;
-                    vr[e][1] = x.y;
-                } else if constexpr (P == 2) {
-                    vr[e][0] = buf_load32<NT>(rV, off);
-                } else {
-                    vr[e][0] = buf_load16<NT>(rV, off);
-                }
-            }
-#pragma unroll
-            for (int jb = 0; jb < P; ++jb) {
-                uint32_t vb[4];
-#pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2) {
-                    uint32_t hv[2];
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const uint32_t word = vr[2 * e2 + h][jb / 2];
-                        hv[h] = (P > 1 && (jb & 1)) ? word >> 16 : word & 0xffffu;
-                    }
-                    vb[e2] = hv[0] | (hv[1] << 16);
-                }
-                const bf16x8 bv = __builtin_bit_cast(bf16x8, u32x4{vb[0], vb[1], vb[2], vb[3]});
+            for (int jb = 0; jb < P; ++jb) {  // V operand: keys of tile u, then of tile u + 1 (zero if absent)
+                const u32x2 v0 = vbuf[(u * P + jb) * 64 + lane];
+                const u32x2 v1 = two ? vbuf[((u + 1) * P + jb) * 64 + lane] : u32x2{0u, 0u};
+                const bf16x8 bv = __builtin_bit_cast(bf16x8, u32x4{v0.x, v0.y, v1.x, v1.y});
                 acc[jb] = mfma32(ahi, bv, acc[jb]);
                 acc[jb] = mfma32(alo, bv, acc[jb]);
             }
