@@ -8,11 +8,13 @@
 
 One step is one full forward pass (phi, block summaries, mixing, output) over
 the workload's synthetic batch, with inputs resident in HBM before the timed
-region.  Prints ONE JSON line with throughput (tokens/s), model TFLOP/s, the
-HBM roofline of the dominant kernel (its duration measured with HIP events on
-the launch stream: the whole step on the fused path, the stage inside a chain of
-summaries -> mixing -> output calls on the staged path) and the CPU oracle
-timed on this host's cores.
+region and the caches cold: before every call a read of 512 MiB (not timed)
+evicts L2 and the Infinity Cache; the step time is the median over K calls.
+Prints ONE JSON line with throughput (tokens/s), model TFLOP/s, the HBM roofline
+of the dominant kernel (its duration measured with HIP events on the launch
+stream: the whole step on the fused path, the stage inside a chain of
+summaries -> mixing -> output calls on the staged path) and the CPU oracle timed
+on this host's cores.  --warm adds back-to-back steps on cache-resident inputs.
 """
 import argparse
 import json
@@ -301,6 +303,8 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="time mhla_forward over the N x M grid of the paper's scaling study instead of one "
                          "workload; prints its own JSON line")
+    ap.add_argument("--warm", action="store_true",
+                    help="also time back-to-back steps on cache-resident inputs (reported under `warm`)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy (3x), the reference that scales "
                          "the FETCH_SIZE / WRITE_SIZE counters in counter-collection runs")
@@ -333,11 +337,6 @@ def main():
     path = mh.mhla_forward_path(w.B, w.H, w.N, w.d, w.M, w.causal,
                                 mh.MHLA_DTYPE_BF16 if w.dtype == "bf16" else mh.MHLA_DTYPE_F32)
 
-    # ---- whole-pass throughput ----
-    def run_steps(n):
-        for _ in range(n):
-            fwd(qd, kd, vd, Wd, out, causal=w.causal)
-
     def elapsed_ms(fn):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -347,35 +346,67 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1)
 
-    run_steps(args.warmup)
-    eager_ms = elapsed_ms(lambda: run_steps(args.steps)) / args.steps
-    # The timed steps run as one HIP graph replay (the launch-bound short workloads would
-    # otherwise measure the host).  The replayed output must equal the eager one bit for bit.
-    ref = out.clone()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        run_steps(args.steps)
-    out.zero_()
-    graph.replay()
+    # ---- whole-pass throughput, cold caches ----
+    # Before every call, timed or not, a pass over 512 MiB (not timed) evicts L2 and the
+    # 256 MiB Infinity Cache, so each step reads its inputs from HBM.  HIP events bracket
+    # the one call on its stream (the fill keeps the GPU busy while the host enqueues it);
+    # `ms_per_step` is the median over the K steps.
+    # The eviction pass reads 512 MiB (a sum), so it leaves only clean lines behind: a fill
+    # would leave up to 256 MiB of dirty lines whose write-back the next call would pay.
+    flush = torch.ones(1 << 27, dtype=torch.float32, device="cuda")
+
+    def evict():
+        flush.sum()
+
+    for _ in range(args.warmup):
+        evict()
+        fwd(qd, kd, vd, Wd, out, causal=w.causal)
+    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+    for e0, e1 in step_ev:
+        evict()
+        e0.record(stream)
+        fwd(qd, kd, vd, Wd, out, causal=w.causal)
+        e1.record(stream)
     torch.cuda.synchronize()
-    if not torch.equal(out, ref):
-        raise RuntimeError("graph replay of the forward pass differs from the eager result")
-    graph.replay()
-    graph_ms = elapsed_ms(graph.replay) / args.steps
-    # Both are whole steps on resident inputs; the graph wins when launches dominate,
-    # eager launches when the graph's workspace nodes cost more than the host does.
-    ms = min(graph_ms, eager_ms)
+    step_all = sorted(e0.elapsed_time(e1) for e0, e1 in step_ev)
+    ms = step_all[len(step_all) // 2]
     tokens_s = w.tokens / (ms * 1e-3)
     tflops = model_flops(w) / (ms * 1e-3) / 1e12
 
-    # ---- per-stage durations inside the chain: `steps` iterations of summaries -> mixing
-    # -> output on the launch stream, with HIP events between the stages.  Each stage
-    # consumes the previous one's output, as inside mhla_forward, so the caches hold what
-    # they would in a forward pass (timing a stage alone, repeated, would let the 256 MiB
-    # Infinity Cache keep its inputs).  When mhla_forward takes the fused path these
-    # stage timings are reported for reference only (`staged_kernels`); the step itself
-    # is the fused kernel. ----
-    stream = torch.cuda.current_stream()
+    # ---- optional: warm steps (back to back on the same, cache-resident inputs), as one
+    # HIP graph replay of K calls and as K eager launches; the replayed output must equal
+    # the eager output bit for bit. ----
+    warm = None
+    if args.warm:
+        def run_steps(n):
+            for _ in range(n):
+                fwd(qd, kd, vd, Wd, out, causal=w.causal)
+
+        run_steps(args.warmup)
+        eager_ms = elapsed_ms(lambda: run_steps(args.steps)) / args.steps
+        ref = out.clone()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            run_steps(args.steps)
+        out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(out, ref):
+            raise RuntimeError("graph replay of the forward pass differs from the eager result")
+        graph.replay()
+        graph_ms = elapsed_ms(graph.replay) / args.steps
+        wms = min(graph_ms, eager_ms)
+        warm = {"ms_per_step": round(wms, 5), "value": round(w.tokens / (wms * 1e-3), 1),
+                "graph_ms_per_step": round(graph_ms, 5), "eager_ms_per_step": round(eager_ms, 5),
+                "timing": "K steps back to back on cache-resident inputs, faster of one HIP graph replay "
+                          "and K eager launches"}
+
+    # ---- per-stage durations: K chains of summaries -> mixing -> output (each stage
+    # consuming the previous one's result, as inside mhla_forward), each chain after a
+    # cache-evicting read, HIP events between the stages on the launch stream; median per
+    # stage.  When mhla_forward takes the fused path these are reported for reference only
+    # (`staged_kernels`); the step itself is the fused kernel. ----
     L = w.d * w.d + w.d
     S = torch.empty(w.M * w.B * w.H * L, dtype=torch.float32, device="cuda")
     St = torch.empty_like(S)
@@ -386,28 +417,31 @@ def main():
         lambda: mh.mhla_output(qd, kd, vd, St, Wd, out, causal=w.causal),
     ]
     for _ in range(args.warmup):
+        evict()
         for f in stages:
             f()
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     # A pre-roll of device fills keeps the GPU busy while the host enqueues the timed
-    # stages, so no host launch gap falls between two events.  `pre_done` still pending
+    # chains, so no host launch gap falls between two events.  `pre_done` still pending
     # once everything is enqueued shows that the GPU never waited for the host.
-    filler = torch.empty(1 << 26, dtype=torch.float32, device="cuda")
-    for _ in range(8 * args.steps):  # ~50 us of GPU work per fill, several per timed launch
-        filler.fill_(0.0)
+    for _ in range(2 * args.steps):
+        evict()
     pre_done = torch.cuda.Event()
     pre_done.record(stream)
     for it in range(args.steps):
+        evict()
         evs[it][0].record(stream)
         for j, f in enumerate(stages):
             f()
             evs[it][j + 1].record(stream)
     gapless = not pre_done.query()
     torch.cuda.synchronize()
-    del filler
-    kms = {name: sum(evs[it][j].elapsed_time(evs[it][j + 1]) for it in range(args.steps)) / args.steps
-           for j, name in enumerate(names)}
+    del flush
+    kms = {}
+    for j, name in enumerate(names):
+        d = sorted(evs[it][j].elapsed_time(evs[it][j + 1]) for it in range(args.steps))
+        kms[name] = d[len(d) // 2]
     kb = kernel_bytes(w)
 
     def entry(name, t_ms):
@@ -468,9 +502,10 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
-        "timing": "K steps as one HIP graph replay" if graph_ms <= eager_ms else "K eager launches",
-        "graph_ms_per_step": round(graph_ms, 5),
-        "eager_ms_per_step": round(eager_ms, 5),
+        "timing": "median of K single calls, each after a cache-evicting read of 512 MiB (not timed)",
+        "ms_min": round(step_all[0], 5),
+        "ms_max": round(step_all[-1], 5),
+        "warm": warm,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -482,7 +517,8 @@ def main():
         "path": "fused" if path == mh.MHLA_PATH_FUSED else "staged",
         "kernels": kernels,
         "staged_kernels": staged,
-        "stage_timing": "in chain, " + ("no host gaps" if gapless else "host gaps possible"),
+        "stage_timing": "medians of K chains, each after a cache-evicting read; "
+                        + ("no host gaps" if gapless else "host gaps possible"),
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
