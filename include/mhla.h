@@ -75,9 +75,12 @@ enum { MHLA_PATH_STAGED = 0, MHLA_PATH_FUSED = 1 };
  * causal != 0 selects the causal variant.  Two execution paths compute the same
  * four steps:
  *   - staged: the three stage kernels below (block summaries, mixing, output)
- *     through a stream-ordered workspace of mhla_workspace_bytes() bytes taken
- *     from a library-owned memory pool on the current device and returned to it
- *     (stream-ordered) before the call returns;
+ *     through a workspace of mhla_workspace_bytes() bytes.  The library keeps
+ *     one workspace per (device, stream) handle, shared by all calls on that
+ *     stream (they run in order) and grown from a library-owned memory pool when
+ *     a call needs more; an outgrown workspace is kept until the process ends, so
+ *     HIP graphs captured with it stay valid.  A call that needs no growth
+ *     allocates nothing and does not wait for the device;
  *   - fused (non-causal; M <= 16 blocks of at most 16 tokens, or N <= 256 in
  *     blocks of 32, 48 or 64 tokens): one workgroup per (batch, head) pair that
  *     keeps the block summaries and their mix in LDS; no workspace.
@@ -184,7 +187,7 @@ int mhla_block_summaries(const void* k, const void* v, int dtype, float* S,
  * use the packed layout of mhla_block_summaries; `precise` selects float32
  * products (used by the float32 path) instead of the bfloat16 hi/lo split
  * (three bfloat16 products per term, float32 accumulation).  The split W
- * fragments go to stream-ordered scratch from the library's memory pool.
+ * fragments go to the stream's workspace (as for mhla_forward).
  */
 int mhla_mix_summaries(const float* S, const float* W, float* St, int64_t BH, int64_t d, int64_t M,
                        int causal, int precise, mhla_stream_t stream);
@@ -215,8 +218,8 @@ int mhla_output(const void* q, const void* k, const void* v, int dtype, const fl
  * both operands split into bf16 hi + lo parts (about 16 significant bits each;
  * exact bf16 inputs enter unsplit), accumulated in float32 in a fixed order
  * (bit-reproducible); phi uses the hardware exp2.  Workspace of
- * mhla_backward_workspace_bytes() bytes comes from the library's stream-ordered
- * pool, as for mhla_forward.  Outputs must not overlap each other or an input.
+ * mhla_backward_workspace_bytes() bytes comes from the stream's workspace, as
+ * for mhla_forward.  Outputs must not overlap each other or an input.
  */
 int64_t mhla_backward_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int64_t M, int causal);
 

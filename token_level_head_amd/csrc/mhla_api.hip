@@ -6,6 +6,7 @@
 // the device.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -142,6 +143,60 @@ int pool_alloc(void** ptr, size_t bytes, hipStream_t stream) {
     return MHLA_OK;
 }
 
+// Workspace kept per (device, stream).  Calls on one stream run in order, so they can
+// share one buffer; a steady-state call then makes no allocation call at all (a
+// stream-ordered malloc/free pair per call made the host wait for the GPU on every
+// call on this runtime).  A call that needs more takes a larger buffer from the pool
+// (at least 1.5x the old one); the outgrown buffer is kept, not freed, so that HIP
+// graphs captured with it stay valid.  Calls on different streams use different
+// buffers.
+struct StreamWorkspace {
+    int dev;
+    hipStream_t stream;
+    void* ptr;
+    size_t bytes;
+};
+struct WorkspaceCache {
+    std::mutex mu;
+    std::vector<StreamWorkspace> live;
+    std::vector<void*> retired;
+};
+WorkspaceCache& workspace_cache() {
+    static WorkspaceCache c;
+    return c;
+}
+
+int stream_workspace(size_t bytes, hipStream_t stream, void** out) {
+    *out = nullptr;
+    if (bytes == 0) return MHLA_OK;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "workspace device");
+    WorkspaceCache& c = workspace_cache();
+    std::lock_guard<std::mutex> lock(c.mu);
+    StreamWorkspace* entry = nullptr;
+    for (auto& w : c.live)
+        if (w.dev == dev && w.stream == stream) entry = &w;
+    if (entry && entry->bytes >= bytes) {
+        *out = entry->ptr;
+        return MHLA_OK;
+    }
+    size_t want = entry ? std::max(bytes, entry->bytes + entry->bytes / 2) : bytes;
+    want = (want + (2u << 20) - 1) / (2u << 20) * (2u << 20);
+    void* p = nullptr;
+    const int st = pool_alloc(&p, want, stream);
+    if (st) return st;
+    if (entry) {
+        c.retired.push_back(entry->ptr);
+        entry->ptr = p;
+        entry->bytes = want;
+    } else {
+        c.live.push_back({dev, stream, p, want});
+    }
+    *out = p;
+    return MHLA_OK;
+}
+
 int forward_path(int64_t B, int64_t H, int64_t N, int64_t d, int64_t M, int causal, int dtype) {
     return dtype == mhla::kDtypeBF16 && !causal && mhla::fused_applicable((int)d, B * H, N, M) ? MHLA_PATH_FUSED
                                                                                              : MHLA_PATH_STAGED;
@@ -193,7 +248,7 @@ int forward_impl(int dtype, const void* q, const void* k, const void* v, const f
     const size_t arr = (size_t)(M * BH * summary_floats(d)) * sizeof(float);
     const size_t total = workspace_bytes(dtype, BH, max_block, d, M, nw);
     void* ws = nullptr;
-    int st2 = pool_alloc(&ws, total, stream);
+    int st2 = stream_workspace(total, stream, &ws);
     if (st2) return st2;
     float* S = static_cast<float*>(ws);
     float* St = S + arr / sizeof(float);
@@ -212,9 +267,7 @@ int forward_impl(int dtype, const void* q, const void* k, const void* v, const f
         e = mhla::launch_output(dtype, q, k, v, St, W, os, BH, N, (int)d, M, causal != 0, heads, lay, max_block,
                                 stream);
     }
-    hipError_t fe = hipFreeAsync(ws, stream);
     if (e != hipSuccess) return hip_fail(e, what);
-    if (fe != hipSuccess) return hip_fail(fe, "workspace release");
     return ok();
 }
 
@@ -276,13 +329,11 @@ int mhla_block_summaries(const void* k, const void* v, int dtype, float* S, int6
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     void* partial = nullptr;
     const size_t pbytes = mhla::summary_partial_bytes(dtype, B * H, N / M, (int)d, M);
-    if (pbytes && (st = pool_alloc(&partial, pbytes, s))) return st;
+    if (pbytes && (st = stream_workspace(pbytes, s, &partial))) return st;
     const mhla::BlockLayout equal{nullptr, nullptr};
     hipError_t e = mhla::launch_summaries(dtype, k, v, S, B * H, N, (int)d, M, 0, equal, N / M,
                                           static_cast<float*>(partial), s);
-    hipError_t fe = partial ? hipFreeAsync(partial, s) : hipSuccess;
     if (e != hipSuccess) return hip_fail(e, "summary kernel");
-    if (fe != hipSuccess) return hip_fail(fe, "workspace release");
     return ok();
 }
 
@@ -297,11 +348,9 @@ int mhla_mix_summaries(const float* S, const float* W, float* St, int64_t BH, in
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     void* frags = nullptr;
     const size_t fbytes = precise ? 0 : mhla::mix_fragment_bytes(M);
-    if (fbytes && (st = pool_alloc(&frags, fbytes, s))) return st;
+    if (fbytes && (st = stream_workspace(fbytes, s, &frags))) return st;
     hipError_t e = mhla::launch_mix(S, W, St, BH, (int)d, M, causal != 0, precise != 0, 0, frags, s);
-    hipError_t fe = frags ? hipFreeAsync(frags, s) : hipSuccess;
     if (e != hipSuccess) return hip_fail(e, "mixing kernel");
-    if (fe != hipSuccess) return hip_fail(fe, "workspace release");
     return ok();
 }
 
@@ -365,12 +414,10 @@ int mhla_backward(const void* q, const void* k, const void* v, int dtype, const 
                           16 * 16;
     const size_t total = fbytes + mhla::mix_fragment_bytes(M);
     void* ws = nullptr;
-    if ((st = pool_alloc(&ws, total, stream))) return st;
+    if ((st = stream_workspace(total, stream, &ws))) return st;
     hipError_t e = mhla::launch_backward(dtype, q, k, v, W, dy, dq, dk, dv, dW, B * H, N, (int)d, M, causal != 0,
                                          static_cast<float*>(ws), static_cast<char*>(ws) + fbytes, stream);
-    hipError_t fe = hipFreeAsync(ws, stream);
     if (e != hipSuccess) return hip_fail(e, "backward kernels");
-    if (fe != hipSuccess) return hip_fail(fe, "workspace release");
     return ok();
 }
 

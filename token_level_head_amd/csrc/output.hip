@@ -22,27 +22,6 @@
 
 namespace mhla {
 
-// 4P consecutive bf16 values starting at p (P = d/16): 8, 16 or 32 bytes.
-template <int P, bool NT>
-__device__ __forceinline__ void load_group(const uint16_t* p, bool ok, const uint16_t* safe, uint16_t (&out)[4 * P]) {
-    if constexpr (P == 1) {
-        const uint2 x = load_token_or_zero<NT>(reinterpret_cast<const uint2*>(p), ok, reinterpret_cast<const uint2*>(safe));
-        out[0] = (uint16_t)x.x; out[1] = (uint16_t)(x.x >> 16);
-        out[2] = (uint16_t)x.y; out[3] = (uint16_t)(x.y >> 16);
-    } else {
-#pragma unroll
-        for (int h = 0; h < P / 2; ++h) {
-            const uint4 x = load_token_or_zero<NT>(reinterpret_cast<const uint4*>(p + 8 * h), ok, reinterpret_cast<const uint4*>(safe));
-            const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                out[8 * h + 2 * u] = (uint16_t)w[u];
-                out[8 * h + 2 * u + 1] = (uint16_t)(w[u] >> 16);
-            }
-        }
-    }
-}
-
 // B operands from packed chunks: slot e of k-step ks is group-local feature
 // fl = 8*ks + e, held in chunk (fl % P, jb) at row fl / P (zero past 4P).
 template <int P, int KS>
@@ -128,17 +107,35 @@ __global__ __launch_bounds__(256) void output_bf16_kernel(const uint16_t* __rest
     bf16x8 bh[KS][P], bl[KS][P];
     build_b<P, KS>(sch, bh, bl);
 
-    const uint16_t* Qp = Q + pair * N * D;
     const int64_t ybase = pair * N * D;
+    // Q rows through a per-pair buffer descriptor: a row outside the block reads zero
+    // with no mask, so the next tile's loads stay in flight while this tile computes.
+    const rsrc_t rQ = make_rsrc(Q + pair * N * D, (uint32_t)N * D * 2);
+    auto qload = [&](int tile, uint32_t (&w)[2 * P], bool& ok) {
+        const int tq = bstart + 16 * tile + n;  // list entry
+        const int qrow = (tile < tile_end && tq < bend) ? token_row(lay, tq, N) : -1;
+        ok = qrow >= 0;
+        const uint32_t off = off_if(ok, ((uint32_t)(ok ? qrow : 0) * D + FL * g) * 2);
+        if constexpr (P == 4) {
+            const u32x4 a = buf_load128<NT>(rQ, off), b = buf_load128<NT>(rQ, off + 16);
+            w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+            w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+        } else if constexpr (P == 2) {
+            const u32x4 a = buf_load128<NT>(rQ, off);
+            w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+        } else {
+            const u32x2 a = buf_load64<NT>(rQ, off);
+            w[0] = a.x; w[1] = a.y;
+        }
+    };
+    uint32_t qcur[2 * P], qnext[2 * P];
+    bool okcur = false, oknext = false;
+    if (tile_beg < tile_end) qload(tile_beg, qcur, okcur);
     for (int tile = tile_beg; tile < tile_end; ++tile) {
         const int t0 = bstart + 16 * tile;
-        // phi(Q) as the A operand: token t0 + n, group-local features of group g.
-        const int tq = t0 + n;  // list entry
-        const int qrow = tq < bend ? token_row(lay, tq, N) : -1;
-        const bool qok = qrow >= 0;
-        uint16_t qr[FL];
-        load_group<P, NT>(Qp + (qok ? qrow : 0) * D + FL * g, qok, Q, qr);
+        qload(tile + 1, qnext, oknext);  // the next tile's rows (none past the last: zero)
         issue_fence();
+        // phi(Q) as the A operand: token t0 + n, group-local features of group g.
         bf16x8 aq[KS];
         float den = 0.f;
 #pragma unroll
@@ -146,7 +143,12 @@ __global__ __launch_bounds__(256) void output_bf16_kernel(const uint16_t* __rest
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int fl = 8 * ks + e;
-                const __bf16 ph = (__bf16)((fl < FL && qok) ? phi_fast(bf16_to_f32(qr[fl < FL ? fl : 0])) : 0.f);
+                float x = 0.f;
+                if (fl < FL) {
+                    const uint32_t word = qcur[fl / 2];
+                    x = __uint_as_float((fl & 1) ? (word & 0xffff0000u) : (word << 16));
+                }
+                const __bf16 ph = (__bf16)((fl < FL && okcur) ? phi_fast(x) : 0.f);
                 aq[ks][e] = ph;
                 if (fl < FL) den = fmaf(bf16v_to_f32(ph), zt[fl], den);
             }
@@ -163,6 +165,9 @@ __global__ __launch_bounds__(256) void output_bf16_kernel(const uint16_t* __rest
             }
         }
         store_rows<P, P>(o, ybase, t0, bend, g, n, 0, acc, den, lay, N);
+#pragma unroll
+        for (int h = 0; h < 2 * P; ++h) qcur[h] = qnext[h];
+        okcur = oknext;
     }
 }
 

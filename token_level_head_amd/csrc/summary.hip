@@ -290,12 +290,15 @@ struct SummarySplit {
 };
 
 // Waves per block (1, 2, 4) and, for long blocks on few (batch, head) pairs, token
-// segments over several workgroups, so that about 1024 workgroups exist.  Every
-// wave keeps at least two 32-token steps; segments are multiples of 128 tokens.
+// segments over several workgroups, so that about 1024 workgroups exist.  Splitting
+// stops at 2048 waves (half the resident slots at 4 waves per SIMD), so that all of
+// them run in one round: 1536 blocks of 256 tokens in 6144 waves left the second
+// round half empty.  Every wave keeps at least two 32-token steps; segments are
+// multiples of 128 tokens.
 SummarySplit summary_split(int64_t BH, int64_t C, int64_t M) {
     const int64_t units = BH * M;
     SummarySplit sp{1, 1, (int)C};
-    while (sp.wpb < 4 && units * sp.wpb < 4096 && C >= 64 * (2 * sp.wpb)) sp.wpb *= 2;
+    while (sp.wpb < 4 && units * sp.wpb * 2 <= 4096 && C >= 64 * (2 * sp.wpb)) sp.wpb *= 2;
     if (sp.wpb == 4 && units < 1024 && C >= 512) {
         const int64_t want = (1024 + units - 1) / units;
         const int64_t segC = ((C + want - 1) / want + 127) / 128 * 128;
