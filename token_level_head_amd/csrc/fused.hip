@@ -340,7 +340,8 @@ __device__ __forceinline__ void fused_pair(const uint16_t* __restrict__ Q, const
 
 // Workgroups [0, nfull) each run the whole pair of their index; the rest run the
 // remaining pairs in column halves, two workgroups per pair (dispatched after all
-// the whole pairs, so that a CU holding two workgroups gets a whole pair and a half).
+// the whole pairs, so that a CU holding two workgroups gets a whole pair and a half;
+// the two halves of a pair are numbered 8 apart, which keeps them on one XCD).
 template <int D, bool FULL>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4))) void fused_small_kernel(
                                                           const uint16_t* __restrict__ Q,
@@ -355,9 +356,21 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4))
     if (w < nfull) {
         fused_pair<D, FULL, 0>(Q, K, V, W, o, N, M, heads, T, lds, w);
     } else if constexpr (P >= 2) {
+        // Halves of one pair are 8 workgroups apart, so that round-robin dispatch puts
+        // both on the same XCD and the second reads the pair's inputs from that L2.
         const int u = w - nfull;
-        const int64_t pair = nfull + u / 2;
-        if (u & 1)
+        const int nh = ((int)gridDim.x - nfull) / 2;  // pairs run in halves
+        const int g16 = (nh / 8) * 16;
+        int j, h;
+        if (u < g16) {
+            j = 8 * (u / 16) + (u % 8);
+            h = (u / 8) & 1;
+        } else {
+            j = (nh / 8) * 8 + (u - g16) / 2;
+            h = (u - g16) & 1;
+        }
+        const int64_t pair = nfull + j;
+        if (h)
             fused_pair<D, FULL, 2>(Q, K, V, W, o, N, M, heads, T, lds, pair);
         else
             fused_pair<D, FULL, 1>(Q, K, V, W, o, N, M, heads, T, lds, pair);
