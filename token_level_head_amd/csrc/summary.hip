@@ -290,11 +290,11 @@ struct SummarySplit {
 };
 
 // Waves per block (1, 2, 4) and, for long blocks on few (batch, head) pairs, token
-// segments over several workgroups, so that about 1024 workgroups exist.  Splitting
-// stops at 2048 waves (half the resident slots at 4 waves per SIMD), so that all of
-// them run in one round: 1536 blocks of 256 tokens in 6144 waves left the second
-// round half empty.  Every wave keeps at least two 32-token steps; segments are
-// multiples of 128 tokens.
+// segments over several workgroups, so that about 1024 workgroups exist.  A block is
+// split further only while the waves stay within 4096 (the resident slots at 4 waves
+// per SIMD), so that all of them run in one round: 1536 blocks of 256 tokens in 6144
+// waves left the second round half empty.  Every wave keeps at least two 32-token
+// steps; segments are multiples of 128 tokens.
 SummarySplit summary_split(int64_t BH, int64_t C, int64_t M) {
     const int64_t units = BH * M;
     SummarySplit sp{1, 1, (int)C};
