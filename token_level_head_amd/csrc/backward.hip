@@ -1001,8 +1001,8 @@ __global__ __launch_bounds__(256) void bwd_wt_kernel(const float* __restrict__ W
 // dW partials: part[ch][i][b] = sum over columns of chunk ch of dSt[i][col] S[b][col],
 // one 64 x 64 output block per workgroup (wave w: rows 16w .. 16w + 15), on MFMA
 // with hi + lo operands.  ncols and chunk are multiples of 8.  Each step's loads are
-// issued one step ahead (unconditional loads: a column or row out of range reads a
-// valid address and is masked to zero).
+// issued two steps ahead (unconditional loads: a column or row out of range reads a
+// valid address and is masked to zero when used).
 struct DwRun {  // 8 consecutive floats of one row, loaded ahead; masked when used
     f32x4 x[2];
     bool ok;
@@ -1027,6 +1027,7 @@ __device__ __forceinline__ void dw_split(const DwRun& r, bf16x8& hi, bf16x8& lo)
     lo = __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], l[2], l[3]});
 }
 
+template <int JT>
 __global__ __launch_bounds__(256) void bwd_dw_kernel(const float* __restrict__ dSt, const float* __restrict__ S,
                                                      float* __restrict__ part, int64_t ncols, int M, int64_t chunk,
                                                      int nb, int rt) {
@@ -1037,43 +1038,47 @@ __global__ __launch_bounds__(256) void bwd_dw_kernel(const float* __restrict__ d
     const int ob = (int)(blockIdx.x % (nb * nb));
     const int64_t ch = (blockIdx.x / (nb * nb)) * (4 / rt) + wave / rt;
     const int i0 = 64 * (ob / nb) + 16 * (wave % rt), b0 = 64 * (ob % nb);
-    const int jt = min(4, (M - b0 + 15) / 16);  // column tiles of this block
+    // JT column tiles of 16 per block (tiles past M read zero and are not stored)
     const int64_t k0 = ch * chunk, k1 = min(ncols, k0 + chunk);
-    f32x4 acc[4];
+    f32x4 acc[JT];
 #pragma unroll
-    for (int jb = 0; jb < 4; ++jb) acc[jb] = zero4();
+    for (int jb = 0; jb < JT; ++jb) acc[jb] = zero4();
     if (i0 < M && k0 < ncols) {
         const int nsteps = (int)((k1 - k0 + 31) / 32);
-        DwRun xa, xb[4];
+        // two register sets: the loads of step s + 2 are issued while step s computes
+        DwRun xa[2], xb[2][JT];
         int64_t k = k0 + 8 * g;
-        dw_load(dSt, ncols, i0 + n, M, k, k1, xa);
 #pragma unroll
-        for (int jb = 0; jb < 4; ++jb)
-            if (jb < jt) dw_load(S, ncols, b0 + 16 * jb + n, M, k, k1, xb[jb]);
-        for (int st = 0; st < nsteps; ++st) {
-            bf16x8 ah, al, bh[4], bl[4];
-            dw_split(xa, ah, al);
+        for (int h = 0; h < 2; ++h) {
+            dw_load(dSt, ncols, i0 + n, M, k + 32 * h, k1, xa[h]);
 #pragma unroll
-            for (int jb = 0; jb < 4; ++jb)
-                if (jb < jt) dw_split(xb[jb], bh[jb], bl[jb]);
-            k += 32;
-            dw_load(dSt, ncols, i0 + n, M, k, k1, xa);
+            for (int jb = 0; jb < JT; ++jb) dw_load(S, ncols, b0 + 16 * jb + n, M, k + 32 * h, k1, xb[h][jb]);
+        }
+        auto step = [&](DwRun& a, DwRun (&b)[JT], int64_t knext) {
+            bf16x8 ah, al, bh[JT], bl[JT];
+            dw_split(a, ah, al);
 #pragma unroll
-            for (int jb = 0; jb < 4; ++jb)
-                if (jb < jt) dw_load(S, ncols, b0 + 16 * jb + n, M, k, k1, xb[jb]);
+            for (int jb = 0; jb < JT; ++jb) dw_split(b[jb], bh[jb], bl[jb]);
+            dw_load(dSt, ncols, i0 + n, M, knext, k1, a);
+#pragma unroll
+            for (int jb = 0; jb < JT; ++jb) dw_load(S, ncols, b0 + 16 * jb + n, M, knext, k1, b[jb]);
             issue_fence();
 #pragma unroll
-            for (int jb = 0; jb < 4; ++jb)
-                if (jb < jt) {
-                    acc[jb] = mfma32(ah, bh[jb], acc[jb]);
-                    acc[jb] = mfma32(ah, bl[jb], acc[jb]);
-                    acc[jb] = mfma32(al, bh[jb], acc[jb]);
-                }
+            for (int jb = 0; jb < JT; ++jb) {
+                acc[jb] = mfma32(ah, bh[jb], acc[jb]);
+                acc[jb] = mfma32(ah, bl[jb], acc[jb]);
+                acc[jb] = mfma32(al, bh[jb], acc[jb]);
+            }
+        };
+        for (int st = 0; st < nsteps; st += 2, k += 64) {
+            step(xa[0], xb[0], k + 64);
+            if (st + 1 >= nsteps) break;
+            step(xa[1], xb[1], k + 96);
         }
     }
     if (k0 >= ncols) return;
 #pragma unroll
-    for (int jb = 0; jb < 4; ++jb)
+    for (int jb = 0; jb < JT; ++jb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = i0 + 4 * g + i, col = b0 + 16 * jb + n;
@@ -1134,8 +1139,12 @@ DwPlan dw_plan(int64_t ncols, int64_t M) {
     if (p.rt == 3) p.rt = 4;
     const int64_t subs = 4 / p.rt;
     const int64_t nblk = (int64_t)p.nb * p.nb;
-    const int64_t want = std::max<int64_t>(1, 2048 / nblk) * subs;  // partials (one per wave slot)
-    const int64_t most = std::max<int64_t>(1, ncols / 512);         // at least 512 columns per partial
+    // One round of resident workgroups: 256 CUs x (waves per SIMD of bwd_dw_kernel<rt>:
+    // 6, 4, 2 for rt = 1, 2, 4) four-wave workgroups; a few workgroups past it would
+    // form a second round alone.
+    const int64_t round = 256 * (p.rt == 1 ? 6 : p.rt == 2 ? 4 : 2);
+    const int64_t want = std::max<int64_t>(1, round / nblk) * subs;  // partials (one per wave slot)
+    const int64_t most = std::max<int64_t>(1, ncols / 512);          // at least 512 columns per partial
     const int64_t nch = std::min(want, most);
     p.chunk = ((ncols + nch - 1) / nch + 31) / 32 * 32;
     p.nchunks = (ncols + p.chunk - 1) / p.chunk;
@@ -1215,8 +1224,13 @@ hipError_t run_backward(const T* q, const T* k, const T* v, const float* W, cons
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const DwPlan p = dw_plan(BH * L, M);
     const int64_t subs = 4 / p.rt;
-    bwd_dw_kernel<<<dim3((unsigned)((p.nchunks + subs - 1) / subs * p.nb * p.nb)), dim3(256), 0, stream>>>(
-        dSt, S, part, BH * L, (int)M, p.chunk, p.nb, p.rt);
+    const dim3 dw_grid((unsigned)((p.nchunks + subs - 1) / subs * p.nb * p.nb));
+    if (p.rt == 1)
+        bwd_dw_kernel<1><<<dw_grid, dim3(256), 0, stream>>>(dSt, S, part, BH * L, (int)M, p.chunk, p.nb, p.rt);
+    else if (p.rt == 2)
+        bwd_dw_kernel<2><<<dw_grid, dim3(256), 0, stream>>>(dSt, S, part, BH * L, (int)M, p.chunk, p.nb, p.rt);
+    else
+        bwd_dw_kernel<4><<<dw_grid, dim3(256), 0, stream>>>(dSt, S, part, BH * L, (int)M, p.chunk, p.nb, p.rt);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t groups = (M * M + 255) / 256;
     bwd_dw_reduce1_kernel<<<dim3((unsigned)(groups * p.nsplit)), dim3(256), 0, stream>>>(part, part2, M * M,
