@@ -28,6 +28,9 @@ BACKWARD = [  # (B, H, N, d, M, causal, dtype)
     (1, 2, 48, 16, 48, True, "f32"),    # one token per block
     (1, 1, 256, 64, 1, True, "bf16"),   # one block of 16 tiles: the plain recurrence
     (1, 1, 640, 16, 80, False, "bf16"), # M = 80: mixing through split-W fragments
+    (1, 2, 1024, 64, 4, False, "bf16"), # C = 256: a block's tiles over 4 waves, partials added in LDS
+    (1, 3, 512, 32, 16, False, "f32"),  # C = 32: 2 waves per block, float32 inputs
+    (1, 1, 512, 16, 32, True, "bf16"),  # M = 32: two column tiles per dW block
 ]
 
 
