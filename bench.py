@@ -8,8 +8,9 @@
 
 One step is one full forward pass (phi, block summaries, mixing, output) over
 the workload's synthetic batch, with inputs resident in HBM before the timed
-region and the caches cold: before every call a read of 512 MiB (not timed)
-evicts L2 and the Infinity Cache; the step time is the median over K calls.
+region and the caches cold: the K timed calls rotate over copies of the inputs
+and outputs that together exceed twice the Infinity Cache, so each call reads
+its inputs from HBM.
 Prints ONE JSON line with throughput (tokens/s), model TFLOP/s, the HBM roofline
 of the dominant kernel (its duration measured with HIP events on the launch
 stream: the whole step on the fused path, the stage inside a chain of
@@ -347,30 +348,37 @@ def main():
         return e0.elapsed_time(e1)
 
     # ---- whole-pass throughput, cold caches ----
-    # Before every call, timed or not, a pass over 512 MiB (not timed) evicts L2 and the
-    # 256 MiB Infinity Cache, so each step reads its inputs from HBM.  HIP events bracket
-    # the one call on its stream (the fill keeps the GPU busy while the host enqueues it);
-    # `ms_per_step` is the median over the K steps.
-    # The eviction pass reads 512 MiB (a sum), so it leaves only clean lines behind: a fill
-    # would leave up to 256 MiB of dirty lines whose write-back the next call would pay.
-    flush = torch.ones(1 << 27, dtype=torch.float32, device="cuda")
+    # The calls rotate over `nbuf` copies of the inputs and outputs, at least 512 MiB in
+    # all (twice the Infinity Cache), so each call's buffers were last touched nbuf - 1
+    # calls earlier and have been evicted from L2 and the Infinity Cache: every call
+    # reads its inputs from HBM.  K back-to-back calls between two HIP events on the
+    # launch stream.
+    per_call = sum(t.numel() * t.element_size() for t in (qd, kd, vd, out))
+    nbuf = int(min(16, max(1, -(-(512 << 20) // per_call))))
+    sets = [(qd, kd, vd, out)] + [tuple(t.clone() for t in (qd, kd, vd, out)) for _ in range(nbuf - 1)]
 
-    def evict():
-        flush.sum()
+    def run_cold(n, start=0):
+        for i in range(n):
+            a, b_, c, o = sets[(start + i) % nbuf]
+            fwd(a, b_, c, Wd, o, causal=w.causal)
 
-    for _ in range(args.warmup):
-        evict()
-        fwd(qd, kd, vd, Wd, out, causal=w.causal)
-    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
-    for e0, e1 in step_ev:
-        evict()
-        e0.record(stream)
-        fwd(qd, kd, vd, Wd, out, causal=w.causal)
-        e1.record(stream)
+    # A pre-roll of device work (reads, so no dirty lines are left behind) keeps the GPU
+    # busy while the host enqueues the timed calls; `pre_done` still pending once they are
+    # enqueued shows that the GPU never waited for the host.
+    preroll = torch.ones(1 << 26, dtype=torch.float32, device="cuda")
+    run_cold(args.warmup)
     torch.cuda.synchronize()
-    step_all = sorted(e0.elapsed_time(e1) for e0, e1 in step_ev)
-    ms = step_all[len(step_all) // 2]
+    for _ in range(8 * args.steps):
+        preroll.sum()
+    pre_done = torch.cuda.Event()
+    pre_done.record(stream)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    run_cold(args.steps, args.warmup)
+    t1.record(stream)
+    steps_gapless = not pre_done.query()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
     tokens_s = w.tokens / (ms * 1e-3)
     tflops = model_flops(w) / (ms * 1e-3) / 1e12
 
@@ -403,45 +411,44 @@ def main():
                           "and K eager launches"}
 
     # ---- per-stage durations: K chains of summaries -> mixing -> output (each stage
-    # consuming the previous one's result, as inside mhla_forward), each chain after a
-    # cache-evicting read, HIP events between the stages on the launch stream; median per
-    # stage.  When mhla_forward takes the fused path these are reported for reference only
+    # consuming the previous one's result, as inside mhla_forward) over the rotating
+    # buffer sets, HIP events between the stages on the launch stream; mean per stage.  When mhla_forward takes the fused path these are reported for reference only
     # (`staged_kernels`); the step itself is the fused kernel. ----
     L = w.d * w.d + w.d
     S = torch.empty(w.M * w.B * w.H * L, dtype=torch.float32, device="cuda")
     St = torch.empty_like(S)
     names = ["summaries", "mix", "output"]
-    stages = [
-        lambda: mh.mhla_block_summaries(kd, vd, S, w.M),
-        lambda: mh.mhla_mix_summaries(S, Wd, St, w.B * w.H, w.d, causal=w.causal, precise=(w.dtype == "f32")),
-        lambda: mh.mhla_output(qd, kd, vd, St, Wd, out, causal=w.causal),
-    ]
-    for _ in range(args.warmup):
-        evict()
-        for f in stages:
+
+    def chain(i):
+        a, b_, c, o = sets[i % nbuf]
+        return [
+            lambda: mh.mhla_block_summaries(b_, c, S, w.M),
+            lambda: mh.mhla_mix_summaries(S, Wd, St, w.B * w.H, w.d, causal=w.causal, precise=(w.dtype == "f32")),
+            lambda: mh.mhla_output(a, b_, c, St, Wd, o, causal=w.causal),
+        ]
+
+    for i in range(args.warmup):
+        for f in chain(i):
             f()
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     # A pre-roll of device fills keeps the GPU busy while the host enqueues the timed
     # chains, so no host launch gap falls between two events.  `pre_done` still pending
     # once everything is enqueued shows that the GPU never waited for the host.
-    for _ in range(2 * args.steps):
-        evict()
+    for _ in range(8 * args.steps):
+        preroll.sum()
     pre_done = torch.cuda.Event()
     pre_done.record(stream)
     for it in range(args.steps):
-        evict()
         evs[it][0].record(stream)
-        for j, f in enumerate(stages):
+        for j, f in enumerate(chain(args.warmup + it)):
             f()
             evs[it][j + 1].record(stream)
     gapless = not pre_done.query()
     torch.cuda.synchronize()
-    del flush
-    kms = {}
-    for j, name in enumerate(names):
-        d = sorted(evs[it][j].elapsed_time(evs[it][j + 1]) for it in range(args.steps))
-        kms[name] = d[len(d) // 2]
+    del preroll
+    kms = {name: sum(evs[it][j].elapsed_time(evs[it][j + 1]) for it in range(args.steps)) / args.steps
+           for j, name in enumerate(names)}
     kb = kernel_bytes(w)
 
     def entry(name, t_ms):
@@ -502,9 +509,10 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
-        "timing": "median of K single calls, each after a cache-evicting read of 512 MiB (not timed)",
-        "ms_min": round(step_all[0], 5),
-        "ms_max": round(step_all[-1], 5),
+        "timing": "K back-to-back calls rotating over copies of the inputs and outputs that together "
+                  "exceed twice the Infinity Cache (each call reads from HBM)",
+        "buffer_sets": nbuf,
+        "host_gaps": not steps_gapless,
         "warm": warm,
         "higher_is_better": True,
         "scaling": "weak",
@@ -517,7 +525,7 @@ def main():
         "path": "fused" if path == mh.MHLA_PATH_FUSED else "staged",
         "kernels": kernels,
         "staged_kernels": staged,
-        "stage_timing": "medians of K chains, each after a cache-evicting read; "
+        "stage_timing": "K chains over the rotating buffer sets; "
                         + ("no host gaps" if gapless else "host gaps possible"),
         "roofline": roofline,
         "cpu_baseline": cpu,
