@@ -31,6 +31,8 @@ BACKWARD = [  # (B, H, N, d, M, causal, dtype)
     (1, 2, 1024, 64, 4, False, "bf16"), # C = 256: a block's tiles over 4 waves, partials added in LDS
     (1, 3, 512, 32, 16, False, "f32"),  # C = 32: 2 waves per block, float32 inputs
     (1, 1, 512, 16, 32, True, "bf16"),  # M = 32: two column tiles per dW block
+    (1, 1, 8192, 64, 64, True, "bf16"),    # the causal LM shape: 64 blocks of 128 tokens (8 tiles each)
+    (1, 1, 16384, 64, 256, False, "bf16"), # M = 256: streaming mixing GEMM, 4 x 4 dW output blocks
 ]
 
 
