@@ -243,6 +243,39 @@ __device__ __forceinline__ void gemm_packed(const bf16x8 (&ah)[KS], const bf16x8
         }
 }
 
+// B operands of packed chunks of X, split once into LDS in lane order: entry (ks, jb,
+// hi/lo) of lane l at sb[2 (ks P + jb) + hl][l].  The nw waves of the workgroup build
+// the entries (ks P + jb) = w, w + nw, ... between them; a barrier must follow.
+template <int P, int KS>
+__device__ __forceinline__ void packed_b_lds(const f32x4 (&ch)[P * P], u32x4 (*sb)[64], int lane, int w, int nw) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int jb = 0; jb < P; ++jb)
+            if ((ks * P + jb) % nw == w) {
+                bf16x8 h, l;
+                packed_slots<P>(ch, ks, jb, h, l);
+                sb[2 * (ks * P + jb)][lane] = __builtin_bit_cast(u32x4, h);
+                sb[2 * (ks * P + jb) + 1][lane] = __builtin_bit_cast(u32x4, l);
+            }
+}
+
+// gemm_rl with the B operands read from LDS (laid out by packed_b_lds).
+template <int P, int KS, bool ALO>
+__device__ __forceinline__ void gemm_lds(const bf16x8 (&ah)[KS], const bf16x8 (&al)[KS], const u32x4 (*sb)[64],
+                                         int lane, f32x4 (&acc)[P]) {
+#pragma unroll
+    for (int jb = 0; jb < P; ++jb)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 bh = __builtin_bit_cast(bf16x8, sb[2 * (ks * P + jb)][lane]);
+            const bf16x8 bl = __builtin_bit_cast(bf16x8, sb[2 * (ks * P + jb) + 1][lane]);
+            acc[jb] = mfma32(ah[ks], bh, acc[jb]);
+            acc[jb] = mfma32(ah[ks], bl, acc[jb]);
+            if constexpr (ALO) acc[jb] = mfma32(al[ks], bh, acc[jb]);
+        }
+}
+
 // acc (packed chunks of X) += sum over the tile's tokens of a_t b_t^T, X[r][c] with
 // r from the A side and c from the B side (both in dot layout).
 template <int P, bool ALO>
@@ -373,7 +406,7 @@ __global__ __launch_bounds__(256) void bwd_sum_kernel(const T* __restrict__ K, c
 
 // dq and dS~_i^T, dz~_i for one (pair, block i) per workgroup of wpu waves (non-causal).
 template <int D, typename T>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_query_kernel(const T* __restrict__ Q, const float* __restrict__ dY,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void bwd_query_kernel(const T* __restrict__ Q, const float* __restrict__ dY,
                                                         const float* __restrict__ St, float* __restrict__ dQ,
                                                         float* __restrict__ dSt, int64_t BH, int N, int M, int wpu) {
     using Dm = Dim<D>;
@@ -387,15 +420,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
     const int ntiles = (C + 15) / 16;
 
     const float* sv = St + ((int64_t)blk * BH + pair) * L;
-    bf16x8 bh[KS][P], bl[KS][P];  // B[k = c][col = r] = S~[r][c]
+    __shared__ u32x4 sb[2 * KS * P][64];  // B[k = c][col = r] = S~[r][c], shared by the waves
     float zt[P];
     {
         f32x4 ch[P * P];
         load_packed<P>(sv, lane, ch);
-        packed_b<P, KS>(ch, bh, bl);
+        packed_b_lds<P, KS>(ch, sb, lane, wave, wpu);
 #pragma unroll
         for (int b = 0; b < P; ++b) zt[b] = sv[D * D + P * n + b];
     }
+    __syncthreads();
     f32x4 acc[P * P];
     float zacc[P];
 #pragma unroll
@@ -416,7 +450,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
         f32x4 u[P];  // U[4g + i][Pn + jb] = (S~_i dy_t)[r]
 #pragma unroll
         for (int jb = 0; jb < P; ++jb) u[jb] = zero4();
-        gemm_rl<P, KS, true>(yh, yl, bh, bl, u);
+        gemm_lds<P, KS, true>(yh, yl, sb, lane, u);
 
         float fq[4][P], dp[4][P], dn[4][P], dden[4];
 #pragma unroll
