@@ -419,8 +419,17 @@ __global__ __launch_bounds__(512) void mix_stream_kernel(const float* __restrict
     // written, two tiles ahead of their use.
     const rsrc_t rS = make_rsrc(S, (uint32_t)((int64_t)M * ld * 4));
     const uint32_t soff0 = (uint32_t)(((int64_t)(2 * bp) * ld + 4 * cg) * 4);
+    // Column tile of this workgroup's j-th step.  In whole rounds of 256 workgroups the
+    // tiles are permuted so that the two 16-column tiles sharing each 128-byte line of S
+    // go to workgroups on one XCD (ids congruent mod 8): the line is fetched into one L2.
+    auto tile_col = [&](int64_t j) -> int64_t {
+        const int64_t t = blockIdx.x + j * gridDim.x;
+        if (gridDim.x != 256 || t >= ntiles / 256 * 256) return t;
+        const int b = (int)(t % 256);
+        return t - b + 2 * (b % 8 + 8 * (b / 16)) + (b / 8) % 2;
+    };
     auto load_tile = [&](int64_t j, f32x4 (&x)[2]) {
-        const uint32_t col = (uint32_t)((blockIdx.x + j * gridDim.x) * 16);
+        const uint32_t col = (uint32_t)(tile_col(j) * 16);
         const bool ok = j < my_tiles;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -459,7 +468,7 @@ __global__ __launch_bounds__(512) void mix_stream_kernel(const float* __restrict
                 }
             }
         }
-        const int64_t col0 = (blockIdx.x + j * gridDim.x) * 16;
+        const int64_t col0 = tile_col(j) * 16;
 #pragma unroll
         for (int r = 0; r < 2; ++r) {  // lane (g, n): row i0 + 16r + n, columns 4g .. 4g + 3
             const int row = 16 * r + n;
