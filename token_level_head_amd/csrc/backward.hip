@@ -491,7 +491,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
 
 // dk, dv for one (pair, key block b) from dS_b^T, dz_b (non-causal); waves of the
 // workgroup take the block's tiles in turn.
-template <int D, typename T>
+template <int D, typename T, bool SHARED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_key_kernel(const T* __restrict__ K, const T* __restrict__ V,
                                                       const float* __restrict__ dS, float* __restrict__ dK,
                                                       float* __restrict__ dV, int64_t BH, int N, int M, int wpu) {
@@ -504,21 +504,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
     const int blk = (int)(unit % M), C = N / M;
     const int64_t row0 = pair * N + (int64_t)blk * C;
     const int ntiles = (C + 15) / 16;
-    if (wave >= ntiles) return;  // no barriers in this kernel
 
+    // The B operands of dS in both orientations: per wave in registers, or (SHARED, when
+    // several waves share the block) split once into LDS for all of them.
     const float* sv = dS + ((int64_t)blk * BH + pair) * L;
-    bf16x8 b1h[KS][P], b1l[KS][P];  // B[k = c][col = r] = dS[r][c]   (d phi(k) = dS v + dz)
-    bf16x8 b2h[KS][P], b2l[KS][P];  // B[k = r][col = c] = dS[r][c]   (dv = dS^T phi(k))
+    bf16x8 b1h[SHARED ? 1 : KS][P], b1l[SHARED ? 1 : KS][P];  // B[k = c][col = r] = dS[r][c]  (d phi(k))
+    bf16x8 b2h[SHARED ? 1 : KS][P], b2l[SHARED ? 1 : KS][P];  // B[k = r][col = c] = dS[r][c]  (dv)
+    __shared__ u32x4 sb1[SHARED ? 2 * KS * P : 1][64], sb2[SHARED ? 2 * KS * P : 1][64];
     float dz[P];
     {
         f32x4 ch[P * P];
         load_packed<P>(sv, lane, ch);
-        packed_b<P, KS>(ch, b1h, b1l);
+        if constexpr (SHARED) packed_b_lds<P, KS>(ch, sb1, lane, wave, wpu);
+        else packed_b<P, KS>(ch, b1h, b1l);
         load_packed_t<P>(sv, g, n, ch);
-        packed_b<P, KS>(ch, b2h, b2l);
+        if constexpr (SHARED) packed_b_lds<P, KS>(ch, sb2, lane, wave, wpu);
+        else packed_b<P, KS>(ch, b2h, b2l);
 #pragma unroll
         for (int b = 0; b < P; ++b) dz[b] = sv[D * D + P * n + b];
     }
+    if constexpr (SHARED) __syncthreads();
+    if (wave >= ntiles) return;  // no barriers past this point
     for (int tile = wave; tile < ntiles; tile += wpu) {
         const int t0 = 16 * tile, rows = min(16, C - t0);
         const rsrc_t rk = tile_rsrc(K, row0 + t0, rows, D), rv = tile_rsrc(V, row0 + t0, rows, D);
@@ -535,8 +541,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
         f32x4 a1[P], a2[P];
 #pragma unroll
         for (int b = 0; b < P; ++b) a1[b] = a2[b] = zero4();
-        gemm_rl<P, KS, VLO>(vh, vl, b1h, b1l, a1);
-        gemm_rl<P, KS, true>(kh, kl, b2h, b2l, a2);
+        if constexpr (SHARED) {
+            gemm_lds<P, KS, VLO>(vh, vl, sb1, lane, a1);
+            gemm_lds<P, KS, true>(kh, kl, sb2, lane, a2);
+        } else {
+            gemm_rl<P, KS, VLO>(vh, vl, b1h, b1l, a1);
+            gemm_rl<P, KS, true>(kh, kl, b2h, b2l, a2);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             float ok[P], ov[P];
@@ -1254,7 +1265,10 @@ hipError_t run_backward(const T* q, const T* k, const T* v, const float* W, cons
         bwd_key_causal_kernel<D, T><<<grid, dim3(128), 0, stream>>>(q, k, v, dy, W, G, dS, dk, dv, BH, (int)N,
                                                                       (int)M);
     else
-        bwd_key_kernel<D, T><<<grid, block, 0, stream>>>(k, v, dS, dk, dv, BH, (int)N, (int)M, wpu);
+        if (wpu > 1)
+            bwd_key_kernel<D, T, true><<<grid, block, 0, stream>>>(k, v, dS, dk, dv, BH, (int)N, (int)M, wpu);
+        else
+            bwd_key_kernel<D, T, false><<<grid, block, 0, stream>>>(k, v, dS, dk, dv, BH, (int)N, (int)M, wpu);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const DwPlan p = dw_plan(BH * L, M);
     const int64_t subs = 4 / p.rt;
