@@ -44,8 +44,9 @@
 // bwd_dw_reduce1_kernel / bwd_dw_reduce_kernel form dW as a split-K MFMA GEMM with a
 // two-level fixed-order reduction.
 // Non-causal kernels spread a block's tiles over up to four waves of one workgroup
-// (partial sums added in LDS in a fixed order); causal kernels walk a block's tiles
-// in order (queries) or in reverse (keys) in one wave, carrying the running summary.
+// (partial sums added in LDS in a fixed order).  Causal kernels walk a block's tiles
+// in order (queries: two waves splitting the feature columns) or in reverse (keys: one
+// wave per orientation of the running sum), carrying the running summary.
 #include <algorithm>
 #include <type_traits>
 
