@@ -78,9 +78,11 @@ enum { MHLA_PATH_STAGED = 0, MHLA_PATH_FUSED = 1 };
  *     through a workspace of mhla_workspace_bytes() bytes.  The library keeps
  *     one workspace per (device, stream) handle, shared by all calls on that
  *     stream (they run in order) and grown from a library-owned memory pool when
- *     a call needs more; an outgrown workspace is kept until the process ends, so
- *     HIP graphs captured with it stay valid.  A call that needs no growth
- *     allocates nothing and does not wait for the device;
+ *     a call needs more (the outgrown one is freed in stream order).  A call that
+ *     needs no growth allocates nothing and does not wait for the device.  A call
+ *     made while its stream is being captured into a HIP graph takes its own
+ *     workspace from the pool and frees it at its end, both in stream order, so
+ *     the graph owns that memory and never shares the stream's workspace;
  *   - fused (non-causal; M <= 16 blocks of at most 16 tokens, or N <= 256 in
  *     blocks of 32, 48 or 64 tokens): one workgroup per (batch, head) pair that
  *     keeps the block summaries and their mix in LDS; no workspace.

@@ -4,8 +4,11 @@
   own workspace; the calls interleave on the device).
 * Growth: a small call, then a larger one on the same stream (the workspace is
   replaced by a larger one), then the small one again.
-* A HIP graph captured while the workspace was small is replayed after the
-  workspace has grown: the outgrown buffer is kept, so the replay stays correct.
+* A HIP graph captured on the stream is replayed after the stream's workspace has
+  grown: a captured call takes its own workspace inside the graph (allocation and
+  free nodes), so the replay does not depend on the stream's workspace.
+* Graphs captured, replayed and deleted one after another on the same stream, with
+  eager calls of other sizes in between (each graph's workspace ends with it).
 """
 import os
 import sys
@@ -100,3 +103,25 @@ def test_growth_and_graph_across_growth(orc):
         mh.mhla_forward(*small[2], small[3], out_s)
     s.synchronize()
     say(f"[workspace] small call after the growth: {check(orc, small[1], out_s):.2e}")
+
+
+def test_graphs_deleted_between_captures(orc):
+    cases = [case(1, 2, 1024, 16, 7420), case(2, 2, 2048, 64, 7421), case(1, 3, 1024, 32, 7422)]
+    s = torch.cuda.Stream()
+    outs = [torch.empty(c[2][0].shape, dtype=torch.float32, device="cuda") for c in cases]
+    for rnd in range(2):
+        for c, out in zip(cases, outs):
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=s):
+                mh.mhla_forward(*c[2], c[3], out)
+            for _ in range(2):
+                out.zero_()
+                graph.replay()
+            torch.cuda.synchronize()
+            say(f"[workspace] round {rnd}, B={c[0].B} N={c[0].N} M={c[0].M}: graph {check(orc, c[1], out):.2e}")
+            del graph
+            with torch.cuda.stream(s):
+                out.zero_()
+                mh.mhla_forward(*c[2], c[3], out)
+            s.synchronize()
+            say(f"[workspace]   eager on the capture stream: {check(orc, c[1], out):.2e}")

@@ -147,9 +147,15 @@ int pool_alloc(void** ptr, size_t bytes, hipStream_t stream) {
 // share one buffer; a steady-state call then makes no allocation call at all (a
 // stream-ordered malloc/free pair per call made the host wait for the GPU on every
 // call on this runtime).  A call that needs more takes a larger buffer from the pool
-// (at least 1.5x the old one); the outgrown buffer is kept, not freed, so that HIP
-// graphs captured with it stay valid.  Calls on different streams use different
-// buffers.
+// (at least 1.5x the old one) and frees the old one in stream order.  Calls on
+// different streams use different buffers.
+//
+// A call made while its stream is being captured into a graph must not use that
+// buffer: memory allocated during capture belongs to the graph (it is not valid once
+// the graph is gone), and a graph replayed later could overlap eager calls on the
+// stream.  Such a call allocates its own workspace from the pool and frees it at its
+// end, both in stream order, so the graph holds an allocation and a free node of its
+// own (*owned = true: the caller frees it).
 struct StreamWorkspace {
     int dev;
     hipStream_t stream;
@@ -159,16 +165,27 @@ struct StreamWorkspace {
 struct WorkspaceCache {
     std::mutex mu;
     std::vector<StreamWorkspace> live;
-    std::vector<void*> retired;
 };
 WorkspaceCache& workspace_cache() {
     static WorkspaceCache c;
     return c;
 }
 
-int stream_workspace(size_t bytes, hipStream_t stream, void** out) {
+int stream_workspace(size_t bytes, hipStream_t stream, void** out, bool* owned) {
     *out = nullptr;
+    *owned = false;
     if (bytes == 0) return MHLA_OK;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess) {
+        (void)hipGetLastError();
+        cs = hipStreamCaptureStatusNone;
+    }
+    if (cs != hipStreamCaptureStatusNone) {
+        const int st = pool_alloc(out, bytes, stream);
+        if (st) return st;
+        *owned = true;
+        return MHLA_OK;
+    }
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "workspace device");
@@ -187,7 +204,11 @@ int stream_workspace(size_t bytes, hipStream_t stream, void** out) {
     const int st = pool_alloc(&p, want, stream);
     if (st) return st;
     if (entry) {
-        c.retired.push_back(entry->ptr);
+        e = hipFreeAsync(entry->ptr, stream);  // after the calls already enqueued that use it
+        if (e != hipSuccess) {
+            (void)hipFreeAsync(p, stream);
+            return hip_fail(e, "workspace release");
+        }
         entry->ptr = p;
         entry->bytes = want;
     } else {
@@ -195,6 +216,11 @@ int stream_workspace(size_t bytes, hipStream_t stream, void** out) {
     }
     *out = p;
     return MHLA_OK;
+}
+
+// Releases a workspace that stream_workspace() handed to this call alone.
+hipError_t release_workspace(void* ws, bool owned, hipStream_t stream) {
+    return owned && ws ? hipFreeAsync(ws, stream) : hipSuccess;
 }
 
 int forward_path(int64_t B, int64_t H, int64_t N, int64_t d, int64_t M, int causal, int dtype) {
@@ -248,7 +274,8 @@ int forward_impl(int dtype, const void* q, const void* k, const void* v, const f
     const size_t arr = (size_t)(M * BH * summary_floats(d)) * sizeof(float);
     const size_t total = workspace_bytes(dtype, BH, max_block, d, M, nw);
     void* ws = nullptr;
-    int st2 = stream_workspace(total, stream, &ws);
+    bool owned = false;
+    int st2 = stream_workspace(total, stream, &ws, &owned);
     if (st2) return st2;
     float* S = static_cast<float*>(ws);
     float* St = S + arr / sizeof(float);
@@ -267,7 +294,9 @@ int forward_impl(int dtype, const void* q, const void* k, const void* v, const f
         e = mhla::launch_output(dtype, q, k, v, St, W, os, BH, N, (int)d, M, causal != 0, heads, lay, max_block,
                                 stream);
     }
+    const hipError_t fe = release_workspace(ws, owned, stream);
     if (e != hipSuccess) return hip_fail(e, what);
+    if (fe != hipSuccess) return hip_fail(fe, "workspace release");
     return ok();
 }
 
@@ -329,11 +358,14 @@ int mhla_block_summaries(const void* k, const void* v, int dtype, float* S, int6
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     void* partial = nullptr;
     const size_t pbytes = mhla::summary_partial_bytes(dtype, B * H, N / M, (int)d, M);
-    if (pbytes && (st = stream_workspace(pbytes, s, &partial))) return st;
+    bool owned = false;
+    if (pbytes && (st = stream_workspace(pbytes, s, &partial, &owned))) return st;
     const mhla::BlockLayout equal{nullptr, nullptr};
     hipError_t e = mhla::launch_summaries(dtype, k, v, S, B * H, N, (int)d, M, 0, equal, N / M,
                                           static_cast<float*>(partial), s);
+    const hipError_t fe = release_workspace(partial, owned, s);
     if (e != hipSuccess) return hip_fail(e, "summary kernel");
+    if (fe != hipSuccess) return hip_fail(fe, "workspace release");
     return ok();
 }
 
@@ -348,9 +380,12 @@ int mhla_mix_summaries(const float* S, const float* W, float* St, int64_t BH, in
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     void* frags = nullptr;
     const size_t fbytes = precise ? 0 : mhla::mix_fragment_bytes(M);
-    if (fbytes && (st = stream_workspace(fbytes, s, &frags))) return st;
+    bool owned = false;
+    if (fbytes && (st = stream_workspace(fbytes, s, &frags, &owned))) return st;
     hipError_t e = mhla::launch_mix(S, W, St, BH, (int)d, M, causal != 0, precise != 0, 0, frags, s);
+    const hipError_t fe = release_workspace(frags, owned, s);
     if (e != hipSuccess) return hip_fail(e, "mixing kernel");
+    if (fe != hipSuccess) return hip_fail(fe, "workspace release");
     return ok();
 }
 
@@ -414,10 +449,13 @@ int mhla_backward(const void* q, const void* k, const void* v, int dtype, const 
                           16 * 16;
     const size_t total = fbytes + mhla::mix_fragment_bytes(M);
     void* ws = nullptr;
-    if ((st = stream_workspace(total, stream, &ws))) return st;
+    bool owned = false;
+    if ((st = stream_workspace(total, stream, &ws, &owned))) return st;
     hipError_t e = mhla::launch_backward(dtype, q, k, v, W, dy, dq, dk, dv, dW, B * H, N, (int)d, M, causal != 0,
                                          static_cast<float*>(ws), static_cast<char*>(ws) + fbytes, stream);
+    const hipError_t fe = release_workspace(ws, owned, stream);
     if (e != hipSuccess) return hip_fail(e, "backward kernels");
+    if (fe != hipSuccess) return hip_fail(fe, "workspace release");
     return ok();
 }
 
