@@ -82,7 +82,9 @@ enum { MHLA_PATH_STAGED = 0, MHLA_PATH_FUSED = 1 };
  *     needs no growth allocates nothing and does not wait for the device.  A call
  *     made while its stream is being captured into a HIP graph takes its own
  *     workspace from the pool and frees it at its end, both in stream order, so
- *     the graph owns that memory and never shares the stream's workspace;
+ *     the graph owns that memory and never shares the stream's workspace.  Host
+ *     threads that issue calls on one stream must serialise those calls (the
+ *     workspace relies on their order on the stream);
  *   - fused (non-causal; M <= 16 blocks of at most 16 tokens, or N <= 256 in
  *     blocks of 32, 48 or 64 tokens): one workgroup per (batch, head) pair that
  *     keeps the block summaries and their mix in LDS; no workspace.
