@@ -1,0 +1,40 @@
+"""Host-side parts of bench.py (no GPU): the one-GPU rule of its command line and the
+algorithmic byte counts its roofline figures divide by."""
+import os
+import subprocess
+import sys
+
+import bench
+from token_level_head_amd.workloads import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300, cwd=ROOT)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
+    assert not r.stdout.strip().startswith("{")  # no result line
+
+
+def test_fused_bytes_of_the_dit_workload():
+    # DiT-S/2 at 256x256: 64 images x 6 heads x 256 tokens x 64 features.  Q, K, V are read
+    # once as bf16 (2 bytes), Y written once as float32, W (16 x 16 float32) read once.
+    elems = 64 * 6 * 256 * 64
+    assert elems == 6291456
+    expect = 3 * elems * 2 + elems * 4 + 16 * 16 * 4
+    assert expect == 62915584
+    assert bench.kernel_bytes(WORKLOADS["dit_s2_256"])["fused"] == expect
+
+
+def test_staged_bytes_of_the_long_dit_workload():
+    # DiT-S/2 at 4096x4096: one image, 6 heads, 65536 tokens, d = 64, 256 blocks.
+    # Summaries: 256 blocks x 6 pairs x (64*64 + 64) float32 = 25,559,040 bytes.
+    tok = 6 * 65536 * 64 * 2          # one bf16 token tensor
+    summ = 256 * 6 * 4160 * 4
+    assert summ == 25559040
+    b = bench.kernel_bytes(WORKLOADS["dit_s2_4096"])
+    assert b["summaries"] == 2 * tok + summ        # K, V in; S out
+    assert b["mix"] == 2 * summ + 256 * 256 * 4    # S in, S~ out, W in
+    assert b["output"] == tok + summ + 2 * tok     # Q, S~ in; float32 Y out (twice the bf16 size)
