@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the MHLA forward pass on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload dit_s2_256] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--workload sana_128] [--gpus 1]
     python bench.py --sweep          # N x M throughput grid (the paper's scaling study)
     python bench.py --decode         # streaming causal decode step (lm_causal_8k shape)
     python bench.py --backward       # backward pass (dq, dk, dv, dW) on the workload
@@ -89,26 +89,64 @@ def measured_traffic(workload, stage):
     return None
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(w, q, k, v, W, budget_s):
+    """The oracle (test infrastructure, never tuned) on this host's cores, on a bounded
+    sample of the workload: whole (batch, head) pairs -- the oracle's unit of work, each
+    pair the full sequence of N tokens -- taken in [B][H] order, once on one thread and
+    once on all the threads this process may use (at most 16, the host share of one
+    GPU).  Rates are scaled to the metric's unit: a token of the workload is H
+    token-heads, so tokens/s = pairs * N / H / seconds."""
     import oracle  # test infrastructure: used only for this reported baseline
 
     orc = oracle.default_oracle()
-    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
-    cores = max(1, min(cores, 16))
-    orc.forward(q, k, v, W, causal=w.causal, nthreads=cores)  # warm caches and page-in
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        orc.forward(q, k, v, W, causal=w.causal, nthreads=cores)
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= budget_s:
-            break
+    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    threads = max(1, min(avail, 16))
+    BH = w.B * w.H
+    shape = (1, BH, w.N, w.d)
+    qs, ks, vs = (np.ascontiguousarray(a).reshape(shape) for a in (q, k, v))
+
+    def run(pairs, nthreads):
+        sl = slice(0, pairs)
+        t0 = time.perf_counter()
+        orc.forward(qs[:, sl], ks[:, sl], vs[:, sl], W, causal=w.causal, nthreads=nthreads)
+        return time.perf_counter() - t0
+
+    def measured(nthreads, unit):
+        """Calibrate on `unit` pairs, then time enough pairs (a multiple of unit) for
+        about budget_s seconds."""
+        t_unit = run(unit, nthreads)
+        reps = max(1, min(BH // unit, int(budget_s / max(t_unit, 1e-6))))
+        pairs = reps * unit
+        dt = run(pairs, nthreads)
+        return pairs, dt
+
+    p1, t1 = measured(1, 1)
+    unit = min(threads, BH)
+    pm, tm = measured(threads, unit)
+    rate = lambda pairs, dt: pairs * w.N / w.H / dt  # noqa: E731
     return {
-        "value": w.tokens * reps / dt,
+        "value": rate(pm, tm),
         "unit": "tokens/s",
-        "cores": cores,
+        "cores": threads,
         "kind": "oracle",
-        "sample": f"the whole {w.key} batch ({w.tokens} tokens), repeated {reps}x in {dt:.2f} s on {cores} threads",
+        "sample": f"{pm} of the {BH} (batch, head) pairs of {w.key} (each {w.N} tokens, d={w.d}, M={w.M}) "
+                  f"in {tm:.2f} s on {threads} threads; tokens/s = pairs * N / H / s",
+        "single_thread": {"value": rate(p1, t1), "unit": "tokens/s", "cores": 1,
+                          "sample": f"{p1} pairs in {t1:.2f} s on 1 thread"},
+        "host": {"nproc": os.cpu_count(), "threads_available": avail, "cpu_model": _cpu_model()},
     }
 
 
@@ -293,8 +331,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="dit_s2_256", choices=sorted(WORKLOADS))
-    ap.add_argument("--cpu-budget", type=float, default=1.5, help="seconds of oracle wall time")
+    ap.add_argument("--workload", default="sana_128", choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-budget", type=float, default=5.0,
+                    help="seconds of oracle wall time for each of the one-thread and all-thread samples")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode", action="store_true",
                     help="time the streaming causal decode step (one token per call) on the workload's "

@@ -268,6 +268,27 @@ int mhla_decode_step(const void* q, const void* k, const void* v, int dtype, con
  */
 int mhla_unpack_summaries(const float* packed, int64_t count, int64_t d, float* S, float* z);
 
+/*
+ * Frees the workspace the library keeps for `stream` on the current device (the
+ * buffer that staged mhla_forward* calls, mhla_block_summaries,
+ * mhla_mix_summaries and mhla_backward share on that stream), in stream order:
+ * work already enqueued on the stream that uses it completes first.  Call it
+ * before destroying a stream that the library was called on: the cache is keyed
+ * by the stream handle, and a stream created later may receive the same handle.
+ * A later call on the stream takes a new workspace.  Returns MHLA_OK also when
+ * no workspace was held; MHLA_ERR_HIP if the free could not be enqueued.
+ */
+int mhla_release_workspace(mhla_stream_t stream);
+
+/*
+ * Test hook for the allocation-failure path: the next `count` calls that need
+ * workspace memory (staged forward, stage calls that use it, backward) return
+ * MHLA_ERR_NO_MEMORY before making any HIP call, so nothing is enqueued, exactly
+ * as when the allocation itself fails.  count <= 0 switches it off.  Not meant
+ * for production use.
+ */
+void mhla_debug_fail_workspace(int count);
+
 /* Human-readable name of a status code (static storage). */
 const char* mhla_status_string(int status);
 

@@ -208,3 +208,22 @@ def test_unpack_validation(mhla_lib):
     p = buf.ctypes.data_as(ctypes.c_void_p)
     assert mhla_lib.mhla_unpack_summaries(None, 1, 16, p, p) == mh.MHLA_ERR_INVALID_ARG
     assert mhla_lib.mhla_unpack_summaries(p, 1, 20, p, p) == mh.MHLA_ERR_UNSUPPORTED
+
+
+def test_no_memory_path_enqueues_nothing(mhla_lib):
+    """A failed workspace allocation returns MHLA_ERR_NO_MEMORY before any HIP call (the
+    test hook fails the request; no device is touched, so this runs without a GPU)."""
+    p = [FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5]
+    try:
+        mh.mhla_debug_fail_workspace(2)
+        # staged shapes (the fused path takes no workspace): C3's block count, and the backward pass
+        assert mhla_lib.mhla_forward(*p, 1, 2, 4096, 64, 256, 0, None) == mh.MHLA_ERR_NO_MEMORY
+        assert "simulated" in mh.mhla_last_error()
+        g = [FAKE * 6, FAKE * 7, FAKE * 8, FAKE * 9]
+        assert mhla_lib.mhla_backward(FAKE, FAKE * 2, FAKE * 3, 0, FAKE * 4, FAKE * 5, *g, 1, 1, 256, 16, 4, 0,
+                                      None) == mh.MHLA_ERR_NO_MEMORY
+        # validation still comes first: a bad argument is reported as such, not as memory
+        mh.mhla_debug_fail_workspace(1)
+        assert mhla_lib.mhla_forward(*p, 1, 2, 4100, 64, 256, 0, None) == mh.MHLA_ERR_INVALID_ARG
+    finally:
+        mh.mhla_debug_fail_workspace(0)

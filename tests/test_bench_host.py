@@ -38,3 +38,34 @@ def test_staged_bytes_of_the_long_dit_workload():
     assert b["summaries"] == 2 * tok + summ        # K, V in; S out
     assert b["mix"] == 2 * summ + 256 * 256 * 4    # S in, S~ out, W in
     assert b["output"] == tok + summ + 2 * tok     # Q, S~ in; float32 Y out (twice the bf16 size)
+
+
+def test_default_workload_is_the_largest_single_gpu_config():
+    src = open(os.path.join(ROOT, "bench.py")).read()
+    assert 'default="sana_128"' in src
+    by_bytes = max((w for w in WORKLOADS.values() if w.dtype == "bf16"),
+                   key=lambda w: 3 * w.B * w.H * w.N * w.d * 2 + w.B * w.H * w.N * w.d * 4)
+    assert by_bytes.key == "sana_128"
+
+
+def test_staged_bytes_of_the_sana_workload():
+    # 4 images x 70 heads x 16384 tokens x 32 features; 64 blocks of 256 tokens.
+    tok = 4 * 70 * 16384 * 32 * 2      # one bf16 token tensor: 293,601,280 bytes
+    assert tok == 293601280
+    summ = 64 * 280 * (32 * 32 + 32) * 4
+    assert summ == 75694080
+    b = bench.kernel_bytes(WORKLOADS["sana_128"])
+    assert b["summaries"] == 2 * tok + summ
+    assert b["mix"] == 2 * summ + 64 * 64 * 4
+    assert b["output"] == tok + summ + 2 * tok
+
+
+def test_cpu_baseline_reports_host_and_both_samples():
+    from token_level_head_amd.workloads import make_inputs
+
+    w = WORKLOADS["sana_128"].shrink(B=1, H=3, N=1024, M=4)
+    q, k, v, W = make_inputs(w)
+    cb = bench.cpu_baseline(w, q, k, v, W, 0.05)
+    assert cb["kind"] == "oracle" and cb["unit"] == "tokens/s" and cb["value"] > 0
+    assert 1 <= cb["cores"] <= 16 and cb["single_thread"]["cores"] == 1 and cb["single_thread"]["value"] > 0
+    assert cb["host"]["nproc"] >= 1 and cb["host"]["cpu_model"]

@@ -312,7 +312,8 @@ def test_errors_raise_on_device():
     with pytest.raises(mh.MhlaError) as e:
         mh.mhla_forward(q, q, q, W, out)
     assert e.value.status == mh.MHLA_ERR_INVALID_ARG
-    q = torch.zeros((1, 1, 256, 64), dtype=torch.bfloat16, device="cuda")
-    with pytest.raises(mh.MhlaError) as e:  # out aliases q
-        mh.mhla_forward(q, q, q, W, q.view(torch.float32).view(1, 1, 128, 64))
+    out = torch.zeros((1, 1, 256, 64), dtype=torch.float32, device="cuda")
+    q = out.view(-1).view(torch.bfloat16)[: 256 * 64].view(1, 1, 256, 64)  # the first half of out
+    with pytest.raises(mh.MhlaError) as e:  # out overlaps q
+        mh.mhla_forward(q, q, q, W, out)
     assert e.value.status == mh.MHLA_ERR_INVALID_ARG

@@ -403,13 +403,7 @@ hipError_t launch_fused(const void* q, const void* k, const void* v, const float
     // Between one and two pairs per CU, the CUs holding two whole pairs would set the
     // time: split 2 * CUs - BH pairs into column halves, so that every CU gets a whole
     // pair and a half (d >= 32; d = 16 has a single column chunk).
-    static int cus = 0;
-    if (!cus) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-            cus = 256;
-    }
+    const int cus = device_cu_count();
     const int64_t nhalf = (D >= 32 && BH > cus && BH < 2 * (int64_t)cus) ? 2 * cus - BH : 0;
     const int nfull = (int)(BH - nhalf);
     const dim3 grid((unsigned)(nfull + 2 * nhalf)), block(64 * kWaves);

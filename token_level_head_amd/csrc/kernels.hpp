@@ -8,6 +8,11 @@
 
 namespace mhla {
 
+// Compute units of the current device (cached per device, safe to call from several
+// host threads at once; 256 if the query fails).  Launchers size persistent grids and
+// work splits with it.
+int device_cu_count();
+
 constexpr int kDtypeBF16 = 0;
 constexpr int kDtypeF32 = 1;
 

@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -17,9 +18,38 @@
 #include "kernels.hpp"
 #include "mhla.h"
 
+namespace mhla {
+
+int device_cu_count() {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cached[kMaxDevices];  // 0: not queried yet (static storage starts zeroed)
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    if (dev >= 0 && dev < kMaxDevices) {
+        const int c = cached[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) {
+        (void)hipGetLastError();
+        cus = 256;
+    }
+    if (dev >= 0 && dev < kMaxDevices) cached[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
+}  // namespace mhla
+
 namespace {
 
 thread_local char g_err[512] = "";
+
+// Test hook (mhla_debug_fail_workspace): number of upcoming workspace requests that
+// fail as if the allocation had failed.
+std::atomic<int> g_fail_workspace{0};
 
 int fail(int status, const char* fmt, ...) {
     va_list ap;
@@ -175,6 +205,10 @@ int stream_workspace(size_t bytes, hipStream_t stream, void** out, bool* owned) 
     *out = nullptr;
     *owned = false;
     if (bytes == 0) return MHLA_OK;
+    for (int n = g_fail_workspace.load(); n > 0;)
+        if (g_fail_workspace.compare_exchange_weak(n, n - 1))
+            return fail(MHLA_ERR_NO_MEMORY, "workspace of %zu bytes: allocation failure simulated by the test hook",
+                        bytes);
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(stream, &cs) != hipSuccess) {
         (void)hipGetLastError();
@@ -221,6 +255,23 @@ int stream_workspace(size_t bytes, hipStream_t stream, void** out, bool* owned) 
 // Releases a workspace that stream_workspace() handed to this call alone.
 hipError_t release_workspace(void* ws, bool owned, hipStream_t stream) {
     return owned && ws ? hipFreeAsync(ws, stream) : hipSuccess;
+}
+
+// Frees the cached workspace of (current device, stream), in stream order.
+int drop_stream_workspace(hipStream_t stream) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "workspace device");
+    WorkspaceCache& c = workspace_cache();
+    std::lock_guard<std::mutex> lock(c.mu);
+    for (size_t i = 0; i < c.live.size(); ++i) {
+        if (c.live[i].dev != dev || c.live[i].stream != stream) continue;
+        e = hipFreeAsync(c.live[i].ptr, stream);  // after the work already enqueued that uses it
+        if (e != hipSuccess) return hip_fail(e, "workspace release");
+        c.live.erase(c.live.begin() + (std::ptrdiff_t)i);
+        break;
+    }
+    return ok();
 }
 
 int forward_path(int64_t B, int64_t H, int64_t N, int64_t d, int64_t M, int causal, int dtype) {
@@ -510,6 +561,12 @@ int mhla_unpack_summaries(const float* packed, int64_t count, int64_t d, float* 
     }
     return ok();
 }
+
+int mhla_release_workspace(mhla_stream_t stream) {
+    return drop_stream_workspace(reinterpret_cast<hipStream_t>(stream));
+}
+
+void mhla_debug_fail_workspace(int count) { g_fail_workspace.store(count > 0 ? count : 0); }
 
 const char* mhla_status_string(int status) {
     switch (status) {

@@ -827,13 +827,7 @@ hipError_t launch_mix(const float* S, const float* W, float* St, int64_t BH, int
     }
     if (M <= 256 && M * ld * 4 < (int64_t(1) << 32) - 64) {  // 64 < M <= 256: persistent tile walk
         const int64_t ntiles = ncols / 16;  // d*d + d is a multiple of 16
-        static int cus = 0;
-        if (!cus) {
-            int dev = 0;
-            if (hipGetDevice(&dev) != hipSuccess ||
-                hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-                cus = 256;
-        }
+        const int cus = device_cu_count();
         const dim3 grid((unsigned)std::max<int64_t>(1, std::min<int64_t>(ntiles, cus)), gy);
         if (causal)
             mix_stream_kernel<true, false><<<grid, dim3(512), 0, stream>>>(S, W, St, ncols, ld, (int)M, ntiles);
