@@ -138,13 +138,18 @@ __device__ __forceinline__ void store_dl(rsrc_t r, int g, int n, int i, const fl
 
 // phi(x) = ELU(x) + 1 = max(x, 0) + exp(min(x, 0)) and its derivative, with the
 // hardware exp2 (relative error about |x| 2^-24 + 1 ulp, far inside what the split
-// products keep).
+// products keep).  min(x, 0) is taken as x - max(x, 0), exact for finite x, so that
+// a NaN input stays NaN (max(NaN, 0) is 0 under IEEE maxNum); relu0 as in common.hpp.
 __device__ __forceinline__ float bexp(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
-__device__ __forceinline__ float phi_b(float x) { return fmaxf(x, 0.f) + bexp(fminf(x, 0.f)); }
+__device__ __forceinline__ float phi_b(float x) {
+    const float m = relu0(x);
+    return m + bexp(x - m);
+}
 __device__ __forceinline__ float phi_grad(float x, float& dphi) {
-    const float e = bexp(fminf(x, 0.f));
+    const float m = relu0(x);
+    const float e = bexp(x - m);
     dphi = x > 0.f ? 1.f : e;
-    return fmaxf(x, 0.f) + e;
+    return m + e;
 }
 
 // Row-layout values as 16x16x32 operands (slot 8ks + e = group-local feature); the

@@ -29,17 +29,36 @@ __device__ __forceinline__ float bf16v_to_f32(__bf16 b) {
     return __uint_as_float((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
-// phi(x) = ELU(x) + 1 ("Linear Attention 笔记" §2) = max(x, 0) + exp(min(x, 0)).
-// phi_fast is for results rounded to bfloat16 afterwards: with y = x log2(e),
-// phi = 2^min(y, 0) + max(y, 0) ln(2), i.e. one multiply, a min, a max, the
-// hardware exp2 and one fma, with no compare and select.  (min and max act on y,
-// the result of an arithmetic op, so they need no quieting of a raw input.)
-// phi_precise keeps float32 accuracy.
-__device__ __forceinline__ float phi_fast(float x) {
-    const float y = x * 1.44269504088896341f;
-    return fmaf(fmaxf(y, 0.f), 0.693147180559945309f, __builtin_amdgcn_exp2f(fminf(y, 0.f)));
+// phi(x) = ELU(x) + 1 ("Linear Attention 笔记" §2) = max(x, 0) + exp(min(x, 0)),
+// formed as m + exp(x - m) with m = max(x, 0): x - m is exactly min(x, 0) for every
+// finite x (x - x = 0 above zero, x - 0 = x below), and a NaN input stays NaN through
+// the subtraction, where a min (IEEE maxNum/minNum: max(NaN, 0) = 0) would turn it
+// into phi = 1.  For x > 0 the result is x + 1 rounded once.  No step is a product
+// feeding an add, so floating-point contraction cannot fuse any two of them (fusing
+// x*log2(e) into a subtraction of its own rounded value would leave that product's
+// rounding error inside the exponential).
+// phi_fast is for results rounded to bfloat16 afterwards: the exponential is the
+// hardware exp2 of (x - m) log2(e): a max, a subtract, a multiply, exp2 and an add.
+// phi_precise keeps float32 accuracy.  Both give NaN for x = NaN and x = +inf.
+//
+// relu0(x) = max(x, 0) as the single v_max_f32.  Written through fmaxf, the compiler
+// first quiets x (a second v_max_f32 x, x) whenever x is not the result of arithmetic
+// -- here it is usually a bf16 value widened by a shift -- since IEEE maxNum must not
+// see a signalling NaN.  phi needs no quieting: whatever the max returns for a NaN
+// (0, or a quiet NaN), the subtraction x - m is NaN and so is phi.
+__device__ __forceinline__ float relu0(float x) {
+    float m;
+    asm("v_max_f32 %0, 0, %1" : "=v"(m) : "v"(x));
+    return m;
 }
-__device__ __forceinline__ float phi_precise(float x) { return fmaxf(x, 0.f) + expf(fminf(x, 0.f)); }
+__device__ __forceinline__ float phi_fast(float x) {
+    const float m = relu0(x);
+    return m + __builtin_amdgcn_exp2f((x - m) * 1.44269504088896341f);
+}
+__device__ __forceinline__ float phi_precise(float x) {
+    const float m = relu0(x);
+    return m + expf(x - m);
+}
 
 // Hardware reciprocal (about 1 ulp).  Every denominator here is >= 1e-6 and finite.
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
