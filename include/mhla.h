@@ -94,6 +94,29 @@ int mhla_forward(const void* q, const void* k, const void* v, const float* W, fl
                  int64_t B, int64_t H, int64_t N, int64_t d, int64_t M, int causal,
                  mhla_stream_t stream);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): mhla_forward whose staged path
+ * takes its workspace from a fixed scratch array that the library keeps on each device
+ * (MHLA_NOALLOC_SCRATCH_BYTES bytes, held from the moment the library's code is
+ * loaded on that device until the process ends) instead of allocating one.  The call
+ * makes no allocation and no free.  Arguments, paths and results are those of
+ * mhla_forward, bit for bit; the caller still provides q, k, v, W and out.  Sizes whose
+ * workspace (mhla_workspace_bytes) exceeds MHLA_NOALLOC_SCRATCH_BYTES give
+ * MHLA_ERR_UNSUPPORTED with nothing enqueued (the fused path needs no workspace and has
+ * no such limit).  The first call on a device looks up that device's array address
+ * (a host-side lookup, not a stream operation).
+ *
+ * Every call on one device uses that device's one array, which keeps the last call's
+ * contents (no stage reads anything it has not written in the same call, so nothing
+ * needs clearing).  Calls that overlap in time on one device -- on different streams,
+ * or from several host threads -- race on it and give wrong results: serialise them.
+ */
+#define MHLA_NOALLOC_SCRATCH_BYTES ((int64_t)256 << 20)
+int mhla_forward_noalloc(const void* q, const void* k, const void* v, const float* W, float* out,
+                         int64_t B, int64_t H, int64_t N, int64_t d, int64_t M, int causal,
+                         mhla_stream_t stream);
+
 /* Same as mhla_forward with float32 q/k/v; every step runs in float32. */
 int mhla_forward_f32(const float* q, const float* k, const float* v, const float* W, float* out,
                      int64_t B, int64_t H, int64_t N, int64_t d, int64_t M, int causal,

@@ -29,6 +29,7 @@ MHLA_OPT_CAUSAL = 1
 MHLA_OPT_NO_NORMALIZER = 2
 MHLA_OPT_OUT_BF16 = 4
 MHLA_OPT_W_PER_HEAD = 8
+MHLA_NOALLOC_SCRATCH_BYTES = 256 << 20
 
 # Every symbol include/mhla.h declares, with (restype, argtypes).
 _P = ctypes.c_void_p
@@ -37,6 +38,7 @@ _I = ctypes.c_int
 SIGNATURES = {
     "mhla_forward": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _P]),
     "mhla_forward_f32": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _P]),
+    "mhla_forward_noalloc": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _P]),
     "mhla_forward_ex": (_I, [_P, _P, _P, _I, _P, _P, _I64, _I64, _I64, _I64, _I64, ctypes.c_uint, _P]),
     "mhla_forward_blocks": (_I, [_P, _P, _P, _I, _P, _P, _I64, _I64, _I64, _I64, _I64, _P, _P, _I64, ctypes.c_uint,
                                  _P]),
@@ -193,6 +195,24 @@ def mhla_forward(q, k, v, W, out, causal=False, stream=None):
     with ctx:
         _check(load_library().mhla_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(W), _ptr(out), B, H, N, d, M,
                                            int(bool(causal)), s))
+    return out
+
+
+def mhla_forward_noalloc(q, k, v, W, out, causal=False, stream=None):
+    """mhla_forward with its workspace in the library's fixed per-device scratch array
+    (no allocation; workspaces above MHLA_NOALLOC_SCRATCH_BYTES are refused; calls that
+    overlap on one device race)."""
+    _dtype(q, "q", torch.bfloat16)
+    _tokens(q)
+    _same(q, "q", k=k, v=v)
+    M = _mixing(W)
+    _dtype(out, "out", torch.float32)
+    _shape(out, "out", q.shape)
+    ctx, s = _launch(_device_of(q=q, k=k, v=v, W=W, out=out), stream)
+    B, H, N, d = q.shape
+    with ctx:
+        _check(load_library().mhla_forward_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(W), _ptr(out), B, H, N, d, M,
+                                                   int(bool(causal)), s))
     return out
 
 

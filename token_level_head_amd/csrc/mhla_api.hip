@@ -257,6 +257,44 @@ hipError_t release_workspace(void* ws, bool owned, hipStream_t stream) {
     return owned && ws ? hipFreeAsync(ws, stream) : hipSuccess;
 }
 
+// Scratch memory of mhla_forward_noalloc: a file-scope device array, one copy per device
+// (each holds it from the moment the library's code is loaded there until the process
+// ends).  In host code `scratch` names a host-side stand-in, not device memory: the
+// device address of each device's copy is looked up once, with that device current,
+// and only that address is used.
+constexpr size_t kNoAllocScratchBytes = size_t(MHLA_NOALLOC_SCRATCH_BYTES);
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+struct ScratchAddresses {
+    std::mutex mu;
+    std::vector<void*> ptr;  // per device; null until looked up
+};
+ScratchAddresses& scratch_addresses() {
+    static ScratchAddresses a;
+    return a;
+}
+
+int fixed_workspace(void** out) {
+    *out = nullptr;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "scratch device");
+    ScratchAddresses& a = scratch_addresses();
+    std::lock_guard<std::mutex> lock(a.mu);
+    if ((int)a.ptr.size() <= dev) a.ptr.resize(dev + 1, nullptr);
+    if (!a.ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "scratch array address");
+        }
+        a.ptr[dev] = p;
+    }
+    *out = a.ptr[dev];
+    return MHLA_OK;
+}
+
 // Frees the cached workspace of (current device, stream), in stream order.
 int drop_stream_workspace(hipStream_t stream) {
     int dev = 0;
@@ -283,9 +321,15 @@ constexpr unsigned kKnownOptions = MHLA_OPT_CAUSAL | MHLA_OPT_NO_NORMALIZER | MH
 
 // order/offsets: a token list per block (both null: M equal contiguous blocks);
 // max_block bounds the block lengths for launch planning.
+// fixed: when given, the staged path takes its workspace from there (at most
+// fixed_cap bytes; larger needs give MHLA_ERR_UNSUPPORTED before anything is enqueued)
+// instead of the stream's cached workspace, so the call allocates nothing.
+int fixed_workspace(void** out);
+
 int forward_impl(int dtype, const void* q, const void* k, const void* v, const float* W, void* out, int64_t B,
                  int64_t H, int64_t N, int64_t d, int64_t M, unsigned options, const int32_t* order,
-                 const int32_t* offsets, int64_t max_block, mhla_stream_t stream_) {
+                 const int32_t* offsets, int64_t max_block, mhla_stream_t stream_, bool fixed = false,
+                 size_t fixed_cap = 0) {
     const bool listed = order || offsets;
     int st = check_sizes(B, H, N, d, M, !listed);
     if (st) return st;
@@ -326,8 +370,16 @@ int forward_impl(int dtype, const void* q, const void* k, const void* v, const f
     const size_t total = workspace_bytes(dtype, BH, max_block, d, M, nw);
     void* ws = nullptr;
     bool owned = false;
-    int st2 = stream_workspace(total, stream, &ws, &owned);
-    if (st2) return st2;
+    if (fixed) {
+        if (total > fixed_cap)
+            return fail(MHLA_ERR_UNSUPPORTED, "these sizes need %zu bytes of workspace, more than the %zu-byte scratch "
+                        "array of the non-allocating entry point", total, fixed_cap);
+        const int st2 = fixed_workspace(&ws);
+        if (st2) return st2;
+    } else {
+        const int st2 = stream_workspace(total, stream, &ws, &owned);
+        if (st2) return st2;
+    }
     float* S = static_cast<float*>(ws);
     float* St = S + arr / sizeof(float);
     void* frags = St + arr / sizeof(float);
@@ -359,6 +411,12 @@ int mhla_forward(const void* q, const void* k, const void* v, const float* W, fl
                  int64_t N, int64_t d, int64_t M, int causal, mhla_stream_t stream) {
     return forward_impl(mhla::kDtypeBF16, q, k, v, W, out, B, H, N, d, M, causal ? MHLA_OPT_CAUSAL : 0u, nullptr,
                         nullptr, 0, stream);
+}
+
+int mhla_forward_noalloc(const void* q, const void* k, const void* v, const float* W, float* out, int64_t B,
+                         int64_t H, int64_t N, int64_t d, int64_t M, int causal, mhla_stream_t stream) {
+    return forward_impl(mhla::kDtypeBF16, q, k, v, W, out, B, H, N, d, M, causal ? MHLA_OPT_CAUSAL : 0u, nullptr,
+                        nullptr, 0, stream, true, kNoAllocScratchBytes);
 }
 
 int mhla_forward_f32(const float* q, const float* k, const float* v, const float* W, float* out, int64_t B,
