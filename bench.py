@@ -80,7 +80,7 @@ def measured_traffic(workload, stage):
         return None
     with open(path) as f:
         prof = json.load(f)
-    prefix = {"fused": "fused_small_kernel", "summaries": "summaries_", "mix": "mix_", "output": "output_"}[stage]
+    prefix = {"fused": "fused_", "summaries": "summaries_", "mix": "mix_", "output": "output_"}[stage]
     for name, k in prof["kernels"].items():
         if name.startswith(prefix):
             if k.get("source_digest") != kernel_source_digest(name):

@@ -172,7 +172,7 @@ def test_backward_validation(mhla_lib):
 
 
 def test_forward_path_selection(mhla_lib):
-    # non-causal bf16 with blocks of at most 16 tokens and at most 16 blocks: fused; otherwise staged
+    # non-causal bf16 with at most 256 tokens in at most 16 blocks: fused; otherwise staged
     assert mh.mhla_forward_path(64, 6, 256, 64, 16) == mh.MHLA_PATH_FUSED
     assert mh.mhla_forward_path(64, 6, 256, 64, 16, causal=True) == mh.MHLA_PATH_STAGED
     assert mh.mhla_forward_path(64, 6, 256, 64, 16, dtype=mh.MHLA_DTYPE_F32) == mh.MHLA_PATH_STAGED
@@ -182,6 +182,9 @@ def test_forward_path_selection(mhla_lib):
     assert mh.mhla_forward_path(256, 1, 64, 16, 64) == mh.MHLA_PATH_STAGED     # M > 16
     assert mh.mhla_forward_path(8, 2, 272, 64, 16) == mh.MHLA_PATH_STAGED      # 17-token blocks
     assert mh.mhla_forward_path(8, 2, 60, 32, 5) == mh.MHLA_PATH_FUSED
+    assert mh.mhla_forward_path(8, 2, 256, 64, 1) == mh.MHLA_PATH_FUSED       # one block of 256 tokens
+    assert mh.mhla_forward_path(8, 2, 200, 32, 8) == mh.MHLA_PATH_FUSED       # 25-token blocks
+    assert mh.mhla_forward_path(8, 2, 512, 64, 16) == mh.MHLA_PATH_STAGED     # N > 256
     assert mh.mhla_forward_path(1, 1, 250, 64, 16) == -1
 
 

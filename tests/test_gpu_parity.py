@@ -142,8 +142,12 @@ FUSED = [  # (B, H, N, d, M): shapes mhla_forward runs through the fused on-chip
     (8, 2, 192, 32, 4),     # blocks of 48 tokens: 12 tiles, 3 per block
     (16, 1, 128, 16, 2),    # 8 tiles, 4 per block
     (4, 2, 256, 64, 8),     # blocks of 32 tokens
-    (100, 3, 256, 32, 16),  # 300 pairs: some split into column halves over two workgroups
-    (70, 5, 160, 64, 16),   # 350 pairs, 10-token blocks, column halves
+    (100, 3, 256, 32, 16),  # 300 pairs: some run as two halves of their query tiles
+    (70, 5, 160, 64, 16),   # 350 pairs, 10-token blocks, halves
+    (24, 2, 256, 64, 1),    # one block of 256 tokens (global linear attention)
+    (6, 3, 200, 32, 8),     # 25-token blocks: block edges inside 4-key groups, 7 padded keys
+    (12, 1, 96, 16, 3),     # blocks of 32 tokens, d = 16, three 32-key steps
+    (260, 1, 224, 64, 14),  # 260 pairs (4 in halves), 14 query tiles, 16-token blocks
 ]
 
 

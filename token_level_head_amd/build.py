@@ -26,7 +26,7 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, 
 # The source file that defines each kernel family (by kernel-name prefix); a
 # kernel's measurements stay valid while this file and the shared headers do.
 KERNEL_SOURCES = [
-    ("fused_small_kernel", "fused.hip"),
+    ("fused_", "fused.hip"),
     ("summaries_", "summary.hip"),
     ("mix_", "mix.hip"),
     ("wsplit_", "mix.hip"),
