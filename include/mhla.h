@@ -255,6 +255,19 @@ int mhla_backward(const void* q, const void* k, const void* v, int dtype, const 
                   int64_t M, int causal, mhla_stream_t stream);
 
 /*
+ * The backward pass with options: MHLA_OPT_CAUSAL (as causal != 0 above) and
+ * MHLA_OPT_NO_NORMALIZER, the gradients of the forward form without the normaliser
+ * (y_t = phi(q_t)^T S~_i, causal plus W[i,i] phi(q_t)^T P_t; §4.1, remark on the
+ * output), where the den terms of the chain rule vanish and dnum_t = dy_t.
+ * MHLA_OPT_OUT_BF16 and MHLA_OPT_W_PER_HEAD give MHLA_ERR_UNSUPPORTED, unknown bits
+ * MHLA_ERR_INVALID_ARG.  mhla_backward(..., causal, ...) is mhla_backward_ex(...,
+ * causal ? MHLA_OPT_CAUSAL : 0, ...).  Everything else as for mhla_backward.
+ */
+int mhla_backward_ex(const void* q, const void* k, const void* v, int dtype, const float* W, const float* dy,
+                     float* dq, float* dk, float* dv, float* dW, int64_t B, int64_t H, int64_t N, int64_t d,
+                     int64_t M, unsigned options, mhla_stream_t stream);
+
+/*
  * Streaming causal decoding (App. C inference: fold the new token into its
  * block's running summary, re-mix, read out; the running sum is the recurrence of
  * "Linear Attention 笔记" §4).  One call produces y_t for token t of every
@@ -283,6 +296,21 @@ int64_t mhla_decode_state_bytes(int64_t B, int64_t H, int64_t d, int64_t M);
 int mhla_decode_step(const void* q, const void* k, const void* v, int dtype, const float* W, float* state,
                      float* out, int64_t B, int64_t H, int64_t d, int64_t M, int64_t C, int64_t t,
                      mhla_stream_t stream);
+
+/*
+ * Decoding with options (the stream of calls as for mhla_decode_step; the decode is
+ * always causal, MHLA_OPT_CAUSAL may be given or not): MHLA_OPT_NO_NORMALIZER writes
+ * the numerator phi(q_t)^T (S~_i + W[i,i] P_t) alone (§4.1, remark on the output, the
+ * form meant for long sequences), equal up to rounding to row t of mhla_forward_ex
+ * with MHLA_OPT_CAUSAL | MHLA_OPT_NO_NORMALIZER; MHLA_OPT_W_PER_HEAD takes W as
+ * [H][M][M], head h mixing with W + h*M*M.  MHLA_OPT_OUT_BF16 gives
+ * MHLA_ERR_UNSUPPORTED, unknown bits MHLA_ERR_INVALID_ARG.  mhla_decode_step is
+ * mhla_decode_step_ex(..., MHLA_OPT_CAUSAL, ...).  A state must be driven with the
+ * same options from t = 0 on.
+ */
+int mhla_decode_step_ex(const void* q, const void* k, const void* v, int dtype, const float* W, float* state,
+                        float* out, int64_t B, int64_t H, int64_t d, int64_t M, int64_t C, int64_t t,
+                        unsigned options, mhla_stream_t stream);
 
 /*
  * Host-only helper (no HIP calls): decodes `count` packed summary vectors in

@@ -9,7 +9,8 @@ chain rule through the four steps of §4.1 (and App. C's causal form):
     num_t = phi(q_t) A_t,   den_t = phi(q_t) . a_t + 1e-6,   y_t = num_t / den_t
     A_t = S~_i (+ W[i,i] P_t causal),   a_t = z~_i (+ W[i,i] p_t causal)
 
-so that, with dnum_t = dy_t / den_t and dden_t = -(dy_t . y_t) / den_t,
+so that, with dnum_t = dy_t / den_t and dden_t = -(dy_t . y_t) / den_t (without the
+normaliser, y_t = num_t: dnum_t = dy_t and dden_t = 0),
 
     d phi(q_t) = A_t dnum_t + dden_t a_t
     dS~_i      = sum_{t in i} phi(q_t) dnum_t^T,   dz~_i = sum_{t in i} dden_t phi(q_t)
@@ -35,11 +36,13 @@ def dphi(x):
     return np.where(x > 0, 1.0, np.exp(np.minimum(x, 0.0)))
 
 
-def backward(q, k, v, W, dy, causal=False):
+def backward(q, k, v, W, dy, causal=False, normalize=True):
     """(dq, dk, dv, dW) of sum(dy * forward(q, k, v, W)) in binary64.
 
     q, k, v, dy: [B, H, N, d]; W: [M, M] (causal: entries above the diagonal are
     never used and get zero gradient); blocks are contiguous, C = N / M.
+    normalize=False differentiates the form without the normaliser (MHLA §4.1,
+    remark on the output), y_t = num_t: then dnum_t = dy_t and the den terms vanish.
     """
     q, k, v, dy = (np.asarray(a, dtype=np.float64) for a in (q, k, v, dy))
     W = np.asarray(W, dtype=np.float64)
@@ -76,10 +79,14 @@ def backward(q, k, v, W, dy, causal=False):
                     else:
                         A, a = St, zt
                     num = Fq[t] @ A
-                    den = Fq[t] @ a + EPS
-                    y = num / den
-                    dnum = dY[t] / den
-                    dden = -(dY[t] @ y) / den
+                    if normalize:
+                        den = Fq[t] @ a + EPS
+                        y = num / den
+                        dnum = dY[t] / den
+                        dden = -(dY[t] @ y) / den
+                    else:
+                        dnum = dY[t]
+                        dden = 0.0
                     dfq[bb, hh, t] += A @ dnum + dden * a
                     dA = np.outer(Fq[t], dnum)
                     da = dden * Fq[t]

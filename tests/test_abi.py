@@ -171,6 +171,22 @@ def test_backward_validation(mhla_lib):
     assert "overlap" in mh.mhla_last_error()
 
 
+def test_option_entry_points_validate_options(mhla_lib):
+    # host-side rejections before any device work (null pointers are never touched)
+    b = mhla_lib.mhla_backward_ex
+    args = (FAKE, FAKE * 2, FAKE * 3, 0, FAKE * 4, FAKE * 5, FAKE * 6, FAKE * 7, FAKE * 8, FAKE * 9, 1, 1, 256, 16, 4)
+    assert b(*args, mh.MHLA_OPT_OUT_BF16, None) == mh.MHLA_ERR_UNSUPPORTED
+    assert b(*args, mh.MHLA_OPT_W_PER_HEAD, None) == mh.MHLA_ERR_UNSUPPORTED
+    assert b(*args, 64, None) == mh.MHLA_ERR_INVALID_ARG
+    assert "unknown option" in mh.mhla_last_error()
+    assert b(*args[:5], None, *args[6:], mh.MHLA_OPT_NO_NORMALIZER, None) == mh.MHLA_ERR_INVALID_ARG  # dy NULL
+    dstep = mhla_lib.mhla_decode_step_ex
+    dargs = (FAKE, FAKE * 2, FAKE * 3, 0, FAKE * 4, FAKE * 5, FAKE * 6, 1, 1, 16, 4, 8, 0)
+    assert dstep(*dargs, mh.MHLA_OPT_OUT_BF16, None) == mh.MHLA_ERR_UNSUPPORTED
+    assert dstep(*dargs, 64, None) == mh.MHLA_ERR_INVALID_ARG
+    assert dstep(*dargs[:-1], 32, mh.MHLA_OPT_NO_NORMALIZER, None) == mh.MHLA_ERR_INVALID_ARG  # t past M * C
+
+
 def test_forward_path_selection(mhla_lib):
     # non-causal bf16 with at most 256 tokens in at most 16 blocks: fused; otherwise staged
     assert mh.mhla_forward_path(64, 6, 256, 64, 16) == mh.MHLA_PATH_FUSED

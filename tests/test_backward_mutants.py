@@ -26,6 +26,11 @@ MUTANTS = [
     ("dW[i, i] += np.sum(dA * P) + da @ p", "dW[i, i] += np.sum(dA * P)"),
     ("dfk[bb, hh, j] += W[i, i] * (dA @ V[j] + da)", "dfk[bb, hh, j] += W[i, i] * dA @ V[j]"),
     ("dnum = dY[t] / den", "dnum = dY[t]"),
+    # the form without the normaliser
+    ("                        dnum = dY[t]\n                        dden = 0.0",
+     "                        dnum = dY[t]\n                        dden = -(dY[t] @ num)"),
+    ("                        dnum = dY[t]\n                        dden = 0.0",
+     "                        dnum = dY[t] / (Fq[t] @ a + EPS)\n                        dden = 0.0"),
 ]
 
 
@@ -41,3 +46,6 @@ def test_mutant_is_caught(mut, monkeypatch):
         for shape in pins.SHAPES:
             pins.test_backward_matches_finite_differences(shape)
         pins.test_backward_row_homogeneity()
+        for shape in pins.SHAPES[:5]:
+            pins.test_backward_without_normaliser_matches_finite_differences(shape)
+        pins.test_backward_without_normaliser_dv_is_a_transpose_product()

@@ -35,11 +35,11 @@ def _case(shape, seed):
     return q, k, v, W, dy
 
 
-def _loss(q, k, v, W, dy, causal):
-    return float(np.sum(dy * bruteforce.forward(q, k, v, W, causal=causal)))
+def _loss(q, k, v, W, dy, causal, normalize=True):
+    return float(np.sum(dy * bruteforce.forward(q, k, v, W, causal=causal, normalize=normalize)))
 
 
-def _fd(q, k, v, W, dy, causal, h=1e-5):
+def _fd(q, k, v, W, dy, causal, h=1e-5, normalize=True):
     args = [q, k, v, W]
     grads = []
     for a in range(4):
@@ -49,7 +49,7 @@ def _fd(q, k, v, W, dy, causal, h=1e-5):
             minus = [x.copy() for x in args]
             plus[a][idx] += h
             minus[a][idx] -= h
-            g[idx] = (_loss(*plus, dy, causal) - _loss(*minus, dy, causal)) / (2 * h)
+            g[idx] = (_loss(*plus, dy, causal, normalize) - _loss(*minus, dy, causal, normalize)) / (2 * h)
         grads.append(g)
     return grads
 
@@ -73,3 +73,26 @@ def test_backward_row_homogeneity():
     dW = backward(q, k, v, W, dy)[3]
     for i in range(W.shape[0]):
         assert abs(np.dot(W[i], dW[i])) < 1e-5 * np.max(np.abs(dW))
+
+
+@pytest.mark.parametrize("shape", SHAPES[:5], ids=lambda s: "B{}H{}N{}d{}M{}{}".format(*s[:5], "c" if s[5] else ""))
+def test_backward_without_normaliser_matches_finite_differences(shape):
+    # the form without the normaliser (MHLA §4.1, remark on the output): y = A V
+    q, k, v, W, dy = _case(shape, 7200 + SHAPES.index(shape))
+    causal = shape[5]
+    got = backward(q, k, v, W, dy, causal=causal, normalize=False)
+    ref = _fd(q, k, v, W, dy, causal, normalize=False)
+    for name, g, r in zip(("dq", "dk", "dv", "dW"), got, ref):
+        assert np.max(np.abs(g - r)) <= 1e-7 * np.max(np.abs(r)) + 1e-9, name
+
+
+def test_backward_without_normaliser_dv_is_a_transpose_product():
+    # y = A V is linear in V, so dv = A^T dy exactly, with A the explicit matrix of
+    # MHLA §4.2 Eq. 5 (brute force, independent of the backward code)
+    q, k, v, W, dy = _case((1, 2, 12, 4, 3, False), 7300)
+    dv = backward(q, k, v, W, dy, normalize=False)[2]
+    M, N = W.shape[0], q.shape[2]
+    blk = np.arange(N) * M // N
+    for h in range(q.shape[1]):
+        A = W[np.ix_(blk, blk)] * (bruteforce.phi(q[0, h]) @ bruteforce.phi(k[0, h]).T)
+        assert np.allclose(dv[0, h], A.T @ dy[0, h], rtol=1e-12, atol=1e-12)

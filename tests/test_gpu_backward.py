@@ -41,14 +41,17 @@ def say(msg):
     sys.stdout.flush()
 
 
-def gpu_backward(q, k, v, W, dy, causal, dtype):
+def gpu_backward(q, k, v, W, dy, causal, dtype, normalize=True):
     dt = torch.bfloat16 if dtype == "bf16" else torch.float32
     qd, kd, vd = (torch.from_numpy(np.ascontiguousarray(a)).to("cuda", dt) for a in (q, k, v))
     Wd = torch.from_numpy(W).cuda()
     dyd = torch.from_numpy(dy.astype(np.float32)).cuda()
     dq, dk, dv = (torch.full(q.shape, float("nan"), device="cuda") for _ in range(3))
     dW = torch.full(W.shape, float("nan"), device="cuda")
-    mh.mhla_backward(qd, kd, vd, Wd, dyd, dq, dk, dv, dW, causal=causal)
+    if normalize:
+        mh.mhla_backward(qd, kd, vd, Wd, dyd, dq, dk, dv, dW, causal=causal)
+    else:
+        mh.mhla_backward_ex(qd, kd, vd, Wd, dyd, dq, dk, dv, dW, causal=causal, normalize=False)
     torch.cuda.synchronize()
     return [t.cpu().numpy() for t in (dq, dk, dv, dW)]
 
@@ -87,3 +90,28 @@ def test_backward_is_deterministic():
     b = gpu_backward(q, k, v, W, dy, True, "bf16")
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+NO_NORMALISER = [BACKWARD[i] for i in (0, 1, 2, 3, 7, 9, 11)]
+
+
+@pytest.mark.parametrize("case", NO_NORMALISER,
+                         ids=lambda c: "B{}H{}N{}d{}M{}{}{}".format(*c[:5], "c" if c[5] else "", c[6]))
+def test_backward_without_normaliser_matches_oracle(case):
+    # the gradients of y = A V, the form without the normaliser ("MHLA" §4.1, remark on
+    # the output); the same 1e-4 bar
+    B, H, N, d, M, causal, dtype = case
+    w = WORKLOADS["lm_causal_8k"].shrink(B=B, H=H, N=N, d=d, M=M, causal=causal, dtype=dtype,
+                                         seed=6300 + NO_NORMALISER.index(case))
+    q, k, v, W = make_inputs(w)
+    dy = np.random.default_rng(6400 + NO_NORMALISER.index(case)).standard_normal(q.shape).astype(np.float32)
+    say(f"[backward, no normaliser] B={B} H={H} N={N} d={d} M={M} causal={causal} dtype={dtype}")
+    got = gpu_backward(q, k, v, W, dy, causal, dtype, normalize=False)
+    ref = oracle_backward(q, k, v, W, dy, causal=causal, normalize=False)
+    for name, g, r in zip(("dq", "dk", "dv", "dW"), got, ref):
+        assert np.all(np.isfinite(g)), name
+        e = float(np.max(np.abs(g.astype(np.float64) - r)) / np.max(np.abs(r)))
+        say(f"[backward, no normaliser]   {name}: max|d|/max|ref| = {e:.2e}")
+        assert e <= TOL, (name, e)
+    if causal:
+        assert np.all(np.triu(got[3], 1) == 0)

@@ -53,6 +53,10 @@ SIGNATURES = {
     "mhla_backward_workspace_bytes": (_I64, [_I64, _I64, _I64, _I64, _I64, _I]),
     "mhla_backward": (_I, [_P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _P]),
     "mhla_decode_step": (_I, [_P, _P, _P, _I, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _P]),
+    "mhla_backward_ex": (_I, [_P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, ctypes.c_uint,
+                              _P]),
+    "mhla_decode_step_ex": (_I, [_P, _P, _P, _I, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, ctypes.c_uint,
+                                 _P]),
     "mhla_release_workspace": (_I, [_P]),
     "mhla_debug_fail_workspace": (None, [_I]),
     "mhla_status_string": (ctypes.c_char_p, [_I]),
@@ -362,6 +366,12 @@ def mhla_backward_workspace_bytes(B, H, N, d, M, causal=False):
 def mhla_backward(q, k, v, W, dy, dq, dk, dv, dW, causal=False, stream=None):
     """Gradients of sum(dy * forward(q, k, v, W)): q, k, v [B, H, N, d] bf16 or float32,
     dy and the outputs dq, dk, dv float32 [B, H, N, d], dW float32 [M, M]."""
+    return mhla_backward_ex(q, k, v, W, dy, dq, dk, dv, dW, causal=causal, stream=stream)
+
+
+def mhla_backward_ex(q, k, v, W, dy, dq, dk, dv, dW, causal=False, normalize=True, stream=None):
+    """mhla_backward with options: normalize=False differentiates the form without the
+    normaliser."""
     _tokens(q)
     _same(q, "q", k=k, v=v)
     M = _mixing(W)
@@ -373,9 +383,9 @@ def mhla_backward(q, k, v, W, dy, dq, dk, dv, dW, causal=False, stream=None):
     ctx, s = _launch(_device_of(q=q, k=k, v=v, W=W, dy=dy, dq=dq, dk=dk, dv=dv, dW=dW), stream)
     B, H, N, d = q.shape
     with ctx:
-        _check(load_library().mhla_backward(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(W), _ptr(dy),
-                                            _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dW), B, H, N, d, M,
-                                            int(bool(causal)), s))
+        opts = (MHLA_OPT_CAUSAL if causal else 0) | (0 if normalize else MHLA_OPT_NO_NORMALIZER)
+        _check(load_library().mhla_backward_ex(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(W), _ptr(dy),
+                                               _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dW), B, H, N, d, M, opts, s))
     return dq, dk, dv, dW
 
 
@@ -386,9 +396,15 @@ def mhla_decode_state_bytes(B, H, d, M):
 def mhla_decode_step(q, k, v, W, state, out, C, t, stream=None):
     """One causal decoding step: q, k, v [B, H, d] (token t), out [B, H, d] float32,
     state a float32 device buffer of mhla_decode_state_bytes bytes; blocks of C tokens."""
+    return mhla_decode_step_ex(q, k, v, W, state, out, C, t, stream=stream)
+
+
+def mhla_decode_step_ex(q, k, v, W, state, out, C, t, normalize=True, stream=None):
+    """mhla_decode_step with options: normalize=False writes the numerator alone; W may be
+    [H, M, M] (one matrix per head)."""
     _tokens(q, dims=3)
     _same(q, "q", k=k, v=v)
-    M = _mixing(W)
+    M = _mixing(W, H=q.shape[1])
     B, H, d = q.shape
     _dtype(state, "state", torch.float32)
     _numel(state, "state", ((M + 1) * (d * d + d) + d) * B * H)
@@ -396,8 +412,10 @@ def mhla_decode_step(q, k, v, W, state, out, C, t, stream=None):
     _shape(out, "out", q.shape)
     ctx, s = _launch(_device_of(q=q, k=k, v=v, W=W, state=state, out=out), stream)
     with ctx:
-        _check(load_library().mhla_decode_step(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(W), _ptr(state),
-                                               _ptr(out), B, H, d, M, C, t, s))
+        opts = MHLA_OPT_CAUSAL | (0 if normalize else MHLA_OPT_NO_NORMALIZER)
+        opts |= MHLA_OPT_W_PER_HEAD if W.dim() == 3 else 0
+        _check(load_library().mhla_decode_step_ex(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(W), _ptr(state),
+                                                  _ptr(out), B, H, d, M, C, t, opts, s))
     return out
 
 

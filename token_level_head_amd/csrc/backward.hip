@@ -414,7 +414,8 @@ __global__ __launch_bounds__(256) void bwd_sum_kernel(const T* __restrict__ K, c
 template <int D, typename T>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void bwd_query_kernel(const T* __restrict__ Q, const float* __restrict__ dY,
                                                         const float* __restrict__ St, float* __restrict__ dQ,
-                                                        float* __restrict__ dSt, int64_t BH, int N, int M, int wpu) {
+                                                        float* __restrict__ dSt, int64_t BH, int N, int M, int wpu,
+                                                        int norm) {
     using Dm = Dim<D>;
     constexpr int P = Dm::P, FL = Dm::FL, KS = Dm::KS, L = Dm::L;
     extern __shared__ float red[];
@@ -470,8 +471,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
             }
             den = sum16(den) + kEps;
             dyn = sum16(dyn);
-            const float rden = fast_rcp(den);
-            dden[i] = -dyn * rden * rden;
+            // without the normaliser y = num: dnum = dy, no den terms
+            const float rden = norm ? fast_rcp(den) : 1.f;
+            dden[i] = norm ? -dyn * rden * rden : 0.f;
             float out[P];
 #pragma unroll
             for (int b = 0; b < P; ++b) {
@@ -595,7 +597,7 @@ __device__ __forceinline__ void query_causal_wave(const T* __restrict__ Q, const
                                                   const float* __restrict__ W, const float* __restrict__ St,
                                                   float* __restrict__ dQ, float* __restrict__ dSt,
                                                   float* __restrict__ G, float* __restrict__ dWdiag, int64_t BH,
-                                                  int N, int M, QcShared<D>& sh) {
+                                                  int N, int M, int norm, QcShared<D>& sh) {
     using Dm = Dim<D>;
     constexpr int P = Dm::P, FL = Dm::FL, KS = Dm::KS, L = Dm::L;
     constexpr int CP = QcShared<D>::CP, PH = QcShared<D>::PH;
@@ -780,9 +782,10 @@ __device__ __forceinline__ void query_causal_wave(const T* __restrict__ Q, const
         load_dl<float, D>(ry, g, n, yd);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float den = tot[0][i] + kEps;
-            const float rden = fast_rcp(den);
-            dden[i] = -tot[2][i] * rden * rden;
+            // without the normaliser: den = 1 (stored, so that the key kernel's dnum = dy), dden = 0
+            const float den = norm ? tot[0][i] + kEps : 1.f;
+            const float rden = norm ? fast_rcp(den) : 1.f;
+            dden[i] = norm ? -tot[2][i] * rden * rden : 0.f;
             float out[PH];
 #pragma unroll
             for (int j = 0; j < PH; ++j) {
@@ -856,12 +859,12 @@ template <int D, typename T>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void bwd_query_causal_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const float* __restrict__ dY,
     const float* __restrict__ W, const float* __restrict__ St, float* __restrict__ dQ, float* __restrict__ dSt,
-    float* __restrict__ G, float* __restrict__ dWdiag, int64_t BH, int N, int M) {
+    float* __restrict__ G, float* __restrict__ dWdiag, int64_t BH, int N, int M, int norm) {
     __shared__ QcShared<D> sh;
     if (threadIdx.x < 64)
-        query_causal_wave<D, T, 0>(Q, K, V, dY, W, St, dQ, dSt, G, dWdiag, BH, N, M, sh);
+        query_causal_wave<D, T, 0>(Q, K, V, dY, W, St, dQ, dSt, G, dWdiag, BH, N, M, norm, sh);
     else if constexpr (QcShared<D>::CP == 2)
-        query_causal_wave<D, T, 1>(Q, K, V, dY, W, St, dQ, dSt, G, dWdiag, BH, N, M, sh);
+        query_causal_wave<D, T, 1>(Q, K, V, dY, W, St, dQ, dSt, G, dWdiag, BH, N, M, norm, sh);
 }
 
 // Causal, two waves per (pair, key block b), tiles in reverse order.  The running
@@ -1244,7 +1247,7 @@ BwdLayout bwd_layout(int64_t BH, int64_t N, int D, int64_t M, bool causal) {
 
 template <int D, typename T>
 hipError_t run_backward(const T* q, const T* k, const T* v, const float* W, const float* dy, float* dq, float* dk,
-                        float* dv, float* dW, int64_t BH, int64_t N, int64_t M, bool causal, float* ws,
+                        float* dv, float* dW, int64_t BH, int64_t N, int64_t M, bool causal, bool normalize, float* ws,
                         void* frag_ws, hipStream_t stream) {
     constexpr int L = D * D + D;
     const BwdLayout o = bwd_layout(BH, N, D, M, causal);
@@ -1259,10 +1262,11 @@ hipError_t run_backward(const T* q, const T* k, const T* v, const float* W, cons
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = launch_mix(S, W, St, BH, D, M, causal, false, 0, frag_ws, stream)) != hipSuccess) return e;
     if (causal)
-        bwd_query_causal_kernel<D, T><<<grid, dim3(D >= 32 ? 128 : 64), 0, stream>>>(q, k, v, dy, W, St, dq, dSt, G,
-                                                                                     dWdiag, BH, (int)N, (int)M);
+        bwd_query_causal_kernel<D, T><<<grid, dim3(D >= 32 ? 128 : 64), 0, stream>>>(
+            q, k, v, dy, W, St, dq, dSt, G, dWdiag, BH, (int)N, (int)M, normalize ? 1 : 0);
     else
-        bwd_query_kernel<D, T><<<grid, block, red, stream>>>(q, dy, St, dq, dSt, BH, (int)N, (int)M, wpu);
+        bwd_query_kernel<D, T><<<grid, block, red, stream>>>(q, dy, St, dq, dSt, BH, (int)N, (int)M, wpu,
+                                                             normalize ? 1 : 0);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     bwd_wt_kernel<<<dim3((unsigned)((M * M + 255) / 256)), dim3(256), 0, stream>>>(W, Wt, (int)M, causal);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1300,18 +1304,18 @@ hipError_t run_backward(const T* q, const T* k, const T* v, const float* W, cons
 
 hipError_t launch_backward(int dtype, const void* q, const void* k, const void* v, const float* W, const float* dy,
                            float* dq, float* dk, float* dv, float* dW, int64_t BH, int64_t N, int D, int64_t M,
-                           bool causal, float* ws, void* frag_ws, hipStream_t stream) {
+                           bool causal, bool normalize, float* ws, void* frag_ws, hipStream_t stream) {
 #define MHLA_BWD(T)                                                                                             \
     switch (D) {                                                                                                \
         case 16:                                                                                                \
             return run_backward<16, T>((const T*)q, (const T*)k, (const T*)v, W, dy, dq, dk, dv, dW, BH, N, M,  \
-                                       causal, ws, frag_ws, stream);                                            \
+                                       causal, normalize, ws, frag_ws, stream);                                 \
         case 32:                                                                                                \
             return run_backward<32, T>((const T*)q, (const T*)k, (const T*)v, W, dy, dq, dk, dv, dW, BH, N, M,  \
-                                       causal, ws, frag_ws, stream);                                            \
+                                       causal, normalize, ws, frag_ws, stream);                                 \
         case 64:                                                                                                \
             return run_backward<64, T>((const T*)q, (const T*)k, (const T*)v, W, dy, dq, dk, dv, dW, BH, N, M,  \
-                                       causal, ws, frag_ws, stream);                                            \
+                                       causal, normalize, ws, frag_ws, stream);                                 \
         default:                                                                                                \
             return hipErrorInvalidValue;                                                                        \
     }

@@ -16,7 +16,8 @@
 // i - 1 (P goes to hist[i-1] and is reset) and forms St = sum_{b<i} W[i,b] hist[b];
 // then every token adds phi(k_t) v_t^T to P and writes
 //   y_t = phi(q_t)(St + W[i,i] P) / (phi(q_t)(z~ + W[i,i] p) + 1e-6),
-// which is row t of the causal forward pass.  All arithmetic is float32 (phi with
+// which is row t of the causal forward pass (without the normaliser, §4.1's remark
+// on the output: the numerator alone).  W may be one matrix per head.  All arithmetic is float32 (phi with
 // the full-precision exp), in a fixed order: results are bit-reproducible.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -40,7 +41,8 @@ __device__ __forceinline__ float load_in<float>(const float* p, int64_t i) {
 
 // Closing block i - 1 and mixing for block i: one thread per (pair, entry).
 __global__ __launch_bounds__(256) void decode_advance_kernel(const float* __restrict__ W, float* __restrict__ state,
-                                                             int64_t BH, int D, int M, int i, int first, int odd) {
+                                                             int64_t BH, int D, int M, int i, int first, int odd,
+                                                             int heads) {
     const int64_t L = (int64_t)D * D + D;
     const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // pair * L + entry
     if (e >= BH * L) return;
@@ -49,6 +51,7 @@ __global__ __launch_bounds__(256) void decode_advance_kernel(const float* __rest
     float* p2 = state + 2 * BH * L;
     float* hist = p2 + BH * D;
     const int64_t pair = e / L, ent = e % L;
+    if (heads > 0) W += (pair % heads) * M * M;  // one matrix per head
     // p of an odd token index lives in p2 (see the state description above)
     float* src = (odd && ent >= (int64_t)D * D) ? p2 + pair * D + (ent - (int64_t)D * D) : P + e;
     float x = 0.f;
@@ -73,7 +76,7 @@ template <int D, typename T>
 __global__ __launch_bounds__(256) void decode_token_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                            const T* __restrict__ v, const float* __restrict__ W,
                                                            float* __restrict__ state, float* __restrict__ out,
-                                                           int64_t BH, int M, int i, int odd) {
+                                                           int64_t BH, int M, int i, int odd, int norm, int heads) {
     constexpr int L = D * D + D;
     constexpr int CG = D / 16;  // column groups (workgroups) per pair
     constexpr int RPT = D / 16; // rows per thread: 16 row groups of 16 threads
@@ -88,6 +91,7 @@ __global__ __launch_bounds__(256) void decode_token_kernel(const T* __restrict__
     float* p2 = state + 2 * BH * L + pair * D;
     const float* pin = odd ? p2 : P + D * D;  // p after the previous token
     float* pout = odd ? P + D * D : p2;       // p after this one
+    if (heads > 0) W += (pair % heads) * M * M;  // one matrix per head
     const float wii = W[(int64_t)i * M + i];
 
     if (tid < D) {
@@ -120,25 +124,26 @@ __global__ __launch_bounds__(256) void decode_token_kernel(const T* __restrict__
         float n = 0.f, den = 0.f;
         for (int g = 0; g < 16; ++g) n += part[g][tid];
         for (int r = 0; r < D; ++r) den += dpart[r];
-        out[pair * D + 16 * cg + tid] = n / (den + kEps);
+        out[pair * D + 16 * cg + tid] = norm ? n / (den + kEps) : n;  // without the normaliser: the numerator
     }
 }
 
 hipError_t launch_decode_step(int dtype, const void* q, const void* k, const void* v, const float* W, float* state,
-                              float* out, int64_t BH, int D, int64_t M, int64_t C, int64_t t, hipStream_t stream) {
+                              float* out, int64_t BH, int D, int64_t M, int64_t C, int64_t t, bool normalize,
+                              int heads, hipStream_t stream) {
     const int64_t L = (int64_t)D * D + D;
     const int i = (int)(t / C);
     if (t % C == 0) {
         const int64_t total = BH * L;
         decode_advance_kernel<<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream>>>(
-            W, state, BH, D, (int)M, i, t == 0 ? 1 : 0, (int)(t & 1));
+            W, state, BH, D, (int)M, i, t == 0 ? 1 : 0, (int)(t & 1), heads);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     const dim3 grid((unsigned)(((BH + 7) / 8) * 8 * (D / 16))), block(256);
 #define MHLA_DECODE(DD, TT)                                                                                \
     decode_token_kernel<DD, TT><<<grid, block, 0, stream>>>((const TT*)q, (const TT*)k, (const TT*)v, W, state, \
-                                                            out, BH, (int)M, i, (int)(t & 1))
+                                                            out, BH, (int)M, i, (int)(t & 1), normalize ? 1 : 0, heads)
     if (dtype == kDtypeF32) {
         switch (D) {
             case 16: MHLA_DECODE(16, float); break;

@@ -77,14 +77,15 @@ hipError_t launch_causal_quad(const void* q, const void* k, const void* v, const
 
 // Streaming causal decoding of token t (state layout in decode.hip).
 hipError_t launch_decode_step(int dtype, const void* q, const void* k, const void* v, const float* W, float* state,
-                              float* out, int64_t BH, int D, int64_t M, int64_t C, int64_t t, hipStream_t stream);
+                              float* out, int64_t BH, int D, int64_t M, int64_t C, int64_t t, bool normalize,
+                              int heads, hipStream_t stream);
 
 // Backward pass (float32 arithmetic): dq, dk, dv [pair][N][d] and dW [M][M] from dy.
 // ws holds backward_workspace_floats() floats; frag_ws mix_fragment_bytes(M) bytes.
 size_t backward_workspace_floats(int64_t BH, int64_t N, int D, int64_t M, bool causal);
 hipError_t launch_backward(int dtype, const void* q, const void* k, const void* v, const float* W, const float* dy,
                            float* dq, float* dk, float* dv, float* dW, int64_t BH, int64_t N, int D, int64_t M,
-                           bool causal, float* ws, void* frag_ws, hipStream_t stream);
+                           bool causal, bool normalize, float* ws, void* frag_ws, hipStream_t stream);
 
 // Fused path (non-causal bf16, short blocks): the whole pass in one kernel with
 // the summaries in LDS; needs no workspace.

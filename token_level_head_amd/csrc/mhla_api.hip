@@ -529,7 +529,19 @@ int64_t mhla_backward_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d
 
 int mhla_backward(const void* q, const void* k, const void* v, int dtype, const float* W, const float* dy,
                   float* dq, float* dk, float* dv, float* dW, int64_t B, int64_t H, int64_t N, int64_t d,
-                  int64_t M, int causal, mhla_stream_t stream_) {
+                  int64_t M, int causal, mhla_stream_t stream) {
+    return mhla_backward_ex(q, k, v, dtype, W, dy, dq, dk, dv, dW, B, H, N, d, M, causal ? MHLA_OPT_CAUSAL : 0,
+                            stream);
+}
+
+int mhla_backward_ex(const void* q, const void* k, const void* v, int dtype, const float* W, const float* dy,
+                     float* dq, float* dk, float* dv, float* dW, int64_t B, int64_t H, int64_t N, int64_t d,
+                     int64_t M, unsigned options, mhla_stream_t stream_) {
+    if (options & ~kKnownOptions) return fail(MHLA_ERR_INVALID_ARG, "unknown option bits 0x%x", options & ~kKnownOptions);
+    if (options & (MHLA_OPT_OUT_BF16 | MHLA_OPT_W_PER_HEAD))
+        return fail(MHLA_ERR_UNSUPPORTED, "the backward pass takes MHLA_OPT_CAUSAL and MHLA_OPT_NO_NORMALIZER only");
+    const int causal = (options & MHLA_OPT_CAUSAL) != 0;
+    const bool normalize = (options & MHLA_OPT_NO_NORMALIZER) == 0;
     int st = check_sizes(B, H, N, d, M);
     if (st) return st;
     if (dtype != MHLA_DTYPE_BF16 && dtype != MHLA_DTYPE_F32) return fail(MHLA_ERR_INVALID_ARG, "bad dtype %d", dtype);
@@ -560,7 +572,7 @@ int mhla_backward(const void* q, const void* k, const void* v, int dtype, const 
     void* ws = nullptr;
     bool owned = false;
     if ((st = stream_workspace(total, stream, &ws, &owned))) return st;
-    hipError_t e = mhla::launch_backward(dtype, q, k, v, W, dy, dq, dk, dv, dW, B * H, N, (int)d, M, causal != 0,
+    hipError_t e = mhla::launch_backward(dtype, q, k, v, W, dy, dq, dk, dv, dW, B * H, N, (int)d, M, causal != 0, normalize,
                                          static_cast<float*>(ws), static_cast<char*>(ws) + fbytes, stream);
     const hipError_t fe = release_workspace(ws, owned, stream);
     if (e != hipSuccess) return hip_fail(e, "backward kernels");
@@ -576,6 +588,16 @@ int64_t mhla_decode_state_bytes(int64_t B, int64_t H, int64_t d, int64_t M) {
 int mhla_decode_step(const void* q, const void* k, const void* v, int dtype, const float* W, float* state,
                      float* out, int64_t B, int64_t H, int64_t d, int64_t M, int64_t C, int64_t t,
                      mhla_stream_t stream) {
+    return mhla_decode_step_ex(q, k, v, dtype, W, state, out, B, H, d, M, C, t, MHLA_OPT_CAUSAL, stream);
+}
+
+int mhla_decode_step_ex(const void* q, const void* k, const void* v, int dtype, const float* W, float* state,
+                        float* out, int64_t B, int64_t H, int64_t d, int64_t M, int64_t C, int64_t t,
+                        unsigned options, mhla_stream_t stream) {
+    if (options & ~kKnownOptions) return fail(MHLA_ERR_INVALID_ARG, "unknown option bits 0x%x", options & ~kKnownOptions);
+    if (options & MHLA_OPT_OUT_BF16) return fail(MHLA_ERR_UNSUPPORTED, "decoding writes float32 only");
+    const bool normalize = (options & MHLA_OPT_NO_NORMALIZER) == 0;
+    const int heads = (options & MHLA_OPT_W_PER_HEAD) ? (int)H : 0;
     if (C < 1) return fail(MHLA_ERR_INVALID_ARG, "C=%lld must be >= 1", (long long)C);
     if (M > (((int64_t)1 << 30) / C)) return fail(MHLA_ERR_UNSUPPORTED, "M*C too large");
     int st = check_sizes(B, H, M * C, d, M);
@@ -591,7 +613,7 @@ int mhla_decode_step(const void* q, const void* k, const void* v, int dtype, con
     const size_t in_bytes = (size_t)(B * H * d) * esz;
     const size_t out_bytes = (size_t)(B * H * d) * 4;
     const size_t st_bytes = (size_t)mhla_decode_state_bytes(B, H, d, M);
-    const size_t w_bytes = (size_t)(M * M) * 4;
+    const size_t w_bytes = (size_t)(M * M) * 4 * (heads > 0 ? (size_t)H : 1);
     if (overlaps(out, out_bytes, q, in_bytes) || overlaps(out, out_bytes, k, in_bytes) ||
         overlaps(out, out_bytes, v, in_bytes) || overlaps(out, out_bytes, W, w_bytes) ||
         overlaps(out, out_bytes, state, st_bytes))
@@ -599,7 +621,7 @@ int mhla_decode_step(const void* q, const void* k, const void* v, int dtype, con
     if (overlaps(state, st_bytes, q, in_bytes) || overlaps(state, st_bytes, k, in_bytes) ||
         overlaps(state, st_bytes, v, in_bytes) || overlaps(state, st_bytes, W, w_bytes))
         return fail(MHLA_ERR_INVALID_ARG, "state overlaps an input");
-    hipError_t e = mhla::launch_decode_step(dtype, q, k, v, W, state, out, B * H, (int)d, M, C, t,
+    hipError_t e = mhla::launch_decode_step(dtype, q, k, v, W, state, out, B * H, (int)d, M, C, t, normalize, heads,
                                             reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "decode kernels");
     return ok();
