@@ -30,6 +30,7 @@ import token_level_head_amd as mh
 from token_level_head_amd.workloads import WORKLOADS, make_inputs
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+PATH_NAMES = {0: "staged", 1: "fused", 2: "pair"}  # mhla_forward_path() values
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 METRIC = "MHLA fwd tokens/s and TFLOP/s at 1 MI355X; % of HBM/MFMA roofline"
 
@@ -67,6 +68,7 @@ def kernel_bytes(w):
         "output": BH * N * d * e + summ + BH * N * d * 4 + (2 * BH * N * d * e + M * 4 if w.causal else 0),
         # one kernel, summaries on chip: q, k, v read once, y written once
         "fused": 3 * BH * N * d * e + BH * N * d * 4 + M * M * 4,
+        "pair": 3 * BH * N * d * e + BH * N * d * 4 + M * M * 4,
     }
 
 
@@ -80,7 +82,7 @@ def measured_traffic(workload, stage):
         return None
     with open(path) as f:
         prof = json.load(f)
-    prefix = {"fused": "fused_", "summaries": "summaries_", "mix": "mix_", "output": "output_"}[stage]
+    prefix = {"fused": "fused_", "pair": "pair_", "summaries": "summaries_", "mix": "mix_", "output": "output_"}[stage]
     for name, k in prof["kernels"].items():
         if name.startswith(prefix):
             if k.get("source_digest") != kernel_source_digest(name):
@@ -313,7 +315,7 @@ def sweep_bench(args):
             path = mh.mhla_forward_path(B, H, N, d, M, False, mh.MHLA_DTYPE_BF16)
             points.append({"N": N, "M": M, "B": B, "M2_lt_N": M * M < N, "ms": round(ms, 5),
                            "tokens_per_s": round(tok_s, 1), "rel_to_M1": round(tok_s / base, 4),
-                           "path": "fused" if path == mh.MHLA_PATH_FUSED else "staged"})
+                           "path": PATH_NAMES[path]})
             print(f"N={N} M={M} B={B}: {ms * 1e3:.1f} us, {tok_s:.3e} tokens/s, x{tok_s / base:.3f} of M=1",
                   file=sys.stderr, flush=True)
             del graph
@@ -503,11 +505,12 @@ def main():
     if w.dtype == "bf16":
         staged["mix"]["mfma_TFLOPs"] = round(mf_exec / t_mix / 1e12, 2)
         staged["mix"]["mfma_frac"] = round(mf_exec / t_mix / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
-    if path == mh.MHLA_PATH_FUSED:
-        # the step is the fused kernel alone: its duration is the step's
-        kms["fused"] = ms
-        kernels = {"fused": entry("fused", ms)}
-        dom = "fused"
+    if path in (mh.MHLA_PATH_FUSED, mh.MHLA_PATH_PAIR):
+        # the step is one kernel: its duration is the step's
+        one = PATH_NAMES[path]
+        kms[one] = ms
+        kernels = {one: entry(one, ms)}
+        dom = one
     else:
         kernels = staged
         dom = max(names, key=lambda n: kms[n])
@@ -561,7 +564,7 @@ def main():
         "config": {"workload": w.key, "description": w.description, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "M": w.M, "causal": w.causal, "global_batch": w.B, "seq_len": w.N, "parallelism": "none (1 GPU)"},
         "tflops": round(tflops, 3),
-        "path": "fused" if path == mh.MHLA_PATH_FUSED else "staged",
+        "path": PATH_NAMES[path],
         "kernels": kernels,
         "staged_kernels": staged,
         "stage_timing": "K chains over the rotating buffer sets; "

@@ -68,7 +68,7 @@ enum {
 enum { MHLA_DTYPE_BF16 = 0, MHLA_DTYPE_F32 = 1 };
 
 /* The kernels mhla_forward runs (see mhla_forward_path). */
-enum { MHLA_PATH_STAGED = 0, MHLA_PATH_FUSED = 1 };
+enum { MHLA_PATH_STAGED = 0, MHLA_PATH_FUSED = 1, MHLA_PATH_PAIR = 2 };
 
 /*
  * Full forward pass, bfloat16 q/k/v (float32 accumulation, float32 W and out).
@@ -85,9 +85,12 @@ enum { MHLA_PATH_STAGED = 0, MHLA_PATH_FUSED = 1 };
  *     the graph owns that memory and never shares the stream's workspace.  Host
  *     threads that issue calls on one stream must serialise those calls (the
  *     workspace relies on their order on the stream);
- *   - fused (non-causal; M <= 16 blocks of at most 16 tokens, or N <= 256 in
- *     blocks of 32, 48 or 64 tokens): one workgroup per (batch, head) pair that
- *     keeps the block summaries and their mix in LDS; no workspace.
+ *   - fused (non-causal, bf16; N <= 256 tokens in M <= 16 blocks): one kernel in
+ *     the token-level form of §4.2 Eq. 5, keys streamed through LDS; no workspace;
+ *   - pair (non-causal, bf16; 256 < N <= 8192 tokens in M <= 16 blocks of a
+ *     multiple of 32 tokens, d in {32, 64}, B*H >= 256): one workgroup per (batch,
+ *     head) pair that keeps every block summary and its mix in registers (§4.1's
+ *     four steps without a workspace round trip); no workspace.
  * mhla_forward_path() reports which one a call with given sizes uses.
  */
 int mhla_forward(const void* q, const void* k, const void* v, const float* W, float* out,
@@ -179,8 +182,8 @@ int mhla_forward_blocks(const void* q, const void* k, const void* v, int dtype, 
                         const int32_t* offsets, int64_t max_block, unsigned options, mhla_stream_t stream);
 
 /* Which path mhla_forward (dtype MHLA_DTYPE_BF16) or mhla_forward_f32
- * (MHLA_DTYPE_F32; always staged) takes for these sizes: MHLA_PATH_STAGED or
- * MHLA_PATH_FUSED; -1 for invalid sizes or dtype. */
+ * (MHLA_DTYPE_F32; always staged) takes for these sizes: MHLA_PATH_STAGED,
+ * MHLA_PATH_FUSED or MHLA_PATH_PAIR; -1 for invalid sizes or dtype. */
 int mhla_forward_path(int64_t B, int64_t H, int64_t N, int64_t d, int64_t M, int causal, int dtype);
 
 /* Bytes of device workspace one staged bf16 forward call uses (the fused path uses none): the S and

@@ -18,7 +18,7 @@ _BINDING_NAMES = {
     "mhla_backward_workspace_bytes", "mhla_backward", "mhla_forward_ex", "MHLA_OPT_CAUSAL",
     "MHLA_OPT_NO_NORMALIZER", "MHLA_OPT_OUT_BF16", "MHLA_OPT_W_PER_HEAD", "mhla_forward_blocks",
     "mhla_release_workspace", "mhla_debug_fail_workspace", "mhla_forward_noalloc", "MHLA_NOALLOC_SCRATCH_BYTES",
-    "mhla_backward_ex", "mhla_decode_step_ex",
+    "mhla_backward_ex", "mhla_decode_step_ex", "MHLA_PATH_PAIR",
 }
 
 

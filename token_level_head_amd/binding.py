@@ -25,6 +25,7 @@ MHLA_DTYPE_BF16 = 0
 MHLA_DTYPE_F32 = 1
 MHLA_PATH_STAGED = 0
 MHLA_PATH_FUSED = 1
+MHLA_PATH_PAIR = 2
 MHLA_OPT_CAUSAL = 1
 MHLA_OPT_NO_NORMALIZER = 2
 MHLA_OPT_OUT_BF16 = 4
@@ -289,7 +290,7 @@ def mhla_workspace_bytes(B, H, N, d, M, causal=False):
 
 
 def mhla_forward_path(B, H, N, d, M, causal=False, dtype=MHLA_DTYPE_BF16):
-    """MHLA_PATH_STAGED or MHLA_PATH_FUSED: the kernels mhla_forward runs for these sizes."""
+    """MHLA_PATH_STAGED, MHLA_PATH_FUSED or MHLA_PATH_PAIR: the kernels mhla_forward runs for these sizes."""
     return int(load_library().mhla_forward_path(B, H, N, d, M, int(bool(causal)), dtype))
 
 

@@ -12,7 +12,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmhla.so")
-SOURCES = ["summary.hip", "mix.hip", "output.hip", "causal.hip", "decode.hip", "backward.hip", "fused.hip", "mhla_api.hip"]
+SOURCES = ["summary.hip", "mix.hip", "output.hip", "causal.hip", "decode.hip", "backward.hip", "fused.hip", "pair.hip",
+           "mhla_api.hip"]
 OBJDIR = os.path.join(ROOT, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -27,6 +28,7 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, 
 # kernel's measurements stay valid while this file and the shared headers do.
 KERNEL_SOURCES = [
     ("fused_", "fused.hip"),
+    ("pair_", "pair.hip"),
     ("summaries_", "summary.hip"),
     ("mix_", "mix.hip"),
     ("wsplit_", "mix.hip"),
@@ -35,7 +37,7 @@ KERNEL_SOURCES = [
     ("decode_", "decode.hip"),
     ("bwd_", "backward.hip"),
 ]
-SHARED_SOURCES = ["common.hpp", "kernels.hpp", "mhla_api.hip", "../../include/mhla.h"]
+SHARED_SOURCES = ["common.hpp", "kernels.hpp", "lds_tiles.hpp", "mhla_api.hip", "../../include/mhla.h"]
 
 
 def source_digest(files=None):

@@ -53,6 +53,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "lds_tiles.hpp"
 
 namespace mhla {
 
@@ -87,42 +88,12 @@ struct FusedLds {
     static constexpr int kBytes = kQBase + kJobTiles * kTileQ;
 };
 
-// Physical 16-byte unit of chunk `chunk` of row `row` in an LDS array of `cpr` 16-byte
-// chunks per row, XOR-swizzled so that eight consecutive rows read at one chunk fall
-// on eight different groups of four banks: inside the row when rows are whole 128-byte
-// lines (cpr a multiple of 8), else inside each aligned 128-byte line of the array.
-__device__ __forceinline__ int swz(int row, int chunk, int cpr) {
-    if ((cpr & 7) == 0) return row * cpr + (chunk ^ (row & 7));
-    const int u = row * cpr + chunk, line = u >> 3;
-    return (line << 3) | ((u & 7) ^ (line & 7));
-}
-
-// The (row, chunk) that swz maps to 16-byte unit L: its inverse.
-__device__ __forceinline__ void unswz(int L, int cpr, int& row, int& chunk) {
-    if ((cpr & 7) == 0) {
-        row = L / cpr;
-        chunk = (L % cpr) ^ (row & 7);
-    } else {
-        const int line = L >> 3, u = (line << 3) | ((L & 7) ^ (line & 7));
-        row = u / cpr;
-        chunk = u % cpr;
-    }
-}
-
 // Global -> LDS copy of 16 bytes per lane (no registers): lane i writes LDS bytes
 // dst + 16 i .. +15 (dst wave-uniform) with 16 bytes of buffer r at byte offset off
 // (zeros at or past the end of the buffer).  Counted by vmcnt; the data is read only
 // after a barrier whose release fence waits for it.
 __device__ __forceinline__ void buf_to_lds16(rsrc_t r, unsigned char* dst, uint32_t off) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
-}
-
-__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-// phi of the two bf16 values of a word, packed back to bf16.
-__device__ __forceinline__ uint32_t phi_pair(uint32_t w) {
-    return pack_bf16(phi_fast(lo_bf16(w)), phi_fast(hi_bf16(w)));
 }
 
 // Score operand types: 16x16x32 (8 bf16 per lane) for d >= 32, 16x16x16 (4) for d = 16.
@@ -461,16 +432,6 @@ __device__ __forceinline__ void load_bq(const unsigned char* qarea, int wave, in
     }
 }
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-// 8 bytes at LDS byte address `a`, transposed across each 16-lane group: lane i gets,
-// as element e, element i % 4 of what lane 4e + i / 4 of its group addressed (gfx950
-// ds_read_b64_tr_b16).
-__device__ __forceinline__ s16x4 lds_read_tr16(const unsigned char* a) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4*)(const_cast<unsigned char*>(a)));
-}
-
 // Operands of one 32-key step read from LDS: phi(K) of key tiles 2S, 2S + 1 as the
 // score MFMA's A operand (key n, features 32 f + 8 g .. +7; d = 16: 4 g .. 4 g + 3), and
 // V as the output MFMA's A operand, read transposed: lane (g, n) of value tile c gets
@@ -503,18 +464,8 @@ __device__ __forceinline__ void step_ak(const unsigned char* buf, int S, int g, 
 
 template <int D>
 __device__ __forceinline__ void step_av(const unsigned char* vbuf, int S, int g, int n, StepOps<D>& o) {
-    constexpr int VT = StepOps<D>::VT, CPR = D / 8;
-    const unsigned char* const fv = vbuf;
 #pragma unroll
-    for (int c = 0; c < VT; ++c) {
-        s16x4 half[2];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            const int key = 32 * S + 16 * hh + 4 * g + (n >> 2), col = 16 * c + 4 * (n & 3);
-            half[hh] = lds_read_tr16(fv + 16 * swz(key, col >> 3, CPR) + 2 * (col & 7));
-        }
-        o.av[c] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
-    }
+    for (int c = 0; c < StepOps<D>::VT; ++c) o.av[c] = lds_operand_t(vbuf, 32 * S, 16 * c, D / 8, g, n);
 }
 
 template <int D>

@@ -87,6 +87,13 @@ hipError_t launch_backward(int dtype, const void* q, const void* k, const void* 
                            float* dq, float* dk, float* dv, float* dW, int64_t BH, int64_t N, int D, int64_t M,
                            bool causal, bool normalize, float* ws, void* frag_ws, hipStream_t stream);
 
+// Pair path (non-causal bf16, 256 < N <= 8192, at most 16 blocks of a multiple of 32
+// tokens, at least 256 pairs): the whole pass in one kernel per (batch, head) pair,
+// every block summary on chip; needs no workspace.
+bool pair_applicable(int D, int64_t BH, int64_t N, int64_t M);
+hipError_t launch_pair(const void* q, const void* k, const void* v, const float* W, const OutSpec& out, int64_t BH,
+                       int64_t N, int D, int64_t M, int heads, hipStream_t stream);
+
 // Fused path (non-causal bf16, short blocks): the whole pass in one kernel with
 // the summaries in LDS; needs no workspace.
 bool fused_applicable(int D, int64_t BH, int64_t N, int64_t M);

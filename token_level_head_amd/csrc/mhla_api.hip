@@ -313,8 +313,10 @@ int drop_stream_workspace(hipStream_t stream) {
 }
 
 int forward_path(int64_t B, int64_t H, int64_t N, int64_t d, int64_t M, int causal, int dtype) {
-    return dtype == mhla::kDtypeBF16 && !causal && mhla::fused_applicable((int)d, B * H, N, M) ? MHLA_PATH_FUSED
-                                                                                             : MHLA_PATH_STAGED;
+    if (dtype != mhla::kDtypeBF16 || causal) return MHLA_PATH_STAGED;
+    if (mhla::fused_applicable((int)d, B * H, N, M)) return MHLA_PATH_FUSED;
+    if (mhla::pair_applicable((int)d, B * H, N, M)) return MHLA_PATH_PAIR;
+    return MHLA_PATH_STAGED;
 }
 
 constexpr unsigned kKnownOptions = MHLA_OPT_CAUSAL | MHLA_OPT_NO_NORMALIZER | MHLA_OPT_OUT_BF16 | MHLA_OPT_W_PER_HEAD;
@@ -361,9 +363,15 @@ int forward_impl(int dtype, const void* q, const void* k, const void* v, const f
 
     hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
     const int64_t BH = B * H;
-    if (!listed && forward_path(B, H, N, d, M, causal, dtype) == MHLA_PATH_FUSED) {
+    const int path = listed ? MHLA_PATH_STAGED : forward_path(B, H, N, d, M, causal, dtype);
+    if (path == MHLA_PATH_FUSED) {
         hipError_t e = mhla::launch_fused(q, k, v, W, os, BH, N, (int)d, M, heads, stream);
         if (e != hipSuccess) return hip_fail(e, "fused kernel");
+        return ok();
+    }
+    if (path == MHLA_PATH_PAIR) {
+        hipError_t e = mhla::launch_pair(q, k, v, W, os, BH, N, (int)d, M, heads, stream);
+        if (e != hipSuccess) return hip_fail(e, "pair kernel");
         return ok();
     }
     const size_t arr = (size_t)(M * BH * summary_floats(d)) * sizeof(float);
