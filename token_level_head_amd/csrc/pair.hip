@@ -70,6 +70,15 @@ struct PairShape {
     int N, M, C, nchunks, heads;
 };
 
+// The wave's tiles of S~_i for every block i: element e of tile j of block i is lane
+// element (j * 16 + i) of vector e, so that a block picked at run time is read with
+// one indexed register move per element.
+template <int D>
+struct Mixed {
+    typedef float vec __attribute__((ext_vector_type(16 * PairCfg<D>::TW)));
+    vec v[4];
+};
+
 // The row pieces one wave loads for a chunk of one [N][D] matrix: rows kPRowsW * wave
 // .. + kPRowsW - 1 of the chunk, 16 bytes per lane and piece; rows past N (and chunks
 // past the end) read zero.
@@ -130,7 +139,7 @@ __device__ __forceinline__ void pair_stage(const PairLoads<D>& L, unsigned char*
 // that are never read), so the column of W comes in four reads and no branch.
 template <int D>
 __device__ __forceinline__ void pair_flush(const float* wt, int b, f32x4 (&cur)[PairCfg<D>::TW],
-                                           f32x4 (&mix)[kPMaxB][PairCfg<D>::TW]) {
+                                           Mixed<D>& mix) {
     f32x4 wc[kPMaxB / 4];
 #pragma unroll
     for (int r = 0; r < kPMaxB / 4; ++r) wc[r] = reinterpret_cast<const f32x4*>(wt + kPMaxB * b)[r];
@@ -140,7 +149,7 @@ __device__ __forceinline__ void pair_flush(const float* wt, int b, f32x4 (&cur)[
 #pragma unroll
         for (int j = 0; j < PairCfg<D>::TW; ++j)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) mix[i][j][e] = fmaf(w, cur[j][e], mix[i][j][e]);
+            for (int e = 0; e < 4; ++e) mix.v[e][16 * j + i] = fmaf(w, cur[j][e], mix.v[e][16 * j + i]);
     }
 #pragma unroll
     for (int j = 0; j < PairCfg<D>::TW; ++j) cur[j] = zero4();
@@ -152,7 +161,7 @@ __device__ __forceinline__ void pair_flush(const float* wt, int b, f32x4 (&cur)[
 template <int D>
 __device__ __forceinline__ void pair_accumulate(const unsigned char* slot, int chunk, const PairShape& sh,
                                                 const float* wt, int wave, int g, int n, int& curblk,
-                                                f32x4 (&cur)[PairCfg<D>::TW], f32x4 (&mix)[kPMaxB][PairCfg<D>::TW],
+                                                f32x4 (&cur)[PairCfg<D>::TW], Mixed<D>& mix,
                                                 f32x4& zacc) {
     constexpr int P = PairCfg<D>::P, T = PairCfg<D>::T, TW = PairCfg<D>::TW, CPR = PairCfg<D>::CPR;
     const unsigned char* const fk = slot;
@@ -205,20 +214,17 @@ __device__ __forceinline__ void pair_stage_block(unsigned char* st, const f32x4 
     }
 }
 
-// S~_i of blocks first .. last to the ring (buffer i % 4).  mix[i] is picked by a chain
-// of selects over the 16 blocks, which keeps the register indices static.
+// S~_i of blocks first .. last to the ring (buffer i % 4); block i's tiles are read
+// with indexed register moves.
 template <int D>
-__device__ __forceinline__ void pair_stage_mixed(unsigned char* ring, const f32x4 (&mix)[kPMaxB][PairCfg<D>::TW],
+__device__ __forceinline__ void pair_stage_mixed(unsigned char* ring, const Mixed<D>& mix,
                                                  int first, int last, int wave, int g, int n) {
     constexpr int TW = PairCfg<D>::TW;
     for (int i = first; i <= last; ++i) {
         f32x4 tiles[TW];
 #pragma unroll
-        for (int j = 0; j < TW; ++j) {
-            tiles[j] = zero4();
-#pragma unroll
-            for (int ii = 0; ii < kPMaxB; ++ii) tiles[j] = ii == i ? mix[ii][j] : tiles[j];
-        }
+        for (int j = 0; j < TW; ++j)
+            tiles[j] = f32x4{mix.v[0][16 * j + i], mix.v[1][16 * j + i], mix.v[2][16 * j + i], mix.v[3][16 * j + i]};
         pair_stage_block<D>(ring + (i & 3) * PairCfg<D>::kStBuf, tiles, wave, g, n);
     }
 }
@@ -280,7 +286,7 @@ __device__ __forceinline__ void pair_outputs(const unsigned char* lds, const rsr
 // chunk's Q area and ring buffers at the leading barrier.  A chunk meets at most four
 // blocks (blocks hold at least 32 tokens), so the ring holds every block it reads.
 template <int D, bool OUT16>
-__device__ __forceinline__ void pair_q_chunk(unsigned char* lds, const f32x4 (&mix)[kPMaxB][PairCfg<D>::TW],
+__device__ __forceinline__ void pair_q_chunk(unsigned char* lds, const Mixed<D>& mix,
                                              PairRows<D>& R, const rsrc_t& rQ, const rsrc_t& rY, const OutSpec& o,
                                              const PairShape& sh, int c, int& staged, int wave, int lane) {
     const int g = lane >> 4, n = lane & 15;
@@ -320,11 +326,10 @@ __global__ __launch_bounds__(64 * kPW) void pair_kernel(const uint16_t* __restri
     }
 
     // ---- phase 1: summaries, mixed into S~ as each block completes ----
-    f32x4 mix[kPMaxB][TW], cur[TW];  // the wave's tiles of S~_i for every i; of S_b for the current block
+    Mixed<D> mix;  // the wave's tiles of S~_i for every i
+    f32x4 cur[TW];  // of S_b for the current block
 #pragma unroll
-    for (int i = 0; i < kPMaxB; ++i)
-#pragma unroll
-        for (int j = 0; j < TW; ++j) mix[i][j] = zero4();
+    for (int e = 0; e < 4; ++e) mix.v[e] = 0.f;
 #pragma unroll
     for (int j = 0; j < TW; ++j) cur[j] = zero4();
     f32x4 zacc = zero4();
