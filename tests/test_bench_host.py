@@ -69,3 +69,12 @@ def test_cpu_baseline_reports_host_and_both_samples():
     assert cb["kind"] == "oracle" and cb["unit"] == "tokens/s" and cb["value"] > 0
     assert 1 <= cb["cores"] <= 16 and cb["single_thread"]["cores"] == 1 and cb["single_thread"]["value"] > 0
     assert cb["host"]["nproc"] >= 1 and cb["host"]["cpu_model"]
+
+
+def test_pair_bytes_of_the_dit_512_workload():
+    # 64 images x 6 heads x 1024 tokens x 64 features, 16 blocks of 64 tokens: the
+    # per-pair kernel reads Q, K, V once and writes the float32 Y once.
+    tok = 64 * 6 * 1024 * 64 * 2       # one bf16 token tensor: 50,331,648 bytes
+    assert tok == 50331648
+    b = bench.kernel_bytes(WORKLOADS["dit_s2_512"])
+    assert b["pair"] == 3 * tok + 2 * tok + 16 * 16 * 4

@@ -30,7 +30,7 @@ COPY_BYTES = 1 << 30  # bench.py --copy-calibration copies 2^28 float32 values
 
 
 def short_name(name):
-    base = name.split("(")[0].replace("void ", "")
+    base = name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
     return base.replace("mhla::", "")
 
 

@@ -5,7 +5,7 @@ GPU library's tests and the CPU oracle can both take their inputs from it.
 
 Each workload mirrors a shape the MHLA paper's experiments use ("MHLA: Restoring
 Expressivity of Linear Attention via Token-Level Multi-Head", §5.2 image
-generation with DiT-S/2 at 256 and 4096 resolution, SANA-style text-to-image,
+generation with DiT-S/2 at 256, 512 and 4096 resolution, SANA-style text-to-image,
 §5.4 causal language modelling), with random data in place of trained
 projections: Q, K, V ~ N(0, 1) * scale and each row of W a softmax of N(0, 1) *
 wscale logits (nonnegative rows summing to one, as §4.2 asks of M_c).  For the
@@ -61,6 +61,8 @@ WORKLOADS = {
                  B=1, H=1, N=256, d=16, M=4, causal=False, dtype="f32", scale=1.0, wscale=1.0, seed=1001),
         Workload("dit_s2_256", "DiT-S/2 at 256x256: 16x16 latent grid, 16 blocks of 4x4 tokens",
                  B=64, H=6, N=256, d=64, M=16, causal=False, dtype="bf16", scale=1.0, wscale=1.0, seed=1002),
+        Workload("dit_s2_512", "DiT-S/2 at 512x512: 32x32 latent grid, 16 blocks of 8x8 tokens",
+                 B=64, H=6, N=1024, d=64, M=16, causal=False, dtype="bf16", scale=1.0, wscale=1.0, seed=1006),
         Workload("dit_s2_4096", "DiT-S/2 at 4096x4096: 256x256 latent grid, 256 blocks of 16x16 tokens",
                  B=1, H=6, N=65536, d=64, M=256, causal=False, dtype="bf16", scale=1.0, wscale=1.0, seed=1003),
         Workload("sana_128", "SANA-like 128x128 grid, 70 heads of 32, 64 blocks of 16x16 tokens",
