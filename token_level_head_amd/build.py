@@ -1,6 +1,7 @@
 """Build libmhla.so (the HIP library for gfx950) in-tree with hipcc.
 
     python -m token_level_head_amd.build
+    python -m token_level_head_amd.build --resources   # per-kernel registers, scratch, LDS (markdown)
 """
 import os
 import subprocess
@@ -93,5 +94,52 @@ def build(verbose=False, out=LIB):
     return out
 
 
+def resources():
+    """Markdown table of every kernel's resource usage, from the compiler's
+    kernel-resource-usage remarks (device code only, the library's own flags)."""
+    import re
+
+    rows = []
+    for src in SOURCES:
+        r = subprocess.run([HIPCC, *FLAGS, "--cuda-device-only", "-Rpass-analysis=kernel-resource-usage", "-c",
+                            os.path.join(CSRC, src), "-o", os.devnull], capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(r.stderr[-2000:])
+        cur = None
+        for line in r.stderr.splitlines():
+            m = re.search(r"remark:\s+(Function Name|VGPRs|AGPRs|ScratchSize \[bytes/lane\]|Occupancy \[waves/SIMD\]|"
+                          r"VGPRs Spill|LDS Size \[bytes/block\]): (\S+)", line)
+            if not m:
+                continue
+            key, val = m.groups()
+            if key == "Function Name":
+                cur = {"kernel": _demangle(val), "source": src}
+                rows.append(cur)
+            elif cur is not None:
+                cur[key] = val
+    out = ["| kernel | source | VGPRs | AGPRs | VGPR spills | scratch B/lane | LDS B | waves/SIMD |", "|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        out.append(f"| `{r['kernel']}` | {r['source']} | {r.get('VGPRs')} | {r.get('AGPRs')} | {r.get('VGPRs Spill')} | "
+                   f"{r.get('ScratchSize [bytes/lane]')} | {r.get('LDS Size [bytes/block]')} | {r.get('Occupancy [waves/SIMD]')} |")
+    return "\n".join(out)
+
+
+def _demangle(name):
+    for tool in ("c++filt", "llvm-cxxfilt"):
+        try:
+            r = subprocess.run([tool, name], capture_output=True, text=True)
+        except OSError:
+            continue
+        if r.returncode == 0 and r.stdout.strip():
+            name = r.stdout.strip()
+            break
+    return name.replace("(anonymous namespace)::", "").replace("mhla::", "").split("(")[0].replace("void ", "")
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    if "--resources" in sys.argv:
+        print(f"# Kernel resources (gfx950)\n\nCommand: `python -m token_level_head_amd.build --resources`\n\n"
+              f"Kernel sources digest: `{source_digest()}`\n")
+        print(resources())
+    else:
+        print(build(verbose=True))
