@@ -31,6 +31,27 @@ __device__ __forceinline__ void unswz(int L, int cpr, int& row, int& chunk) {
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// x of lane n ^ 8 of the same 16-lane group (DPP row rotate by 8: a VALU move, no LDS).
+__device__ __forceinline__ float swap_half_row(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false));
+}
+
+// Two 16 x 16 float32 output tiles c and c + 1 that share the 128-byte lines of their 16
+// rows (lane (g, n) holds columns 4g .. 4g + 3 of row n of each) regrouped so that each
+// of two 16-byte stores per lane writes whole lines: `top` holds rows 0 .. 7 (lanes n < 8
+// tile c of row n, lanes n >= 8 tile c + 1 of row n - 8), `bottom` rows 8 .. 15 (lanes
+// n < 8 tile c of row n + 8, lanes n >= 8 tile c + 1 of row n).  Lane (g, n) stores
+// both at column 16 (c + n / 8) + 4g, rows n % 8 and 8 + n % 8.
+__device__ __forceinline__ void whole_lines(const f32x4& y0, const f32x4& y1, int n, f32x4& top, f32x4& bottom) {
+    const bool lo = n < 8;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float u = swap_half_row(y1[e]), v = swap_half_row(y0[e]);
+        top[e] = lo ? y0[e] : u;
+        bottom[e] = lo ? v : y1[e];
+    }
+}
+
 // phi of the two bf16 values of a word, packed back to bf16.
 __device__ __forceinline__ uint32_t phi_pair(uint32_t w) {
     return pack_bf16(phi_fast(lo_bf16(w)), phi_fast(hi_bf16(w)));

@@ -258,9 +258,7 @@ __device__ __forceinline__ void pair_outputs(const unsigned char* lds, const rsr
     }
     const float den = __shfl(dacc[0] + dacc[1], n, 64);  // lane (0, n): rows 0 and 1 of column n
     const float rden = out_scale(o, den + kEps);
-    constexpr uint32_t esz = OUT16 ? 2 : 4;
-#pragma unroll
-    for (int c = 0; c < P; ++c) {
+    auto tile = [&](int c) {  // value tile c of the 16 queries, normalised
         f32x4 y = zero4();
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
@@ -271,12 +269,28 @@ __device__ __forceinline__ void pair_outputs(const unsigned char* lds, const rsr
             y = mfma32(al, bq[ks], y);
         }
         // lane (g, n): values 16c + 4g .. +3 of query row0 + n
-        const uint32_t off = off_if(valid, ((uint32_t)(row0 + n) * D + 16 * c + 4 * g) * esz);
-        const f32x4 v = {y[0] * rden, y[1] * rden, y[2] * rden, y[3] * rden};
-        if constexpr (OUT16)
+        return f32x4{y[0] * rden, y[1] * rden, y[2] * rden, y[3] * rden};
+    };
+    if constexpr (OUT16) {
+#pragma unroll
+        for (int c = 0; c < P; ++c) {
+            const f32x4 v = tile(c);
+            const uint32_t off = off_if(valid, ((uint32_t)(row0 + n) * D + 16 * c + 4 * g) * 2);
             __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])}, rY, (int)off, 0, 2);
-        else
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rY, (int)off, 0, 2);
+        }
+    } else {
+        // tiles c, c + 1 fill the 128-byte lines of their rows: two stores of whole lines
+#pragma unroll
+        for (int c = 0; c < P; c += 2) {
+            const f32x4 y0 = tile(c), y1 = tile(c + 1);
+            f32x4 top, bottom;
+            whole_lines(y0, y1, n, top, bottom);
+            const uint32_t col = 16 * (c + n / 8) + 4 * g, r = row0 + n % 8;
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, top), rY,
+                                                   (int)off_if(valid, (r * D + col) * 4), 0, 2);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, bottom), rY,
+                                                   (int)off_if(valid, ((r + 8) * D + col) * 4), 0, 2);
+        }
     }
 }
 
