@@ -657,32 +657,13 @@ __device__ __forceinline__ void chunk_compute(const Cursor& at, const FusedShape
         // lane (g, n): value columns 16c + 4g .. +3 of query n
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
-            if (!jt.live[r]) continue;  // uniform
+            if (!jt.live[r] || jt.tq[r] >= sh.N) continue;
             const float rden = out_scale(o, jt.dacc[r][0] + kEps);
-            auto scaled = [&](int c) {
+#pragma unroll
+            for (int c = 0; c < VT; ++c) {
                 const f32x4 a = jt.oacc[r][c];
-                return f32x4{a[0] * rden, a[1] * rden, a[2] * rden, a[3] * rden};
-            };
-            if constexpr (VT % 2 == 0) {
-                if (!o.bf16) {  // uniform: float32 rows of whole 128-byte lines
-                    // value tiles c, c + 1 share the lines of their rows: regrouped so that
-                    // each store writes whole lines of 8 rows (rows past N are skipped)
-                    const int t0 = jt.tq[r] - n;  // the tile's first query
-                    const int64_t y0 = jt.yrow[r] - (int64_t)n * D;
-#pragma unroll
-                    for (int c = 0; c < VT; c += 2) {
-                        f32x4 top, bottom;
-                        whole_lines(scaled(c), scaled(c + 1), n, top, bottom);
-                        const int col = 16 * (c + n / 8) + 4 * g;
-                        if (t0 + n % 8 < sh.N) store_out(o, y0 + (int64_t)(n % 8) * D + col, top);
-                        if (t0 + 8 + n % 8 < sh.N) store_out(o, y0 + (int64_t)(8 + n % 8) * D + col, bottom);
-                    }
-                    continue;
-                }
+                store_out(o, jt.yrow[r] + 16 * c + 4 * g, f32x4{a[0] * rden, a[1] * rden, a[2] * rden, a[3] * rden});
             }
-            if (jt.tq[r] >= sh.N) continue;
-#pragma unroll
-            for (int c = 0; c < VT; ++c) store_out(o, jt.yrow[r] + 16 * c + 4 * g, scaled(c));
         }
     }
 }
