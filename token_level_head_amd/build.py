@@ -14,7 +14,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmhla.so")
 SOURCES = ["summary.hip", "mix.hip", "output.hip", "causal.hip", "decode.hip", "backward.hip", "fused.hip", "pair.hip",
-           "mhla_api.hip"]
+           "bwd_fused.hip", "mhla_api.hip"]
 OBJDIR = os.path.join(ROOT, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -36,6 +36,7 @@ KERNEL_SOURCES = [
     ("output_causal_quad", "causal.hip"),
     ("output_", "output.hip"),
     ("decode_", "decode.hip"),
+    ("bwd_fused", "bwd_fused.hip"),
     ("bwd_", "backward.hip"),
 ]
 SHARED_SOURCES = ["common.hpp", "kernels.hpp", "lds_tiles.hpp", "mhla_api.hip", "../../include/mhla.h"]

@@ -1305,6 +1305,8 @@ hipError_t run_backward(const T* q, const T* k, const T* v, const float* W, cons
 hipError_t launch_backward(int dtype, const void* q, const void* k, const void* v, const float* W, const float* dy,
                            float* dq, float* dk, float* dv, float* dW, int64_t BH, int64_t N, int D, int64_t M,
                            bool causal, bool normalize, float* ws, void* frag_ws, hipStream_t stream) {
+    if (bwd_fused_applicable(dtype, D, N, M, causal))
+        return launch_bwd_fused(q, k, v, W, dy, dq, dk, dv, dW, BH, N, D, M, normalize, ws, stream);
 #define MHLA_BWD(T)                                                                                             \
     switch (D) {                                                                                                \
         case 16:                                                                                                \

@@ -83,6 +83,12 @@ hipError_t launch_decode_step(int dtype, const void* q, const void* k, const voi
 // Backward pass (float32 arithmetic): dq, dk, dv [pair][N][d] and dW [M][M] from dy.
 // ws holds backward_workspace_floats() floats; frag_ws mix_fragment_bytes(M) bytes.
 size_t backward_workspace_floats(int64_t BH, int64_t N, int D, int64_t M, bool causal);
+// Token-level backward for short sequences (bwd_fused.hip); launch_backward takes it
+// when it applies, with BH * M * M floats of ws for the per-pair dW partials.
+bool bwd_fused_applicable(int dtype, int D, int64_t N, int64_t M, bool causal);
+hipError_t launch_bwd_fused(const void* q, const void* k, const void* v, const float* W, const float* dy, float* dq,
+                            float* dk, float* dv, float* dW, int64_t BH, int64_t N, int D, int64_t M, bool normalize,
+                            float* ws, hipStream_t stream);
 hipError_t launch_backward(int dtype, const void* q, const void* k, const void* v, const float* W, const float* dy,
                            float* dq, float* dk, float* dv, float* dW, int64_t BH, int64_t N, int D, int64_t M,
                            bool causal, bool normalize, float* ws, void* frag_ws, hipStream_t stream);
