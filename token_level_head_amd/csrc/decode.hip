@@ -80,7 +80,7 @@ __global__ __launch_bounds__(256) void decode_token_kernel(const T* __restrict__
     constexpr int L = D * D + D;
     constexpr int CG = D / 16;  // column groups (workgroups) per pair
     constexpr int RPT = D / 16; // rows per thread: 16 row groups of 16 threads
-    __shared__ float fq[D], fk[D], fv[16], part[16][16], dpart[D];
+    __shared__ float fq[D], fk[D], fv[16], part[4][16], sden;
     const int tid = threadIdx.x;
     const int64_t bid = blockIdx.x;
     const int cg = (int)((bid >> 3) % CG);
@@ -94,6 +94,22 @@ __global__ __launch_bounds__(256) void decode_token_kernel(const T* __restrict__
     if (heads > 0) W += (pair % heads) * M * M;  // one matrix per head
     const float wii = W[(int64_t)i * M + i];
 
+    // The state this thread updates and reads, loaded before the token's features so
+    // that both loads are in flight together (the state does not depend on them).
+    const int c = tid & 15, rg = tid >> 4;
+    const int base = cg * 16 * D;  // this column group's span
+    float pv[RPT], sv[RPT];
+#pragma unroll
+    for (int rr = 0; rr < RPT; ++rr) {
+        const int e = base + (rg * RPT + rr) * 16 + c;
+        pv[rr] = P[e];
+        sv[rr] = St[e];
+    }
+    float zv = 0.f, pz0 = 0.f;
+    if (tid < D) {
+        zv = St[D * D + tid];
+        pz0 = pin[tid];
+    }
     if (tid < D) {
         fq[tid] = phi_precise(load_in<T>(q, pair * D + tid));
         fk[tid] = phi_precise(load_in<T>(k, pair * D + tid));
@@ -102,29 +118,35 @@ __global__ __launch_bounds__(256) void decode_token_kernel(const T* __restrict__
     }
     __syncthreads();
 
-    const int c = tid & 15, rg = tid >> 4;
-    const int base = cg * 16 * D;  // this column group's span
     float num = 0.f;
 #pragma unroll
     for (int rr = 0; rr < RPT; ++rr) {
         const int r = rg * RPT + rr;
         const int e = base + r * 16 + c;
-        const float pn = fmaf(fk[r], fv[c], P[e]);
+        const float pn = fmaf(fk[r], fv[c], pv[rr]);
         P[e] = pn;
-        num = fmaf(fq[r], fmaf(wii, pn, St[e]), num);
+        num = fmaf(fq[r], fmaf(wii, pn, sv[rr]), num);
     }
-    part[rg][c] = num;
-    if (tid < D) {  // normaliser: p[r] + phi(k)[r]; the den term phi(q)[r] (z~[r] + W[i,i] p[r])
-        const float pz = pin[tid] + fk[tid];
-        if (cg == 0) pout[tid] = pz;
-        dpart[tid] = fq[tid] * fmaf(wii, pz, St[D * D + tid]);
+    // numerator of column c: the four row groups of each wave by lane exchange, then the
+    // four waves' parts in wave order
+    num += __shfl_xor(num, 16, 64);
+    num += __shfl_xor(num, 32, 64);
+    if ((tid & 63) < 16) part[tid >> 6][c] = num;
+    if (tid < 64) {  // normaliser: p[r] + phi(k)[r]; den = sum_r phi(q)[r] (z~[r] + W[i,i] p[r])
+        float dp = 0.f;
+        if (tid < D) {
+            const float pz = pz0 + fk[tid];
+            if (cg == 0) pout[tid] = pz;
+            dp = fq[tid] * fmaf(wii, pz, zv);
+        }
+#pragma unroll
+        for (int m = 1; m < 64; m *= 2) dp += __shfl_xor(dp, m, 64);
+        if (tid == 0) sden = dp;
     }
     __syncthreads();
     if (tid < 16) {
-        float n = 0.f, den = 0.f;
-        for (int g = 0; g < 16; ++g) n += part[g][tid];
-        for (int r = 0; r < D; ++r) den += dpart[r];
-        out[pair * D + 16 * cg + tid] = norm ? n / (den + kEps) : n;  // without the normaliser: the numerator
+        const float n = (part[0][tid] + part[1][tid]) + (part[2][tid] + part[3][tid]);
+        out[pair * D + 16 * cg + tid] = norm ? n / (sden + kEps) : n;  // without the normaliser: the numerator
     }
 }
 
