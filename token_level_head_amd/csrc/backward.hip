@@ -98,6 +98,49 @@ __device__ __forceinline__ void load_run(rsrc_t r, uint32_t off, float (&x)[CNT]
     }
 }
 
+// load_run in two halves: the loads (raw words, kept in registers) and, later, the
+// conversion to floats, so that a tile's loads can be issued a whole tile ahead.
+template <typename T, int CNT>
+struct RawRun {
+    static constexpr int BYTES = CNT * (int)sizeof(T);
+    static constexpr int WORDS = BYTES >= 4 ? BYTES / 4 : 1;
+    uint32_t w[WORDS];
+};
+
+template <typename T, int CNT>
+__device__ __forceinline__ void raw_load(rsrc_t r, uint32_t off, RawRun<T, CNT>& x) {
+    constexpr int BYTES = RawRun<T, CNT>::BYTES;
+    if constexpr (BYTES >= 16) {
+#pragma unroll
+        for (int h = 0; h < BYTES / 16; ++h) {
+            const u32x4 v = buf_load128(r, off + 16 * h);
+            x.w[4 * h] = v.x;
+            x.w[4 * h + 1] = v.y;
+            x.w[4 * h + 2] = v.z;
+            x.w[4 * h + 3] = v.w;
+        }
+    } else if constexpr (BYTES == 8) {
+        const u32x2 v = buf_load64(r, off);
+        x.w[0] = v.x;
+        x.w[1] = v.y;
+    } else if constexpr (BYTES == 4) {
+        x.w[0] = buf_load32(r, off);
+    } else {
+        x.w[0] = buf_load16(r, off);
+    }
+}
+
+template <typename T, int CNT>
+__device__ __forceinline__ void raw_cvt(const RawRun<T, CNT>& x, float (&y)[CNT]) {
+#pragma unroll
+    for (int c = 0; c < CNT; ++c) {
+        if constexpr (std::is_same<T, float>::value)
+            y[c] = __uint_as_float(x.w[c]);
+        else
+            y[c] = __uint_as_float((c & 1) ? (x.w[c >> 1] & 0xffff0000u) : (x.w[c >> 1] << 16));
+    }
+}
+
 template <int CNT>
 __device__ __forceinline__ void store_run(rsrc_t r, uint32_t off, const float (&x)[CNT]) {
     if constexpr (CNT == 4) {
@@ -638,16 +681,39 @@ __device__ __forceinline__ void query_causal_wave(const T* __restrict__ Q, const
     for (int j = 0; j < PH; ++j) pz[j] = zacc[j] = 0.f;
     __syncthreads();
 
-    for (int tile = 0; tile < ntiles; ++tile) {
+    // The tile's first operands (dy and v in row layout, k and q in dot layout) are
+    // loaded one tile ahead, as raw words, and converted when the tile starts.
+    RawRun<float, FL> pyr;
+    RawRun<T, FL> pvr;
+    RawRun<T, P> pkd[4], pqd[4];
+    auto prefetch = [&](int tile) {
         const int t0 = 16 * tile, rows = min(16, C - t0);
         const int64_t r0 = row0 + t0;
         const rsrc_t rq = tile_rsrc(Q, r0, rows, D), rk = tile_rsrc(K, r0, rows, D), rv = tile_rsrc(V, r0, rows, D);
         const rsrc_t ry = tile_rsrc(dY, r0, rows, D);
+        raw_load<float, FL>(ry, (uint32_t)((n * D + FL * g) * 4), pyr);
+        raw_load<T, FL>(rv, (uint32_t)((n * D + FL * g) * (int)sizeof(T)), pvr);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            raw_load<T, P>(rk, (uint32_t)(((4 * g + i) * D + P * n) * (int)sizeof(T)), pkd[i]);
+            raw_load<T, P>(rq, (uint32_t)(((4 * g + i) * D + P * n) * (int)sizeof(T)), pqd[i]);
+        }
+    };
+    prefetch(0);
+    for (int tile = 0; tile < ntiles; ++tile) {
+        const int t0 = 16 * tile, rows = min(16, C - t0);
+        const int64_t r0 = row0 + t0;
+        const rsrc_t rv = tile_rsrc(V, r0, rows, D);
+        const rsrc_t ry = tile_rsrc(dY, r0, rows, D);
         float yr[FL], vr[FL], kd[4][P], qd[4][P];
-        load_rl<float, D>(ry, g, n, yr);
-        load_rl<T, D>(rv, g, n, vr);
-        load_dl<T, D>(rk, g, n, kd);
-        load_dl<T, D>(rq, g, n, qd);
+        raw_cvt<float, FL>(pyr, yr);
+        raw_cvt<T, FL>(pvr, vr);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            raw_cvt<T, P>(pkd[i], kd[i]);
+            raw_cvt<T, P>(pqd[i], qd[i]);
+        }
+        if (tile + 1 < ntiles) prefetch(tile + 1);
 
         bf16x8 yh[KS], yl[KS];
         split_rl<FL, KS>(yr, yh, yl);
