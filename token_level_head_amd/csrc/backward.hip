@@ -487,14 +487,43 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
 #pragma unroll
     for (int b = 0; b < P; ++b) zacc[b] = 0.f;
 
-    for (int tile = wave; tile < ntiles; tile += wpu) {
+    // For d <= 32 the tile's operands are loaded one tile ahead as raw words (at d = 64
+    // the registers for them would push the kernel below three waves per SIMD).
+    constexpr bool PRE = D <= 32;
+    RawRun<float, FL> pyr;
+    RawRun<float, P> pyd[4];
+    RawRun<T, P> pqd[4];
+    auto prefetch = [&](int tile) {
         const int t0 = 16 * tile, rows = min(16, C - t0);
         const rsrc_t rq = tile_rsrc(Q, row0 + t0, rows, D), ry = tile_rsrc(dY, row0 + t0, rows, D);
+        raw_load<float, FL>(ry, (uint32_t)((n * D + FL * g) * 4), pyr);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            raw_load<float, P>(ry, (uint32_t)(((4 * g + i) * D + P * n) * 4), pyd[i]);
+            raw_load<T, P>(rq, (uint32_t)(((4 * g + i) * D + P * n) * (int)sizeof(T)), pqd[i]);
+        }
+    };
+    if constexpr (PRE) {
+        if (wave < ntiles) prefetch(wave);
+    }
+    for (int tile = wave; tile < ntiles; tile += wpu) {
+        const int t0 = 16 * tile, rows = min(16, C - t0);
         const rsrc_t rdq = tile_rsrc(dQ, row0 + t0, rows, D);
         float yr[FL], yd[4][P], qd[4][P];
-        load_rl<float, D>(ry, g, n, yr);
-        load_dl<float, D>(ry, g, n, yd);
-        load_dl<T, D>(rq, g, n, qd);
+        if constexpr (PRE) {
+            raw_cvt<float, FL>(pyr, yr);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                raw_cvt<float, P>(pyd[i], yd[i]);
+                raw_cvt<T, P>(pqd[i], qd[i]);
+            }
+            if (tile + wpu < ntiles) prefetch(tile + wpu);
+        } else {
+            const rsrc_t rq = tile_rsrc(Q, row0 + t0, rows, D), ry = tile_rsrc(dY, row0 + t0, rows, D);
+            load_rl<float, D>(ry, g, n, yr);
+            load_dl<float, D>(ry, g, n, yd);
+            load_dl<T, D>(rq, g, n, qd);
+        }
         bf16x8 yh[KS], yl[KS];
         split_rl<FL, KS>(yr, yh, yl);
         f32x4 u[P];  // U[4g + i][Pn + jb] = (S~_i dy_t)[r]
@@ -576,14 +605,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
     }
     if constexpr (SHARED) __syncthreads();
     if (wave >= ntiles) return;  // no barriers past this point
-    for (int tile = wave; tile < ntiles; tile += wpu) {
+    // For d <= 32 the tile's k and v are loaded one tile ahead as raw words.
+    constexpr bool PRE = D <= 32;
+    RawRun<T, FL> pvr, pkr;
+    RawRun<T, P> pkd[4];
+    auto prefetch = [&](int tile) {
         const int t0 = 16 * tile, rows = min(16, C - t0);
         const rsrc_t rk = tile_rsrc(K, row0 + t0, rows, D), rv = tile_rsrc(V, row0 + t0, rows, D);
+        raw_load<T, FL>(rv, (uint32_t)((n * D + FL * g) * (int)sizeof(T)), pvr);
+        raw_load<T, FL>(rk, (uint32_t)((n * D + FL * g) * (int)sizeof(T)), pkr);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) raw_load<T, P>(rk, (uint32_t)(((4 * g + i) * D + P * n) * (int)sizeof(T)), pkd[i]);
+    };
+    if constexpr (PRE) prefetch(wave);
+    for (int tile = wave; tile < ntiles; tile += wpu) {
+        const int t0 = 16 * tile, rows = min(16, C - t0);
         const rsrc_t rdk = tile_rsrc(dK, row0 + t0, rows, D), rdv = tile_rsrc(dV, row0 + t0, rows, D);
         float vr[FL], kr[FL], kd[4][P];
-        load_rl<T, D>(rv, g, n, vr);
-        load_rl<T, D>(rk, g, n, kr);
-        load_dl<T, D>(rk, g, n, kd);
+        if constexpr (PRE) {
+            raw_cvt<T, FL>(pvr, vr);
+            raw_cvt<T, FL>(pkr, kr);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) raw_cvt<T, P>(pkd[i], kd[i]);
+            if (tile + wpu < ntiles) prefetch(tile + wpu);
+        } else {
+            const rsrc_t rk = tile_rsrc(K, row0 + t0, rows, D), rv = tile_rsrc(V, row0 + t0, rows, D);
+            load_rl<T, D>(rv, g, n, vr);
+            load_rl<T, D>(rk, g, n, kr);
+            load_dl<T, D>(rk, g, n, kd);
+        }
 #pragma unroll
         for (int f = 0; f < FL; ++f) kr[f] = phi_b(kr[f]);
         bf16x8 vh[KS], vl[KS], kh[KS], kl[KS];
