@@ -605,8 +605,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
     }
     if constexpr (SHARED) __syncthreads();
     if (wave >= ntiles) return;  // no barriers past this point
-    // For d <= 32 the tile's k and v are loaded one tile ahead as raw words.
-    constexpr bool PRE = D <= 32;
+    // The tile's k and v are loaded one tile ahead as raw words (not for float32 inputs
+    // at d = 64, where their registers would spill).
+    constexpr bool PRE = D <= 32 || !VLO;
     RawRun<T, FL> pvr, pkr;
     RawRun<T, P> pkd[4];
     auto prefetch = [&](int tile) {
