@@ -126,7 +126,10 @@ TOKEN_LEVEL = [  # (B, H, N, d, M): shapes the token-level backward takes (bf16,
     (3, 1, 96, 32, 3),    # blocks of 32 tokens, 6 tiles
     (1, 1, 32, 64, 2),    # two tiles
     (1, 2, 160, 64, 5),   # 10 tiles: waves 2 .. 7 own one query and one key tile
-    (64, 6, 256, 64, 16), # the full DiT-S/2 256 batch
+    (64, 6, 256, 64, 16), # the full DiT-S/2 256 batch (between one and two workgroups per CU:
+    #                       some pairs split into halves)
+    (40, 8, 256, 32, 16), # 320 pairs, d = 32: 192 of them in halves
+    (33, 9, 256, 64, 4),  # 297 pairs: 208 in halves, 89 whole
 ]
 
 
@@ -156,7 +159,7 @@ def test_token_level_backward_matches_oracle(case, normalize):
 
 
 def test_token_level_backward_is_deterministic():
-    w = WORKLOADS["dit_s2_256"].shrink(B=4, H=2, seed=6700)
+    w = WORKLOADS["dit_s2_256"].shrink(B=50, H=6, seed=6700)  # 300 pairs: whole and split
     q, k, v, W = make_inputs(w)
     dy = np.random.default_rng(6701).standard_normal(q.shape).astype(np.float32)
     a = gpu_backward(q, k, v, W, dy, False, "bf16")

@@ -54,19 +54,18 @@ struct BwdCfg {
     static constexpr int CPR = D / 8;  // 16-byte pieces per row
     static constexpr int kPlane = kBMaxRows * D * 2;  // one bf16 [256][D] array
     // LDS: four planes (pass A: phi(K) hi, phi(K) lo, V; pass B: phi(Q) hi, phi(Q) lo,
-    // dy hi, dy lo), then 1 / den and dden per token, z~ per block, W, dW bins per wave,
-    // z per block.
+    // dy hi, dy lo), then 1 / den and dden per token, z~ per block, W, dW bins per wave.
     static constexpr int kDen = 4 * kPlane;
     static constexpr int kDden = kDen + kBMaxRows * 4;
     static constexpr int kZt = kDden + kBMaxRows * 4;
     static constexpr int kW = kZt + kBMaxBlocks * D * 4;
     static constexpr int kBins = kW + kBMaxBlocks * kBMaxBlocks * 4;
-    static constexpr int kZ = kBins + kBW * kBMaxBlocks * kBMaxBlocks * 4;
-    static constexpr int kBytes = kZ + kBMaxBlocks * D * 4;
+    static constexpr int kBytes = kBins + kBW * kBMaxBlocks * kBMaxBlocks * 4;
 };
 
 struct BwdShape {
     int N, M, C, QT, norm;  // QT: 16-token tiles (queries and keys alike)
+    int nwhole;             // workgroups that take a whole pair (the rest take halves)
 };
 
 // phi(x) = ELU(x) + 1 and phi'(x) (1 above zero, exp(x) = phi(x) at or below), float32.
@@ -148,11 +147,24 @@ __device__ __forceinline__ void split8(const f32x4& a, const f32x4& b, bf16x8& h
     l = __builtin_bit_cast(bf16x8, u32x4{ll[0], ll[1], ll[2], ll[3]});
 }
 
-// Sum over the 64 lanes of the wave (fixed butterfly order).
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int m = 1; m < 64; m *= 2) x += __shfl_xor(x, m, 64);
-    return x;
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 64 lanes of the wave, in a fixed order, returned in every lane: each row of
+// 16 lanes by DPP moves within the row (quad swaps, half-row then row mirror), then the
+// four row sums read from lanes 0, 16, 32, 48.  No LDS round trips.
+__device__ __forceinline__ float wave_total(float x) {
+    x += dpp_f32<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+    x += dpp_f32<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+    x += dpp_f32<0x141>(x);  // row_half_mirror
+    x += dpp_f32<0x140>(x);  // row_mirror
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+    return (r0 + r1) + (r2 + r3);
 }
 
 __device__ __forceinline__ f32x4 mfma3(const bf16x8& ah, const bf16x8& al, const bf16x8& bh, const bf16x8& bl,
@@ -168,12 +180,13 @@ struct BwdLds {
     float *rden, *dden, *zt, *wl, *bins;
 };
 
-// Pass A for NT query tiles qt0, qt0 + 8 (NT = 2) of the wave: phi(K) hi/lo in pl0/pl1,
-// V in pl2.  Writes dq and 1 / den_t, dden_t of the tiles' queries.
-template <int D, int NT>
+// Pass A for NT query tiles qts[0 .. NT) of the wave: phi(K) hi/lo in pl0/pl1, V in pl2.
+// Writes 1 / den_t, dden_t of the tiles' queries, and dq of the first NX tiles (the
+// others only need their normaliser terms, for pass B).
+template <int D, int NT, int NX>
 __device__ __forceinline__ void bwd_pass_a(const BwdLds& L, const uint16_t* __restrict__ Q,
                                            const float* __restrict__ dY, float* __restrict__ dQ, const BwdShape& sh,
-                                           int64_t pair, int qt0, int g, int n) {
+                                           int64_t pair, const int (&qts)[NT], int g, int n) {
     using Cfg = BwdCfg<D>;
     constexpr int P = Cfg::P, KS = Cfg::KS, CPR = Cfg::CPR;
     const int M = sh.M, QT = sh.QT, CT = sh.C / 16;
@@ -183,7 +196,7 @@ __device__ __forceinline__ void bwd_pass_a(const BwdLds& L, const uint16_t* __re
     int bt[NT];
 #pragma unroll
     for (int u = 0; u < NT; ++u) {
-        const int qt = qt0 + kBW * u;
+        const int qt = qts[u];
         bt[u] = qt / CT;
         qrow[u] = pair * sh.N + 16 * qt + n;
 #pragma unroll
@@ -193,16 +206,16 @@ __device__ __forceinline__ void bwd_pass_a(const BwdLds& L, const uint16_t* __re
             split8(src[0], src[1], byh[u][ks], byl[u][ks]);
         }
     }
-    f32x4 xacc[NT][P];  // (sum_j W g_tj phi(k_j))^T: features 16f + 4g + i, query n
+    f32x4 xacc[NX][P];  // (sum_j W g_tj phi(k_j))^T: features 16f + 4g + i, query n
     float dsum[NT], nsum[NT];  // this lane's keys' part of den_t and dn_t (query n)
 #pragma unroll
-    for (int u = 0; u < NT; ++u) {
-        dsum[u] = nsum[u] = 0.f;
+    for (int u = 0; u < NT; ++u) dsum[u] = nsum[u] = 0.f;
+#pragma unroll
+    for (int u = 0; u < NX; ++u)
 #pragma unroll
         for (int f = 0; f < P; ++f) xacc[u][f] = zero4();
-    }
     for (int jp = 0; jp < QT / 2; ++jp) {
-        f32x4 wg[NT][2];
+        f32x4 wg[NX][2];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const int kt = 2 * jp + hh;
@@ -228,24 +241,24 @@ __device__ __forceinline__ void bwd_pass_a(const BwdLds& L, const uint16_t* __re
                     const float a = w * s[e];
                     dsum[u] += a;
                     nsum[u] = fmaf(a, gg[e], nsum[u]);
-                    wg[u][hh][e] = w * gg[e];
+                    if (u < NX) wg[u < NX ? u : 0][hh][e] = w * gg[e];
                 }
             }
         }
-        bf16x8 gh[NT], gl[NT];  // (W g)^T as B: k-slot 8g + 4hh + e = key 32 jp + 16 hh + 4g + e
+        bf16x8 gh[NX], gl[NX];  // (W g)^T as B: k-slot 8g + 4hh + e = key 32 jp + 16 hh + 4g + e
 #pragma unroll
-        for (int u = 0; u < NT; ++u) split8(wg[u][0], wg[u][1], gh[u], gl[u]);
+        for (int u = 0; u < NX; ++u) split8(wg[u][0], wg[u][1], gh[u], gl[u]);
 #pragma unroll
         for (int f = 0; f < P; ++f) {
             const bf16x8 kth = lds_operand_t(L.pl0, 32 * jp, 16 * f, CPR, g, n);
             const bf16x8 ktl = lds_operand_t(L.pl1, 32 * jp, 16 * f, CPR, g, n);
 #pragma unroll
-            for (int u = 0; u < NT; ++u) xacc[u][f] = mfma3(kth, ktl, gh[u], gl[u], xacc[u][f]);
+            for (int u = 0; u < NX; ++u) xacc[u][f] = mfma3(kth, ktl, gh[u], gl[u], xacc[u][f]);
         }
     }
 #pragma unroll
     for (int u = 0; u < NT; ++u) {
-        const int qt = qt0 + kBW * u;
+        const int qt = qts[u];
         // den_t, dn_t for query n: the four lane groups hold disjoint keys
         const float dtot = sum_over_groups(dsum[u]), ntot = sum_over_groups(nsum[u]);
         const float rden = norm ? 1.f / (dtot + kEps) : 1.f;
@@ -254,6 +267,7 @@ __device__ __forceinline__ void bwd_pass_a(const BwdLds& L, const uint16_t* __re
             L.rden[16 * qt + n] = rden;
             L.dden[16 * qt + n] = dden;
         }
+        if (u >= NX) continue;
         // d phi(q)^T = X^T / den + dden z~_b(t), times phi'(q); 16-byte stores
 #pragma unroll
         for (int f = 0; f < P; ++f) {
@@ -265,7 +279,7 @@ __device__ __forceinline__ void bwd_pass_a(const BwdLds& L, const uint16_t* __re
             for (int i = 0; i < 4; ++i) {
                 float dp;
                 (void)phi_d(qv[i], dp);
-                out[i] = fmaf(xacc[u][f][i], rden, dden * L.zt[bt[u] * D + f0 + i]) * dp;
+                out[i] = fmaf(xacc[u < NX ? u : 0][f][i], rden, dden * L.zt[bt[u] * D + f0 + i]) * dp;
             }
             *reinterpret_cast<f32x4*>(dQ + qrow[u] * D + f0) = out;
         }
@@ -305,13 +319,22 @@ __device__ __forceinline__ void bwd_pass_b(const BwdLds& L, const uint16_t* __re
         for (int c = 0; c < P; ++c) vacc[u][c] = kacc[u][c] = zero4();
     }
     int bcur = 0;
+    // The query blocks come in order, so each (query block, key block) bin of the wave is
+    // written once: plain stores, no read-modify-write (both tiles' parts summed first when
+    // they fall in one key block).
     auto flush = [&]() {
+        if (NT == 2 && bj[0] == bj[NT - 1]) {
+            const float tot = wave_total(dwl[0] + dwl[NT - 1]);
+            if (lane == 0) mybins[bcur * kBMaxBlocks + bj[0]] = tot;
+        } else {
 #pragma unroll
-        for (int u = 0; u < NT; ++u) {
-            const float tot = wave_sum(dwl[u]);
-            if (lane == 0) mybins[bcur * kBMaxBlocks + bj[u]] += tot;
-            dwl[u] = 0.f;
+            for (int u = 0; u < NT; ++u) {
+                const float tot = wave_total(dwl[u]);
+                if (lane == 0) mybins[bcur * kBMaxBlocks + bj[u]] = tot;
+            }
         }
+#pragma unroll
+        for (int u = 0; u < NT; ++u) dwl[u] = 0.f;
     };
     for (int tp = 0; tp < QT / 2; ++tp) {
         f32x4 ad[NT][2], ds[NT][2];
@@ -410,12 +433,24 @@ __global__ __launch_bounds__(64 * kBW) void bwd_fused_kernel(const uint16_t* __r
     float* const zt = reinterpret_cast<float*>(lds + Cfg::kZt);
     float* const wl = reinterpret_cast<float*>(lds + Cfg::kW);
     float* const bins = reinterpret_cast<float*>(lds + Cfg::kBins);
-    float* const zb = reinterpret_cast<float*>(lds + Cfg::kZ);
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, n = lane & 15;
-    const int64_t pair = blockIdx.x;
+    // Workgroups below nwhole take a whole pair; the rest take half of one (the split
+    // pairs' two halves 8 workgroups apart, on one XCD): query tiles 8h .. 8h + 7 in
+    // pass A (plus the normaliser terms of the other half's tiles) and the same key tiles
+    // in pass B.  Pair counts between one and two rounds of workgroups thus end in a
+    // second round of shorter halves instead of a half-empty round of whole pairs.
+    int64_t pair;
+    int half = -1;
+    if ((int)blockIdx.x < sh.nwhole) {
+        pair = blockIdx.x;
+    } else {
+        const int idx = (int)blockIdx.x - sh.nwhole;
+        pair = sh.nwhole + (idx / 16) * 8 + idx % 8;
+        half = (idx / 8) % 2;
+    }
     const int64_t base = pair * sh.N * D;
     const int N = sh.N, M = sh.M, QT = sh.QT, CT = sh.C / 16;  // CT: tiles per block
     const bool norm = sh.norm != 0;
@@ -426,33 +461,43 @@ __global__ __launch_bounds__(64 * kBW) void bwd_fused_kernel(const uint16_t* __r
     for (int t = threadIdx.x; t < M * M; t += 64 * kBW) wl[t] = W[t];
     for (int t = threadIdx.x; t < kBW * kBMaxBlocks * kBMaxBlocks; t += 64 * kBW) bins[t] = 0.f;
     __syncthreads();
-    // z_b = sum over block b of phi(k) (hi + lo), then z~_i = sum_b W[i, b] z_b, in LDS
-    for (int t = threadIdx.x; t < M * D; t += 64 * kBW) {
-        const int b = t / D, f = t % D;
-        float z = 0.f;
-        for (int r = b * sh.C; r < (b + 1) * sh.C; ++r) {
-            const int off = 16 * swz(r, f >> 3, CPR) + 2 * (f & 7);
-            z += __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t*>(pl0 + off) << 16) +
-                 __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t*>(pl1 + off) << 16);
+    // z~_i = sum_b W[i, b] z_b = sum_r W[i, b(r)] phi(k_r): one [M x N] x [N x D] product on
+    // MFMA, wave w < P taking features 16w .. 16w + 15 (W and phi(K) as hi/lo bf16).
+    if (wave < P) {
+        f32x4 acc = zero4();  // rows (i) 4g + e, feature 16 wave + n
+        for (int kp = 0; kp < N / 32; ++kp) {
+            f32x4 w2[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                // k-slots 8g + 4hh + e are rows 32 kp + 16 hh + 4g + e (one block: C % 16 = 0)
+                const float w = n < M ? wl[n * M + (32 * kp + 16 * hh + 4 * g) / sh.C] : 0.f;
+                w2[hh] = f32x4{w, w, w, w};
+            }
+            bf16x8 wh, wlo;
+            split8(w2[0], w2[1], wh, wlo);
+            const bf16x8 kh = lds_operand_t(pl0, 32 * kp, 16 * wave, CPR, g, n);
+            const bf16x8 kl = lds_operand_t(pl1, 32 * kp, 16 * wave, CPR, g, n);
+            acc = mfma3(wh, wlo, kh, kl, acc);
         }
-        zb[t] = z;
-    }
-    __syncthreads();
-    for (int t = threadIdx.x; t < M * D; t += 64 * kBW) {
-        const int i = t / D, f = t % D;
-        float z = 0.f;
-        for (int b = 0; b < M; ++b) z = fmaf(wl[i * M + b], zb[b * D + f], z);
-        zt[t] = z;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (4 * g + e < M) zt[(4 * g + e) * D + 16 * wave + n] = acc[e];
     }
     __syncthreads();
 
     // ---- pass A: the wave's query tiles (w, and w + 8 when there is one) ----
     const BwdLds L{pl0, pl1, pl2, pl3, rden_s, dden_s, zt, wl, bins};
-    if (wave < QT) {
-        if (wave + kBW < QT)
-            bwd_pass_a<D, 2>(L, Q, dY, dQ, sh, pair, wave, g, n);
-        else
-            bwd_pass_a<D, 1>(L, Q, dY, dQ, sh, pair, wave, g, n);
+    if (half >= 0) {  // (QT = 16)
+        const int qts[2] = {8 * half + wave, 8 * (1 - half) + wave};
+        bwd_pass_a<D, 2, 1>(L, Q, dY, dQ, sh, pair, qts, g, n);
+    } else if (wave < QT) {
+        if (wave + kBW < QT) {
+            const int qts[2] = {wave, wave + kBW};
+            bwd_pass_a<D, 2, 2>(L, Q, dY, dQ, sh, pair, qts, g, n);
+        } else {
+            const int qts[1] = {wave};
+            bwd_pass_a<D, 1, 1>(L, Q, dY, dQ, sh, pair, qts, g, n);
+        }
     }
     __syncthreads();  // every wave is done with phi(K) and V in LDS; 1 / den, dden written
 
@@ -461,7 +506,9 @@ __global__ __launch_bounds__(64 * kBW) void bwd_fused_kernel(const uint16_t* __r
     stage_dy<D>(dY, base, N, pl2, pl3);
     __syncthreads();
     float* const mybins = bins + wave * kBMaxBlocks * kBMaxBlocks;
-    if (wave < QT) {
+    if (half >= 0) {
+        bwd_pass_b<D, 1>(L, K, V, dK, dV, mybins, sh, pair, 8 * half + wave, lane, g, n);
+    } else if (wave < QT) {
         if (wave + kBW < QT)
             bwd_pass_b<D, 2>(L, K, V, dK, dV, mybins, sh, pair, wave, lane, g, n);
         else
@@ -474,7 +521,7 @@ __global__ __launch_bounds__(64 * kBW) void bwd_fused_kernel(const uint16_t* __r
         float s = 0.f;
 #pragma unroll
         for (int w = 0; w < kBW; ++w) s += bins[w * kBMaxBlocks * kBMaxBlocks + i * kBMaxBlocks + b];
-        dWpart[pair * M * M + t] = s;
+        dWpart[(int64_t)blockIdx.x * M * M + t] = s;  // one partial per workgroup
     }
 }
 
@@ -506,7 +553,7 @@ bool bwd_fused_applicable(int dtype, int D, int64_t N, int64_t M, bool causal) {
     return C % 16 == 0 && (N / 16) % 2 == 0;
 }
 
-size_t bwd_fused_workspace_floats(int64_t BH, int64_t M) { return (size_t)(BH * M * M); }
+size_t bwd_fused_workspace_floats(int64_t BH, int64_t M) { return (size_t)(2 * BH * M * M); }
 
 hipError_t launch_bwd_fused(const void* q, const void* k, const void* v, const float* W, const float* dy, float* dq,
                             float* dk, float* dv, float* dW, int64_t BH, int64_t N, int D, int64_t M, bool normalize,
@@ -517,10 +564,17 @@ hipError_t launch_bwd_fused(const void* q, const void* k, const void* v, const f
     sh.C = (int)(N / M);
     sh.QT = (int)(N / 16);
     sh.norm = normalize ? 1 : 0;
+    // Between one and two rounds of workgroups (one per CU): split the pairs that would
+    // run alone in the second round into halves (a multiple of 8 of them).
+    const int64_t cus = device_cu_count();
+    int64_t nsplit = 0;
+    if (sh.QT == 16 && BH > cus && BH < 2 * cus) nsplit = (2 * cus - BH) / 8 * 8;
+    sh.nwhole = (int)(BH - nsplit);
     const uint16_t* qq = static_cast<const uint16_t*>(q);
     const uint16_t* kk = static_cast<const uint16_t*>(k);
     const uint16_t* vv = static_cast<const uint16_t*>(v);
-    const dim3 grid((unsigned)BH), block(64 * kBW);
+    const int64_t nwg = BH + nsplit;
+    const dim3 grid((unsigned)nwg), block(64 * kBW);
     switch (D) {
         case 32: bwd_fused_kernel<32><<<grid, block, 0, stream>>>(qq, kk, vv, W, dy, dq, dk, dv, ws, sh); break;
         case 64: bwd_fused_kernel<64><<<grid, block, 0, stream>>>(qq, kk, vv, W, dy, dq, dk, dv, ws, sh); break;
@@ -529,7 +583,7 @@ hipError_t launch_bwd_fused(const void* q, const void* k, const void* v, const f
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int MM = (int)(M * M);
-    bwd_fused_dw_kernel<<<dim3((unsigned)MM), dim3(256), 0, stream>>>(ws, dW, BH, MM);
+    bwd_fused_dw_kernel<<<dim3((unsigned)MM), dim3(256), 0, stream>>>(ws, dW, nwg, MM);
     return hipGetLastError();
 }
 
