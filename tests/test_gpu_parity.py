@@ -112,6 +112,8 @@ SWEEP = [  # (B, H, N, d, M, causal, dtype)
     (1, 1, 2048, 16, 2048, True, "bf16"),
     (2, 1, 1024, 64, 32, False, "bf16"),  # M = 32 mixing variant
     (2, 1, 1024, 64, 32, True, "bf16"),
+    (1, 3, 768, 16, 48, False, "bf16"),  # 32 < M <= 64, persistent mixing walk: ragged last column tile
+    (2, 1, 680, 32, 34, True, "bf16"),   # M = 34 causal: 33 blocks in two k-chunks, the second of one
 ]
 
 

@@ -37,6 +37,8 @@ constexpr int kWideMaxNT = 8;        // 64 < M <= 256 kernel: column tiles of 16
 constexpr int kWideMaxKC = 8;        // ... k-chunks of 32 (M <= 256)
 constexpr int kWideTasks = 2;        // ... strip-load tasks per thread: 16 * KC * NT / 512
 constexpr int kWideRT = 2;           // ... row tiles of 16 per wave (8 waves: 256 rows)
+constexpr int kWalkPerCU = 2;       // 32 < M <= 64 kernel: persistent workgroups of four waves per CU
+constexpr int kWalkJ = 4;           // ... columns per lane (a wave's tile: 16 J columns)
 
 template <int KSTEP>
 struct MixOps;
@@ -656,6 +658,143 @@ __global__ __launch_bounds__(256) void mix_lds_kernel(const float* __restrict__ 
     }
 }
 
+// 32 < M <= 64 (two 32-deep k-chunks, RT = 4 row tiles, J columns per lane): the kernel above made
+// persistent.  Each workgroup splits W into LDS once; its waves then walk column tiles
+// 4 blockIdx.x + wave, plus multiples of 4 gridDim.x, with the S loads one k-chunk
+// ahead across tile boundaries, so the next tile's first chunk is in flight while the
+// current tile's last chunk is multiplied and its rows are stored.  S and St are
+// addressed through buffer descriptors: a load past a valid row or column reads zero
+// and a store there is dropped, so every wave issues the same loads and stores on
+// every tile (the wait counts stay exact) and the last prefetch needs no branch.
+template <int J, bool CAUSAL>
+__global__ __launch_bounds__(256) void mix_walk_kernel(const float* __restrict__ S, const float* __restrict__ W,
+                                                       float* __restrict__ St, int64_t ncols, int64_t ld, int M,
+                                                       int64_t ntiles, int kc_cap) {
+    constexpr int KSTEP = 32, RT = 4;
+    using colv = typename std::conditional<J == 4, f32x4, f32x2>::type;
+    S += (int64_t)blockIdx.y * ncols;
+    St += (int64_t)blockIdx.y * ncols;
+    W += (int64_t)blockIdx.y * M * M;
+    using Ops = MixOps<KSTEP>;
+    using frag = typename Ops::frag;
+    constexpr int E = Ops::E;
+    extern __shared__ __align__(16) unsigned char smem[];
+    frag* wf = reinterpret_cast<frag*>(smem);
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, n = lane & 15;
+    const int imax = min(M, 16 * RT);
+    const int kend = CAUSAL ? imax - 1 : M;
+    const int kcn = 2;  // 32 < kend <= 64
+    const uint32_t span = (uint32_t)((int64_t)(M - 1) * ld + ncols) * 4;  // rows 0 .. M-1 of this column block
+    const rsrc_t rS = make_rsrc(S, span), rT = make_rsrc(St, span);
+    const int64_t stride = 4 * (int64_t)gridDim.x;
+    int64_t ct = (int64_t)blockIdx.x * 4 + wave;
+
+    auto load = [&](int64_t t, int kc, colv (&sv)[E]) {
+        const int64_t col = t * 16 * J + J * n;
+        const bool ok = t < ntiles && col < ncols;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int b = kc * KSTEP + E * g + e;
+            const uint32_t off = off_if(ok && b < kend, (uint32_t)(b * ld + col) * 4);
+            if constexpr (J == 4)
+                sv[e] = __builtin_bit_cast(f32x4, buf_load128(rS, off));
+            else
+                sv[e] = __builtin_bit_cast(f32x2, buf_load64(rS, off));
+        }
+    };
+    auto compute = [&](int kc, const colv (&sv)[E], f32x4 (&acc)[RT][J]) {
+        // W fragments are read from LDS here on every chunk rather than kept in
+        // registers across the walk (which would cost 64 VGPRs and halve the waves
+        // that keep loads in flight)
+        asm volatile("" ::: "memory");
+        frag bh[J], bl[J];
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const bf16pair p = split_bf16(sv[e][j]);
+                bh[j][e] = p.hi;
+                bl[j][e] = p.lo;
+            }
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            if (16 * r < imax) {  // uniform
+                const frag ah = wf[((r * kc_cap + kc) * 64 + lane) * 2];
+                const frag al = wf[((r * kc_cap + kc) * 64 + lane) * 2 + 1];
+#pragma unroll
+                for (int j = 0; j < J; ++j) {
+                    acc[r][j] = Ops::mma(ah, bh[j], acc[r][j]);
+                    acc[r][j] = Ops::mma(ah, bl[j], acc[r][j]);
+                    acc[r][j] = Ops::mma(al, bh[j], acc[r][j]);
+                }
+            }
+        }
+    };
+    auto store = [&](int64_t t, f32x4 (&acc)[RT][J]) {
+        const int64_t col = t * 16 * J + J * n;
+        const bool colok = t < ntiles && col < ncols;
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * r + 4 * g + i;
+                const int off = (int)off_if(colok && row < imax, (uint32_t)(row * ld + col) * 4);
+                if constexpr (J == 4) {
+                    const f32x4 v = f32x4{acc[r][0][i], acc[r][1][i], acc[r][2][i], acc[r][3][i]};
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rT, off, 0, 0);
+                } else {
+                    const u32x2 v = u32x2{__float_as_uint(acc[r][0][i]), __float_as_uint(acc[r][1][i])};
+                    __builtin_amdgcn_raw_buffer_store_b64(v, rT, off, 0, 0);
+                }
+#pragma unroll
+                for (int j = 0; j < J; ++j) acc[r][j][i] = 0.f;
+            }
+    };
+
+    colv sa[E], sb[E];
+    load(ct, 0, sa);  // in flight while W is split
+    for (int slot = threadIdx.x; slot < RT * kcn * 64; slot += blockDim.x) {
+        const int ln = slot & 63, t = slot >> 6;
+        const int kc = t % kcn, rt = t / kcn;
+        const int i = 16 * rt + (ln & 15);
+        const int b0 = kc * KSTEP + E * (ln >> 4);
+        frag h, l;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int b = b0 + e;
+            const bool use = i < M && b < kend && (!CAUSAL || b < i);
+            const bf16pair p = split_bf16(load_or_zero(W + (int64_t)i * M + b, use, W));
+            h[e] = p.hi;
+            l[e] = p.lo;
+        }
+        wf[((rt * kc_cap + kc) * 64 + ln) * 2] = h;
+        wf[((rt * kc_cap + kc) * 64 + ln) * 2 + 1] = l;
+    }
+    __syncthreads();
+    if (ct >= ntiles) return;  // no barriers below
+
+    f32x4 acc[RT][J];
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int j = 0; j < J; ++j) acc[r][j] = zero4();
+    while (true) {
+        load(ct, 1, sb);
+        issue_fence();
+        compute(0, sa, acc);
+        issue_fence();  // sa is free before its next loads are issued
+        const int64_t nt = ct + stride;
+        load(nt, 0, sa);  // past the last tile: reads nothing
+        issue_fence();
+        compute(1, sb, acc);
+        store(ct, acc);
+        if (nt >= ntiles) break;
+        ct = nt;
+    }
+}
+
 // M = 1: the mixing is a single scale, St = W[0][0] S (causal: no earlier block, St = 0),
 // done as a streaming float32 multiply (exact products, HBM-bound).
 template <bool CAUSAL>
@@ -817,12 +956,25 @@ hipError_t launch_mix(const float* S, const float* W, float* St, int64_t BH, int
                 mix_lds_kernel<KSTEP, RT, J, PIPE, false><<<grid, dim3(256), lds, stream>>>(S, W, St, ncols, ld,
                                                                                            (int)M, ntiles, KC);
         };
-        if (M <= 16)
+        if (M <= 16) {
             run(I16{}, I1{}, I4{});
-        else if (M <= 32)
+        } else if (M <= 32) {
             run(I32{}, I2{}, I4{});
-        else
+        } else if (M > 32 + (causal ? 1 : 0) && (M * ld + 64) * 4 < (int64_t(1) << 32)) {  // two k-chunks;
+            //                                                                    32-bit buffer offsets
+            const int KC = (int)((M + 31) / 32);
+            const size_t lds = (size_t)4 * KC * 64 * 2 * 16;
+            const int64_t ntiles = (ncols + 16 * kWalkJ - 1) / (16 * kWalkJ);
+            // kWalkPerCU workgroups of four waves per CU, shared out over the heads
+            const int64_t per_head = std::max<int64_t>(1, (int64_t)device_cu_count() * kWalkPerCU / gy);
+            const dim3 grid((unsigned)std::min<int64_t>((ntiles + 3) / 4, per_head), gy);
+            if (causal)
+                mix_walk_kernel<kWalkJ, true><<<grid, dim3(256), lds, stream>>>(S, W, St, ncols, ld, (int)M, ntiles, KC);
+            else
+                mix_walk_kernel<kWalkJ, false><<<grid, dim3(256), lds, stream>>>(S, W, St, ncols, ld, (int)M, ntiles, KC);
+        } else {
             run(I32{}, I4{}, I4{});
+        }
         return hipGetLastError();
     }
     if (M <= 256 && M * ld * 4 < (int64_t(1) << 32) - 64) {  // 64 < M <= 256: persistent tile walk
