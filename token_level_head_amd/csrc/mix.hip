@@ -487,6 +487,14 @@ __global__ __launch_bounds__(512) void mix_stream_kernel(const float* __restrict
     // lane (g, n) holds W[i0 + 16r + n][32kc + 8g + e], e < 8 (zero past M; causal b < i).
     // W (at most 256 KiB) is read through a buffer descriptor: 32-bit offsets, and an
     // offset past the end reads zero.
+    // M = 256 (FULL): each load instruction reads 8 whole 128-byte lines (lane l: row
+    // 8h + l / 8 of the row tile, floats 32kc + 4 (l % 8) .. + 3), and the k-chunk's 16 rows
+    // are turned into the operand layout through a 2 KiB slice of the second tile buffer
+    // per wave, which no wave uses before the first barrier (16-byte pieces swizzled by
+    // row: conflict-free writes, two-way reads).  Loads of the operand layout itself touch
+    // 16 half lines per instruction, and every CU reading all of W that way took twice as
+    // long on cold inputs.
+    uint32_t* const wslot = &tile[1][0][0] + 512 * wave;
     const rsrc_t rW = make_rsrc(W, (uint32_t)M * M * 4);
 #pragma unroll
     for (int r = 0; r < 2; ++r) {  // one row tile at a time: all its loads, then the splits
@@ -497,8 +505,10 @@ __global__ __launch_bounds__(512) void mix_stream_kernel(const float* __restrict
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int b = 32 * kc + 8 * g + 4 * h;
-                if constexpr (FULL) {  // M = 256: rows 16-byte aligned, 16-byte loads
-                    x[kc][h] = __builtin_bit_cast(f32x4, buf_load128(rW, (uint32_t)(i * M + b) * 4));
+                if constexpr (FULL) {
+                    const int row = i0 + 16 * r + 8 * h + (lane >> 3);
+                    x[kc][h] = __builtin_bit_cast(f32x4,
+                                                  buf_load128(rW, (uint32_t)(row * M + 32 * kc + 4 * (lane & 7)) * 4));
                 } else {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
@@ -508,6 +518,18 @@ __global__ __launch_bounds__(512) void mix_stream_kernel(const float* __restrict
         issue_fence();
 #pragma unroll
         for (int kc = 0; kc < kStreamKC; ++kc) {
+            if constexpr (FULL) {  // rows 8h + l / 8, piece l % 8 -> lane (g, n): row n, pieces 2g, 2g + 1
+                asm volatile("" ::: "memory");  // the previous k-chunk's reads come first
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int row = 8 * h + (lane >> 3);
+                    *reinterpret_cast<f32x4*>(wslot + 32 * row + 4 * ((lane & 7) ^ (row & 7))) = x[kc][h];
+                }
+                asm volatile("" ::: "memory");
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    x[kc][h] = *reinterpret_cast<const f32x4*>(wslot + 32 * n + 4 * ((2 * g + h) ^ (n & 7)));
+            }
             uint32_t hw[4], lw[4];
 #pragma unroll
             for (int e2 = 0; e2 < 4; ++e2) {
