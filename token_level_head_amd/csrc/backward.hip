@@ -1257,6 +1257,66 @@ __global__ __launch_bounds__(256) void bwd_dw_kernel(const float* __restrict__ d
         }
 }
 
+// The same partials for four row tiles per workgroup (M > 32): the waves take row tiles
+// 16w of one 64 x 64 output block and share its S rows.  Wave w loads S rows
+// b0 + 16w .. + 15, splits them into the B operand of column tile w and hands it to
+// the other waves through LDS (double-buffered, one LDS-scoped barrier per 32-column
+// step, so the loads issued two steps ahead stay in flight), so each S row is read once
+// per workgroup instead of once per wave.  Same products in the same order as above.
+__global__ __launch_bounds__(256) void bwd_dw_shared_kernel(const float* __restrict__ dSt,
+                                                            const float* __restrict__ S, float* __restrict__ part,
+                                                            int64_t ncols, int M, int64_t chunk, int nb) {
+    __shared__ bf16x8 bop[2][4][2][64];  // [buffer][column tile][hi, lo][lane]
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, n = lane & 15;
+    const int ob = (int)(blockIdx.x % (nb * nb));
+    const int64_t ch = blockIdx.x / (nb * nb);
+    const int i0 = 64 * (ob / nb) + 16 * wave, b0 = 64 * (ob % nb);
+    const int64_t k0 = ch * chunk, k1 = min(ncols, k0 + chunk);
+    if (k0 >= ncols) return;  // the whole workgroup
+    f32x4 acc[4];
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) acc[jb] = zero4();
+    const int nsteps = (int)((k1 - k0 + 31) / 32);
+    DwRun xa[2], xs[2];
+    int64_t k = k0 + 8 * g;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        dw_load(dSt, ncols, i0 + n, M, k + 32 * h, k1, xa[h]);
+        dw_load(S, ncols, b0 + 16 * wave + n, M, k + 32 * h, k1, xs[h]);
+    }
+    auto step = [&](DwRun& a, DwRun& sr, int64_t knext, int buf) {
+        bf16x8 ah, al, sh, sl;
+        dw_split(a, ah, al);
+        dw_split(sr, sh, sl);
+        dw_load(dSt, ncols, i0 + n, M, knext, k1, a);
+        dw_load(S, ncols, b0 + 16 * wave + n, M, knext, k1, sr);
+        issue_fence();
+        bop[buf][wave][0][lane] = sh;
+        bop[buf][wave][1][lane] = sl;
+        lds_barrier();
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+            const bf16x8 bh = bop[buf][jb][0][lane], bl = bop[buf][jb][1][lane];
+            acc[jb] = mfma32(ah, bh, acc[jb]);
+            acc[jb] = mfma32(ah, bl, acc[jb]);
+            acc[jb] = mfma32(al, bh, acc[jb]);
+        }
+    };
+    for (int st = 0; st < nsteps; st += 2, k += 64) {  // nsteps is uniform: every wave meets every barrier
+        step(xa[0], xs[0], k + 64, 0);
+        if (st + 1 >= nsteps) break;
+        step(xa[1], xs[1], k + 96, 1);
+    }
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = i0 + 4 * g + i, col = b0 + 16 * jb + n;
+            if (row < M && col < M) part[(ch * M + row) * (int64_t)M + col] = acc[jb][i];
+        }
+}
+
 // First reduction level: part2[s][x] = sum of part[ch][x] over chunks ch of group s
 // (cps chunks per group), in chunk order; consecutive threads take consecutive x.
 __global__ __launch_bounds__(256) void bwd_dw_reduce1_kernel(const float* __restrict__ part,
@@ -1310,10 +1370,10 @@ DwPlan dw_plan(int64_t ncols, int64_t M) {
     if (p.rt == 3) p.rt = 4;
     const int64_t subs = 4 / p.rt;
     const int64_t nblk = (int64_t)p.nb * p.nb;
-    // One round of resident workgroups: 256 CUs x (waves per SIMD of bwd_dw_kernel<rt>:
-    // 6, 4, 2 for rt = 1, 2, 4) four-wave workgroups; a few workgroups past it would
-    // form a second round alone.
-    const int64_t round = 256 * (p.rt == 1 ? 6 : p.rt == 2 ? 4 : 2);
+    // One round of resident workgroups: 256 CUs x (waves per SIMD of bwd_dw_kernel<rt>
+    // and bwd_dw_shared_kernel: 6, 4, 4 for rt = 1, 2, 4) four-wave workgroups; a few
+    // workgroups past it would form a second round alone.
+    const int64_t round = 256 * (p.rt == 1 ? 6 : 4);
     const int64_t want = std::max<int64_t>(1, round / nblk) * subs;  // partials (one per wave slot)
     const int64_t most = std::max<int64_t>(1, ncols / 512);          // at least 512 columns per partial
     const int64_t nch = std::min(want, most);
@@ -1373,7 +1433,7 @@ hipError_t run_backward(const T* q, const T* k, const T* v, const float* W, cons
     const int64_t units = BH * M, C = N / M, ntiles = (C + 15) / 16;
     const int wpu = waves_per_unit(units, ntiles);
     const size_t red = (size_t)(wpu / 2) * L * sizeof(float);
-    const dim3 grid((unsigned)units), block(64 * wpu), one(64);
+    const dim3 grid((unsigned)units), block(64 * wpu);
     hipError_t e;
     bwd_sum_kernel<D, T><<<grid, block, red, stream>>>(k, v, S, BH, (int)N, (int)M, wpu);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1405,7 +1465,7 @@ hipError_t run_backward(const T* q, const T* k, const T* v, const float* W, cons
     else if (p.rt == 2)
         bwd_dw_kernel<2><<<dw_grid, dim3(256), 0, stream>>>(dSt, S, part, BH * L, (int)M, p.chunk, p.nb, p.rt);
     else
-        bwd_dw_kernel<4><<<dw_grid, dim3(256), 0, stream>>>(dSt, S, part, BH * L, (int)M, p.chunk, p.nb, p.rt);
+        bwd_dw_shared_kernel<<<dw_grid, dim3(256), 0, stream>>>(dSt, S, part, BH * L, (int)M, p.chunk, p.nb);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t groups = (M * M + 255) / 256;
     bwd_dw_reduce1_kernel<<<dim3((unsigned)(groups * p.nsplit)), dim3(256), 0, stream>>>(part, part2, M * M,

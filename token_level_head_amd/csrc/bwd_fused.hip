@@ -422,7 +422,7 @@ __global__ __launch_bounds__(64 * kBW) void bwd_fused_kernel(const uint16_t* __r
                                                              float* __restrict__ dK, float* __restrict__ dV,
                                                              float* __restrict__ dWpart, BwdShape sh) {
     using Cfg = BwdCfg<D>;
-    constexpr int P = Cfg::P, KS = Cfg::KS, CPR = Cfg::CPR;
+    constexpr int P = Cfg::P, CPR = Cfg::CPR;
     __shared__ __align__(16) unsigned char lds[Cfg::kBytes];
     unsigned char* const pl0 = lds;
     unsigned char* const pl1 = lds + Cfg::kPlane;
@@ -452,8 +452,7 @@ __global__ __launch_bounds__(64 * kBW) void bwd_fused_kernel(const uint16_t* __r
         half = (idx / 8) % 2;
     }
     const int64_t base = pair * sh.N * D;
-    const int N = sh.N, M = sh.M, QT = sh.QT, CT = sh.C / 16;  // CT: tiles per block
-    const bool norm = sh.norm != 0;
+    const int N = sh.N, M = sh.M, QT = sh.QT;
 
     // ---- set-up: phi(K) hi/lo and V to LDS, W, cleared dW bins ----
     stage_rows<D, true>(K, base, N, pl0, pl1);
