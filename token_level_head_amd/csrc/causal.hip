@@ -148,48 +148,85 @@ __global__ __launch_bounds__(256) void output_causal_quad_kernel(const uint16_t*
     // Lane (g, n) of a row load reads features 4Pg .. 4Pg + 4P - 1 of token row n.
     auto row_off = [&](int tile, int r) { return ((uint32_t)(bstart + 16 * tile + r) * D + 4 * P * g) * 2; };
 
-    // ---- before the barrier: S~ operands into LDS, phi(K) of own tiles into LDS ----
-    for (int pi = wave; pi < KS * P; pi += 4) {  // uniform
-        const int ks = pi / P, jb = pi % P;
-        const f32x4 c0 = *reinterpret_cast<const f32x4*>(sv + ((2 * ks) * P + jb) * 256 + lane * 4);
-        f32x4 c1 = zero4();
-        if (2 * ks + 1 < P) c1 = *reinterpret_cast<const f32x4*>(sv + ((2 * ks + 1) * P + jb) * 256 + lane * 4);
-        const float x[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
-        bf16x8 hi, lo;
-        split8(x, hi, lo);
-        sh[pi * 64 + lane] = __builtin_bit_cast(uint4, hi);
-        sl[pi * 64 + lane] = __builtin_bit_cast(uint4, lo);
+    // ---- before the barrier: S~ operands into LDS, phi(K) and V of own tiles into LDS ----
+    // Every load of this part is issued first -- the S~ chunks the wave splits, z~, the K
+    // and V rows of its first two tiles (reading zero where a tile or row is absent) and
+    // the first Q row -- so that their latencies overlap instead of forming a chain.
+    constexpr int PRE = 2;                  // own tiles whose rows are loaded up front
+    constexpr int NPI = (KS * P + 3) / 4;   // S~ chunks per wave
+    f32x4 sc[NPI][2];
+#pragma unroll
+    for (int q = 0; q < NPI; ++q) {
+        const int pi = wave + 4 * q, ks = pi / P, jb = pi % P;
+        const bool has = pi < KS * P, has1 = has && 2 * ks + 1 < P;
+        sc[q][0] = *reinterpret_cast<const f32x4*>(sv + (has ? ((2 * ks) * P + jb) * 256 : 0) + lane * 4);
+        sc[q][1] = *reinterpret_cast<const f32x4*>(sv + (has1 ? ((2 * ks + 1) * P + jb) * 256 : 0) + lane * 4);
+        if (!has1) sc[q][1] = zero4();
     }
-    uint32_t qraw[2 * P];  // Q row of the first own tile, loaded before the barrier
+    f32x4 z4[P];
+#pragma unroll
+    for (int h = 0; h < P; ++h) z4[h] = *reinterpret_cast<const f32x4*>(sv + D * D + 4 * P * g + 4 * h);
+    typedef uint32_t VRun[P == 4 ? 2 : 1];
+    auto load_own = [&](int t, uint32_t (&kraw)[2 * P], VRun (&vr)[4]) {
+        load_row<P, NT>(rK, off_if(t < T && 16 * t + n < C, row_off(t, n)), kraw);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int row = 16 * t + 4 * g + e;
+            const uint32_t off = off_if(t < T && row < C, ((uint32_t)(bstart + row) * D + P * n) * 2);
+            if constexpr (P == 4) {
+                const u32x2 x = buf_load64<NT>(rV, off);
+                vr[e][0] = x.x;
+                vr[e][1] = x.y;
+            } else if constexpr (P == 2) {
+                vr[e][0] = buf_load32<NT>(rV, off);
+            } else {
+                vr[e][0] = buf_load16<NT>(rV, off);
+            }
+        }
+    };
+    uint32_t kpre[PRE][2 * P];
+    VRun vpre[PRE][4];
+#pragma unroll
+    for (int s = 0; s < PRE; ++s) load_own(own_tile(wave, s), kpre[s], vpre[s]);
+    uint32_t qraw[2 * P];  // Q row of the first own tile
     load_row<P, NT>(rQ, off_if(16 * own_tile(wave, 0) + n < C, row_off(own_tile(wave, 0), n)), qraw);
+    issue_fence();
+
+#pragma unroll
+    for (int q = 0; q < NPI; ++q) {
+        const int pi = wave + 4 * q;
+        if (pi < KS * P) {  // uniform
+            const float x[8] = {sc[q][0][0], sc[q][0][1], sc[q][0][2], sc[q][0][3],
+                                sc[q][1][0], sc[q][1][1], sc[q][1][2], sc[q][1][3]};
+            bf16x8 hi, lo;
+            split8(x, hi, lo);
+            sh[pi * 64 + lane] = __builtin_bit_cast(uint4, hi);
+            sl[pi * 64 + lane] = __builtin_bit_cast(uint4, lo);
+        }
+    }
 #pragma unroll
     for (int s = 0; s < kQuadMaxOwn; ++s) {
         const int t = own_tile(wave, s);
         if (t < T) {  // uniform
             uint32_t kraw[2 * P];
+            VRun vr[4];
+            if (s < PRE) {
+#pragma unroll
+                for (int w = 0; w < 2 * P; ++w) kraw[w] = kpre[s < PRE ? s : 0][w];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+#pragma unroll
+                    for (int h = 0; h < (P == 4 ? 2 : 1); ++h) vr[e][h] = vpre[s < PRE ? s : 0][e][h];
+            } else {
+                load_own(t, kraw, vr);
+            }
             const bool ok = 16 * t + n < C;
-            load_row<P, NT>(rK, off_if(ok, row_off(t, n)), kraw);
             bf16x8 ak[KS];
             phi_operand<P, KS>(kraw, ok, ak);
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) kb[(t * KS + ks) * 64 + lane] = __builtin_bit_cast(uint4, ak[ks]);
             // V of keys 4g + e (e < 4) of tile t, value columns P n + jb, packed per column
             // block as the four bf16 of one half of the score x V B operand.
-            uint32_t vr[4][P == 4 ? 2 : 1];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = 16 * t + 4 * g + e;
-                const uint32_t off = off_if(row < C, ((uint32_t)(bstart + row) * D + P * n) * 2);
-                if constexpr (P == 4) {
-                    const u32x2 x = buf_load64<NT>(rV, off);
-                    vr[e][0] = x.x;
-                    vr[e][1] = x.y;
-                } else if constexpr (P == 2) {
-                    vr[e][0] = buf_load32<NT>(rV, off);
-                } else {
-                    vr[e][0] = buf_load16<NT>(rV, off);
-                }
-            }
 #pragma unroll
             for (int jb = 0; jb < P; ++jb) {
                 uint32_t hv[4];
@@ -207,11 +244,9 @@ __global__ __launch_bounds__(256) void output_causal_quad_kernel(const uint16_t*
     {
         float zf[4 * P];
 #pragma unroll
-        for (int h = 0; h < P; ++h) {
-            const f32x4 z4 = *reinterpret_cast<const f32x4*>(sv + D * D + 4 * P * g + 4 * h);
+        for (int h = 0; h < P; ++h)
 #pragma unroll
-            for (int u = 0; u < 4; ++u) zf[4 * h + u] = z4[u];
-        }
+            for (int u = 0; u < 4; ++u) zf[4 * h + u] = z4[h][u];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             float x[8];
