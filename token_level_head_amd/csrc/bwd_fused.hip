@@ -180,18 +180,29 @@ struct BwdLds {
     float *rden, *dden, *zt, *wl, *bins;
 };
 
+// The row-layout operands of two 16-row tiles (hi and lo planes of one matrix).
+template <int D>
+struct TileOps {
+    bf16x8 h[2][BwdCfg<D>::KS], l[2][BwdCfg<D>::KS];
+};
+
 // Pass A for NT query tiles qts[0 .. NT) of the wave: phi(K) hi/lo in pl0/pl1, V in pl2.
 // Writes 1 / den_t, dden_t of the tiles' queries, and dq of the first NX tiles (the
-// others only need their normaliser terms, for pass B).
+// others only need their normaliser terms, for pass B).  The tiles' phi(q) and dy
+// operands are left in qo and yo for pass B's planes.
 template <int D, int NT, int NX>
 __device__ __forceinline__ void bwd_pass_a(const BwdLds& L, const uint16_t* __restrict__ Q,
                                            const float* __restrict__ dY, float* __restrict__ dQ, const BwdShape& sh,
-                                           int64_t pair, const int (&qts)[NT], int g, int n) {
+                                           int64_t pair, const int (&qts)[NT], int g, int n, TileOps<D>& qo,
+                                           TileOps<D>& yo) {
     using Cfg = BwdCfg<D>;
     constexpr int P = Cfg::P, KS = Cfg::KS, CPR = Cfg::CPR;
     const int M = sh.M, QT = sh.QT, CT = sh.C / 16;
     const bool norm = sh.norm != 0;
-    bf16x8 bqh[NT][KS], bql[NT][KS], byh[NT][KS], byl[NT][KS];  // phi(q) and dy as B operands: query n
+    auto& bqh = qo.h;  // phi(q) and dy as B operands: query n
+    auto& bql = qo.l;
+    auto& byh = yo.h;
+    auto& byl = yo.l;
     int64_t qrow[NT];
     int bt[NT];
 #pragma unroll
@@ -287,16 +298,19 @@ __device__ __forceinline__ void bwd_pass_a(const BwdLds& L, const uint16_t* __re
 }
 
 // Pass B for NT key tiles kt0, kt0 + 8 (NT = 2) of the wave: phi(Q) hi/lo in pl0/pl1, dy
-// hi/lo in pl2/pl3.  Writes dk, dv and adds sum dA s to the wave's dW bins.
+// hi/lo in pl2/pl3; the tiles' phi(k) operands in ko (hi, lo) and their v in vo.h.
+// Writes dk, dv and adds sum dA s to the wave's dW bins.
 template <int D, int NT>
-__device__ __forceinline__ void bwd_pass_b(const BwdLds& L, const uint16_t* __restrict__ K,
-                                           const uint16_t* __restrict__ V, float* __restrict__ dK,
+__device__ __forceinline__ void bwd_pass_b(const BwdLds& L, const uint16_t* __restrict__ K, float* __restrict__ dK,
                                            float* __restrict__ dV, float* mybins, const BwdShape& sh, int64_t pair,
-                                           int kt0, int lane, int g, int n) {
+                                           int kt0, int lane, int g, int n, const TileOps<D>& ko,
+                                           const TileOps<D>& vo) {
     using Cfg = BwdCfg<D>;
     constexpr int P = Cfg::P, KS = Cfg::KS, CPR = Cfg::CPR;
     const int M = sh.M, QT = sh.QT, CT = sh.C / 16;
-    bf16x8 bkh[NT][KS], bkl[NT][KS], bv[NT][KS];  // phi(k) and v as B operands: key n
+    const auto& bkh = ko.h;  // phi(k) and v as B operands: key n
+    const auto& bkl = ko.l;
+    const auto& bv = vo.h;
     int64_t krow[NT];
     int bj[NT];
 #pragma unroll
@@ -304,11 +318,6 @@ __device__ __forceinline__ void bwd_pass_b(const BwdLds& L, const uint16_t* __re
         const int kt = kt0 + kBW * u;
         bj[u] = kt / CT;
         krow[u] = pair * sh.N + 16 * kt + n;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            row_phi_operand<D>(K, krow[u], ks, g, bkh[u][ks], bkl[u][ks]);
-            bv[u][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(V + krow[u] * D + 32 * ks + 8 * g));
-        }
     }
     f32x4 vacc[NT][P], kacc[NT][P];  // dv^T, d phi(k)^T: values / features 16c + 4g + i, key n
     float dwl[NT];  // this lane's part of sum dA s for block pair (bcur, bj)
@@ -486,33 +495,64 @@ __global__ __launch_bounds__(64 * kBW) void bwd_fused_kernel(const uint16_t* __r
 
     // ---- pass A: the wave's query tiles (w, and w + 8 when there is one) ----
     const BwdLds L{pl0, pl1, pl2, pl3, rden_s, dden_s, zt, wl, bins};
+    // Query tiles of the wave in pass A (every tile of the pair has exactly one owner), and
+    // its key tiles in pass B.
+    int nq = 0, nk = 0, qt_[2] = {0, 0}, kt0 = wave;
     if (half >= 0) {  // (QT = 16)
-        const int qts[2] = {8 * half + wave, 8 * (1 - half) + wave};
-        bwd_pass_a<D, 2, 1>(L, Q, dY, dQ, sh, pair, qts, g, n);
+        nq = 2, qt_[0] = 8 * half + wave, qt_[1] = 8 * (1 - half) + wave;
+        nk = 1, kt0 = 8 * half + wave;
     } else if (wave < QT) {
-        if (wave + kBW < QT) {
-            const int qts[2] = {wave, wave + kBW};
-            bwd_pass_a<D, 2, 2>(L, Q, dY, dQ, sh, pair, qts, g, n);
-        } else {
-            const int qts[1] = {wave};
-            bwd_pass_a<D, 1, 1>(L, Q, dY, dQ, sh, pair, qts, g, n);
+        nq = nk = wave + kBW < QT ? 2 : 1;
+        qt_[0] = wave, qt_[1] = wave + kBW;
+    }
+    TileOps<D> qo, yo;
+    if (half >= 0) {
+        const int qts[2] = {qt_[0], qt_[1]};
+        bwd_pass_a<D, 2, 1>(L, Q, dY, dQ, sh, pair, qts, g, n, qo, yo);
+    } else if (nq == 2) {
+        const int qts[2] = {qt_[0], qt_[1]};
+        bwd_pass_a<D, 2, 2>(L, Q, dY, dQ, sh, pair, qts, g, n, qo, yo);
+    } else if (nq == 1) {
+        const int qts[1] = {qt_[0]};
+        bwd_pass_a<D, 1, 1>(L, Q, dY, dQ, sh, pair, qts, g, n, qo, yo);
+    }
+    // Pass B's key operands -- phi(K) hi/lo and V rows of the wave's key tiles -- are taken
+    // from the planes before pass B's operands replace them.
+    TileOps<D> ko, vo;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        if (u < nk) {  // uniform
+#pragma unroll
+            for (int ks = 0; ks < Cfg::KS; ++ks) {
+                ko.h[u][ks] = lds_rows<D>(pl0, 16 * (kt0 + kBW * u), ks, g, n);
+                ko.l[u][ks] = lds_rows<D>(pl1, 16 * (kt0 + kBW * u), ks, g, n);
+                vo.h[u][ks] = lds_rows<D>(pl2, 16 * (kt0 + kBW * u), ks, g, n);
+            }
         }
     }
     __syncthreads();  // every wave is done with phi(K) and V in LDS; 1 / den, dden written
 
-    // ---- pass B: phi(Q) hi/lo and dy hi/lo to LDS; the wave's key tiles ----
-    stage_rows<D, true>(Q, base, N, pl0, pl1);
-    stage_dy<D>(dY, base, N, pl2, pl3);
+    // ---- pass B: phi(Q) hi/lo and dy hi/lo to LDS from pass A's operands (each query tile
+    // has one owner, and the row-layout operand is what lds_rows reads back) ----
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        if (u < nq) {  // uniform
+#pragma unroll
+            for (int ks = 0; ks < Cfg::KS; ++ks) {
+                const int off = 16 * swz(16 * qt_[u] + n, 4 * ks + g, CPR);
+                *reinterpret_cast<bf16x8*>(pl0 + off) = qo.h[u][ks];
+                *reinterpret_cast<bf16x8*>(pl1 + off) = qo.l[u][ks];
+                *reinterpret_cast<bf16x8*>(pl2 + off) = yo.h[u][ks];
+                *reinterpret_cast<bf16x8*>(pl3 + off) = yo.l[u][ks];
+            }
+        }
+    }
     __syncthreads();
     float* const mybins = bins + wave * kBMaxBlocks * kBMaxBlocks;
-    if (half >= 0) {
-        bwd_pass_b<D, 1>(L, K, V, dK, dV, mybins, sh, pair, 8 * half + wave, lane, g, n);
-    } else if (wave < QT) {
-        if (wave + kBW < QT)
-            bwd_pass_b<D, 2>(L, K, V, dK, dV, mybins, sh, pair, wave, lane, g, n);
-        else
-            bwd_pass_b<D, 1>(L, K, V, dK, dV, mybins, sh, pair, wave, lane, g, n);
-    }
+    if (nk == 2)
+        bwd_pass_b<D, 2>(L, K, dK, dV, mybins, sh, pair, kt0, lane, g, n, ko, vo);
+    else if (nk == 1)
+        bwd_pass_b<D, 1>(L, K, dK, dV, mybins, sh, pair, kt0, lane, g, n, ko, vo);
     __syncthreads();
     // the pair's dW: the waves' bins in wave order
     for (int t = threadIdx.x; t < M * M; t += 64 * kBW) {
