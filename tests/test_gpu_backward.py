@@ -133,6 +133,48 @@ TOKEN_LEVEL = [  # (B, H, N, d, M): shapes the token-level backward takes (bf16,
 ]
 
 
+CAUSAL_QUERIES = [  # (B, H, N, d, M): causal bf16 shapes whose query side runs in the token-level form
+    #                  (blocks of an even number of 16-token tiles, at most 256 tokens)
+    (2, 2, 256, 64, 8),   # blocks of 32 tokens: two tiles
+    (1, 3, 384, 32, 6),   # 64 tokens, d = 32
+    (1, 2, 768, 64, 4),   # 192 tokens: 12 tiles, the larger LDS variant, snake slots partly empty
+    (1, 1, 1024, 64, 4),  # 256 tokens: 16 tiles, four per wave
+    (2, 2, 1024, 32, 8),  # 128 tokens at d = 32
+]
+
+
+@pytest.mark.parametrize("normalize", [True, False], ids=["norm", "nonorm"])
+@pytest.mark.parametrize("case", CAUSAL_QUERIES, ids=lambda c: "B{}H{}N{}d{}M{}".format(*c))
+def test_causal_token_level_queries_match_oracle(case, normalize):
+    """Causal backward whose query side (dq, dS~, dz~, dW[i,i], per-token den) takes masked
+    query x key products over the block instead of a running state, against the backward
+    oracle at the same 1e-4 bar, with and without the normaliser."""
+    B, H, N, d, M = case
+    idx = CAUSAL_QUERIES.index(case)
+    w = WORKLOADS["lm_causal_8k"].shrink(B=B, H=H, N=N, d=d, M=M, causal=True, dtype="bf16", seed=6800 + idx)
+    q, k, v, W = make_inputs(w)
+    dy = np.random.default_rng(6900 + idx).standard_normal(q.shape).astype(np.float32)
+    say(f"[backward, causal queries] B={B} H={H} N={N} d={d} M={M} normalize={normalize}")
+    got = gpu_backward(q, k, v, W, dy, True, "bf16", normalize=normalize)
+    ref = oracle_backward(q, k, v, W, dy, causal=True, normalize=normalize)
+    for name, g, r in zip(("dq", "dk", "dv", "dW"), got, ref):
+        assert np.all(np.isfinite(g)), name
+        e = float(np.max(np.abs(g.astype(np.float64) - r))) / float(np.max(np.abs(r)))
+        say(f"[backward, causal queries]   {name}: max|d|/max|ref| = {e:.2e}")
+        assert e <= TOL, (name, e)
+    assert np.all(np.triu(got[3], 1) == 0)
+
+
+def test_causal_token_level_queries_deterministic():
+    w = WORKLOADS["lm_causal_8k"].shrink(B=2, H=2, N=1024, M=8, seed=6950)
+    q, k, v, W = make_inputs(w)
+    dy = np.random.default_rng(6951).standard_normal(q.shape).astype(np.float32)
+    a = gpu_backward(q, k, v, W, dy, True, "bf16")
+    b = gpu_backward(q, k, v, W, dy, True, "bf16")
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
 @pytest.mark.parametrize("normalize", [True, False], ids=["norm", "nonorm"])
 @pytest.mark.parametrize("case", TOKEN_LEVEL, ids=lambda c: "B{}H{}N{}d{}M{}".format(*c))
 def test_token_level_backward_matches_oracle(case, normalize):

@@ -52,6 +52,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "lds_tiles.hpp"
 
 namespace mhla {
 
@@ -984,6 +985,309 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void b
         query_causal_wave<D, T, 1>(Q, K, V, dY, W, St, dQ, dSt, G, dWdiag, BH, N, M, norm, sh);
 }
 
+// Causal query side in the token-level form, for blocks of an even number of whole
+// 16-token tiles (C <= CMAX).  With A_t = S~_i + W[i,i] P_t (P_t: the block's phi(k) v^T
+// up to and including t), the within-block parts of U_t = A_t dy_t and of the normaliser
+// a_t = z~_i + W[i,i] p_t are sums over keys j <= t of the block,
+//
+//   P_t dy_t = sum_{j <= t} g_tj phi(k_j),  g_tj = v_j . dy_t,    p_t = sum_{j <= t} phi(k_j),
+//   phi(q_t).P_t dy_t = sum_{j <= t} s_tj g_tj,  phi(q_t).p_t = sum_{j <= t} s_tj,  s_tj = phi(q_t).phi(k_j),
+//
+// formed as masked products over the block's key tiles rather than by carrying P_t tile
+// by tile, so that the block's query tiles are independent.  One workgroup of four waves
+// per (pair, block): phi(K) hi/lo, V and S~_i hi/lo (row-major [r][c]) in LDS; wave w
+// takes the query tiles of its snake slots.  Per tile, in the transposed layout (features
+// 16F + 4g + i of query n): U^T = S~ dy^T + sum_j W g phi(k_j) and p^T (the masked product
+// with ones); den, dden, dq.  A second loop over the same tiles then adds, in the dot
+// layout of the other kernels, the tiles' parts of dS~_i^T = sum_t phi(q_t) dnum_t^T and
+// dz~_i (so that their accumulators do not share registers with the first loop's), and
+// the waves' parts are added in a fixed order at the end.  Outputs as bwd_query_causal_kernel: dq, dS~^T and dz~ of
+// the block, (den, dden) per token, and the block's part of dW[i,i].
+// Eight float32 values (k-slots 0-3 from a, 4-7 from b) as bf16 hi and lo operands.
+__device__ __forceinline__ void split_pair8(const f32x4& a, const f32x4& b, bf16x8& h, bf16x8& l) {
+    uint32_t hh[4], ll[4];
+    split2_bf16(a[0], a[1], hh[0], ll[0]);
+    split2_bf16(a[2], a[3], hh[1], ll[1]);
+    split2_bf16(b[0], b[1], hh[2], ll[2]);
+    split2_bf16(b[2], b[3], hh[3], ll[3]);
+    h = __builtin_bit_cast(bf16x8, u32x4{hh[0], hh[1], hh[2], hh[3]});
+    l = __builtin_bit_cast(bf16x8, u32x4{ll[0], ll[1], ll[2], ll[3]});
+}
+
+template <int D, int CMAX>
+struct QcTl {
+    static constexpr int P = D / 16, KS = D / 32, CPR = D / 8;
+    static constexpr int kPlane = CMAX * D * 2;  // one bf16 [CMAX][D] plane
+    static constexpr int kSt = D * D * 2;        // one bf16 [D][D] plane
+    // phi(K) hi, phi(K) lo, V, S~ hi, S~ lo, z~ (D floats), per-wave dW parts (4 floats)
+    static constexpr int kBytes = 3 * kPlane + 2 * kSt + D * 4 + 16;
+};
+
+template <int D, int CMAX>
+__global__ __launch_bounds__(256) void bwd_query_causal_tl_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const float* __restrict__ dY, const float* __restrict__ W, const float* __restrict__ St, float* __restrict__ dQ,
+    float* __restrict__ dSt, float* __restrict__ G, float* __restrict__ dWdiag, int64_t BH, int N, int M, int norm) {
+    using Cf = QcTl<D, CMAX>;
+    constexpr int P = Cf::P, KS = Cf::KS, CPR = Cf::CPR, L = D * D + D;
+    __shared__ __align__(16) unsigned char lds[Cf::kBytes];
+    unsigned char* const pkh = lds;
+    unsigned char* const pkl = lds + Cf::kPlane;
+    unsigned char* const pv = lds + 2 * Cf::kPlane;
+    unsigned char* const sth = lds + 3 * Cf::kPlane;
+    unsigned char* const stl = sth + Cf::kSt;
+    float* const zts = reinterpret_cast<float*>(stl + Cf::kSt);
+    float* const dwp = zts + D;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4, n = lane & 15;
+    const int64_t unit = blockIdx.x, pair = unit / M;
+    const int blk = (int)(unit % M), C = N / M, T = C / 16;
+    const int64_t tok0 = pair * N + (int64_t)blk * C;
+    const float wii = W[(int64_t)blk * M + blk];
+    const float* sv = St + ((int64_t)blk * BH + pair) * L;
+
+    // ---- staging: phi(K) hi/lo and V rows of the block, S~_i to [r][c] hi/lo, z~_i ----
+    {
+        constexpr int NU = CMAX * CPR / 256, NS = D * D / 1024;
+        u32x4 kw[NU], vw[NU];
+        f32x4 sw[NS];
+#pragma unroll
+        for (int j = 0; j < NU; ++j) {
+            const int u = threadIdx.x + 256 * j, row = min(u / CPR, C - 1), pc = u % CPR;  // (rows past C: unused)
+            kw[j] = *reinterpret_cast<const u32x4*>(K + (tok0 + row) * D + 8 * pc);
+            vw[j] = *reinterpret_cast<const u32x4*>(V + (tok0 + row) * D + 8 * pc);
+        }
+#pragma unroll
+        for (int j = 0; j < NS; ++j) sw[j] = *reinterpret_cast<const f32x4*>(sv + (threadIdx.x + 256 * j) * 4);
+        if ((int)threadIdx.x < D) zts[threadIdx.x] = sv[D * D + threadIdx.x];
+#pragma unroll
+        for (int j = 0; j < NU; ++j) {
+            const int u = threadIdx.x + 256 * j, row = u / CPR, pc = u % CPR;
+            if (row >= C) break;  // (uniform in j: C is a multiple of 32 rows)
+            const int off = 16 * swz(row, pc, CPR);
+            uint32_t h[4], l[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                split2_bf16(phi_b(__uint_as_float(kw[j][e] << 16)), phi_b(__uint_as_float(kw[j][e] & 0xffff0000u)),
+                            h[e], l[e]);
+            *reinterpret_cast<u32x4*>(pkh + off) = u32x4{h[0], h[1], h[2], h[3]};
+            *reinterpret_cast<u32x4*>(pkl + off) = u32x4{l[0], l[1], l[2], l[3]};
+            *reinterpret_cast<u32x4*>(pv + off) = vw[j];
+        }
+        // S~_i is stored transposed in the packed layout: chunk (ia, ib), lane l, element i
+        // holds S~[r = P (l % 16) + ib][c = P (4 (l / 16) + i) + ia].
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+            const int x = threadIdx.x + 256 * j;
+            const int chunk = x / 64, l = x % 64, ia = chunk / P, ib = chunk % P;
+            const int r = P * (l % 16) + ib;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int c = P * (4 * (l / 16) + i) + ia;
+                const int off = 16 * swz(r, c >> 3, CPR) + 2 * (c & 7);
+                uint32_t h, lo;
+                split2_bf16(sw[j][i], 0.f, h, lo);
+                *reinterpret_cast<uint16_t*>(sth + off) = (uint16_t)h;
+                *reinterpret_cast<uint16_t*>(stl + off) = (uint16_t)lo;
+            }
+        }
+    }
+    __syncthreads();
+    // A 16 x 32 operand from a plane: lane (g, n) takes row r0 + n, k-slots 8g .. 8g + 7
+    // (columns 32 ks + 8g ..).
+    auto rows_op = [&](const unsigned char* plane, int r0, int ks) {
+        return *reinterpret_cast<const bf16x8*>(plane + 16 * swz(r0 + n, 4 * ks + g, CPR));
+    };
+
+    float dwl = 0.f, rden_q[4], dden_q[4];  // (query n of the wave's slots)
+#pragma unroll
+    for (int slot = 0; slot < 4; ++slot) {
+        rden_q[slot] = dden_q[slot] = 0.f;
+        const int qt = 8 * (slot >> 1) + ((slot & 1) ? 7 - wave : wave);  // snake order balances the triangle
+        if (qt >= T) continue;                                               // uniform
+        const int64_t qrow = tok0 + 16 * qt + n;                             // query n of the tile
+        bf16x8 bqh[KS], bql[KS], byh[KS], byl[KS];  // phi(q) and dy as B operands (features 32 ks + 8g ..)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const u32x4 w = *reinterpret_cast<const u32x4*>(Q + qrow * D + 32 * ks + 8 * g);
+            uint32_t h[4], l[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                split2_bf16(phi_b(__uint_as_float(w[e] << 16)), phi_b(__uint_as_float(w[e] & 0xffff0000u)), h[e],
+                            l[e]);
+            bqh[ks] = __builtin_bit_cast(bf16x8, u32x4{h[0], h[1], h[2], h[3]});
+            bql[ks] = __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], l[2], l[3]});
+            const f32x4* src = reinterpret_cast<const f32x4*>(dY + qrow * D + 32 * ks + 8 * g);
+            const f32x4 a = src[0], b = src[1];
+            split2_bf16(a[0], a[1], h[0], l[0]);
+            split2_bf16(a[2], a[3], h[1], l[1]);
+            split2_bf16(b[0], b[1], h[2], l[2]);
+            split2_bf16(b[2], b[3], h[3], l[3]);
+            byh[ks] = __builtin_bit_cast(bf16x8, u32x4{h[0], h[1], h[2], h[3]});
+            byl[ks] = __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], l[2], l[3]});
+        }
+        // U^T = S~ dy^T, to which the within-block sum_j W g phi(k_j) is added below, and p^T
+        // (features 16F + 4g + i, query n)
+        f32x4 us[P], ps[P];
+#pragma unroll
+        for (int F = 0; F < P; ++F) {
+            f32x4 a = zero4();
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 sh = rows_op(sth, 16 * F, ks), sl = rows_op(stl, 16 * F, ks);
+                a = mfma32(sh, byh[ks], a);
+                a = mfma32(sh, byl[ks], a);
+                a = mfma32(sl, byh[ks], a);
+            }
+            us[F] = a;
+            ps[F] = zero4();
+        }
+        // phi(q) and phi'(q) at features 16F + 4g + i of query n; its dots with z~ and S~ dy
+        float fq[P][4], dpq[P][4], pz = 0.f, pu = 0.f;
+#pragma unroll
+        for (int F = 0; F < P; ++F) {
+            const u32x2 qw = *reinterpret_cast<const u32x2*>(Q + qrow * D + 16 * F + 4 * g);
+            const float qv[4] = {__uint_as_float(qw[0] << 16), __uint_as_float(qw[0] & 0xffff0000u),
+                                 __uint_as_float(qw[1] << 16), __uint_as_float(qw[1] & 0xffff0000u)};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                fq[F][i] = phi_grad(qv[i], dpq[F][i]);
+                pz = fmaf(fq[F][i], zts[16 * F + 4 * g + i], pz);
+                pu = fmaf(fq[F][i], us[F][i], pu);
+            }
+        }
+        const float pzt = sum_over_groups(pz), pst = sum_over_groups(pu);
+        float ssum = 0.f, sgsum = 0.f;  // this lane's keys of sum_j s_tj, sum_j s_tj g_tj (query n)
+        for (int jp = 0; 2 * jp <= qt; ++jp) {
+            f32x4 wg2[2], mk2[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int kt = 2 * jp + hh;
+                wg2[hh] = mk2[hh] = zero4();
+                if (kt > qt) continue;  // uniform
+                f32x4 sc = zero4(), gg = zero4();  // keys 16 kt + 4g + e, query n
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const bf16x8 akh = rows_op(pkh, 16 * kt, ks), akl = rows_op(pkl, 16 * kt, ks);
+                    const bf16x8 av = rows_op(pv, 16 * kt, ks);
+                    sc = mfma32(akh, bqh[ks], sc);
+                    sc = mfma32(akh, bql[ks], sc);
+                    sc = mfma32(akl, bqh[ks], sc);
+                    gg = mfma32(av, byh[ks], gg);
+                    gg = mfma32(av, byl[ks], gg);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const bool keep = 16 * kt + 4 * g + e <= 16 * qt + n;  // key <= query
+                    const float s1 = keep ? sc[e] : 0.f, g1 = keep ? gg[e] : 0.f;
+                    ssum += s1;
+                    sgsum = fmaf(s1, g1, sgsum);
+                    wg2[hh][e] = wii * g1;
+                    mk2[hh][e] = keep ? 1.f : 0.f;
+                }
+            }
+            bf16x8 gh, gl, mh, ml;  // k-slot 8g + 4hh + e = key 32 jp + 16 hh + 4g + e
+            split_pair8(wg2[0], wg2[1], gh, gl);
+            split_pair8(mk2[0], mk2[1], mh, ml);  // (0 and 1 are exact: ml is zero)
+#pragma unroll
+            for (int F = 0; F < P; ++F) {
+                const bf16x8 kth = lds_operand_t(pkh, 32 * jp, 16 * F, CPR, g, n);
+                const bf16x8 ktl = lds_operand_t(pkl, 32 * jp, 16 * F, CPR, g, n);
+                us[F] = mfma32(kth, gh, us[F]);
+                us[F] = mfma32(kth, gl, us[F]);
+                us[F] = mfma32(ktl, gh, us[F]);
+                ps[F] = mfma32(kth, mh, ps[F]);
+                ps[F] = mfma32(ktl, mh, ps[F]);
+            }
+        }
+        const float st = sum_over_groups(ssum), sgt = sum_over_groups(sgsum);
+        // den_t = phi(q).a_t + eps = phi(q).z~ + W sum_j s_tj + eps, and phi(q).U_t =
+        // phi(q).S~ dy_t + W sum_j s_tj g_tj (the within-block parts from the same sums that
+        // dW[i,i] takes, so that they cancel there as they should); without the normaliser
+        // den = 1 (stored so that the key pass's dnum = dy) and dden = 0
+        const float den = norm ? fmaf(wii, st, pzt) + kEps : 1.f;
+        const float rden = norm ? fast_rcp(den) : 1.f;
+        const float dden = norm ? -fmaf(wii, sgt, pst) * rden * rden : 0.f;
+        rden_q[slot] = rden;
+        dden_q[slot] = dden;
+        // dq = (U / den + dden (z~ + W p)) phi'(q)
+#pragma unroll
+        for (int F = 0; F < P; ++F) {
+            f32x4 out;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float a = fmaf(wii, ps[F][i], zts[16 * F + 4 * g + i]);
+                out[i] = fmaf(us[F][i], rden, dden * a) * dpq[F][i];
+            }
+            *reinterpret_cast<f32x4*>(dQ + qrow * D + 16 * F + 4 * g) = out;
+        }
+        if (g == 0) {
+            *reinterpret_cast<float2*>(G + qrow * 2) = make_float2(den, dden);
+            dwl += fmaf(sgt, rden, dden * st);  // this query's part of dW[i,i]
+        }
+    }
+    // dS~^T += dnum phi(q)^T, dz~ += dden phi(q) over the wave's tiles, in the dot layout
+    // (tokens 4g + i, features P n + b): chunk (ia, ib) of the packed layout directly
+    f32x4 acc[P * P];
+    float zacc[P];
+#pragma unroll
+    for (int c = 0; c < P * P; ++c) acc[c] = zero4();
+#pragma unroll
+    for (int b = 0; b < P; ++b) zacc[b] = 0.f;
+#pragma unroll
+    for (int slot = 0; slot < 4; ++slot) {
+        const int qt = 8 * (slot >> 1) + ((slot & 1) ? 7 - wave : wave);
+        if (qt >= T) continue;  // uniform
+        {
+            const rsrc_t rq = tile_rsrc(Q, tok0 + 16 * qt, 16, D), ry = tile_rsrc(dY, tok0 + 16 * qt, 16, D);
+            float qd[4][P], yd[4][P];
+            load_dl<uint16_t, D>(rq, g, n, qd);
+            load_dl<float, D>(ry, g, n, yd);
+            float dn[4][P], fd[4][P], ddi[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float ri = __shfl(rden_q[slot], 4 * g + i, 64);  // lane 4g + i holds query 4g + i
+                ddi[i] = __shfl(dden_q[slot], 4 * g + i, 64);
+#pragma unroll
+                for (int b = 0; b < P; ++b) {
+                    fd[i][b] = phi_b(qd[i][b]);
+                    dn[i][b] = yd[i][b] * ri;
+                }
+            }
+            bf16x4 nh[P], nl[P];
+            split_dl<P>(dn, nh, nl);
+#pragma unroll
+            for (int j = 0; j < P; ++j) {
+                bf16x4 qh, ql;
+                split4(fd[0][j], fd[1][j], fd[2][j], fd[3][j], qh, ql);
+#pragma unroll
+                for (int ia = 0; ia < P; ++ia) {
+                    f32x4 c = acc[ia * P + j];
+                    c = mfma16(nh[ia], qh, c);
+                    c = mfma16(nh[ia], ql, c);
+                    c = mfma16(nl[ia], qh, c);
+                    acc[ia * P + j] = c;
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) zacc[j] = fmaf(ddi[i], fd[i][j], zacc[j]);
+            }
+        }
+    }
+    // ---- the block's dS~^T, dz~ and dW[i,i] part: the waves' parts added in wave order ----
+#pragma unroll
+    for (int b = 0; b < P; ++b) zacc[b] = sum_over_groups(zacc[b]);
+    dwl = sum_over_groups(sum16(dwl));
+    if (lane == 0) dwp[wave] = dwl;
+    __syncthreads();  // the planes are free for the reduction below
+    reduce_waves<P>(acc, zacc, reinterpret_cast<float*>(lds), wave, 4, lane, g, n);
+    if (wave == 0) {
+        store_packed<P>(dSt + ((int64_t)blk * BH + pair) * L, lane, g, n, acc, zacc);
+        if (lane == 0) dWdiag[pair * M + blk] = ((dwp[0] + dwp[1]) + dwp[2]) + dwp[3];
+    }
+}
+
 // Causal, two waves per (pair, key block b), tiles in reverse order.  The running
 // dS_b + W_bb R_{>tile} is needed in two orientations: rows c for d phi(k) (contracted
 // over c with v) and rows r for dv (contracted over r with phi(k)).  Wave 0 keeps the
@@ -1438,7 +1742,22 @@ hipError_t run_backward(const T* q, const T* k, const T* v, const float* W, cons
     bwd_sum_kernel<D, T><<<grid, block, red, stream>>>(k, v, S, BH, (int)N, (int)M, wpu);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = launch_mix(S, W, St, BH, D, M, causal, false, 0, frag_ws, stream)) != hipSuccess) return e;
-    if (causal)
+    if (causal && std::is_same<T, uint16_t>::value && (D == 32 || D == 64) && C % 32 == 0 && C <= 256) {
+        // token-level form of the within-block part (blocks of an even number of whole tiles)
+        const uint16_t* q16 = reinterpret_cast<const uint16_t*>(q);
+        const uint16_t* k16 = reinterpret_cast<const uint16_t*>(k);
+        const uint16_t* v16 = reinterpret_cast<const uint16_t*>(v);
+#define MHLA_QCTL(DD, CM)                                                                                      \
+        bwd_query_causal_tl_kernel<DD, CM><<<grid, dim3(256), 0, stream>>>(q16, k16, v16, dy, W, St, dq, dSt, G, \
+                                                                            dWdiag, BH, (int)N, (int)M,          \
+                                                                            normalize ? 1 : 0)
+        if constexpr (D == 32) {
+            if (C <= 128) MHLA_QCTL(32, 128); else MHLA_QCTL(32, 256);
+        } else if constexpr (D == 64) {
+            if (C <= 128) MHLA_QCTL(64, 128); else MHLA_QCTL(64, 256);
+        }
+#undef MHLA_QCTL
+    } else if (causal)
         bwd_query_causal_kernel<D, T><<<grid, dim3(D >= 32 ? 128 : 64), 0, stream>>>(
             q, k, v, dy, W, St, dq, dSt, G, dWdiag, BH, (int)N, (int)M, normalize ? 1 : 0);
     else
