@@ -91,6 +91,7 @@ SWEEP = [  # (B, H, N, d, M, causal, dtype)
     (1, 1, 64, 16, 64, True, "f32"),
     (3, 1, 40, 16, 8, True, "bf16"),    # C = 5
     (1, 1, 4096, 32, 256, False, "bf16"),
+    (1, 1, 4096, 64, 256, False, "bf16"),  # M = 256 walk: 260 column tiles, 4 in the last round
     (1, 1, 4096, 64, 256, True, "bf16"),
     (1, 2, 1536, 64, 3, False, "bf16"),  # C = 512: split summaries
     (1, 2, 1536, 64, 3, True, "bf16"),

@@ -131,6 +131,7 @@ PER_HEAD = [  # (B, H, N, d, M, causal, dtype): one per mixing kernel and output
     (2, 70, 256, 32, 64, False, "bf16"),  # 70 heads: the persistent M <= 64 walk with a grid row per head
     (1, 6, 960, 16, 48, True, "bf16"),    # causal 32 < M <= 64 walk, per head
     (1, 2, 2560, 16, 160, True, "bf16"),  # 64 < M <= 256 mixing
+    (1, 2, 4096, 64, 256, False, "bf16"),  # M = 256 walk, one grid row per head
     (1, 2, 600, 32, 300, False, "bf16"),  # split-W fragments, one copy per head
     (1, 2, 2048, 16, 2048, False, "bf16"),  # M > 1024 mixing
     (1, 2, 1536, 32, 3, True, "bf16"),    # running-state causal output kernel
