@@ -208,3 +208,40 @@ def test_token_level_backward_is_deterministic():
     b = gpu_backward(q, k, v, W, dy, False, "bf16")
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["noncausal", "causal"])
+def test_streaming_backward_matches_split_batch(causal):
+    """Token inputs larger than the 256 MiB Infinity Cache are summarised with streaming
+    (non-temporal) loads; the same pairs run as two half batches below that size take the
+    cached loads, whose results the oracle cases above pin.  The per-pair gradients of the
+    two runs agree to rounding (the reduction order may follow the batch size) and dW of
+    the whole batch is the sum of the halves' dW."""
+    B, H, N, d, M = 4, 2, 98304, 64, 256  # C = 384: one pass without token segments
+    assert 3 * B * H * N * d * 2 > 256 << 20 >= 3 * (B // 2) * H * N * d * 2
+    say(f"[backward streaming] B={B} H={H} N={N} d={d} M={M} causal={causal}")
+    g = torch.Generator(device="cuda").manual_seed(7100 + causal)
+    q, k, v = (torch.randn((B, H, N, d), generator=g, device="cuda").to(torch.bfloat16) for _ in range(3))
+    W = torch.rand((M, M), generator=g, device="cuda") + 0.05
+    dy = torch.randn((B, H, N, d), generator=g, device="cuda")
+
+    def run(lo, hi):
+        grads = [torch.empty((hi - lo, H, N, d), device="cuda") for _ in range(3)]
+        dW = torch.empty((M, M), device="cuda")
+        mh.mhla_backward(q[lo:hi].contiguous(), k[lo:hi].contiguous(), v[lo:hi].contiguous(), W,
+                         dy[lo:hi].contiguous(), *grads, dW, causal=causal)
+        return grads, dW
+
+    whole, dW = run(0, B)
+    first, dW0 = run(0, B // 2)
+    second, dW1 = run(B // 2, B)
+    torch.cuda.synchronize()
+    for name, a, b0, b1 in zip(("dq", "dk", "dv"), whole, first, second):
+        ref = torch.cat([b0, b1])
+        assert torch.isfinite(a).all(), name
+        e = float((a - ref).abs().max() / ref.abs().max())
+        say(f"[backward streaming]   {name}: {e:.2e}")
+        assert e <= 1e-5, (name, e)
+    e = float((dW - (dW0 + dW1)).abs().max() / dW.abs().max())
+    say(f"[backward streaming]   dW: {e:.2e}")
+    assert e <= 1e-5, e

@@ -1739,8 +1739,13 @@ hipError_t run_backward(const T* q, const T* k, const T* v, const float* W, cons
     const size_t red = (size_t)(wpu / 2) * L * sizeof(float);
     const dim3 grid((unsigned)units), block(64 * wpu);
     hipError_t e;
-    bwd_sum_kernel<D, T><<<grid, block, red, stream>>>(k, v, S, BH, (int)N, (int)M, wpu);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (std::is_same<T, uint16_t>::value && summaries_t_fits(BH, N, D, M)) {
+        e = launch_summaries_t((const uint16_t*)k, (const uint16_t*)v, S, BH, N, D, M, stream);
+    } else {
+        bwd_sum_kernel<D, T><<<grid, block, red, stream>>>(k, v, S, BH, (int)N, (int)M, wpu);
+        e = hipGetLastError();
+    }
+    if (e != hipSuccess) return e;
     if ((e = launch_mix(S, W, St, BH, D, M, causal, false, 0, frag_ws, stream)) != hipSuccess) return e;
     if (causal && std::is_same<T, uint16_t>::value && (D == 32 || D == 64) && C % 32 == 0 && C <= 256) {
         // token-level form of the within-block part (blocks of an even number of whole tiles)

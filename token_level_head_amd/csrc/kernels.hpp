@@ -52,6 +52,12 @@ inline bool stream_token_inputs(int64_t BH, int64_t N, int D, int esize) {
 // is 0) and are then added into S.
 // `cmax` bounds the block length (N / M without a token list) and plans the split.
 size_t summary_partial_bytes(int dtype, int64_t BH, int64_t cmax, int D, int64_t M);
+// The transposed summaries S_b^T, z_b of equal contiguous bf16 blocks for the backward
+// pass (packed layout, [M][BH][d*d + d]); summaries_t_fits() says whether one pass
+// without token segments covers the shape (else launch_summaries_t refuses it).
+bool summaries_t_fits(int64_t BH, int64_t N, int D, int64_t M);
+hipError_t launch_summaries_t(const uint16_t* k, const uint16_t* v, float* St, int64_t BH, int64_t N, int D,
+                              int64_t M, hipStream_t stream);
 hipError_t launch_summaries(int dtype, const void* k, const void* v, float* S, int64_t BH, int64_t N,
                             int D, int64_t M, int heads, const BlockLayout& lay, int64_t cmax, float* partial,
                             hipStream_t stream);

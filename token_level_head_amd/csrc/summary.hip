@@ -67,8 +67,12 @@ __device__ __forceinline__ uint32_t token_bits(const typename TokenWords<P>::typ
     else return w;
 }
 
-template <int D, bool PIPE, bool NT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void summaries_bf16_kernel(
+// TR: the transposed summary S_b^T[c][r] = sum_j v_j[c] phi(k_j)[r] in the same packed
+// layout (value features along the MFMA rows, key features along its columns), with
+// phi(k) split into bf16 hi + lo (two products; v is an exact bf16 operand) and z
+// summed in float32: the operand the backward pass contracts over the value index.
+template <int D, bool PIPE, bool NT, bool TR = false>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TR && D == 64 ? 3 : 4))) void summaries_bf16_kernel(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, float* __restrict__ S, int64_t BH, int N, int M,
     int wpb, int nseg, int segC, int heads, BlockLayout lay) {
     constexpr int P = D / 16;
@@ -126,6 +130,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
         };
         auto compute = [&](const TW (&kr)[8], const TW (&vr)[8], int t, auto masked_c) {
             constexpr bool masked = decltype(masked_c)::value;
+            if constexpr (TR) {
+#pragma unroll
+                for (int ib = 0; ib < P; ++ib) {  // B operand: phi(k) feature Pn + ib, hi and lo
+                    uint32_t fh[4], fl[4];
+#pragma unroll
+                    for (int e2 = 0; e2 < 4; ++e2) {
+                        float f0 = phi_fast(token_feature<P>(kr[2 * e2], ib));
+                        float f1 = phi_fast(token_feature<P>(kr[2 * e2 + 1], ib));
+                        if constexpr (masked) {
+                            f0 = t + 8 * e2 + g < t_end ? f0 : 0.f;
+                            f1 = t + 8 * e2 + 4 + g < t_end ? f1 : 0.f;
+                        }
+                        zacc[ib] += f0 + f1;
+                        split2_bf16(f0, f1, fh[e2], fl[e2]);
+                    }
+                    const bf16x8 bh = __builtin_bit_cast(bf16x8, u32x4{fh[0], fh[1], fh[2], fh[3]});
+                    const bf16x8 bl = __builtin_bit_cast(bf16x8, u32x4{fl[0], fl[1], fl[2], fl[3]});
+#pragma unroll
+                    for (int ia = 0; ia < P; ++ia) {  // A operand: v feature Pn + ia
+                        uint32_t vb[4];
+#pragma unroll
+                        for (int e2 = 0; e2 < 4; ++e2)
+                            vb[e2] = token_bits<P>(vr[2 * e2], ia) | (token_bits<P>(vr[2 * e2 + 1], ia) << 16);
+                        const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{vb[0], vb[1], vb[2], vb[3]});
+                        acc[ia][ib] = mfma32(a, bh, acc[ia][ib]);
+                        acc[ia][ib] = mfma32(a, bl, acc[ia][ib]);
+                    }
+                }
+                return;
+            }
 #pragma unroll
             for (int ia = 0; ia < P; ++ia) {
                 uint32_t pk[4];
@@ -313,6 +347,40 @@ SummarySplit summary_split(int64_t BH, int64_t C, int64_t M) {
 }
 
 }  // namespace
+
+bool summaries_t_fits(int64_t BH, int64_t N, int D, int64_t M) {
+    return (D == 16 || D == 32 || D == 64) && M > 0 && N % M == 0 && summary_split(BH, N / M, M).nseg == 1;
+}
+
+hipError_t launch_summaries_t(const uint16_t* k, const uint16_t* v, float* St, int64_t BH, int64_t N, int D,
+                              int64_t M, hipStream_t stream) {
+    if (!summaries_t_fits(BH, N, D, M)) return hipErrorInvalidValue;
+    const int64_t units = BH * M;
+    const SummarySplit sp = summary_split(BH, N / M, M);
+    const int per_wg = 4 / sp.wpb;
+    const int64_t grid = (units + per_wg - 1) / per_wg;
+    const int P = D / 16;
+    const size_t lds = sp.wpb > 1 ? (size_t)(4 - per_wg) * 64 * (4 * P * P + P) * sizeof(float) : 0;
+    const BlockLayout lay{nullptr, nullptr};
+    const bool nt = stream_token_inputs(BH, N, D, 2);
+#define MHLA_SUMMARIES_T_CASE(DD, PIPE)                                                                      \
+    case DD:                                                                                               \
+        if (nt)                                                                                            \
+            summaries_bf16_kernel<DD, PIPE, true, true><<<dim3((unsigned)grid), dim3(256), lds, stream>>>( \
+                k, v, St, BH, (int)N, (int)M, sp.wpb, 1, (int)(N / M), 0, lay);                            \
+        else                                                                                               \
+            summaries_bf16_kernel<DD, PIPE, false, true><<<dim3((unsigned)grid), dim3(256), lds, stream>>>(\
+                k, v, St, BH, (int)N, (int)M, sp.wpb, 1, (int)(N / M), 0, lay);                            \
+        break;
+    switch (D) {
+        MHLA_SUMMARIES_T_CASE(16, true)
+        MHLA_SUMMARIES_T_CASE(32, true)
+        MHLA_SUMMARIES_T_CASE(64, false)
+        default: return hipErrorInvalidValue;
+    }
+#undef MHLA_SUMMARIES_T_CASE
+    return hipGetLastError();
+}
 
 size_t summary_partial_bytes(int dtype, int64_t BH, int64_t C, int D, int64_t M) {
     if (dtype == kDtypeF32) return 0;
