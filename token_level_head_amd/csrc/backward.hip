@@ -1679,7 +1679,7 @@ DwPlan dw_plan(int64_t ncols, int64_t M) {
     // workgroups past it would form a second round alone.
     const int64_t round = 256 * (p.rt == 1 ? 6 : 4);
     const int64_t want = std::max<int64_t>(1, round / nblk) * subs;  // partials (one per wave slot)
-    const int64_t most = std::max<int64_t>(1, ncols / 512);          // at least 512 columns per partial
+    const int64_t most = std::max<int64_t>(1, ncols / 256);          // at least 256 columns per partial
     const int64_t nch = std::min(want, most);
     p.chunk = ((ncols + nch - 1) / nch + 31) / 32 * 32;
     p.nchunks = (ncols + p.chunk - 1) / p.chunk;
